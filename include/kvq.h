@@ -1,0 +1,238 @@
+/*
+ * kvq.h -- C ABI of libkvq: low-bit, mixed-precision KV-cache quantization,
+ * the Equivalent Right Shift bit-width shrink, and decode attention over the
+ * packed cache, for AMD Instinct MI355X (gfx950).
+ *
+ * Sources, cited by page title and section:
+ *   [PMKVQ]   "PM-KVQ: Progressive Mixed-Precision KV Cache Quantization for
+ *              Long-CoT LLMs" (papernotes.org summary).
+ *   [CHANMIX] "Channel-Aware Mixed-Precision Quantization for Efficient
+ *              Long-Context Inference" (papernotes.org summary).
+ *
+ * ------------------------------------------------------------------------
+ * Conventions
+ *   - Every buffer is owned by the caller.  Pointers named "device" are HIP
+ *     device memory; the library never allocates or frees device memory.
+ *   - The kvq_cache struct is host memory and is read during the call only;
+ *     kvq_quantize, kvq_shrink and kvq_append update its n_tokens / k_bits /
+ *     v_bits fields as documented.
+ *   - All device work is enqueued on the given stream; calls return before it
+ *     completes.  Every argument is validated on the host first: any status
+ *     other than KVQ_OK / KVQ_EHIP means no device work was enqueued.
+ *     KVQ_EHIP means a HIP call failed (work already enqueued may be partial).
+ *   - No exceptions cross the ABI.  The library holds no global mutable
+ *     state; calls on different caches are independent.  Calls that touch the
+ *     same cache or workspace must be ordered by the caller (same stream).
+ *
+ * ------------------------------------------------------------------------
+ * The quantizer ([CHANMIX] Key design 1; [PMKVQ] Training strategy)
+ *   A group is a set of real values x.  With mn = min x, mx = max x:
+ *     S  = (mx - mn) / (2^b - 1)      (binary32: one subtraction, one division)
+ *     S' = narrow(S),  Z' = narrow(mn)   (round to nearest even to the
+ *                                         parameter dtype; e4m3 saturates)
+ *     q  = clamp(rne((x - Z') / S'), 0, 2^b - 1)   (binary32), or 0 if S' == 0
+ *   and the reconstruction is x^ = S' * q + Z'.  Inputs must be finite and
+ *   small enough that S' and Z' are finite in the parameter dtype.
+ *   Keys are grouped channel-wise: one group = one channel (slot) over one
+ *   128-token tile.  Values are grouped token-wise: one group = the 128
+ *   channels of one token ([CHANMIX] Background; [PMKVQ] related work on KIVI).
+ *   Bit widths: 16, 8, 4, 2, 1 ("16-bit" is an integer code, not fp16).
+ *
+ * Equivalent Right Shift ([PMKVQ] Key design 1, ERS equation), per code:
+ *     X_b = ((2^(2b) - 2^b + 1) * (X_2b + 2^(b-1))) >> 3b   (unsigned 32-bit)
+ *     Z'_b = Z'_2b,   S'_b = narrow((2^b + 1) * S'_2b)       (binary32 product)
+ *
+ * ------------------------------------------------------------------------
+ * Packed layouts
+ *   Tokens of a (batch b, kv head h) stream are cut into tiles of 128 tokens;
+ *   tile g holds tokens [128g, 128g + 128).
+ *
+ *   Packed row: a little-endian bit string -- bit i of the row is bit (i mod 8)
+ *   of byte (i div 8); element e of a b-bit row occupies bits [e*b, e*b + b),
+ *   least significant code bit first.
+ *
+ *   Key tile, uniform width b (2048*b bytes): 128 rows of 16*b bytes; row t is
+ *     token 128g + t, element c is channel c.
+ *   Value tile, width b (2048*b bytes): 128 rows of 16*b bytes; row c is
+ *     channel c, element t is token 128g + t.
+ *   Key tile, mixed width (k_bits == KVQ_KMIXED, 4352 bytes) ([CHANMIX] Key
+ *     design 3: 4/3/2/1-bit channel classes, as many 1-bit as 3-bit channels,
+ *     channels reordered so every byte holds exactly 8 code bits):
+ *     slot j of a token holds channel k_slot_chan[h][j]; slots 0..7 are 4-bit,
+ *     slots 8..23 alternate 3-bit (even j) and 1-bit (odd j), slots 24..127 are
+ *     2-bit.  A token's logical 34-byte row is the packed row of its 128 slot
+ *     codes in slot order (widths as listed), so bytes 0..3 hold 4-bit pairs,
+ *     bytes 4..7 hold (3,1,3,1)-bit groups, bytes 8..33 hold 2-bit quads.  The
+ *     tile stores these rows as five column planes: logical bytes [0,8),
+ *     [8,16), [16,24), [24,32) go to planes 0..3 at tile offsets 0, 1024, 2048,
+ *     3072 with 8 bytes per token; logical bytes [32,34) go to plane 4 at tile
+ *     offset 4096 with 2 bytes per token; tokens are in order inside a plane.
+ *
+ *   Tile placement: tile g of stream (b, h) starts at
+ *     k_codes + k_tile_off[(g * batch + b) * n_kv_heads + h]   if k_tile_off,
+ *     k_codes + ((b * n_kv_heads + h) * max_tiles + g) * k_tile_stride   else,
+ *   (same for values) with max_tiles = max_tokens / 128.  Offsets and strides
+ *   are multiples of 256 bytes; a stride is at least the current tile size.
+ *   kvq_shrink rewrites every tile in place: the narrower tile occupies the
+ *   first half of the bytes the wider one used, at the same offset.
+ *
+ *   Parameters (S', Z' raw values of param_dtype):
+ *     k_scale, k_zero: [batch][n_kv_heads][max_tiles][128]  (per tile, per slot;
+ *                      for uniform keys slot j is channel j)
+ *     v_scale, v_zero: [batch][n_kv_heads][max_tokens]       (per token)
+ *
+ * ------------------------------------------------------------------------
+ * Decode attention ([CHANMIX] Overall framework and Key design 3: read the
+ * packed cache, dequantize to full precision, FlashAttention-style decode)
+ *   For batch b and query head hq, with G = n_q_heads / n_kv_heads and kv head
+ *   h = hq / G (query heads of one kv head are contiguous):
+ *     s_t = softmax_scale * sum_c q[b][hq][c] * K^[b][h][t][c],  t < n_tokens
+ *     out[b][hq][c] = sum_t softmax(s)_t * V^[b][h][t][c]
+ *   where K^, V^ are the reconstructions S' * q + Z' of the stored codes.
+ *   q is bfloat16 [batch][n_q_heads][128]; out is float32, same shape.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_EINVAL = 1,        /* invalid argument (null pointer, bad size, bad width ...) */
+    KVQ_EUNSUPPORTED = 2,  /* valid request this build does not implement */
+    KVQ_EBUDGET = 3,       /* kvq_append: the group does not fit even at floor_bits */
+    KVQ_EWORKSPACE = 4,    /* workspace pointer null or smaller than required */
+    KVQ_EHIP = 5           /* a HIP runtime call or kernel launch failed */
+} kvq_status;
+
+typedef enum {
+    KVQ_F32 = 0,
+    KVQ_F16 = 1,   /* IEEE binary16 */
+    KVQ_BF16 = 2,  /* bfloat16 */
+    KVQ_E4M3 = 3   /* OCP FP8 E4M3 (bias 7, max 448, no infinities), saturating */
+} kvq_dtype;
+
+#define KVQ_HEAD_DIM 128
+#define KVQ_GROUP 128
+#define KVQ_KMIXED 0          /* k_bits value selecting the mixed-width key tile */
+#define KVQ_MIXED_TILE_BYTES 4352
+
+typedef struct kvq_cache {
+    int32_t batch;            /* B >= 1 */
+    int32_t n_kv_heads;       /* Hkv >= 1 */
+    int32_t head_dim;         /* must be 128 */
+    int32_t group;            /* must be 128 */
+    int32_t max_tokens;       /* capacity per stream, multiple of 128 */
+    int32_t n_tokens;         /* tokens stored per stream, multiple of 128 */
+    int32_t k_bits;           /* 16, 8, 4, 2, 1, or KVQ_KMIXED */
+    int32_t v_bits;           /* 16, 8, 4, 2, 1 */
+    int32_t param_dtype;      /* kvq_dtype of S' and Z': F32, F16, BF16 or E4M3 */
+    int32_t reserved0;        /* must be 0 */
+    void *k_codes;            /* device: key tiles */
+    void *v_codes;            /* device: value tiles */
+    const int64_t *k_tile_off;  /* device [max_tiles][B][Hkv] byte offsets, or NULL */
+    const int64_t *v_tile_off;  /* device [max_tiles][B][Hkv] byte offsets, or NULL */
+    int64_t k_tile_stride;    /* bytes between tiles when k_tile_off is NULL */
+    int64_t v_tile_stride;    /* bytes between tiles when v_tile_off is NULL */
+    void *k_scale;            /* device [B][Hkv][max_tiles][128] */
+    void *k_zero;             /* device [B][Hkv][max_tiles][128] */
+    void *v_scale;            /* device [B][Hkv][max_tokens] */
+    void *v_zero;             /* device [B][Hkv][max_tokens] */
+    const int16_t *k_slot_chan; /* device [Hkv][128]: channel held by slot j
+                                   (mixed keys only, a permutation per head) */
+} kvq_cache;
+
+/* Human-readable name of a status code (static string). */
+const char *kvq_strerror(kvq_status status);
+
+/* Bytes of one packed tile at width `bits` (KVQ_KMIXED: the mixed key tile);
+ * 0 for an invalid width. */
+size_t kvq_tile_bytes(int32_t bits);
+
+/* Memory of a cache holding n_tokens tokens per stream at the given widths,
+ * as the progressive schedule counts it ([PMKVQ] Key design 2: total KV
+ * memory within the budget): key codes + value codes + every stored scale and
+ * zero point, over all B * Hkv streams.  k_bits may be KVQ_KMIXED.  Returns -1
+ * for invalid arguments. */
+int64_t kvq_cache_bytes(const kvq_cache *cache, int32_t n_tokens, int32_t k_bits, int32_t v_bits);
+
+/* Quantize and pack tokens [t0, t0 + n_new) of every stream at the cache's
+ * current widths (keys channel-wise per tile, values token-wise), writing the
+ * tiles and their S', Z'.  k / v: device inputs of logical shape
+ * [B][Hkv][n_new][128]; element (b, h, t, c) is at base + b*s[0] + h*s[1] +
+ * t*s[2] + c (strides in elements, channel stride 1).  in_dtype: KVQ_F32 or
+ * KVQ_BF16.  Either k or v may be NULL to skip that side.  t0 and n_new are
+ * multiples of 128, n_new >= 128, t0 + n_new <= max_tokens.  On success
+ * n_tokens becomes max(n_tokens, t0 + n_new). */
+kvq_status kvq_quantize(kvq_cache *cache, const void *k, const void *v, kvq_dtype in_dtype,
+                        const int64_t k_strides[3], const int64_t v_strides[3],
+                        int32_t t0, int32_t n_new, hipStream_t stream);
+
+/* Equivalent Right Shift of the whole cache ([PMKVQ] Key design 1): every
+ * stored key and value tile of every stream goes from 2*to_bits to to_bits
+ * bits in place, scales become narrow((2^b + 1) * S'), zero points stay.
+ * Requires k_bits == v_bits == 2 * to_bits (uniform keys), to_bits in
+ * {8, 4, 2, 1}.  On success k_bits = v_bits = to_bits. */
+kvq_status kvq_shrink(kvq_cache *cache, int32_t to_bits, hipStream_t stream);
+
+/* Workspace bytes kvq_decode_attn needs for this cache geometry (sized for
+ * max_tokens, so it stays valid as the cache grows).  0 on invalid input. */
+size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads);
+
+/* Decode attention of one query token per sequence over the n_tokens stored
+ * tokens (see "Decode attention" above).  q: device bfloat16
+ * [B][n_q_heads][128]; out: device float32 [B][n_q_heads][128]; n_q_heads a
+ * multiple of n_kv_heads with 1 <= n_q_heads / n_kv_heads <= 16; n_tokens >= 128.
+ * workspace: device buffer of at least kvq_decode_workspace_bytes() bytes; it
+ * must be zero-filled before its first use, and every call leaves it so.
+ * Concurrent calls must not share a workspace. */
+kvq_status kvq_decode_attn(const kvq_cache *cache, const void *q, int32_t n_q_heads,
+                           float softmax_scale, float *out, void *workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* ------------------------------------------------------------------------
+ * Progressive schedule ([PMKVQ] Overall framework and Key design 1: each
+ * block's cache starts at 16 bits; when its memory budget is full, the whole
+ * cache drops one width, 16 -> 8 -> 4 -> 2, down to the block's target).
+ *
+ * A kvq_pool is a host-side tile allocator over a caller-owned device code
+ * buffer of pool_bytes bytes that serves as both k_codes and v_codes; it
+ * writes the device offset tables k_tile_off_dev / v_tile_off_dev (each
+ * [max_tiles][B][Hkv] int64, caller-owned) and keeps a host copy.  After a
+ * shrink, the second half of every tile returns to the pool; new tiles are
+ * carved from freed halves first.  The cache must use these tables (its
+ * k_tile_off / v_tile_off pointers equal the two device pointers).
+ */
+typedef struct kvq_pool kvq_pool;
+
+kvq_status kvq_pool_create(const kvq_cache *cache, int64_t pool_bytes, int64_t *k_tile_off_dev,
+                           int64_t *v_tile_off_dev, kvq_pool **out);
+void kvq_pool_destroy(kvq_pool *pool);
+/* Bytes of the pool currently holding tiles, and its high-water mark. */
+int64_t kvq_pool_used_bytes(const kvq_pool *pool);
+int64_t kvq_pool_high_water(const kvq_pool *pool);
+
+/* Append n_new tokens (multiple of 128) to every stream of a uniform-width
+ * cache under a memory budget: while kvq_cache_bytes(n_tokens + n_new) at the
+ * current width exceeds budget_bytes, halve the width with kvq_shrink (never
+ * below floor_bits); then allocate the new tiles (from `pool`, or at the
+ * contiguous placement when pool is NULL) and kvq_quantize them at the
+ * resulting width.  If the group does not fit even at floor_bits, returns
+ * KVQ_EBUDGET before any work.  *n_shrinks (may be NULL) receives the number
+ * of halvings performed.  Input arguments as for kvq_quantize. */
+kvq_status kvq_append(kvq_cache *cache, kvq_pool *pool, int64_t budget_bytes, int32_t floor_bits,
+                      const void *k, const void *v, kvq_dtype in_dtype,
+                      const int64_t k_strides[3], const int64_t v_strides[3], int32_t n_new,
+                      hipStream_t stream, int32_t *n_shrinks);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,162 @@
+"""Seeded synthetic inputs shaped like the pages' workloads.
+
+This module holds no quantization, shrink or attention arithmetic: it only
+draws keys, values, queries and channel-class maps.  Both the HIP path and the
+CPU oracle consume exactly what it returns.
+
+Recipes (stand-ins for real model activations; no dataset or weights are used):
+  tiny     1 x 1 kv head x 1 query head, 512 tokens; K, V ~ N(0,1) with key
+           channels 3 and 77 scaled x10, then RoPE on K at positions 0..511.
+  layer    Qwen2.5-7B-shaped (B=16, Hkv=4, Hq=28, T=32768) and the other GQA
+           layers: K ~ N(0,1) pre-RoPE with 4 fixed outlier channels per kv head
+           scaled x8, RoPE at the true positions; V ~ N(0,1); q ~ N(0,1) bf16.
+  mixed    Llama-3.1-8B-shaped long context (B=1, Hkv=8, Hq=32, T=131072): per kv
+           head a seeded permutation picks 8 channels at 4 bits, 8 at 3 bits,
+           8 at 1 bit, the other 104 at 2 bits; K ~ N(0,1) with the 3/4-bit
+           channels x6 and the 1-bit channels x0.2, no RoPE; V ~ N(0,1).
+RoPE here is rotate-half over channel pairs (i, i+64), theta_i = 1e4^(-2i/128),
+angle = position * theta_i, evaluated in float64 and stored as float32.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+HEAD_DIM = 128
+ROPE_THETA = 10000.0
+
+
+def rope_inv_freq(head_dim: int = HEAD_DIM, theta: float = ROPE_THETA) -> np.ndarray:
+    i = np.arange(head_dim // 2, dtype=np.float64)
+    return theta ** (-2.0 * i / head_dim)
+
+
+def apply_rope(x: np.ndarray, pos0: int = 0) -> np.ndarray:
+    """x: [..., T, 128] float32 -> rotated float32 (rotate-half pairs)."""
+    T = x.shape[-2]
+    ang = np.arange(pos0, pos0 + T, dtype=np.float64)[:, None] * rope_inv_freq()[None, :]
+    c, s = np.cos(ang), np.sin(ang)
+    a = x[..., :64].astype(np.float64)
+    b = x[..., 64:].astype(np.float64)
+    out = np.empty(x.shape, dtype=np.float32)
+    out[..., :64] = a * c - b * s
+    out[..., 64:] = a * s + b * c
+    return out
+
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 raw bits, round to nearest even (input recipe only:
+    the query is drawn in float32 and handed to both sides as bfloat16)."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    r = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    return (np.asarray(b, dtype=np.uint32) << 16).view(np.float32)
+
+
+def tiny(seed: int = 0):
+    """-> dict(k [1,1,512,128] f32, v, q_bf16 [1,1,128] uint16)"""
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((512, HEAD_DIM), dtype=np.float32)
+    v = rng.standard_normal((512, HEAD_DIM), dtype=np.float32)
+    q = rng.standard_normal(HEAD_DIM, dtype=np.float32)
+    k[:, 3] *= 10.0
+    k[:, 77] *= 10.0
+    k = apply_rope(k, 0)
+    return dict(k=k[None, None], v=v[None, None], q_bf16=to_bf16_bits(q)[None, None])
+
+
+def layer(B: int, Hkv: int, Hq: int, T: int, seed: int, n_outliers: int = 4,
+          outlier_scale: float = 8.0, rope: bool = True, pos0: int = 0):
+    """GQA layer inputs.  -> dict(k, v [B,Hkv,T,128] f32, q_bf16 [B,Hq,128] uint16,
+    outliers [Hkv, n_outliers])"""
+    rng = np.random.default_rng(seed)
+    outl = np.stack([rng.choice(HEAD_DIM, n_outliers, replace=False) for _ in range(Hkv)])
+    k = rng.standard_normal((B, Hkv, T, HEAD_DIM), dtype=np.float32)
+    for h in range(Hkv):
+        k[:, h, :, outl[h]] *= np.float32(outlier_scale)
+    if rope:
+        for b in range(B):
+            for h in range(Hkv):
+                k[b, h] = apply_rope(k[b, h], pos0)
+    v = rng.standard_normal((B, Hkv, T, HEAD_DIM), dtype=np.float32)
+    q = rng.standard_normal((B, Hq, HEAD_DIM), dtype=np.float32)
+    return dict(k=k, v=v, q_bf16=to_bf16_bits(q), outliers=outl)
+
+
+def mixed_class_map(Hkv: int, seed: int):
+    """Per kv head: a seeded permutation assigns 8 channels to 4 bits, the next
+    8 to 3 bits, the next 8 to 1 bit and the rest to 2 bits.  Returns
+    slot_chan [Hkv,128] int16 in the mixed key layout's slot order (slots 0..7:
+    4-bit channels; slots 8,10,..,22: 3-bit channels; slots 9,11,..,23: 1-bit
+    channels; slots 24..127: 2-bit channels; ascending channel order inside
+    every class) and the class sets."""
+    rng = np.random.default_rng(seed)
+    slot_chan = np.empty((Hkv, HEAD_DIM), dtype=np.int16)
+    classes = []
+    for h in range(Hkv):
+        perm = rng.permutation(HEAD_DIM)
+        c4, c3, c1, c2 = (np.sort(perm[:8]), np.sort(perm[8:16]), np.sort(perm[16:24]),
+                          np.sort(perm[24:]))
+        slot_chan[h, 0:8] = c4
+        slot_chan[h, 8:24:2] = c3
+        slot_chan[h, 9:24:2] = c1
+        slot_chan[h, 24:] = c2
+        classes.append(dict(b4=c4, b3=c3, b1=c1, b2=c2))
+    return slot_chan, classes
+
+
+def mixed_layer(B: int, Hkv: int, Hq: int, T: int, seed: int):
+    """Channel-class key generator (no RoPE).  -> dict(k, v, q_bf16, slot_chan)"""
+    slot_chan, classes = mixed_class_map(Hkv, seed + 1)
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, Hkv, T, HEAD_DIM), dtype=np.float32)
+    for h in range(Hkv):
+        big = np.concatenate([classes[h]["b4"], classes[h]["b3"]])
+        k[:, h, :, big] *= np.float32(6.0)
+        k[:, h, :, classes[h]["b1"]] *= np.float32(0.2)
+    v = rng.standard_normal((B, Hkv, T, HEAD_DIM), dtype=np.float32)
+    q = rng.standard_normal((B, Hq, HEAD_DIM), dtype=np.float32)
+    return dict(k=k, v=v, q_bf16=to_bf16_bits(q), slot_chan=slot_chan)
+
+
+def layer_bits_table(n_layers: int = 64, seed: int = 0):
+    """Per-layer widths for the 64-layer step: layer 0 at 8 bits; layer l >= 1
+    at 4 bits with probability 0.75*l/(n_layers-1), else 2 bits (deeper layers
+    get more bits), so the expected mean is about 2.84 bits."""
+    rng = np.random.default_rng(seed)
+    u = rng.random(n_layers)
+    bits = [8]
+    for l in range(1, n_layers):
+        bits.append(4 if u[l] < 0.75 * l / (n_layers - 1) else 2)
+    return bits
+
+
+def layer_device(B: int, Hkv: int, Hq: int, T: int, seed: int, device, n_outliers: int = 4,
+                 outlier_scale: float = 8.0):
+    """Same recipe as layer() drawn with torch on a device (used where the
+    host draw is too slow, e.g. 64 layers of B=16, Hkv=8, T=32768).  The draw
+    differs from layer()'s numpy stream but follows the same distribution."""
+    import torch
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    outl = torch.stack([torch.randperm(HEAD_DIM, generator=g, device=device)[:n_outliers]
+                        for _ in range(Hkv)])
+    k = torch.randn((B, Hkv, T, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    scale = torch.ones((Hkv, HEAD_DIM), device=device, dtype=torch.float32)
+    for h in range(Hkv):
+        scale[h, outl[h]] = outlier_scale
+    k *= scale[None, :, None, :]
+    inv = torch.tensor(rope_inv_freq(), device=device, dtype=torch.float64)
+    pos = torch.arange(T, device=device, dtype=torch.float64)
+    ang = pos[:, None] * inv[None, :]
+    c, s = torch.cos(ang), torch.sin(ang)
+    for b in range(B):
+        a = k[b, :, :, :64].double()
+        bb = k[b, :, :, 64:].double()
+        k[b, :, :, :64] = (a * c - bb * s).float()
+        k[b, :, :, 64:] = (a * s + bb * c).float()
+    v = torch.randn((B, Hkv, T, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    q = torch.randn((B, Hq, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    return dict(k=k, v=v, q=q.to(torch.bfloat16))

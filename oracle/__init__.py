@@ -1,0 +1,313 @@
+"""CPU oracle for packed KV quantization, ERS shrink and decode attention.
+
+TEST INFRASTRUCTURE ONLY.  Only the tests, ``__graft_entry__.smoke()`` and the
+CPU-baseline leg of ``bench.py`` import this package.  The product library never
+loads it and shares no code with it; the two meet only through the seeded
+input generators and the layout text of the public header.
+
+The arithmetic lives in ``kvq_oracle.c`` (plain C, single-threaded, binary32
+quantizer with one rounding per operation, binary64 attention).  This module
+builds it with gcc, loads it with ctypes and offers numpy-level wrappers that
+work on one (batch, kv-head) stream at a time.
+
+Sources, cited by page title and section:
+  * "PM-KVQ: Progressive Mixed-Precision KV Cache Quantization for Long-CoT
+    LLMs" (papernotes.org summary) -- Key design 1 (ERS equation, progressive
+    16->8->4->2 schedule), Training strategy (asymmetric groups of 128).
+  * "Channel-Aware Mixed-Precision Quantization for Efficient Long-Context
+    Inference" (papernotes.org summary) -- Background (key channel-wise, value
+    token-wise), Key design 1 (S = (Cmax - Cmin)/(2^b - 1), Emax = S/2), Key
+    design 3 (4/3/2/1-bit classes in 8-bit-aligned blocks, fp8 parameters).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "kvq_oracle.c")
+_LIB_PATH = os.path.join(_HERE, "_kvq_oracle.so")
+
+F32, F16, BF16, E4M3 = 0, 1, 2, 3
+PARAM_NP = {F32: np.float32, F16: np.uint16, BF16: np.uint16, E4M3: np.uint8}
+PARAM_BYTES = {F32: 4, F16: 2, BF16: 2, E4M3: 1}
+MIXED_TILE_BYTES = 4352
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (no fast-math, no FMA contraction)."""
+    if force or not os.path.exists(_LIB_PATH):
+        tmp = _LIB_PATH + ".tmp%d" % os.getpid()
+        cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off",
+               "-fno-fast-math", "-o", tmp, _SRC, "-lm"]
+        subprocess.check_call(cmd)
+        os.replace(tmp, _LIB_PATH)
+    return _LIB_PATH
+
+
+def lib():
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_LIB_PATH) or os.path.getmtime(_LIB_PATH) < os.path.getmtime(_SRC):
+                build()
+            L = ctypes.CDLL(_LIB_PATH)
+            vp, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+            L.orc_f32_to_f16.restype = ctypes.c_uint16
+            L.orc_f32_to_f16.argtypes = [ctypes.c_float]
+            L.orc_f32_to_e4m3.restype = ctypes.c_uint8
+            L.orc_f32_to_e4m3.argtypes = [ctypes.c_float]
+            L.orc_ers.restype = ctypes.c_uint32
+            L.orc_ers.argtypes = [ctypes.c_uint32, i32]
+            L.orc_narrow_array.argtypes = [vp, i64, i32, vp]
+            L.orc_decode_array.argtypes = [vp, i64, i32, vp]
+            L.orc_ers_array.argtypes = [vp, i64, i32, vp]
+            L.orc_quantize_group.argtypes = [vp, i64, i32, i32, i32, vp, i64, vp, vp, i64]
+            L.orc_pack_rows.argtypes = [vp, i32, vp]
+            L.orc_unpack_rows.argtypes = [vp, i32, vp]
+            L.orc_pack_mixed.argtypes = [vp, vp]
+            L.orc_unpack_mixed.argtypes = [vp, vp]
+            L.orc_mixed_slot_bits.restype = i32
+            L.orc_mixed_slot_bits.argtypes = [i32]
+            L.orc_quantize_k.argtypes = [vp, i64, i32, i32, i32, vp, i64, vp, vp]
+            L.orc_quantize_k_mixed.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp, vp]
+            L.orc_quantize_v.argtypes = [vp, i64, i32, i32, i32, vp, i64, vp, vp]
+            L.orc_shrink_tile.argtypes = [vp, i32]
+            L.orc_shrink_scales.argtypes = [vp, i64, i32, i32]
+            L.orc_decode_attn.restype = i32
+            L.orc_decode_attn.argtypes = [vp, i64, vp, vp, i32, vp, vp, i64, vp, vp, i32,
+                                          i32, i32, vp, i32, ctypes.c_float, vp]
+            L.orc_block_bytes.restype = i64
+            L.orc_block_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
+            L.orc_schedule.restype = i32
+            L.orc_schedule.argtypes = [i32, i32, i64, i32, i32, i32, i64, vp, i32]
+            _lib = L
+    return _lib
+
+
+def _p(a: np.ndarray):
+    assert a.flags["C_CONTIGUOUS"] or a.ndim == 0
+    return ctypes.c_void_p(a.ctypes.data)
+
+
+# --------------------------------------------------------------------------
+# number formats
+# --------------------------------------------------------------------------
+def narrow(x: np.ndarray, pdt: int) -> np.ndarray:
+    """binary32 -> raw bits of the parameter dtype (RNE; e4m3 saturates)."""
+    x = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.empty(x.shape, dtype=PARAM_NP[pdt])
+    lib().orc_narrow_array(_p(x), x.size, pdt, _p(out))
+    return out
+
+
+def decode(raw: np.ndarray, pdt: int) -> np.ndarray:
+    """raw bits of a parameter dtype -> exact float64 values."""
+    raw = np.ascontiguousarray(raw, dtype=PARAM_NP[pdt])
+    out = np.empty(raw.shape, dtype=np.float64)
+    lib().orc_decode_array(_p(raw), raw.size, pdt, _p(out))
+    return out
+
+
+def bf16_bits(x: np.ndarray) -> np.ndarray:
+    """binary32 -> bfloat16 raw bits (RNE)."""
+    return narrow(x, BF16)
+
+
+def ers(x: np.ndarray, b: int) -> np.ndarray:
+    x = np.ascontiguousarray(x, dtype=np.uint32)
+    out = np.empty_like(x)
+    lib().orc_ers_array(_p(x), x.size, b, _p(out))
+    return out
+
+
+# --------------------------------------------------------------------------
+# quantizer, packing
+# --------------------------------------------------------------------------
+def quantize_group(x: np.ndarray, bits: int, pdt: int):
+    """One group -> (codes uint16, S raw, Z raw)."""
+    x = np.ascontiguousarray(x, dtype=np.float32).ravel()
+    codes = np.empty(x.size, dtype=np.uint16)
+    s = np.empty(1, dtype=PARAM_NP[pdt])
+    z = np.empty(1, dtype=PARAM_NP[pdt])
+    lib().orc_quantize_group(_p(x), 1, x.size, bits, pdt, _p(codes), 1, _p(s), _p(z), 0)
+    return codes, s[0], z[0]
+
+
+def pack_rows(codes: np.ndarray, bits: int) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint16).reshape(128, 128)
+    tile = np.zeros(16 * bits * 128, dtype=np.uint8)
+    lib().orc_pack_rows(_p(codes), bits, _p(tile))
+    return tile
+
+
+def unpack_rows(tile: np.ndarray, bits: int) -> np.ndarray:
+    tile = np.ascontiguousarray(tile, dtype=np.uint8)
+    assert tile.size >= 16 * bits * 128
+    codes = np.empty((128, 128), dtype=np.uint16)
+    lib().orc_unpack_rows(_p(tile), bits, _p(codes))
+    return codes
+
+
+def pack_mixed(codes: np.ndarray) -> np.ndarray:
+    codes = np.ascontiguousarray(codes, dtype=np.uint16).reshape(128, 128)
+    tile = np.zeros(MIXED_TILE_BYTES, dtype=np.uint8)
+    lib().orc_pack_mixed(_p(codes), _p(tile))
+    return tile
+
+
+def unpack_mixed(tile: np.ndarray) -> np.ndarray:
+    tile = np.ascontiguousarray(tile, dtype=np.uint8)
+    assert tile.size >= MIXED_TILE_BYTES
+    codes = np.empty((128, 128), dtype=np.uint16)
+    lib().orc_unpack_mixed(_p(tile), _p(codes))
+    return codes
+
+
+def mixed_slot_bits() -> np.ndarray:
+    return np.array([lib().orc_mixed_slot_bits(j) for j in range(128)], dtype=np.int32)
+
+
+def tile_bytes(bits: int) -> int:
+    """bytes of one packed tile; bits == 0 selects the mixed-bit key tile"""
+    return MIXED_TILE_BYTES if bits == 0 else 2048 * bits
+
+
+# --------------------------------------------------------------------------
+# one (batch, kv-head) stream
+# --------------------------------------------------------------------------
+class Stream:
+    """Packed cache of one (batch, kv-head) stream, as the oracle builds it.
+
+    k_tiles: [n_tiles, tile_bytes(k_bits)] uint8, ks/kz: [n_tiles, 128] raw
+    v_tiles: [n_tiles, 2048*v_bits] uint8, vs/vz: [n_tok] raw
+    """
+
+    def __init__(self, k_bits, v_bits, pdt, k_tiles, ks, kz, v_tiles, vs, vz, slot_chan=None):
+        self.k_bits, self.v_bits, self.pdt = k_bits, v_bits, pdt
+        self.k_tiles, self.ks, self.kz = k_tiles, ks, kz
+        self.v_tiles, self.vs, self.vz = v_tiles, vs, vz
+        self.slot_chan = slot_chan
+
+    @property
+    def n_tok(self):
+        return self.vs.shape[0]
+
+
+def quantize_stream(k: np.ndarray, v: np.ndarray, k_bits: int, v_bits: int, pdt: int,
+                    slot_chan: np.ndarray | None = None) -> Stream:
+    """k, v: [T, 128] float32 (T multiple of 128).  k_bits == 0 -> mixed keys."""
+    k = np.ascontiguousarray(k, dtype=np.float32)
+    v = np.ascontiguousarray(v, dtype=np.float32)
+    T = k.shape[0]
+    assert k.shape == (T, 128) and v.shape == (T, 128) and T % 128 == 0
+    nt = T // 128
+    L = lib()
+    kt = np.zeros((nt, tile_bytes(k_bits)), dtype=np.uint8)
+    ks = np.empty((nt, 128), dtype=PARAM_NP[pdt])
+    kz = np.empty((nt, 128), dtype=PARAM_NP[pdt])
+    if k_bits == 0:
+        sc = np.ascontiguousarray(slot_chan, dtype=np.int16)
+        assert sc.shape == (128,) and sorted(sc.tolist()) == list(range(128))
+        L.orc_quantize_k_mixed(_p(k), 128, T, pdt, _p(sc), _p(kt), kt.shape[1], _p(ks), _p(kz))
+    else:
+        sc = None
+        L.orc_quantize_k(_p(k), 128, T, k_bits, pdt, _p(kt), kt.shape[1], _p(ks), _p(kz))
+    vt = np.zeros((nt, tile_bytes(v_bits)), dtype=np.uint8)
+    vs = np.empty(T, dtype=PARAM_NP[pdt])
+    vz = np.empty(T, dtype=PARAM_NP[pdt])
+    L.orc_quantize_v(_p(v), 128, T, v_bits, pdt, _p(vt), vt.shape[1], _p(vs), _p(vz))
+    return Stream(k_bits, v_bits, pdt, kt, ks, kz, vt, vs, vz, sc)
+
+
+def shrink_stream(st: Stream, to_bits: int) -> Stream:
+    """ERS 2b -> b of every tile of a uniform-width stream (returns a new Stream)."""
+    assert st.k_bits == 2 * to_bits and st.v_bits == 2 * to_bits
+    L = lib()
+    out = []
+    for tiles in (st.k_tiles, st.v_tiles):
+        t2 = np.array(tiles, copy=True)
+        for i in range(t2.shape[0]):
+            row = np.ascontiguousarray(t2[i])
+            L.orc_shrink_tile(_p(row), to_bits)
+            t2[i] = row
+        out.append(np.ascontiguousarray(t2[:, : tile_bytes(to_bits)]))
+    ks = np.array(st.ks, copy=True)
+    vs = np.array(st.vs, copy=True)
+    L.orc_shrink_scales(_p(ks), ks.size, to_bits, st.pdt)
+    L.orc_shrink_scales(_p(vs), vs.size, to_bits, st.pdt)
+    return Stream(to_bits, to_bits, st.pdt, out[0], ks, st.kz.copy(), out[1], vs, st.vz.copy(),
+                  st.slot_chan)
+
+
+def dequant_k(st: Stream) -> np.ndarray:
+    """[T, 128] float64 keys (channel order) reconstructed from the stream."""
+    nt = st.k_tiles.shape[0]
+    S = decode(st.ks, st.pdt)
+    Z = decode(st.kz, st.pdt)
+    out = np.empty((nt * 128, 128), dtype=np.float64)
+    for g in range(nt):
+        if st.k_bits == 0:
+            codes = unpack_mixed(st.k_tiles[g]).astype(np.float64)  # [t][slot]
+            val = codes * S[g][None, :] + Z[g][None, :]
+            blk = np.empty_like(val)
+            blk[:, st.slot_chan.astype(np.int64)] = val
+        else:
+            codes = unpack_rows(st.k_tiles[g], st.k_bits).astype(np.float64)  # [t][c]
+            blk = codes * S[g][None, :] + Z[g][None, :]
+        out[g * 128:(g + 1) * 128] = blk
+    return out
+
+
+def dequant_v(st: Stream) -> np.ndarray:
+    nt = st.v_tiles.shape[0]
+    S = decode(st.vs, st.pdt)
+    Z = decode(st.vz, st.pdt)
+    out = np.empty((nt * 128, 128), dtype=np.float64)
+    for g in range(nt):
+        codes = unpack_rows(st.v_tiles[g], st.v_bits).astype(np.float64)  # [c][t]
+        out[g * 128:(g + 1) * 128] = codes.T * S[g * 128:(g + 1) * 128, None] + \
+            Z[g * 128:(g + 1) * 128, None]
+    return out
+
+
+def decode_attn(st: Stream, q_bf16: np.ndarray, scale: float) -> np.ndarray:
+    """q_bf16: [G, 128] uint16 raw bfloat16 -> [G, 128] float64."""
+    q = np.ascontiguousarray(q_bf16, dtype=np.uint16)
+    G = q.shape[0]
+    out = np.empty((G, 128), dtype=np.float64)
+    sc = st.slot_chan if st.slot_chan is not None else np.zeros(128, dtype=np.int16)
+    sc = np.ascontiguousarray(sc, dtype=np.int16)
+    kt = np.ascontiguousarray(st.k_tiles)
+    vt = np.ascontiguousarray(st.v_tiles)
+    rc = lib().orc_decode_attn(_p(kt), kt.shape[1], _p(np.ascontiguousarray(st.ks)),
+                               _p(np.ascontiguousarray(st.kz)), st.k_bits, _p(sc),
+                               _p(vt), vt.shape[1], _p(np.ascontiguousarray(st.vs)),
+                               _p(np.ascontiguousarray(st.vz)), st.v_bits, st.pdt, st.n_tok,
+                               _p(q), G, ctypes.c_float(scale), _p(out))
+    if rc != 0:
+        raise RuntimeError("orc_decode_attn failed: %d" % rc)
+    return out
+
+
+# --------------------------------------------------------------------------
+# schedule accounting
+# --------------------------------------------------------------------------
+def block_bytes(B, H, n_tok, k_bits, v_bits, pdt) -> int:
+    return int(lib().orc_block_bytes(B, H, n_tok, k_bits, v_bits, pdt))
+
+
+def schedule(B, H, n_total, start_bits, floor_bits, pdt, budget):
+    """-> list of (tokens stored before the append that triggered it, new width)"""
+    ev = np.zeros(64, dtype=np.int64)
+    n = lib().orc_schedule(B, H, n_total, start_bits, floor_bits, pdt, budget, _p(ev), 32)
+    if n < 0:
+        return None
+    return [(int(ev[2 * i]), int(ev[2 * i + 1])) for i in range(n)]
