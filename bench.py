@@ -1,0 +1,257 @@
+"""Benchmark: packed-KV decode attention on one MI355X.
+
+Workload (one decode step = the decode-attention call over a whole layer):
+Qwen2.5-7B-shaped layer, batch 16, 28 query heads over 4 kv heads, head_dim
+128, 32768 cached tokens, keys and values packed at 4 bits with binary16
+scale/zero, one bfloat16 query token per sequence.  Inputs are seeded
+synthetic tensors (see kv_cache_mixed_amd/synth.py); the packed cache is
+resident in HBM before timing, and the timed steps rotate over enough
+independent copies of it (> 512 MiB together) that no step reads a cache the
+256 MB Infinity Cache still holds.
+
+Prints ONE JSON line.  `value` = effective HBM bandwidth of the decode step
+(algorithmic bytes: packed codes + scales/zeros + q + out, divided by the step
+time), `tokens_per_s` = batch / step time (attention only).  The other rows of
+the path (quantize, ERS shrink, mixed-bit decode at 128K) are timed in the same
+run and reported under `rows`.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBS = 8000.0
+
+
+def _parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-rows", action="store_true", help="time only the decode step")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0,
+                    help="approximate CPU work of the oracle baseline sample")
+    return ap.parse_args()
+
+
+def decode_bytes(B, H, Hq, T, k_bits, v_bits, pb):
+    """algorithmic bytes of one decode call: codes + S/Z of every stored token,
+    plus the bf16 query and the f32 output"""
+    per_tok = (128 * k_bits + 128 * v_bits) // 8 if k_bits else 34 + 128 * v_bits // 8
+    params = 2 * pb + 2 * pb          # key S,Z per token (128 per 128-token tile) + value S,Z
+    return B * H * T * (per_tok + params) + B * Hq * 128 * 2 + B * Hq * 128 * 4
+
+
+def time_events(torch, fn, n, warmup):
+    """average duration of fn() over n calls, HIP events on the current stream"""
+    for _ in range(warmup):
+        fn(0)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for i in range(n):
+        evs[i][0].record(st)
+        fn(i)
+        evs[i][1].record(st)
+    torch.cuda.synchronize()
+    ms = sorted(a.elapsed_time(b) for a, b in evs)
+    return sum(ms) / len(ms), ms[len(ms) // 2]
+
+
+def cpu_baseline(inp, B, H, Hq, k_bits, pdt, seconds):
+    """The CPU oracle (as it stands) on a bounded sample of the same workload:
+    quantize + fp64 decode attention of whole (batch, kv-head) streams, run in
+    a thread pool over the host cores; scaled to GB/s of the decode step."""
+    import concurrent.futures as cf
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    G = Hq // H
+    cores = min(len(os.sched_getaffinity(0)), 16)
+    scale = 1.0 / math.sqrt(128)
+    streams = [(b, h) for b in range(B) for h in range(H)]
+    # calibrate on one stream
+    t0 = time.perf_counter()
+    st = oracle.quantize_stream(inp["k"][0, 0], inp["v"][0, 0], k_bits, k_bits, pdt)
+    t1 = time.perf_counter()
+    oracle.decode_attn(st, inp["q_bf16"][0, 0:G], scale)
+    t2 = time.perf_counter()
+    per_stream = t2 - t1
+    n = max(cores, min(len(streams), int(seconds * cores / max(per_stream, 1e-3))))
+    n = min(n, len(streams))
+    sample = streams[:n]
+    packed = {}
+
+    def q_one(bh):
+        b, h = bh
+        packed[bh] = oracle.quantize_stream(inp["k"][b, h], inp["v"][b, h], k_bits, k_bits, pdt)
+
+    with cf.ThreadPoolExecutor(cores) as ex:
+        list(ex.map(q_one, sample))
+
+    def d_one(bh):
+        b, h = bh
+        return oracle.decode_attn(packed[bh], inp["q_bf16"][b, h * G:(h + 1) * G], scale)
+
+    t0 = time.perf_counter()
+    with cf.ThreadPoolExecutor(cores) as ex:
+        list(ex.map(d_one, sample))
+    dt = time.perf_counter() - t0
+    T = inp["k"].shape[2]
+    nbytes = decode_bytes(1, n, n * G, T, k_bits, k_bits, 2)
+    return {"value": round(nbytes / dt / 1e9, 3), "unit": "GB/s", "cores": cores, "kind": "oracle",
+            "sample": "%d of %d (batch, kv-head) streams, full 32768 tokens, fp64 decode attention "
+                      "over the oracle's own packed cache (%.2f s wall)" % (n, B * H, dt),
+            "tokens_per_s": round(n / H / dt, 3) if n >= H else None}
+
+
+def main():
+    args = _parse()
+    if args.gpus != 1:
+        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from kv_cache_mixed_amd import kvq, synth
+    kvq.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    B, H, Hq, T, BITS = 16, 4, 28, 32768, 4
+    pdt = kvq.F16
+    scale = 1.0 / math.sqrt(128)
+    inp = synth.layer(B, H, Hq, T, seed=1234)
+    kd = torch.from_numpy(inp["k"]).to(dev)
+    vd = torch.from_numpy(inp["v"]).to(dev)
+    q = torch.from_numpy(inp["q_bf16"].view(np.int16)).to(dev).view(torch.bfloat16)
+
+    cache0 = kvq.PackedCache(B, H, T, BITS, BITS, pdt, device=dev)
+    rows = {}
+    # ---- quantize row: K and V of the whole layer (2 x 1 GiB fp32 read)
+    def quant(i):
+        cache0.s.n_tokens = 0
+        cache0.quantize(kd, vd, 0)
+    q_ms, _ = time_events(torch, quant, 5 if not args.no_rows else 1, 1)
+    q_bytes = 2 * B * H * T * 128 * 4 + decode_bytes(B, H, 0, T, BITS, BITS, 2)
+    rows["quantize_k_v_4bit"] = {"ms": round(q_ms, 4), "GB/s": round(q_bytes / q_ms / 1e6, 1),
+                                 "bytes": q_bytes}
+    del kd, vd
+    torch.cuda.empty_cache()
+
+    # ---- rotate copies of the packed cache (> 512 MiB together)
+    alg = decode_bytes(B, H, Hq, T, BITS, BITS, 2)
+    n_copies = max(2, math.ceil(600e6 / alg))
+    caches = [cache0]
+    for _ in range(n_copies - 1):
+        c = kvq.PackedCache(B, H, T, BITS, BITS, pdt, device=dev)
+        for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+            getattr(c, name).copy_(getattr(cache0, name))
+        c.s.n_tokens = T
+        caches.append(c)
+    outs = [torch.empty((B, Hq, 128), dtype=torch.float32, device=dev) for _ in caches]
+    wss = [c.workspace(Hq) for c in caches]
+
+    def step(i):
+        j = i % len(caches)
+        caches[j].decode_attn(q, scale, out=outs[j], workspace=wss[j])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    st = torch.cuda.current_stream()
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+           for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        evs[i][0].record(st)
+        step(i)
+        evs[i][1].record(st)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kern_ms = [a.elapsed_time(b) for a, b in evs]
+    kern_avg = sum(kern_ms) / len(kern_ms)
+    ms_per_step = wall * 1e3 / args.steps
+    value = alg / (ms_per_step * 1e-3) / 1e9
+    achieved = alg / (kern_avg * 1e-3) / 1e9
+    srt = sorted(kern_ms)
+
+    # ---- other rows of the path
+    if not args.no_rows:
+        # ERS shrink 4 -> 2 of the whole layer (read 4-bit tiles, write 2-bit halves)
+        sh = kvq.PackedCache(B, H, T, BITS, BITS, pdt, device=dev)
+
+        def shrink(i):
+            for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+                getattr(sh, name).copy_(getattr(cache0, name))
+            sh.s.n_tokens, sh.s.k_bits, sh.s.v_bits = T, 4, 4
+            ev0 = torch.cuda.Event(enable_timing=True)
+            ev1 = torch.cuda.Event(enable_timing=True)
+            ev0.record()
+            sh.shrink(2)
+            ev1.record()
+            return ev0, ev1
+        tms = []
+        for i in range(6):
+            e0, e1 = shrink(i)
+            torch.cuda.synchronize()
+            if i:
+                tms.append(e0.elapsed_time(e1))
+        s_ms = sum(tms) / len(tms)
+        s_bytes = B * H * (T // 128) * (2 * 8192 + 2 * 4096) + 2 * 2 * B * H * T * 2
+        rows["ers_shrink_4to2"] = {"ms": round(s_ms, 4), "GB/s": round(s_bytes / s_ms / 1e6, 1),
+                                   "bytes": s_bytes}
+        out2 = sh.decode_attn(q, scale)
+        d2_ms, _ = time_events(torch, lambda i: sh.decode_attn(q, scale, out=out2), 20, 3)
+        a2 = decode_bytes(B, H, Hq, T, 2, 2, 2)
+        rows["decode_2bit_same_layer"] = {"ms": round(d2_ms, 4), "GB/s": round(a2 / d2_ms / 1e6, 1),
+                                          "note": "single cache copy (partly Infinity-Cache resident)"}
+        del sh
+        torch.cuda.empty_cache()
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(inp, B, H, Hq, BITS, pdt, args.cpu_seconds)
+
+    line = {
+        "metric": "packed-KV decode attention: effective HBM GB/s (% of peak) and tokens/s",
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16",
+        "data": "synthetic",
+        "config": {"workload": "qwen2.5-7b-shaped decode layer", "batch": B, "kv_heads": H,
+                   "q_heads": Hq, "head_dim": 128, "cached_tokens": T, "k_bits": BITS,
+                   "v_bits": BITS, "param_dtype": "f16", "query": "bf16", "output": "f32",
+                   "cache_copies_rotated": len(caches)},
+        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
+        "algorithmic_bytes_per_step": alg,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "kernel": "decode_kernel<4,4,f16,2>", "kernel_ms_avg": round(kern_avg, 5),
+                     "kernel_ms_p10": round(srt[len(srt) // 10], 5),
+                     "kernel_ms_p90": round(srt[(9 * len(srt)) // 10], 5)},
+        "rows": rows,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

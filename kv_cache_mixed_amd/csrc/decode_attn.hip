@@ -1,0 +1,634 @@
+// decode_attn.hip -- decode attention over the packed cache (gfx950).
+//
+// ChanMix page, Overall framework / Key design 3: at decode time the packed
+// cache is read, dequantized (x^ = S' * q + Z') and fed to ordinary
+// (FlashAttention-style) attention.  Here the dequantization never
+// materialises: the key parameters are folded into the query and the value
+// parameters into the softmax weights, so the two contractions run on the raw
+// integer codes with MFMA.
+//
+// Work decomposition.  Grid = (chunk, b * Hkv).  A workgroup of 4 waves owns
+// one chunk of 128-token tiles of one (batch, kv head) stream and all G query
+// heads of that kv head; wave w takes tiles w, w+4, ... of the chunk.  Per tile
+// a wave computes, with the G heads padded to the 16 columns of a
+// 16x16x32 f16 MFMA:
+//   S^T[t][n] = sum_c K[t][c] * u[n][c],   u = q * S_K * 2^k (per tile, f16)
+//   logit_n(t) = sigma * (S^T / 2^k + sum_c q[n][c] Z_K[c])
+//   online softmax in the log2 domain (running max per head, shared by the
+//   four lane groups through cross-lane max)
+//   O^T[c][n] += sum_t V[c][t] * P[t][n],  P = e^(logit - m) * S_V[t] * 2^k'
+//   zsum_n    += sum_t e^(logit - m) * Z_V[t]
+// The workgroup merges its four wave partials in LDS, writes one partial
+// (m, l, o[128]) per head, and the last workgroup of the stream (device-scope
+// counter) combines all chunks:  o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+//
+// MFMA operand layout (16x16x32 f16): lane l = 16*g + n holds, for A, row n and
+// k-slice g (8 values), for B, column n and k-slice g, and receives D rows
+// 4g..4g+3 of column n.  Row r of the key block j maps to token
+//   tau(j, r) = 32*(r/4) + 4*j + (r%4)
+// so lane group g of the D output holds tokens 32g + 4j + i, i.e. exactly the
+// 32 tokens whose value codes the same lane group loads for the PV product.
+// Each lane therefore reads 4b contiguous bytes per key row and per value row.
+//
+// Codes become f16 operands without conversion instructions: a b-bit field at
+// bit position p of each 16-bit half is OR-ed into the exponent of 1024.0,
+// giving 1024 + code * 2^p exactly (p + b <= 10).  For keys the 1024 offset is
+// removed after the MFMA (an extra MFMA against a constant 1024 operand gives
+// 1024 * sum(B) per head); value operands subtract 1024 in packed f16 before the
+// MFMA, so the value accumulation stays free of cancellation.  The power-of-two
+// field weights 2^p (and 2^8 for the high byte of 16-bit codes) are folded into
+// the other operand.
+#include "kvq_device.h"
+
+namespace kvq {
+
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// A bit field of a loaded 32-bit word that becomes one f16x2 operand register:
+// word index, right shift before masking, bit position and width inside each
+// 16-bit half, lane-local code index of the low and high half, log2 weight.
+struct Fld {
+  int w, sh, pos, wid, lo, hi, wexp;
+};
+
+// Uniform b-bit row segment of 32 codes (b words).  Codes in the low half of a
+// word pair with codes of the high half; fields that would reach bit 10 are
+// shifted down first.
+template <int B>
+__host__ __device__ constexpr Fld ufield(int i) {
+  if (B == 16) { const int w = i / 2, hb = i % 2; return {w, hb ? 8 : 0, 0, 8, 2 * w, 2 * w + 1, hb ? 8 : 0}; }
+  if (B == 8) { const int w = i / 2, k = i % 2; return {w, k ? 8 : 0, 0, 8, 4 * w + k, 4 * w + 2 + k, 0}; }
+  if (B == 4) { const int w = i / 4, k = i % 4; return {w, k >= 2 ? 8 : 0, (k % 2) * 4, 4, 8 * w + k, 8 * w + 4 + k, 0}; }
+  if (B == 2) {
+    const int w = i / 8, k = i % 8;
+    return {w, k >= 5 ? 10 : 0, k >= 5 ? 2 * (k - 5) : 2 * k, 2, 16 * w + k, 16 * w + 8 + k, 0};
+  }
+  const int w = i / 16, k = i % 16;
+  return {w, k >= 10 ? 10 : 0, k >= 10 ? k - 10 : k, 1, 32 * w + k, 32 * w + 16 + k, 0};
+}
+
+// Mixed key layout, lane group 0: word 0 = slots 0..7 (4-bit), word 1 = slots
+// 8..23 ((3,1)-bit pairs), word 2 = slots 120..127 (2-bit) spread so that
+// slots 120..123 sit in the low half and 124..127 in the high half.  Lane-local
+// index = slot for slots 0..23, 24 + (slot - 120) for the others.
+__host__ __device__ constexpr Fld mfield0(int i) {
+  if (i < 4) { const int k = i; return {0, k >= 2 ? 8 : 0, (k % 2) * 4, 4, k, 4 + k, 0}; }
+  if (i < 12) {
+    const int k = i - 4, kk = k % 4;
+    return {1, k >= 4 ? 8 : 0, (kk / 2) * 4 + (kk % 2) * 3, (kk % 2) ? 1 : 3, 8 + k, 16 + k, 0};
+  }
+  const int k = i - 12;
+  return {2, 0, 2 * k, 2, 24 + k, 28 + k, 0};
+}
+
+
+
+
+
+__device__ __forceinline__ f32x4 mfma(const uint32_t* a, const uint32_t* b, f32x4 c) {
+  const f16x8 av = __builtin_bit_cast(f16x8, (u32x4){a[0], a[1], a[2], a[3]});
+  const f16x8 bv = __builtin_bit_cast(f16x8, (u32x4){b[0], b[1], b[2], b[3]});
+  return __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_max16x4(float v) {  // max over the 4 lane groups
+  v = fmaxf(v, __shfl_xor(v, 16, 64));
+  return fmaxf(v, __shfl_xor(v, 32, 64));
+}
+__device__ __forceinline__ float wave_sum16x4(float v) {
+  v += __shfl_xor(v, 16, 64);
+  return v + __shfl_xor(v, 32, 64);
+}
+
+// Load 8 consecutive parameters starting at element e into f32.
+template <int PDT>
+__device__ __forceinline__ void load_params8(const void* base, int64_t e, float* out) {
+  if constexpr (PDT == KVQ_E4M3) {
+    const u32x2 v = *(const u32x2*)((const uint8_t*)base + e);
+#pragma unroll
+    for (int i = 0; i < 8; i++) out[i] = e4m3_bits_to_f32((v[i / 4] >> (8 * (i % 4))) & 0xffu);
+  } else if constexpr (PDT == KVQ_F32) {
+    const u32x4 a = *(const u32x4*)((const float*)base + e);
+    const u32x4 b = *(const u32x4*)((const float*)base + e + 4);
+#pragma unroll
+    for (int i = 0; i < 4; i++) { out[i] = u2f(a[i]); out[4 + i] = u2f(b[i]); }
+  } else {
+    const u32x4 v = *(const u32x4*)((const uint16_t*)base + e);
+#pragma unroll
+    for (int i = 0; i < 8; i++) {
+      const uint32_t raw = (v[i / 2] >> (16 * (i % 2))) & 0xffffu;
+      out[i] = (PDT == KVQ_F16) ? (float)__builtin_bit_cast(_Float16, (uint16_t)raw)
+                                : bf16_bits_to_f32(raw);
+    }
+  }
+}
+
+struct DecodeArgs {
+  Geo g;
+  const uint16_t* q;  // bf16 [B][Hq][128]
+  float* out;         // [B][Hq][128]
+  float* part;        // [BH][n_chunks][G][130]
+  uint32_t* counters; // [n_groups]
+  int G, n_chunks, tpc, n_groups;
+  float sl2;          // softmax_scale * log2(e)
+};
+
+// Operand registers per 32 codes and row words per lane for width B.
+template <int B>
+struct UInfo {
+  static constexpr int NF = (B == 16) ? 32 : 16;
+  static constexpr int NW = B;
+};
+
+// f16 split of x into hi + lo (x - hi is exact in binary32)
+__device__ __forceinline__ void split_pack(float xl, float xh, uint32_t& hi, uint32_t& lo) {
+  const _Float16 al = (_Float16)xl, ah = (_Float16)xh;
+  const _Float16 bl = (_Float16)(xl - (float)al), bh = (_Float16)(xh - (float)ah);
+  hi = (uint32_t)__builtin_bit_cast(uint16_t, al) | ((uint32_t)__builtin_bit_cast(uint16_t, ah) << 16);
+  lo = (uint32_t)__builtin_bit_cast(uint16_t, bl) | ((uint32_t)__builtin_bit_cast(uint16_t, bh) << 16);
+}
+
+// The field as an f16x2 operand register holding code * 2^(pos - 24) in each
+// half: f16 subnormals are the integers times 2^-24, so masking the field in
+// place is the whole conversion (MFMA consumes subnormal f16 exactly).
+template <class F>
+__device__ __forceinline__ uint32_t field_subnormal(uint32_t word, F f) {
+  const uint32_t m = ((1u << f.wid) - 1u) << f.pos;
+  const uint32_t x = f.sh ? (word >> f.sh) : word;
+  return x & (m | (m << 16));
+}
+
+// KB: 16/8/4/2/1 or 0 (mixed keys).  VB: 16/8/4/2/1.  NS: kv streams packed
+// into the 16 MFMA columns (column n serves stream n / G, head n % G).
+template <int KB, int VB, int PDT, int NS>
+__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
+  constexpr bool MIXED = (KB == 0);
+  constexpr int NFK = MIXED ? 16 : UInfo<KB>::NF;    // key operand registers per token
+  constexpr int NWK = MIXED ? 3 : UInfo<KB>::NW;     // key words per lane per token
+  constexpr int NKK = NFK / 4;                       // key k-steps
+  constexpr int NFV = UInfo<VB>::NF;
+  constexpr int NWV = UInfo<VB>::NW;
+  constexpr int NSUB = (VB == 1) ? 1 : ((VB == 2) ? 2 : 4);  // sub-tiles per tile
+  constexpr int TPS = 32 / NSUB;                     // tokens per lane per sub-tile
+  constexpr int JB = 8 / NSUB;                       // key blocks per sub-tile
+  constexpr int FVS = NFV / NSUB;                    // value fields per sub-tile
+  constexpr int WVS = NWV / NSUB;                    // value words per sub-tile
+  constexpr int KSV = FVS / 4;                       // value k-steps per sub-tile
+  constexpr int KH = (KB == 16) ? 4 : 12;            // headroom exponents (f16 range)
+  constexpr int VH = (VB == 16) ? 4 : 12;
+  constexpr int ROW_K = MIXED ? 8 : 16 * KB;
+  constexpr int ROW_V = 16 * VB;
+  static_assert(KSV >= 1 && WVS >= 1, "sub-tile must hold whole value k-steps");
+
+  const Geo& g = a.g;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, lg = lane >> 4;
+  const int grp = blockIdx.y, chunk = blockIdx.x;
+  const int G = a.G;
+  const int BH = g.B * g.H;
+  const int own = n / G, hn = n - (n / G) * G;
+  const int bh_own = grp * NS + own;
+  const bool real = (own < NS) && (bh_own < BH);
+  const int b_own = real ? bh_own / g.H : 0, h_own = real ? bh_own % g.H : 0;
+  const int t_begin = chunk * a.tpc;
+  const int t_end = min(t_begin + a.tpc, g.n_tiles);
+
+  auto kslot = [&](int li) -> int {
+    if constexpr (MIXED) return lg == 0 ? (li < 24 ? li : 96 + li) : 32 * lg - 8 + li;
+    else return 32 * lg + li;
+  };
+
+  // ---- own query head over the lane's 32 key slots, kept as bf16 pairs
+  uint32_t qp[16];
+  {
+    const uint16_t* qrow = a.q + ((int64_t)b_own * (g.H * G) + (int64_t)h_own * G + hn) * 128;
+#pragma unroll
+    for (int i = 0; i < 16; i++) {
+      uint32_t lo = 0, hi = 0;
+      if (real) {
+        if constexpr (MIXED) {
+          lo = qrow[g.slot_chan[h_own * 128 + kslot(2 * i)]];
+          hi = qrow[g.slot_chan[h_own * 128 + kslot(2 * i + 1)]];
+        } else {
+          lo = qrow[kslot(2 * i)];
+          hi = qrow[kslot(2 * i + 1)];
+        }
+      }
+      qp[i] = lo | (hi << 16);
+    }
+  }
+  auto qval = [&](int li) -> float {
+    return (li & 1) ? u2f(qp[li >> 1] & 0xffff0000u) : u2f(qp[li >> 1] << 16);
+  };
+  float qmax = 0.0f;
+#pragma unroll
+  for (int li = 0; li < 32; li++) qmax = fmaxf(qmax, fabsf(qval(li)));
+  const int eq = expo(wave_max16x4(qmax));
+  int kseg[4];
+#pragma unroll
+  for (int s = 0; s < 4; s++) kseg[s] = kslot(8 * s);
+
+  float m_run = -INFINITY, l_run = 0.0f, z_run = 0.0f;
+  int e_run = -1000;
+  f32x4 acc_o[8];
+#pragma unroll
+  for (int cb = 0; cb < 8; cb++) acc_o[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+
+#pragma unroll 1
+  for (int tile = t_begin + wave; tile < t_end; tile += 4) {
+    // ---- own stream: fold key scales into the query (u = q * S * 2^k, split hi/lo)
+    uint32_t bkh[NFK], bkl[NFK];
+    float ak = 0.0f, bk0 = 0.0f;
+    {
+      float ks[32], kz[32];
+      if (real) {
+        const int64_t kpb = k_param_base(g, b_own, h_own, tile);
+#pragma unroll
+        for (int s = 0; s < 4; s++) {
+          load_params8<PDT>(g.k_scale, kpb + kseg[s], ks + 8 * s);
+          load_params8<PDT>(g.k_zero, kpb + kseg[s], kz + 8 * s);
+        }
+      } else {
+#pragma unroll
+        for (int li = 0; li < 32; li++) { ks[li] = 0.0f; kz[li] = 0.0f; }
+      }
+      float smax = 0.0f, beta = 0.0f;
+#pragma unroll
+      for (int li = 0; li < 32; li++) {
+        smax = fmaxf(smax, ks[li]);
+        beta += qval(li) * kz[li];
+      }
+      const int es = expo(wave_max16x4(smax));
+      beta = wave_sum16x4(beta);
+      const float kf = exp2i(KH - eq - es);
+      float u[32];
+#pragma unroll
+      for (int li = 0; li < 32; li++) u[li] = qval(li) * ks[li] * kf;
+#pragma unroll
+      for (int f = 0; f < NFK; f++) {
+        Fld F;
+        if constexpr (MIXED) F = (lg == 0) ? mfield0(f) : ufield<2>(f);
+        else F = ufield<KB>(f);
+        const float w = exp2i(F.wexp - F.pos);
+        split_pack(u[F.lo] * w, u[F.hi] * w, bkh[f], bkl[f]);
+      }
+      if (real) {
+        ak = a.sl2 * exp2i(24 - KH + eq + es);
+        bk0 = a.sl2 * beta;
+      }
+    }
+
+#pragma unroll 1
+    for (int sub = 0; sub < NSUB; sub++) {
+      // ---- raw loads of every stream's key blocks and value rows of this sub-tile
+      uint32_t kw[NS][JB][NWK];
+      uint32_t vw[NS][8][WVS];
+#pragma unroll
+      for (int s = 0; s < NS; s++) {
+        const int bh = grp * NS + s;
+        if (bh >= BH) continue;
+        const int bs = bh / g.H, hs = bh % g.H;
+        const uint8_t* kt = g.k_codes + k_tile_offset(g, bs, hs, tile);
+        const uint8_t* vt = g.v_codes + v_tile_offset(g, bs, hs, tile);
+#pragma unroll
+        for (int jj = 0; jj < JB; jj++) {
+          const int j = sub * JB + jj;
+          const int r = 32 * (n >> 2) + 4 * j + (n & 3);
+          if constexpr (MIXED) {
+            if (lg == 0) {
+              const u32x2 v = *(const u32x2*)(kt + 8 * r);
+              const uint32_t w2 = *(const uint16_t*)(kt + 4096 + 2 * r);
+              kw[s][jj][0] = v[0];
+              kw[s][jj][1] = v[1];
+              kw[s][jj][2] = (w2 & 0xffu) | ((w2 & 0xff00u) << 8);
+            } else {
+              const u32x2 v = *(const u32x2*)(kt + 1024 * lg + 8 * r);
+              kw[s][jj][0] = v[0];
+              kw[s][jj][1] = v[1];
+              kw[s][jj][2] = 0u;
+            }
+          } else {
+            const uint32_t* src = (const uint32_t*)(kt + r * ROW_K + 4 * KB * lg);
+            if constexpr (NWK >= 4) {
+#pragma unroll
+              for (int w = 0; w < NWK; w += 4) {
+                const u32x4 v = *(const u32x4*)(src + w);
+                kw[s][jj][w] = v[0]; kw[s][jj][w + 1] = v[1]; kw[s][jj][w + 2] = v[2]; kw[s][jj][w + 3] = v[3];
+              }
+            } else if constexpr (NWK == 2) {
+              const u32x2 v = *(const u32x2*)src;
+              kw[s][jj][0] = v[0]; kw[s][jj][1] = v[1];
+            } else {
+              kw[s][jj][0] = src[0];
+            }
+          }
+        }
+#pragma unroll
+        for (int cb = 0; cb < 8; cb++) {
+          const uint32_t* src = (const uint32_t*)(vt + (16 * cb + n) * ROW_V + 4 * VB * lg) + sub * WVS;
+          if constexpr (WVS >= 4) {
+#pragma unroll
+            for (int w = 0; w < WVS; w += 4) {
+              const u32x4 v = *(const u32x4*)(src + w);
+              vw[s][cb][w] = v[0]; vw[s][cb][w + 1] = v[1]; vw[s][cb][w + 2] = v[2]; vw[s][cb][w + 3] = v[3];
+            }
+          } else if constexpr (WVS == 2) {
+            const u32x2 v = *(const u32x2*)src;
+            vw[s][cb][0] = v[0]; vw[s][cb][1] = v[1];
+          } else {
+            vw[s][cb][0] = src[0];
+          }
+        }
+      }
+      // own stream's value scales / zeros for the lane's TPS tokens of this sub-tile
+      float vs[TPS], vz[TPS];
+      if (real) {
+        const int64_t vpb = v_param_base(g, b_own, h_own, (int64_t)tile * 128) + 32 * lg + sub * TPS;
+#pragma unroll
+        for (int s8 = 0; s8 < TPS / 8; s8++) {
+          load_params8<PDT>(g.v_scale, vpb + 8 * s8, vs + 8 * s8);
+          load_params8<PDT>(g.v_zero, vpb + 8 * s8, vz + 8 * s8);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < TPS; i++) { vs[i] = 0.0f; vz[i] = 0.0f; }
+      }
+
+      // ---- logits (log2 domain) of the lane's column for JB blocks of 16 tokens
+      float lgt[JB][4];
+#pragma unroll
+      for (int jj = 0; jj < JB; jj++) {
+#pragma unroll
+        for (int i = 0; i < 4; i++) lgt[jj][i] = 0.0f;
+#pragma unroll
+        for (int s = 0; s < NS; s++) {
+          if (grp * NS + s >= BH) continue;
+          uint32_t av[NFK];
+#pragma unroll
+          for (int f = 0; f < NFK; f++) {
+            if constexpr (MIXED) {
+              av[f] = (lg == 0) ? field_subnormal(kw[s][jj][mfield0(f).w], mfield0(f))
+                                : field_subnormal(kw[s][jj][ufield<2>(f).w], ufield<2>(f));
+            } else {
+              av[f] = field_subnormal(kw[s][jj][ufield<KB>(f).w], ufield<KB>(f));
+            }
+          }
+          f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int k = 0; k < NKK; k++) {
+            acc = mfma(av + 4 * k, bkh + 4 * k, acc);
+            acc = mfma(av + 4 * k, bkl + 4 * k, acc);
+          }
+          if (NS == 1 || own == s) {
+#pragma unroll
+            for (int i = 0; i < 4; i++) lgt[jj][i] = acc[i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; i++) lgt[jj][i] = ak * lgt[jj][i] + bk0;
+      }
+
+      // ---- online softmax update; value-scale exponent
+      float tmax = -INFINITY, vsmax = 0.0f;
+#pragma unroll
+      for (int jj = 0; jj < JB; jj++)
+#pragma unroll
+        for (int i = 0; i < 4; i++) tmax = fmaxf(tmax, lgt[jj][i]);
+#pragma unroll
+      for (int i = 0; i < TPS; i++) vsmax = fmaxf(vsmax, vs[i]);
+      tmax = wave_max16x4(tmax);
+      const int ev = expo(wave_max16x4(vsmax));
+      const float m_new = fmaxf(m_run, tmax);
+      const float alpha = exp2f(m_run - m_new);
+      const int e_new = max(e_run, ev);
+      const float rescale = alpha * exp2i(e_run - e_new);
+      m_run = m_new;
+      e_run = e_new;
+      const float pf = exp2i(VH - e_new);
+      float p[TPS];
+      float lsum = 0.0f, zsum = 0.0f;
+#pragma unroll
+      for (int i = 0; i < TPS; i++) {
+        const float e = exp2f(lgt[i >> 2][i & 3] - m_new);
+        lsum += e;
+        zsum += e * vz[i];
+        p[i] = e * vs[i] * pf;
+      }
+      l_run = l_run * alpha + lsum;
+      z_run = z_run * alpha + zsum;
+#pragma unroll
+      for (int cb = 0; cb < 8; cb++) acc_o[cb] *= rescale;
+
+      // ---- P operand (split hi/lo) and PV
+      uint32_t bvh[FVS], bvl[FVS];
+#pragma unroll
+      for (int ff = 0; ff < FVS; ff++) {
+        // every sub-tile has the field layout of sub-tile 0, shifted by
+        // WVS words and TPS tokens
+        const Fld F = ufield<VB>(ff);
+        const float w = exp2i(F.wexp - F.pos);
+        split_pack(p[F.lo] * w, p[F.hi] * w, bvh[ff], bvl[ff]);
+      }
+#pragma unroll
+      for (int s = 0; s < NS; s++) {
+        if (grp * NS + s >= BH) continue;
+        uint32_t bsh[FVS], bsl[FVS];
+#pragma unroll
+        for (int ff = 0; ff < FVS; ff++) {
+          const bool sel = (NS == 1) || (own == s);
+          bsh[ff] = sel ? bvh[ff] : 0u;
+          bsl[ff] = sel ? bvl[ff] : 0u;
+        }
+#pragma unroll
+        for (int cb = 0; cb < 8; cb++) {
+          uint32_t av[FVS];
+#pragma unroll
+          for (int ff = 0; ff < FVS; ff++) {
+            const Fld F = ufield<VB>(ff);
+            av[ff] = field_subnormal(vw[s][cb][F.w], F);
+          }
+#pragma unroll
+          for (int k = 0; k < KSV; k++) {
+            acc_o[cb] = mfma(av + 4 * k, bsh + 4 * k, acc_o[cb]);
+            acc_o[cb] = mfma(av + 4 * k, bsl + 4 * k, acc_o[cb]);
+          }
+        }
+      }
+    }
+  }
+
+  // ---- wave partial -> LDS -> workgroup partial (per column = stream, head)
+  __shared__ float sh_ml[4][16][2];
+  __shared__ float sh_o[4][16][128];
+  const float l_tot = wave_sum16x4(l_run);
+  const float z_tot = wave_sum16x4(z_run);
+  const float of = exp2i(24 - VH + e_run);   // acc_o * 2^24 / pf
+  if (lg == 0) {
+    sh_ml[wave][n][0] = m_run;
+    sh_ml[wave][n][1] = l_tot;
+  }
+#pragma unroll
+  for (int cb = 0; cb < 8; cb++)
+#pragma unroll
+    for (int i = 0; i < 4; i++)
+      sh_o[wave][n][16 * cb + 4 * lg + i] = (m_run == -INFINITY) ? 0.0f : acc_o[cb][i] * of + z_tot;
+  __syncthreads();
+
+  const int Hq = g.H * G;
+  const bool single = (a.n_chunks == 1);
+  for (int idx = threadIdx.x; idx < NS * G * 128; idx += 256) {
+    const int col = idx >> 7, c = idx & 127;
+    const int s = col / G, hh = col - s * G;
+    const int bh = grp * NS + s;
+    if (bh >= BH) continue;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; w++) M = fmaxf(M, sh_ml[w][col][0]);
+    float num = 0.0f, den = 0.0f;
+#pragma unroll
+    for (int w = 0; w < 4; w++) {
+      const float mw = sh_ml[w][col][0];
+      const float sc = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
+      num += sc * sh_o[w][col][c];
+      den += sc * sh_ml[w][col][1];
+    }
+    const int bo = bh / g.H, ho = bh % g.H;
+    if (single) {
+      a.out[((int64_t)bo * Hq + (int64_t)ho * G + hh) * 128 + c] = num / den;
+    } else {
+      float* pp = a.part + (((int64_t)bh * a.n_chunks + chunk) * G + hh) * 130;
+      if (c == 0) { pp[0] = M; pp[1] = den; }
+      pp[2 + c] = num;
+    }
+  }
+  if (single) return;
+
+  // ---- last workgroup of the stream group combines all chunks
+  __shared__ int s_last;
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t prev = atomicAdd(&a.counters[grp], 1u);
+    s_last = (prev == (uint32_t)(a.n_chunks - 1));
+  }
+  __syncthreads();
+  if (!s_last) return;
+  __threadfence();
+  for (int idx = threadIdx.x; idx < NS * G * 128; idx += 256) {
+    const int col = idx >> 7, c = idx & 127;
+    const int s = col / G, hh = col - s * G;
+    const int bh = grp * NS + s;
+    if (bh >= BH) continue;
+    const float* pp0 = a.part + ((int64_t)bh * a.n_chunks * G + hh) * 130;
+    const int64_t cs = (int64_t)G * 130;
+    float M = -INFINITY;
+    for (int k = 0; k < a.n_chunks; k++) M = fmaxf(M, __builtin_nontemporal_load(pp0 + k * cs));
+    float num = 0.0f, den = 0.0f;
+    for (int k = 0; k < a.n_chunks; k++) {
+      const float* pp = pp0 + k * cs;
+      const float w = exp2f(__builtin_nontemporal_load(pp) - M);
+      num += w * __builtin_nontemporal_load(pp + 2 + c);
+      den += w * __builtin_nontemporal_load(pp + 1);
+    }
+    const int bo = bh / g.H, ho = bh % g.H;
+    a.out[((int64_t)bo * Hq + (int64_t)ho * G + hh) * 128 + c] = num / den;
+  }
+  if (threadIdx.x == 0) a.counters[grp] = 0u;
+}
+
+// ---------------------------------------------------------------------------
+// host side
+// ---------------------------------------------------------------------------
+// kv streams per wave: as many query groups as fit the 16 MFMA columns,
+// capped per width so the kernel keeps two waves per SIMD without spilling.
+template <int KB, int VB>
+constexpr int ns_cap() {
+  return (KB == 16 || VB == 16 || KB == 1 || VB == 1) ? 1 : (KB == 4 ? 3 : 2);
+}
+static int streams_per_wave(int G, int cap) {
+  const int ns = 16 / G;
+  return ns > cap ? cap : (ns < 1 ? 1 : ns);
+}
+
+int decode_chunks(int n_groups, int n_tiles) {
+  // aim for ~1536 workgroups (6 per CU on 256 CUs), 4..64 tiles per chunk
+  const long total = (long)n_groups * n_tiles;
+  int tpc = (int)((total + 1535) / 1536);
+  tpc = ((tpc + 3) / 4) * 4;
+  if (tpc < 4) tpc = 4;
+  if (tpc > 64) tpc = 64;
+  return (n_tiles + tpc - 1) / tpc;
+}
+
+static size_t counters_bytes(int BH) { return ((size_t)BH * 4 + 255) / 256 * 256; }
+
+size_t decode_workspace_bytes(int B, int H, int G, int max_tiles) {
+  // sized for every packing and every n_tokens <= max_tokens: the chunk count
+  // only grows with n_tiles and is largest for one stream per group
+  const int BH = B * H;
+  const size_t part = (size_t)BH * decode_chunks(BH, max_tiles) * G * 130 * 4;
+  return counters_bytes(BH) + part;
+}
+
+bool decode_supported(int k_bits, int v_bits, int pdt) {
+  (void)pdt;
+  if (k_bits == 0) return v_bits == 1 || v_bits == 2 || v_bits == 4;
+  return k_bits == v_bits && (k_bits == 1 || k_bits == 2 || k_bits == 4 || k_bits == 8 || k_bits == 16);
+}
+
+template <int KB, int VB, int PDT>
+static hipError_t launch_ns(const DecodeArgs& a0, hipStream_t st) {
+  constexpr int CAP = ns_cap<KB, VB>();
+  DecodeArgs a = a0;
+  const int ns = streams_per_wave(a.G, CAP);
+  const int BH = a.g.B * a.g.H;
+  a.n_groups = (BH + ns - 1) / ns;
+  a.n_chunks = decode_chunks(a.n_groups, a.g.n_tiles);
+  a.tpc = (a.g.n_tiles + a.n_chunks - 1) / a.n_chunks;
+  const dim3 grid(a.n_chunks, a.n_groups), block(256);
+  if (ns == 1) {
+    hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 1>), grid, block, 0, st, a);
+  } else if (ns == 2) {
+    if constexpr (CAP >= 2) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 2>), grid, block, 0, st, a);
+  } else {
+    if constexpr (CAP >= 3) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 3>), grid, block, 0, st, a);
+  }
+  return hipGetLastError();
+}
+
+template <int PDT>
+static hipError_t launch_decode_pdt(const DecodeArgs& a, hipStream_t st) {
+  const int kb = a.g.k_bits, vb = a.g.v_bits;
+#define KVQ_DEC(KBV, VBV) \
+  if (kb == KBV && vb == VBV) return launch_ns<KBV, VBV, PDT>(a, st);
+  KVQ_DEC(16, 16) KVQ_DEC(8, 8) KVQ_DEC(4, 4) KVQ_DEC(2, 2) KVQ_DEC(1, 1)
+  KVQ_DEC(0, 1) KVQ_DEC(0, 2) KVQ_DEC(0, 4)
+#undef KVQ_DEC
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float* out, void* ws,
+                         hipStream_t st) {
+  DecodeArgs a;
+  a.g = g;
+  a.q = (const uint16_t*)q;
+  a.out = out;
+  const int BH = g.B * g.H;
+  a.counters = (uint32_t*)ws;
+  a.part = (float*)((uint8_t*)ws + counters_bytes(BH));
+  a.G = G;
+  a.sl2 = scale * 1.4426950408889634f;
+  a.n_chunks = a.tpc = a.n_groups = 0;
+  switch (g.pdt) {
+    case KVQ_F32: return launch_decode_pdt<KVQ_F32>(a, st);
+    case KVQ_F16: return launch_decode_pdt<KVQ_F16>(a, st);
+    case KVQ_BF16: return launch_decode_pdt<KVQ_BF16>(a, st);
+    case KVQ_E4M3: return launch_decode_pdt<KVQ_E4M3>(a, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

@@ -1,0 +1,339 @@
+// kvq_api.cpp -- the C ABI of libkvq (include/kvq.h): argument validation on
+// the host, kernel launches, and the progressive-schedule runtime (tile pool
+// and budget-driven append).
+//
+// Every entry point validates all of its arguments before enqueuing any device
+// work, and never lets a C++ exception cross the ABI.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <map>
+#include <new>
+#include <vector>
+
+#include "kvq.h"
+#include "kvq_device.h"
+
+namespace {
+
+bool valid_bits(int b) { return b == 1 || b == 2 || b == 4 || b == 8 || b == 16; }
+bool valid_kbits(int b) { return b == KVQ_KMIXED || valid_bits(b); }
+bool valid_pdt(int p) { return p == KVQ_F32 || p == KVQ_F16 || p == KVQ_BF16 || p == KVQ_E4M3; }
+int param_bytes(int p) { return p == KVQ_F32 ? 4 : (p == KVQ_E4M3 ? 1 : 2); }
+int64_t tile_bytes(int bits) {
+  return bits == KVQ_KMIXED ? (int64_t)KVQ_MIXED_TILE_BYTES : (int64_t)2048 * bits;
+}
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+// Structural checks shared by every call.  `bits_ok` lets callers validate
+// widths themselves.
+kvq_status check_cache(const kvq_cache* c) {
+  if (!c) return KVQ_EINVAL;
+  if (c->batch < 1 || c->n_kv_heads < 1) return KVQ_EINVAL;
+  if (c->head_dim != KVQ_HEAD_DIM || c->group != KVQ_GROUP) return KVQ_EUNSUPPORTED;
+  if (c->max_tokens < 128 || c->max_tokens % 128) return KVQ_EINVAL;
+  if (c->n_tokens < 0 || c->n_tokens % 128 || c->n_tokens > c->max_tokens) return KVQ_EINVAL;
+  if (!valid_kbits(c->k_bits) || !valid_bits(c->v_bits)) return KVQ_EINVAL;
+  if (!valid_pdt(c->param_dtype) || c->reserved0 != 0) return KVQ_EINVAL;
+  if (!c->k_codes || !c->v_codes || !c->k_scale || !c->k_zero || !c->v_scale || !c->v_zero)
+    return KVQ_EINVAL;
+  if (!aligned(c->k_codes, 256) || !aligned(c->v_codes, 256)) return KVQ_EINVAL;
+  if (!aligned(c->k_scale, 16) || !aligned(c->k_zero, 16) || !aligned(c->v_scale, 16) ||
+      !aligned(c->v_zero, 16))
+    return KVQ_EINVAL;
+  if (c->k_bits == KVQ_KMIXED && !c->k_slot_chan) return KVQ_EINVAL;
+  if (!c->k_tile_off) {
+    if (c->k_tile_stride < tile_bytes(c->k_bits) || c->k_tile_stride % 256) return KVQ_EINVAL;
+  }
+  if (!c->v_tile_off) {
+    if (c->v_tile_stride < tile_bytes(c->v_bits) || c->v_tile_stride % 256) return KVQ_EINVAL;
+  }
+  return KVQ_OK;
+}
+
+kvq::Geo make_geo(const kvq_cache* c) {
+  kvq::Geo g;
+  g.B = c->batch;
+  g.H = c->n_kv_heads;
+  g.max_tiles = c->max_tokens / 128;
+  g.n_tiles = c->n_tokens / 128;
+  g.max_tokens = c->max_tokens;
+  g.k_bits = c->k_bits;
+  g.v_bits = c->v_bits;
+  g.pdt = c->param_dtype;
+  g.k_codes = (uint8_t*)c->k_codes;
+  g.v_codes = (uint8_t*)c->v_codes;
+  g.k_off = c->k_tile_off;
+  g.v_off = c->v_tile_off;
+  g.k_stride = c->k_tile_stride;
+  g.v_stride = c->v_tile_stride;
+  g.k_scale = c->k_scale;
+  g.k_zero = c->k_zero;
+  g.v_scale = c->v_scale;
+  g.v_zero = c->v_zero;
+  g.slot_chan = c->k_slot_chan;
+  return g;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* kvq_strerror(kvq_status s) {
+  switch (s) {
+    case KVQ_OK: return "ok";
+    case KVQ_EINVAL: return "invalid argument";
+    case KVQ_EUNSUPPORTED: return "unsupported configuration";
+    case KVQ_EBUDGET: return "memory budget exceeded even at the floor bit width";
+    case KVQ_EWORKSPACE: return "workspace missing or too small";
+    case KVQ_EHIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+size_t kvq_tile_bytes(int32_t bits) {
+  if (!valid_kbits(bits)) return 0;
+  return (size_t)tile_bytes(bits);
+}
+
+int64_t kvq_cache_bytes(const kvq_cache* c, int32_t n_tokens, int32_t k_bits, int32_t v_bits) {
+  if (!c || c->batch < 1 || c->n_kv_heads < 1 || !valid_pdt(c->param_dtype)) return -1;
+  if (n_tokens < 0 || n_tokens % 128 || !valid_kbits(k_bits) || !valid_bits(v_bits)) return -1;
+  const int64_t groups = n_tokens / 128;
+  const int64_t pb = param_bytes(c->param_dtype);
+  const int64_t per_group = tile_bytes(k_bits) + tile_bytes(v_bits) + 2 * 128 * pb  // key S,Z
+                            + 2 * 128 * pb;                                         // value S,Z
+  return (int64_t)c->batch * c->n_kv_heads * groups * per_group;
+}
+
+kvq_status kvq_quantize(kvq_cache* c, const void* k, const void* v, kvq_dtype in_dtype,
+                        const int64_t k_strides[3], const int64_t v_strides[3], int32_t t0,
+                        int32_t n_new, hipStream_t stream) {
+  try {
+    kvq_status s = check_cache(c);
+    if (s != KVQ_OK) return s;
+    if (!k && !v) return KVQ_EINVAL;
+    if (in_dtype != KVQ_F32 && in_dtype != KVQ_BF16) return KVQ_EINVAL;
+    if ((k && !k_strides) || (v && !v_strides)) return KVQ_EINVAL;
+    if (t0 < 0 || t0 % 128 || n_new < 128 || n_new % 128) return KVQ_EINVAL;
+    if ((int64_t)t0 + n_new > c->max_tokens) return KVQ_EINVAL;
+    if ((int64_t)n_new / 128 > 65535 || c->n_kv_heads > 65535 || c->batch > 65535)
+      return KVQ_EUNSUPPORTED;
+    const int64_t zero[3] = {0, 0, 0};
+    kvq::Geo g = make_geo(c);
+    hipError_t e = kvq::launch_quantize(g, k, v, in_dtype, k ? k_strides : zero,
+                                        v ? v_strides : zero, t0, n_new, stream);
+    if (e != hipSuccess) return KVQ_EHIP;
+    c->n_tokens = std::max(c->n_tokens, t0 + n_new);
+    return KVQ_OK;
+  } catch (...) {
+    return KVQ_EHIP;
+  }
+}
+
+kvq_status kvq_shrink(kvq_cache* c, int32_t to_bits, hipStream_t stream) {
+  try {
+    kvq_status s = check_cache(c);
+    if (s != KVQ_OK) return s;
+    if (to_bits != 8 && to_bits != 4 && to_bits != 2 && to_bits != 1) return KVQ_EINVAL;
+    if (c->k_bits == KVQ_KMIXED) return KVQ_EUNSUPPORTED;
+    if (c->k_bits != 2 * to_bits || c->v_bits != 2 * to_bits) return KVQ_EINVAL;
+    if ((int64_t)c->batch * c->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+    kvq::Geo g = make_geo(c);
+    hipError_t e = kvq::launch_shrink(g, to_bits, stream);
+    if (e != hipSuccess) return KVQ_EHIP;
+    c->k_bits = to_bits;
+    c->v_bits = to_bits;
+    return KVQ_OK;
+  } catch (...) {
+    return KVQ_EHIP;
+  }
+}
+
+size_t kvq_decode_workspace_bytes(const kvq_cache* c, int32_t n_q_heads) {
+  if (!c || c->batch < 1 || c->n_kv_heads < 1 || c->max_tokens < 128 || c->max_tokens % 128)
+    return 0;
+  if (n_q_heads < 1 || n_q_heads % c->n_kv_heads) return 0;
+  const int G = n_q_heads / c->n_kv_heads;
+  if (G > 16) return 0;
+  return kvq::decode_workspace_bytes(c->batch, c->n_kv_heads, G, c->max_tokens / 128);
+}
+
+kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t n_q_heads,
+                           float softmax_scale, float* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  try {
+    kvq_status s = check_cache(c);
+    if (s != KVQ_OK) return s;
+    if (!q || !out) return KVQ_EINVAL;
+    if (!aligned(q, 16) || !aligned(out, 16)) return KVQ_EINVAL;
+    if (n_q_heads < 1 || n_q_heads % c->n_kv_heads) return KVQ_EINVAL;
+    const int G = n_q_heads / c->n_kv_heads;
+    if (G > 16) return KVQ_EUNSUPPORTED;
+    if (c->n_tokens < 128) return KVQ_EINVAL;
+    if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY ||
+        softmax_scale == -INFINITY)
+      return KVQ_EINVAL;
+    if (!kvq::decode_supported(c->k_bits, c->v_bits, c->param_dtype)) return KVQ_EUNSUPPORTED;
+    if ((int64_t)c->batch * c->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+    const size_t need = kvq::decode_workspace_bytes(c->batch, c->n_kv_heads, G, c->max_tokens / 128);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return KVQ_EWORKSPACE;
+    kvq::Geo g = make_geo(c);
+    hipError_t e = kvq::launch_decode(g, q, G, softmax_scale, out, workspace, stream);
+    return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
+  } catch (...) {
+    return KVQ_EHIP;
+  }
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Tile pool: power-of-two extents of one device buffer.  Every tile at width b
+// is 2048*b bytes; after a halving the second half of each tile is returned.
+// Allocation takes the smallest free extent that fits (splitting larger ones)
+// before growing the high-water mark, so freed halves are always reused first.
+// ---------------------------------------------------------------------------
+struct kvq_pool {
+  int B, H, max_tiles;
+  int64_t capacity;
+  int64_t high = 0;
+  int64_t used = 0;
+  int64_t* k_dev;
+  int64_t* v_dev;
+  std::vector<int64_t> k_host, v_host;   // [max_tiles][B][H]
+  std::map<int64_t, std::vector<int64_t>> free_by_size;
+
+  bool alloc(int64_t size, int64_t* off) {
+    auto it = free_by_size.lower_bound(size);
+    while (it != free_by_size.end() && it->second.empty()) ++it;
+    if (it != free_by_size.end()) {
+      int64_t ext = it->first, o = it->second.back();
+      it->second.pop_back();
+      // split: keep the first `size` bytes, return the rest as power-of-two pieces
+      int64_t piece = size;
+      while (piece < ext) {
+        free_by_size[piece].push_back(o + piece);
+        piece *= 2;
+      }
+      *off = o;
+      used += size;
+      return true;
+    }
+    if (high + size > capacity) return false;
+    *off = high;
+    high += size;
+    used += size;
+    return true;
+  }
+  void release(int64_t off, int64_t size) {
+    free_by_size[size].push_back(off);
+    used -= size;
+  }
+};
+
+extern "C" {
+
+kvq_status kvq_pool_create(const kvq_cache* c, int64_t pool_bytes, int64_t* k_dev, int64_t* v_dev,
+                           kvq_pool** out) {
+  try {
+    if (!out) return KVQ_EINVAL;
+    *out = nullptr;
+    kvq_status s = check_cache(c);
+    if (s != KVQ_OK) return s;
+    if (!k_dev || !v_dev || pool_bytes < 2048 || pool_bytes % 256) return KVQ_EINVAL;
+    if (c->k_tile_off != k_dev || c->v_tile_off != v_dev) return KVQ_EINVAL;
+    if (c->k_codes != c->v_codes) return KVQ_EINVAL;
+    if (c->n_tokens != 0) return KVQ_EINVAL;
+    kvq_pool* p = new (std::nothrow) kvq_pool();
+    if (!p) return KVQ_EINVAL;
+    p->B = c->batch;
+    p->H = c->n_kv_heads;
+    p->max_tiles = c->max_tokens / 128;
+    p->capacity = pool_bytes;
+    p->k_dev = k_dev;
+    p->v_dev = v_dev;
+    const size_t n = (size_t)p->max_tiles * p->B * p->H;
+    p->k_host.assign(n, -1);
+    p->v_host.assign(n, -1);
+    *out = p;
+    return KVQ_OK;
+  } catch (...) {
+    return KVQ_EINVAL;
+  }
+}
+
+void kvq_pool_destroy(kvq_pool* p) { delete p; }
+int64_t kvq_pool_used_bytes(const kvq_pool* p) { return p ? p->used : -1; }
+int64_t kvq_pool_high_water(const kvq_pool* p) { return p ? p->high : -1; }
+
+kvq_status kvq_append(kvq_cache* c, kvq_pool* pool, int64_t budget, int32_t floor_bits,
+                      const void* k, const void* v, kvq_dtype in_dtype, const int64_t k_strides[3],
+                      const int64_t v_strides[3], int32_t n_new, hipStream_t stream,
+                      int32_t* n_shrinks) {
+  try {
+    if (n_shrinks) *n_shrinks = 0;
+    kvq_status s = check_cache(c);
+    if (s != KVQ_OK) return s;
+    if (!k || !v || !k_strides || !v_strides) return KVQ_EINVAL;
+    if (in_dtype != KVQ_F32 && in_dtype != KVQ_BF16) return KVQ_EINVAL;
+    if (c->k_bits == KVQ_KMIXED || c->k_bits != c->v_bits) return KVQ_EUNSUPPORTED;
+    if (!valid_bits(floor_bits) || floor_bits > c->k_bits) return KVQ_EINVAL;
+    if (n_new < 128 || n_new % 128 || (int64_t)c->n_tokens + n_new > c->max_tokens)
+      return KVQ_EINVAL;
+    if (pool && (pool->B != c->batch || pool->H != c->n_kv_heads ||
+                 pool->max_tiles != c->max_tokens / 128 || c->k_tile_off != pool->k_dev ||
+                 c->v_tile_off != pool->v_dev))
+      return KVQ_EINVAL;
+    if (!pool && (c->k_tile_off || c->v_tile_off)) return KVQ_EINVAL;
+    // plan the halvings first: fail with no work done if the floor cannot hold it
+    int bits = c->k_bits, halvings = 0;
+    const int32_t target = c->n_tokens + n_new;
+    while (kvq_cache_bytes(c, target, bits, bits) > budget) {
+      if (bits == 1 || bits / 2 < floor_bits) return KVQ_EBUDGET;
+      bits /= 2;
+      halvings++;
+    }
+    for (int i = 0; i < halvings; i++) {
+      s = kvq_shrink(c, c->k_bits / 2, stream);
+      if (s != KVQ_OK) return s;
+      if (n_shrinks) (*n_shrinks)++;
+      if (pool) {
+        const int64_t half = tile_bytes(c->k_bits);     // new (halved) tile size
+        const int n_tiles = c->n_tokens / 128;
+        for (int t = 0; t < n_tiles; t++)
+          for (int i2 = 0; i2 < c->batch * c->n_kv_heads; i2++) {
+            const size_t idx = (size_t)t * c->batch * c->n_kv_heads + i2;
+            pool->release(pool->k_host[idx] + half, half);
+            pool->release(pool->v_host[idx] + half, half);
+          }
+      }
+    }
+    if (pool) {
+      const int64_t sz = tile_bytes(c->k_bits);
+      const int t_first = c->n_tokens / 128, t_last = target / 128;
+      const size_t per = (size_t)c->batch * c->n_kv_heads;
+      for (int t = t_first; t < t_last; t++)
+        for (size_t i2 = 0; i2 < per; i2++) {
+          int64_t ko, vo;
+          if (!pool->alloc(sz, &ko)) return KVQ_EBUDGET;
+          if (!pool->alloc(sz, &vo)) return KVQ_EBUDGET;
+          pool->k_host[t * per + i2] = ko;
+          pool->v_host[t * per + i2] = vo;
+        }
+      const size_t first = (size_t)t_first * per, count = (size_t)(t_last - t_first) * per;
+      if (hipMemcpyAsync(pool->k_dev + first, pool->k_host.data() + first, count * 8,
+                         hipMemcpyHostToDevice, stream) != hipSuccess)
+        return KVQ_EHIP;
+      if (hipMemcpyAsync(pool->v_dev + first, pool->v_host.data() + first, count * 8,
+                         hipMemcpyHostToDevice, stream) != hipSuccess)
+        return KVQ_EHIP;
+    }
+    return kvq_quantize(c, k, v, in_dtype, k_strides, v_strides, c->n_tokens, n_new, stream);
+  } catch (...) {
+    return KVQ_EHIP;
+  }
+}
+
+}  // extern "C"

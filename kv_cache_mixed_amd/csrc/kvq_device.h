@@ -1,0 +1,213 @@
+// kvq_device.h -- device-side numerics and cache addressing shared by the
+// libkvq kernels (gfx950).  Not part of the public ABI.
+//
+// Number formats are written from their definitions (IEEE 754 binary16,
+// bfloat16, OCP FP8 E4M3): narrowing is round-to-nearest-even on the bit
+// pattern, with no dependence on the hardware rounding or denormal mode.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvq.h"
+
+namespace kvq {
+
+// ---------------------------------------------------------------------------
+// binary32 helpers
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t f2u(float x) { return __builtin_bit_cast(uint32_t, x); }
+__device__ __forceinline__ float u2f(uint32_t x) { return __builtin_bit_cast(float, x); }
+
+// 2^k as a binary32 for k in [-126, 127]
+__device__ __forceinline__ float exp2i(int k) {
+  k = k < -126 ? -126 : (k > 127 ? 127 : k);
+  return u2f((uint32_t)(k + 127) << 23);
+}
+
+// unbiased exponent field of a non-negative binary32 (-127 for zero/subnormal)
+__device__ __forceinline__ int expo(float x) { return (int)((f2u(x) >> 23) & 0xffu) - 127; }
+
+// round-to-nearest-even right shift of an unsigned significand by s >= 1 bits
+__device__ __forceinline__ uint32_t rne_shift(uint32_t m, uint32_t s) {
+  if (s >= 32) return 0;
+  uint32_t q = m >> s;
+  uint32_t rem = m & ((1u << s) - 1u);
+  uint32_t half = 1u << (s - 1);
+  if (rem > half || (rem == half && (q & 1u))) q += 1;
+  return q;
+}
+
+// ---------------------------------------------------------------------------
+// IEEE binary16: 1 sign, 5 exponent (bias 15), 10 fraction bits; subnormal
+// quantum 2^-24; |x| >= 65520 overflows to infinity.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_f16_bits(float f) {
+  uint32_t x = f2u(f);
+  uint32_t sign = (x >> 16) & 0x8000u;
+  uint32_t a = x & 0x7fffffffu;
+  if (a > 0x7f800000u) return (uint16_t)(sign | 0x7e00u);          // NaN
+  if (a >= 0x477ff000u) return (uint16_t)(sign | 0x7c00u);         // >= 65520 -> inf
+  uint32_t e = a >> 23;
+  if (e >= 113) {                                                   // normal binary16
+    uint32_t r = rne_shift(a - (112u << 23), 13);                   // rebias, carry ok
+    return (uint16_t)(sign | r);
+  }
+  // subnormal binary16: value = m * 2^-24 with m = round(a_value * 2^24)
+  if (e == 0) return (uint16_t)sign;                                // binary32 subnormal: < 2^-126
+  uint32_t mant = (a & 0x7fffffu) | 0x800000u;                      // value = mant * 2^(e-150)
+  uint32_t s = 126u - e;                                            // shift into 2^-24 units
+  return (uint16_t)(sign | rne_shift(mant, s));
+}
+
+__device__ __forceinline__ float f16_bits_to_f32(uint32_t h) {
+  uint32_t sign = (h & 0x8000u) << 16;
+  uint32_t e = (h >> 10) & 31u, m = h & 1023u;
+  float v;
+  if (e == 0) v = (float)m * 5.9604644775390625e-08f;               // m * 2^-24, exact
+  else if (e == 31) v = u2f(0x7f800000u | (m << 13));
+  else v = u2f(((e + 112u) << 23) | (m << 13));
+  return u2f(f2u(v) | sign);
+}
+
+// ---------------------------------------------------------------------------
+// bfloat16: the upper half of a binary32, round to nearest even.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t x = f2u(f);
+  if ((x & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((x >> 16) | 0x40u);
+  return (uint16_t)((x + 0x7fffu + ((x >> 16) & 1u)) >> 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) { return u2f(h << 16); }
+
+// ---------------------------------------------------------------------------
+// OCP FP8 E4M3: 1 sign, 4 exponent (bias 7), 3 fraction bits, no infinities,
+// S.1111.111 = NaN, largest finite 448; subnormal quantum 2^-9.  Narrowing
+// rounds to nearest even and saturates finite overflow to +-448.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint8_t f32_to_e4m3_bits(float f) {
+  uint32_t x = f2u(f);
+  uint32_t sign = (x >> 24) & 0x80u;
+  uint32_t a = x & 0x7fffffffu;
+  if (a > 0x7f800000u) return (uint8_t)(sign | 0x7fu);
+  if (a >= 0x43e00000u) return (uint8_t)(sign | 0x7eu);            // >= 448 -> 448
+  uint32_t e = a >> 23;
+  if (e >= 121) {                                                   // normal e4m3 (>= 2^-6)
+    uint32_t r = rne_shift(a - (120u << 23), 20);
+    if (r > 0x7eu) r = 0x7eu;                                       // [448, 464) rounds to 448
+    return (uint8_t)(sign | r);
+  }
+  if (e == 0) return (uint8_t)sign;
+  uint32_t mant = (a & 0x7fffffu) | 0x800000u;                      // value = mant * 2^(e-150)
+  uint32_t s = 141u - e;                                            // into 2^-9 units
+  return (uint8_t)(sign | rne_shift(mant, s));
+}
+
+__device__ __forceinline__ float e4m3_bits_to_f32(uint32_t c) {
+  uint32_t sign = (c & 0x80u) << 24;
+  uint32_t e = (c >> 3) & 15u, m = c & 7u;
+  float v;
+  if (e == 0) v = (float)m * 0.001953125f;                          // m * 2^-9
+  else if (e == 15 && m == 7) v = u2f(0x7fc00000u);
+  else v = u2f(((e + 120u) << 23) | (m << 20));
+  return u2f(f2u(v) | sign);
+}
+
+// ---------------------------------------------------------------------------
+// parameter arrays (raw values of param dtype)
+// ---------------------------------------------------------------------------
+template <int PDT>
+struct Param;
+template <>
+struct Param<KVQ_F32> {
+  static constexpr int bytes = 4;
+  __device__ static float load(const void* p, int64_t i) { return ((const float*)p)[i]; }
+  __device__ static float narrow(float x) { return x; }
+  __device__ static void store(void* p, int64_t i, float x) { ((float*)p)[i] = x; }
+  __device__ static float dec(uint32_t raw) { return u2f(raw); }
+};
+template <>
+struct Param<KVQ_F16> {
+  static constexpr int bytes = 2;
+  __device__ static float load(const void* p, int64_t i) {
+    return f16_bits_to_f32(((const uint16_t*)p)[i]);
+  }
+  __device__ static float narrow(float x) { return f16_bits_to_f32(f32_to_f16_bits(x)); }
+  __device__ static void store(void* p, int64_t i, float x) { ((uint16_t*)p)[i] = f32_to_f16_bits(x); }
+  __device__ static float dec(uint32_t raw) { return f16_bits_to_f32(raw); }
+};
+template <>
+struct Param<KVQ_BF16> {
+  static constexpr int bytes = 2;
+  __device__ static float load(const void* p, int64_t i) {
+    return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+  }
+  __device__ static float narrow(float x) { return bf16_bits_to_f32(f32_to_bf16_bits(x)); }
+  __device__ static void store(void* p, int64_t i, float x) { ((uint16_t*)p)[i] = f32_to_bf16_bits(x); }
+  __device__ static float dec(uint32_t raw) { return bf16_bits_to_f32(raw); }
+};
+template <>
+struct Param<KVQ_E4M3> {
+  static constexpr int bytes = 1;
+  __device__ static float load(const void* p, int64_t i) {
+    return e4m3_bits_to_f32(((const uint8_t*)p)[i]);
+  }
+  __device__ static float narrow(float x) { return e4m3_bits_to_f32(f32_to_e4m3_bits(x)); }
+  __device__ static void store(void* p, int64_t i, float x) { ((uint8_t*)p)[i] = f32_to_e4m3_bits(x); }
+  __device__ static float dec(uint32_t raw) { return e4m3_bits_to_f32(raw); }
+};
+
+// ---------------------------------------------------------------------------
+// cache geometry passed to kernels by value
+// ---------------------------------------------------------------------------
+struct Geo {
+  int32_t B, H, max_tiles, n_tiles;
+  int32_t k_bits, v_bits, pdt;
+  uint8_t* k_codes;
+  uint8_t* v_codes;
+  const int64_t* k_off;
+  const int64_t* v_off;
+  int64_t k_stride, v_stride;
+  void* k_scale;
+  void* k_zero;
+  void* v_scale;
+  void* v_zero;
+  const int16_t* slot_chan;
+  int32_t max_tokens;
+};
+
+__device__ __forceinline__ int64_t k_tile_offset(const Geo& g, int b, int h, int tile) {
+  if (g.k_off) return g.k_off[((int64_t)tile * g.B + b) * g.H + h];
+  return (((int64_t)b * g.H + h) * g.max_tiles + tile) * g.k_stride;
+}
+__device__ __forceinline__ int64_t v_tile_offset(const Geo& g, int b, int h, int tile) {
+  if (g.v_off) return g.v_off[((int64_t)tile * g.B + b) * g.H + h];
+  return (((int64_t)b * g.H + h) * g.max_tiles + tile) * g.v_stride;
+}
+// first parameter index of key tile (b, h, tile); value token (b, h, t)
+__device__ __forceinline__ int64_t k_param_base(const Geo& g, int b, int h, int tile) {
+  return (((int64_t)b * g.H + h) * g.max_tiles + tile) * 128;
+}
+__device__ __forceinline__ int64_t v_param_base(const Geo& g, int b, int h, int64_t t) {
+  return ((int64_t)b * g.H + h) * (int64_t)g.max_tokens + t;
+}
+
+// mixed-width key slots: 0..7 4-bit, 8..23 alternating 3/1-bit, 24..127 2-bit
+__host__ __device__ constexpr int mixed_slot_bits(int j) {
+  return j < 8 ? 4 : (j < 24 ? ((j & 1) ? 1 : 3) : 2);
+}
+
+}  // namespace kvq
+
+// launchers (host side), implemented in the .hip files
+namespace kvq {
+hipError_t launch_quantize(const Geo& g, const void* k, const void* v, int in_dtype,
+                           const int64_t* ks, const int64_t* vs, int t0, int n_new,
+                           hipStream_t st);
+hipError_t launch_shrink(const Geo& g, int to_bits, hipStream_t st);
+int decode_chunks(int n_groups, int n_tiles);
+size_t decode_workspace_bytes(int B, int H, int G, int max_tiles);
+hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float* out,
+                         void* ws, hipStream_t st);
+bool decode_supported(int k_bits, int v_bits, int pdt);
+}  // namespace kvq

@@ -1,0 +1,247 @@
+// quantize.hip -- quantize-and-pack kernels for one or more 128-token tiles.
+//
+// Keys are quantized channel-wise (one group = one channel, or one slot of the
+// mixed layout, over the 128 tokens of a tile), values token-wise (one group =
+// the 128 channels of one token), following the key-channel / value-token
+// convention described on the ChanMix page (Background, Overall framework).
+// The quantizer is the asymmetric uniform one of the ChanMix page (Key design 1:
+// S = (max - min) / (2^b - 1), zero point = min) with parameters narrowed to
+// the stored dtype before the codes are computed from them.
+//
+// Bit-exactness: every step is one IEEE binary32 operation (no contraction),
+// division is correctly rounded (HIP default), rounding of the quotient is
+// round-half-even (v_rndne_f32), narrowing is done on the bit pattern.
+//
+// One workgroup (256 threads) per (tile, kv head, batch).  The input tile is
+// read once with coalesced loads, codes are staged in LDS as uint16, and the
+// packed rows are written with coalesced 32-bit stores.
+#pragma clang fp contract(off)
+
+#include "kvq_device.h"
+
+namespace kvq {
+
+template <int IN>  // KVQ_F32 or KVQ_BF16
+__device__ __forceinline__ float load_in(const void* p, int64_t i) {
+  if constexpr (IN == KVQ_F32) return ((const float*)p)[i];
+  else return bf16_bits_to_f32(((const uint16_t*)p)[i]);
+}
+
+// Quantize one group member given the stored (narrowed) S', Z'.
+__device__ __forceinline__ uint32_t quant_code(float x, float sp, float zp, float levels) {
+  if (sp == 0.0f) return 0u;
+  float d = x - zp;
+  float r = d / sp;
+  float rr = __builtin_rintf(r);
+  rr = rr > 0.0f ? rr : 0.0f;   // also maps NaN to 0
+  rr = rr < levels ? rr : levels;
+  return (uint32_t)rr;
+}
+
+// Pack codes[row][elem] (LDS, uint16, row pitch PITCH) into 128 rows of
+// 16*BITS bytes; each thread writes whole 32-bit words.
+template <int BITS, int PITCH = 128>
+__device__ __forceinline__ void pack_rows_store(const uint16_t* codes, uint8_t* tile) {
+  constexpr int WORDS_PER_ROW = 4 * BITS;        // 16*BITS bytes
+  constexpr int PER_WORD = 32 / BITS;            // codes in one 32-bit word (BITS<=16)
+  uint32_t* out = (uint32_t*)tile;
+  for (int w = threadIdx.x; w < 128 * WORDS_PER_ROW; w += blockDim.x) {
+    int row = w / WORDS_PER_ROW;
+    int e0 = (w % WORDS_PER_ROW) * PER_WORD;
+    const uint16_t* src = codes + row * PITCH + e0;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < PER_WORD; i++) word |= (uint32_t)src[i] << (i * BITS);
+    out[w] = word;
+  }
+}
+
+// Mixed key tile: codes[t][slot]; five planes (see include/kvq.h).
+__device__ __forceinline__ void pack_mixed_store(const uint16_t* codes, uint8_t* tile) {
+  // planes 0..3: 8 bytes per token = 2 words; 1024 words in total
+  uint32_t* out = (uint32_t*)tile;
+  for (int w = threadIdx.x; w < 1024; w += blockDim.x) {
+    int plane = w >> 8, t = (w >> 1) & 127, half = w & 1;
+    const uint16_t* c = codes + t * 128;
+    uint32_t word = 0;
+    if (plane == 0 && half == 0) {            // logical bytes 0..3: slots 0..7 at 4 bits
+#pragma unroll
+      for (int i = 0; i < 8; i++) word |= (uint32_t)c[i] << (4 * i);
+    } else if (plane == 0) {                  // logical bytes 4..7: (3,1) pairs, slots 8..23
+#pragma unroll
+      for (int i = 0; i < 8; i++)
+        word |= ((uint32_t)c[8 + 2 * i] << (4 * i)) | ((uint32_t)c[9 + 2 * i] << (4 * i + 3));
+    } else {                                  // logical bytes 8p+4h .. : 16 two-bit slots
+      int s0 = 24 + 32 * (plane - 1) + 16 * half;
+#pragma unroll
+      for (int i = 0; i < 16; i++) word |= (uint32_t)c[s0 + i] << (2 * i);
+    }
+    out[w] = word;
+  }
+  // plane 4: logical bytes 32..33 = slots 120..127, 2 bytes per token
+  uint16_t* out4 = (uint16_t*)(tile + 4096);
+  for (int t = threadIdx.x; t < 128; t += blockDim.x) {
+    const uint16_t* c = codes + t * 128 + 120;
+    uint32_t v = 0;
+#pragma unroll
+    for (int i = 0; i < 8; i++) v |= (uint32_t)c[i] << (2 * i);
+    out4[t] = (uint16_t)v;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Keys: thread (slot j = tid & 127, half = tid >> 7) scans 64 tokens.
+// KB = 0 selects the mixed layout (slot j holds channel slot_chan[h][j]).
+// ---------------------------------------------------------------------------
+template <int KB, int PDT, int IN>
+__global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __restrict__ kin,
+                                                         int64_t sb, int64_t sh, int64_t st,
+                                                         int t0) {
+  __shared__ uint16_t codes[128 * 128];
+  __shared__ float red_mn[2][128], red_mx[2][128];
+  const int tile_local = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tile = t0 / 128 + tile_local;
+  const int j = threadIdx.x & 127, half = threadIdx.x >> 7;
+  const int chan = (KB == 0) ? (int)g.slot_chan[h * 128 + j] : j;
+  const int bits = (KB == 0) ? mixed_slot_bits(j) : KB;
+
+  const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (int64_t)(tile_local * 128) * st + chan;
+  float x[64];
+#pragma unroll
+  for (int i = 0; i < 64; i++) x[i] = load_in<IN>(kin, base + (int64_t)(half * 64 + i) * st);
+  float mn = x[0], mx = x[0];
+#pragma unroll
+  for (int i = 1; i < 64; i++) {
+    mn = x[i] < mn ? x[i] : mn;
+    mx = x[i] > mx ? x[i] : mx;
+  }
+  red_mn[half][j] = mn;
+  red_mx[half][j] = mx;
+  __syncthreads();
+  mn = red_mn[0][j] < red_mn[1][j] ? red_mn[0][j] : red_mn[1][j];
+  mx = red_mx[0][j] > red_mx[1][j] ? red_mx[0][j] : red_mx[1][j];
+  const float levels = (float)((1u << bits) - 1u);
+  const float s = (mx - mn) / levels;
+  const float sp = Param<PDT>::narrow(s);
+  const float zp = Param<PDT>::narrow(mn);
+  if (half == 0) {
+    const int64_t pi = k_param_base(g, b, h, tile) + j;
+    Param<PDT>::store(g.k_scale, pi, s);
+    Param<PDT>::store(g.k_zero, pi, mn);
+  }
+#pragma unroll
+  for (int i = 0; i < 64; i++)
+    codes[(half * 64 + i) * 128 + j] = (uint16_t)quant_code(x[i], sp, zp, levels);
+  __syncthreads();
+  uint8_t* dst = g.k_codes + k_tile_offset(g, b, h, tile);
+  if constexpr (KB == 0) pack_mixed_store(codes, dst);
+  else pack_rows_store<KB>(codes, dst);
+}
+
+// ---------------------------------------------------------------------------
+// Values: wave w handles tokens [32w, 32w+32) of the tile, one token at a time;
+// lane l holds channels 2l, 2l+1.  Codes are stored transposed ([c][t]) and
+// packed as channel rows.
+// ---------------------------------------------------------------------------
+template <int VB, int PDT, int IN>
+__global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __restrict__ vin,
+                                                         int64_t sb, int64_t sh, int64_t st,
+                                                         int t0) {
+  constexpr int PITCH = 130;  // odd word pitch: lanes writing one column hit different banks
+  __shared__ uint16_t codes[128 * PITCH];
+  const int tile_local = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tile = t0 / 128 + tile_local;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const float levels = (float)((1u << VB) - 1u);
+  for (int i = 0; i < 32; i++) {
+    const int t = wave * 32 + i;
+    const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (int64_t)(tile_local * 128 + t) * st;
+    const float x0 = load_in<IN>(vin, base + 2 * lane);
+    const float x1 = load_in<IN>(vin, base + 2 * lane + 1);
+    float mn = x0 < x1 ? x0 : x1, mx = x0 > x1 ? x0 : x1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) {
+      const float a = __shfl_xor(mn, o, 64), c = __shfl_xor(mx, o, 64);
+      mn = a < mn ? a : mn;
+      mx = c > mx ? c : mx;
+    }
+    const float s = (mx - mn) / levels;
+    const float sp = Param<PDT>::narrow(s);
+    const float zp = Param<PDT>::narrow(mn);
+    if (lane == 0) {
+      const int64_t pi = v_param_base(g, b, h, (int64_t)tile * 128 + t);
+      Param<PDT>::store(g.v_scale, pi, s);
+      Param<PDT>::store(g.v_zero, pi, mn);
+    }
+    codes[(2 * lane) * PITCH + t] = (uint16_t)quant_code(x0, sp, zp, levels);
+    codes[(2 * lane + 1) * PITCH + t] = (uint16_t)quant_code(x1, sp, zp, levels);
+  }
+  __syncthreads();
+  pack_rows_store<VB, PITCH>(codes, g.v_codes + v_tile_offset(g, b, h, tile));
+}
+
+// ---------------------------------------------------------------------------
+// host launchers
+// ---------------------------------------------------------------------------
+template <int PDT, int IN>
+static hipError_t launch_k(const Geo& g, const void* k, const int64_t* s, int t0, int n_new,
+                           hipStream_t stm) {
+  dim3 grid(n_new / 128, g.H, g.B), block(256);
+#define KVQ_QK(KBV)                                                                          \
+  case KBV:                                                                                  \
+    hipLaunchKernelGGL((quantize_k_kernel<KBV, PDT, IN>), grid, block, 0, stm, g, k, s[0],   \
+                       s[1], s[2], t0);                                                      \
+    break;
+  switch (g.k_bits) {
+    KVQ_QK(0) KVQ_QK(1) KVQ_QK(2) KVQ_QK(4) KVQ_QK(8) KVQ_QK(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef KVQ_QK
+  return hipGetLastError();
+}
+
+template <int PDT, int IN>
+static hipError_t launch_v(const Geo& g, const void* v, const int64_t* s, int t0, int n_new,
+                           hipStream_t stm) {
+  dim3 grid(n_new / 128, g.H, g.B), block(256);
+#define KVQ_QV(VBV)                                                                          \
+  case VBV:                                                                                  \
+    hipLaunchKernelGGL((quantize_v_kernel<VBV, PDT, IN>), grid, block, 0, stm, g, v, s[0],   \
+                       s[1], s[2], t0);                                                      \
+    break;
+  switch (g.v_bits) {
+    KVQ_QV(1) KVQ_QV(2) KVQ_QV(4) KVQ_QV(8) KVQ_QV(16)
+    default: return hipErrorInvalidValue;
+  }
+#undef KVQ_QV
+  return hipGetLastError();
+}
+
+template <int PDT>
+static hipError_t launch_pdt(const Geo& g, const void* k, const void* v, int in_dtype,
+                             const int64_t* ks, const int64_t* vs, int t0, int n_new,
+                             hipStream_t st) {
+  hipError_t e = hipSuccess;
+  if (in_dtype == KVQ_F32) {
+    if (k) e = launch_k<PDT, KVQ_F32>(g, k, ks, t0, n_new, st);
+    if (e == hipSuccess && v) e = launch_v<PDT, KVQ_F32>(g, v, vs, t0, n_new, st);
+  } else {
+    if (k) e = launch_k<PDT, KVQ_BF16>(g, k, ks, t0, n_new, st);
+    if (e == hipSuccess && v) e = launch_v<PDT, KVQ_BF16>(g, v, vs, t0, n_new, st);
+  }
+  return e;
+}
+
+hipError_t launch_quantize(const Geo& g, const void* k, const void* v, int in_dtype,
+                           const int64_t* ks, const int64_t* vs, int t0, int n_new,
+                           hipStream_t st) {
+  switch (g.pdt) {
+    case KVQ_F32: return launch_pdt<KVQ_F32>(g, k, v, in_dtype, ks, vs, t0, n_new, st);
+    case KVQ_F16: return launch_pdt<KVQ_F16>(g, k, v, in_dtype, ks, vs, t0, n_new, st);
+    case KVQ_BF16: return launch_pdt<KVQ_BF16>(g, k, v, in_dtype, ks, vs, t0, n_new, st);
+    case KVQ_E4M3: return launch_pdt<KVQ_E4M3>(g, k, v, in_dtype, ks, vs, t0, n_new, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace kvq

@@ -1,0 +1,308 @@
+"""ctypes binding of libkvq (C ABI in include/kvq.h).
+
+Argument marshalling only: every step of quantize / shrink / decode attention
+runs in the HIP kernels of libkvq.so.  torch supplies device memory and the
+current HIP stream.  There is no fallback: if the library is missing, load()
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+F32, F16, BF16, E4M3 = 0, 1, 2, 3
+PARAM_BYTES = {F32: 4, F16: 2, BF16: 2, E4M3: 1}
+KMIXED = 0
+MIXED_TILE_BYTES = 4352
+OK, EINVAL, EUNSUPPORTED, EBUDGET, EWORKSPACE, EHIP = range(6)
+
+
+class KvqCacheStruct(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32), ("group", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int32), ("n_tokens", ctypes.c_int32),
+        ("k_bits", ctypes.c_int32), ("v_bits", ctypes.c_int32),
+        ("param_dtype", ctypes.c_int32), ("reserved0", ctypes.c_int32),
+        ("k_codes", ctypes.c_void_p), ("v_codes", ctypes.c_void_p),
+        ("k_tile_off", ctypes.c_void_p), ("v_tile_off", ctypes.c_void_p),
+        ("k_tile_stride", ctypes.c_int64), ("v_tile_stride", ctypes.c_int64),
+        ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
+        ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
+        ("k_slot_chan", ctypes.c_void_p),
+    ]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__("%s failed: %s (status %d)" % (what, strerror(status), status))
+
+
+_lib = None
+
+EXPORTS = ["kvq_strerror", "kvq_tile_bytes", "kvq_cache_bytes", "kvq_quantize", "kvq_shrink",
+           "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_pool_create", "kvq_pool_destroy",
+           "kvq_pool_used_bytes", "kvq_pool_high_water", "kvq_append"]
+
+
+def load():
+    """Load libkvq.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libkvq.so not built at %s (run __graft_entry__.build())" % LIB_PATH)
+    L = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER(KvqCacheStruct)
+    vp, i32, i64 = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64
+    L.kvq_strerror.restype = ctypes.c_char_p
+    L.kvq_strerror.argtypes = [ctypes.c_int]
+    L.kvq_tile_bytes.restype = ctypes.c_size_t
+    L.kvq_tile_bytes.argtypes = [i32]
+    L.kvq_cache_bytes.restype = i64
+    L.kvq_cache_bytes.argtypes = [P, i32, i32, i32]
+    L.kvq_quantize.restype = ctypes.c_int
+    L.kvq_quantize.argtypes = [P, vp, vp, ctypes.c_int, vp, vp, i32, i32, vp]
+    L.kvq_shrink.restype = ctypes.c_int
+    L.kvq_shrink.argtypes = [P, i32, vp]
+    L.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
+    L.kvq_decode_workspace_bytes.argtypes = [P, i32]
+    L.kvq_decode_attn.restype = ctypes.c_int
+    L.kvq_decode_attn.argtypes = [P, vp, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+    L.kvq_pool_create.restype = ctypes.c_int
+    L.kvq_pool_create.argtypes = [P, i64, vp, vp, ctypes.POINTER(vp)]
+    L.kvq_pool_destroy.restype = None
+    L.kvq_pool_destroy.argtypes = [vp]
+    L.kvq_pool_used_bytes.restype = i64
+    L.kvq_pool_used_bytes.argtypes = [vp]
+    L.kvq_pool_high_water.restype = i64
+    L.kvq_pool_high_water.argtypes = [vp]
+    L.kvq_append.restype = ctypes.c_int
+    L.kvq_append.argtypes = [P, vp, i64, i32, vp, vp, ctypes.c_int, vp, vp, i32, vp,
+                             ctypes.POINTER(i32)]
+    _lib = L
+    return L
+
+
+def strerror(status: int) -> str:
+    return load().kvq_strerror(status).decode()
+
+
+def _check(status: int, what: str):
+    if status != OK:
+        raise KvqError(status, what)
+
+
+def _stream_ptr(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _strides3(t):
+    """(b, h, t) element strides of a [B][H][T][128] tensor with unit channel stride."""
+    assert t.dim() == 4 and t.shape[-1] == 128 and t.stride(-1) == 1
+    return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+def tile_bytes(bits: int) -> int:
+    return int(load().kvq_tile_bytes(bits))
+
+
+class PackedCache:
+    """Device buffers of one block's packed cache plus the kvq_cache struct.
+
+    layout="contiguous": tiles at ((b*H + h)*max_tiles + g) * stride (stride =
+    tile size at the initial widths); layout="pool": one code pool of
+    pool_bytes with per-tile offset tables managed by a kvq_pool.
+    """
+
+    def __init__(self, batch, n_kv_heads, max_tokens, k_bits, v_bits, param_dtype=F16,
+                 slot_chan=None, device="cuda", layout="contiguous", pool_bytes=None):
+        import torch
+        load()
+        self.device = torch.device(device)
+        self.B, self.H, self.max_tokens = batch, n_kv_heads, max_tokens
+        self.max_tiles = max_tokens // 128
+        self.pdt = param_dtype
+        pb = PARAM_BYTES[param_dtype]
+        u8 = dict(dtype=torch.uint8, device=self.device)
+        s = KvqCacheStruct()
+        s.batch, s.n_kv_heads, s.head_dim, s.group = batch, n_kv_heads, 128, 128
+        s.max_tokens, s.n_tokens = max_tokens, 0
+        s.k_bits, s.v_bits, s.param_dtype, s.reserved0 = k_bits, v_bits, param_dtype, 0
+        n_streams = batch * n_kv_heads
+        self.layout = layout
+        self.pool = None
+        if layout == "contiguous":
+            self.k_stride = tile_bytes(k_bits)
+            self.v_stride = tile_bytes(v_bits)
+            self.k_codes = torch.zeros(n_streams * self.max_tiles * self.k_stride, **u8)
+            self.v_codes = torch.zeros(n_streams * self.max_tiles * self.v_stride, **u8)
+            s.k_codes, s.v_codes = self.k_codes.data_ptr(), self.v_codes.data_ptr()
+            s.k_tile_off = s.v_tile_off = None
+            s.k_tile_stride, s.v_tile_stride = self.k_stride, self.v_stride
+            self.k_off = self.v_off = None
+        elif layout == "pool":
+            assert pool_bytes is not None
+            self.k_codes = torch.zeros(pool_bytes, **u8)
+            self.v_codes = self.k_codes
+            s.k_codes = s.v_codes = self.k_codes.data_ptr()
+            self.k_off = torch.full((self.max_tiles * n_streams,), -1, dtype=torch.int64,
+                                    device=self.device)
+            self.v_off = torch.full_like(self.k_off, -1)
+            s.k_tile_off, s.v_tile_off = self.k_off.data_ptr(), self.v_off.data_ptr()
+            s.k_tile_stride = s.v_tile_stride = 0
+        else:
+            raise ValueError(layout)
+        self.k_scale = torch.zeros(n_streams * self.max_tiles * 128 * pb, **u8)
+        self.k_zero = torch.zeros_like(self.k_scale)
+        self.v_scale = torch.zeros(n_streams * max_tokens * pb, **u8)
+        self.v_zero = torch.zeros_like(self.v_scale)
+        s.k_scale, s.k_zero = self.k_scale.data_ptr(), self.k_zero.data_ptr()
+        s.v_scale, s.v_zero = self.v_scale.data_ptr(), self.v_zero.data_ptr()
+        self.slot_chan = None
+        if slot_chan is not None:
+            self.slot_chan = torch.as_tensor(np.ascontiguousarray(slot_chan, dtype=np.int16),
+                                             device=self.device)
+            s.k_slot_chan = self.slot_chan.data_ptr()
+        else:
+            s.k_slot_chan = None
+        self.s = s
+        self._ws = {}
+        if layout == "pool":
+            h = ctypes.c_void_p()
+            _check(load().kvq_pool_create(ctypes.byref(s), pool_bytes, _ptr(self.k_off),
+                                          _ptr(self.v_off), ctypes.byref(h)), "kvq_pool_create")
+            self.pool = h
+
+    def __del__(self):
+        try:
+            if self.pool is not None and _lib is not None:
+                _lib.kvq_pool_destroy(self.pool)
+                self.pool = None
+        except Exception:
+            pass
+
+    # -- state ----------------------------------------------------------------
+    @property
+    def n_tokens(self):
+        return self.s.n_tokens
+
+    @property
+    def k_bits(self):
+        return self.s.k_bits
+
+    @property
+    def v_bits(self):
+        return self.s.v_bits
+
+    def cache_bytes(self, n_tokens=None, k_bits=None, v_bits=None):
+        return int(load().kvq_cache_bytes(ctypes.byref(self.s),
+                                          self.n_tokens if n_tokens is None else n_tokens,
+                                          self.k_bits if k_bits is None else k_bits,
+                                          self.v_bits if v_bits is None else v_bits))
+
+    def pool_used(self):
+        return int(load().kvq_pool_used_bytes(self.pool))
+
+    def pool_high_water(self):
+        return int(load().kvq_pool_high_water(self.pool))
+
+    # -- operations -----------------------------------------------------------
+    def quantize(self, k, v, t0=0, stream=None):
+        """k, v: [B][H][n_new][128] float32 or bfloat16 device tensors (either may be None)."""
+        import torch
+        ref = k if k is not None else v
+        in_dtype = {torch.float32: F32, torch.bfloat16: BF16}[ref.dtype]
+        n_new = ref.shape[2]
+        st = load().kvq_quantize(ctypes.byref(self.s), _ptr(k), _ptr(v), in_dtype,
+                                 _strides3(k) if k is not None else None,
+                                 _strides3(v) if v is not None else None,
+                                 t0, n_new, _stream_ptr(stream))
+        _check(st, "kvq_quantize")
+
+    def shrink(self, to_bits, stream=None):
+        _check(load().kvq_shrink(ctypes.byref(self.s), to_bits, _stream_ptr(stream)), "kvq_shrink")
+
+    def append(self, k, v, budget_bytes, floor_bits, stream=None):
+        import torch
+        in_dtype = {torch.float32: F32, torch.bfloat16: BF16}[k.dtype]
+        n = ctypes.c_int32(0)
+        st = load().kvq_append(ctypes.byref(self.s), self.pool, budget_bytes, floor_bits,
+                               _ptr(k), _ptr(v), in_dtype, _strides3(k), _strides3(v),
+                               k.shape[2], _stream_ptr(stream), ctypes.byref(n))
+        _check(st, "kvq_append")
+        return n.value
+
+    def workspace_bytes(self, n_q_heads):
+        return int(load().kvq_decode_workspace_bytes(ctypes.byref(self.s), n_q_heads))
+
+    def workspace(self, n_q_heads):
+        import torch
+        if n_q_heads not in self._ws:
+            nb = self.workspace_bytes(n_q_heads)
+            if nb == 0:
+                raise KvqError(EINVAL, "kvq_decode_workspace_bytes")
+            self._ws[n_q_heads] = torch.zeros(nb, dtype=torch.uint8, device=self.device)
+        return self._ws[n_q_heads]
+
+    def decode_attn(self, q, softmax_scale, out=None, workspace=None, stream=None):
+        """q: [B][Hq][128] bfloat16 device tensor -> out [B][Hq][128] float32."""
+        import torch
+        assert q.dtype == torch.bfloat16 and q.is_contiguous()
+        Hq = q.shape[1]
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        ws = workspace if workspace is not None else self.workspace(Hq)
+        st = load().kvq_decode_attn(ctypes.byref(self.s), _ptr(q), Hq, float(softmax_scale),
+                                    _ptr(out), _ptr(ws), ws.numel(), _stream_ptr(stream))
+        _check(st, "kvq_decode_attn")
+        return out
+
+    # -- host views for tests --------------------------------------------------
+    def k_tile(self, b, h, g):
+        """bytes of key tile (b, h, g) at the current width (host numpy)."""
+        n = tile_bytes(self.k_bits)
+        off = self._tile_off(self.k_off, self.k_stride if self.layout == "contiguous" else 0,
+                             b, h, g)
+        return self.k_codes[off:off + n].cpu().numpy()
+
+    def v_tile(self, b, h, g):
+        n = tile_bytes(self.v_bits)
+        off = self._tile_off(self.v_off, self.v_stride if self.layout == "contiguous" else 0,
+                             b, h, g)
+        return self.v_codes[off:off + n].cpu().numpy()
+
+    def _tile_off(self, table, stride, b, h, g):
+        if table is None:
+            return ((b * self.H + h) * self.max_tiles + g) * stride
+        return int(table[(g * self.B + b) * self.H + h].item())
+
+    def k_params(self, b, h):
+        """(S raw, Z raw) of stream (b, h) for stored tiles: [n_tiles, 128] numpy."""
+        pb = PARAM_BYTES[self.pdt]
+        nt = self.n_tokens // 128
+        base = ((b * self.H + h) * self.max_tiles) * 128 * pb
+        npdt = {F32: np.float32, F16: np.uint16, BF16: np.uint16, E4M3: np.uint8}[self.pdt]
+        sl = slice(base, base + nt * 128 * pb)
+        return (self.k_scale[sl].cpu().numpy().view(npdt).reshape(nt, 128),
+                self.k_zero[sl].cpu().numpy().view(npdt).reshape(nt, 128))
+
+    def v_params(self, b, h):
+        pb = PARAM_BYTES[self.pdt]
+        base = ((b * self.H + h) * self.max_tokens) * pb
+        npdt = {F32: np.float32, F16: np.uint16, BF16: np.uint16, E4M3: np.uint8}[self.pdt]
+        sl = slice(base, base + self.n_tokens * pb)
+        return (self.v_scale[sl].cpu().numpy().view(npdt),
+                self.v_zero[sl].cpu().numpy().view(npdt))

@@ -1,0 +1,141 @@
+"""C-ABI contract checks that need no GPU: the library loads, exports every
+function include/kvq.h declares, and rejects invalid arguments on the host
+before any launch (no call here reaches the device)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_mixed_amd import kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def _lib():
+    if not os.path.exists(kvq.LIB_PATH):
+        pytest.skip("libkvq.so not built")
+    return kvq.load()
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z_]+)\s*\(", src)))
+
+
+def test_every_declared_symbol_is_exported():
+    L = _lib()
+    names = _declared()
+    assert set(names) == set(kvq.EXPORTS)
+    for n in names:
+        assert hasattr(L, n), n
+
+
+def test_pure_host_helpers():
+    L = _lib()
+    assert kvq.tile_bytes(4) == 8192 and kvq.tile_bytes(0) == 4352 and kvq.tile_bytes(3) == 0
+    assert kvq.strerror(kvq.EBUDGET).startswith("memory budget")
+    s = _fake_struct(16, 4, 32768, 4, 4)
+    s.n_tokens = 32768
+    assert L.kvq_cache_bytes(ctypes.byref(s), 32768, 4, 4) == 285212672
+    assert L.kvq_cache_bytes(ctypes.byref(s), 100, 4, 4) == -1
+    s4 = _fake_struct(1, 8, 131072, 0, 2, kvq.E4M3)
+    assert L.kvq_cache_bytes(ctypes.byref(s4), 131072, 0, 2) == 73400320
+    ws = L.kvq_decode_workspace_bytes(ctypes.byref(s), 28)
+    assert ws > 0 and ws % 4 == 0
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(s), 30) == 0      # not a multiple of Hkv
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(s), 4 * 17) == 0  # G > 16
+
+
+FAKE = 0x10000000  # never dereferenced: every call below fails validation first
+
+
+def _fake_struct(B, H, T, kb, vb, pdt=kvq.F16):
+    s = kvq.KvqCacheStruct()
+    s.batch, s.n_kv_heads, s.head_dim, s.group = B, H, 128, 128
+    s.max_tokens, s.n_tokens, s.k_bits, s.v_bits = T, 0, kb, vb
+    s.param_dtype, s.reserved0 = pdt, 0
+    s.k_codes = s.v_codes = FAKE
+    s.k_tile_off = s.v_tile_off = None
+    s.k_tile_stride = kvq.tile_bytes(kb)
+    s.v_tile_stride = kvq.tile_bytes(vb)
+    s.k_scale = s.k_zero = s.v_scale = s.v_zero = FAKE
+    s.k_slot_chan = FAKE if kb == 0 else None
+    return s
+
+
+def test_validation_rejects_before_launch():
+    L = _lib()
+    st3 = (ctypes.c_int64 * 3)(0, 0, 128)
+    vp = ctypes.c_void_p
+    s = _fake_struct(2, 2, 1024, 4, 4)
+    P = ctypes.byref
+    # quantize
+    assert L.kvq_quantize(None, vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 0, 128, None) == kvq.EINVAL
+    assert L.kvq_quantize(P(s), None, None, kvq.F32, st3, st3, 0, 128, None) == kvq.EINVAL
+    assert L.kvq_quantize(P(s), vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 64, 128, None) == kvq.EINVAL
+    assert L.kvq_quantize(P(s), vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 0, 100, None) == kvq.EINVAL
+    assert L.kvq_quantize(P(s), vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 896, 256, None) == kvq.EINVAL
+    assert L.kvq_quantize(P(s), vp(FAKE), vp(FAKE), kvq.E4M3, st3, st3, 0, 128, None) == kvq.EINVAL
+    assert L.kvq_quantize(P(s), vp(FAKE), None, kvq.F32, None, None, 0, 128, None) == kvq.EINVAL
+    bad = _fake_struct(2, 2, 1024, 4, 4)
+    bad.head_dim = 64
+    assert L.kvq_quantize(P(bad), vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 0, 128, None) == kvq.EUNSUPPORTED
+    bad = _fake_struct(2, 2, 1000, 4, 4)
+    assert L.kvq_quantize(P(bad), vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 0, 128, None) == kvq.EINVAL
+    bad = _fake_struct(2, 2, 1024, 3, 4)
+    assert L.kvq_quantize(P(bad), vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 0, 128, None) == kvq.EINVAL
+    bad = _fake_struct(2, 2, 1024, 4, 4)
+    bad.k_tile_stride = 1000
+    assert L.kvq_quantize(P(bad), vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 0, 128, None) == kvq.EINVAL
+    bad = _fake_struct(2, 2, 1024, 0, 2)
+    bad.k_slot_chan = None
+    assert L.kvq_quantize(P(bad), vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 0, 128, None) == kvq.EINVAL
+    bad = _fake_struct(2, 2, 1024, 4, 4)
+    bad.k_codes = FAKE + 4                                   # misaligned code buffer
+    assert L.kvq_quantize(P(bad), vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 0, 128, None) == kvq.EINVAL
+    # shrink
+    s2 = _fake_struct(2, 2, 1024, 4, 4)
+    assert L.kvq_shrink(P(s2), 4, None) == kvq.EINVAL        # 4 -> 4 is not a halving
+    assert L.kvq_shrink(P(s2), 1, None) == kvq.EINVAL        # 4 -> 1 skips a width
+    assert L.kvq_shrink(P(s2), 3, None) == kvq.EINVAL
+    sm = _fake_struct(1, 1, 1024, 0, 2)
+    assert L.kvq_shrink(P(sm), 1, None) == kvq.EUNSUPPORTED  # mixed keys
+    assert s2.k_bits == 4                                    # untouched on failure
+    # decode
+    s3 = _fake_struct(2, 2, 1024, 4, 4)
+    s3.n_tokens = 512
+    ws = L.kvq_decode_workspace_bytes(P(s3), 8)
+    assert L.kvq_decode_attn(P(s3), vp(FAKE), 8, 0.088, vp(FAKE), None, ws, None) == kvq.EWORKSPACE
+    assert L.kvq_decode_attn(P(s3), vp(FAKE), 8, 0.088, vp(FAKE), vp(FAKE), ws - 4, None) == kvq.EWORKSPACE
+    assert L.kvq_decode_attn(P(s3), vp(FAKE), 7, 0.088, vp(FAKE), vp(FAKE), ws, None) == kvq.EINVAL
+    assert L.kvq_decode_attn(P(s3), vp(FAKE), 2 * 17, 0.088, vp(FAKE), vp(FAKE), ws, None) == kvq.EUNSUPPORTED
+    assert L.kvq_decode_attn(P(s3), None, 8, 0.088, vp(FAKE), vp(FAKE), ws, None) == kvq.EINVAL
+    assert L.kvq_decode_attn(P(s3), vp(FAKE), 8, float("nan"), vp(FAKE), vp(FAKE), ws, None) == kvq.EINVAL
+    s4 = _fake_struct(2, 2, 1024, 4, 2)                      # K4/V2 is not built
+    s4.n_tokens = 512
+    assert L.kvq_decode_attn(P(s4), vp(FAKE), 8, 0.088, vp(FAKE), vp(FAKE), ws, None) == kvq.EUNSUPPORTED
+    s5 = _fake_struct(2, 2, 1024, 4, 4)                      # empty cache
+    assert L.kvq_decode_attn(P(s5), vp(FAKE), 8, 0.088, vp(FAKE), vp(FAKE), ws, None) == kvq.EINVAL
+
+
+def test_append_budget_rejected_before_work():
+    L = _lib()
+    st3 = (ctypes.c_int64 * 3)(0, 0, 128)
+    vp = ctypes.c_void_p
+    s = _fake_struct(8, 4, 32768, 16, 16)
+    s.n_tokens = 30720
+    s.k_bits = s.v_bits = 2
+    s.k_tile_stride = s.v_tile_stride = 2048 * 16
+    n = ctypes.c_int32(-1)
+    # 2-bit, floor 2: 30720 + 2048 tokens need 73.7 MiB > 70 MiB
+    r = L.kvq_append(ctypes.byref(s), None, 70 * 2 ** 20, 2, vp(FAKE), vp(FAKE), kvq.F32, st3, st3,
+                     2048, None, ctypes.byref(n))
+    assert r == kvq.EBUDGET and n.value == 0 and s.k_bits == 2 and s.n_tokens == 30720
+    # floor above the current width
+    s.k_bits = s.v_bits = 4
+    r = L.kvq_append(ctypes.byref(s), None, 1 << 40, 8, vp(FAKE), vp(FAKE), kvq.F32, st3, st3,
+                     128, None, None)
+    assert r == kvq.EINVAL

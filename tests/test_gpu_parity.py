@@ -1,0 +1,190 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Integer codes, packed bytes, scales/zeros and ERS output must be bit-exact;
+attention must agree within max relative error 2e-3 per output row
+(||o - o_ref||_inf / ||o_ref||_inf, float64 oracle).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_mixed_amd import kvq, synth
+from tests.gpu_helpers import (REL_TOL, SCALE, assert_stream_bytes_equal, oracle_attn,
+                               oracle_stream, q_to_dev, rel_err_rows, to_dev)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    oracle.build(force=False)
+    kvq.load()
+
+
+def _quantized(B, H, Hq, T, k_bits, v_bits, pdt, seed, mixed=False):
+    if mixed:
+        inp = synth.mixed_layer(B, H, Hq, T, seed)
+        slot_chan = inp["slot_chan"]
+    else:
+        inp = synth.layer(B, H, Hq, T, seed)
+        slot_chan = None
+    cache = kvq.PackedCache(B, H, T, k_bits, v_bits, pdt,
+                            slot_chan=slot_chan if mixed else None)
+    cache.quantize(to_dev(inp["k"], torch), to_dev(inp["v"], torch), 0)
+    torch.cuda.synchronize()
+    return inp, cache
+
+
+@pytest.mark.parametrize("bits", [16, 8, 4, 2, 1])
+@pytest.mark.parametrize("pdt", [kvq.F16, kvq.E4M3, kvq.BF16, kvq.F32])
+def test_quantize_bitexact(bits, pdt):
+    print("case quantize bits=%d pdt=%d" % (bits, pdt), flush=True)
+    inp, cache = _quantized(2, 2, 4, 384, bits, bits, pdt, seed=10 + bits + 17 * pdt)
+    for b in range(2):
+        for h in range(2):
+            st = oracle_stream(inp, b, h, bits, bits, pdt)
+            assert_stream_bytes_equal(cache, st, b, h, "bits=%d pdt=%d" % (bits, pdt))
+
+
+@pytest.mark.parametrize("pdt", [kvq.F16, kvq.E4M3])
+def test_quantize_mixed_bitexact(pdt):
+    print("case quantize mixed pdt=%d" % pdt, flush=True)
+    inp, cache = _quantized(1, 3, 6, 512, kvq.KMIXED, 2, pdt, seed=5, mixed=True)
+    for h in range(3):
+        st = oracle_stream(inp, 0, h, 0, 2, pdt, inp["slot_chan"][h])
+        assert_stream_bytes_equal(cache, st, 0, h, "mixed pdt=%d" % pdt)
+
+
+def test_quantize_bf16_input_and_offset_t0():
+    """bfloat16 inputs, quantizing into a later tile range with strided input."""
+    inp = synth.layer(1, 2, 2, 512, 77)
+    kb = torch.from_numpy(inp["k"]).to(torch.bfloat16)
+    vb = torch.from_numpy(inp["v"]).to(torch.bfloat16)
+    cache = kvq.PackedCache(1, 2, 1024, 4, 4, kvq.F16)
+    big_k = torch.zeros(1, 2, 640, 128, dtype=torch.bfloat16)
+    big_k[:, :, 64:576] = kb
+    kd = big_k.cuda()[:, :, 64:576]                 # non-contiguous view, stride(2) = 128
+    cache.quantize(kd, vb.cuda(), t0=256)
+    cache.quantize(kd[:, :, :256], vb.cuda()[:, :, :256], t0=0)
+    torch.cuda.synchronize()
+    assert cache.n_tokens == 768
+    kf = np.concatenate([kb.float().numpy()[:, :, :256], kb.float().numpy()], axis=2)
+    vf = np.concatenate([vb.float().numpy()[:, :, :256], vb.float().numpy()], axis=2)
+    for h in range(2):
+        st = oracle.quantize_stream(kf[0, h], vf[0, h], 4, 4, oracle.F16)
+        assert_stream_bytes_equal(cache, st, 0, h, "bf16 input")
+
+
+@pytest.mark.parametrize("to_bits", [8, 4, 2, 1])
+@pytest.mark.parametrize("pdt", [kvq.F16, kvq.E4M3])
+def test_shrink_bitexact(to_bits, pdt):
+    print("case shrink to=%d pdt=%d" % (to_bits, pdt), flush=True)
+    inp, cache = _quantized(2, 2, 4, 384, 2 * to_bits, 2 * to_bits, pdt, seed=30 + to_bits)
+    cache.shrink(to_bits)
+    torch.cuda.synchronize()
+    assert cache.k_bits == to_bits and cache.v_bits == to_bits
+    for b in range(2):
+        for h in range(2):
+            st = oracle.shrink_stream(oracle_stream(inp, b, h, 2 * to_bits, 2 * to_bits, pdt), to_bits)
+            assert_stream_bytes_equal(cache, st, b, h, "shrink to %d" % to_bits)
+
+
+def _decode_case(B, H, Hq, T, k_bits, v_bits, pdt, seed, mixed=False, pairs=None):
+    inp, cache = _quantized(B, H, Hq, T, k_bits, v_bits, pdt, seed, mixed)
+    q = q_to_dev(inp["q_bf16"], torch)
+    out = cache.decode_attn(q, SCALE).cpu().numpy()
+    G = Hq // H
+    worst = 0.0
+    for (b, h) in (pairs or [(b, h) for b in range(B) for h in range(H)]):
+        st = oracle_stream(inp, b, h, k_bits, v_bits, pdt,
+                           inp["slot_chan"][h] if mixed else None)
+        ref = oracle_attn(st, inp["q_bf16"][b, h * G:(h + 1) * G])
+        err = rel_err_rows(out[b, h * G:(h + 1) * G], ref).max()
+        worst = max(worst, err)
+    assert np.all(np.isfinite(out))
+    assert worst <= REL_TOL, "max row relative error %.3e" % worst
+    return worst
+
+
+@pytest.mark.parametrize("bits", [4, 2, 8, 1, 16])
+@pytest.mark.parametrize("pdt", [kvq.F16, kvq.E4M3])
+def test_decode_uniform(bits, pdt):
+    print("case decode bits=%d pdt=%d" % (bits, pdt), flush=True)
+    _decode_case(2, 2, 14, 1152, bits, bits, pdt, seed=40 + bits)
+
+
+@pytest.mark.parametrize("v_bits", [2, 4, 1])
+def test_decode_mixed(v_bits):
+    print("case decode mixed v=%d" % v_bits, flush=True)
+    _decode_case(1, 2, 8, 1280, kvq.KMIXED, v_bits, kvq.E4M3, seed=60 + v_bits, mixed=True)
+
+
+@pytest.mark.parametrize("G", [1, 5, 16])
+def test_decode_group_sizes(G):
+    print("case decode G=%d" % G, flush=True)
+    _decode_case(1, 2, 2 * G, 640, 4, 4, kvq.F16, seed=70 + G)
+
+
+@pytest.mark.parametrize("T", [128, 384, 8192])
+def test_decode_lengths(T):
+    """one tile, a ragged chunk (fewer tiles than waves), many chunks."""
+    print("case decode T=%d" % T, flush=True)
+    _decode_case(2, 1, 4, T, 4, 4, kvq.F16, seed=80 + T // 128)
+
+
+@pytest.mark.parametrize("pdt", [kvq.BF16, kvq.F32])
+def test_decode_other_param_dtypes(pdt):
+    _decode_case(1, 2, 8, 512, 4, 4, pdt, seed=90 + pdt)
+
+
+def test_decode_repeat_and_workspace_reuse():
+    """The workspace counters reset themselves: repeated calls give identical output."""
+    inp, cache = _quantized(2, 2, 8, 4096, 4, 4, kvq.F16, seed=95)
+    q = q_to_dev(inp["q_bf16"], torch)
+    o1 = cache.decode_attn(q, SCALE).cpu().numpy()
+    o2 = cache.decode_attn(q, SCALE).cpu().numpy()
+    o3 = cache.decode_attn(q, SCALE).cpu().numpy()
+    assert np.array_equal(o1, o2) and np.array_equal(o2, o3)
+    ws = cache.workspace(8)
+    n_counters = 2 * 2
+    assert int(ws[:4 * n_counters].view(torch.int32).abs().sum().item()) == 0
+
+
+def test_tiny_config():
+    """1 kv head, 1 query head, 512 tokens: 4-bit quantize, ERS 4->2, decode on both."""
+    inp = synth.tiny(0)
+    cache = kvq.PackedCache(1, 1, 512, 4, 4, kvq.F16)
+    cache.quantize(to_dev(inp["k"], torch), to_dev(inp["v"], torch))
+    q = q_to_dev(inp["q_bf16"], torch)
+    o4 = cache.decode_attn(q, SCALE).cpu().numpy()
+    st4 = oracle_stream(inp, 0, 0, 4, 4, kvq.F16)
+    assert_stream_bytes_equal(cache, st4, 0, 0, "tiny 4-bit")
+    assert rel_err_rows(o4[0], oracle_attn(st4, inp["q_bf16"][0])).max() <= REL_TOL
+    cache.shrink(2)
+    o2 = cache.decode_attn(q, SCALE).cpu().numpy()
+    st2 = oracle.shrink_stream(st4, 2)
+    assert_stream_bytes_equal(cache, st2, 0, 0, "tiny 2-bit")
+    assert rel_err_rows(o2[0], oracle_attn(st2, inp["q_bf16"][0])).max() <= REL_TOL
+
+
+def test_pool_layout_decode():
+    """Tiles placed through a kvq_pool (offset tables) decode like the contiguous layout."""
+    B, H, Hq, T = 2, 2, 8, 1024
+    inp = synth.layer(B, H, Hq, T, 99)
+    pool_bytes = B * H * (T // 128) * 2 * 2048 * 4
+    cache = kvq.PackedCache(B, H, T, 4, 4, kvq.F16, layout="pool", pool_bytes=pool_bytes)
+    kd, vd = to_dev(inp["k"], torch), to_dev(inp["v"], torch)
+    for t0 in range(0, T, 256):
+        cache.append(kd[:, :, t0:t0 + 256], vd[:, :, t0:t0 + 256], budget_bytes=1 << 40,
+                     floor_bits=4)
+    torch.cuda.synchronize()
+    for b in range(B):
+        for h in range(H):
+            assert_stream_bytes_equal(cache, oracle_stream(inp, b, h, 4, 4, kvq.F16), b, h, "pool")
+    out = cache.decode_attn(q_to_dev(inp["q_bf16"], torch), SCALE).cpu().numpy()
+    G = Hq // H
+    for b in range(B):
+        for h in range(H):
+            ref = oracle_attn(oracle_stream(inp, b, h, 4, 4, kvq.F16), inp["q_bf16"][b, h * G:(h + 1) * G])
+            assert rel_err_rows(out[b, h * G:(h + 1) * G], ref).max() <= REL_TOL
