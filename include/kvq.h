@@ -26,7 +26,8 @@
  *
  * ------------------------------------------------------------------------
  * The quantizer ([CHANMIX] Key design 1; [PMKVQ] Training strategy)
- *   A group is a set of real values x.  With mn = min x, mx = max x:
+ *   A group is a set of real values x.  With mn = min x, mx = max x (a zero
+ *   extreme is +0 whatever the signs of the zeros in the group):
  *     S  = (mx - mn) / (2^b - 1)      (binary32: one subtraction, one division)
  *     S' = narrow(S),  Z' = narrow(mn)   (round to nearest even to the
  *                                         parameter dtype; e4m3 saturates)
@@ -53,8 +54,13 @@
  *
  *   Key tile, uniform width b (2048*b bytes): 128 rows of 16*b bytes; row t is
  *     token 128g + t, element c is channel c.
- *   Value tile, width b (2048*b bytes): 128 rows of 16*b bytes; row c is
- *     channel c, element t is token 128g + t.
+ *   Value tile, width b (2048*b bytes): 32-bit little-endian words W[w][c][a]
+ *     for w in [0, b), c in [0, 128), a in [0, 4), a varying fastest (word
+ *     index (w * 128 + c) * 4 + a).  Word W[w][c][a] holds channel c of the
+ *     32/b tokens 128g + 32a + w*(32/b) + i, i = 0 .. 32/b - 1, code i at bits
+ *     [i*b, i*b + b).  (At b = 1 these are channel rows of 16 bytes; wider
+ *     codes split every channel's 128 tokens into b word planes, so the words
+ *     holding one token slice are contiguous across all channels.)
  *   Key tile, mixed width (k_bits == KVQ_KMIXED, 4352 bytes) ([CHANMIX] Key
  *     design 3: 4/3/2/1-bit channel classes, as many 1-bit as 3-bit channels,
  *     channels reordered so every byte holds exactly 8 code bits):
@@ -74,7 +80,8 @@
  *   (same for values) with max_tiles = max_tokens / 128.  Offsets and strides
  *   are multiples of 256 bytes; a stride is at least the current tile size.
  *   kvq_shrink rewrites every tile in place: the narrower tile occupies the
- *   first half of the bytes the wider one used, at the same offset.
+ *   first half of the bytes the wider one used, at the same offset (key codes
+ *   keep their order; value codes move to the word planes of the new width).
  *
  *   Parameters (S', Z' raw values of param_dtype):
  *     k_scale, k_zero: [batch][n_kv_heads][max_tiles][128]  (per tile, per slot;

@@ -107,9 +107,17 @@ __device__ __forceinline__ float wave_sum16x4(float v) {
 template <int PDT>
 __device__ __forceinline__ void load_params8(const void* base, int64_t e, float* out) {
   if constexpr (PDT == KVQ_E4M3) {
+    // v_cvt_f32_fp8 converts OCP E4M3 on gfx950 (exact: every e4m3 value is a
+    // binary32 value)
     const u32x2 v = *(const u32x2*)((const uint8_t*)base + e);
-#pragma unroll
-    for (int i = 0; i < 8; i++) out[i] = e4m3_bits_to_f32((v[i / 4] >> (8 * (i % 4))) & 0xffu);
+    out[0] = __builtin_amdgcn_cvt_f32_fp8((int)v[0], 0);
+    out[1] = __builtin_amdgcn_cvt_f32_fp8((int)v[0], 1);
+    out[2] = __builtin_amdgcn_cvt_f32_fp8((int)v[0], 2);
+    out[3] = __builtin_amdgcn_cvt_f32_fp8((int)v[0], 3);
+    out[4] = __builtin_amdgcn_cvt_f32_fp8((int)v[1], 0);
+    out[5] = __builtin_amdgcn_cvt_f32_fp8((int)v[1], 1);
+    out[6] = __builtin_amdgcn_cvt_f32_fp8((int)v[1], 2);
+    out[7] = __builtin_amdgcn_cvt_f32_fp8((int)v[1], 3);
   } else if constexpr (PDT == KVQ_F32) {
     const u32x4 a = *(const u32x4*)((const float*)base + e);
     const u32x4 b = *(const u32x4*)((const float*)base + e + 4);
@@ -130,7 +138,8 @@ struct DecodeArgs {
   Geo g;
   const uint16_t* q;  // bf16 [B][Hq][128]
   float* out;         // [B][Hq][128]
-  float* part;        // [BH][n_chunks][G][130]
+  float* part_ml;     // [BH][n_chunks][G][2]   (running max in log2 units, sum)
+  float* part_o;      // [BH][n_chunks][G][128] (unnormalised output)
   uint32_t* counters; // [n_groups]
   int G, n_chunks, tpc, n_groups;
   float sl2;          // softmax_scale * log2(e)
@@ -180,7 +189,6 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   constexpr int KH = (KB == 16) ? 4 : 12;            // headroom exponents (f16 range)
   constexpr int VH = (VB == 16) ? 4 : 12;
   constexpr int ROW_K = MIXED ? 8 : 16 * KB;
-  constexpr int ROW_V = 16 * VB;
   static_assert(KSV >= 1 && WVS >= 1, "sub-tile must hold whole value k-steps");
 
   const Geo& g = a.g;
@@ -243,17 +251,21 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     uint32_t bkh[NFK], bkl[NFK];
     float ak = 0.0f, bk0 = 0.0f;
     {
+      // every lane loads (fake lanes read stream (0, 0), always in bounds) and
+      // fake lanes zero the values: no divergent branch around the loads
       float ks[32], kz[32];
-      if (real) {
+      {
         const int64_t kpb = k_param_base(g, b_own, h_own, tile);
 #pragma unroll
         for (int s = 0; s < 4; s++) {
           load_params8<PDT>(g.k_scale, kpb + kseg[s], ks + 8 * s);
           load_params8<PDT>(g.k_zero, kpb + kseg[s], kz + 8 * s);
         }
-      } else {
 #pragma unroll
-        for (int li = 0; li < 32; li++) { ks[li] = 0.0f; kz[li] = 0.0f; }
+        for (int li = 0; li < 32; li++) {
+          ks[li] = real ? ks[li] : 0.0f;
+          kz[li] = real ? kz[li] : 0.0f;
+        }
       }
       float smax = 0.0f, beta = 0.0f;
 #pragma unroll
@@ -281,18 +293,26 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
       }
     }
 
+    const uint8_t* ktile[NS];
+    const uint8_t* vtile[NS];
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+      const int bh = min(grp * NS + s, BH - 1);
+      const int bs = bh / g.H, hs = bh % g.H;
+      ktile[s] = g.k_codes + k_tile_offset(g, bs, hs, tile);
+      vtile[s] = g.v_codes + v_tile_offset(g, bs, hs, tile);
+    }
 #pragma unroll 1
     for (int sub = 0; sub < NSUB; sub++) {
-      // ---- raw loads of every stream's key blocks and value rows of this sub-tile
+      // ---- raw loads of every stream's key blocks and value words of this sub-tile
       uint32_t kw[NS][JB][NWK];
       uint32_t vw[NS][8][WVS];
 #pragma unroll
       for (int s = 0; s < NS; s++) {
         const int bh = grp * NS + s;
         if (bh >= BH) continue;
-        const int bs = bh / g.H, hs = bh % g.H;
-        const uint8_t* kt = g.k_codes + k_tile_offset(g, bs, hs, tile);
-        const uint8_t* vt = g.v_codes + v_tile_offset(g, bs, hs, tile);
+        const uint8_t* kt = ktile[s];
+        const uint8_t* vt = vtile[s];
 #pragma unroll
         for (int jj = 0; jj < JB; jj++) {
           const int j = sub * JB + jj;
@@ -326,35 +346,28 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
             }
           }
         }
+        // value word planes: word (w, c, a) at ((w*128 + c)*4 + a); the 64
+        // lanes read 256 contiguous bytes per (plane, channel block)
 #pragma unroll
-        for (int cb = 0; cb < 8; cb++) {
-          const uint32_t* src = (const uint32_t*)(vt + (16 * cb + n) * ROW_V + 4 * VB * lg) + sub * WVS;
-          if constexpr (WVS >= 4) {
+        for (int cb = 0; cb < 8; cb++)
 #pragma unroll
-            for (int w = 0; w < WVS; w += 4) {
-              const u32x4 v = *(const u32x4*)(src + w);
-              vw[s][cb][w] = v[0]; vw[s][cb][w + 1] = v[1]; vw[s][cb][w + 2] = v[2]; vw[s][cb][w + 3] = v[3];
-            }
-          } else if constexpr (WVS == 2) {
-            const u32x2 v = *(const u32x2*)src;
-            vw[s][cb][0] = v[0]; vw[s][cb][1] = v[1];
-          } else {
-            vw[s][cb][0] = src[0];
-          }
-        }
+          for (int w = 0; w < WVS; w++)
+            vw[s][cb][w] = ((const uint32_t*)vt)[((sub * WVS + w) * 128 + 16 * cb + n) * 4 + lg];
       }
       // own stream's value scales / zeros for the lane's TPS tokens of this sub-tile
       float vs[TPS], vz[TPS];
-      if (real) {
+      {
         const int64_t vpb = v_param_base(g, b_own, h_own, (int64_t)tile * 128) + 32 * lg + sub * TPS;
 #pragma unroll
         for (int s8 = 0; s8 < TPS / 8; s8++) {
           load_params8<PDT>(g.v_scale, vpb + 8 * s8, vs + 8 * s8);
           load_params8<PDT>(g.v_zero, vpb + 8 * s8, vz + 8 * s8);
         }
-      } else {
 #pragma unroll
-        for (int i = 0; i < TPS; i++) { vs[i] = 0.0f; vz[i] = 0.0f; }
+        for (int i = 0; i < TPS; i++) {
+          vs[i] = real ? vs[i] : 0.0f;
+          vz[i] = real ? vz[i] : 0.0f;
+        }
       }
 
       // ---- logits (log2 domain) of the lane's column for JB blocks of 16 tokens
@@ -478,8 +491,9 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   __syncthreads();
 
   const int Hq = g.H * G;
+  const int ncol = NS * G;
   const bool single = (a.n_chunks == 1);
-  for (int idx = threadIdx.x; idx < NS * G * 128; idx += 256) {
+  for (int idx = threadIdx.x; idx < ncol * 128; idx += 256) {
     const int col = idx >> 7, c = idx & 127;
     const int s = col / G, hh = col - s * G;
     const int bh = grp * NS + s;
@@ -499,15 +513,20 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
     if (single) {
       a.out[((int64_t)bo * Hq + (int64_t)ho * G + hh) * 128 + c] = num / den;
     } else {
-      float* pp = a.part + (((int64_t)bh * a.n_chunks + chunk) * G + hh) * 130;
-      if (c == 0) { pp[0] = M; pp[1] = den; }
-      pp[2 + c] = num;
+      const int64_t row = ((int64_t)bh * a.n_chunks + chunk) * G + hh;
+      if (c == 0) { a.part_ml[2 * row] = M; a.part_ml[2 * row + 1] = den; }
+      a.part_o[row * 128 + c] = num;
     }
   }
   if (single) return;
 
-  // ---- last workgroup of the stream group combines all chunks
+  // ---- the last workgroup of the stream group combines all chunks:
+  //   o = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k
+  // All loads of a phase are independent and coalesced, so the combine costs
+  // a few memory round trips, not one per chunk.
   __shared__ int s_last;
+  __shared__ float s_w[KVQ_MAX_CHUNKS][16];
+  __shared__ float s_red[16][16];
   __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -517,24 +536,67 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   __syncthreads();
   if (!s_last) return;
   __threadfence();
-  for (int idx = threadIdx.x; idx < NS * G * 128; idx += 256) {
-    const int col = idx >> 7, c = idx & 127;
+  const int nck = a.n_chunks;
+  // phase 1: chunk maxima -> per-column maximum
+  for (int idx = threadIdx.x; idx < nck * ncol; idx += 256) {
+    const int k = idx / ncol, col = idx - k * ncol;
+    const int s = col / G, hh = col - s * G;
+    const int bh = grp * NS + s;
+    s_w[k][col] = (bh < BH) ? __builtin_nontemporal_load(a.part_ml + 2 * (((int64_t)bh * nck + k) * G + hh))
+                            : 0.0f;
+  }
+  __syncthreads();
+  {
+    const int col = threadIdx.x >> 4, part = threadIdx.x & 15;
+    float M = -INFINITY;
+    if (col < ncol)
+      for (int k = part; k < nck; k += 16) M = fmaxf(M, s_w[k][col]);
+    s_red[col][part] = M;
+  }
+  __syncthreads();
+  // phase 2: weights 2^(m_k - M) and the denominator
+  if (threadIdx.x < 16) {
+    float M = -INFINITY;
+    for (int i = 0; i < 16; i++) M = fmaxf(M, s_red[threadIdx.x][i]);
+    s_red[threadIdx.x][0] = M;
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < nck * ncol; idx += 256) {
+    const int k = idx / ncol, col = idx - k * ncol;
+    s_w[k][col] = exp2f(s_w[k][col] - s_red[col][0]);
+  }
+  __syncthreads();
+  {
+    const int col = threadIdx.x >> 4, part = threadIdx.x & 15;
+    float den = 0.0f;
+    if (col < ncol) {
+      const int s = col / G, hh = col - s * G;
+      const int bh = grp * NS + s;
+      if (bh < BH)
+        for (int k = part; k < nck; k += 16)
+          den += s_w[k][col] * __builtin_nontemporal_load(a.part_ml + 2 * (((int64_t)bh * nck + k) * G + hh) + 1);
+    }
+    for (int o = 8; o >= 1; o >>= 1) den += __shfl_xor(den, o, 16);
+    if (part == 0 && col < ncol) s_red[col][1] = den;
+  }
+  __syncthreads();
+  // phase 3: weighted sum of the chunk outputs, 4 channels per thread
+  for (int idx = threadIdx.x; idx < ncol * 32; idx += 256) {
+    const int col = idx >> 5, c4 = (idx & 31) * 4;
     const int s = col / G, hh = col - s * G;
     const int bh = grp * NS + s;
     if (bh >= BH) continue;
-    const float* pp0 = a.part + ((int64_t)bh * a.n_chunks * G + hh) * 130;
-    const int64_t cs = (int64_t)G * 130;
-    float M = -INFINITY;
-    for (int k = 0; k < a.n_chunks; k++) M = fmaxf(M, __builtin_nontemporal_load(pp0 + k * cs));
-    float num = 0.0f, den = 0.0f;
-    for (int k = 0; k < a.n_chunks; k++) {
-      const float* pp = pp0 + k * cs;
-      const float w = exp2f(__builtin_nontemporal_load(pp) - M);
-      num += w * __builtin_nontemporal_load(pp + 2 + c);
-      den += w * __builtin_nontemporal_load(pp + 1);
+    const float* po = a.part_o + (((int64_t)bh * nck) * G + hh) * 128 + c4;
+    const int64_t ks = (int64_t)G * 128;
+    f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int k = 0; k < nck; k++) {
+      const f32x4 v = __builtin_nontemporal_load((const f32x4*)(po + k * ks));
+      acc += s_w[k][col] * v;
     }
+    const float inv = 1.0f / s_red[col][1];
     const int bo = bh / g.H, ho = bh % g.H;
-    a.out[((int64_t)bo * Hq + (int64_t)ho * G + hh) * 128 + c] = num / den;
+    *(f32x4*)(a.out + ((int64_t)bo * Hq + (int64_t)ho * G + hh) * 128 + c4) = acc * inv;
   }
   if (threadIdx.x == 0) a.counters[grp] = 0u;
 }
@@ -544,33 +606,51 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 // kv streams per wave: as many query groups as fit the 16 MFMA columns,
 // capped per width so the kernel keeps two waves per SIMD without spilling.
-template <int KB, int VB>
-constexpr int ns_cap() {
-  return (KB == 16 || VB == 16 || KB == 1 || VB == 1) ? 1 : (KB == 4 ? 3 : 2);
-}
-static int streams_per_wave(int G, int cap) {
-  const int ns = 16 / G;
-  return ns > cap ? cap : (ns < 1 ? 1 : ns);
+constexpr int ns_cap(int kb, int vb) {
+  return (kb == 16 || vb == 16 || kb == 1 || vb == 1) ? 1 : (kb == 4 ? 3 : 2);
 }
 
-int decode_chunks(int n_groups, int n_tiles) {
-  // aim for ~1536 workgroups (6 per CU on 256 CUs), 4..64 tiles per chunk
-  const long total = (long)n_groups * n_tiles;
-  int tpc = (int)((total + 1535) / 1536);
+// Launch plan (shared by workspace sizing, validation and launch): NS streams
+// per wave, n_groups = ceil(BH / NS) stream groups, and the token tiles of a
+// group cut into n_chunks chunks of tpc tiles, aiming at about 512 workgroups
+// (two per CU, the register-limited residency) with 4..64 tiles per chunk and
+// at most KVQ_MAX_CHUNKS chunks.
+DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int n_tiles) {
+  DecodePlan p;
+  const int cap = ns_cap(k_bits, v_bits);
+  int ns = 16 / G;
+  p.ns = ns > cap ? cap : (ns < 1 ? 1 : ns);
+  p.n_groups = (BH + p.ns - 1) / p.ns;
+  const long total = (long)p.n_groups * n_tiles;
+  int tpc = (int)((total + 511) / 512);
   tpc = ((tpc + 3) / 4) * 4;
   if (tpc < 4) tpc = 4;
   if (tpc > 64) tpc = 64;
-  return (n_tiles + tpc - 1) / tpc;
+  const int tmin = (n_tiles + KVQ_MAX_CHUNKS - 1) / KVQ_MAX_CHUNKS;
+  if (tpc < tmin) tpc = tmin;
+  p.n_chunks = (n_tiles + tpc - 1) / tpc;
+  p.tpc = (n_tiles + p.n_chunks - 1) / p.n_chunks;   // balanced, every chunk non-empty
+  return p;
 }
 
 static size_t counters_bytes(int BH) { return ((size_t)BH * 4 + 255) / 256 * 256; }
+static size_t ml_bytes(int BH, int n_chunks, int G) {
+  return ((size_t)BH * n_chunks * G * 2 * 4 + 255) / 256 * 256;
+}
+
+size_t decode_workspace_needed(int BH, int G, const DecodePlan& p) {
+  return counters_bytes(BH) + ml_bytes(BH, p.n_chunks, G) + (size_t)BH * p.n_chunks * G * 128 * 4;
+}
 
 size_t decode_workspace_bytes(int B, int H, int G, int max_tiles) {
-  // sized for every packing and every n_tokens <= max_tokens: the chunk count
-  // only grows with n_tiles and is largest for one stream per group
+  // upper bound over every n_tokens <= max_tokens and every packing: a chunk
+  // holds at least 4 tiles and there are at most KVQ_MAX_CHUNKS of them
   const int BH = B * H;
-  const size_t part = (size_t)BH * decode_chunks(BH, max_tiles) * G * 130 * 4;
-  return counters_bytes(BH) + part;
+  int nc = (max_tiles + 3) / 4;
+  if (nc > KVQ_MAX_CHUNKS) nc = KVQ_MAX_CHUNKS;
+  DecodePlan p;
+  p.n_chunks = nc;
+  return decode_workspace_needed(BH, G, p);
 }
 
 bool decode_supported(int k_bits, int v_bits, int pdt) {
@@ -581,17 +661,16 @@ bool decode_supported(int k_bits, int v_bits, int pdt) {
 
 template <int KB, int VB, int PDT>
 static hipError_t launch_ns(const DecodeArgs& a0, hipStream_t st) {
-  constexpr int CAP = ns_cap<KB, VB>();
+  constexpr int CAP = ns_cap(KB, VB);
   DecodeArgs a = a0;
-  const int ns = streams_per_wave(a.G, CAP);
-  const int BH = a.g.B * a.g.H;
-  a.n_groups = (BH + ns - 1) / ns;
-  a.n_chunks = decode_chunks(a.n_groups, a.g.n_tiles);
-  a.tpc = (a.g.n_tiles + a.n_chunks - 1) / a.n_chunks;
+  const DecodePlan p = decode_plan(a.g.B * a.g.H, a.G, KB, VB, a.g.n_tiles);
+  a.n_groups = p.n_groups;
+  a.n_chunks = p.n_chunks;
+  a.tpc = p.tpc;
   const dim3 grid(a.n_chunks, a.n_groups), block(256);
-  if (ns == 1) {
+  if (p.ns == 1) {
     hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 1>), grid, block, 0, st, a);
-  } else if (ns == 2) {
+  } else if (p.ns == 2) {
     if constexpr (CAP >= 2) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 2>), grid, block, 0, st, a);
   } else {
     if constexpr (CAP >= 3) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 3>), grid, block, 0, st, a);
@@ -617,8 +696,10 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
   a.q = (const uint16_t*)q;
   a.out = out;
   const int BH = g.B * g.H;
+  const DecodePlan p = decode_plan(BH, G, g.k_bits, g.v_bits, g.n_tiles);
   a.counters = (uint32_t*)ws;
-  a.part = (float*)((uint8_t*)ws + counters_bytes(BH));
+  a.part_ml = (float*)((uint8_t*)ws + counters_bytes(BH));
+  a.part_o = (float*)((uint8_t*)a.part_ml + ml_bytes(BH, p.n_chunks, G));
   a.G = G;
   a.sl2 = scale * 1.4426950408889634f;
   a.n_chunks = a.tpc = a.n_groups = 0;

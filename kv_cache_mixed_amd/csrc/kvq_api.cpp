@@ -179,6 +179,13 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t n_q_heads,
     if ((int64_t)c->batch * c->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
     const size_t need = kvq::decode_workspace_bytes(c->batch, c->n_kv_heads, G, c->max_tokens / 128);
     if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return KVQ_EWORKSPACE;
+    // the plan of this call must fit the workspace (guaranteed by the bound
+    // above; checked so a sizing mistake can never turn into stray writes)
+    const kvq::DecodePlan plan = kvq::decode_plan(c->batch * c->n_kv_heads, G, c->k_bits, c->v_bits,
+                                                  c->n_tokens / 128);
+    if (kvq::decode_workspace_needed(c->batch * c->n_kv_heads, G, plan) > workspace_bytes ||
+        plan.n_chunks > kvq::KVQ_MAX_CHUNKS || plan.n_chunks * plan.tpc < c->n_tokens / 128)
+      return KVQ_EWORKSPACE;
     kvq::Geo g = make_geo(c);
     hipError_t e = kvq::launch_decode(g, q, G, softmax_scale, out, workspace, stream);
     return e == hipSuccess ? KVQ_OK : KVQ_EHIP;

@@ -205,7 +205,12 @@ hipError_t launch_quantize(const Geo& g, const void* k, const void* v, int in_dt
                            const int64_t* ks, const int64_t* vs, int t0, int n_new,
                            hipStream_t st);
 hipError_t launch_shrink(const Geo& g, int to_bits, hipStream_t st);
-int decode_chunks(int n_groups, int n_tiles);
+constexpr int KVQ_MAX_CHUNKS = 128;
+struct DecodePlan {
+  int ns, n_groups, n_chunks, tpc;
+};
+DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int n_tiles);
+size_t decode_workspace_needed(int BH, int G, const DecodePlan& p);
 size_t decode_workspace_bytes(int B, int H, int G, int max_tiles);
 hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float* out,
                          void* ws, hipStream_t st);

@@ -56,6 +56,23 @@ __device__ __forceinline__ void pack_rows_store(const uint16_t* codes, uint8_t* 
   }
 }
 
+// Value tile: codes[c][t] (LDS, pitch PITCH) -> 32-bit words W[w][c][a]
+// (word index (w*128 + c)*4 + a) holding channel c of tokens
+// 32a + w*(32/BITS) + i, code i at bits [i*BITS, (i+1)*BITS).
+template <int BITS, int PITCH>
+__device__ __forceinline__ void pack_vtile_store(const uint16_t* codes, uint8_t* tile) {
+  constexpr int PER_WORD = 32 / BITS;
+  uint32_t* out = (uint32_t*)tile;
+  for (int idx = threadIdx.x; idx < 512 * BITS; idx += blockDim.x) {
+    const int w = idx >> 9, c = (idx >> 2) & 127, a = idx & 3;
+    const uint16_t* src = codes + c * PITCH + 32 * a + w * PER_WORD;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < PER_WORD; i++) word |= (uint32_t)src[i] << (i * BITS);
+    out[idx] = word;
+  }
+}
+
 // Mixed key tile: codes[t][slot]; five planes (see include/kvq.h).
 __device__ __forceinline__ void pack_mixed_store(const uint16_t* codes, uint8_t* tile) {
   // planes 0..3: 8 bytes per token = 2 words; 1024 words in total
@@ -120,6 +137,8 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __re
   __syncthreads();
   mn = red_mn[0][j] < red_mn[1][j] ? red_mn[0][j] : red_mn[1][j];
   mx = red_mx[0][j] > red_mx[1][j] ? red_mx[0][j] : red_mx[1][j];
+  mn = mn + 0.0f;   // -0 and +0 are one value: keep +0 whatever the reduction order
+  mx = mx + 0.0f;
   const float levels = (float)((1u << bits) - 1u);
   const float s = (mx - mn) / levels;
   const float sp = Param<PDT>::narrow(s);
@@ -139,11 +158,32 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __re
 }
 
 // ---------------------------------------------------------------------------
-// Values: wave w handles tokens [32w, 32w+32) of the tile, one token at a time;
-// lane l holds channels 2l, 2l+1.  Codes are stored transposed ([c][t]) and
-// packed as channel rows.
+// Values: wave w handles tokens [32w, 32w+32) of the tile.  Lanes 0..31 and
+// 32..63 each hold one token per load (lane l32 holds channels 4*l32..+3), so
+// one load instruction covers two whole token rows; all 16 loads of a wave are
+// issued before any reduction.  The min/max of a token is reduced inside its
+// 32-lane half.  Codes are staged transposed ([c][t]) and packed into the
+// value word planes.  VEC: the input allows 16-byte (F32) / 8-byte (BF16)
+// loads of 4 channels.
 // ---------------------------------------------------------------------------
-template <int VB, int PDT, int IN>
+template <int IN, bool VEC>
+__device__ __forceinline__ void load4(const void* p, int64_t i, float* x) {
+  if constexpr (VEC && IN == KVQ_F32) {
+    typedef float f4 __attribute__((ext_vector_type(4)));
+    const f4 v = *(const f4*)((const float*)p + i);
+    x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
+  } else if constexpr (VEC && IN == KVQ_BF16) {
+    typedef uint32_t u2 __attribute__((ext_vector_type(2)));
+    const u2 v = *(const u2*)((const uint16_t*)p + i);
+    x[0] = bf16_bits_to_f32(v[0] & 0xffffu); x[1] = bf16_bits_to_f32(v[0] >> 16);
+    x[2] = bf16_bits_to_f32(v[1] & 0xffffu); x[3] = bf16_bits_to_f32(v[1] >> 16);
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; k++) x[k] = load_in<IN>(p, i + k);
+  }
+}
+
+template <int VB, int PDT, int IN, bool VEC>
 __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __restrict__ vin,
                                                          int64_t sb, int64_t sh, int64_t st,
                                                          int t0) {
@@ -152,32 +192,40 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __re
   const int tile_local = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tile = t0 / 128 + tile_local;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int half = lane >> 5, l32 = lane & 31;
   const float levels = (float)((1u << VB) - 1u);
-  for (int i = 0; i < 32; i++) {
-    const int t = wave * 32 + i;
-    const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (int64_t)(tile_local * 128 + t) * st;
-    const float x0 = load_in<IN>(vin, base + 2 * lane);
-    const float x1 = load_in<IN>(vin, base + 2 * lane + 1);
-    float mn = x0 < x1 ? x0 : x1, mx = x0 > x1 ? x0 : x1;
+  const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (int64_t)(tile_local * 128) * st + 4 * l32;
+  float x[16][4];
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      const float a = __shfl_xor(mn, o, 64), c = __shfl_xor(mx, o, 64);
-      mn = a < mn ? a : mn;
-      mx = c > mx ? c : mx;
+  for (int i = 0; i < 16; i++) {
+    const int t = wave * 32 + 2 * i + half;
+    load4<IN, VEC>(vin, base + (int64_t)t * st, x[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 16; i++) {
+    const int t = wave * 32 + 2 * i + half;
+    float mn = fminf(fminf(x[i][0], x[i][1]), fminf(x[i][2], x[i][3]));
+    float mx = fmaxf(fmaxf(x[i][0], x[i][1]), fmaxf(x[i][2], x[i][3]));
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) {
+      mn = fminf(mn, __shfl_xor(mn, o, 32));
+      mx = fmaxf(mx, __shfl_xor(mx, o, 32));
     }
+    mn = mn + 0.0f;   // -0 and +0 are one value: keep +0 whatever the reduction order
+    mx = mx + 0.0f;
     const float s = (mx - mn) / levels;
     const float sp = Param<PDT>::narrow(s);
     const float zp = Param<PDT>::narrow(mn);
-    if (lane == 0) {
+    if (l32 == 0) {
       const int64_t pi = v_param_base(g, b, h, (int64_t)tile * 128 + t);
       Param<PDT>::store(g.v_scale, pi, s);
       Param<PDT>::store(g.v_zero, pi, mn);
     }
-    codes[(2 * lane) * PITCH + t] = (uint16_t)quant_code(x0, sp, zp, levels);
-    codes[(2 * lane + 1) * PITCH + t] = (uint16_t)quant_code(x1, sp, zp, levels);
+#pragma unroll
+    for (int k = 0; k < 4; k++) codes[(4 * l32 + k) * PITCH + t] = (uint16_t)quant_code(x[i][k], sp, zp, levels);
   }
   __syncthreads();
-  pack_rows_store<VB, PITCH>(codes, g.v_codes + v_tile_offset(g, b, h, tile));
+  pack_vtile_store<VB, PITCH>(codes, g.v_codes + v_tile_offset(g, b, h, tile));
 }
 
 // ---------------------------------------------------------------------------
@@ -204,10 +252,17 @@ template <int PDT, int IN>
 static hipError_t launch_v(const Geo& g, const void* v, const int64_t* s, int t0, int n_new,
                            hipStream_t stm) {
   dim3 grid(n_new / 128, g.H, g.B), block(256);
-#define KVQ_QV(VBV)                                                                          \
-  case VBV:                                                                                  \
-    hipLaunchKernelGGL((quantize_v_kernel<VBV, PDT, IN>), grid, block, 0, stm, g, v, s[0],   \
-                       s[1], s[2], t0);                                                      \
+  const int eb = (IN == KVQ_F32) ? 4 : 2;
+  const bool vec = ((uintptr_t)v % (4 * eb) == 0) && (s[0] % 4 == 0) && (s[1] % 4 == 0) &&
+                   (s[2] % 4 == 0);
+#define KVQ_QV(VBV)                                                                           \
+  case VBV:                                                                                   \
+    if (vec)                                                                                  \
+      hipLaunchKernelGGL((quantize_v_kernel<VBV, PDT, IN, true>), grid, block, 0, stm, g, v,  \
+                         s[0], s[1], s[2], t0);                                               \
+    else                                                                                      \
+      hipLaunchKernelGGL((quantize_v_kernel<VBV, PDT, IN, false>), grid, block, 0, stm, g, v, \
+                         s[0], s[1], s[2], t0);                                               \
     break;
   switch (g.v_bits) {
     KVQ_QV(1) KVQ_QV(2) KVQ_QV(4) KVQ_QV(8) KVQ_QV(16)

@@ -5,12 +5,13 @@
 // the zero point is kept and the scale becomes (2^b + 1) * S.  The product
 // stays below 2^32 for b <= 8, so the arithmetic is unsigned 32-bit.
 //
-// A uniform-width tile is a stream of 16384 codes (keys token-major, values
-// channel-major); the shrink keeps the code order, so key and value tiles use
-// the same kernel.  One workgroup of 256 threads owns one tile: every thread
-// loads its 64 codes (16*b bytes at 2b bits) into registers, the workgroup
-// synchronises, and only then writes the 8*b-byte result into the first half
-// of the tile.  No workgroup touches another tile, so in-place is race-free.
+// A uniform-width key tile is a stream of 16384 codes whose order the shrink
+// keeps.  A value tile's word planes depend on the width: output word
+// (w, c, a) at b bits is made of input words (2w, c, a) and (2w+1, c, a) at 2b
+// bits.  One workgroup of 256 threads owns one tile: every thread loads the
+// input words it needs into registers, the workgroup synchronises, and only
+// then writes the b-bit result into the first half of the tile.  No
+// workgroup touches another tile, so in-place is race-free.
 // Threads 0..127 also rescale the tile's 128 scales (key: per channel of this
 // tile; value: per token of this tile).
 #pragma clang fp contract(off)
@@ -19,26 +20,51 @@
 
 namespace kvq {
 
-template <int B, int PDT>
-__global__ __launch_bounds__(256) void shrink_kernel(Geo g) {
-  constexpr int IN_BITS = 2 * B;
-  constexpr int IN_WORDS = 4 * B;             // 64 codes * 2B bits / 32
-  constexpr int OUT_WORDS = 2 * B;            // 64 codes * B bits / 32
+template <int B>
+__device__ __forceinline__ uint32_t ers(uint32_t x) {
   constexpr uint32_t C = (1u << (2 * B)) - (1u << B) + 1u;
   constexpr uint32_t HALF = 1u << (B - 1);
-  constexpr uint32_t IN_MASK = (IN_BITS == 32) ? 0xffffffffu : ((1u << IN_BITS) - 1u);
+  return (C * (x + HALF)) >> (3 * B);
+}
 
+// ERS of n codes of 2B bits in the low bits of w (LSB first) -> n codes of B bits
+template <int B, int N>
+__device__ __forceinline__ uint32_t ers_word(uint32_t w) {
+  constexpr uint32_t MASK = (2 * B == 32) ? 0xffffffffu : ((1u << (2 * B)) - 1u);
+  uint32_t o = 0;
+#pragma unroll
+  for (int i = 0; i < N; i++) o |= ers<B>((w >> (i * 2 * B)) & MASK) << (i * B);
+  return o;
+}
+
+template <int B, int PDT>
+__global__ __launch_bounds__(256) void shrink_kernel(Geo g) {
+  constexpr int IN_WORDS = 4 * B;             // per thread: 64 codes * 2B bits / 32
+  constexpr int OUT_WORDS = 2 * B;            // per thread: 64 codes * B bits / 32
   const int tile = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / g.H, h = bh % g.H;
   const bool is_v = blockIdx.z != 0;
   uint8_t* base = is_v ? g.v_codes + v_tile_offset(g, b, h, tile)
                        : g.k_codes + k_tile_offset(g, b, h, tile);
-  uint32_t* in = (uint32_t*)base + threadIdx.x * IN_WORDS;
   uint32_t w[IN_WORDS];
+  if (!is_v) {
+    // key tile: a flat stream of codes; thread t owns codes [64t, 64t + 64)
+    const uint32_t* in = (const uint32_t*)base + threadIdx.x * IN_WORDS;
 #pragma unroll
-  for (int i = 0; i < IN_WORDS; i++) w[i] = in[i];
-
+    for (int i = 0; i < IN_WORDS; i++) w[i] = in[i];
+  } else {
+    // value tile: output word o = (wp*128 + c)*4 + a takes its low half from
+    // input word o + wp*512 (plane 2wp) and its high half from o + (wp+1)*512
+    const uint32_t* in = (const uint32_t*)base;
+#pragma unroll
+    for (int k = 0; k < OUT_WORDS; k++) {
+      const int o = threadIdx.x + 256 * k;
+      const int wp = o >> 9;
+      w[2 * k] = in[o + wp * 512];
+      w[2 * k + 1] = in[o + (wp + 1) * 512];
+    }
+  }
   void* sarr = is_v ? g.v_scale : g.k_scale;
   const int64_t pbase = is_v ? v_param_base(g, b, h, (int64_t)tile * 128)
                              : k_param_base(g, b, h, tile);
@@ -49,20 +75,19 @@ __global__ __launch_bounds__(256) void shrink_kernel(Geo g) {
   }
   __syncthreads();   // every code of the tile is in registers before any write
 
-  uint32_t o[OUT_WORDS];
+  uint32_t* out = (uint32_t*)base;
+  if (!is_v) {
+    // 2 input words (2 * 16/B codes each) -> 1 output word
 #pragma unroll
-  for (int i = 0; i < OUT_WORDS; i++) o[i] = 0u;
+    for (int k = 0; k < OUT_WORDS; k++)
+      out[threadIdx.x * OUT_WORDS + k] =
+          ers_word<B, 16 / B>(w[2 * k]) | (ers_word<B, 16 / B>(w[2 * k + 1]) << 16);
+  } else {
 #pragma unroll
-  for (int k = 0; k < 64; k++) {
-    const int ib = k * IN_BITS;
-    const uint32_t x = (w[ib >> 5] >> (ib & 31)) & IN_MASK;
-    const uint32_t y = (C * (x + HALF)) >> (3 * B);
-    const int ob = k * B;
-    o[ob >> 5] |= y << (ob & 31);
+    for (int k = 0; k < OUT_WORDS; k++)
+      out[threadIdx.x + 256 * k] =
+          ers_word<B, 16 / B>(w[2 * k]) | (ers_word<B, 16 / B>(w[2 * k + 1]) << 16);
   }
-  uint32_t* out = (uint32_t*)base + threadIdx.x * OUT_WORDS;
-#pragma unroll
-  for (int i = 0; i < OUT_WORDS; i++) out[i] = o[i];
   if (threadIdx.x < 128) Param<PDT>::store(sarr, pbase + threadIdx.x, s_new);
 }
 

@@ -72,6 +72,9 @@ def lib():
             L.orc_quantize_group.argtypes = [vp, i64, i32, i32, i32, vp, i64, vp, vp, i64]
             L.orc_pack_rows.argtypes = [vp, i32, vp]
             L.orc_unpack_rows.argtypes = [vp, i32, vp]
+            L.orc_pack_vtile.argtypes = [vp, i32, vp]
+            L.orc_unpack_vtile.argtypes = [vp, i32, vp]
+            L.orc_shrink_vtile.argtypes = [vp, i32]
             L.orc_pack_mixed.argtypes = [vp, vp]
             L.orc_unpack_mixed.argtypes = [vp, vp]
             L.orc_mixed_slot_bits.restype = i32
@@ -156,6 +159,22 @@ def unpack_rows(tile: np.ndarray, bits: int) -> np.ndarray:
     return codes
 
 
+def pack_vtile(codes: np.ndarray, bits: int) -> np.ndarray:
+    """codes[c][t] -> value tile (word planes W[w][c][a])"""
+    codes = np.ascontiguousarray(codes, dtype=np.uint16).reshape(128, 128)
+    tile = np.zeros(16 * bits * 128, dtype=np.uint8)
+    lib().orc_pack_vtile(_p(codes), bits, _p(tile))
+    return tile
+
+
+def unpack_vtile(tile: np.ndarray, bits: int) -> np.ndarray:
+    tile = np.ascontiguousarray(tile, dtype=np.uint8)
+    assert tile.size >= 16 * bits * 128
+    codes = np.empty((128, 128), dtype=np.uint16)
+    lib().orc_unpack_vtile(_p(tile), bits, _p(codes))
+    return codes
+
+
 def pack_mixed(codes: np.ndarray) -> np.ndarray:
     codes = np.ascontiguousarray(codes, dtype=np.uint16).reshape(128, 128)
     tile = np.zeros(MIXED_TILE_BYTES, dtype=np.uint8)
@@ -232,11 +251,11 @@ def shrink_stream(st: Stream, to_bits: int) -> Stream:
     assert st.k_bits == 2 * to_bits and st.v_bits == 2 * to_bits
     L = lib()
     out = []
-    for tiles in (st.k_tiles, st.v_tiles):
+    for tiles, fn in ((st.k_tiles, L.orc_shrink_tile), (st.v_tiles, L.orc_shrink_vtile)):
         t2 = np.array(tiles, copy=True)
         for i in range(t2.shape[0]):
             row = np.ascontiguousarray(t2[i])
-            L.orc_shrink_tile(_p(row), to_bits)
+            fn(_p(row), to_bits)
             t2[i] = row
         out.append(np.ascontiguousarray(t2[:, : tile_bytes(to_bits)]))
     ks = np.array(st.ks, copy=True)
@@ -272,7 +291,7 @@ def dequant_v(st: Stream) -> np.ndarray:
     Z = decode(st.vz, st.pdt)
     out = np.empty((nt * 128, 128), dtype=np.float64)
     for g in range(nt):
-        codes = unpack_rows(st.v_tiles[g], st.v_bits).astype(np.float64)  # [c][t]
+        codes = unpack_vtile(st.v_tiles[g], st.v_bits).astype(np.float64)  # [c][t]
         out[g * 128:(g + 1) * 128] = codes.T * S[g * 128:(g + 1) * 128, None] + \
             Z[g * 128:(g + 1) * 128, None]
     return out

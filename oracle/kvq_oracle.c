@@ -211,6 +211,9 @@ void orc_quantize_group(const float *x, int64_t stride, int n, int bits, int pdt
         if (v < mn) mn = v;
         if (v > mx) mx = v;
     }
+    /* the extremes are real numbers: -0 and +0 are the same value, kept as +0 */
+    mn = mn + 0.0f;
+    mx = mx + 0.0f;
     float levels = (float)((1u << bits) - 1u);
     float s = (mx - mn) / levels;                 /* two binary32 roundings */
     param_store(s_arr, pidx, pdt, s);
@@ -276,6 +279,33 @@ void orc_unpack_rows(const uint8_t *tile, int bits, uint16_t *codes)
     for (int r = 0; r < 128; r++)
         for (int e = 0; e < 128; e++)
             codes[r * 128 + e] = (uint16_t)get_bits(tile + (int64_t)r * row_bytes, (int64_t)e * bits, bits);
+}
+
+/* Value tile (header layout text): 32-bit little-endian words W[w][c][a],
+ * word index (w*128 + c)*4 + a, w < b, c < 128, a < 4; word W[w][c][a] holds
+ * the codes of channel c for tokens 32a + w*(32/b) + i, i < 32/b, code i at
+ * bits [i*b, i*b + b).  Bit position of the code of (channel c, token t): */
+static int64_t vtile_bitpos(int c, int t, int bits)
+{
+    int per_word = 32 / bits;
+    int a = t / 32, w = (t % 32) / per_word, i = t % per_word;
+    int64_t word = ((int64_t)w * 128 + c) * 4 + a;
+    return word * 32 + (int64_t)i * bits;
+}
+
+/* codes[c][t] (128x128, channel-major) -> 2048*bits-byte value tile */
+void orc_pack_vtile(const uint16_t *codes, int bits, uint8_t *tile)
+{
+    for (int c = 0; c < 128; c++)
+        for (int t = 0; t < 128; t++)
+            put_bits(tile, vtile_bitpos(c, t, bits), bits, codes[c * 128 + t]);
+}
+
+void orc_unpack_vtile(const uint8_t *tile, int bits, uint16_t *codes)
+{
+    for (int c = 0; c < 128; c++)
+        for (int t = 0; t < 128; t++)
+            codes[c * 128 + t] = (uint16_t)get_bits(tile, vtile_bitpos(c, t, bits), bits);
 }
 
 /* Mixed-bit key tile ([CHANMIX] Key design 3: retrieval 4 / outlier 3 /
@@ -381,7 +411,7 @@ void orc_quantize_v(const float *v, int64_t t_stride, int n_tok, int bits, int p
         }
         for (int t = 0; t < 128; t++)
             for (int ch = 0; ch < 128; ch++) ct[ch * 128 + t] = tc[t * 128 + ch];
-        orc_pack_rows(ct, bits, codes + (int64_t)g * tile_stride);
+        orc_pack_vtile(ct, bits, codes + (int64_t)g * tile_stride);
     }
     free(tc);
     free(ct);
@@ -403,9 +433,8 @@ uint32_t orc_ers(uint32_t x2b, int b)
     return (uint32_t)((c * n) >> (3 * b));
 }
 
-/* Shrink one packed tile in place: 16384 codes of 2b bits -> b bits (the
- * code order is unchanged, so the same routine serves key and value tiles of
- * uniform width). */
+/* Shrink one packed uniform-width key tile in place: 16384 codes of 2b bits
+ * -> b bits, code order unchanged. */
 void orc_shrink_tile(uint8_t *tile, int to_bits)
 {
     int from = 2 * to_bits;
@@ -414,6 +443,19 @@ void orc_shrink_tile(uint8_t *tile, int to_bits)
     for (int i = 0; i < 128 * 128; i++) c[i] = (uint16_t)orc_ers(c[i], to_bits);
     memset(tile, 0, (size_t)16 * from * 128);
     orc_pack_rows(c, to_bits, tile);
+    free(c);
+}
+
+/* Shrink one value tile in place: every code goes from its position in the
+ * 2b-bit word planes to its position in the b-bit word planes. */
+void orc_shrink_vtile(uint8_t *tile, int to_bits)
+{
+    int from = 2 * to_bits;
+    uint16_t *c = (uint16_t *)malloc(128 * 128 * sizeof(uint16_t));
+    orc_unpack_vtile(tile, from, c);
+    for (int i = 0; i < 128 * 128; i++) c[i] = (uint16_t)orc_ers(c[i], to_bits);
+    memset(tile, 0, (size_t)16 * from * 128);
+    orc_pack_vtile(c, to_bits, tile);
     free(c);
 }
 
@@ -462,7 +504,7 @@ int orc_decode_attn(const uint8_t *kc, int64_t k_tile_stride, const void *ks, co
                 K[((int64_t)g * 128 + t) * 128 + ch] = S * codes[t * 128 + j] + Z;
             }
         /* values: codes[c][t] */
-        orc_unpack_rows(vc + (int64_t)g * v_tile_stride, v_bits, codes);
+        orc_unpack_vtile(vc + (int64_t)g * v_tile_stride, v_bits, codes);
         for (int t = 0; t < 128; t++) {
             int64_t tok = (int64_t)g * 128 + t;
             double S = param_load(vs, tok, pdt);

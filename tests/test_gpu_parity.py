@@ -188,3 +188,59 @@ def test_pool_layout_decode():
         for h in range(H):
             ref = oracle_attn(oracle_stream(inp, b, h, 4, 4, kvq.F16), inp["q_bf16"][b, h * G:(h + 1) * G])
             assert rel_err_rows(out[b, h * G:(h + 1) * G], ref).max() <= REL_TOL
+
+
+@pytest.mark.parametrize("B,H,Hq,T", [(64, 4, 28, 8192), (16, 4, 28, 4096), (1, 8, 32, 4096)])
+def test_workspace_and_output_guard_bytes(B, H, Hq, T):
+    """Regression: the workspace must hold every chunk the launch plan uses
+    (a plan with several kv streams per wave has more chunks).  Guard bytes
+    after the workspace and after the output must stay untouched."""
+    print("case guard B=%d H=%d Hq=%d T=%d" % (B, H, Hq, T), flush=True)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(B + T)
+    cache = kvq.PackedCache(B, H, T, 4, 4, kvq.F16)
+    for t0 in range(0, T, 2048):
+        k = torch.randn((B, H, 2048, 128), generator=g, device="cuda")
+        v = torch.randn((B, H, 2048, 128), generator=g, device="cuda")
+        cache.quantize(k, v, t0)
+    q = torch.randn((B, Hq, 128), generator=g, device="cuda").to(torch.bfloat16)
+    nb = cache.workspace_bytes(Hq)
+    GUARD = 1 << 20
+    ws_full = torch.zeros(nb + GUARD, dtype=torch.uint8, device="cuda")
+    ws_full[nb:] = 0xA5
+    out_full = torch.full((B * Hq * 128 + 4096,), 7.0, dtype=torch.float32, device="cuda")
+    out = out_full[:B * Hq * 128].view(B, Hq, 128)
+    for _ in range(2):
+        cache.decode_attn(q, SCALE, out=out, workspace=ws_full[:nb])
+    torch.cuda.synchronize()
+    assert bool((ws_full[nb:] == 0xA5).all()), "workspace overrun"
+    assert bool((out_full[B * Hq * 128:] == 7.0).all()), "output overrun"
+    assert bool(torch.isfinite(out).all())
+
+
+@pytest.mark.parametrize("pdt", [kvq.F16, kvq.E4M3])
+def test_quantize_edge_groups(pdt):
+    """Constant groups (S' = 0), groups of signed zeros, ranges so small that
+    S' is subnormal or flushes to zero, one huge outlier, exact integers."""
+    print("case edge groups pdt=%d" % pdt, flush=True)
+    rng = np.random.default_rng(123)
+    T = 512
+    k = rng.standard_normal((1, 2, T, 128)).astype(np.float32)
+    v = rng.standard_normal((1, 2, T, 128)).astype(np.float32)
+    k[0, 0, 0:128, 5] = 1.25                       # constant key group
+    k[0, 0, 0:128, 6] = np.where(np.arange(128) % 2, -0.0, 0.0).astype(np.float32)
+    k[0, 0, 128:256, 7] = 1.0 + rng.standard_normal(128).astype(np.float32) * 1e-6
+    k[0, 1, 256:384, 9] *= 1e-7                     # subnormal-range scale
+    k[0, 1, 384:512, 11][17] = 300.0 if pdt == kvq.E4M3 else 5000.0   # huge outlier
+    v[0, 0, 3, :] = -2.5                            # constant value group
+    v[0, 0, 4, :] = np.where(np.arange(128) % 3, 0.0, -0.0)
+    v[0, 1, 5, :] = np.arange(128, dtype=np.float32)  # exact integers
+    v[0, 1, 6, :] *= 1e-6
+    inp = dict(k=k, v=v)
+    for bits in (4, 2, 8):
+        cache = kvq.PackedCache(1, 2, T, bits, bits, pdt)
+        cache.quantize(to_dev(k, torch), to_dev(v, torch), 0)
+        torch.cuda.synchronize()
+        for h in range(2):
+            st = oracle_stream(inp, 0, h, bits, bits, pdt)
+            assert_stream_bytes_equal(cache, st, 0, h, "edge bits=%d pdt=%d" % (bits, pdt))

@@ -290,6 +290,32 @@ def test_pack_bit_positions_by_hand():
     assert oracle.pack_rows(c1, 1)[1] == 0x02
 
 
+def test_value_tile_positions_by_hand():
+    """Value word planes W[w][c][a] (header layout text), positions worked out
+    by hand: 4-bit -> 8 tokens per word, word index (w*128 + c)*4 + a."""
+    c = np.zeros((128, 128), np.uint16)          # [channel][token]
+    c[0, 0] = 0x3                                # w=0,c=0,a=0,i=0 -> byte 0 low nibble
+    c[0, 9] = 0x5                                # t=9: a=0, w=1, i=1 -> word 512, bits 4..7
+    c[2, 33] = 0xF                               # t=33: a=1, w=0, i=1 -> word 9, bits 4..7
+    c[127, 127] = 0x6                            # a=3, w=3, i=7 -> word (3*128+127)*4+3, bits 28..31
+    t = oracle.pack_vtile(c, 4)
+    assert t[0] == 0x03
+    assert t[4 * 512] == 0x50
+    assert t[4 * 9] == 0xF0
+    assert t[4 * ((3 * 128 + 127) * 4 + 3) + 3] == 0x60
+    c1 = np.zeros((128, 128), np.uint16)
+    c1[5, 40] = 1                                # 1-bit: w=0, a=1, i=8 -> word 21, bit 8
+    assert oracle.pack_vtile(c1, 1)[4 * 21 + 1] == 0x01
+    c16 = np.zeros((128, 128), np.uint16)
+    c16[1, 3] = 0xBEEF                           # 16-bit: 2 tokens per word; t=3: w=1, i=1
+    t16 = oracle.pack_vtile(c16, 16)
+    wi = (1 * 128 + 1) * 4 + 0
+    assert t16[4 * wi + 2] == 0xEF and t16[4 * wi + 3] == 0xBE
+    for bits in (1, 2, 4, 8, 16):
+        r = np.random.default_rng(bits).integers(0, 2 ** bits, (128, 128)).astype(np.uint16)
+        assert np.array_equal(oracle.unpack_vtile(oracle.pack_vtile(r, bits), bits), r)
+
+
 def test_mixed_pack_by_hand():
     c = np.zeros((128, 128), np.uint16)
     c[0, 0] = 0x9                 # 4-bit slot 0 -> logical byte 0 low nibble
@@ -433,6 +459,9 @@ def test_shrink_stream_matches_requantized_codes():
         c4 = oracle.unpack_rows(st.k_tiles[g], 4).astype(np.int64)
         c2 = oracle.unpack_rows(st2.k_tiles[g], 2).astype(np.int64)
         assert np.array_equal(c2, np.floor(c4 / 5 + 0.5).astype(np.int64))
+        v4 = oracle.unpack_vtile(st.v_tiles[g], 4).astype(np.int64)
+        v2 = oracle.unpack_vtile(st2.v_tiles[g], 2).astype(np.int64)
+        assert np.array_equal(v2, np.floor(v4 / 5 + 0.5).astype(np.int64))
     assert st2.k_tiles.shape[1] == st.k_tiles.shape[1] // 2
     # error after one shrink is within S'_4/2 + 2 S'_4
     K2 = oracle.dequant_k(st2)
