@@ -128,6 +128,9 @@ typedef enum {
 #define KVQ_HEAD_DIM 128
 #define KVQ_GROUP 128
 #define KVQ_KMIXED 0          /* k_bits value selecting the mixed-width key tile */
+/* Largest per-stream capacity (2^26 tokens): device offsets into the
+ * per-stream parameter arrays are 32-bit. */
+#define KVQ_MAX_TOKENS (1 << 26)
 #define KVQ_MIXED_TILE_BYTES 4352
 
 typedef struct kvq_cache {
@@ -135,7 +138,7 @@ typedef struct kvq_cache {
     int32_t n_kv_heads;       /* Hkv >= 1 */
     int32_t head_dim;         /* must be 128 */
     int32_t group;            /* must be 128 */
-    int32_t max_tokens;       /* capacity per stream, multiple of 128 */
+    int32_t max_tokens;       /* capacity per stream, multiple of 128, <= KVQ_MAX_TOKENS */
     int32_t n_tokens;         /* tokens stored per stream, multiple of 128 */
     int32_t k_bits;           /* 16, 8, 4, 2, 1, or KVQ_KMIXED */
     int32_t v_bits;           /* 16, 8, 4, 2, 1 */

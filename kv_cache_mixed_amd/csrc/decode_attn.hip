@@ -31,14 +31,21 @@
 // Each lane therefore reads 4b contiguous bytes per key row and per value row.
 //
 // Codes become f16 operands without conversion instructions: a b-bit field at
-// bit position p of each 16-bit half is OR-ed into the exponent of 1024.0,
-// giving 1024 + code * 2^p exactly (p + b <= 10).  For keys the 1024 offset is
-// removed after the MFMA (an extra MFMA against a constant 1024 operand gives
-// 1024 * sum(B) per head); value operands subtract 1024 in packed f16 before the
-// MFMA, so the value accumulation stays free of cancellation.  The power-of-two
-// field weights 2^p (and 2^8 for the high byte of 16-bit codes) are folded into
-// the other operand.
+// bit position p (p + b <= 10) of both 16-bit halves of a loaded word, masked in
+// place, is the f16 subnormal code * 2^(p - 24), which MFMA multiplies exactly.
+// The power-of-two field weights (2^-p, and 2^8 for the high byte of 16-bit
+// codes) are folded into the other operand.  That operand (u for keys, P for
+// values) is split into f16 hi + lo parts (two MFMAs), so the products carry
+// about 22 significant bits and the sums accumulate in binary32.
+//
+// Softmax uses a lazy running max: the reference m only moves when a logit
+// exceeds it by more than TAU (log2 units), so e = 2^(logit - m) <= 2^TAU and
+// the output accumulator is rescaled only when some head's reference moved.
 #include "kvq_device.h"
+// waves of the decode kernel resident per SIMD (register budget 512 / n)
+#ifndef KVQ_DECODE_WAVES_PER_SIMD
+#define KVQ_DECODE_WAVES_PER_SIMD 1
+#endif
 
 namespace kvq {
 
@@ -94,13 +101,28 @@ __device__ __forceinline__ f32x4 mfma(const uint32_t* a, const uint32_t* b, f32x
   return __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ float wave_max16x4(float v) {  // max over the 4 lane groups
-  v = fmaxf(v, __shfl_xor(v, 16, 64));
-  return fmaxf(v, __shfl_xor(v, 32, 64));
+// Reductions over the four lane groups (lanes n, n+16, n+32, n+48) with the
+// gfx950 lane-swap instructions: after v_permlane32_swap (v_permlane16_swap)
+// of a register with itself, each lane holds its own value and that of lane
+// l ^ 32 (l ^ 16) in the two results.
+__device__ __forceinline__ float wave_max16x4(float v) {
+  auto r = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+  v = u2f(r[0]) > u2f(r[1]) ? u2f(r[0]) : u2f(r[1]);
+  r = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
+  return u2f(r[0]) > u2f(r[1]) ? u2f(r[0]) : u2f(r[1]);
+}
+// maximum of non-negative binary32 values, as bit patterns
+__device__ __forceinline__ uint32_t wave_maxu16x4(uint32_t v) {
+  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  v = max(r[0], r[1]);
+  r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return max(r[0], r[1]);
 }
 __device__ __forceinline__ float wave_sum16x4(float v) {
-  v += __shfl_xor(v, 16, 64);
-  return v + __shfl_xor(v, 32, 64);
+  auto r = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
+  v = u2f(r[0]) + u2f(r[1]);
+  r = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
+  return u2f(r[0]) + u2f(r[1]);
 }
 
 // Load 8 consecutive parameters starting at element e into f32.
@@ -152,12 +174,23 @@ struct UInfo {
   static constexpr int NW = B;
 };
 
-// f16 split of x into hi + lo (x - hi is exact in binary32)
+// f16 split of a pair: hi = f16 truncation of x (one v_cvt_pkrtz for both),
+// lo = f16 of the exact binary32 residual x - hi.  In the f16 normal range the
+// truncated value is x with its 13 low significand bits cleared, so the
+// residual is formed without converting hi back; values below the f16 normal
+// range (at least 2^-28 of the largest operand, see the headroom exponents)
+// only lose an error of that relative size.
 __device__ __forceinline__ void split_pack(float xl, float xh, uint32_t& hi, uint32_t& lo) {
-  const _Float16 al = (_Float16)xl, ah = (_Float16)xh;
-  const _Float16 bl = (_Float16)(xl - (float)al), bh = (_Float16)(xh - (float)ah);
-  hi = (uint32_t)__builtin_bit_cast(uint16_t, al) | ((uint32_t)__builtin_bit_cast(uint16_t, ah) << 16);
-  lo = (uint32_t)__builtin_bit_cast(uint16_t, bl) | ((uint32_t)__builtin_bit_cast(uint16_t, bh) << 16);
+  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xl, xh));
+  const float rl = xl - u2f(f2u(xl) & 0xffffe000u);
+  const float rh = xh - u2f(f2u(xh) & 0xffffe000u);
+  lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(rl, rh));
+}
+
+// buffer resource over [base, base + bytes): raw buffer loads take a 32-bit
+// lane offset plus SGPR/immediate offsets and return 0 beyond `bytes`
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, (int)bytes, 0x00020000);
 }
 
 // The field as an f16x2 operand register holding code * 2^(pos - 24) in each
@@ -170,10 +203,69 @@ __device__ __forceinline__ uint32_t field_subnormal(uint32_t word, F f) {
   return x & (m | (m << 16));
 }
 
+
+
+
+
+// binary32 of parameter I (compile-time) of a raw parameter-word array
+template <int PDT, int I>
+__device__ __forceinline__ float praw(const uint32_t* w) {
+  if constexpr (PDT == KVQ_E4M3) {
+    return __builtin_amdgcn_cvt_f32_fp8((int)w[I / 4], I % 4);   // OCP E4M3 on gfx950
+  } else if constexpr (PDT == KVQ_F32) {
+    return u2f(w[I]);
+  } else if constexpr (PDT == KVQ_F16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)((w[I / 2] >> (16 * (I % 2))) & 0xffffu));
+  } else {
+    return u2f((I % 2) ? (w[I / 2] & 0xffff0000u) : (w[I / 2] << 16));
+  }
+}
+template <int PDT, int N>
+__device__ __forceinline__ void praw_unpack(const uint32_t* w, float* out) {
+  if constexpr (N > 0) {
+    praw_unpack<PDT, N - 1>(w, out);
+    out[N - 1] = praw<PDT, N - 1>(w);
+  }
+}
+// raw 32-bit words holding N parameters
+template <int PDT, int N>
+struct PW {
+  static constexpr int W = (N * (PDT == KVQ_F32 ? 4 : (PDT == KVQ_E4M3 ? 1 : 2))) / 4;
+};
+// load N consecutive parameters (N * bytes a multiple of 4, offset aligned)
+template <int PDT, int N>
+__device__ __forceinline__ void pload(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff,
+                                      uint32_t* w) {
+  constexpr int W = PW<PDT, N>::W;
+  if constexpr (W % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < W; i += 4) {
+      const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(r, voff + 4 * i, soff, 0);
+      w[i] = v[0]; w[i + 1] = v[1]; w[i + 2] = v[2]; w[i + 3] = v[3];
+    }
+  } else if constexpr (W == 2) {
+    const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(r, voff, soff, 0);
+    w[0] = v[0]; w[1] = v[1];
+  } else {
+    static_assert(W == 1, "parameter group");
+    w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, 0);
+  }
+}
+
 // KB: 16/8/4/2/1 or 0 (mixed keys).  VB: 16/8/4/2/1.  NS: kv streams packed
 // into the 16 MFMA columns (column n serves stream n / G, head n % G).
+//
+// Main loop: the wave walks its tiles in sub-tiles of TPS tokens per lane
+// group.  Sub-tile operands (key blocks, value words, value parameters) are
+// double buffered in registers: the loads of the next sub-tile are issued
+// before the current one is computed.  All loads are raw buffer loads with an
+// SGPR base per (stream, tile) and lane offsets fixed for the whole kernel.
+// The folded query u = q * S_K * 2^k (split into f16 hi + lo) lives in LDS,
+// one 4-register group per k-step, computed once per tile.  Lanes of columns
+// that serve no head have q = 0, so their operands are harmless and never
+// masked.
 template <int KB, int VB, int PDT, int NS>
-__global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, KVQ_DECODE_WAVES_PER_SIMD) void decode_kernel(DecodeArgs a) {
   constexpr bool MIXED = (KB == 0);
   constexpr int NFK = MIXED ? 16 : UInfo<KB>::NF;    // key operand registers per token
   constexpr int NWK = MIXED ? 3 : UInfo<KB>::NW;     // key words per lane per token
@@ -186,13 +278,29 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   constexpr int FVS = NFV / NSUB;                    // value fields per sub-tile
   constexpr int WVS = NWV / NSUB;                    // value words per sub-tile
   constexpr int KSV = FVS / 4;                       // value k-steps per sub-tile
-  constexpr int KH = (KB == 16) ? 4 : 12;            // headroom exponents (f16 range)
-  constexpr int VH = (VB == 16) ? 4 : 12;
+  constexpr int PB = (PDT == KVQ_F32) ? 4 : ((PDT == KVQ_E4M3) ? 1 : 2);
+  constexpr int PWV = PW<PDT, TPS>::W;               // value-parameter words per sub-tile
+  constexpr int PWK = PW<PDT, 8>::W;                 // key-parameter words per 8 slots
+  constexpr int KPA = 32 * PB;                       // words per 128 key parameters
+  constexpr int KPL = (PB == 4) ? 2 : 1;             // of which one lane loads
+  // Headroom exponents keep every f16 operand below 2^15: |u| < 2^(KH+2) and
+  // P = e * S_V * 2^(VH - E) < 2^(VH + 1 + TAU), times the field weights.
+  constexpr int TAU = 8;                             // lazy-max slack (log2 units)
+  constexpr int KH = (KB == 16) ? 4 : 12;
+  constexpr int VH = (VB == 16) ? -2 : 6;
   constexpr int ROW_K = MIXED ? 8 : 16 * KB;
+  constexpr int LDS_WAVE = NFK * 2 * 64;             // u32 words of folded query per wave
   static_assert(KSV >= 1 && WVS >= 1, "sub-tile must hold whole value k-steps");
+  static_assert(LDS_WAVE >= 16 * 128 && TPS % 8 == 0, "layout assumptions");
+
+  // folded query (per wave) during the loop; the wave partial afterwards
+  __shared__ __attribute__((aligned(16))) uint32_t lds[4][LDS_WAVE];
+  // key scales / zeros of the current tile of each stream, per wave
+  __shared__ __attribute__((aligned(16))) uint32_t kst[4][NS][2][KPA];
 
   const Geo& g = a.g;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  // the wave index is uniform: keep it (and everything derived) in SGPRs
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, lg = lane >> 4;
   const int grp = blockIdx.y, chunk = blockIdx.x;
   const int G = a.G;
@@ -203,11 +311,35 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   const int b_own = real ? bh_own / g.H : 0, h_own = real ? bh_own % g.H : 0;
   const int t_begin = chunk * a.tpc;
   const int t_end = min(t_begin + a.tpc, g.n_tiles);
+  const int my_tiles = (t_end - t_begin - wave + 3) / 4;   // tiles t_begin + wave + 4i
+  const int n_iter = (my_tiles > 0 ? my_tiles : 0) * NSUB;
 
   auto kslot = [&](int li) -> int {
     if constexpr (MIXED) return lg == 0 ? (li < 24 ? li : 96 + li) : 32 * lg - 8 + li;
     else return 32 * lg + li;
   };
+
+  // ---- lane offsets, fixed for the whole kernel
+  // key block j row r = 32*(n/4) + 4j + n%4; the lane reads its lane group's
+  // 4*KB bytes of the row (mixed: its plane's 8 bytes, lane group 0 also the
+  // 2 plane-4 bytes)
+  const uint32_t row0 = 32 * (n >> 2) + (n & 3);
+  const uint32_t koff = MIXED ? (uint32_t)((lg == 0 ? 0 : 1024 * lg) + 8 * row0)
+                              : (uint32_t)(row0 * ROW_K + 4 * KB * lg);
+  const uint32_t koff4 = 4096 + 2 * row0;                       // mixed plane 4
+  const uint32_t voff = (uint32_t)(4 * n + lg) * 4;             // value word (w, c, a)
+  // parameter arrays from the group's first stream on (offsets stay below 2^32:
+  // the host bounds max_tokens)
+  const int64_t s0 = (int64_t)grp * NS;
+  const int own_c = real ? own : 0;
+  const uint32_t vpoff = (uint32_t)(((int64_t)own_c * g.max_tokens + 32 * lg) * PB);
+  const __amdgpu_buffer_rsrc_t r_vs = rsrc((const uint8_t*)g.v_scale + s0 * g.max_tokens * PB, 0xffffffffu);
+  const __amdgpu_buffer_rsrc_t r_vz = rsrc((const uint8_t*)g.v_zero + s0 * g.max_tokens * PB, 0xffffffffu);
+  const __amdgpu_buffer_rsrc_t r_ks = rsrc((const uint8_t*)g.k_scale + s0 * g.max_tokens * PB, 0xffffffffu);
+  const __amdgpu_buffer_rsrc_t r_kz = rsrc((const uint8_t*)g.k_zero + s0 * g.max_tokens * PB, 0xffffffffu);
+  // key parameters: lane l loads word l (and l + 64) of the tile's 128 (e4m3:
+  // lanes 32.. repeat words 0..31)
+  const uint32_t kloff = (uint32_t)((PB == 1) ? (lane & 31) : lane) * 4;
 
   // ---- own query head over the lane's 32 key slots, kept as bf16 pairs
   uint32_t qp[16];
@@ -231,251 +363,289 @@ __global__ __launch_bounds__(256, 2) void decode_kernel(DecodeArgs a) {
   auto qval = [&](int li) -> float {
     return (li & 1) ? u2f(qp[li >> 1] & 0xffff0000u) : u2f(qp[li >> 1] << 16);
   };
-  float qmax = 0.0f;
+  uint32_t qmax = 0;
 #pragma unroll
-  for (int li = 0; li < 32; li++) qmax = fmaxf(qmax, fabsf(qval(li)));
-  const int eq = expo(wave_max16x4(qmax));
-  int kseg[4];
-#pragma unroll
-  for (int s = 0; s < 4; s++) kseg[s] = kslot(8 * s);
+  for (int li = 0; li < 32; li++) qmax = max(qmax, f2u(qval(li)) & 0x7fffffffu);
+  const int eq = expo(u2f(wave_maxu16x4(qmax)));
 
   float m_run = -INFINITY, l_run = 0.0f, z_run = 0.0f;
   int e_run = -1000;
+  float ak = 0.0f, bk0 = 0.0f;
   f32x4 acc_o[8];
 #pragma unroll
   for (int cb = 0; cb < 8; cb++) acc_o[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  uint32_t* my_lds = lds[wave];
 
-#pragma unroll 1
-  for (int tile = t_begin + wave; tile < t_end; tile += 4) {
-    // ---- own stream: fold key scales into the query (u = q * S * 2^k, split hi/lo)
-    uint32_t bkh[NFK], bkl[NFK];
-    float ak = 0.0f, bk0 = 0.0f;
-    {
-      // every lane loads (fake lanes read stream (0, 0), always in bounds) and
-      // fake lanes zero the values: no divergent branch around the loads
-      float ks[32], kz[32];
-      {
-        const int64_t kpb = k_param_base(g, b_own, h_own, tile);
-#pragma unroll
-        for (int s = 0; s < 4; s++) {
-          load_params8<PDT>(g.k_scale, kpb + kseg[s], ks + 8 * s);
-          load_params8<PDT>(g.k_zero, kpb + kseg[s], kz + 8 * s);
-        }
-#pragma unroll
-        for (int li = 0; li < 32; li++) {
-          ks[li] = real ? ks[li] : 0.0f;
-          kz[li] = real ? kz[li] : 0.0f;
-        }
-      }
-      float smax = 0.0f, beta = 0.0f;
-#pragma unroll
-      for (int li = 0; li < 32; li++) {
-        smax = fmaxf(smax, ks[li]);
-        beta += qval(li) * kz[li];
-      }
-      const int es = expo(wave_max16x4(smax));
-      beta = wave_sum16x4(beta);
-      const float kf = exp2i(KH - eq - es);
-      float u[32];
-#pragma unroll
-      for (int li = 0; li < 32; li++) u[li] = qval(li) * ks[li] * kf;
-#pragma unroll
-      for (int f = 0; f < NFK; f++) {
-        Fld F;
-        if constexpr (MIXED) F = (lg == 0) ? mfield0(f) : ufield<2>(f);
-        else F = ufield<KB>(f);
-        const float w = exp2i(F.wexp - F.pos);
-        split_pack(u[F.lo] * w, u[F.hi] * w, bkh[f], bkl[f]);
-      }
-      if (real) {
-        ak = a.sl2 * exp2i(24 - KH + eq + es);
-        bk0 = a.sl2 * beta;
-      }
-    }
+  // one sub-tile of raw operands
+  struct Buf {
+    uint32_t kw[NS][JB][NWK];
+    uint32_t vw[NS][8][WVS];
+    uint32_t vs[PWV], vz[PWV];
+    uint32_t kp[NS][2][KPL];   // next tile's key scales / zeros (sub-tile 0 only)
+  };
 
-    const uint8_t* ktile[NS];
-    const uint8_t* vtile[NS];
+  auto load = [&](Buf& bf, int it) {
+    const int tile = t_begin + wave + 4 * (it / NSUB);
+    const int sub = it % NSUB;
 #pragma unroll
     for (int s = 0; s < NS; s++) {
-      const int bh = min(grp * NS + s, BH - 1);
+      const int bh = min(grp * NS + s, BH - 1);   // a missing stream re-reads a valid one
       const int bs = bh / g.H, hs = bh % g.H;
-      ktile[s] = g.k_codes + k_tile_offset(g, bs, hs, tile);
-      vtile[s] = g.v_codes + v_tile_offset(g, bs, hs, tile);
+      const __amdgpu_buffer_rsrc_t rk =
+          rsrc(g.k_codes + k_tile_offset(g, bs, hs, tile), MIXED ? KVQ_MIXED_TILE_BYTES : 2048 * KB);
+      const __amdgpu_buffer_rsrc_t rv = rsrc(g.v_codes + v_tile_offset(g, bs, hs, tile), 2048 * VB);
+#pragma unroll
+      for (int jj = 0; jj < JB; jj++) {
+        const uint32_t soff = (uint32_t)(sub * JB) * 4 * ROW_K;       // rows 4j apart
+        if constexpr (MIXED) {
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rk, koff + jj * 32, soff, 0);
+          const uint32_t w2 = __builtin_amdgcn_raw_buffer_load_b16(rk, koff4 + jj * 8, soff / 4, 0);
+          bf.kw[s][jj][0] = v[0];
+          bf.kw[s][jj][1] = v[1];
+          bf.kw[s][jj][2] = (w2 & 0xffu) | ((w2 & 0xff00u) << 8);
+        } else if constexpr (NWK >= 4) {
+#pragma unroll
+          for (int w = 0; w < NWK; w += 4) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(rk, koff + jj * 4 * ROW_K + 4 * w, soff, 0);
+            bf.kw[s][jj][w] = v[0]; bf.kw[s][jj][w + 1] = v[1];
+            bf.kw[s][jj][w + 2] = v[2]; bf.kw[s][jj][w + 3] = v[3];
+          }
+        } else if constexpr (NWK == 2) {
+          const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rk, koff + jj * 4 * ROW_K, soff, 0);
+          bf.kw[s][jj][0] = v[0]; bf.kw[s][jj][1] = v[1];
+        } else {
+          bf.kw[s][jj][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, koff + jj * 4 * ROW_K, soff, 0);
+        }
+      }
+      // value word planes: word (w, c, a) at byte ((w*128 + c)*4 + a)*4
+#pragma unroll
+      for (int w = 0; w < WVS; w++) {
+        // the per-load constant goes to the scalar offset: one lane offset
+#pragma unroll
+        for (int cb = 0; cb < 8; cb++)
+          bf.vw[s][cb][w] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, (uint32_t)(sub * WVS + w) * 2048 + 256 * cb, 0);
+      }
     }
-#pragma unroll 1
-    for (int sub = 0; sub < NSUB; sub++) {
-      // ---- raw loads of every stream's key blocks and value words of this sub-tile
-      uint32_t kw[NS][JB][NWK];
-      uint32_t vw[NS][8][WVS];
+    if (sub == 0) {
 #pragma unroll
       for (int s = 0; s < NS; s++) {
-        const int bh = grp * NS + s;
-        if (bh >= BH) continue;
-        const uint8_t* kt = ktile[s];
-        const uint8_t* vt = vtile[s];
+        const int bh = min(grp * NS + s, BH - 1);
+        const uint32_t soff = (uint32_t)((((int64_t)(bh - grp * NS)) * g.max_tiles + tile) * 128 * PB);
 #pragma unroll
-        for (int jj = 0; jj < JB; jj++) {
-          const int j = sub * JB + jj;
-          const int r = 32 * (n >> 2) + 4 * j + (n & 3);
-          if constexpr (MIXED) {
-            if (lg == 0) {
-              const u32x2 v = *(const u32x2*)(kt + 8 * r);
-              const uint32_t w2 = *(const uint16_t*)(kt + 4096 + 2 * r);
-              kw[s][jj][0] = v[0];
-              kw[s][jj][1] = v[1];
-              kw[s][jj][2] = (w2 & 0xffu) | ((w2 & 0xff00u) << 8);
-            } else {
-              const u32x2 v = *(const u32x2*)(kt + 1024 * lg + 8 * r);
-              kw[s][jj][0] = v[0];
-              kw[s][jj][1] = v[1];
-              kw[s][jj][2] = 0u;
-            }
-          } else {
-            const uint32_t* src = (const uint32_t*)(kt + r * ROW_K + 4 * KB * lg);
-            if constexpr (NWK >= 4) {
+        for (int j = 0; j < KPL; j++) {
+          bf.kp[s][0][j] = __builtin_amdgcn_raw_buffer_load_b32(r_ks, kloff + 256 * j, soff, 0);
+          bf.kp[s][1][j] = __builtin_amdgcn_raw_buffer_load_b32(r_kz, kloff + 256 * j, soff, 0);
+        }
+      }
+    }
+    // own stream's value scales / zeros of the lane's TPS tokens
+    const uint32_t psoff = (uint32_t)(tile * 128 + sub * TPS) * PB;
+    pload<PDT, TPS>(r_vs, vpoff, psoff, bf.vs);
+    pload<PDT, TPS>(r_vz, vpoff, psoff, bf.vz);
+  };
+
+  // fold the key scales of `tile` into the query: u = q * S * 2^k as f16 hi/lo
+  // operand registers in LDS; logit constants ak, bk0
+  auto fold_query = [&](const Buf& bf) {
+    // stage the tile's key parameters in LDS, then read the own stream's 32
+    // slots (four runs of 8 consecutive slots)
 #pragma unroll
-              for (int w = 0; w < NWK; w += 4) {
-                const u32x4 v = *(const u32x4*)(src + w);
-                kw[s][jj][w] = v[0]; kw[s][jj][w + 1] = v[1]; kw[s][jj][w + 2] = v[2]; kw[s][jj][w + 3] = v[3];
-              }
-            } else if constexpr (NWK == 2) {
-              const u32x2 v = *(const u32x2*)src;
-              kw[s][jj][0] = v[0]; kw[s][jj][1] = v[1];
+    for (int s = 0; s < NS; s++)
+#pragma unroll
+      for (int a2 = 0; a2 < 2; a2++)
+#pragma unroll
+        for (int j = 0; j < KPL; j++) kst[wave][s][a2][(kloff >> 2) + 64 * j] = bf.kp[s][a2][j];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    uint32_t kss[4][PWK], kzz[4][PWK];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; s4++) {
+      const int wo = kslot(8 * s4) * PB / 4;
+#pragma unroll
+      for (int i = 0; i < PWK; i++) {
+        kss[s4][i] = kst[wave][own_c][0][wo + i];
+        kzz[s4][i] = kst[wave][own_c][1][wo + i];
+      }
+    }
+    float ks[32], kz[32];
+#pragma unroll
+    for (int s4 = 0; s4 < 4; s4++) {
+      praw_unpack<PDT, 8>(kss[s4], ks + 8 * s4);
+      praw_unpack<PDT, 8>(kzz[s4], kz + 8 * s4);
+    }
+    uint32_t smax = 0;
+    float beta = 0.0f;
+#pragma unroll
+    for (int li = 0; li < 32; li++) {
+      smax = max(smax, f2u(ks[li]));   // scales are >= +0
+      beta = fmaf(qval(li), kz[li], beta);
+    }
+    // eq + es is bounded below so that kf * 2^(field weight) stays finite when
+    // a tile's scales are all zero (codes then 0, u = 0)
+    const int eqs = max(eq + expo(u2f(wave_maxu16x4(smax))), -100);
+    beta = wave_sum16x4(beta);
+    const float kf = exp2i(KH - eqs);
+#pragma unroll
+    for (int f = 0; f < NFK; f++) {
+      Fld F;
+      if constexpr (MIXED) F = (lg == 0) ? mfield0(f) : ufield<2>(f);
+      else F = ufield<KB>(f);
+      const float w = kf * exp2i(F.wexp - F.pos);
+      uint32_t hi, lo;
+      split_pack(qval(F.lo) * ks[F.lo] * w, qval(F.hi) * ks[F.hi] * w, hi, lo);
+      // [k-step][hi/lo][lane][4]: one ds_read_b128 per operand group
+      my_lds[(((f >> 2) * 2 + 0) * 64 + lane) * 4 + (f & 3)] = hi;
+      my_lds[(((f >> 2) * 2 + 1) * 64 + lane) * 4 + (f & 3)] = lo;
+    }
+    ak = a.sl2 * exp2i(24 - KH + eqs);
+    bk0 = a.sl2 * beta;
+  };
+
+  auto compute = [&](const Buf& bf, int it) {
+    if (it % NSUB == 0) fold_query(bf);
+    // ---- logits: k-step-major over all (stream, block) accumulators
+    f32x4 acc[NS][JB];
+#pragma unroll
+    for (int s = 0; s < NS; s++)
+#pragma unroll
+      for (int jj = 0; jj < JB; jj++) acc[s][jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < NKK; k++) {
+      const u32x4 bhv = *(const u32x4*)(my_lds + ((k * 2 + 0) * 64 + lane) * 4);
+      const u32x4 blv = *(const u32x4*)(my_lds + ((k * 2 + 1) * 64 + lane) * 4);
+      const uint32_t bh4[4] = {bhv[0], bhv[1], bhv[2], bhv[3]};
+      const uint32_t bl4[4] = {blv[0], blv[1], blv[2], blv[3]};
+      uint32_t av[NS][JB][4];
+#pragma unroll
+      for (int s = 0; s < NS; s++)
+#pragma unroll
+        for (int jj = 0; jj < JB; jj++)
+#pragma unroll
+          for (int r = 0; r < 4; r++) {
+            const int f = 4 * k + r;
+            if constexpr (MIXED) {
+              const uint32_t x0 = field_subnormal(bf.kw[s][jj][mfield0(f).w], mfield0(f));
+              const uint32_t x1 = field_subnormal(bf.kw[s][jj][ufield<2>(f).w], ufield<2>(f));
+              av[s][jj][r] = (lg == 0) ? x0 : x1;
             } else {
-              kw[s][jj][0] = src[0];
+              av[s][jj][r] = field_subnormal(bf.kw[s][jj][ufield<KB>(f).w], ufield<KB>(f));
             }
           }
-        }
-        // value word planes: word (w, c, a) at ((w*128 + c)*4 + a); the 64
-        // lanes read 256 contiguous bytes per (plane, channel block)
+#pragma unroll
+      for (int s = 0; s < NS; s++)
+#pragma unroll
+        for (int jj = 0; jj < JB; jj++) acc[s][jj] = mfma(av[s][jj], bh4, acc[s][jj]);
+#pragma unroll
+      for (int s = 0; s < NS; s++)
+#pragma unroll
+        for (int jj = 0; jj < JB; jj++) acc[s][jj] = mfma(av[s][jj], bl4, acc[s][jj]);
+    }
+    float lgt[JB][4];
+#pragma unroll
+    for (int jj = 0; jj < JB; jj++) {
+      f32x4 v = acc[0][jj];
+#pragma unroll
+      for (int s = 1; s < NS; s++)
+        if (own == s) v = acc[s][jj];
+#pragma unroll
+      for (int i = 0; i < 4; i++) lgt[jj][i] = fmaf(ak, v[i], bk0);
+    }
+
+    // ---- online softmax with a lazy running max: the reference max m_run
+    // only moves when a logit exceeds it by more than TAU (so e <= 2^TAU), and
+    // the accumulator is rescaled only when some column's reference moved
+    float vs[TPS], vz[TPS];
+    praw_unpack<PDT, TPS>(bf.vs, vs);
+    praw_unpack<PDT, TPS>(bf.vz, vz);
+    float tmax = -INFINITY;
+    uint32_t vsmax = 0;
+#pragma unroll
+    for (int jj = 0; jj < JB; jj++)
+#pragma unroll
+      for (int i = 0; i < 4; i++) tmax = fmaxf(tmax, lgt[jj][i]);
+#pragma unroll
+    for (int i = 0; i < TPS; i++) vsmax = max(vsmax, f2u(vs[i]));   // scales are >= +0
+    tmax = wave_max16x4(tmax);
+    const int ev = expo(u2f(wave_maxu16x4(vsmax)));
+    const float m_new = (tmax > m_run + (float)TAU) ? tmax : m_run;
+    const float alpha = exp2f(m_run - m_new);
+    const int e_new = max(e_run, ev);
+    const float rescale = alpha * exp2i(e_run - e_new);
+    m_run = m_new;
+    e_run = e_new;
+    const float pf = exp2i(VH - e_new);
+    float p[TPS];
+    float lsum = 0.0f, zsum = 0.0f;
+#pragma unroll
+    for (int i = 0; i < TPS; i++) {
+      const float e = exp2f(lgt[i >> 2][i & 3] - m_new);
+      lsum += e;
+      zsum = fmaf(e, vz[i], zsum);
+      p[i] = e * (vs[i] * pf);
+    }
+    l_run = fmaf(l_run, alpha, lsum);
+    z_run = fmaf(z_run, alpha, zsum);
+    if (__builtin_amdgcn_ballot_w64(rescale != 1.0f) != 0) {
+#pragma unroll
+      for (int cb = 0; cb < 8; cb++) acc_o[cb] *= rescale;
+    }
+
+    // ---- P operand (split hi/lo) and PV
+    uint32_t bvh[FVS], bvl[FVS];
+#pragma unroll
+    for (int ff = 0; ff < FVS; ff++) {
+      // every sub-tile has the field layout of sub-tile 0, shifted by WVS
+      // words and TPS tokens
+      const Fld F = ufield<VB>(ff);
+      const float w = exp2i(F.wexp - F.pos);
+      split_pack(p[F.lo] * w, p[F.hi] * w, bvh[ff], bvl[ff]);
+    }
+#pragma unroll
+    for (int s = 0; s < NS; s++) {
+      uint32_t bsh[FVS], bsl[FVS];
+#pragma unroll
+      for (int ff = 0; ff < FVS; ff++) {
+        const bool sel = (NS == 1) || (own == s);
+        bsh[ff] = sel ? bvh[ff] : 0u;
+        bsl[ff] = sel ? bvl[ff] : 0u;
+      }
+#pragma unroll
+      for (int k = 0; k < KSV; k++) {
+        uint32_t av[8][4];
 #pragma unroll
         for (int cb = 0; cb < 8; cb++)
 #pragma unroll
-          for (int w = 0; w < WVS; w++)
-            vw[s][cb][w] = ((const uint32_t*)vt)[((sub * WVS + w) * 128 + 16 * cb + n) * 4 + lg];
-      }
-      // own stream's value scales / zeros for the lane's TPS tokens of this sub-tile
-      float vs[TPS], vz[TPS];
-      {
-        const int64_t vpb = v_param_base(g, b_own, h_own, (int64_t)tile * 128) + 32 * lg + sub * TPS;
+          for (int r = 0; r < 4; r++) {
+            const Fld F = ufield<VB>(4 * k + r);
+            av[cb][r] = field_subnormal(bf.vw[s][cb][F.w], F);
+          }
 #pragma unroll
-        for (int s8 = 0; s8 < TPS / 8; s8++) {
-          load_params8<PDT>(g.v_scale, vpb + 8 * s8, vs + 8 * s8);
-          load_params8<PDT>(g.v_zero, vpb + 8 * s8, vz + 8 * s8);
-        }
+        for (int cb = 0; cb < 8; cb++) acc_o[cb] = mfma(av[cb], bsh + 4 * k, acc_o[cb]);
 #pragma unroll
-        for (int i = 0; i < TPS; i++) {
-          vs[i] = real ? vs[i] : 0.0f;
-          vz[i] = real ? vz[i] : 0.0f;
-        }
+        for (int cb = 0; cb < 8; cb++) acc_o[cb] = mfma(av[cb], bsl + 4 * k, acc_o[cb]);
       }
+    }
+  };
 
-      // ---- logits (log2 domain) of the lane's column for JB blocks of 16 tokens
-      float lgt[JB][4];
-#pragma unroll
-      for (int jj = 0; jj < JB; jj++) {
-#pragma unroll
-        for (int i = 0; i < 4; i++) lgt[jj][i] = 0.0f;
-#pragma unroll
-        for (int s = 0; s < NS; s++) {
-          if (grp * NS + s >= BH) continue;
-          uint32_t av[NFK];
-#pragma unroll
-          for (int f = 0; f < NFK; f++) {
-            if constexpr (MIXED) {
-              av[f] = (lg == 0) ? field_subnormal(kw[s][jj][mfield0(f).w], mfield0(f))
-                                : field_subnormal(kw[s][jj][ufield<2>(f).w], ufield<2>(f));
-            } else {
-              av[f] = field_subnormal(kw[s][jj][ufield<KB>(f).w], ufield<KB>(f));
-            }
-          }
-          f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-          for (int k = 0; k < NKK; k++) {
-            acc = mfma(av + 4 * k, bkh + 4 * k, acc);
-            acc = mfma(av + 4 * k, bkl + 4 * k, acc);
-          }
-          if (NS == 1 || own == s) {
-#pragma unroll
-            for (int i = 0; i < 4; i++) lgt[jj][i] = acc[i];
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; i++) lgt[jj][i] = ak * lgt[jj][i] + bk0;
-      }
-
-      // ---- online softmax update; value-scale exponent
-      float tmax = -INFINITY, vsmax = 0.0f;
-#pragma unroll
-      for (int jj = 0; jj < JB; jj++)
-#pragma unroll
-        for (int i = 0; i < 4; i++) tmax = fmaxf(tmax, lgt[jj][i]);
-#pragma unroll
-      for (int i = 0; i < TPS; i++) vsmax = fmaxf(vsmax, vs[i]);
-      tmax = wave_max16x4(tmax);
-      const int ev = expo(wave_max16x4(vsmax));
-      const float m_new = fmaxf(m_run, tmax);
-      const float alpha = exp2f(m_run - m_new);
-      const int e_new = max(e_run, ev);
-      const float rescale = alpha * exp2i(e_run - e_new);
-      m_run = m_new;
-      e_run = e_new;
-      const float pf = exp2i(VH - e_new);
-      float p[TPS];
-      float lsum = 0.0f, zsum = 0.0f;
-#pragma unroll
-      for (int i = 0; i < TPS; i++) {
-        const float e = exp2f(lgt[i >> 2][i & 3] - m_new);
-        lsum += e;
-        zsum += e * vz[i];
-        p[i] = e * vs[i] * pf;
-      }
-      l_run = l_run * alpha + lsum;
-      z_run = z_run * alpha + zsum;
-#pragma unroll
-      for (int cb = 0; cb < 8; cb++) acc_o[cb] *= rescale;
-
-      // ---- P operand (split hi/lo) and PV
-      uint32_t bvh[FVS], bvl[FVS];
-#pragma unroll
-      for (int ff = 0; ff < FVS; ff++) {
-        // every sub-tile has the field layout of sub-tile 0, shifted by
-        // WVS words and TPS tokens
-        const Fld F = ufield<VB>(ff);
-        const float w = exp2i(F.wexp - F.pos);
-        split_pack(p[F.lo] * w, p[F.hi] * w, bvh[ff], bvl[ff]);
-      }
-#pragma unroll
-      for (int s = 0; s < NS; s++) {
-        if (grp * NS + s >= BH) continue;
-        uint32_t bsh[FVS], bsl[FVS];
-#pragma unroll
-        for (int ff = 0; ff < FVS; ff++) {
-          const bool sel = (NS == 1) || (own == s);
-          bsh[ff] = sel ? bvh[ff] : 0u;
-          bsl[ff] = sel ? bvl[ff] : 0u;
-        }
-#pragma unroll
-        for (int cb = 0; cb < 8; cb++) {
-          uint32_t av[FVS];
-#pragma unroll
-          for (int ff = 0; ff < FVS; ff++) {
-            const Fld F = ufield<VB>(ff);
-            av[ff] = field_subnormal(vw[s][cb][F.w], F);
-          }
-#pragma unroll
-          for (int k = 0; k < KSV; k++) {
-            acc_o[cb] = mfma(av + 4 * k, bsh + 4 * k, acc_o[cb]);
-            acc_o[cb] = mfma(av + 4 * k, bsl + 4 * k, acc_o[cb]);
-          }
-        }
-      }
+  // ---- software-pipelined main loop (two register buffers)
+  Buf b0, b1;
+  if (n_iter > 0) load(b0, 0);
+#pragma unroll 1
+  for (int it = 0; it < n_iter; it += 2) {
+    if (it + 1 < n_iter) load(b1, it + 1);
+    compute(b0, it);
+    if (it + 1 < n_iter) {
+      if (it + 2 < n_iter) load(b0, it + 2);
+      compute(b1, it + 1);
     }
   }
 
-  // ---- wave partial -> LDS -> workgroup partial (per column = stream, head)
+  // ---- wave partial -> LDS -> workgroup partial (per column = stream, head);
+  // each wave overwrites only its own LDS region, which it no longer reads
   __shared__ float sh_ml[4][16][2];
-  __shared__ float sh_o[4][16][128];
+  float(*sh_o)[16][128] = (float(*)[16][128])lds;
+  static_assert(sizeof(lds[0]) >= sizeof(float) * 16 * 128, "partial fits the wave region");
   const float l_tot = wave_sum16x4(l_run);
   const float z_tot = wave_sum16x4(z_run);
   const float of = exp2i(24 - VH + e_run);   // acc_o * 2^24 / pf
@@ -612,8 +782,8 @@ constexpr int ns_cap(int kb, int vb) {
 
 // Launch plan (shared by workspace sizing, validation and launch): NS streams
 // per wave, n_groups = ceil(BH / NS) stream groups, and the token tiles of a
-// group cut into n_chunks chunks of tpc tiles, aiming at about 512 workgroups
-// (two per CU, the register-limited residency) with 4..64 tiles per chunk and
+// group cut into n_chunks chunks of tpc tiles, aiming at one round of
+// resident workgroups (256 CUs x waves per SIMD) with 4..64 tiles per chunk and
 // at most KVQ_MAX_CHUNKS chunks.
 DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int n_tiles) {
   DecodePlan p;
@@ -622,7 +792,8 @@ DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int n_tiles) {
   p.ns = ns > cap ? cap : (ns < 1 ? 1 : ns);
   p.n_groups = (BH + p.ns - 1) / p.ns;
   const long total = (long)p.n_groups * n_tiles;
-  int tpc = (int)((total + 511) / 512);
+  const long wg_target = 256L * KVQ_DECODE_WAVES_PER_SIMD;   // one round of resident workgroups
+  int tpc = (int)((total + wg_target - 1) / wg_target);
   tpc = ((tpc + 3) / 4) * 4;
   if (tpc < 4) tpc = 4;
   if (tpc > 64) tpc = 64;

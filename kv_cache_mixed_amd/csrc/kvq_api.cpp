@@ -32,7 +32,7 @@ kvq_status check_cache(const kvq_cache* c) {
   if (!c) return KVQ_EINVAL;
   if (c->batch < 1 || c->n_kv_heads < 1) return KVQ_EINVAL;
   if (c->head_dim != KVQ_HEAD_DIM || c->group != KVQ_GROUP) return KVQ_EUNSUPPORTED;
-  if (c->max_tokens < 128 || c->max_tokens % 128) return KVQ_EINVAL;
+  if (c->max_tokens < 128 || c->max_tokens % 128 || c->max_tokens > KVQ_MAX_TOKENS) return KVQ_EINVAL;
   if (c->n_tokens < 0 || c->n_tokens % 128 || c->n_tokens > c->max_tokens) return KVQ_EINVAL;
   if (!valid_kbits(c->k_bits) || !valid_bits(c->v_bits)) return KVQ_EINVAL;
   if (!valid_pdt(c->param_dtype) || c->reserved0 != 0) return KVQ_EINVAL;

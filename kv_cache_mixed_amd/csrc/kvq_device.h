@@ -176,12 +176,15 @@ struct Geo {
   int32_t max_tokens;
 };
 
+// The offset tables are read through the constant address space (they never
+// change while a kernel runs), so a wave-uniform index becomes a scalar load.
+typedef const __attribute__((address_space(4))) int64_t* const_i64_ptr;
 __device__ __forceinline__ int64_t k_tile_offset(const Geo& g, int b, int h, int tile) {
-  if (g.k_off) return g.k_off[((int64_t)tile * g.B + b) * g.H + h];
+  if (g.k_off) return ((const_i64_ptr)g.k_off)[((int64_t)tile * g.B + b) * g.H + h];
   return (((int64_t)b * g.H + h) * g.max_tiles + tile) * g.k_stride;
 }
 __device__ __forceinline__ int64_t v_tile_offset(const Geo& g, int b, int h, int tile) {
-  if (g.v_off) return g.v_off[((int64_t)tile * g.B + b) * g.H + h];
+  if (g.v_off) return ((const_i64_ptr)g.v_off)[((int64_t)tile * g.B + b) * g.H + h];
   return (((int64_t)b * g.H + h) * g.max_tiles + tile) * g.v_stride;
 }
 // first parameter index of key tile (b, h, tile); value token (b, h, t)
