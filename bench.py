@@ -29,6 +29,22 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBS = 8000.0
 
+# HBM bytes of one decode launch as read by rocprofv3 counters (FETCH_SIZE and
+# WRITE_SIZE, KiB per dispatch) for the kernel source with the given digest,
+# and the factors that map each counter onto true bytes: a plain 512 MiB device
+# copy in the same run reads FETCH_SIZE = 262160.6 KiB and WRITE_SIZE =
+# 524288.0 KiB per dispatch, so the fetch counter is scaled by 524288/262160.6
+# and the write counter by 1.  The figure is reported only while the kernel
+# source is unchanged.
+COUNTER_TRAFFIC = {
+    "source_sha256": None,
+    "fetch_kib": None,
+    "write_kib": None,
+    "fetch_factor": 524288.0 / 262160.6,
+    "write_factor": 1.0,
+}
+KERNEL_SOURCES = ("kv_cache_mixed_amd/csrc/decode_attn.hip", "kv_cache_mixed_amd/csrc/kvq_device.h")
+
 
 def _parse():
     ap = argparse.ArgumentParser()
@@ -39,6 +55,9 @@ def _parse():
     ap.add_argument("--no-rows", action="store_true", help="time only the decode step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="approximate CPU work of the oracle baseline sample")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 512 MiB device copy three times (reference "
+                         "dispatch for scaling HBM counters)")
     return ap.parse_args()
 
 
@@ -48,6 +67,24 @@ def decode_bytes(B, H, Hq, T, k_bits, v_bits, pb):
     per_tok = (128 * k_bits + 128 * v_bits) // 8 if k_bits else 34 + 128 * v_bits // 8
     params = 2 * pb + 2 * pb          # key S,Z per token (128 per 128-token tile) + value S,Z
     return B * H * T * (per_tok + params) + B * Hq * 128 * 2 + B * Hq * 128 * 4
+
+
+def kernel_source_digest():
+    import hashlib
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def counter_traffic():
+    """HBM bytes per decode launch from the recorded counters, or None when the
+    kernel source changed since they were taken"""
+    c = COUNTER_TRAFFIC
+    if c["source_sha256"] is None or c["source_sha256"] != kernel_source_digest():
+        return None
+    return round((c["fetch_kib"] * c["fetch_factor"] + c["write_kib"] * c["write_factor"]) * 1024)
 
 
 def time_events(torch, fn, n, warmup):
@@ -218,6 +255,14 @@ def main():
         del sh
         torch.cuda.empty_cache()
 
+    if args.copy_calibration:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(inp, B, H, Hq, BITS, pdt, args.cpu_seconds)
@@ -243,7 +288,7 @@ def main():
         "pct_of_peak": round(100 * value / PEAK_HBM_GBS, 2),
         "algorithmic_bytes_per_step": alg,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
-                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": None,
+                     "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic(),
                      "kernel": "decode_kernel<4,4,f16,2>", "kernel_ms_avg": round(kern_avg, 5),
                      "kernel_ms_p10": round(srt[len(srt) // 10], 5),
                      "kernel_ms_p90": round(srt[(9 * len(srt)) // 10], 5)},
