@@ -199,9 +199,10 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads);
  * tokens (see "Decode attention" above).  q: device bfloat16
  * [B][n_q_heads][128]; out: device float32 [B][n_q_heads][128]; n_q_heads a
  * multiple of n_kv_heads with 1 <= n_q_heads / n_kv_heads <= 16; n_tokens >= 128.
- * workspace: device buffer of at least kvq_decode_workspace_bytes() bytes; it
- * must be zero-filled before its first use, and every call leaves it so.
- * Concurrent calls must not share a workspace. */
+ * workspace: device buffer of at least kvq_decode_workspace_bytes() bytes
+ * (per-chunk partials; no initial contents required).  When the tokens are
+ * split over several chunks a second kernel on the same stream combines the
+ * partials into out.  Concurrent calls must not share a workspace. */
 kvq_status kvq_decode_attn(const kvq_cache *cache, const void *q, int32_t n_q_heads,
                            float softmax_scale, float *out, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);

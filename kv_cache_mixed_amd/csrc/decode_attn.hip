@@ -46,6 +46,18 @@
 #ifndef KVQ_DECODE_WAVES_PER_SIMD
 #define KVQ_DECODE_WAVES_PER_SIMD 1
 #endif
+// most sub-tiles a 128-token tile is cut into (4, 2 or 1)
+#ifndef KVQ_DECODE_NSUB_MAX
+#define KVQ_DECODE_NSUB_MAX 4
+#endif
+// chunks own strided tile sets (1) or contiguous tile ranges (0)
+#ifndef KVQ_DECODE_STRIDED
+#define KVQ_DECODE_STRIDED 0
+#endif
+// workgroups one decode launch aims at
+#ifndef KVQ_DECODE_WG_TARGET
+#define KVQ_DECODE_WG_TARGET (256 * KVQ_DECODE_WAVES_PER_SIMD)
+#endif
 
 namespace kvq {
 
@@ -162,7 +174,6 @@ struct DecodeArgs {
   float* out;         // [B][Hq][128]
   float* part_ml;     // [BH][n_chunks][G][2]   (running max in log2 units, sum)
   float* part_o;      // [BH][n_chunks][G][128] (unnormalised output)
-  uint32_t* counters; // [n_groups]
   int G, n_chunks, tpc, n_groups;
   float sl2;          // softmax_scale * log2(e)
 };
@@ -272,7 +283,8 @@ __global__ __launch_bounds__(256, KVQ_DECODE_WAVES_PER_SIMD) void decode_kernel(
   constexpr int NKK = NFK / 4;                       // key k-steps
   constexpr int NFV = UInfo<VB>::NF;
   constexpr int NWV = UInfo<VB>::NW;
-  constexpr int NSUB = (VB == 1) ? 1 : ((VB == 2) ? 2 : 4);  // sub-tiles per tile
+  constexpr int NSUB0 = (VB == 1) ? 1 : ((VB == 2) ? 2 : 4);
+  constexpr int NSUB = NSUB0 < KVQ_DECODE_NSUB_MAX ? NSUB0 : KVQ_DECODE_NSUB_MAX;  // sub-tiles per tile
   constexpr int TPS = 32 / NSUB;                     // tokens per lane per sub-tile
   constexpr int JB = 8 / NSUB;                       // key blocks per sub-tile
   constexpr int FVS = NFV / NSUB;                    // value fields per sub-tile
@@ -309,9 +321,18 @@ __global__ __launch_bounds__(256, KVQ_DECODE_WAVES_PER_SIMD) void decode_kernel(
   const int bh_own = grp * NS + own;
   const bool real = (own < NS) && (bh_own < BH);
   const int b_own = real ? bh_own / g.H : 0, h_own = real ? bh_own % g.H : 0;
-  const int t_begin = chunk * a.tpc;
-  const int t_end = min(t_begin + a.tpc, g.n_tiles);
-  const int my_tiles = (t_end - t_begin - wave + 3) / 4;   // tiles t_begin + wave + 4i
+#if KVQ_DECODE_STRIDED
+  // chunk c owns tiles c, c + n_chunks, ...; wave w takes every fourth of them,
+  // so at any moment the workgroups of a stream read neighbouring tiles
+  const int t_count = (g.n_tiles - chunk + a.n_chunks - 1) / a.n_chunks;
+  const int t_step = 4 * a.n_chunks;
+  const int t_first = chunk + wave * a.n_chunks;
+#else
+  const int t_count = min(a.tpc, g.n_tiles - chunk * a.tpc);
+  const int t_step = 4;
+  const int t_first = chunk * a.tpc + wave;
+#endif
+  const int my_tiles = (t_count - wave + 3) / 4;
   const int n_iter = (my_tiles > 0 ? my_tiles : 0) * NSUB;
 
   auto kslot = [&](int li) -> int {
@@ -385,7 +406,7 @@ __global__ __launch_bounds__(256, KVQ_DECODE_WAVES_PER_SIMD) void decode_kernel(
   };
 
   auto load = [&](Buf& bf, int it) {
-    const int tile = t_begin + wave + 4 * (it / NSUB);
+    const int tile = t_first + t_step * (it / NSUB);
     const int sub = it % NSUB;
 #pragma unroll
     for (int s = 0; s < NS; s++) {
@@ -688,88 +709,8 @@ __global__ __launch_bounds__(256, KVQ_DECODE_WAVES_PER_SIMD) void decode_kernel(
       a.part_o[row * 128 + c] = num;
     }
   }
-  if (single) return;
-
-  // ---- the last workgroup of the stream group combines all chunks:
-  //   o = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k
-  // All loads of a phase are independent and coalesced, so the combine costs
-  // a few memory round trips, not one per chunk.
-  __shared__ int s_last;
-  __shared__ float s_w[KVQ_MAX_CHUNKS][16];
-  __shared__ float s_red[16][16];
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const uint32_t prev = atomicAdd(&a.counters[grp], 1u);
-    s_last = (prev == (uint32_t)(a.n_chunks - 1));
-  }
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  const int nck = a.n_chunks;
-  // phase 1: chunk maxima -> per-column maximum
-  for (int idx = threadIdx.x; idx < nck * ncol; idx += 256) {
-    const int k = idx / ncol, col = idx - k * ncol;
-    const int s = col / G, hh = col - s * G;
-    const int bh = grp * NS + s;
-    s_w[k][col] = (bh < BH) ? __builtin_nontemporal_load(a.part_ml + 2 * (((int64_t)bh * nck + k) * G + hh))
-                            : 0.0f;
-  }
-  __syncthreads();
-  {
-    const int col = threadIdx.x >> 4, part = threadIdx.x & 15;
-    float M = -INFINITY;
-    if (col < ncol)
-      for (int k = part; k < nck; k += 16) M = fmaxf(M, s_w[k][col]);
-    s_red[col][part] = M;
-  }
-  __syncthreads();
-  // phase 2: weights 2^(m_k - M) and the denominator
-  if (threadIdx.x < 16) {
-    float M = -INFINITY;
-    for (int i = 0; i < 16; i++) M = fmaxf(M, s_red[threadIdx.x][i]);
-    s_red[threadIdx.x][0] = M;
-  }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < nck * ncol; idx += 256) {
-    const int k = idx / ncol, col = idx - k * ncol;
-    s_w[k][col] = exp2f(s_w[k][col] - s_red[col][0]);
-  }
-  __syncthreads();
-  {
-    const int col = threadIdx.x >> 4, part = threadIdx.x & 15;
-    float den = 0.0f;
-    if (col < ncol) {
-      const int s = col / G, hh = col - s * G;
-      const int bh = grp * NS + s;
-      if (bh < BH)
-        for (int k = part; k < nck; k += 16)
-          den += s_w[k][col] * __builtin_nontemporal_load(a.part_ml + 2 * (((int64_t)bh * nck + k) * G + hh) + 1);
-    }
-    for (int o = 8; o >= 1; o >>= 1) den += __shfl_xor(den, o, 16);
-    if (part == 0 && col < ncol) s_red[col][1] = den;
-  }
-  __syncthreads();
-  // phase 3: weighted sum of the chunk outputs, 4 channels per thread
-  for (int idx = threadIdx.x; idx < ncol * 32; idx += 256) {
-    const int col = idx >> 5, c4 = (idx & 31) * 4;
-    const int s = col / G, hh = col - s * G;
-    const int bh = grp * NS + s;
-    if (bh >= BH) continue;
-    const float* po = a.part_o + (((int64_t)bh * nck) * G + hh) * 128 + c4;
-    const int64_t ks = (int64_t)G * 128;
-    f32x4 acc = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int k = 0; k < nck; k++) {
-      const f32x4 v = __builtin_nontemporal_load((const f32x4*)(po + k * ks));
-      acc += s_w[k][col] * v;
-    }
-    const float inv = 1.0f / s_red[col][1];
-    const int bo = bh / g.H, ho = bh % g.H;
-    *(f32x4*)(a.out + ((int64_t)bo * Hq + (int64_t)ho * G + hh) * 128 + c4) = acc * inv;
-  }
-  if (threadIdx.x == 0) a.counters[grp] = 0u;
 }
+
 
 // ---------------------------------------------------------------------------
 // host side
@@ -792,7 +733,7 @@ DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int n_tiles) {
   p.ns = ns > cap ? cap : (ns < 1 ? 1 : ns);
   p.n_groups = (BH + p.ns - 1) / p.ns;
   const long total = (long)p.n_groups * n_tiles;
-  const long wg_target = 256L * KVQ_DECODE_WAVES_PER_SIMD;   // one round of resident workgroups
+  const long wg_target = KVQ_DECODE_WG_TARGET;   // about one round of resident workgroups
   int tpc = (int)((total + wg_target - 1) / wg_target);
   tpc = ((tpc + 3) / 4) * 4;
   if (tpc < 4) tpc = 4;
@@ -804,13 +745,42 @@ DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int n_tiles) {
   return p;
 }
 
-static size_t counters_bytes(int BH) { return ((size_t)BH * 4 + 255) / 256 * 256; }
+// Chunk combine (one workgroup per (batch, kv head) stream, a separate launch
+// so that the partials are visible without device-scope fences):
+//   o = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k
+// thread = (head, 4 channels); the loads of each pass are independent.
+__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part_ml,
+                                                             const float* __restrict__ part_o,
+                                                             float* __restrict__ out, int H, int G,
+                                                             int nck) {
+  const int bh = blockIdx.x;
+  const int bo = bh / H, ho = bh % H;
+  for (int idx = threadIdx.x; idx < G * 32; idx += 256) {
+    const int hh = idx >> 5, c4 = (idx & 31) * 4;
+    const float* ml = part_ml + 2 * ((int64_t)bh * nck * G + hh);
+    const float* po = part_o + ((int64_t)bh * nck * G + hh) * 128 + c4;
+    const int64_t step = G;   // rows between chunks
+    float M = -INFINITY;
+#pragma unroll 8
+    for (int k = 0; k < nck; k++) M = fmaxf(M, ml[2 * step * k]);
+    float den = 0.0f;
+    f32x4 num = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll 8
+    for (int k = 0; k < nck; k++) {
+      const float w = exp2f(ml[2 * step * k] - M);   // 0 for an empty chunk (m = -inf)
+      den += w * ml[2 * step * k + 1];
+      num += w * *(const f32x4*)(po + step * 128 * k);
+    }
+    *(f32x4*)(out + ((int64_t)bo * H * G + (int64_t)ho * G + hh) * 128 + c4) = num * (1.0f / den);
+  }
+}
+
 static size_t ml_bytes(int BH, int n_chunks, int G) {
   return ((size_t)BH * n_chunks * G * 2 * 4 + 255) / 256 * 256;
 }
 
 size_t decode_workspace_needed(int BH, int G, const DecodePlan& p) {
-  return counters_bytes(BH) + ml_bytes(BH, p.n_chunks, G) + (size_t)BH * p.n_chunks * G * 128 * 4;
+  return ml_bytes(BH, p.n_chunks, G) + (size_t)BH * p.n_chunks * G * 128 * 4;
 }
 
 size_t decode_workspace_bytes(int B, int H, int G, int max_tiles) {
@@ -846,6 +816,10 @@ static hipError_t launch_ns(const DecodeArgs& a0, hipStream_t st) {
   } else {
     if constexpr (CAP >= 3) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 3>), grid, block, 0, st, a);
   }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.n_chunks == 1) return e;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.g.B * a.g.H), dim3(256), 0, st,
+                     (const float*)a.part_ml, (const float*)a.part_o, a.out, a.g.H, a.G, a.n_chunks);
   return hipGetLastError();
 }
 
@@ -868,8 +842,7 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
   a.out = out;
   const int BH = g.B * g.H;
   const DecodePlan p = decode_plan(BH, G, g.k_bits, g.v_bits, g.n_tiles);
-  a.counters = (uint32_t*)ws;
-  a.part_ml = (float*)((uint8_t*)ws + counters_bytes(BH));
+  a.part_ml = (float*)ws;
   a.part_o = (float*)((uint8_t*)a.part_ml + ml_bytes(BH, p.n_chunks, G));
   a.G = G;
   a.sl2 = scale * 1.4426950408889634f;

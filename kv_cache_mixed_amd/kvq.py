@@ -13,7 +13,8 @@ import os
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkvq.so")
+# KVQ_LIB selects another build of the same library (for example a tuning variant)
+LIB_PATH = os.environ.get("KVQ_LIB") or os.path.join(_HERE, "libkvq.so")
 
 F32, F16, BF16, E4M3 = 0, 1, 2, 3
 PARAM_BYTES = {F32: 4, F16: 2, BF16: 2, E4M3: 1}

@@ -139,16 +139,18 @@ def test_decode_other_param_dtypes(pdt):
 
 
 def test_decode_repeat_and_workspace_reuse():
-    """The workspace counters reset themselves: repeated calls give identical output."""
+    """Repeated calls give identical output, and the workspace needs no initial
+    contents: a workspace filled with garbage (NaN bit patterns included) gives
+    the same bits."""
     inp, cache = _quantized(2, 2, 8, 4096, 4, 4, kvq.F16, seed=95)
     q = q_to_dev(inp["q_bf16"], torch)
     o1 = cache.decode_attn(q, SCALE).cpu().numpy()
     o2 = cache.decode_attn(q, SCALE).cpu().numpy()
-    o3 = cache.decode_attn(q, SCALE).cpu().numpy()
-    assert np.array_equal(o1, o2) and np.array_equal(o2, o3)
     ws = cache.workspace(8)
-    n_counters = 2 * 2
-    assert int(ws[:4 * n_counters].view(torch.int32).abs().sum().item()) == 0
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=torch.Generator().manual_seed(7)))
+    ws[:64].fill_(0xff)
+    o3 = cache.decode_attn(q, SCALE, workspace=ws).cpu().numpy()
+    assert np.array_equal(o1, o2) and np.array_equal(o2, o3)
 
 
 def test_tiny_config():
