@@ -43,8 +43,10 @@
 // the output accumulator is rescaled only when some head's reference moved.
 #include "kvq_device.h"
 // waves of the decode kernel resident per SIMD (register budget 512 / n)
+// A nonzero KVQ_DECODE_WAVES_PER_SIMD forces every decode instance to that
+// occupancy (tuning builds); 0 uses the per-instance table decode_occ().
 #ifndef KVQ_DECODE_WAVES_PER_SIMD
-#define KVQ_DECODE_WAVES_PER_SIMD 1
+#define KVQ_DECODE_WAVES_PER_SIMD 0
 #endif
 // most sub-tiles a 128-token tile is cut into (4, 2 or 1)
 #ifndef KVQ_DECODE_NSUB_MAX
@@ -54,9 +56,13 @@
 #ifndef KVQ_DECODE_STRIDED
 #define KVQ_DECODE_STRIDED 0
 #endif
-// workgroups one decode launch aims at
-#ifndef KVQ_DECODE_WG_TARGET
-#define KVQ_DECODE_WG_TARGET (256 * KVQ_DECODE_WAVES_PER_SIMD)
+// most kv streams one decode wave packs into its MFMA columns
+#ifndef KVQ_DECODE_NS_MAX
+#define KVQ_DECODE_NS_MAX 3
+#endif
+// workgroups one decode launch aims at per wave-per-SIMD of the instance
+#ifndef KVQ_DECODE_WG_PER_OCC
+#define KVQ_DECODE_WG_PER_OCC 256
 #endif
 
 namespace kvq {
@@ -231,6 +237,25 @@ __device__ __forceinline__ float praw(const uint32_t* w) {
     return u2f((I % 2) ? (w[I / 2] & 0xffff0000u) : (w[I / 2] << 16));
   }
 }
+// parameter i of a raw parameter-word array, i a constant after unrolling
+template <int PDT>
+__device__ __forceinline__ float pget(const uint32_t* w, int i) {
+  if constexpr (PDT == KVQ_E4M3) {
+    const int x = (int)w[i / 4];
+    switch (i & 3) {
+      case 0: return __builtin_amdgcn_cvt_f32_fp8(x, 0);
+      case 1: return __builtin_amdgcn_cvt_f32_fp8(x, 1);
+      case 2: return __builtin_amdgcn_cvt_f32_fp8(x, 2);
+      default: return __builtin_amdgcn_cvt_f32_fp8(x, 3);
+    }
+  } else if constexpr (PDT == KVQ_F32) {
+    return u2f(w[i]);
+  } else if constexpr (PDT == KVQ_F16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)((w[i / 2] >> (16 * (i % 2))) & 0xffffu));
+  } else {
+    return u2f((i % 2) ? (w[i / 2] & 0xffff0000u) : (w[i / 2] << 16));
+  }
+}
 template <int PDT, int N>
 __device__ __forceinline__ void praw_unpack(const uint32_t* w, float* out) {
   if constexpr (N > 0) {
@@ -263,6 +288,20 @@ __device__ __forceinline__ void pload(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
   }
 }
 
+// Waves per SIMD a decode instance is compiled for.  Two (two workgroups of 4
+// waves per CU) wherever the instance fits in 256 registers per lane with at
+// most a few spilled words -- the stream counts of ns_cap() are chosen for
+// that; measured, a second resident wave hides more latency than any
+// register-hungry schedule of a single one.  16-bit codes and mixed keys with
+// 1-bit values need the full register file.
+constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
+  (void)pdt;
+  (void)ns;
+  if (KVQ_DECODE_WAVES_PER_SIMD) return KVQ_DECODE_WAVES_PER_SIMD;
+  if (kb == 16 || (kb == 0 && vb == 1)) return 1;
+  return 2;
+}
+
 // KB: 16/8/4/2/1 or 0 (mixed keys).  VB: 16/8/4/2/1.  NS: kv streams packed
 // into the 16 MFMA columns (column n serves stream n / G, head n % G).
 //
@@ -276,7 +315,7 @@ __device__ __forceinline__ void pload(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 // that serve no head have q = 0, so their operands are harmless and never
 // masked.
 template <int KB, int VB, int PDT, int NS>
-__global__ __launch_bounds__(256, KVQ_DECODE_WAVES_PER_SIMD) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kernel(DecodeArgs a) {
   constexpr bool MIXED = (KB == 0);
   constexpr int NFK = MIXED ? 16 : UInfo<KB>::NF;    // key operand registers per token
   constexpr int NWK = MIXED ? 3 : UInfo<KB>::NW;     // key words per lane per token
@@ -309,6 +348,8 @@ __global__ __launch_bounds__(256, KVQ_DECODE_WAVES_PER_SIMD) void decode_kernel(
   __shared__ __attribute__((aligned(16))) uint32_t lds[4][LDS_WAVE];
   // key scales / zeros of the current tile of each stream, per wave
   __shared__ __attribute__((aligned(16))) uint32_t kst[4][NS][2][KPA];
+  // query heads of the group in slot order
+  __shared__ __attribute__((aligned(16))) uint16_t qs[16][128];
 
   const Geo& g = a.g;
   // the wave index is uniform: keep it (and everything derived) in SGPRs
@@ -362,32 +403,42 @@ __global__ __launch_bounds__(256, KVQ_DECODE_WAVES_PER_SIMD) void decode_kernel(
   // lanes 32.. repeat words 0..31)
   const uint32_t kloff = (uint32_t)((PB == 1) ? (lane & 31) : lane) * 4;
 
-  // ---- own query head over the lane's 32 key slots, kept as bf16 pairs
-  uint32_t qp[16];
-  {
-    const uint16_t* qrow = a.q + ((int64_t)b_own * (g.H * G) + (int64_t)h_own * G + hn) * 128;
+  // ---- the query heads of the group in slot order, [column][slot] bf16 in
+  // LDS (column n = stream n / G, head n % G; zero for columns without a head)
 #pragma unroll
-    for (int i = 0; i < 16; i++) {
-      uint32_t lo = 0, hi = 0;
-      if (real) {
-        if constexpr (MIXED) {
-          lo = qrow[g.slot_chan[h_own * 128 + kslot(2 * i)]];
-          hi = qrow[g.slot_chan[h_own * 128 + kslot(2 * i + 1)]];
-        } else {
-          lo = qrow[kslot(2 * i)];
-          hi = qrow[kslot(2 * i + 1)];
-        }
-      }
-      qp[i] = lo | (hi << 16);
+  for (int i = threadIdx.x; i < 16 * 128; i += 256) {
+    const int cn = i >> 7, j = i & 127;
+    const int cs = cn / G, ch = cn - cs * G;
+    const int cbh = grp * NS + cs;
+    uint16_t v = 0;
+    if (cs < NS && cbh < BH) {
+      const int cb = cbh / g.H, chh = cbh % g.H;
+      const int chan = MIXED ? (int)g.slot_chan[chh * 128 + j] : j;
+      v = a.q[((int64_t)cb * (g.H * G) + (int64_t)chh * G + ch) * 128 + chan];
     }
+    qs[cn][j] = v;
   }
-  auto qval = [&](int li) -> float {
-    return (li & 1) ? u2f(qp[li >> 1] & 0xffff0000u) : u2f(qp[li >> 1] << 16);
-  };
-  uint32_t qmax = 0;
+  __syncthreads();
+  // the lane's 32 query values (slots kslot(0..31)) as bf16 pairs
+  auto load_q = [&](uint32_t* qw) {
 #pragma unroll
-  for (int li = 0; li < 32; li++) qmax = max(qmax, f2u(qval(li)) & 0x7fffffffu);
-  const int eq = expo(u2f(wave_maxu16x4(qmax)));
+    for (int c = 0; c < 4; c++) {
+      const u32x4 v = *(const u32x4*)&qs[n][kslot(8 * c)];
+      qw[4 * c] = v[0]; qw[4 * c + 1] = v[1]; qw[4 * c + 2] = v[2]; qw[4 * c + 3] = v[3];
+    }
+  };
+  auto qget = [](const uint32_t* qw, int li) -> float {
+    return (li & 1) ? u2f(qw[li >> 1] & 0xffff0000u) : u2f(qw[li >> 1] << 16);
+  };
+  int eq;
+  {
+    uint32_t qw[16];
+    load_q(qw);
+    uint32_t qmax = 0;
+#pragma unroll
+    for (int li = 0; li < 32; li++) qmax = max(qmax, f2u(qget(qw, li)) & 0x7fffffffu);
+    eq = expo(u2f(wave_maxu16x4(qmax)));
+  }
 
   float m_run = -INFINITY, l_run = 0.0f, z_run = 0.0f;
   int e_run = -1000;
@@ -479,42 +530,51 @@ __global__ __launch_bounds__(256, KVQ_DECODE_WAVES_PER_SIMD) void decode_kernel(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    uint32_t kss[4][PWK], kzz[4][PWK];
+    // raw words of the lane's 32 key parameters (four runs of 8 slots)
+    auto load_kp = [&](int which, uint32_t* pw) {
 #pragma unroll
-    for (int s4 = 0; s4 < 4; s4++) {
-      const int wo = kslot(8 * s4) * PB / 4;
+      for (int s4 = 0; s4 < 4; s4++) {
+        const int wo = kslot(8 * s4) * PB / 4;
 #pragma unroll
-      for (int i = 0; i < PWK; i++) {
-        kss[s4][i] = kst[wave][own_c][0][wo + i];
-        kzz[s4][i] = kst[wave][own_c][1][wo + i];
+        for (int i = 0; i < PWK; i++) pw[s4 * PWK + i] = kst[wave][own_c][which][wo + i];
       }
-    }
-    float ks[32], kz[32];
-#pragma unroll
-    for (int s4 = 0; s4 < 4; s4++) {
-      praw_unpack<PDT, 8>(kss[s4], ks + 8 * s4);
-      praw_unpack<PDT, 8>(kzz[s4], kz + 8 * s4);
-    }
-    uint32_t smax = 0;
+    };
+    uint32_t qw[16];
+    load_q(qw);
     float beta = 0.0f;
+    {
+      uint32_t zw[4 * PWK];
+      load_kp(1, zw);
 #pragma unroll
-    for (int li = 0; li < 32; li++) {
-      smax = max(smax, f2u(ks[li]));   // scales are >= +0
-      beta = fmaf(qval(li), kz[li], beta);
+      for (int li = 0; li < 32; li++) beta = fmaf(qget(qw, li), pget<PDT>(zw, li), beta);
     }
+    uint32_t sw[4 * PWK];
+    load_kp(0, sw);
+    uint32_t smax = 0;
+#pragma unroll
+    for (int li = 0; li < 32; li++) smax = max(smax, f2u(pget<PDT>(sw, li)));   // scales are >= +0
     // eq + es is bounded below so that kf * 2^(field weight) stays finite when
     // a tile's scales are all zero (codes then 0, u = 0)
     const int eqs = max(eq + expo(u2f(wave_maxu16x4(smax))), -100);
     beta = wave_sum16x4(beta);
     const float kf = exp2i(KH - eqs);
+    auto uval = [&](int li) -> float { return qget(qw, li) * pget<PDT>(sw, li); };
 #pragma unroll
     for (int f = 0; f < NFK; f++) {
-      Fld F;
-      if constexpr (MIXED) F = (lg == 0) ? mfield0(f) : ufield<2>(f);
-      else F = ufield<KB>(f);
-      const float w = kf * exp2i(F.wexp - F.pos);
+      float ul, uh, w;
+      if constexpr (MIXED) {
+        const Fld F0 = mfield0(f), F1 = ufield<2>(f);
+        ul = (lg == 0) ? uval(F0.lo) : uval(F1.lo);
+        uh = (lg == 0) ? uval(F0.hi) : uval(F1.hi);
+        w = kf * ((lg == 0) ? exp2i(F0.wexp - F0.pos) : exp2i(F1.wexp - F1.pos));
+      } else {
+        const Fld F = ufield<KB>(f);
+        ul = uval(F.lo);
+        uh = uval(F.hi);
+        w = kf * exp2i(F.wexp - F.pos);
+      }
       uint32_t hi, lo;
-      split_pack(qval(F.lo) * ks[F.lo] * w, qval(F.hi) * ks[F.hi] * w, hi, lo);
+      split_pack(ul * w, uh * w, hi, lo);
       // [k-step][hi/lo][lane][4]: one ds_read_b128 per operand group
       my_lds[(((f >> 2) * 2 + 0) * 64 + lane) * 4 + (f & 3)] = hi;
       my_lds[(((f >> 2) * 2 + 1) * 64 + lane) * 4 + (f & 3)] = lo;
@@ -718,7 +778,8 @@ __global__ __launch_bounds__(256, KVQ_DECODE_WAVES_PER_SIMD) void decode_kernel(
 // kv streams per wave: as many query groups as fit the 16 MFMA columns,
 // capped per width so the kernel keeps two waves per SIMD without spilling.
 constexpr int ns_cap(int kb, int vb) {
-  return (kb == 16 || vb == 16 || kb == 1 || vb == 1) ? 1 : (kb == 4 ? 3 : 2);
+  if (kb == 0) return vb == 4 ? 2 : 1;
+  return (kb == 4 || kb == 2) ? 2 : 1;
 }
 
 // Launch plan (shared by workspace sizing, validation and launch): NS streams
@@ -726,14 +787,16 @@ constexpr int ns_cap(int kb, int vb) {
 // group cut into n_chunks chunks of tpc tiles, aiming at one round of
 // resident workgroups (256 CUs x waves per SIMD) with 4..64 tiles per chunk and
 // at most KVQ_MAX_CHUNKS chunks.
-DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int n_tiles) {
+DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_tiles) {
   DecodePlan p;
   const int cap = ns_cap(k_bits, v_bits);
   int ns = 16 / G;
+  if (ns > KVQ_DECODE_NS_MAX) ns = KVQ_DECODE_NS_MAX;
   p.ns = ns > cap ? cap : (ns < 1 ? 1 : ns);
   p.n_groups = (BH + p.ns - 1) / p.ns;
   const long total = (long)p.n_groups * n_tiles;
-  const long wg_target = KVQ_DECODE_WG_TARGET;   // about one round of resident workgroups
+  // about one round of resident workgroups
+  const long wg_target = (long)KVQ_DECODE_WG_PER_OCC * decode_occ(k_bits, v_bits, pdt, p.ns);
   int tpc = (int)((total + wg_target - 1) / wg_target);
   tpc = ((tpc + 3) / 4) * 4;
   if (tpc < 4) tpc = 4;
@@ -745,34 +808,57 @@ DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int n_tiles) {
   return p;
 }
 
-// Chunk combine (one workgroup per (batch, kv head) stream, a separate launch
-// so that the partials are visible without device-scope fences):
-//   o = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k
-// thread = (head, 4 channels); the loads of each pass are independent.
+// Chunk combine, a separate launch so that the partials are visible without
+// device-scope fences.  One wave per output row (batch, query head):
+//   o = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k.
+// Lane k holds the (m, l) of chunks k and k + 64; each lane owns two channels
+// of o and walks the chunks with the weight broadcast from its owner lane.
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part_ml,
                                                              const float* __restrict__ part_o,
-                                                             float* __restrict__ out, int H, int G,
-                                                             int nck) {
-  const int bh = blockIdx.x;
-  const int bo = bh / H, ho = bh % H;
-  for (int idx = threadIdx.x; idx < G * 32; idx += 256) {
-    const int hh = idx >> 5, c4 = (idx & 31) * 4;
-    const float* ml = part_ml + 2 * ((int64_t)bh * nck * G + hh);
-    const float* po = part_o + ((int64_t)bh * nck * G + hh) * 128 + c4;
-    const int64_t step = G;   // rows between chunks
-    float M = -INFINITY;
-#pragma unroll 8
-    for (int k = 0; k < nck; k++) M = fmaxf(M, ml[2 * step * k]);
-    float den = 0.0f;
-    f32x4 num = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll 8
-    for (int k = 0; k < nck; k++) {
-      const float w = exp2f(ml[2 * step * k] - M);   // 0 for an empty chunk (m = -inf)
-      den += w * ml[2 * step * k + 1];
-      num += w * *(const f32x4*)(po + step * 128 * k);
-    }
-    *(f32x4*)(out + ((int64_t)bo * H * G + (int64_t)ho * G + hh) * 128 + c4) = num * (1.0f / den);
+                                                             float* __restrict__ out, int BH, int H,
+                                                             int G, int nck) {
+  const int lane = threadIdx.x & 63;
+  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);   // bh * G + hh
+  if (row >= BH * G) return;
+  const int bh = row / G, hh = row - (row / G) * G;
+  const int64_t r0 = (int64_t)bh * nck * G + hh;         // partial row of chunk 0
+  float m0 = -INFINITY, m1 = -INFINITY, l0 = 0.0f, l1 = 0.0f;
+  if (lane < nck) { m0 = part_ml[2 * (r0 + (int64_t)lane * G)]; l0 = part_ml[2 * (r0 + (int64_t)lane * G) + 1]; }
+  if (lane + 64 < nck) {
+    m1 = part_ml[2 * (r0 + (int64_t)(lane + 64) * G)];
+    l1 = part_ml[2 * (r0 + (int64_t)(lane + 64) * G) + 1];
   }
+  // the first 16 chunk outputs are loaded before the weights are known, so a
+  // typical combine costs one memory round trip
+  const float* po = part_o + r0 * 128 + 2 * lane;
+  const int64_t step = (int64_t)G * 128;
+  float2 v[16];
+#pragma unroll
+  for (int k = 0; k < 16; k++) v[k] = (k < nck) ? *(const float2*)(po + step * k) : make_float2(0.f, 0.f);
+  float M = fmaxf(m0, m1);
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
+  const float w0 = exp2f(m0 - M), w1 = exp2f(m1 - M);   // 0 for absent chunks
+  float den = w0 * l0 + w1 * l1;
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
+  float n0 = 0.0f, n1 = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; k++) {
+    const float w = u2f(__builtin_amdgcn_readlane(f2u(w0), k));   // 0 beyond nck
+    n0 = fmaf(w, v[k].x, n0);
+    n1 = fmaf(w, v[k].y, n1);
+  }
+#pragma unroll 8
+  for (int k = 16; k < nck; k++) {
+    const float w = u2f(__builtin_amdgcn_readlane(f2u(k < 64 ? w0 : w1), k & 63));
+    const float2 x = *(const float2*)(po + step * k);
+    n0 = fmaf(w, x.x, n0);
+    n1 = fmaf(w, x.y, n1);
+  }
+  const float inv = 1.0f / den;
+  const int bo = bh / H, ho = bh - (bh / H) * H;
+  *(float2*)(out + ((int64_t)bo * H * G + (int64_t)ho * G + hh) * 128 + 2 * lane) = make_float2(n0 * inv, n1 * inv);
 }
 
 static size_t ml_bytes(int BH, int n_chunks, int G) {
@@ -804,7 +890,7 @@ template <int KB, int VB, int PDT>
 static hipError_t launch_ns(const DecodeArgs& a0, hipStream_t st) {
   constexpr int CAP = ns_cap(KB, VB);
   DecodeArgs a = a0;
-  const DecodePlan p = decode_plan(a.g.B * a.g.H, a.G, KB, VB, a.g.n_tiles);
+  const DecodePlan p = decode_plan(a.g.B * a.g.H, a.G, KB, VB, PDT, a.g.n_tiles);
   a.n_groups = p.n_groups;
   a.n_chunks = p.n_chunks;
   a.tpc = p.tpc;
@@ -818,8 +904,9 @@ static hipError_t launch_ns(const DecodeArgs& a0, hipStream_t st) {
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3(a.g.B * a.g.H), dim3(256), 0, st,
-                     (const float*)a.part_ml, (const float*)a.part_o, a.out, a.g.H, a.G, a.n_chunks);
+  const int rows = a.g.B * a.g.H * a.G;
+  hipLaunchKernelGGL(decode_combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, (const float*)a.part_ml,
+                     (const float*)a.part_o, a.out, a.g.B * a.g.H, a.g.H, a.G, a.n_chunks);
   return hipGetLastError();
 }
 
@@ -841,7 +928,7 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
   a.q = (const uint16_t*)q;
   a.out = out;
   const int BH = g.B * g.H;
-  const DecodePlan p = decode_plan(BH, G, g.k_bits, g.v_bits, g.n_tiles);
+  const DecodePlan p = decode_plan(BH, G, g.k_bits, g.v_bits, g.pdt, g.n_tiles);
   a.part_ml = (float*)ws;
   a.part_o = (float*)((uint8_t*)a.part_ml + ml_bytes(BH, p.n_chunks, G));
   a.G = G;

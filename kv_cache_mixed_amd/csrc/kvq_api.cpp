@@ -182,7 +182,7 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t n_q_heads,
     // the plan of this call must fit the workspace (guaranteed by the bound
     // above; checked so a sizing mistake can never turn into stray writes)
     const kvq::DecodePlan plan = kvq::decode_plan(c->batch * c->n_kv_heads, G, c->k_bits, c->v_bits,
-                                                  c->n_tokens / 128);
+                                                  c->param_dtype, c->n_tokens / 128);
     if (kvq::decode_workspace_needed(c->batch * c->n_kv_heads, G, plan) > workspace_bytes ||
         plan.n_chunks > kvq::KVQ_MAX_CHUNKS || plan.n_chunks * plan.tpc < c->n_tokens / 128)
       return KVQ_EWORKSPACE;

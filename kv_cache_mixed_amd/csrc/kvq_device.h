@@ -212,7 +212,7 @@ constexpr int KVQ_MAX_CHUNKS = 128;
 struct DecodePlan {
   int ns, n_groups, n_chunks, tpc;
 };
-DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int n_tiles);
+DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_tiles);
 size_t decode_workspace_needed(int BH, int G, const DecodePlan& p);
 size_t decode_workspace_bytes(int B, int H, int G, int max_tiles);
 hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float* out,
