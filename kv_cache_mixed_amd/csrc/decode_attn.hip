@@ -725,7 +725,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // ---- wave partial -> LDS -> workgroup partial (per column = stream, head);
   // each wave overwrites only its own LDS region, which it no longer reads
   __shared__ float sh_ml[4][16][2];
-  float(*sh_o)[16][128] = (float(*)[16][128])lds;
+  // wave w's partial [16][128] sits at the start of ITS OWN region lds[w]
+  // (regions are LDS_WAVE words apart, more than 16*128 for 16-bit codes)
+  auto sh_o = [&](int w, int col, int c) -> float& { return ((float*)&lds[w][0])[col * 128 + c]; };
   static_assert(sizeof(lds[0]) >= sizeof(float) * 16 * 128, "partial fits the wave region");
   const float l_tot = wave_sum16x4(l_run);
   const float z_tot = wave_sum16x4(z_run);
@@ -738,7 +740,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   for (int cb = 0; cb < 8; cb++)
 #pragma unroll
     for (int i = 0; i < 4; i++)
-      sh_o[wave][n][16 * cb + 4 * lg + i] = (m_run == -INFINITY) ? 0.0f : acc_o[cb][i] * of + z_tot;
+      sh_o(wave, n, 16 * cb + 4 * lg + i) = (m_run == -INFINITY) ? 0.0f : acc_o[cb][i] * of + z_tot;
   __syncthreads();
 
   const int Hq = g.H * G;
@@ -757,7 +759,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     for (int w = 0; w < 4; w++) {
       const float mw = sh_ml[w][col][0];
       const float sc = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
-      num += sc * sh_o[w][col][c];
+      num += sc * sh_o(w, col, c);
       den += sc * sh_ml[w][col][1];
     }
     const int bo = bh / g.H, ho = bh % g.H;

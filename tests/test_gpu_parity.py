@@ -114,6 +114,16 @@ def test_decode_uniform(bits, pdt):
     _decode_case(2, 2, 14, 1152, bits, bits, pdt, seed=40 + bits)
 
 
+@pytest.mark.parametrize("bits", [16, 8])
+def test_decode_several_tiles_per_wave(bits):
+    """Regression: with several tiles per wave (B=8, Hkv=4, T=8192 -> 2 tiles per
+    wave) the wide-code instances must not let one wave's partial overwrite the
+    folded query another wave is still reading (LDS regions of 16 KB)."""
+    print("case decode several tiles per wave bits=%d" % bits, flush=True)
+    _decode_case(8, 4, 28, 8192, bits, bits, kvq.F16, seed=140 + bits,
+                 pairs=[(0, 0), (2, 1), (5, 2), (7, 3)])
+
+
 @pytest.mark.parametrize("v_bits", [2, 4, 1])
 def test_decode_mixed(v_bits):
     print("case decode mixed v=%d" % v_bits, flush=True)

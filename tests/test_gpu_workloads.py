@@ -1,0 +1,167 @@
+"""GPU parity at the workloads' full sizes, in the launch configurations the
+benchmark and the workloads use.  The whole cache is produced by the HIP path;
+the oracle recomputes sampled (batch, kv-head) streams one by one (bytes
+bit-exact, attention rows within 2e-3) and, for the progressive workload,
+replays the budget schedule.
+
+Workloads (seeded, synthetic; see kv_cache_mixed_amd/synth.py):
+  qwen7b layer   B=16, Hkv=4, Hq=28, T=32768, 4-bit K/V, fp16 S/Z
+  progressive    B=8, Hkv=4, Hq=28, 128-token groups appended from 16 bits
+                 under a 128 MiB budget up to T=32768 (shrinks 16->8->4->2)
+  llama 128K     B=1, Hkv=8, Hq=32, T=131072, mixed 4/3/2/1-bit keys,
+                 2-bit values, e4m3 S/Z
+  qwen32b layers B=16, Hkv=8, Hq=40, T=32768 at the step's widths 8, 4, 2
+"""
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_mixed_amd import kvq, synth
+from tests.gpu_helpers import (PDT_ORACLE, REL_TOL, SCALE, assert_stream_bytes_equal, oracle_attn,
+                               oracle_stream, q_to_dev, rel_err_rows, to_dev)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    oracle.build(force=False)
+    kvq.load()
+
+
+def _check_streams(cache, inp, out, streams, k_bits, v_bits, pdt, G, slot_chan=None, what=""):
+    worst = 0.0
+    for b, h in streams:
+        st = oracle_stream(inp, b, h, k_bits, v_bits, pdt,
+                           None if slot_chan is None else slot_chan[h])
+        assert_stream_bytes_equal(cache, st, b, h, what)
+        ref = oracle_attn(st, inp["q_bf16"][b, h * G:(h + 1) * G])
+        err = rel_err_rows(out[b, h * G:(h + 1) * G], ref).max()
+        assert err <= REL_TOL, "%s stream (%d,%d): rel err %.3e" % (what, b, h, err)
+        worst = max(worst, err)
+    return worst
+
+
+def test_qwen7b_layer_full_size():
+    """The benchmark's workload and launch plan: quantize the whole layer,
+    decode every query head; six streams checked against the oracle."""
+    B, H, Hq, T = 16, 4, 28, 32768
+    print("case qwen7b layer full size", flush=True)
+    inp = synth.layer(B, H, Hq, T, seed=1234)
+    cache = kvq.PackedCache(B, H, T, 4, 4, kvq.F16)
+    kd, vd = to_dev(inp["k"], torch), to_dev(inp["v"], torch)
+    cache.quantize(kd, vd, 0)
+    del kd, vd
+    out = cache.decode_attn(q_to_dev(inp["q_bf16"], torch), SCALE).cpu().numpy()
+    assert np.isfinite(out).all()
+    worst = _check_streams(cache, inp, out, [(0, 0), (3, 1), (7, 2), (10, 3), (15, 0), (15, 3)],
+                           4, 4, kvq.F16, Hq // H, what="qwen7b")
+    print("qwen7b worst row rel err %.3e" % worst, flush=True)
+
+
+def _progressive_oracle(inp, b, h, events, t_end, pdt):
+    """Oracle stream (b, h) after appending [0, t_end) under the schedule
+    `events` = [(tokens before the shrinking append, new width), ...]: each
+    segment is quantized at the width current when it was appended, then
+    shrunk with every later halving."""
+    bounds = [0] + [t for t, _ in events] + [1 << 40]
+    widths = [16] + [w for _, w in events]
+    final = widths[[i for i in range(len(events) + 1) if bounds[i] < t_end][-1]]
+    parts = []
+    for i in range(len(widths)):
+        s0, s1 = bounds[i], min(bounds[i + 1], t_end)
+        if s0 >= s1:
+            break
+        st = oracle.quantize_stream(inp["k"][b, h, s0:s1], inp["v"][b, h, s0:s1], widths[i],
+                                    widths[i], PDT_ORACLE[pdt])
+        w = widths[i]
+        while w > final:
+            w //= 2
+            st = oracle.shrink_stream(st, w)
+        parts.append(st)
+    cat = lambda name: np.concatenate([getattr(p, name) for p in parts])
+    return oracle.Stream(final, final, PDT_ORACLE[pdt], cat("k_tiles"), cat("ks"), cat("kz"),
+                         cat("v_tiles"), cat("vs"), cat("vz"))
+
+
+def test_progressive_schedule_full_size():
+    """128-token groups appended through kvq_append from 16 bits under a
+    128 MiB budget (codes + S + Z): the halvings fire exactly where the oracle
+    schedule puts them (8064, 15872, 30720 tokens), every tile and parameter of
+    the sampled streams equals the oracle's replay (quantize at the width of
+    the moment, then ERS with each later halving), and attention agrees just
+    before each halving and at the end."""
+    B, H, Hq, T = 8, 4, 28, 32768
+    G = Hq // H
+    budget = 128 << 20
+    print("case progressive schedule", flush=True)
+    inp = synth.layer(B, H, Hq, T, seed=77)
+    expected = oracle.schedule(B, H, T, 16, 2, oracle.F16, budget)
+    assert expected == [(8064, 8), (15872, 4), (30720, 2)]
+    cache = kvq.PackedCache(B, H, T, 16, 16, kvq.F16, layout="pool", pool_bytes=budget)
+    kd, vd = to_dev(inp["k"], torch), to_dev(inp["v"], torch)
+    q = q_to_dev(inp["q_bf16"], torch)
+    sample = [(0, 0), (5, 3)]
+    events = []
+    check_at = {t for t, _ in expected} | {T}
+    for t0 in range(0, T, 128):
+        n = cache.append(kd[:, :, t0:t0 + 128], vd[:, :, t0:t0 + 128], budget_bytes=budget,
+                         floor_bits=2)
+        if n:
+            events.append((t0, cache.k_bits))
+            assert n == 1
+        assert cache.cache_bytes() <= budget
+        t1 = t0 + 128
+        if t1 in check_at:
+            out = cache.decode_attn(q, SCALE).cpu().numpy()
+            for b, h in sample:
+                st = _progressive_oracle(inp, b, h, events, t1, kvq.F16)
+                assert st.k_bits == cache.k_bits
+                assert_stream_bytes_equal(cache, st, b, h, "progressive T=%d" % t1)
+                err = rel_err_rows(out[b, h * G:(h + 1) * G],
+                                   oracle_attn(st, inp["q_bf16"][b, h * G:(h + 1) * G])).max()
+                assert err <= REL_TOL, "T=%d stream (%d,%d) rel err %.3e" % (t1, b, h, err)
+    assert events == expected
+    assert cache.k_bits == 2 and cache.v_bits == 2
+    assert cache.pool_high_water() <= budget
+
+
+def test_llama_128k_mixed_full_size():
+    """Mixed-width keys (8 x 4-bit, 8 x 3-bit, 8 x 1-bit, 104 x 2-bit per kv
+    head), 2-bit values, e4m3 S/Z, one sequence of 131072 tokens: every stream
+    bit-exact and every query head within tolerance."""
+    B, H, Hq, T = 1, 8, 32, 131072
+    print("case llama 128k mixed", flush=True)
+    inp = synth.mixed_layer(B, H, Hq, T, seed=11)
+    cache = kvq.PackedCache(B, H, T, kvq.KMIXED, 2, kvq.E4M3, slot_chan=inp["slot_chan"])
+    kd, vd = to_dev(inp["k"], torch), to_dev(inp["v"], torch)
+    cache.quantize(kd, vd, 0)
+    del kd, vd
+    out = cache.decode_attn(q_to_dev(inp["q_bf16"], torch), SCALE).cpu().numpy()
+    worst = _check_streams(cache, inp, out, [(0, h) for h in range(H)], kvq.KMIXED, 2, kvq.E4M3,
+                           Hq // H, slot_chan=inp["slot_chan"], what="llama128k")
+    print("llama 128k worst row rel err %.3e" % worst, flush=True)
+
+
+@pytest.mark.parametrize("bits", [8, 4, 2])
+def test_qwen32b_layer_widths_full_size(bits):
+    """A 64-layer step's per-layer shape (B=16, Hkv=8, Hq=40, T=32768) at each
+    width the layer table uses; inputs drawn on the device, three streams
+    copied back for the oracle."""
+    B, H, Hq, T = 16, 8, 40, 32768
+    G = Hq // H
+    print("case qwen32b layer bits=%d" % bits, flush=True)
+    dev = synth.layer_device(B, H, Hq, T, seed=500 + bits, device="cuda")
+    cache = kvq.PackedCache(B, H, T, bits, bits, kvq.F16)
+    cache.quantize(dev["k"], dev["v"], 0)
+    out = cache.decode_attn(dev["q"], SCALE).cpu().numpy()
+    assert np.isfinite(out).all()
+    q_bits = dev["q"].view(torch.int16).cpu().numpy().view(np.uint16)
+    for b, h in [(0, 0), (9, 4), (15, 7)]:
+        k = dev["k"][b, h].cpu().numpy()
+        v = dev["v"][b, h].cpu().numpy()
+        st = oracle.quantize_stream(k, v, bits, bits, oracle.F16)
+        assert_stream_bytes_equal(cache, st, b, h, "qwen32b %d-bit" % bits)
+        err = rel_err_rows(out[b, h * G:(h + 1) * G], oracle_attn(st, q_bits[b, h * G:(h + 1) * G])).max()
+        assert err <= REL_TOL, "qwen32b %d-bit stream (%d,%d) rel err %.3e" % (bits, b, h, err)
