@@ -60,6 +60,11 @@
 #ifndef KVQ_DECODE_NS_MAX
 #define KVQ_DECODE_NS_MAX 3
 #endif
+// rescale the output accumulators every sub-tile (1) or only when some head's
+// reference moved (0)
+#ifndef KVQ_DECODE_BRANCHLESS_RESCALE
+#define KVQ_DECODE_BRANCHLESS_RESCALE 0
+#endif
 // workgroups one decode launch aims at per wave-per-SIMD of the instance
 #ifndef KVQ_DECODE_WG_PER_OCC
 #define KVQ_DECODE_WG_PER_OCC 256
@@ -456,9 +461,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     uint32_t kp[NS][2][KPL];   // next tile's key scales / zeros (sub-tile 0 only)
   };
 
-  auto load = [&](Buf& bf, int it) {
-    const int tile = t_first + t_step * (it / NSUB);
-    const int sub = it % NSUB;
+  // sub-tile `sub` (a constant after unrolling) of the wave's tile number ti
+  auto load = [&](Buf& bf, int ti, int sub) {
+    const int tile = t_first + t_step * ti;
 #pragma unroll
     for (int s = 0; s < NS; s++) {
       const int bh = min(grp * NS + s, BH - 1);   // a missing stream re-reads a valid one
@@ -583,8 +588,8 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     bk0 = a.sl2 * beta;
   };
 
-  auto compute = [&](const Buf& bf, int it) {
-    if (it % NSUB == 0) fold_query(bf);
+  auto compute = [&](const Buf& bf, int sub) {
+    if (sub == 0) fold_query(bf);
     // ---- logits: k-step-major over all (stream, block) accumulators
     f32x4 acc[NS][JB];
 #pragma unroll
@@ -667,10 +672,15 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     }
     l_run = fmaf(l_run, alpha, lsum);
     z_run = fmaf(z_run, alpha, zsum);
+#if KVQ_DECODE_BRANCHLESS_RESCALE
+#pragma unroll
+    for (int cb = 0; cb < 8; cb++) acc_o[cb] *= rescale;
+#else
     if (__builtin_amdgcn_ballot_w64(rescale != 1.0f) != 0) {
 #pragma unroll
       for (int cb = 0; cb < 8; cb++) acc_o[cb] *= rescale;
     }
+#endif
 
     // ---- P operand (split hi/lo) and PV
     uint32_t bvh[FVS], bvl[FVS];
@@ -709,16 +719,25 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     }
   };
 
-  // ---- software-pipelined main loop (two register buffers)
+  // ---- software-pipelined main loop (two register buffers).  One iteration
+  // covers U sub-tiles (a whole tile, or two one-sub-tile tiles) unrolled, so
+  // the fold and every buffer choice are compile-time; the prefetch of the
+  // sub-tile after the wave's last one re-reads that last one (harmless, in
+  // bounds) instead of branching.
+  constexpr int U = NSUB >= 2 ? NSUB : 2;
   Buf b0, b1;
-  if (n_iter > 0) load(b0, 0);
+  if (n_iter > 0) load(b0, 0, 0);
 #pragma unroll 1
-  for (int it = 0; it < n_iter; it += 2) {
-    if (it + 1 < n_iter) load(b1, it + 1);
-    compute(b0, it);
-    if (it + 1 < n_iter) {
-      if (it + 2 < n_iter) load(b0, it + 2);
-      compute(b1, it + 1);
+  for (int it = 0; it < n_iter; it += U) {
+    const int ti0 = it / NSUB;
+#pragma unroll
+    for (int u = 0; u < U; u++) {
+      if constexpr (NSUB == 1) {
+        if (u == 1 && it + 1 >= n_iter) break;
+      }
+      const int nti = min(ti0 + (u + 1) / NSUB, my_tiles - 1);
+      load((u % 2 == 0) ? b1 : b0, nti, (u + 1) % NSUB);
+      compute((u % 2 == 0) ? b0 : b1, u % NSUB);
     }
   }
 
