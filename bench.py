@@ -103,6 +103,84 @@ def time_events(torch, fn, n, warmup):
     return sum(ms) / len(ms), ms[len(ms) // 2]
 
 
+def mixed_128k_rows(torch, kvq, synth, dev, scale):
+    """Llama-3.1-8B-shaped 128K context: mixed 4/3/2/1-bit keys (34 B per token),
+    2-bit values, e4m3 S/Z.  Quantize of the whole context, then decode (two
+    cache copies rotated)."""
+    B, H, Hq, T = 1, 8, 32, 131072
+    inp = synth.mixed_layer_device(B, H, Hq, T, seed=4, device=dev)
+    caches = [kvq.PackedCache(B, H, T, kvq.KMIXED, 2, kvq.E4M3, slot_chan=inp["slot_chan"], device=dev)
+              for _ in range(4)]
+
+    def quant(i):
+        c = caches[i % len(caches)]
+        c.s.n_tokens = 0
+        c.quantize(inp["k"], inp["v"], 0)
+    q_ms, _ = time_events(torch, quant, 8, 4)
+    q_bytes = 2 * B * H * T * 128 * 4 + decode_bytes(B, H, 0, T, 0, 2, 1)
+    q = inp["q"]
+    del inp
+    torch.cuda.empty_cache()
+    outs = [torch.empty((B, Hq, 128), dtype=torch.float32, device=dev) for _ in caches]
+    d_ms, _ = time_events(torch, lambda i: caches[i % len(caches)].decode_attn(q, scale, out=outs[i % len(caches)]),
+                          40, 4)
+    alg = decode_bytes(B, H, Hq, T, 0, 2, 1)
+    return {"quantize_mixed_128k": {"ms": round(q_ms, 4), "GB/s": round(q_bytes / q_ms / 1e6, 1), "bytes": q_bytes},
+            "decode_mixed_128k": {"ms": round(d_ms, 4), "GB/s": round(alg / d_ms / 1e6, 1), "bytes": alg,
+                                  "pct_of_peak": round(100 * alg / d_ms / 1e6 / PEAK_HBM_GBS, 2),
+                                  "note": "4 cache copies rotated (%d MB each)" % (alg // 1000000)}}
+
+
+def progressive_rows(torch, kvq, synth, dev, scale):
+    """Progressive schedule: 128-token groups appended from 16 bits under a
+    128 MiB budget (B=8, Hkv=4, Hq=28) up to 32768 tokens.  Times every append
+    (the three that halve the cache include the whole-cache ERS), and decode at
+    the last token count of each width."""
+    B, H, Hq, T = 8, 4, 28, 32768
+    budget = 128 << 20
+    inp = synth.layer_device(B, H, Hq, T, seed=33, device=dev)
+    cache = kvq.PackedCache(B, H, T, 16, 16, kvq.F16, layout="pool", pool_bytes=budget, device=dev)
+    q = inp["q"]
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+    app_ms, events, dec = [], [], {}
+    for t0 in range(0, T, 128):
+        bits = cache.k_bits
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record()
+        n = cache.append(inp["k"][:, :, t0:t0 + 128], inp["v"][:, :, t0:t0 + 128], budget_bytes=budget,
+                         floor_bits=2)
+        e1.record()
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1)
+        if n:
+            events.append({"tokens": t0, "from_bits": bits, "to_bits": cache.k_bits, "append_ms": round(ms, 4),
+                           "shrunk_bytes": cache.cache_bytes(t0, bits, bits)})
+        else:
+            app_ms.append(ms)
+        t1 = t0 + 128
+        if t1 == T or (t1 < T and cache.cache_bytes(t1 + 128) > budget and cache.k_bits > 2):
+            for _ in range(3):
+                cache.decode_attn(q, scale, out=out)
+            torch.cuda.synchronize()
+            d0 = torch.cuda.Event(enable_timing=True)
+            d1 = torch.cuda.Event(enable_timing=True)
+            d0.record()
+            for _ in range(10):
+                cache.decode_attn(q, scale, out=out)
+            d1.record()
+            torch.cuda.synchronize()
+            dms = d0.elapsed_time(d1) / 10
+            alg = decode_bytes(B, H, Hq, t1, cache.k_bits, cache.v_bits, 2)
+            dec["%d-bit@%d" % (cache.k_bits, t1)] = {"ms": round(dms, 4), "GB/s": round(alg / dms / 1e6, 1)}
+    del inp, cache
+    torch.cuda.empty_cache()
+    return {"progressive_schedule": {"shrink_events": events,
+                                     "append_ms_median": round(sorted(app_ms)[len(app_ms) // 2], 4),
+                                     "decode": dec,
+                                     "note": "pool layout, single cache (partly Infinity-Cache resident)"}}
+
+
 def cpu_baseline(inp, B, H, Hq, k_bits, pdt, seconds):
     """The CPU oracle (as it stands) on a bounded sample of the same workload:
     quantize + fp64 decode attention of whole (batch, kv-head) streams, run in
@@ -254,6 +332,8 @@ def main():
                                           "note": "single cache copy (partly Infinity-Cache resident)"}
         del sh
         torch.cuda.empty_cache()
+        rows.update(mixed_128k_rows(torch, kvq, synth, dev, scale))
+        rows.update(progressive_rows(torch, kvq, synth, dev, scale))
 
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)

@@ -408,43 +408,6 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // lanes 32.. repeat words 0..31)
   const uint32_t kloff = (uint32_t)((PB == 1) ? (lane & 31) : lane) * 4;
 
-  // ---- the query heads of the group in slot order, [column][slot] bf16 in
-  // LDS (column n = stream n / G, head n % G; zero for columns without a head)
-#pragma unroll
-  for (int i = threadIdx.x; i < 16 * 128; i += 256) {
-    const int cn = i >> 7, j = i & 127;
-    const int cs = cn / G, ch = cn - cs * G;
-    const int cbh = grp * NS + cs;
-    uint16_t v = 0;
-    if (cs < NS && cbh < BH) {
-      const int cb = cbh / g.H, chh = cbh % g.H;
-      const int chan = MIXED ? (int)g.slot_chan[chh * 128 + j] : j;
-      v = a.q[((int64_t)cb * (g.H * G) + (int64_t)chh * G + ch) * 128 + chan];
-    }
-    qs[cn][j] = v;
-  }
-  __syncthreads();
-  // the lane's 32 query values (slots kslot(0..31)) as bf16 pairs
-  auto load_q = [&](uint32_t* qw) {
-#pragma unroll
-    for (int c = 0; c < 4; c++) {
-      const u32x4 v = *(const u32x4*)&qs[n][kslot(8 * c)];
-      qw[4 * c] = v[0]; qw[4 * c + 1] = v[1]; qw[4 * c + 2] = v[2]; qw[4 * c + 3] = v[3];
-    }
-  };
-  auto qget = [](const uint32_t* qw, int li) -> float {
-    return (li & 1) ? u2f(qw[li >> 1] & 0xffff0000u) : u2f(qw[li >> 1] << 16);
-  };
-  int eq;
-  {
-    uint32_t qw[16];
-    load_q(qw);
-    uint32_t qmax = 0;
-#pragma unroll
-    for (int li = 0; li < 32; li++) qmax = max(qmax, f2u(qget(qw, li)) & 0x7fffffffu);
-    eq = expo(u2f(wave_maxu16x4(qmax)));
-  }
-
   float m_run = -INFINITY, l_run = 0.0f, z_run = 0.0f;
   int e_run = -1000;
   float ak = 0.0f, bk0 = 0.0f;
@@ -520,6 +483,47 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     pload<PDT, TPS>(r_vs, vpoff, psoff, bf.vs);
     pload<PDT, TPS>(r_vz, vpoff, psoff, bf.vz);
   };
+
+  // the first sub-tile's loads are in flight while the query is staged
+  Buf b0, b1;
+  if (n_iter > 0) load(b0, 0, 0);
+
+  // ---- the query heads of the group in slot order, [column][slot] bf16 in
+  // LDS (column n = stream n / G, head n % G; zero for columns without a head)
+#pragma unroll
+  for (int i = threadIdx.x; i < 16 * 128; i += 256) {
+    const int cn = i >> 7, j = i & 127;
+    const int cs = cn / G, ch = cn - cs * G;
+    const int cbh = grp * NS + cs;
+    uint16_t v = 0;
+    if (cs < NS && cbh < BH) {
+      const int cb = cbh / g.H, chh = cbh % g.H;
+      const int chan = MIXED ? (int)g.slot_chan[chh * 128 + j] : j;
+      v = a.q[((int64_t)cb * (g.H * G) + (int64_t)chh * G + ch) * 128 + chan];
+    }
+    qs[cn][j] = v;
+  }
+  __syncthreads();
+  // the lane's 32 query values (slots kslot(0..31)) as bf16 pairs
+  auto load_q = [&](uint32_t* qw) {
+#pragma unroll
+    for (int c = 0; c < 4; c++) {
+      const u32x4 v = *(const u32x4*)&qs[n][kslot(8 * c)];
+      qw[4 * c] = v[0]; qw[4 * c + 1] = v[1]; qw[4 * c + 2] = v[2]; qw[4 * c + 3] = v[3];
+    }
+  };
+  auto qget = [](const uint32_t* qw, int li) -> float {
+    return (li & 1) ? u2f(qw[li >> 1] & 0xffff0000u) : u2f(qw[li >> 1] << 16);
+  };
+  int eq;
+  {
+    uint32_t qw[16];
+    load_q(qw);
+    uint32_t qmax = 0;
+#pragma unroll
+    for (int li = 0; li < 32; li++) qmax = max(qmax, f2u(qget(qw, li)) & 0x7fffffffu);
+    eq = expo(u2f(wave_maxu16x4(qmax)));
+  }
 
   // fold the key scales of `tile` into the query: u = q * S * 2^k as f16 hi/lo
   // operand registers in LDS; logit constants ak, bk0
@@ -725,8 +729,6 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // sub-tile after the wave's last one re-reads that last one (harmless, in
   // bounds) instead of branching.
   constexpr int U = NSUB >= 2 ? NSUB : 2;
-  Buf b0, b1;
-  if (n_iter > 0) load(b0, 0, 0);
 #pragma unroll 1
   for (int it = 0; it < n_iter; it += U) {
     const int ti0 = it / NSUB;

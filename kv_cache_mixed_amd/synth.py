@@ -160,3 +160,22 @@ def layer_device(B: int, Hkv: int, Hq: int, T: int, seed: int, device, n_outlier
     v = torch.randn((B, Hkv, T, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
     q = torch.randn((B, Hq, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
     return dict(k=k, v=v, q=q.to(torch.bfloat16))
+
+
+def mixed_layer_device(B: int, Hkv: int, Hq: int, T: int, seed: int, device):
+    """Same recipe as mixed_layer() drawn with torch on a device (class map from
+    the same seeded permutation; the normal draws differ from numpy's stream)."""
+    import torch
+    slot_chan, classes = mixed_class_map(Hkv, seed + 1)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    k = torch.randn((B, Hkv, T, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    scale = torch.ones((Hkv, HEAD_DIM), device=device, dtype=torch.float32)
+    for h in range(Hkv):
+        big = np.concatenate([classes[h]["b4"], classes[h]["b3"]])
+        scale[h, torch.as_tensor(big, device=device)] = 6.0
+        scale[h, torch.as_tensor(classes[h]["b1"], device=device)] = 0.2
+    k *= scale[None, :, None, :]
+    v = torch.randn((B, Hkv, T, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    q = torch.randn((B, Hq, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    return dict(k=k, v=v, q=q.to(torch.bfloat16), slot_chan=slot_chan)
