@@ -60,6 +60,11 @@
 #ifndef KVQ_DECODE_NS_MAX
 #define KVQ_DECODE_NS_MAX 3
 #endif
+// load a sub-tile's value words when it is computed (1) or with the
+// prefetched buffer one sub-tile earlier (0)
+#ifndef KVQ_DECODE_V_JIT
+#define KVQ_DECODE_V_JIT 1
+#endif
 // rescale the output accumulators every sub-tile (1) or only when some head's
 // reference moved (0)
 #ifndef KVQ_DECODE_BRANCHLESS_RESCALE
@@ -417,11 +422,29 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   uint32_t* my_lds = lds[wave];
 
   // one sub-tile of raw operands
+  // value words either travel with the prefetched buffer or (KVQ_DECODE_V_JIT)
+  // are loaded at the start of the sub-tile's own compute, in flight during
+  // its key product and softmax
+  constexpr bool VJIT = KVQ_DECODE_V_JIT != 0;
   struct Buf {
     uint32_t kw[NS][JB][NWK];
-    uint32_t vw[NS][8][WVS];
+    uint32_t vw[VJIT ? 1 : NS][8][WVS];
     uint32_t vs[PWV], vz[PWV];
     uint32_t kp[NS][2][KPL];   // next tile's key scales / zeros (sub-tile 0 only)
+  };
+
+  // value word planes: word (w, c, a) at byte ((w*128 + c)*4 + a)*4; the
+  // per-load constant goes to the scalar offset (one lane offset)
+  auto load_vw = [&](uint32_t* vw, __amdgpu_buffer_rsrc_t rv, int sub) {
+#pragma unroll
+    for (int w = 0; w < WVS; w++)
+#pragma unroll
+      for (int cb = 0; cb < 8; cb++)
+        vw[cb * WVS + w] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, (uint32_t)(sub * WVS + w) * 2048 + 256 * cb, 0);
+  };
+  auto v_rsrc = [&](int s, int tile) {
+    const int bh = min(grp * NS + s, BH - 1);
+    return rsrc(g.v_codes + v_tile_offset(g, bh / g.H, bh % g.H, tile), 2048 * VB);
   };
 
   // sub-tile `sub` (a constant after unrolling) of the wave's tile number ti
@@ -433,7 +456,8 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       const int bs = bh / g.H, hs = bh % g.H;
       const __amdgpu_buffer_rsrc_t rk =
           rsrc(g.k_codes + k_tile_offset(g, bs, hs, tile), MIXED ? KVQ_MIXED_TILE_BYTES : 2048 * KB);
-      const __amdgpu_buffer_rsrc_t rv = rsrc(g.v_codes + v_tile_offset(g, bs, hs, tile), 2048 * VB);
+      const __amdgpu_buffer_rsrc_t rv = v_rsrc(s, tile);
+      (void)rv;
 #pragma unroll
       for (int jj = 0; jj < JB; jj++) {
         const uint32_t soff = (uint32_t)(sub * JB) * 4 * ROW_K;       // rows 4j apart
@@ -457,14 +481,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
           bf.kw[s][jj][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, koff + jj * 4 * ROW_K, soff, 0);
         }
       }
-      // value word planes: word (w, c, a) at byte ((w*128 + c)*4 + a)*4
-#pragma unroll
-      for (int w = 0; w < WVS; w++) {
-        // the per-load constant goes to the scalar offset: one lane offset
-#pragma unroll
-        for (int cb = 0; cb < 8; cb++)
-          bf.vw[s][cb][w] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, (uint32_t)(sub * WVS + w) * 2048 + 256 * cb, 0);
-      }
+      if constexpr (!VJIT) load_vw(&bf.vw[s][0][0], rv, sub);
     }
     if (sub == 0) {
 #pragma unroll
@@ -592,7 +609,13 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     bk0 = a.sl2 * beta;
   };
 
-  auto compute = [&](const Buf& bf, int sub) {
+  auto compute = [&](const Buf& bf, int ti, int sub) {
+    uint32_t vjit[VJIT ? NS : 1][8][WVS];
+    if constexpr (VJIT) {
+#pragma unroll
+      for (int s = 0; s < NS; s++) load_vw(&vjit[s][0][0], v_rsrc(s, t_first + t_step * ti), sub);
+    }
+    const uint32_t* vwp = VJIT ? &vjit[0][0][0] : &bf.vw[0][0][0];
     if (sub == 0) fold_query(bf);
     // ---- logits: k-step-major over all (stream, block) accumulators
     f32x4 acc[NS][JB];
@@ -713,7 +736,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
           for (int r = 0; r < 4; r++) {
             const Fld F = ufield<VB>(4 * k + r);
-            av[cb][r] = field_subnormal(bf.vw[s][cb][F.w], F);
+            av[cb][r] = field_subnormal(vwp[(s * 8 + cb) * WVS + F.w], F);
           }
 #pragma unroll
         for (int cb = 0; cb < 8; cb++) acc_o[cb] = mfma(av[cb], bsh + 4 * k, acc_o[cb]);
@@ -739,7 +762,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       }
       const int nti = min(ti0 + (u + 1) / NSUB, my_tiles - 1);
       load((u % 2 == 0) ? b1 : b0, nti, (u + 1) % NSUB);
-      compute((u % 2 == 0) ? b0 : b1, u % NSUB);
+      compute((u % 2 == 0) ? b0 : b1, ti0 + u / NSUB, u % NSUB);
     }
   }
 
