@@ -65,6 +65,11 @@
 #ifndef KVQ_DECODE_V_JIT
 #define KVQ_DECODE_V_JIT 1
 #endif
+// prefetch key blocks / value parameters two sub-tiles ahead, refilling a
+// buffer as soon as its part has been consumed (1), or one sub-tile ahead (0)
+#ifndef KVQ_DECODE_PF2
+#define KVQ_DECODE_PF2 1
+#endif
 // rescale the output accumulators every sub-tile (1) or only when some head's
 // reference moved (0)
 #ifndef KVQ_DECODE_BRANCHLESS_RESCALE
@@ -426,6 +431,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // are loaded at the start of the sub-tile's own compute, in flight during
   // its key product and softmax
   constexpr bool VJIT = KVQ_DECODE_V_JIT != 0;
+  constexpr bool PF2 = KVQ_DECODE_PF2 != 0;
   struct Buf {
     uint32_t kw[NS][JB][NWK];
     uint32_t vw[VJIT ? 1 : NS][8][WVS];
@@ -447,8 +453,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     return rsrc(g.v_codes + v_tile_offset(g, bh / g.H, bh % g.H, tile), 2048 * VB);
   };
 
-  // sub-tile `sub` (a constant after unrolling) of the wave's tile number ti
-  auto load = [&](Buf& bf, int ti, int sub) {
+  // sub-tile `sub` (a constant after unrolling) of the wave's tile number ti:
+  // key blocks (and, for sub-tile 0, the tile's key parameters) ...
+  auto load_k = [&](Buf& bf, int ti, int sub) {
     const int tile = t_first + t_step * ti;
 #pragma unroll
     for (int s = 0; s < NS; s++) {
@@ -495,10 +502,17 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
         }
       }
     }
-    // own stream's value scales / zeros of the lane's TPS tokens
+  };
+  // ... and the own stream's value scales / zeros of the lane's TPS tokens
+  auto load_p = [&](Buf& bf, int ti, int sub) {
+    const int tile = t_first + t_step * ti;
     const uint32_t psoff = (uint32_t)(tile * 128 + sub * TPS) * PB;
     pload<PDT, TPS>(r_vs, vpoff, psoff, bf.vs);
     pload<PDT, TPS>(r_vz, vpoff, psoff, bf.vz);
+  };
+  auto load = [&](Buf& bf, int ti, int sub) {
+    load_k(bf, ti, sub);
+    load_p(bf, ti, sub);
   };
 
   // the first sub-tile's loads are in flight while the query is staged
@@ -609,7 +623,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     bk0 = a.sl2 * beta;
   };
 
-  auto compute = [&](const Buf& bf, int ti, int sub) {
+  // compute sub-tile (ti, sub) from bf; with the two-ahead prefetch, bf is
+  // refilled with sub-tile (ti2, sub2) as soon as each part has been read
+  auto compute = [&](Buf& bf, int ti, int sub, int ti2, int sub2) {
     uint32_t vjit[VJIT ? NS : 1][8][WVS];
     if constexpr (VJIT) {
 #pragma unroll
@@ -654,6 +670,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
         for (int jj = 0; jj < JB; jj++) acc[s][jj] = mfma(av[s][jj], bl4, acc[s][jj]);
     }
+    if constexpr (PF2) load_k(bf, ti2, sub2);
     float lgt[JB][4];
 #pragma unroll
     for (int jj = 0; jj < JB; jj++) {
@@ -671,6 +688,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     float vs[TPS], vz[TPS];
     praw_unpack<PDT, TPS>(bf.vs, vs);
     praw_unpack<PDT, TPS>(bf.vz, vz);
+    if constexpr (PF2) load_p(bf, ti2, sub2);
     float tmax = -INFINITY;
     uint32_t vsmax = 0;
 #pragma unroll
@@ -752,6 +770,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // sub-tile after the wave's last one re-reads that last one (harmless, in
   // bounds) instead of branching.
   constexpr int U = NSUB >= 2 ? NSUB : 2;
+  if constexpr (PF2) {
+    if (n_iter > 0) load(b1, min(1 / NSUB, my_tiles - 1), 1 % NSUB);
+  }
 #pragma unroll 1
   for (int it = 0; it < n_iter; it += U) {
     const int ti0 = it / NSUB;
@@ -760,9 +781,12 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       if constexpr (NSUB == 1) {
         if (u == 1 && it + 1 >= n_iter) break;
       }
-      const int nti = min(ti0 + (u + 1) / NSUB, my_tiles - 1);
-      load((u % 2 == 0) ? b1 : b0, nti, (u + 1) % NSUB);
-      compute((u % 2 == 0) ? b0 : b1, ti0 + u / NSUB, u % NSUB);
+      const int ti2 = min(ti0 + (u + 2) / NSUB, my_tiles - 1);
+      if constexpr (!PF2) {
+        const int nti = min(ti0 + (u + 1) / NSUB, my_tiles - 1);
+        load((u % 2 == 0) ? b1 : b0, nti, (u + 1) % NSUB);
+      }
+      compute((u % 2 == 0) ? b0 : b1, ti0 + u / NSUB, u % NSUB, ti2, (u + 2) % NSUB);
     }
   }
 
