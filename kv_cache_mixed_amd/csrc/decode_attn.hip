@@ -70,6 +70,11 @@
 #ifndef KVQ_DECODE_PF2
 #define KVQ_DECODE_PF2 1
 #endif
+// one set of output accumulators per packed stream (1) or one shared set with
+// the probabilities masked per stream (0)
+#ifndef KVQ_DECODE_SACC
+#define KVQ_DECODE_SACC 0
+#endif
 // rescale the output accumulators every sub-tile (1) or only when some head's
 // reference moved (0)
 #ifndef KVQ_DECODE_BRANCHLESS_RESCALE
@@ -356,6 +361,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   constexpr int VH = (VB == 16) ? -2 : 6;
   constexpr int ROW_K = MIXED ? 8 : 16 * KB;
   constexpr int LDS_WAVE = NFK * 2 * 64;             // u32 words of folded query per wave
+  constexpr bool SACC = (KVQ_DECODE_SACC != 0) && NS > 1;
   static_assert(KSV >= 1 && WVS >= 1, "sub-tile must hold whole value k-steps");
   static_assert(LDS_WAVE >= 16 * 128 && TPS % 8 == 0, "layout assumptions");
 
@@ -421,9 +427,14 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   float m_run = -INFINITY, l_run = 0.0f, z_run = 0.0f;
   int e_run = -1000;
   float ak = 0.0f, bk0 = 0.0f;
-  f32x4 acc_o[8];
+  // output accumulators: one set per stream when SACC (no masking of the
+  // probabilities; column n then takes its own stream's set at the end)
+  constexpr int NA = SACC ? NS : 1;
+  f32x4 acc_o[NA][8];
 #pragma unroll
-  for (int cb = 0; cb < 8; cb++) acc_o[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int s = 0; s < NA; s++)
+#pragma unroll
+    for (int cb = 0; cb < 8; cb++) acc_o[s][cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   uint32_t* my_lds = lds[wave];
 
   // one sub-tile of raw operands
@@ -700,7 +711,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     tmax = wave_max16x4(tmax);
     const int ev = expo(u2f(wave_maxu16x4(vsmax)));
     const float m_new = (tmax > m_run + (float)TAU) ? tmax : m_run;
-    const float alpha = exp2f(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // v_exp_f32, 0 for -inf
     const int e_new = max(e_run, ev);
     const float rescale = alpha * exp2i(e_run - e_new);
     m_run = m_new;
@@ -710,7 +721,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     float lsum = 0.0f, zsum = 0.0f;
 #pragma unroll
     for (int i = 0; i < TPS; i++) {
-      const float e = exp2f(lgt[i >> 2][i & 3] - m_new);
+      const float e = __builtin_amdgcn_exp2f(lgt[i >> 2][i & 3] - m_new);
       lsum += e;
       zsum = fmaf(e, vz[i], zsum);
       p[i] = e * (vs[i] * pf);
@@ -719,11 +730,15 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     z_run = fmaf(z_run, alpha, zsum);
 #if KVQ_DECODE_BRANCHLESS_RESCALE
 #pragma unroll
-    for (int cb = 0; cb < 8; cb++) acc_o[cb] *= rescale;
+    for (int s = 0; s < NA; s++)
+#pragma unroll
+      for (int cb = 0; cb < 8; cb++) acc_o[s][cb] *= rescale;
 #else
     if (__builtin_amdgcn_ballot_w64(rescale != 1.0f) != 0) {
 #pragma unroll
-      for (int cb = 0; cb < 8; cb++) acc_o[cb] *= rescale;
+      for (int s = 0; s < NA; s++)
+#pragma unroll
+        for (int cb = 0; cb < 8; cb++) acc_o[s][cb] *= rescale;
     }
 #endif
 
@@ -742,10 +757,11 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       uint32_t bsh[FVS], bsl[FVS];
 #pragma unroll
       for (int ff = 0; ff < FVS; ff++) {
-        const bool sel = (NS == 1) || (own == s);
+        const bool sel = SACC || (NS == 1) || (own == s);
         bsh[ff] = sel ? bvh[ff] : 0u;
         bsl[ff] = sel ? bvl[ff] : 0u;
       }
+      f32x4* ao = acc_o[SACC ? s : 0];
 #pragma unroll
       for (int k = 0; k < KSV; k++) {
         uint32_t av[8][4];
@@ -757,9 +773,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
             av[cb][r] = field_subnormal(vwp[(s * 8 + cb) * WVS + F.w], F);
           }
 #pragma unroll
-        for (int cb = 0; cb < 8; cb++) acc_o[cb] = mfma(av[cb], bsh + 4 * k, acc_o[cb]);
+        for (int cb = 0; cb < 8; cb++) ao[cb] = mfma(av[cb], bsh + 4 * k, ao[cb]);
 #pragma unroll
-        for (int cb = 0; cb < 8; cb++) acc_o[cb] = mfma(av[cb], bsl + 4 * k, acc_o[cb]);
+        for (int cb = 0; cb < 8; cb++) ao[cb] = mfma(av[cb], bsl + 4 * k, ao[cb]);
       }
     }
   };
@@ -807,8 +823,13 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
   for (int cb = 0; cb < 8; cb++)
 #pragma unroll
-    for (int i = 0; i < 4; i++)
-      sh_o(wave, n, 16 * cb + 4 * lg + i) = (m_run == -INFINITY) ? 0.0f : acc_o[cb][i] * of + z_tot;
+    for (int i = 0; i < 4; i++) {
+      float a = acc_o[0][cb][i];
+#pragma unroll
+      for (int s = 1; s < NA; s++)
+        if (own == s) a = acc_o[s][cb][i];
+      sh_o(wave, n, 16 * cb + 4 * lg + i) = (m_run == -INFINITY) ? 0.0f : a * of + z_tot;
+    }
   __syncthreads();
 
   const int Hq = g.H * G;
