@@ -75,6 +75,11 @@
 #ifndef KVQ_DECODE_SACC
 #define KVQ_DECODE_SACC 0
 #endif
+// hand the chunk's tiles to its waves one at a time through an LDS counter (1)
+// or in a fixed round robin (0)
+#ifndef KVQ_DECODE_DYN
+#define KVQ_DECODE_DYN 0
+#endif
 // rescale the output accumulators every sub-tile (1) or only when some head's
 // reference moved (0)
 #ifndef KVQ_DECODE_BRANCHLESS_RESCALE
@@ -383,19 +388,16 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   const int bh_own = grp * NS + own;
   const bool real = (own < NS) && (bh_own < BH);
   const int b_own = real ? bh_own / g.H : 0, h_own = real ? bh_own % g.H : 0;
+  // the chunk's tiles, numbered k = 0 .. t_count-1: tile = t_base + t_stride * k
 #if KVQ_DECODE_STRIDED
-  // chunk c owns tiles c, c + n_chunks, ...; wave w takes every fourth of them,
-  // so at any moment the workgroups of a stream read neighbouring tiles
+  // chunk c owns tiles c, c + n_chunks, ...: at any moment the workgroups of a
+  // stream read neighbouring tiles
   const int t_count = (g.n_tiles - chunk + a.n_chunks - 1) / a.n_chunks;
-  const int t_step = 4 * a.n_chunks;
-  const int t_first = chunk + wave * a.n_chunks;
+  const int t_base = chunk, t_stride = a.n_chunks;
 #else
   const int t_count = min(a.tpc, g.n_tiles - chunk * a.tpc);
-  const int t_step = 4;
-  const int t_first = chunk * a.tpc + wave;
+  const int t_base = chunk * a.tpc, t_stride = 1;
 #endif
-  const int my_tiles = (t_count - wave + 3) / 4;
-  const int n_iter = (my_tiles > 0 ? my_tiles : 0) * NSUB;
 
   auto kslot = [&](int li) -> int {
     if constexpr (MIXED) return lg == 0 ? (li < 24 ? li : 96 + li) : 32 * lg - 8 + li;
@@ -443,6 +445,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // its key product and softmax
   constexpr bool VJIT = KVQ_DECODE_V_JIT != 0;
   constexpr bool PF2 = KVQ_DECODE_PF2 != 0;
+  constexpr bool DYN = KVQ_DECODE_DYN != 0;
   struct Buf {
     uint32_t kw[NS][JB][NWK];
     uint32_t vw[VJIT ? 1 : NS][8][WVS];
@@ -464,10 +467,10 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     return rsrc(g.v_codes + v_tile_offset(g, bh / g.H, bh % g.H, tile), 2048 * VB);
   };
 
-  // sub-tile `sub` (a constant after unrolling) of the wave's tile number ti:
-  // key blocks (and, for sub-tile 0, the tile's key parameters) ...
-  auto load_k = [&](Buf& bf, int ti, int sub) {
-    const int tile = t_first + t_step * ti;
+  // sub-tile `sub` (a constant after unrolling) of the chunk's tile k: key
+  // blocks (and, for sub-tile 0, the tile's key parameters) ...
+  auto load_k = [&](Buf& bf, int k, int sub) {
+    const int tile = t_base + t_stride * k;
 #pragma unroll
     for (int s = 0; s < NS; s++) {
       const int bh = min(grp * NS + s, BH - 1);   // a missing stream re-reads a valid one
@@ -515,20 +518,35 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     }
   };
   // ... and the own stream's value scales / zeros of the lane's TPS tokens
-  auto load_p = [&](Buf& bf, int ti, int sub) {
-    const int tile = t_first + t_step * ti;
+  auto load_p = [&](Buf& bf, int k, int sub) {
+    const int tile = t_base + t_stride * k;
     const uint32_t psoff = (uint32_t)(tile * 128 + sub * TPS) * PB;
     pload<PDT, TPS>(r_vs, vpoff, psoff, bf.vs);
     pload<PDT, TPS>(r_vz, vpoff, psoff, bf.vz);
   };
-  auto load = [&](Buf& bf, int ti, int sub) {
-    load_k(bf, ti, sub);
-    load_p(bf, ti, sub);
+  auto load = [&](Buf& bf, int k, int sub) {
+    load_k(bf, k, sub);
+    load_p(bf, k, sub);
   };
 
   // the first sub-tile's loads are in flight while the query is staged
   Buf b0, b1;
-  if (n_iter > 0) load(b0, 0, 0);
+  // tiles of the chunk handed out to the waves one at a time (dynamic) or in
+  // the fixed order k = w, w + 4, ...; the queue holds the wave's next four
+  __shared__ int s_next;
+  auto grab = [&]() -> int {
+    int v = 0;
+    if (lane == 0) v = atomicAdd(&s_next, 1);
+    return __builtin_amdgcn_readfirstlane(v);
+  };
+  int q0, q1, q2, q3;
+  if constexpr (DYN) {
+    if (threadIdx.x == 0) s_next = 4;   // k = 0..3 go to waves 0..3 without an atomic
+    q0 = wave;
+  } else {
+    q0 = wave;
+  }
+  if (q0 < t_count) load(b0, q0, 0);
 
   // ---- the query heads of the group in slot order, [column][slot] bf16 in
   // LDS (column n = stream n / G, head n % G; zero for columns without a head)
@@ -634,13 +652,14 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     bk0 = a.sl2 * beta;
   };
 
-  // compute sub-tile (ti, sub) from bf; with the two-ahead prefetch, bf is
-  // refilled with sub-tile (ti2, sub2) as soon as each part has been read
+  // compute sub-tile sub of the chunk's tile ti from bf; with the two-ahead
+  // prefetch, bf is refilled with sub-tile (ti2, sub2) as soon as each part has
+  // been read
   auto compute = [&](Buf& bf, int ti, int sub, int ti2, int sub2) {
     uint32_t vjit[VJIT ? NS : 1][8][WVS];
     if constexpr (VJIT) {
 #pragma unroll
-      for (int s = 0; s < NS; s++) load_vw(&vjit[s][0][0], v_rsrc(s, t_first + t_step * ti), sub);
+      for (int s = 0; s < NS; s++) load_vw(&vjit[s][0][0], v_rsrc(s, t_base + t_stride * ti), sub);
     }
     const uint32_t* vwp = VJIT ? &vjit[0][0][0] : &bf.vw[0][0][0];
     if (sub == 0) fold_query(bf);
@@ -786,23 +805,38 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // sub-tile after the wave's last one re-reads that last one (harmless, in
   // bounds) instead of branching.
   constexpr int U = NSUB >= 2 ? NSUB : 2;
+  constexpr int TPI = U / NSUB;   // tiles per iteration (2 for one-sub-tile tiles)
+  if constexpr (DYN) {
+    q1 = grab(); q2 = grab(); q3 = grab();
+  } else {
+    q1 = q0 + 4; q2 = q0 + 8; q3 = q0 + 12;
+  }
+  // the queue entry for sub-tile offset d (d = 0..3 tiles ahead), a valid tile
+  // when it lies past the chunk (such prefetches are never consumed)
+  auto qk = [&](int d) -> int {
+    const int v = d == 0 ? q0 : (d == 1 ? q1 : (d == 2 ? q2 : q3));
+    return v < t_count ? v : q0;
+  };
   if constexpr (PF2) {
-    if (n_iter > 0) load(b1, min(1 / NSUB, my_tiles - 1), 1 % NSUB);
+    if (q0 < t_count) load(b1, qk(1 / NSUB), 1 % NSUB);
   }
 #pragma unroll 1
-  for (int it = 0; it < n_iter; it += U) {
-    const int ti0 = it / NSUB;
+  while (q0 < t_count) {
 #pragma unroll
     for (int u = 0; u < U; u++) {
       if constexpr (NSUB == 1) {
-        if (u == 1 && it + 1 >= n_iter) break;
+        if (u == 1 && q1 >= t_count) break;
       }
-      const int ti2 = min(ti0 + (u + 2) / NSUB, my_tiles - 1);
-      if constexpr (!PF2) {
-        const int nti = min(ti0 + (u + 1) / NSUB, my_tiles - 1);
-        load((u % 2 == 0) ? b1 : b0, nti, (u + 1) % NSUB);
-      }
-      compute((u % 2 == 0) ? b0 : b1, ti0 + u / NSUB, u % NSUB, ti2, (u + 2) % NSUB);
+      if constexpr (!PF2) load((u % 2 == 0) ? b1 : b0, qk((u + 1) / NSUB), (u + 1) % NSUB);
+      compute((u % 2 == 0) ? b0 : b1, qk(u / NSUB), u % NSUB, qk((u + 2) / NSUB), (u + 2) % NSUB);
+    }
+    if constexpr (TPI == 1) {
+      q0 = q1; q1 = q2; q2 = q3;
+      q3 = DYN ? grab() : q3 + 4;
+    } else {
+      q0 = q2; q1 = q3;
+      q2 = DYN ? grab() : q2 + 8;
+      q3 = DYN ? grab() : q3 + 8;
     }
   }
 
