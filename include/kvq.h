@@ -55,12 +55,14 @@
  *   Key tile, uniform width b (2048*b bytes): 128 rows of 16*b bytes; row t is
  *     token 128g + t, element c is channel c.
  *   Value tile, width b (2048*b bytes): 32-bit little-endian words W[w][c][a]
- *     for w in [0, b), c in [0, 128), a in [0, 4), a varying fastest (word
- *     index (w * 128 + c) * 4 + a).  Word W[w][c][a] holds channel c of the
- *     32/b tokens 128g + 32a + w*(32/b) + i, i = 0 .. 32/b - 1, code i at bits
- *     [i*b, i*b + b).  (At b = 1 these are channel rows of 16 bytes; wider
- *     codes split every channel's 128 tokens into b word planes, so the words
- *     holding one token slice are contiguous across all channels.)
+ *     for w in [0, b), c in [0, 128), a in [0, 4).  Word W[w][c][a] holds
+ *     channel c of the 32/b tokens 128g + 32a + w*(32/b) + i,
+ *     i = 0 .. 32/b - 1, code i at bits [i*b, i*b + b).  Writing
+ *     c = 64h + 16q + n (h in [0, 2), q in [0, 4), n in [0, 16)), the word sits
+ *     at word index w*512 + ((h*16 + n)*4 + a)*4 + q.  (Every channel's 128
+ *     tokens are split into b word planes of 512 words; inside a plane, the
+ *     four words of channels 16q + n, q = 0..3, for one token slice a are
+ *     contiguous.)
  *   Key tile, mixed width (k_bits == KVQ_KMIXED, 4352 bytes) ([CHANMIX] Key
  *     design 3: 4/3/2/1-bit channel classes, as many 1-bit as 3-bit channels,
  *     channels reordered so every byte holds exactly 8 code bits):

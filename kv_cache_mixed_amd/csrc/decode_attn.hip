@@ -412,7 +412,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   const uint32_t koff = MIXED ? (uint32_t)((lg == 0 ? 0 : 1024 * lg) + 8 * row0)
                               : (uint32_t)(row0 * ROW_K + 4 * KB * lg);
   const uint32_t koff4 = 4096 + 2 * row0;                       // mixed plane 4
-  const uint32_t voff = (uint32_t)(4 * n + lg) * 4;             // value word (w, c, a)
+  const uint32_t voff4 = (uint32_t)(4 * n + lg) * 16;           // value words (w, h, n, lg, 0..3)
   // parameter arrays from the group's first stream on (offsets stay below 2^32:
   // the host bounds max_tokens)
   const int64_t s0 = (int64_t)grp * NS;
@@ -453,14 +453,19 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     uint32_t kp[NS][2][KPL];   // next tile's key scales / zeros (sub-tile 0 only)
   };
 
-  // value word planes: word (w, c, a) at byte ((w*128 + c)*4 + a)*4; the
-  // per-load constant goes to the scalar offset (one lane offset)
+  // value word planes: word (w, c = 64h + 16q + n, a) at word index
+  // w*512 + ((h*16 + n)*4 + a)*4 + q, so lane (n, lg) finds the words of its
+  // channels n, 16+n, 32+n, 48+n (h = 0) and 64+n, ... (h = 1) as 16
+  // contiguous bytes: two 16-byte loads per plane, 1 KB per wave each
   auto load_vw = [&](uint32_t* vw, __amdgpu_buffer_rsrc_t rv, int sub) {
 #pragma unroll
     for (int w = 0; w < WVS; w++)
 #pragma unroll
-      for (int cb = 0; cb < 8; cb++)
-        vw[cb * WVS + w] = __builtin_amdgcn_raw_buffer_load_b32(rv, voff, (uint32_t)(sub * WVS + w) * 2048 + 256 * cb, 0);
+      for (int h = 0; h < 2; h++) {
+        const u32x4 v4 = __builtin_amdgcn_raw_buffer_load_b128(rv, voff4, (uint32_t)(sub * WVS + w) * 2048 + 1024 * h, 0);
+#pragma unroll
+        for (int q = 0; q < 4; q++) vw[(4 * h + q) * WVS + w] = v4[q];
+      }
   };
   auto v_rsrc = [&](int s, int tile) {
     const int bh = min(grp * NS + s, BH - 1);

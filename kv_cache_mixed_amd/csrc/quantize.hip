@@ -57,14 +57,16 @@ __device__ __forceinline__ void pack_rows_store(const uint16_t* codes, uint8_t* 
 }
 
 // Value tile: codes[c][t] (LDS, pitch PITCH) -> 32-bit words W[w][c][a]
-// (word index (w*128 + c)*4 + a) holding channel c of tokens
-// 32a + w*(32/BITS) + i, code i at bits [i*BITS, (i+1)*BITS).
+// holding channel c of tokens 32a + w*(32/BITS) + i, code i at bits
+// [i*BITS, (i+1)*BITS); with c = 64h + 16q + n the word index is
+// w*512 + ((h*16 + n)*4 + a)*4 + q (threads write consecutive words).
 template <int BITS, int PITCH>
 __device__ __forceinline__ void pack_vtile_store(const uint16_t* codes, uint8_t* tile) {
   constexpr int PER_WORD = 32 / BITS;
   uint32_t* out = (uint32_t*)tile;
   for (int idx = threadIdx.x; idx < 512 * BITS; idx += blockDim.x) {
-    const int w = idx >> 9, c = (idx >> 2) & 127, a = idx & 3;
+    const int w = idx >> 9, h = (idx >> 8) & 1, n = (idx >> 4) & 15, a = (idx >> 2) & 3, q = idx & 3;
+    const int c = 64 * h + 16 * q + n;
     const uint16_t* src = codes + c * PITCH + 32 * a + w * PER_WORD;
     uint32_t word = 0;
 #pragma unroll

@@ -54,8 +54,10 @@ __global__ __launch_bounds__(256) void shrink_kernel(Geo g) {
 #pragma unroll
     for (int i = 0; i < IN_WORDS; i++) w[i] = in[i];
   } else {
-    // value tile: output word o = (wp*128 + c)*4 + a takes its low half from
-    // input word o + wp*512 (plane 2wp) and its high half from o + (wp+1)*512
+    // value tile: output word o = wp*512 + r (r: position inside the word
+    // plane, the same function of (channel, lane group) at every width) takes
+    // its low half from input word o + wp*512 (plane 2wp, same r) and its high
+    // half from o + (wp+1)*512 (plane 2wp+1)
     const uint32_t* in = (const uint32_t*)base;
 #pragma unroll
     for (int k = 0; k < OUT_WORDS; k++) {

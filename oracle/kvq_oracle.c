@@ -282,14 +282,17 @@ void orc_unpack_rows(const uint8_t *tile, int bits, uint16_t *codes)
 }
 
 /* Value tile (header layout text): 32-bit little-endian words W[w][c][a],
- * word index (w*128 + c)*4 + a, w < b, c < 128, a < 4; word W[w][c][a] holds
- * the codes of channel c for tokens 32a + w*(32/b) + i, i < 32/b, code i at
- * bits [i*b, i*b + b).  Bit position of the code of (channel c, token t): */
+ * w < b, c < 128, a < 4; word W[w][c][a] holds the codes of channel c for
+ * tokens 32a + w*(32/b) + i, i < 32/b, code i at bits [i*b, i*b + b).  With
+ * c = 64h + 16q + n (h < 2, q < 4, n < 16) it sits at word index
+ * w*512 + ((h*16 + n)*4 + a)*4 + q.  Bit position of the code of (channel c,
+ * token t): */
 static int64_t vtile_bitpos(int c, int t, int bits)
 {
     int per_word = 32 / bits;
     int a = t / 32, w = (t % 32) / per_word, i = t % per_word;
-    int64_t word = ((int64_t)w * 128 + c) * 4 + a;
+    int h = c / 64, q = (c / 16) % 4, n = c % 16;
+    int64_t word = (int64_t)w * 512 + ((h * 16 + n) * 4 + a) * 4 + q;
     return word * 32 + (int64_t)i * bits;
 }
 

@@ -292,24 +292,30 @@ def test_pack_bit_positions_by_hand():
 
 def test_value_tile_positions_by_hand():
     """Value word planes W[w][c][a] (header layout text), positions worked out
-    by hand: 4-bit -> 8 tokens per word, word index (w*128 + c)*4 + a."""
+    by hand: 4-bit -> 8 tokens per word; with c = 64h + 16q + n the word index
+    is w*512 + ((h*16 + n)*4 + a)*4 + q."""
     c = np.zeros((128, 128), np.uint16)          # [channel][token]
     c[0, 0] = 0x3                                # w=0,c=0,a=0,i=0 -> byte 0 low nibble
     c[0, 9] = 0x5                                # t=9: a=0, w=1, i=1 -> word 512, bits 4..7
-    c[2, 33] = 0xF                               # t=33: a=1, w=0, i=1 -> word 9, bits 4..7
-    c[127, 127] = 0x6                            # a=3, w=3, i=7 -> word (3*128+127)*4+3, bits 28..31
+    c[2, 33] = 0xF                               # t=33: a=1, w=0, i=1; n=2 -> word (2*4+1)*4 = 36
+    c[20, 0] = 0x7                               # c=20: h=0, q=1, n=4 -> word (4*4)*4 + 1 = 65
+    c[64, 0] = 0x9                               # c=64: h=1, q=0, n=0 -> word (16*4)*4 = 256
+    c[127, 127] = 0x6                            # h=1,q=3,n=15, a=3, w=3, i=7 -> word 2047, bits 28..31
     t = oracle.pack_vtile(c, 4)
     assert t[0] == 0x03
     assert t[4 * 512] == 0x50
-    assert t[4 * 9] == 0xF0
-    assert t[4 * ((3 * 128 + 127) * 4 + 3) + 3] == 0x60
+    assert t[4 * 36] == 0xF0
+    assert t[4 * 65] == 0x07
+    assert t[4 * 256] == 0x09
+    assert t[4 * 2047 + 3] == 0x60
+    assert int(np.count_nonzero(t)) == 6
     c1 = np.zeros((128, 128), np.uint16)
-    c1[5, 40] = 1                                # 1-bit: w=0, a=1, i=8 -> word 21, bit 8
-    assert oracle.pack_vtile(c1, 1)[4 * 21 + 1] == 0x01
+    c1[5, 40] = 1                                # 1-bit: w=0, a=1, i=8; n=5 -> word (5*4+1)*4 = 84, bit 8
+    assert oracle.pack_vtile(c1, 1)[4 * 84 + 1] == 0x01
     c16 = np.zeros((128, 128), np.uint16)
-    c16[1, 3] = 0xBEEF                           # 16-bit: 2 tokens per word; t=3: w=1, i=1
+    c16[1, 3] = 0xBEEF                           # 16-bit: 2 tokens per word; t=3: w=1, i=1; n=1
     t16 = oracle.pack_vtile(c16, 16)
-    wi = (1 * 128 + 1) * 4 + 0
+    wi = 512 + (1 * 4 + 0) * 4
     assert t16[4 * wi + 2] == 0xEF and t16[4 * wi + 3] == 0xBE
     for bits in (1, 2, 4, 8, 16):
         r = np.random.default_rng(bits).integers(0, 2 ** bits, (128, 128)).astype(np.uint16)
