@@ -321,9 +321,8 @@ __device__ __forceinline__ void pload(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 // 1-bit values need the full register file.
 constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
   (void)pdt;
-  (void)ns;
   if (KVQ_DECODE_WAVES_PER_SIMD) return KVQ_DECODE_WAVES_PER_SIMD;
-  if (kb == 16 || (kb == 0 && vb == 1)) return 1;
+  if (kb == 16 || (kb == 0 && vb == 1) || ns >= 3) return 1;
   return 2;
 }
 
@@ -1029,8 +1028,10 @@ static hipError_t launch_ns(const DecodeArgs& a0, hipStream_t st) {
     hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 1>), grid, block, 0, st, a);
   } else if (p.ns == 2) {
     if constexpr (CAP >= 2) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 2>), grid, block, 0, st, a);
-  } else {
+  } else if (p.ns == 3) {
     if constexpr (CAP >= 3) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 3>), grid, block, 0, st, a);
+  } else {
+    if constexpr (CAP >= 4) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 4>), grid, block, 0, st, a);
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.n_chunks == 1) return e;
