@@ -916,16 +916,13 @@ constexpr int ns_cap(int kb, int vb) {
 // group cut into n_chunks chunks of tpc tiles, aiming at one round of
 // resident workgroups (256 CUs x waves per SIMD) with 4..64 tiles per chunk and
 // at most KVQ_MAX_CHUNKS chunks.
-DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_tiles) {
+static DecodePlan plan_for(int BH, int ns, int k_bits, int v_bits, int pdt, int n_tiles) {
   DecodePlan p;
-  const int cap = ns_cap(k_bits, v_bits);
-  int ns = 16 / G;
-  if (ns > KVQ_DECODE_NS_MAX) ns = KVQ_DECODE_NS_MAX;
-  p.ns = ns > cap ? cap : (ns < 1 ? 1 : ns);
-  p.n_groups = (BH + p.ns - 1) / p.ns;
+  p.ns = ns;
+  p.n_groups = (BH + ns - 1) / ns;
   const long total = (long)p.n_groups * n_tiles;
   // about one round of resident workgroups
-  const long wg_target = (long)KVQ_DECODE_WG_PER_OCC * decode_occ(k_bits, v_bits, pdt, p.ns);
+  const long wg_target = (long)KVQ_DECODE_WG_PER_OCC * decode_occ(k_bits, v_bits, pdt, ns);
   int tpc = (int)((total + wg_target - 1) / wg_target);
   tpc = ((tpc + 3) / 4) * 4;
   if (tpc < 4) tpc = 4;
@@ -934,6 +931,20 @@ DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_til
   if (tpc < tmin) tpc = tmin;
   p.n_chunks = (n_tiles + tpc - 1) / tpc;
   p.tpc = (n_tiles + p.n_chunks - 1) / p.n_chunks;   // balanced, every chunk non-empty
+  return p;
+}
+
+// As many streams per wave as the columns and ns_cap() allow -- unless that
+// leaves a wave fewer than four tiles, where a single stream per wave (twice
+// the tiles, the prologue and partial write amortised over more work) is
+// faster.
+DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_tiles) {
+  const int cap = ns_cap(k_bits, v_bits);
+  int ns = 16 / G;
+  if (ns > KVQ_DECODE_NS_MAX) ns = KVQ_DECODE_NS_MAX;
+  ns = ns > cap ? cap : (ns < 1 ? 1 : ns);
+  DecodePlan p = plan_for(BH, ns, k_bits, v_bits, pdt, n_tiles);
+  if (ns > 1 && p.tpc < 16) p = plan_for(BH, 1, k_bits, v_bits, pdt, n_tiles);
   return p;
 }
 
