@@ -60,10 +60,10 @@
 #ifndef KVQ_DECODE_NS_MAX
 #define KVQ_DECODE_NS_MAX 3
 #endif
-// load a sub-tile's value words when it is computed (1) or with the
-// prefetched buffer one sub-tile earlier (0)
-#ifndef KVQ_DECODE_V_JIT
-#define KVQ_DECODE_V_JIT 1
+// value words of sub-tile j are loaded at the start of sub-tile j (0) or of
+// sub-tile j-1 (1)
+#ifndef KVQ_DECODE_V_AHEAD
+#define KVQ_DECODE_V_AHEAD 0
 #endif
 // prefetch key blocks / value parameters two sub-tiles ahead, refilling a
 // buffer as soon as its part has been consumed (1), or one sub-tile ahead (0)
@@ -439,15 +439,14 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   uint32_t* my_lds = lds[wave];
 
   // one sub-tile of raw operands
-  // value words either travel with the prefetched buffer or (KVQ_DECODE_V_JIT)
-  // are loaded at the start of the sub-tile's own compute, in flight during
-  // its key product and softmax
-  constexpr bool VJIT = KVQ_DECODE_V_JIT != 0;
+  // value words travel outside the prefetch buffers: they are loaded at the
+  // start of their own sub-tile (in flight during its key product and
+  // softmax) or one sub-tile earlier
+  constexpr bool VAHEAD = KVQ_DECODE_V_AHEAD != 0;
   constexpr bool PF2 = KVQ_DECODE_PF2 != 0;
   constexpr bool DYN = KVQ_DECODE_DYN != 0;
   struct Buf {
     uint32_t kw[NS][JB][NWK];
-    uint32_t vw[VJIT ? 1 : NS][8][WVS];
     uint32_t vs[PWV], vz[PWV];
     uint32_t kp[NS][2][KPL];   // next tile's key scales / zeros (sub-tile 0 only)
   };
@@ -481,8 +480,6 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       const int bs = bh / g.H, hs = bh % g.H;
       const __amdgpu_buffer_rsrc_t rk =
           rsrc(g.k_codes + k_tile_offset(g, bs, hs, tile), MIXED ? KVQ_MIXED_TILE_BYTES : 2048 * KB);
-      const __amdgpu_buffer_rsrc_t rv = v_rsrc(s, tile);
-      (void)rv;
 #pragma unroll
       for (int jj = 0; jj < JB; jj++) {
         const uint32_t soff = (uint32_t)(sub * JB) * 4 * ROW_K;       // rows 4j apart
@@ -506,7 +503,6 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
           bf.kw[s][jj][0] = __builtin_amdgcn_raw_buffer_load_b32(rk, koff + jj * 4 * ROW_K, soff, 0);
         }
       }
-      if constexpr (!VJIT) load_vw(&bf.vw[s][0][0], rv, sub);
     }
     if (sub == 0) {
 #pragma unroll
@@ -659,13 +655,16 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // compute sub-tile sub of the chunk's tile ti from bf; with the two-ahead
   // prefetch, bf is refilled with sub-tile (ti2, sub2) as soon as each part has
   // been read
-  auto compute = [&](Buf& bf, int ti, int sub, int ti2, int sub2) {
-    uint32_t vjit[VJIT ? NS : 1][8][WVS];
-    if constexpr (VJIT) {
+  auto issue_v = [&](uint32_t* vw, int k, int sub) {
 #pragma unroll
-      for (int s = 0; s < NS; s++) load_vw(&vjit[s][0][0], v_rsrc(s, t_base + t_stride * ti), sub);
-    }
-    const uint32_t* vwp = VJIT ? &vjit[0][0][0] : &bf.vw[0][0][0];
+    for (int s = 0; s < NS; s++) load_vw(vw + s * 8 * WVS, v_rsrc(s, t_base + t_stride * k), sub);
+  };
+  auto compute = [&](Buf& bf, int ti, int sub, int ti2, int sub2, uint32_t* vcur, uint32_t* vnext,
+                     int ti1, int sub1) {
+    uint32_t vjit[VAHEAD ? 1 : NS * 8 * WVS];
+    if constexpr (VAHEAD) issue_v(vnext, ti1, sub1);
+    else issue_v(vjit, ti, sub);
+    const uint32_t* vwp = VAHEAD ? vcur : vjit;
     if (sub == 0) fold_query(bf);
     // ---- logits: k-step-major over all (stream, block) accumulators
     f32x4 acc[NS][JB];
@@ -824,6 +823,10 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   if constexpr (PF2) {
     if (q0 < t_count) load(b1, qk(1 / NSUB), 1 % NSUB);
   }
+  uint32_t vb[VAHEAD ? 2 : 1][VAHEAD ? NS * 8 * WVS : 1];
+  if constexpr (VAHEAD) {
+    if (q0 < t_count) issue_v(vb[0], q0, 0);
+  }
 #pragma unroll 1
   while (q0 < t_count) {
 #pragma unroll
@@ -832,7 +835,8 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
         if (u == 1 && q1 >= t_count) break;
       }
       if constexpr (!PF2) load((u % 2 == 0) ? b1 : b0, qk((u + 1) / NSUB), (u + 1) % NSUB);
-      compute((u % 2 == 0) ? b0 : b1, qk(u / NSUB), u % NSUB, qk((u + 2) / NSUB), (u + 2) % NSUB);
+      compute((u % 2 == 0) ? b0 : b1, qk(u / NSUB), u % NSUB, qk((u + 2) / NSUB), (u + 2) % NSUB,
+              vb[VAHEAD ? u % 2 : 0], vb[VAHEAD ? (u + 1) % 2 : 0], qk((u + 1) / NSUB), (u + 1) % NSUB);
     }
     if constexpr (TPI == 1) {
       q0 = q1; q1 = q2; q2 = q3;
