@@ -133,6 +133,8 @@ typedef enum {
 /* Largest per-stream capacity (2^26 tokens): device offsets into the
  * per-stream parameter arrays are 32-bit. */
 #define KVQ_MAX_TOKENS (1 << 26)
+/* Most residual (unquantized) tokens one decode call attends per stream. */
+#define KVQ_MAX_RESIDUAL 512
 #define KVQ_MIXED_TILE_BYTES 4352
 
 typedef struct kvq_cache {
@@ -208,6 +210,33 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads);
 kvq_status kvq_decode_attn(const kvq_cache *cache, const void *q, int32_t n_q_heads,
                            float softmax_scale, float *out, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/* Decode attention over the packed cache together with a residual segment
+ * of res_len tokens per stream that are not packed ([PMKVQ] Training
+ * strategy and Related work: as in KIVI, the first token and the most recent
+ * tokens are kept at 16-bit precision instead of the low-bit codes).  The
+ * caller holds those tokens -- the first token, and the recent tokens of the
+ * 128-token group not yet quantized -- in res_k / res_v.  For batch b and
+ * query head hq (kv head h = hq / G) the attended set is the n_tokens stored
+ * tokens (reconstructions S' * q + Z') and the residual tokens
+ * t = 0 .. res_len-1 with keys res_k[b][h][t][0..128) and values
+ * res_v[b][h][t][0..128), read exactly (res_dtype KVQ_F32, KVQ_F16 or
+ * KVQ_BF16) at element offsets b*s[0] + h*s[1] + t*s[2] + c
+ * (s = res_k_strides / res_v_strides, channel stride 1; res_k and res_v
+ * 16-byte aligned and every stride a multiple of 16 bytes, else
+ * KVQ_EINVAL).  Attention does not
+ * depend on the order of the tokens (positions are already applied to the
+ * keys), so the residual tokens may be in any order.
+ * 0 <= res_len <= KVQ_MAX_RESIDUAL; n_tokens may be 0 when res_len >= 1;
+ * res_len = 0 is kvq_decode_attn.  Logits and weights of the residual tokens
+ * are formed in binary32 and merged with the packed part through one more
+ * partial (max, sum, weighted values) per head.  Other arguments, the
+ * workspace and errors as for kvq_decode_attn. */
+kvq_status kvq_decode_attn_residual(const kvq_cache *cache, const void *q, int32_t n_q_heads,
+                                    float softmax_scale, const void *res_k, const void *res_v,
+                                    kvq_dtype res_dtype, const int64_t res_k_strides[3],
+                                    const int64_t res_v_strides[3], int32_t res_len, float *out,
+                                    void *workspace, size_t workspace_bytes, hipStream_t stream);
 
 /* ------------------------------------------------------------------------
  * Progressive schedule ([PMKVQ] Overall framework and Key design 1: each

@@ -18,9 +18,9 @@
 //   four lane groups through cross-lane max)
 //   O^T[c][n] += sum_t V[c][t] * P[t][n],  P = e^(logit - m) * S_V[t] * 2^k'
 //   zsum_n    += sum_t e^(logit - m) * Z_V[t]
-// The workgroup merges its four wave partials in LDS, writes one partial
-// (m, l, o[128]) per head, and the last workgroup of the stream (device-scope
-// counter) combines all chunks:  o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
+// The workgroup merges its four wave partials in LDS and writes one partial
+// (m, l, o[128]) per head; a second kernel combines the chunks of a stream:
+// o = sum_s 2^(m_s - M) o_s / sum_s 2^(m_s - M) l_s.
 //
 // MFMA operand layout (16x16x32 f16): lane l = 16*g + n holds, for A, row n and
 // k-slice g (8 values), for B, column n and k-slice g, and receives D rows
@@ -203,9 +203,10 @@ struct DecodeArgs {
   Geo g;
   const uint16_t* q;  // bf16 [B][Hq][128]
   float* out;         // [B][Hq][128]
-  float* part_ml;     // [BH][n_chunks][G][2]   (running max in log2 units, sum)
-  float* part_o;      // [BH][n_chunks][G][128] (unnormalised output)
+  float* part_ml;     // [BH][n_slots][G][2]   (running max in log2 units, sum)
+  float* part_o;      // [BH][n_slots][G][128] (unnormalised output)
   int G, n_chunks, tpc, n_groups;
+  int n_slots;        // partial slots per stream: n_chunks + residual slots
   float sl2;          // softmax_scale * log2(e)
 };
 
@@ -876,7 +877,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 
   const int Hq = g.H * G;
   const int ncol = NS * G;
-  const bool single = (a.n_chunks == 1);
+  const bool single = (a.n_slots == 1);
   for (int idx = threadIdx.x; idx < ncol * 128; idx += 256) {
     const int col = idx >> 7, c = idx & 127;
     const int s = col / G, hh = col - s * G;
@@ -897,7 +898,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     if (single) {
       a.out[((int64_t)bo * Hq + (int64_t)ho * G + hh) * 128 + c] = num / den;
     } else {
-      const int64_t row = ((int64_t)bh * a.n_chunks + chunk) * G + hh;
+      const int64_t row = ((int64_t)bh * a.n_slots + chunk) * G + hh;
       if (c == 0) { a.part_ml[2 * row] = M; a.part_ml[2 * row + 1] = den; }
       a.part_o[row * 128 + c] = num;
     }
@@ -1005,12 +1006,143 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
   *(float2*)(out + ((int64_t)bo * H * G + (int64_t)ho * G + hh) * 128 + 2 * lane) = make_float2(n0 * inv, n1 * inv);
 }
 
+// Residual segment: R tokens per stream that are not packed (the first and
+// recent tokens the caller keeps at 16-bit or full precision), attended in
+// binary32.  Workgroup (rc, bh) takes tokens [32 rc, 32 rc + 32) of stream bh
+// and emits one more partial (m, l, o) per head in slot slot0 + rc -- or, when
+// it is the only partial of the stream, the normalised row straight into
+// `out`.  Every thread issues all its 16-byte loads (query, keys, values)
+// before the first use, so a workgroup costs one memory round trip; logits,
+// softmax and the value product then run out of LDS.  The LDS footprint
+// (~43 KB) leaves room to run beside two decode workgroups on a CU.
+template <int IN>
+__device__ __forceinline__ float res_elem(uint4 w, int j) {
+  if constexpr (IN == KVQ_F32) {
+    return u2f(j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w);
+  } else {
+    const uint32_t x = (j >> 1) == 0 ? w.x : (j >> 1) == 1 ? w.y : (j >> 1) == 2 ? w.z : w.w;
+    const uint32_t hbits = (j & 1) ? (x >> 16) : (x & 0xffffu);
+    if constexpr (IN == KVQ_F16) return f16_bits_to_f32(hbits);
+    else return bf16_bits_to_f32(hbits);
+  }
+}
+
+template <int IN>
+__global__ __launch_bounds__(256) void decode_residual_kernel(ResArgs r, const uint16_t* __restrict__ q,
+                                                              int H, int G, float sl2,
+                                                              float* __restrict__ part_ml,
+                                                              float* __restrict__ part_o, int n_slots,
+                                                              int slot0, float* __restrict__ out) {
+  constexpr int RC = KVQ_RES_CHUNK;
+  constexpr int VW = IN == KVQ_F32 ? 4 : 8;                 // elements per 16-byte load
+  constexpr int NV = RC * 128 / VW / 256;                   // loads per thread per operand
+  static_assert(RC == 32 && NV >= 1, "one token per half wave in the softmax");
+  __shared__ float qv[16][129];                   // padded rows: conflict-free across tokens
+  __shared__ float ks[RC][129];
+  __shared__ float vs[RC][129];
+  __shared__ __align__(16) float sp[RC][16];      // [token][head]: logits, then weights
+  __shared__ float sm[16][2];                     // per head: max, sum
+  const int tid = threadIdx.x, rc = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / H, h = bh - (bh / H) * H;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int t0 = rc * RC, n = min(RC, r.R - t0);
+  const int64_t kb = (int64_t)b * r.ks[0] + (int64_t)h * r.ks[1] + (int64_t)t0 * r.ks[2];
+  const int64_t vb = (int64_t)b * r.vs[0] + (int64_t)h * r.vs[1] + (int64_t)t0 * r.vs[2];
+  const int esz = IN == KVQ_F32 ? 4 : 2;
+  uint4 qw = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < G * 16) qw = ((const uint4*)(q + ((int64_t)b * H * G + (int64_t)h * G) * 128))[tid];
+  // rows past n repeat row n - 1 (in bounds, never used): the loads need no branch
+  uint4 kw[NV], vw[NV];
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int j = tid + 256 * i, t = min(j / (128 / VW), n - 1), c = (j % (128 / VW)) * VW;
+    kw[i] = *(const uint4*)((const uint8_t*)r.k + (kb + (int64_t)t * r.ks[2] + c) * esz);
+    vw[i] = *(const uint4*)((const uint8_t*)r.v + (vb + (int64_t)t * r.vs[2] + c) * esz);
+  }
+  if (tid < G * 16) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) qv[tid >> 4][(tid & 15) * 8 + e] = res_elem<KVQ_BF16>(qw, e);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int j = tid + 256 * i, t = j / (128 / VW), c = (j % (128 / VW)) * VW;
+#pragma unroll
+    for (int e = 0; e < VW; e++) {
+      ks[t][c + e] = res_elem<IN>(kw[i], e);
+      vs[t][c + e] = res_elem<IN>(vw[i], e);
+    }
+  }
+  __syncthreads();
+  // logits: thread i takes head i / n, token i % n
+  for (int i = tid; i < n * G; i += 256) {
+    const int hh = i / n, t = i - (i / n) * n;
+    float d = 0.0f;
+#pragma unroll 16
+    for (int c = 0; c < 128; c++) d = fmaf(qv[hh][c], ks[t][c], d);
+    sp[t][hh] = d * sl2;
+  }
+  __syncthreads();
+  // softmax: each wave takes two heads at a time, one per half wave (lane & 31 = token)
+  for (int hp = wave; 2 * hp < G; hp += 4) {
+    const int hh = 2 * hp + (lane >> 5), t = lane & 31;
+    const bool ok = hh < G && t < n;
+    const float s = ok ? sp[t][hh] : -INFINITY;
+    float m = s;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float e = ok ? exp2f(s - m) : 0.0f;
+    float l = e;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
+    if (hh < G) {
+      sp[t][hh] = e;                              // 0 for the rows past n
+      if (t == 0) { sm[hh][0] = m; sm[hh][1] = l; }
+    }
+  }
+  __syncthreads();
+  // values: thread takes channel tid & 127 and heads 8 hb .. 8 hb + 7 (hb =
+  // tid >> 7, uniform per wave); the sums of heads >= G are never stored
+  const int c = tid & 127, hb = tid >> 7;
+  if (8 * hb >= G) return;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) acc[j] = 0.0f;
+#pragma unroll 4
+  for (int t = 0; t < n; t++) {
+    const float x = vs[t][c];
+    const float4 w0 = *(const float4*)&sp[t][8 * hb];
+    const float4 w1 = *(const float4*)&sp[t][8 * hb + 4];
+    acc[0] = fmaf(w0.x, x, acc[0]);
+    acc[1] = fmaf(w0.y, x, acc[1]);
+    acc[2] = fmaf(w0.z, x, acc[2]);
+    acc[3] = fmaf(w0.w, x, acc[3]);
+    acc[4] = fmaf(w1.x, x, acc[4]);
+    acc[5] = fmaf(w1.y, x, acc[5]);
+    acc[6] = fmaf(w1.z, x, acc[6]);
+    acc[7] = fmaf(w1.w, x, acc[7]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const int hh = 8 * hb + j;
+    if (hh >= G) break;
+    if (out) {
+      out[((int64_t)b * H * G + (int64_t)h * G + hh) * 128 + c] = acc[j] / sm[hh][1];
+    } else {
+      const int64_t row = ((int64_t)bh * n_slots + slot0 + rc) * G + hh;
+      if (c == 0) { part_ml[2 * row] = sm[hh][0]; part_ml[2 * row + 1] = sm[hh][1]; }
+      part_o[row * 128 + c] = acc[j];
+    }
+  }
+}
+
 static size_t ml_bytes(int BH, int n_chunks, int G) {
   return ((size_t)BH * n_chunks * G * 2 * 4 + 255) / 256 * 256;
 }
 
+// partial slots: every chunk plus the most a residual segment can add
 size_t decode_workspace_needed(int BH, int G, const DecodePlan& p) {
-  return ml_bytes(BH, p.n_chunks, G) + (size_t)BH * p.n_chunks * G * 128 * 4;
+  const int slots = p.n_chunks + KVQ_MAX_RES_SLOTS;
+  return ml_bytes(BH, slots, G) + (size_t)BH * slots * G * 128 * 4;
 }
 
 size_t decode_workspace_bytes(int B, int H, int G, int max_tiles) {
@@ -1038,6 +1170,7 @@ static hipError_t launch_ns(const DecodeArgs& a0, hipStream_t st) {
   a.n_groups = p.n_groups;
   a.n_chunks = p.n_chunks;
   a.tpc = p.tpc;
+  a.n_slots = p.n_chunks + a.n_slots;   // residual slots on entry
   const dim3 grid(a.n_chunks, a.n_groups), block(256);
   if (p.ns == 1) {
     hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 1>), grid, block, 0, st, a);
@@ -1048,11 +1181,6 @@ static hipError_t launch_ns(const DecodeArgs& a0, hipStream_t st) {
   } else {
     if constexpr (CAP >= 4) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 4>), grid, block, 0, st, a);
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || a.n_chunks == 1) return e;
-  const int rows = a.g.B * a.g.H * a.G;
-  hipLaunchKernelGGL(decode_combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, (const float*)a.part_ml,
-                     (const float*)a.part_o, a.out, a.g.B * a.g.H, a.g.H, a.G, a.n_chunks);
   return hipGetLastError();
 }
 
@@ -1067,26 +1195,73 @@ static hipError_t launch_decode_pdt(const DecodeArgs& a, hipStream_t st) {
   return hipErrorInvalidValue;
 }
 
+namespace {
+hipError_t launch_residual(const ResArgs& res, int res_dtype, dim3 grid, const void* q, int H, int G,
+                           float sl2, float* part_ml, float* part_o, int n_slots, int slot0,
+                           float* direct, hipStream_t st) {
+  if (res_dtype == KVQ_F32)
+    hipLaunchKernelGGL(decode_residual_kernel<KVQ_F32>, grid, dim3(256), 0, st, res, (const uint16_t*)q,
+                       H, G, sl2, part_ml, part_o, n_slots, slot0, direct);
+  else if (res_dtype == KVQ_F16)
+    hipLaunchKernelGGL(decode_residual_kernel<KVQ_F16>, grid, dim3(256), 0, st, res, (const uint16_t*)q,
+                       H, G, sl2, part_ml, part_o, n_slots, slot0, direct);
+  else
+    hipLaunchKernelGGL(decode_residual_kernel<KVQ_BF16>, grid, dim3(256), 0, st, res, (const uint16_t*)q,
+                       H, G, sl2, part_ml, part_o, n_slots, slot0, direct);
+  return hipGetLastError();
+}
+}  // namespace
+
+// Packed cache (when it holds tokens) and residual segment (res.R > 0), then
+// the chunk combine when a stream has more than one partial slot.  All on the
+// caller's stream: the residual kernel is short (one memory round trip per
+// workgroup), so a fork onto a second stream would cost more in cross-queue
+// synchronisation than it hides.
 hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float* out, void* ws,
-                         hipStream_t st) {
-  DecodeArgs a;
-  a.g = g;
-  a.q = (const uint16_t*)q;
-  a.out = out;
+                         const ResArgs& res, int res_dtype, hipStream_t st) {
   const int BH = g.B * g.H;
-  const DecodePlan p = decode_plan(BH, G, g.k_bits, g.v_bits, g.pdt, g.n_tiles);
-  a.part_ml = (float*)ws;
-  a.part_o = (float*)((uint8_t*)a.part_ml + ml_bytes(BH, p.n_chunks, G));
-  a.G = G;
-  a.sl2 = scale * 1.4426950408889634f;
-  a.n_chunks = a.tpc = a.n_groups = 0;
-  switch (g.pdt) {
-    case KVQ_F32: return launch_decode_pdt<KVQ_F32>(a, st);
-    case KVQ_F16: return launch_decode_pdt<KVQ_F16>(a, st);
-    case KVQ_BF16: return launch_decode_pdt<KVQ_BF16>(a, st);
-    case KVQ_E4M3: return launch_decode_pdt<KVQ_E4M3>(a, st);
+  const float sl2 = scale * 1.4426950408889634f;
+  const bool has_packed = g.n_tiles > 0;
+  const int n_res = (res.R + KVQ_RES_CHUNK - 1) / KVQ_RES_CHUNK;
+  DecodePlan p;
+  p.n_chunks = 0;
+  if (has_packed) p = decode_plan(BH, G, g.k_bits, g.v_bits, g.pdt, g.n_tiles);
+  const int n_slots = p.n_chunks + n_res;
+  float* part_ml = (float*)ws;
+  float* part_o = (float*)((uint8_t*)ws + ml_bytes(BH, n_slots, G));
+  hipError_t e = hipSuccess;
+  if (n_res > 0) {
+    e = launch_residual(res, res_dtype, dim3(n_res, BH), q, g.H, G, sl2, part_ml, part_o, n_slots,
+                        p.n_chunks, n_slots == 1 ? out : nullptr, st);
+    if (e != hipSuccess) return e;
   }
-  return hipErrorInvalidValue;
+  if (has_packed) {
+    DecodeArgs a;
+    a.g = g;
+    a.q = (const uint16_t*)q;
+    a.out = out;
+    a.part_ml = part_ml;
+    a.part_o = part_o;
+    a.G = G;
+    a.sl2 = sl2;
+    a.n_chunks = a.tpc = a.n_groups = 0;
+    a.n_slots = n_res;
+    switch (g.pdt) {
+      case KVQ_F32: e = launch_decode_pdt<KVQ_F32>(a, st); break;
+      case KVQ_F16: e = launch_decode_pdt<KVQ_F16>(a, st); break;
+      case KVQ_BF16: e = launch_decode_pdt<KVQ_BF16>(a, st); break;
+      case KVQ_E4M3: e = launch_decode_pdt<KVQ_E4M3>(a, st); break;
+      default: return hipErrorInvalidValue;
+    }
+    if (e != hipSuccess) return e;
+  }
+  if (n_slots > 1) {
+    const int rows = BH * G;
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, (const float*)part_ml,
+                       (const float*)part_o, out, BH, g.H, G, n_slots);
+    e = hipGetLastError();
+  }
+  return e;
 }
 
 }  // namespace kvq

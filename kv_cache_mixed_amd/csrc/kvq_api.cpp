@@ -160,25 +160,39 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* c, int32_t n_q_heads) {
   return kvq::decode_workspace_bytes(c->batch, c->n_kv_heads, G, c->max_tokens / 128);
 }
 
-kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t n_q_heads,
-                           float softmax_scale, float* out, void* workspace,
-                           size_t workspace_bytes, hipStream_t stream) {
-  try {
-    kvq_status s = check_cache(c);
-    if (s != KVQ_OK) return s;
-    if (!q || !out) return KVQ_EINVAL;
-    if (!aligned(q, 16) || !aligned(out, 16)) return KVQ_EINVAL;
-    if (n_q_heads < 1 || n_q_heads % c->n_kv_heads) return KVQ_EINVAL;
-    const int G = n_q_heads / c->n_kv_heads;
-    if (G > 16) return KVQ_EUNSUPPORTED;
-    if (c->n_tokens < 128) return KVQ_EINVAL;
-    if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY ||
-        softmax_scale == -INFINITY)
-      return KVQ_EINVAL;
-    if (!kvq::decode_supported(c->k_bits, c->v_bits, c->param_dtype)) return KVQ_EUNSUPPORTED;
-    if ((int64_t)c->batch * c->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
-    const size_t need = kvq::decode_workspace_bytes(c->batch, c->n_kv_heads, G, c->max_tokens / 128);
-    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return KVQ_EWORKSPACE;
+// Shared by kvq_decode_attn and kvq_decode_attn_residual: validate everything
+// on the host, then launch.
+static kvq_status decode_common(const kvq_cache* c, const void* q, int32_t n_q_heads,
+                                float softmax_scale, const kvq::ResArgs& res, int res_dtype,
+                                float* out, void* workspace, size_t workspace_bytes,
+                                hipStream_t stream) {
+  kvq_status s = check_cache(c);
+  if (s != KVQ_OK) return s;
+  if (!q || !out) return KVQ_EINVAL;
+  if (!aligned(q, 16) || !aligned(out, 16)) return KVQ_EINVAL;
+  if (n_q_heads < 1 || n_q_heads % c->n_kv_heads) return KVQ_EINVAL;
+  const int G = n_q_heads / c->n_kv_heads;
+  if (G > 16) return KVQ_EUNSUPPORTED;
+  if (res.R < 0 || res.R > KVQ_MAX_RESIDUAL) return KVQ_EINVAL;
+  if (res.R == 0 && c->n_tokens < 128) return KVQ_EINVAL;   // nothing to attend
+  if (res.R > 0) {
+    if (!res.k || !res.v) return KVQ_EINVAL;
+    if (res_dtype != KVQ_F32 && res_dtype != KVQ_F16 && res_dtype != KVQ_BF16) return KVQ_EINVAL;
+    // rows are read with 16-byte loads: aligned bases, strides in whole 16-byte units
+    const int64_t vw = res_dtype == KVQ_F32 ? 4 : 8;
+    if (!aligned(res.k, 16) || !aligned(res.v, 16)) return KVQ_EINVAL;
+    for (int i = 0; i < 3; i++)
+      if (res.ks[i] < 0 || res.vs[i] < 0 || res.ks[i] % vw || res.vs[i] % vw) return KVQ_EINVAL;
+  }
+  if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY ||
+      softmax_scale == -INFINITY)
+    return KVQ_EINVAL;
+  if (c->n_tokens > 0 && !kvq::decode_supported(c->k_bits, c->v_bits, c->param_dtype))
+    return KVQ_EUNSUPPORTED;
+  if ((int64_t)c->batch * c->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+  const size_t need = kvq::decode_workspace_bytes(c->batch, c->n_kv_heads, G, c->max_tokens / 128);
+  if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return KVQ_EWORKSPACE;
+  if (c->n_tokens > 0) {
     // the plan of this call must fit the workspace (guaranteed by the bound
     // above; checked so a sizing mistake can never turn into stray writes)
     const kvq::DecodePlan plan = kvq::decode_plan(c->batch * c->n_kv_heads, G, c->k_bits, c->v_bits,
@@ -186,9 +200,42 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t n_q_heads,
     if (kvq::decode_workspace_needed(c->batch * c->n_kv_heads, G, plan) > workspace_bytes ||
         plan.n_chunks > kvq::KVQ_MAX_CHUNKS || plan.n_chunks * plan.tpc < c->n_tokens / 128)
       return KVQ_EWORKSPACE;
-    kvq::Geo g = make_geo(c);
-    hipError_t e = kvq::launch_decode(g, q, G, softmax_scale, out, workspace, stream);
-    return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
+  }
+  kvq::Geo g = make_geo(c);
+  hipError_t e = kvq::launch_decode(g, q, G, softmax_scale, out, workspace, res, res_dtype, stream);
+  return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
+}
+
+kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t n_q_heads,
+                           float softmax_scale, float* out, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  try {
+    kvq::ResArgs res{};
+    res.R = 0;
+    return decode_common(c, q, n_q_heads, softmax_scale, res, KVQ_F32, out, workspace,
+                         workspace_bytes, stream);
+  } catch (...) {
+    return KVQ_EHIP;
+  }
+}
+
+kvq_status kvq_decode_attn_residual(const kvq_cache* c, const void* q, int32_t n_q_heads,
+                                    float softmax_scale, const void* res_k, const void* res_v,
+                                    kvq_dtype res_dtype, const int64_t res_k_strides[3],
+                                    const int64_t res_v_strides[3], int32_t res_len, float* out,
+                                    void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  try {
+    if (res_len > 0 && (!res_k_strides || !res_v_strides)) return KVQ_EINVAL;
+    kvq::ResArgs res{};
+    res.k = res_k;
+    res.v = res_v;
+    res.R = res_len;
+    for (int i = 0; i < 3; i++) {
+      res.ks[i] = res_len > 0 ? res_k_strides[i] : 0;
+      res.vs[i] = res_len > 0 ? res_v_strides[i] : 0;
+    }
+    return decode_common(c, q, n_q_heads, softmax_scale, res, (int)res_dtype, out, workspace,
+                         workspace_bytes, stream);
   } catch (...) {
     return KVQ_EHIP;
   }

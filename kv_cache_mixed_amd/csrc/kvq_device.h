@@ -208,14 +208,25 @@ hipError_t launch_quantize(const Geo& g, const void* k, const void* v, int in_dt
                            const int64_t* ks, const int64_t* vs, int t0, int n_new,
                            hipStream_t st);
 hipError_t launch_shrink(const Geo& g, int to_bits, hipStream_t st);
-constexpr int KVQ_MAX_CHUNKS = 128;
+// partial slots per stream: up to KVQ_MAX_CHUNKS packed chunks, then one per
+// KVQ_RES_CHUNK residual tokens; the combine kernel takes at most 128
+constexpr int KVQ_RES_CHUNK = 32;
+constexpr int KVQ_MAX_RES_SLOTS = KVQ_MAX_RESIDUAL / KVQ_RES_CHUNK;
+constexpr int KVQ_MAX_CHUNKS = 128 - KVQ_MAX_RES_SLOTS;
 struct DecodePlan {
   int ns, n_groups, n_chunks, tpc;
 };
 DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_tiles);
 size_t decode_workspace_needed(int BH, int G, const DecodePlan& p);
 size_t decode_workspace_bytes(int B, int H, int G, int max_tiles);
-hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float* out,
-                         void* ws, hipStream_t st);
+// residual segment of a decode call (R = 0: none)
+struct ResArgs {
+  const void* k;
+  const void* v;
+  int64_t ks[3], vs[3];   // element strides of (batch, kv head, token); channel stride 1
+  int R;
+};
+hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float* out, void* ws,
+                         const ResArgs& res, int res_dtype, hipStream_t st);
 bool decode_supported(int k_bits, int v_bits, int pdt);
 }  // namespace kvq

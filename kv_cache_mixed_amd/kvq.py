@@ -21,6 +21,7 @@ PARAM_BYTES = {F32: 4, F16: 2, BF16: 2, E4M3: 1}
 KMIXED = 0
 MIXED_TILE_BYTES = 4352
 OK, EINVAL, EUNSUPPORTED, EBUDGET, EWORKSPACE, EHIP = range(6)
+MAX_RESIDUAL = 512          # KVQ_MAX_RESIDUAL of the header
 
 
 class KvqCacheStruct(ctypes.Structure):
@@ -48,8 +49,9 @@ class KvqError(RuntimeError):
 _lib = None
 
 EXPORTS = ["kvq_strerror", "kvq_tile_bytes", "kvq_cache_bytes", "kvq_quantize", "kvq_shrink",
-           "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_pool_create", "kvq_pool_destroy",
-           "kvq_pool_used_bytes", "kvq_pool_high_water", "kvq_append"]
+           "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_decode_attn_residual",
+           "kvq_pool_create", "kvq_pool_destroy", "kvq_pool_used_bytes", "kvq_pool_high_water",
+           "kvq_append"]
 
 
 def load():
@@ -76,6 +78,9 @@ def load():
     L.kvq_decode_workspace_bytes.argtypes = [P, i32]
     L.kvq_decode_attn.restype = ctypes.c_int
     L.kvq_decode_attn.argtypes = [P, vp, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+    L.kvq_decode_attn_residual.restype = ctypes.c_int
+    L.kvq_decode_attn_residual.argtypes = [P, vp, i32, ctypes.c_float, vp, vp, ctypes.c_int, vp, vp,
+                                           i32, vp, vp, ctypes.c_size_t, vp]
     L.kvq_pool_create.restype = ctypes.c_int
     L.kvq_pool_create.argtypes = [P, i64, vp, vp, ctypes.POINTER(vp)]
     L.kvq_pool_destroy.restype = None
@@ -258,17 +263,30 @@ class PackedCache:
             self._ws[n_q_heads] = torch.zeros(nb, dtype=torch.uint8, device=self.device)
         return self._ws[n_q_heads]
 
-    def decode_attn(self, q, softmax_scale, out=None, workspace=None, stream=None):
-        """q: [B][Hq][128] bfloat16 device tensor -> out [B][Hq][128] float32."""
+    def decode_attn(self, q, softmax_scale, out=None, workspace=None, stream=None, res_k=None,
+                    res_v=None):
+        """q: [B][Hq][128] bfloat16 device tensor -> out [B][Hq][128] float32.
+        res_k, res_v: optional residual segment [B][Hkv][R][128] (float32,
+        float16 or bfloat16, unit channel stride) attended with the packed
+        tokens."""
         import torch
         assert q.dtype == torch.bfloat16 and q.is_contiguous()
         Hq = q.shape[1]
         if out is None:
             out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
         ws = workspace if workspace is not None else self.workspace(Hq)
-        st = load().kvq_decode_attn(ctypes.byref(self.s), _ptr(q), Hq, float(softmax_scale),
-                                    _ptr(out), _ptr(ws), ws.numel(), _stream_ptr(stream))
-        _check(st, "kvq_decode_attn")
+        if res_k is None:
+            st = load().kvq_decode_attn(ctypes.byref(self.s), _ptr(q), Hq, float(softmax_scale),
+                                        _ptr(out), _ptr(ws), ws.numel(), _stream_ptr(stream))
+            _check(st, "kvq_decode_attn")
+            return out
+        assert res_v is not None and res_k.dtype == res_v.dtype and res_k.shape == res_v.shape
+        rdt = {torch.float32: F32, torch.float16: F16, torch.bfloat16: BF16}[res_k.dtype]
+        st = load().kvq_decode_attn_residual(ctypes.byref(self.s), _ptr(q), Hq, float(softmax_scale),
+                                             _ptr(res_k), _ptr(res_v), rdt, _strides3(res_k),
+                                             _strides3(res_v), res_k.shape[2], _ptr(out), _ptr(ws),
+                                             ws.numel(), _stream_ptr(stream))
+        _check(st, "kvq_decode_attn_residual")
         return out
 
     # -- host views for tests --------------------------------------------------

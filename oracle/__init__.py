@@ -316,6 +316,32 @@ def decode_attn(st: Stream, q_bf16: np.ndarray, scale: float) -> np.ndarray:
     return out
 
 
+def decode_attn_residual(st, q_bf16: np.ndarray, scale: float, res_k: np.ndarray,
+                         res_v: np.ndarray) -> np.ndarray:
+    """Attention of the G query heads over the packed stream's reconstructed
+    tokens followed by residual tokens kept at full precision (PM-KVQ page,
+    Training strategy and Related work: first / recent tokens not quantized).
+    Written as its plain definition in float64: dequantize, concatenate,
+    softmax(sigma * q K^T) V.  st may be None (no packed tokens).
+    res_k, res_v: [R, 128] real values (bfloat16 inputs are widened exactly by
+    the caller)."""
+    qf = decode(np.ascontiguousarray(q_bf16, dtype=np.uint16), BF16)
+    parts_k, parts_v = [], []
+    if st is not None and st.n_tok > 0:
+        parts_k.append(dequant_k(st))
+        parts_v.append(dequant_v(st))
+    parts_k.append(np.asarray(res_k, dtype=np.float64))
+    parts_v.append(np.asarray(res_v, dtype=np.float64))
+    K = np.concatenate(parts_k)
+    V = np.concatenate(parts_v)
+    sigma = float(np.float32(scale))
+    s = sigma * (qf @ K.T)                                           # [G, T]
+    s -= s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ V
+
+
 # --------------------------------------------------------------------------
 # schedule accounting
 # --------------------------------------------------------------------------

@@ -139,3 +139,45 @@ def test_append_budget_rejected_before_work():
     r = L.kvq_append(ctypes.byref(s), None, 1 << 40, 8, vp(FAKE), vp(FAKE), kvq.F32, st3, st3,
                      128, None, None)
     assert r == kvq.EINVAL
+
+
+def test_residual_validation_rejects_before_launch():
+    L = _lib()
+    m = re.search(r"#define KVQ_MAX_RESIDUAL (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == kvq.MAX_RESIDUAL
+    vp = ctypes.c_void_p
+    P = ctypes.byref
+    rs = (ctypes.c_int64 * 3)(2 * 40 * 128, 40 * 128, 128)
+    neg = (ctypes.c_int64 * 3)(2 * 40 * 128, -128, 128)
+    s = _fake_struct(2, 2, 1024, 4, 4)
+    s.n_tokens = 512
+    ws = L.kvq_decode_workspace_bytes(P(s), 8)
+    F = vp(FAKE)
+
+    def call(st, rk, rv, rdt, ks, vs, R, w=F, wb=ws):
+        return L.kvq_decode_attn_residual(P(st), F, 8, 0.088, rk, rv, rdt, ks, vs, R, F, w, wb, None)
+
+    assert call(s, F, F, kvq.F32, rs, rs, kvq.MAX_RESIDUAL + 1) == kvq.EINVAL
+    assert call(s, F, F, kvq.F32, rs, rs, -1) == kvq.EINVAL
+    assert call(s, None, F, kvq.F32, rs, rs, 5) == kvq.EINVAL
+    assert call(s, F, None, kvq.BF16, rs, rs, 5) == kvq.EINVAL
+    assert call(s, F, F, kvq.F32, None, rs, 5) == kvq.EINVAL
+    assert call(s, F, F, kvq.E4M3, rs, rs, 5) == kvq.EINVAL       # residual: f32, f16 or bf16
+    assert call(s, F, F, kvq.F32, rs, neg, 5) == kvq.EINVAL
+    odd = (ctypes.c_int64 * 3)(2 * 40 * 128, 40 * 128, 130)        # rows not 16-byte multiples
+    assert call(s, F, F, kvq.F32, odd, rs, 5) == kvq.EINVAL
+    assert call(s, F, F, kvq.BF16, rs, (ctypes.c_int64 * 3)(0, 0, 132), 5) == kvq.EINVAL
+    assert call(s, F, F, kvq.F32, (ctypes.c_int64 * 3)(0, 0, 132), rs, 5, None) == kvq.EWORKSPACE
+    assert call(s, vp(FAKE + 8), F, kvq.F32, rs, rs, 5) == kvq.EINVAL  # misaligned base
+    assert call(s, F, F, kvq.F32, rs, rs, 5, None) == kvq.EWORKSPACE
+    # empty cache: a residual segment alone is a valid request (reaches the
+    # workspace check); with no residual there is nothing to attend
+    e = _fake_struct(2, 2, 1024, 4, 4)
+    assert call(e, F, F, kvq.F32, rs, rs, 0) == kvq.EINVAL
+    assert call(e, F, F, kvq.F32, rs, rs, 3, None) == kvq.EWORKSPACE
+    # a width pair the packed decode does not build is only an error when
+    # the cache holds packed tokens
+    u = _fake_struct(2, 2, 1024, 4, 2)
+    assert call(u, F, F, kvq.F32, rs, rs, 3, None) == kvq.EWORKSPACE
+    u.n_tokens = 128
+    assert call(u, F, F, kvq.F32, rs, rs, 3, None) == kvq.EUNSUPPORTED

@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 from kv_cache_mixed_amd import kvq, synth
-from tests.gpu_helpers import (REL_TOL, SCALE, assert_stream_bytes_equal, oracle_attn,
+from tests.gpu_helpers import (PDT_ORACLE, REL_TOL, SCALE, assert_stream_bytes_equal, oracle_attn,
                                oracle_stream, q_to_dev, rel_err_rows, to_dev)
 
 torch = pytest.importorskip("torch")
@@ -256,3 +256,139 @@ def test_quantize_edge_groups(pdt):
         for h in range(2):
             st = oracle_stream(inp, 0, h, bits, bits, pdt)
             assert_stream_bytes_equal(cache, st, 0, h, "edge bits=%d pdt=%d" % (bits, pdt))
+
+
+# ---------------------------------------------------------------------------
+# decode with a residual segment of unquantized tokens
+# ---------------------------------------------------------------------------
+def _residual_case(B, H, Hq, T, R, bits, pdt, res_dtype, seed, mixed=False):
+    """Tokens [0, T) quantized into the cache, tokens [T, T+R) handed over as the
+    residual segment (float32 or bfloat16); every stream against the oracle."""
+    G = Hq // H
+    if mixed:
+        inp = synth.mixed_layer(B, H, Hq, T + R, seed)
+    else:
+        inp = synth.layer(B, H, Hq, T + R, seed)
+    sc = inp["slot_chan"] if mixed else None
+    cache = kvq.PackedCache(B, H, max(T, 128), kvq.KMIXED if mixed else bits, bits, pdt, slot_chan=sc)
+    if T:
+        cache.quantize(to_dev(inp["k"][:, :, :T], torch), to_dev(inp["v"][:, :, :T], torch), 0)
+    rk = to_dev(inp["k"][:, :, T:], torch).to(res_dtype)
+    rv = to_dev(inp["v"][:, :, T:], torch).to(res_dtype)
+    out = cache.decode_attn(q_to_dev(inp["q_bf16"], torch), SCALE, res_k=rk, res_v=rv).cpu().numpy()
+    assert np.all(np.isfinite(out))
+    rk_h, rv_h = rk.float().cpu().numpy(), rv.float().cpu().numpy()   # exact widening
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            st = None
+            if T:
+                st = oracle.quantize_stream(inp["k"][b, h, :T], inp["v"][b, h, :T],
+                                            0 if mixed else bits, bits, PDT_ORACLE[pdt],
+                                            None if sc is None else sc[h])
+            ref = oracle.decode_attn_residual(st, inp["q_bf16"][b, h * G:(h + 1) * G], SCALE,
+                                              rk_h[b, h], rv_h[b, h])
+            worst = max(worst, rel_err_rows(out[b, h * G:(h + 1) * G], ref).max())
+    assert worst <= REL_TOL, "max row relative error %.3e" % worst
+    return worst
+
+
+@pytest.mark.parametrize("T,R", [(128, 1), (1152, 77), (4096, 128), (384, 512), (0, 1), (0, 200),
+                                 (0, 512)])
+@pytest.mark.parametrize("res_dtype", ["f32", "f16", "bf16"])
+def test_decode_residual(T, R, res_dtype):
+    print("case decode residual T=%d R=%d %s" % (T, R, res_dtype), flush=True)
+    dt = {"f32": torch.float32, "f16": torch.float16, "bf16": torch.bfloat16}[res_dtype]
+    _residual_case(2, 2, 14, T, R, 4, kvq.F16, dt, seed=900 + T + R)
+
+
+@pytest.mark.parametrize("bits,G", [(2, 4), (8, 7), (16, 16), (1, 1)])
+def test_decode_residual_widths_and_groups(bits, G):
+    print("case decode residual bits=%d G=%d" % (bits, G), flush=True)
+    _residual_case(2, 2, 2 * G, 1024, 100, bits, kvq.E4M3 if bits == 2 else kvq.F16,
+                   torch.bfloat16, seed=950 + bits)
+
+
+def test_decode_residual_mixed_keys():
+    print("case decode residual mixed", flush=True)
+    _residual_case(1, 3, 12, 2048, 64, 2, kvq.E4M3, torch.float32, seed=960, mixed=True)
+
+
+def test_decode_residual_strided_views_and_garbage_workspace():
+    """Residual segment read through strided views of a larger ring buffer
+    (element strides of a [B][H][512][128] buffer, window starting at 40);
+    workspace filled with garbage; result equals the contiguous call."""
+    B, H, Hq, T, R = 2, 2, 8, 640, 90
+    inp = synth.layer(B, H, Hq, T + R, 961)
+    cache = kvq.PackedCache(B, H, 1024, 4, 4, kvq.F16)
+    cache.quantize(to_dev(inp["k"][:, :, :T], torch), to_dev(inp["v"][:, :, :T], torch), 0)
+    ring_k = torch.full((B, H, 512, 128), float("nan"), device="cuda")
+    ring_v = torch.full((B, H, 512, 128), float("nan"), device="cuda")
+    ring_k[:, :, 40:40 + R] = to_dev(inp["k"][:, :, T:], torch)
+    ring_v[:, :, 40:40 + R] = to_dev(inp["v"][:, :, T:], torch)
+    q = q_to_dev(inp["q_bf16"], torch)
+    ws = cache.workspace(Hq)
+    ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda"))
+    a = cache.decode_attn(q, SCALE, res_k=ring_k[:, :, 40:40 + R], res_v=ring_v[:, :, 40:40 + R])
+    b = cache.decode_attn(q, SCALE, res_k=ring_k[:, :, 40:40 + R].contiguous(),
+                          res_v=ring_v[:, :, 40:40 + R].contiguous())
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+    G = Hq // H
+    out = a.cpu().numpy()
+    for bb in range(B):
+        for h in range(H):
+            st = oracle.quantize_stream(inp["k"][bb, h, :T], inp["v"][bb, h, :T], 4, 4, oracle.F16)
+            ref = oracle.decode_attn_residual(st, inp["q_bf16"][bb, h * G:(h + 1) * G], SCALE,
+                                              inp["k"][bb, h, T:], inp["v"][bb, h, T:])
+            assert rel_err_rows(out[bb, h * G:(h + 1) * G], ref).max() <= REL_TOL
+
+
+def test_decode_streaming_with_residual():
+    """Decode as generation runs, with the first-token + recent-token window
+    ([PMKVQ] Training strategy): a bfloat16 window buffer per stream holds the
+    first token in row 0 for good and the most recent 1..128 tokens after it.
+    When a token arrives with 128 recent tokens already held, those 128 become
+    one packed group (kvq_append reads them straight from the window) and the
+    new token starts the next window.  Every step's output matches the oracle
+    over (packed tokens, window tokens)."""
+    B, H, Hq, N = 1, 2, 8, 3 * 128 + 46
+    G = Hq // H
+    inp = synth.layer(B, H, Hq, N, 962)
+    cache = kvq.PackedCache(B, H, 512, 4, 4, kvq.F16)
+    kd = to_dev(inp["k"], torch).to(torch.bfloat16)
+    vd = to_dev(inp["v"], torch).to(torch.bfloat16)
+    kf, vf = kd.float().cpu().numpy(), vd.float().cpu().numpy()
+    win_k = torch.zeros((B, H, 129, 128), dtype=torch.bfloat16, device="cuda")
+    win_v = torch.zeros_like(win_k)
+    q = q_to_dev(inp["q_bf16"], torch)
+    streams = [None] * H
+    first_recent = 1             # token index held in window row 1
+    for t in range(N):           # token t arrives
+        if t == 0:
+            win_k[:, :, 0] = kd[:, :, 0]
+            win_v[:, :, 0] = vd[:, :, 0]
+            n_win = 1
+        else:
+            if n_win == 129:     # 128 recent tokens held: pack them, restart the window
+                assert cache.append(win_k[:, :, 1:129], win_v[:, :, 1:129], budget_bytes=1 << 40,
+                                    floor_bits=4) == 0
+                first_recent += 128
+                n_win = 1
+                for h in range(H):
+                    streams[h] = oracle.quantize_stream(kf[0, h, 1:first_recent],
+                                                        vf[0, h, 1:first_recent], 4, 4, oracle.F16)
+            win_k[:, :, n_win] = kd[:, :, t]
+            win_v[:, :, n_win] = vd[:, :, t]
+            n_win += 1
+        assert cache.n_tokens == first_recent - 1
+        out = cache.decode_attn(q, SCALE, res_k=win_k[:, :, :n_win],
+                                res_v=win_v[:, :, :n_win]).cpu().numpy()
+        idx = np.r_[0, first_recent:t + 1]           # the window's tokens
+        for h in range(H):
+            ref = oracle.decode_attn_residual(streams[h], inp["q_bf16"][0, h * G:(h + 1) * G],
+                                              SCALE, kf[0, h, idx], vf[0, h, idx])
+            err = rel_err_rows(out[0, h * G:(h + 1) * G], ref).max()
+            assert err <= REL_TOL, "token %d (packed %d, window %d): %.3e" % (
+                t, cache.n_tokens, n_win, err)
+    assert cache.n_tokens == 384

@@ -455,6 +455,73 @@ def test_split_softmax_combine_equals_two_pass():
     assert np.allclose(num / den[:, None], ref, rtol=1e-12, atol=1e-13)
 
 
+def _first_tiles(st, n):
+    """the stream's first n tiles (n*128 tokens) as a stream of their own"""
+    return oracle.Stream(st.k_bits, st.v_bits, st.pdt, st.k_tiles[:n].copy(), st.ks[:n].copy(),
+                         st.kz[:n].copy(), st.v_tiles[:n].copy(), st.vs[:n * 128].copy(),
+                         st.vz[:n * 128].copy(), st.slot_chan)
+
+
+@pytest.mark.parametrize("mixed", [False, True])
+def test_residual_segment_of_reconstructed_tokens_equals_packed(mixed):
+    """A residual segment holding exactly the reconstructions of the last tile
+    gives the C oracle's attention over the whole packed stream (numpy float64
+    path against the C path)."""
+    st, rng = _stream(384, 21, mixed=mixed, pdt=oracle.E4M3 if mixed else oracle.F16)
+    q = _bf16(rng.standard_normal((4, 128)))
+    full = oracle.decode_attn(st, q, 0.09)
+    head = _first_tiles(st, 2)
+    res = oracle.decode_attn_residual(head, q, 0.09, oracle.dequant_k(st)[256:],
+                                      oracle.dequant_v(st)[256:])
+    assert np.allclose(res, full, rtol=1e-12, atol=1e-13)
+    # and the other way round: no packed tokens, every token residual
+    allres = oracle.decode_attn_residual(None, q, 0.09, oracle.dequant_k(st), oracle.dequant_v(st))
+    assert np.allclose(allres, full, rtol=1e-12, atol=1e-13)
+
+
+def test_residual_segment_special_cases():
+    rng = np.random.default_rng(22)
+    k = rng.standard_normal((37, 128))
+    v = rng.standard_normal((37, 128))
+    # q = 0: uniform weights -> the mean of the value rows
+    out0 = oracle.decode_attn_residual(None, _bf16(np.zeros((1, 128))), 0.1, k, v)
+    assert np.allclose(out0[0], v.mean(axis=0), atol=1e-13)
+    # a single residual token gets all the weight
+    one = oracle.decode_attn_residual(None, _bf16(rng.standard_normal((3, 128))), 0.1, k[:1], v[:1])
+    assert np.array_equal(one, np.repeat(v[:1], 3, axis=0))
+    # one dominant residual key overrides a whole packed stream
+    st, _ = _stream(256, 23)
+    kd = np.zeros((2, 128))
+    kd[1, 5] = 1000.0   # logit 1e7, far above any packed key (|k| < 10)
+    q = np.zeros((1, 128), np.float32)
+    q[0, 5] = 1.0
+    outd = oracle.decode_attn_residual(st, _bf16(q), 1e4, kd, v[:2])
+    assert np.allclose(outd[0], v[1], atol=1e-9)
+
+
+def test_residual_merge_identity():
+    """packed part and residual part combined through their (max, sum,
+    weighted sum) partials equal one softmax over both: the merge the decode
+    kernels use for the residual slot."""
+    st, rng = _stream(512, 24)
+    q = _bf16(rng.standard_normal((3, 128)))
+    rk = rng.standard_normal((77, 128))
+    rv = rng.standard_normal((77, 128))
+    ref = oracle.decode_attn_residual(st, q, 0.088, rk, rv)
+    qd = oracle.decode(q, oracle.BF16)
+    sig = float(np.float32(0.088))
+    parts = []
+    for K, V in ((oracle.dequant_k(st), oracle.dequant_v(st)), (rk, rv)):
+        s = sig * (qd @ K.T)
+        m = s.max(axis=1)
+        e = np.exp(s - m[:, None])
+        parts.append((m, e.sum(axis=1), e @ V))
+    M = np.maximum(parts[0][0], parts[1][0])
+    num = sum(np.exp(p[0] - M)[:, None] * p[2] for p in parts)
+    den = sum(np.exp(p[0] - M) * p[1] for p in parts)
+    assert np.allclose(num / den[:, None], ref, rtol=1e-12, atol=1e-13)
+
+
 # ---------------------------------------------------------------------------
 # shrink on a stream, schedule, sizes
 # ---------------------------------------------------------------------------
