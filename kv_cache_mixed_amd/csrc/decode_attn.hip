@@ -85,6 +85,10 @@
 #ifndef KVQ_DECODE_BRANCHLESS_RESCALE
 #define KVQ_DECODE_BRANCHLESS_RESCALE 0
 #endif
+// wave priority from the tiles a wave has left (1) or the default (0)
+#ifndef KVQ_DECODE_PRIO
+#define KVQ_DECODE_PRIO 1
+#endif
 // workgroups one decode launch aims at per wave-per-SIMD of the instance
 #ifndef KVQ_DECODE_WG_PER_OCC
 #define KVQ_DECODE_WG_PER_OCC 256
@@ -547,22 +551,41 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   } else {
     q0 = wave;
   }
-  if (q0 < t_count) load(b0, q0, 0);
-
   // ---- the query heads of the group in slot order, [column][slot] bf16 in
-  // LDS (column n = stream n / G, head n % G; zero for columns without a head)
+  // LDS (column n = stream n / G, head n % G; zero for columns without a
+  // head).  Column cn is query row grp * NS * G + cn of q (rows are
+  // (batch, kv head, head) in order), valid while cn < NS * G and the row is
+  // inside q.  The query loads go out before the first tile's loads, so they
+  // are not queued behind them when every workgroup starts at once.
+  if constexpr (!MIXED) {
+    // uniform widths: slot = channel, one 16-byte load per thread
+    const int cn = threadIdx.x >> 4, part = threadIdx.x & 15;
+    const int64_t row = (int64_t)grp * NS * G + cn;
+    u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+    if (cn < NS * G && row < (int64_t)BH * G) v = *(const u32x4*)(a.q + row * 128 + 8 * part);
+    if (q0 < t_count) load(b0, q0, 0);
+    *(u32x4*)&qs[cn][8 * part] = v;
+  } else {
+    // mixed widths: slot j holds channel slot_chan[kv head][j]
+    uint16_t qv[8];
 #pragma unroll
-  for (int i = threadIdx.x; i < 16 * 128; i += 256) {
-    const int cn = i >> 7, j = i & 127;
-    const int cs = cn / G, ch = cn - cs * G;
-    const int cbh = grp * NS + cs;
-    uint16_t v = 0;
-    if (cs < NS && cbh < BH) {
-      const int cb = cbh / g.H, chh = cbh % g.H;
-      const int chan = MIXED ? (int)g.slot_chan[chh * 128 + j] : j;
-      v = a.q[((int64_t)cb * (g.H * G) + (int64_t)chh * G + ch) * 128 + chan];
+    for (int r = 0; r < 8; r++) {
+      const int i = threadIdx.x + 256 * r;
+      const int cn = i >> 7, j = i & 127;
+      const int cs = cn / G;
+      const int cbh = grp * NS + cs;
+      qv[r] = 0;
+      if (cs < NS && cbh < BH) {
+        const int chh = cbh % g.H;
+        qv[r] = a.q[((int64_t)grp * NS * G + cn) * 128 + g.slot_chan[chh * 128 + j]];
+      }
     }
-    qs[cn][j] = v;
+    if (q0 < t_count) load(b0, q0, 0);
+#pragma unroll
+    for (int r = 0; r < 8; r++) {
+      const int i = threadIdx.x + 256 * r;
+      qs[i >> 7][i & 127] = qv[r];
+    }
   }
   __syncthreads();
   // the lane's 32 query values (slots kslot(0..31)) as bf16 pairs
@@ -830,6 +853,17 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   }
 #pragma unroll 1
   while (q0 < t_count) {
+    if constexpr (KVQ_DECODE_PRIO != 0) {
+      // The two workgroups sharing a CU have equal work, but the hardware
+      // issues the older wave first when both are ready, so the older one
+      // would finish early and leave its SIMDs half idle.  The wave with more
+      // tiles left runs at the higher priority instead.
+      const int rem = DYN ? 3 : (t_count - q0 + 3) / 4 - 1;
+      if (rem >= 3) __builtin_amdgcn_s_setprio(3);
+      else if (rem == 2) __builtin_amdgcn_s_setprio(2);
+      else if (rem == 1) __builtin_amdgcn_s_setprio(1);
+      else __builtin_amdgcn_s_setprio(0);
+    }
 #pragma unroll
     for (int u = 0; u < U; u++) {
       if constexpr (NSUB == 1) {
@@ -875,32 +909,48 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     }
   __syncthreads();
 
-  const int Hq = g.H * G;
   const int ncol = NS * G;
   const bool single = (a.n_slots == 1);
-  for (int idx = threadIdx.x; idx < ncol * 128; idx += 256) {
-    const int col = idx >> 7, c = idx & 127;
-    const int s = col / G, hh = col - s * G;
-    const int bh = grp * NS + s;
-    if (bh >= BH) continue;
+  // per column: the workgroup max M, the weight 2^(m_w - M) of each wave's
+  // partial, the sum and the destination row -- the output row
+  // (batch, query head) = grp * NS * G + col when this is the stream's only
+  // partial, else the partial row of this chunk (-1: no head in the column)
+  __shared__ float sh_cw[16][4];
+  __shared__ float sh_cd[16][2];
+  __shared__ int sh_row[16];
+  if (threadIdx.x < ncol) {
+    const int col = threadIdx.x;
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; w++) M = fmaxf(M, sh_ml[w][col][0]);
-    float num = 0.0f, den = 0.0f;
+    float den = 0.0f;
 #pragma unroll
     for (int w = 0; w < 4; w++) {
       const float mw = sh_ml[w][col][0];
       const float sc = (mw == -INFINITY) ? 0.0f : exp2f(mw - M);
-      num += sc * sh_o(w, col, c);
+      sh_cw[col][w] = sc;
       den += sc * sh_ml[w][col][1];
     }
-    const int bo = bh / g.H, ho = bh % g.H;
+    sh_cd[col][0] = M;
+    sh_cd[col][1] = den;
+    const int s = col / G, hh = col - s * G;
+    const int bh = grp * NS + s;
+    sh_row[col] = bh >= BH ? -1 : (single ? bh * G + hh : (bh * a.n_slots + chunk) * G + hh);
+  }
+  __syncthreads();
+  // four consecutive channels per thread
+  for (int idx = threadIdx.x; idx < ncol * 32; idx += 256) {
+    const int col = idx >> 5, c4 = (idx & 31) * 4;
+    const int row = sh_row[col];
+    if (row < 0) continue;
+    f32x4 num = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int w = 0; w < 4; w++) num += sh_cw[col][w] * *(const f32x4*)&sh_o(w, col, c4);
     if (single) {
-      a.out[((int64_t)bo * Hq + (int64_t)ho * G + hh) * 128 + c] = num / den;
+      *(f32x4*)(a.out + (int64_t)row * 128 + c4) = num / sh_cd[col][1];
     } else {
-      const int64_t row = ((int64_t)bh * a.n_slots + chunk) * G + hh;
-      if (c == 0) { a.part_ml[2 * row] = M; a.part_ml[2 * row + 1] = den; }
-      a.part_o[row * 128 + c] = num;
+      if (c4 == 0) { a.part_ml[2 * (int64_t)row] = sh_cd[col][0]; a.part_ml[2 * (int64_t)row + 1] = sh_cd[col][1]; }
+      *(f32x4*)(a.part_o + (int64_t)row * 128 + c4) = num;
     }
   }
 }
