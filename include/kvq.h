@@ -197,16 +197,25 @@ kvq_status kvq_shrink(kvq_cache *cache, int32_t to_bits, hipStream_t stream);
 
 /* Workspace bytes kvq_decode_attn needs for this cache geometry (sized for
  * max_tokens, so it stays valid as the cache grows).  0 on invalid input. */
+/* Leading workspace bytes that hold the decode completion counters, for a
+ * cache of n_streams = batch * n_kv_heads streams. */
+#define KVQ_DECODE_COUNTER_BYTES(n_streams) ((((size_t)(n_streams) * 4u) + 255u) / 256u * 256u)
 size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads);
 
 /* Decode attention of one query token per sequence over the n_tokens stored
  * tokens (see "Decode attention" above).  q: device bfloat16
  * [B][n_q_heads][128]; out: device float32 [B][n_q_heads][128]; n_q_heads a
  * multiple of n_kv_heads with 1 <= n_q_heads / n_kv_heads <= 16; n_tokens >= 128.
- * workspace: device buffer of at least kvq_decode_workspace_bytes() bytes
- * (per-chunk partials; no initial contents required).  When the tokens are
- * split over several chunks a second kernel on the same stream combines the
- * partials into out.  Concurrent calls must not share a workspace. */
+ * workspace: device buffer of at least kvq_decode_workspace_bytes() bytes,
+ * 256-byte aligned.  Its first KVQ_DECODE_COUNTER_BYTES(batch * n_kv_heads)
+ * bytes are completion counters that must be zero before the first call (a
+ * zero-filled allocation); every call that returns KVQ_OK leaves them zero
+ * (after any other status, zero them again).  The rest holds per-chunk
+ * partials and needs no initial contents.  When the tokens are split over
+ * several chunks, the partials are combined into out by a second kernel on
+ * the same stream or, for streams cut into many chunks, inside the same
+ * kernel by the workgroup that finishes the last chunk of a group of streams.
+ * Concurrent calls must not share a workspace. */
 kvq_status kvq_decode_attn(const kvq_cache *cache, const void *q, int32_t n_q_heads,
                            float softmax_scale, float *out, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);

@@ -89,6 +89,19 @@
 #ifndef KVQ_DECODE_PRIO
 #define KVQ_DECODE_PRIO 1
 #endif
+// streams split into at least this many chunks are combined inside the decode
+// kernel by the workgroup that finishes the last chunk of a stream group;
+// fewer chunks are combined by a second kernel.  Measured: a second kernel is
+// cheaper at the 16-32 chunks of batched layers, where the write-through wait
+// at the end of every workgroup costs more than the launch; the in-kernel
+// combine wins for the 64 chunks of single-sequence long contexts.
+#ifndef KVQ_DECODE_FUSED_MIN_CHUNKS
+#define KVQ_DECODE_FUSED_MIN_CHUNKS 48
+#endif
+// grid x = stream group, y = chunk (1) or x = chunk, y = stream group (0)
+#ifndef KVQ_DECODE_GRID_SWAP
+#define KVQ_DECODE_GRID_SWAP 0
+#endif
 // workgroups one decode launch aims at per wave-per-SIMD of the instance
 #ifndef KVQ_DECODE_WG_PER_OCC
 #define KVQ_DECODE_WG_PER_OCC 256
@@ -211,6 +224,9 @@ struct DecodeArgs {
   float* part_o;      // [BH][n_slots][G][128] (unnormalised output)
   int G, n_chunks, tpc, n_groups;
   int n_slots;        // partial slots per stream: n_chunks + residual slots
+  unsigned* counters; // [n_groups] finished chunks per stream group: zero on
+                      // entry, left zero (chunk combine inside the kernel)
+  int fused;          // chunks combined inside the kernel (1) or by a second kernel (0)
   float sl2;          // softmax_scale * log2(e)
 };
 
@@ -232,6 +248,11 @@ __device__ __forceinline__ void split_pack(float xl, float xh, uint32_t& hi, uin
   const float rl = xl - u2f(f2u(xl) & 0xffffe000u);
   const float rh = xh - u2f(f2u(xh) & 0xffffe000u);
   lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(rl, rh));
+}
+
+// device-scope store (written through the XCD's L2)
+__device__ __forceinline__ void st_dev(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // buffer resource over [base, base + bytes): raw buffer loads take a 32-bit
@@ -385,7 +406,10 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // the wave index is uniform: keep it (and everything derived) in SGPRs
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, lg = lane >> 4;
-  const int grp = blockIdx.y, chunk = blockIdx.x;
+  // consecutive workgroup ids (which the dispatcher deals out to the XCDs in
+  // turn) walk the stream groups (1) or the chunks of one group (0)
+  const int grp = KVQ_DECODE_GRID_SWAP ? blockIdx.x : blockIdx.y;
+  const int chunk = KVQ_DECODE_GRID_SWAP ? blockIdx.y : blockIdx.x;
   const int G = a.G;
   const int BH = g.B * g.H;
   const int own = n / G, hn = n - (n / G) * G;
@@ -918,6 +942,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   __shared__ float sh_cw[16][4];
   __shared__ float sh_cd[16][2];
   __shared__ int sh_row[16];
+  __shared__ int sh_orow[16];
   if (threadIdx.x < ncol) {
     const int col = threadIdx.x;
     float M = -INFINITY;
@@ -936,6 +961,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     const int s = col / G, hh = col - s * G;
     const int bh = grp * NS + s;
     sh_row[col] = bh >= BH ? -1 : (single ? bh * G + hh : (bh * a.n_slots + chunk) * G + hh);
+    sh_orow[col] = bh * G + hh;
   }
   __syncthreads();
   // four consecutive channels per thread
@@ -949,9 +975,100 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     if (single) {
       *(f32x4*)(a.out + (int64_t)row * 128 + c4) = num / sh_cd[col][1];
     } else {
-      if (c4 == 0) { a.part_ml[2 * (int64_t)row] = sh_cd[col][0]; a.part_ml[2 * (int64_t)row + 1] = sh_cd[col][1]; }
-      *(f32x4*)(a.part_o + (int64_t)row * 128 + c4) = num;
+      if (a.fused) {
+        // device-scope stores: they pass the XCD's own L2, so the workgroup
+        // that combines (on any XCD) reads them without a cache write-back
+        if (c4 == 0) {
+          st_dev(a.part_ml + 2 * (int64_t)row, sh_cd[col][0]);
+          st_dev(a.part_ml + 2 * (int64_t)row + 1, sh_cd[col][1]);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; k++) st_dev(a.part_o + (int64_t)row * 128 + c4 + k, num[k]);
+      } else {
+        if (c4 == 0) { a.part_ml[2 * (int64_t)row] = sh_cd[col][0]; a.part_ml[2 * (int64_t)row + 1] = sh_cd[col][1]; }
+        *(f32x4*)(a.part_o + (int64_t)row * 128 + c4) = num;
+      }
     }
+  }
+  if (a.fused) {
+    if (single) return;
+    // ---- chunk combine by the workgroup that completes the stream group:
+    // once this workgroup's partial stores are complete it counts itself in
+    // the group's counter; the one that brings the count to n_chunks reads
+    // every partial slot of the group's streams back (the chunks and any
+    // residual slots), writes o = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k
+    // and resets the counter for the next call.
+    __builtin_amdgcn_s_waitcnt(0);
+    __syncthreads();
+    __shared__ int s_last;
+    if (threadIdx.x == 0)
+      s_last = __hip_atomic_fetch_add(a.counters + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (unsigned)(a.n_chunks - 1);
+    __syncthreads();
+    if (!s_last) return;
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+    const int ns = a.n_slots;
+    constexpr int KR = 16;   // slots whose outputs are loaded before the weights are known
+    // items: four consecutive channels of one column, two per thread
+    f32x4 ov[2][KR];
+    int icol[2], ic4[2], irow[2];
+#pragma unroll
+    for (int it = 0; it < 2; it++) {
+      const int idx = threadIdx.x + 256 * it;
+      icol[it] = min(idx >> 5, 15);
+      ic4[it] = (idx & 31) * 4;
+      irow[it] = idx < ncol * 32 ? sh_row[icol[it]] : -1;
+      // partial row of slot k = irow + (k - chunk) * G
+      const int64_t r0 = (int64_t)irow[it] - (int64_t)chunk * G;
+#pragma unroll
+      for (int k = 0; k < KR; k++) {
+        ov[it][k] = (f32x4){0.f, 0.f, 0.f, 0.f};
+        if (irow[it] >= 0 && k < ns) ov[it][k] = *(const f32x4*)(a.part_o + (r0 + (int64_t)k * G) * 128 + ic4[it]);
+      }
+    }
+    // (m, l) of every (column, slot), then the weights, in the free LDS
+    float* sml = (float*)&lds[0][0];                 // [16][ns][2]
+    float* sden = sml + 16 * 2 * KVQ_MAX_SLOTS;      // [16]
+    for (int i = threadIdx.x; i < ncol * ns; i += 256) {
+      const int col = i / ns, k = i - (i / ns) * ns;
+      float m = -INFINITY, l = 0.0f;
+      if (sh_row[col] >= 0) {
+        const int64_t r = (int64_t)sh_row[col] + (int64_t)(k - chunk) * G;
+        m = a.part_ml[2 * r];
+        l = a.part_ml[2 * r + 1];
+      }
+      sml[2 * (col * ns + k)] = m;
+      sml[2 * (col * ns + k) + 1] = l;
+    }
+    __syncthreads();
+    if (threadIdx.x < ncol) {
+      const int col = threadIdx.x;
+      float M = -INFINITY;
+      for (int k = 0; k < ns; k++) M = fmaxf(M, sml[2 * (col * ns + k)]);
+      float den = 0.0f;
+      for (int k = 0; k < ns; k++) {
+        const float mk = sml[2 * (col * ns + k)];
+        const float w = (mk == -INFINITY) ? 0.0f : exp2f(mk - M);
+        den += w * sml[2 * (col * ns + k) + 1];
+        sml[2 * (col * ns + k)] = w;
+      }
+      sden[col] = den;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < 2; it++) {
+      if (irow[it] < 0) continue;
+      const int col = icol[it];
+      const float* wk = sml + 2 * col * ns;
+      f32x4 num = (f32x4){0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < KR; k++)
+        if (k < ns) num += wk[2 * k] * ov[it][k];
+      const int64_t r0 = (int64_t)irow[it] - (int64_t)chunk * G;
+      for (int k = KR; k < ns; k++) num += wk[2 * k] * *(const f32x4*)(a.part_o + (r0 + (int64_t)k * G) * 128 + ic4[it]);
+      *(f32x4*)(a.out + (int64_t)sh_orow[col] * 128 + ic4[it]) = num / sden[col];
+    }
+    if (threadIdx.x == 0) __hip_atomic_store(a.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1188,11 +1305,14 @@ __global__ __launch_bounds__(256) void decode_residual_kernel(ResArgs r, const u
 static size_t ml_bytes(int BH, int n_chunks, int G) {
   return ((size_t)BH * n_chunks * G * 2 * 4 + 255) / 256 * 256;
 }
+// per-stream-group counters of the in-kernel combine, at the start of the
+// workspace (at most one group per stream)
+static size_t cnt_bytes(int BH) { return ((size_t)BH * 4 + 255) / 256 * 256; }
 
 // partial slots: every chunk plus the most a residual segment can add
 size_t decode_workspace_needed(int BH, int G, const DecodePlan& p) {
   const int slots = p.n_chunks + KVQ_MAX_RES_SLOTS;
-  return ml_bytes(BH, slots, G) + (size_t)BH * slots * G * 128 * 4;
+  return cnt_bytes(BH) + ml_bytes(BH, slots, G) + (size_t)BH * slots * G * 128 * 4;
 }
 
 size_t decode_workspace_bytes(int B, int H, int G, int max_tiles) {
@@ -1221,7 +1341,9 @@ static hipError_t launch_ns(const DecodeArgs& a0, hipStream_t st) {
   a.n_chunks = p.n_chunks;
   a.tpc = p.tpc;
   a.n_slots = p.n_chunks + a.n_slots;   // residual slots on entry
-  const dim3 grid(a.n_chunks, a.n_groups), block(256);
+  a.fused = a.n_slots > 1 && p.n_chunks >= KVQ_DECODE_FUSED_MIN_CHUNKS;
+  const dim3 grid(KVQ_DECODE_GRID_SWAP ? a.n_groups : a.n_chunks, KVQ_DECODE_GRID_SWAP ? a.n_chunks : a.n_groups),
+      block(256);
   if (p.ns == 1) {
     hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 1>), grid, block, 0, st, a);
   } else if (p.ns == 2) {
@@ -1277,8 +1399,9 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
   p.n_chunks = 0;
   if (has_packed) p = decode_plan(BH, G, g.k_bits, g.v_bits, g.pdt, g.n_tiles);
   const int n_slots = p.n_chunks + n_res;
-  float* part_ml = (float*)ws;
-  float* part_o = (float*)((uint8_t*)ws + ml_bytes(BH, n_slots, G));
+  unsigned* counters = (unsigned*)ws;
+  float* part_ml = (float*)((uint8_t*)ws + cnt_bytes(BH));
+  float* part_o = (float*)((uint8_t*)part_ml + ml_bytes(BH, n_slots, G));
   hipError_t e = hipSuccess;
   if (n_res > 0) {
     e = launch_residual(res, res_dtype, dim3(n_res, BH), q, g.H, G, sl2, part_ml, part_o, n_slots,
@@ -1296,6 +1419,8 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
     a.sl2 = sl2;
     a.n_chunks = a.tpc = a.n_groups = 0;
     a.n_slots = n_res;
+    a.counters = counters;
+    a.fused = 0;   // set by the launch from the plan
     switch (g.pdt) {
       case KVQ_F32: e = launch_decode_pdt<KVQ_F32>(a, st); break;
       case KVQ_F16: e = launch_decode_pdt<KVQ_F16>(a, st); break;
@@ -1305,7 +1430,7 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
     }
     if (e != hipSuccess) return e;
   }
-  if (n_slots > 1) {
+  if (n_slots > 1 && (!has_packed || p.n_chunks < KVQ_DECODE_FUSED_MIN_CHUNKS)) {
     const int rows = BH * G;
     hipLaunchKernelGGL(decode_combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, (const float*)part_ml,
                        (const float*)part_o, out, BH, g.H, G, n_slots);

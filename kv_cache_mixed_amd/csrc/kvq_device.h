@@ -213,6 +213,7 @@ hipError_t launch_shrink(const Geo& g, int to_bits, hipStream_t st);
 constexpr int KVQ_RES_CHUNK = 32;
 constexpr int KVQ_MAX_RES_SLOTS = KVQ_MAX_RESIDUAL / KVQ_RES_CHUNK;
 constexpr int KVQ_MAX_CHUNKS = 128 - KVQ_MAX_RES_SLOTS;
+constexpr int KVQ_MAX_SLOTS = KVQ_MAX_CHUNKS + KVQ_MAX_RES_SLOTS;
 struct DecodePlan {
   int ns, n_groups, n_chunks, tpc;
 };

@@ -181,3 +181,20 @@ def test_residual_validation_rejects_before_launch():
     assert call(u, F, F, kvq.F32, rs, rs, 3, None) == kvq.EWORKSPACE
     u.n_tokens = 128
     assert call(u, F, F, kvq.F32, rs, rs, 3, None) == kvq.EUNSUPPORTED
+
+
+def test_decode_counter_bytes_formula():
+    """The binding's leading counter-region size agrees with the header's
+    KVQ_DECODE_COUNTER_BYTES (4 bytes per stream, rounded up to 256) and fits
+    inside the workspace."""
+    L = _lib()
+    m = re.search(r"#define KVQ_DECODE_COUNTER_BYTES\(n_streams\) (.+)", open(HEADER).read())
+    assert m
+    body = m.group(1).replace("(size_t)", "").replace("u", "").replace("/", "//")
+    for B, H in [(1, 1), (16, 4), (1, 8), (64, 4), (3, 5)]:
+        s = _fake_struct(B, H, 4096, 4, 4)
+        c = kvq.PackedCache.__new__(kvq.PackedCache)
+        c.s = s
+        want = eval(body.replace("n_streams", str(B * H)))
+        assert c.workspace_counter_bytes() == want and want % 256 == 0 and want >= 4 * B * H
+        assert L.kvq_decode_workspace_bytes(ctypes.byref(s), 8 * H) > want

@@ -149,18 +149,24 @@ def test_decode_other_param_dtypes(pdt):
 
 
 def test_decode_repeat_and_workspace_reuse():
-    """Repeated calls give identical output, and the workspace needs no initial
-    contents: a workspace filled with garbage (NaN bit patterns included) gives
-    the same bits."""
+    """Repeated calls give identical output; past the zeroed completion
+    counters the workspace needs no initial contents (garbage, NaN bit
+    patterns included, gives the same bits), and every call leaves the
+    counters zero."""
     inp, cache = _quantized(2, 2, 8, 4096, 4, 4, kvq.F16, seed=95)
     q = q_to_dev(inp["q_bf16"], torch)
     o1 = cache.decode_attn(q, SCALE).cpu().numpy()
     o2 = cache.decode_attn(q, SCALE).cpu().numpy()
     ws = cache.workspace(8)
+    nc = cache.workspace_counter_bytes()
+    assert bool((ws[:nc] == 0).all()), "counters not left zero"
     ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, generator=torch.Generator().manual_seed(7)))
-    ws[:64].fill_(0xff)
+    ws[nc:nc + 64].fill_(0xff)
+    ws[:nc].zero_()
     o3 = cache.decode_attn(q, SCALE, workspace=ws).cpu().numpy()
-    assert np.array_equal(o1, o2) and np.array_equal(o2, o3)
+    o4 = cache.decode_attn(q, SCALE, workspace=ws).cpu().numpy()
+    assert bool((ws[:nc] == 0).all()), "counters not left zero"
+    assert np.array_equal(o1, o2) and np.array_equal(o2, o3) and np.array_equal(o3, o4)
 
 
 def test_tiny_config():
@@ -226,6 +232,7 @@ def test_workspace_and_output_guard_bytes(B, H, Hq, T):
         cache.decode_attn(q, SCALE, out=out, workspace=ws_full[:nb])
     torch.cuda.synchronize()
     assert bool((ws_full[nb:] == 0xA5).all()), "workspace overrun"
+    assert bool((ws_full[:cache.workspace_counter_bytes()] == 0).all()), "counters not left zero"
     assert bool((out_full[B * Hq * 128:] == 7.0).all()), "output overrun"
     assert bool(torch.isfinite(out).all())
 
@@ -329,6 +336,7 @@ def test_decode_residual_strided_views_and_garbage_workspace():
     q = q_to_dev(inp["q_bf16"], torch)
     ws = cache.workspace(Hq)
     ws.copy_(torch.randint(0, 256, ws.shape, dtype=torch.uint8, device="cuda"))
+    ws[:cache.workspace_counter_bytes()].zero_()
     a = cache.decode_attn(q, SCALE, res_k=ring_k[:, :, 40:40 + R], res_v=ring_v[:, :, 40:40 + R])
     b = cache.decode_attn(q, SCALE, res_k=ring_k[:, :, 40:40 + R].contiguous(),
                           res_v=ring_v[:, :, 40:40 + R].contiguous())
@@ -392,3 +400,30 @@ def test_decode_streaming_with_residual():
             assert err <= REL_TOL, "token %d (packed %d, window %d): %.3e" % (
                 t, cache.n_tokens, n_win, err)
     assert cache.n_tokens == 384
+
+
+@pytest.mark.parametrize("B,H,Hq,T,bits,R", [(1, 1, 7, 32768, 4, 0), (2, 2, 8, 32768, 2, 100),
+                                              (1, 2, 8, 24576, 8, 0)])
+def test_decode_in_kernel_combine(B, H, Hq, T, bits, R):
+    """Few streams over many tokens: the plan cuts each stream into 48 or more
+    chunks, which the workgroup finishing a stream group's last chunk combines
+    inside the decode kernel (with residual slots when R > 0).  Against the
+    oracle; repeated calls give identical bits and leave the counters zero."""
+    print("case in-kernel combine B=%d H=%d Hq=%d T=%d bits=%d R=%d" % (B, H, Hq, T, bits, R), flush=True)
+    if R:
+        _residual_case(B, H, Hq, T, R, bits, kvq.F16, torch.bfloat16, seed=970 + T % 97)
+        return
+    inp, cache = _quantized(B, H, Hq, T, bits, bits, kvq.F16, seed=971 + bits)
+    q = q_to_dev(inp["q_bf16"], torch)
+    o1 = cache.decode_attn(q, SCALE)
+    o2 = cache.decode_attn(q, SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2)
+    ws = cache.workspace(Hq)
+    assert bool((ws[:cache.workspace_counter_bytes()] == 0).all()), "counters not left zero"
+    out = o1.cpu().numpy()
+    G = Hq // H
+    for b in range(B):
+        for h in range(H):
+            ref = oracle_attn(oracle_stream(inp, b, h, bits, bits, kvq.F16), inp["q_bf16"][b, h * G:(h + 1) * G])
+            assert rel_err_rows(out[b, h * G:(h + 1) * G], ref).max() <= REL_TOL
