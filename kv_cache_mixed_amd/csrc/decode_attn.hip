@@ -247,16 +247,51 @@ struct UInfo {
 };
 
 // f16 split of a pair: hi = f16 truncation of x (one v_cvt_pkrtz for both),
-// lo = f16 of the exact binary32 residual x - hi.  In the f16 normal range the
-// truncated value is x with its 13 low significand bits cleared, so the
-// residual is formed without converting hi back; values below the f16 normal
-// range (at least 2^-28 of the largest operand, see the headroom exponents)
-// only lose an error of that relative size.
+// lo = f16 of the binary32 residual x - hi, which is exact (hi is x with low
+// significand bits cleared); the residual reads hi's halves directly
+// (v_fma_mix_f32), so the pair costs two conversions and two mixed fmas.
 __device__ __forceinline__ void split_pack(float xl, float xh, uint32_t& hi, uint32_t& lo) {
-  hi = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(xl, xh));
-  const float rl = xl - u2f(f2u(xl) & 0xffffe000u);
-  const float rh = xh - u2f(f2u(xh) & 0xffffe000u);
+  const auto h = __builtin_amdgcn_cvt_pkrtz(xl, xh);
+  hi = __builtin_bit_cast(uint32_t, h);
+  const float rl = __builtin_fmaf((float)h[0], -1.0f, xl);
+  const float rh = __builtin_fmaf((float)h[1], -1.0f, xh);
   lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(rl, rh));
+}
+
+// binary16 half i of a raw word array, widened exactly
+__device__ __forceinline__ float half_at(const uint32_t* w, int i) {
+  return (float)__builtin_bit_cast(_Float16, (uint16_t)((w[i >> 1] >> (16 * (i & 1))) & 0xffffu));
+}
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+// larger of each 16-bit half (v_pk_max_u16)
+__device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+
+// Value field weights.  Token i of a sub-tile (lane-local index) has its codes
+// in field F of ufield<VB>, whose MFMA operand carries code * 2^(pos - 24);
+// the probability operand carries 2^W(i), W = wexp - pos, to make up for it.
+// 16-bit codes span two fields (low byte W = 0, high byte W = 8): W(i) is the
+// first one's.
+template <int VB, int FVS>
+__host__ __device__ constexpr int tok_w(int i) {
+  for (int ff = 0; ff < FVS; ff++) {
+    const Fld F = ufield<VB>(ff);
+    if (F.lo == i || F.hi == i) return F.wexp - F.pos;
+  }
+  return 0;
+}
+// class of a field weight (W is 0, -1 .. -9, or 8 for the high byte of 16-bit
+// codes) and the weight of a class
+__host__ __device__ constexpr int w_class(int w) { return w > 0 ? 1 : -w; }
+template <int VB>
+__host__ __device__ constexpr int class_w(int k) { return (VB == 16 && k == 1) ? 8 : -k; }
+template <int VB, int FVS, int TPS>
+__host__ __device__ constexpr bool class_used(int k) {
+  for (int i = 0; i < TPS; i++)
+    if (w_class(tok_w<VB, FVS>(i)) == k) return true;
+  return false;
 }
 
 // device-scope store (written through the XCD's L2)
@@ -398,6 +433,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   constexpr int TAU = 8;                             // lazy-max slack (log2 units)
   constexpr int KH = (KB == 16) ? 4 : 12;
   constexpr int VH = (VB == 16) ? -2 : 6;
+  // largest probability shift: e * 2^ps * 2^W stays below 2^(TAU + PSMAX + 8)
+  // and its sums over a chunk below 2^127
+  constexpr int PSMAX = 96;
   constexpr int ROW_K = MIXED ? 8 : 16 * KB;
   constexpr int LDS_WAVE = NFK * 2 * 64;             // u32 words of folded query per wave
   constexpr bool SACC = (KVQ_DECODE_SACC != 0) && NS > 1;
@@ -762,7 +800,11 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
         for (int jj = 0; jj < JB; jj++) acc[s][jj] = mfma(av[s][jj], bl4, acc[s][jj]);
     }
     if constexpr (PF2) load_k(bf, ti2, sub2);
-    float lgt[JB][4];
+    // ---- logits l = ak * v + bk0 (v the column's own raw sum) and an online
+    // softmax with a lazy running max: the reference m_run only moves when a
+    // logit exceeds it by more than TAU (so e <= 2^TAU), and the accumulator
+    // is rescaled only when some column's reference moved
+    float lv[TPS];
 #pragma unroll
     for (int jj = 0; jj < JB; jj++) {
       f32x4 v = acc[0][jj];
@@ -770,44 +812,80 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       for (int s = 1; s < NS; s++)
         if (own == s) v = acc[s][jj];
 #pragma unroll
-      for (int i = 0; i < 4; i++) lgt[jj][i] = fmaf(ak, v[i], bk0);
+      for (int i = 0; i < 4; i++) lv[4 * jj + i] = v[i];
     }
-
-    // ---- online softmax with a lazy running max: the reference max m_run
-    // only moves when a logit exceeds it by more than TAU (so e <= 2^TAU), and
-    // the accumulator is rescaled only when some column's reference moved
-    float vs[TPS], vz[TPS];
-    praw_unpack<PDT, TPS>(bf.vs, vs);
-    praw_unpack<PDT, TPS>(bf.vz, vz);
+    // the largest logit comes from the largest raw sum when ak >= 0 (ak has
+    // the sign of the softmax scale) and from the smallest otherwise; fma is
+    // monotone in v
+    float vx = lv[0];
+    if (a.sl2 >= 0.0f) {
+#pragma unroll
+      for (int i = 1; i < TPS; i++) vx = fmaxf(vx, lv[i]);
+    } else {
+#pragma unroll
+      for (int i = 1; i < TPS; i++) vx = fminf(vx, lv[i]);
+    }
+    const float tmax = wave_max16x4(fmaf(ak, vx, bk0));
+    // value parameters of the sub-tile; binary16 ones stay raw and are read
+    // by mixed-precision fmas
+    constexpr bool MIX = (PDT == KVQ_F16);
+    uint32_t rvs[PWV], rvz[PWV];
+    float vs[MIX ? 1 : TPS], vz[MIX ? 1 : TPS];
+    int ev;
+    if constexpr (MIX) {
+#pragma unroll
+      for (int w = 0; w < PWV; w++) { rvs[w] = bf.vs[w]; rvz[w] = bf.vz[w]; }
+      // scales are >= +0, so their binary16 patterns order like the values
+      uint32_t m2 = rvs[0];
+#pragma unroll
+      for (int w = 1; w < PWV; w++) m2 = pk_max_u16(m2, rvs[w]);
+      const uint32_t mh = wave_maxu16x4(max(m2 & 0xffffu, m2 >> 16));
+      ev = expo((float)__builtin_bit_cast(_Float16, (uint16_t)mh));
+    } else {
+      praw_unpack<PDT, TPS>(bf.vs, vs);
+      praw_unpack<PDT, TPS>(bf.vz, vz);
+      uint32_t vsmax = 0;
+#pragma unroll
+      for (int i = 0; i < TPS; i++) vsmax = max(vsmax, f2u(vs[i]));   // scales are >= +0
+      ev = expo(u2f(wave_maxu16x4(vsmax)));
+    }
     if constexpr (PF2) load_p(bf, ti2, sub2);
-    float tmax = -INFINITY;
-    uint32_t vsmax = 0;
-#pragma unroll
-    for (int jj = 0; jj < JB; jj++)
-#pragma unroll
-      for (int i = 0; i < 4; i++) tmax = fmaxf(tmax, lgt[jj][i]);
-#pragma unroll
-    for (int i = 0; i < TPS; i++) vsmax = max(vsmax, f2u(vs[i]));   // scales are >= +0
-    tmax = wave_max16x4(tmax);
-    const int ev = expo(u2f(wave_maxu16x4(vsmax)));
     const float m_new = (tmax > m_run + (float)TAU) ? tmax : m_run;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // v_exp_f32, 0 for -inf
     const int e_new = max(e_run, ev);
-    const float rescale = alpha * exp2i(e_run - e_new);
+    // the probabilities carry 2^ps, ps = VH - e_new (capped so the scaled
+    // sums stay finite), which keeps the value operand below 2^15
+    const int ps_old = min(VH - e_run, PSMAX), ps_new = min(VH - e_new, PSMAX);
+    const float rescale = alpha * exp2i(ps_new - ps_old);
     m_run = m_new;
     e_run = e_new;
-    const float pf = exp2i(VH - e_new);
+    // e''(i) = e(i) * 2^ps * 2^W(i) straight from the exponent; the running
+    // sums l_run, z_run are kept in units of 2^ps
+    const float c0 = bk0 - m_new + (float)ps_new;
     float p[TPS];
-    float lsum = 0.0f, zsum = 0.0f;
+    float lsum = 0.0f;
+    float zc[10];
+#pragma unroll
+    for (int k = 0; k < 10; k++) zc[k] = 0.0f;
 #pragma unroll
     for (int i = 0; i < TPS; i++) {
-      const float e = __builtin_amdgcn_exp2f(lgt[i >> 2][i & 3] - m_new);
-      lsum += e;
-      zsum = fmaf(e, vz[i], zsum);
-      p[i] = e * (vs[i] * pf);
+      const int W = tok_w<VB, FVS>(i);
+      const float e = __builtin_amdgcn_exp2f(fmaf(ak, lv[i], c0 + (float)W));
+      lsum = fmaf(e, exp2i(-W), lsum);
+      if constexpr (MIX) {
+        zc[w_class(W)] = fmaf(e, half_at(rvz, i), zc[w_class(W)]);
+        p[i] = fmaf(e, half_at(rvs, i), 0.0f);
+      } else {
+        zc[w_class(W)] = fmaf(e, vz[i], zc[w_class(W)]);
+        p[i] = e * vs[i];
+      }
     }
-    l_run = fmaf(l_run, alpha, lsum);
-    z_run = fmaf(z_run, alpha, zsum);
+    float zsum = zc[0];
+#pragma unroll
+    for (int k = 1; k < 10; k++)
+      if (class_used<VB, FVS, TPS>(k)) zsum = fmaf(zc[k], exp2i(-class_w<VB>(k)), zsum);
+    l_run = fmaf(l_run, rescale, lsum);
+    z_run = fmaf(z_run, rescale, zsum);
 #if KVQ_DECODE_BRANCHLESS_RESCALE
 #pragma unroll
     for (int s = 0; s < NA; s++)
@@ -822,15 +900,16 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     }
 #endif
 
-    // ---- P operand (split hi/lo) and PV
+    // ---- P operand (split hi/lo) and PV; every sub-tile has the field
+    // layout of sub-tile 0, shifted by WVS words and TPS tokens
     uint32_t bvh[FVS], bvl[FVS];
 #pragma unroll
     for (int ff = 0; ff < FVS; ff++) {
-      // every sub-tile has the field layout of sub-tile 0, shifted by WVS
-      // words and TPS tokens
+      // a token whose codes span two fields (the bytes of a 16-bit code)
+      // carries the weight of its first field; the other gets the difference
       const Fld F = ufield<VB>(ff);
-      const float w = exp2i(F.wexp - F.pos);
-      split_pack(p[F.lo] * w, p[F.hi] * w, bvh[ff], bvl[ff]);
+      const float dw = exp2i((F.wexp - F.pos) - tok_w<VB, FVS>(F.lo));
+      split_pack(p[F.lo] * dw, p[F.hi] * dw, bvh[ff], bvl[ff]);
     }
 #pragma unroll
     for (int s = 0; s < NS; s++) {
@@ -924,9 +1003,11 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // (regions are LDS_WAVE words apart, more than 16*128 for 16-bit codes)
   auto sh_o = [&](int w, int col, int c) -> float& { return ((float*)&lds[w][0])[col * 128 + c]; };
   static_assert(sizeof(lds[0]) >= sizeof(float) * 16 * 128, "partial fits the wave region");
-  const float l_tot = wave_sum16x4(l_run);
-  const float z_tot = wave_sum16x4(z_run);
-  const float of = exp2i(24 - VH + e_run);   // acc_o * 2^24 / pf
+  const int ps = min(VH - e_run, PSMAX);
+  const float unps = exp2i(-ps);
+  const float l_tot = wave_sum16x4(l_run) * unps;
+  const float z_tot = wave_sum16x4(z_run) * unps;
+  const float of = exp2i(24 - ps);           // acc_o * 2^24 / 2^ps
   if (lg == 0) {
     sh_ml[wave][n][0] = m_run;
     sh_ml[wave][n][1] = l_tot;
