@@ -33,14 +33,14 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, profiles/decode_kernel_*.md)
 # for the kernel source with the given digest, and the factors that map each
 # counter onto true bytes: a plain 512 MiB device copy in the same run reads
-# FETCH_SIZE = 262158.9 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
-# fetch counter is scaled by 524288/262158.9 and the write counter by 1.  The
+# FETCH_SIZE = 262160.8 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
+# fetch counter is scaled by 524288/262160.8 and the write counter by 1.  The
 # figure is reported only while the kernel source is unchanged.
 COUNTER_TRAFFIC = {
-    "source_sha256": "a386cf5bb28ca671daa771c77cafb1152e9e0ed4bc956a36702782c3eab9b335",
-    "fetch_kib": 149119.3,
+    "source_sha256": "7592de8713b448f30be1375ddb627777dc0865cd254ed25f054b01dfec5238f8",
+    "fetch_kib": 147927.5,
     "write_kib": 3664.0,
-    "fetch_factor": 524288.0 / 262158.9,
+    "fetch_factor": 524288.0 / 262160.8,
     "write_factor": 1.0,
 }
 KERNEL_SOURCES = ("kv_cache_mixed_amd/csrc/decode_attn.hip", "kv_cache_mixed_amd/csrc/kvq_device.h")
