@@ -175,23 +175,26 @@ __device__ __forceinline__ f32x4 mfma(const uint32_t* a, const uint32_t* b, f32x
 // of a register with itself, each lane holds its own value and that of lane
 // l ^ 32 (l ^ 16) in the two results.
 __device__ __forceinline__ float wave_max16x4(float v) {
-  auto r = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
-  v = u2f(r[0]) > u2f(r[1]) ? u2f(r[0]) : u2f(r[1]);
-  r = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
-  return u2f(r[0]) > u2f(r[1]) ? u2f(r[0]) : u2f(r[1]);
+  uint32_t r0, r1;
+  lane_swap32(f2u(v), r0, r1);
+  v = u2f(r0) > u2f(r1) ? u2f(r0) : u2f(r1);
+  lane_swap16(f2u(v), r0, r1);
+  return u2f(r0) > u2f(r1) ? u2f(r0) : u2f(r1);
 }
 // maximum of non-negative binary32 values, as bit patterns
 __device__ __forceinline__ uint32_t wave_maxu16x4(uint32_t v) {
-  auto r = __builtin_amdgcn_permlane32_swap(v, v, false, false);
-  v = max(r[0], r[1]);
-  r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return max(r[0], r[1]);
+  uint32_t r0, r1;
+  lane_swap32(v, r0, r1);
+  v = max(r0, r1);
+  lane_swap16(v, r0, r1);
+  return max(r0, r1);
 }
 __device__ __forceinline__ float wave_sum16x4(float v) {
-  auto r = __builtin_amdgcn_permlane32_swap(f2u(v), f2u(v), false, false);
-  v = u2f(r[0]) + u2f(r[1]);
-  r = __builtin_amdgcn_permlane16_swap(f2u(v), f2u(v), false, false);
-  return u2f(r[0]) + u2f(r[1]);
+  uint32_t r0, r1;
+  lane_swap32(f2u(v), r0, r1);
+  v = u2f(r0) + u2f(r1);
+  lane_swap16(f2u(v), r0, r1);
+  return u2f(r0) + u2f(r1);
 }
 
 // Load 8 consecutive parameters starting at element e into f32.

@@ -25,6 +25,25 @@ __device__ __forceinline__ float exp2i(int k) {
   return u2f((uint32_t)(k + 127) << 23);
 }
 
+// Lane swaps of gfx950.  v_permlane32_swap / v_permlane16_swap of a register
+// with a copy of itself leave in every lane its own value (r0) and that of
+// lane l ^ 32 / l ^ 16 (r1).  Written as inline assembly: through the
+// builtins the compiler has been seen to use the first result for both
+// (a min or sum of the pair then silently became the lane's own value).  The
+// leading s_nop covers the VALU-write-to-permlane-read wait states.
+__device__ __forceinline__ void lane_swap32(uint32_t x, uint32_t& r0, uint32_t& r1) {
+  uint32_t a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane32_swap_b32 %0, %1\n\ts_nop 0" : "+v"(a), "+v"(b));
+  r0 = a;
+  r1 = b;
+}
+__device__ __forceinline__ void lane_swap16(uint32_t x, uint32_t& r0, uint32_t& r1) {
+  uint32_t a = x, b = x;
+  asm volatile("s_nop 1\n\tv_permlane16_swap_b32 %0, %1\n\ts_nop 0" : "+v"(a), "+v"(b));
+  r0 = a;
+  r1 = b;
+}
+
 // unbiased exponent field of a non-negative binary32 (-127 for zero/subnormal)
 __device__ __forceinline__ int expo(float x) { return (int)((f2u(x) >> 23) & 0xffu) - 127; }
 

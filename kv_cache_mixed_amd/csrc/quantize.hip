@@ -23,7 +23,7 @@ namespace kvq {
 
 template <int IN>  // KVQ_F32 or KVQ_BF16
 __device__ __forceinline__ float load_in(const void* p, int64_t i) {
-  if constexpr (IN == KVQ_F32) return ((const float*)p)[i];
+  if constexpr (IN == KVQ_F32) return __builtin_nontemporal_load((const float*)p + i);
   else return bf16_bits_to_f32(((const uint16_t*)p)[i]);
 }
 
@@ -168,11 +168,26 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __re
 // value word planes.  VEC: the input allows 16-byte (F32) / 8-byte (BF16)
 // loads of 4 channels.
 // ---------------------------------------------------------------------------
+// min / max over each 32-lane half of the wave, result in every lane:
+// quad_perm xor 1 and xor 2, row_half_mirror, row_mirror (DPP, fused into the
+// min / max), then the row swap of v_permlane16_swap
+template <bool MAX>
+__device__ __forceinline__ float half_reduce(float v) {
+  auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
+  v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
+  uint32_t r0, r1;
+  lane_swap16(__builtin_bit_cast(uint32_t, v), r0, r1);
+  return op(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+}
+
 template <int IN, bool VEC>
 __device__ __forceinline__ void load4(const void* p, int64_t i, float* x) {
   if constexpr (VEC && IN == KVQ_F32) {
     typedef float f4 __attribute__((ext_vector_type(4)));
-    const f4 v = *(const f4*)((const float*)p + i);
+    const f4 v = __builtin_nontemporal_load((const f4*)((const float*)p + i));
     x[0] = v[0]; x[1] = v[1]; x[2] = v[2]; x[3] = v[3];
   } else if constexpr (VEC && IN == KVQ_BF16) {
     typedef uint32_t u2 __attribute__((ext_vector_type(2)));
@@ -208,11 +223,8 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __re
     const int t = wave * 32 + 2 * i + half;
     float mn = fminf(fminf(x[i][0], x[i][1]), fminf(x[i][2], x[i][3]));
     float mx = fmaxf(fmaxf(x[i][0], x[i][1]), fmaxf(x[i][2], x[i][3]));
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) {
-      mn = fminf(mn, __shfl_xor(mn, o, 32));
-      mx = fmaxf(mx, __shfl_xor(mx, o, 32));
-    }
+    mn = half_reduce<false>(mn);
+    mx = half_reduce<true>(mx);
     mn = mn + 0.0f;   // -0 and +0 are one value: keep +0 whatever the reduction order
     mx = mx + 0.0f;
     const float s = (mx - mn) / levels;
