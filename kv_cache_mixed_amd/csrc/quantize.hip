@@ -56,25 +56,6 @@ __device__ __forceinline__ void pack_rows_store(const uint16_t* codes, uint8_t* 
   }
 }
 
-// Value tile: codes[c][t] (LDS, pitch PITCH) -> 32-bit words W[w][c][a]
-// holding channel c of tokens 32a + w*(32/BITS) + i, code i at bits
-// [i*BITS, (i+1)*BITS); with c = 64h + 16q + n the word index is
-// w*512 + ((h*16 + n)*4 + a)*4 + q (threads write consecutive words).
-template <int BITS, int PITCH>
-__device__ __forceinline__ void pack_vtile_store(const uint16_t* codes, uint8_t* tile) {
-  constexpr int PER_WORD = 32 / BITS;
-  uint32_t* out = (uint32_t*)tile;
-  for (int idx = threadIdx.x; idx < 512 * BITS; idx += blockDim.x) {
-    const int w = idx >> 9, h = (idx >> 8) & 1, n = (idx >> 4) & 15, a = (idx >> 2) & 3, q = idx & 3;
-    const int c = 64 * h + 16 * q + n;
-    const uint16_t* src = codes + c * PITCH + 32 * a + w * PER_WORD;
-    uint32_t word = 0;
-#pragma unroll
-    for (int i = 0; i < PER_WORD; i++) word |= (uint32_t)src[i] << (i * BITS);
-    out[idx] = word;
-  }
-}
-
 // Mixed key tile: codes[t][slot]; five planes (see include/kvq.h).
 __device__ __forceinline__ void pack_mixed_store(const uint16_t* codes, uint8_t* tile) {
   // planes 0..3: 8 bytes per token = 2 words; 1024 words in total
@@ -164,9 +145,10 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __re
 // 32..63 each hold one token per load (lane l32 holds channels 4*l32..+3), so
 // one load instruction covers two whole token rows; all 16 loads of a wave are
 // issued before any reduction.  The min/max of a token is reduced inside its
-// 32-lane half.  Codes are staged transposed ([c][t]) and packed into the
-// value word planes.  VEC: the input allows 16-byte (F32) / 8-byte (BF16)
-// loads of 4 channels.
+// 32-lane half.  Each lane packs the codes of its 4 channels into the value
+// word planes in registers (the two halves hold alternate tokens of a word and
+// are merged by a lane swap), so no LDS staging.  VEC: the input allows
+// 16-byte (F32) / 8-byte (BF16) loads of 4 channels.
 // ---------------------------------------------------------------------------
 // min / max over each 32-lane half of the wave, result in every lane:
 // quad_perm xor 1 and xor 2, row_half_mirror, row_mirror (DPP, fused into the
@@ -204,8 +186,11 @@ template <int VB, int PDT, int IN, bool VEC>
 __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __restrict__ vin,
                                                          int64_t sb, int64_t sh, int64_t st,
                                                          int t0) {
-  constexpr int PITCH = 130;  // odd word pitch: lanes writing one column hit different banks
-  __shared__ uint16_t codes[128 * PITCH];
+  // word W[w][c][a] holds channel c of the tokens 32a + w*PW + i (i < PW,
+  // code i at bits [i*VB, (i+1)*VB)); a = wave, and local token 2i + half of
+  // iteration i lands in word (2i) / PW at slot (2i) % PW + half
+  constexpr int PW = 32 / VB;                    // codes per word (even: VB <= 16)
+  constexpr int NWD = 32 / PW;                   // words per channel per wave
   const int tile_local = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tile = t0 / 128 + tile_local;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -218,6 +203,13 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __re
     const int t = wave * 32 + 2 * i + half;
     load4<IN, VEC>(vin, base + (int64_t)t * st, x[i]);
   }
+  // codes of the lane's 4 channels packed in registers: this half's slots
+  uint32_t wd[4][NWD];
+#pragma unroll
+  for (int k = 0; k < 4; k++)
+#pragma unroll
+    for (int w = 0; w < NWD; w++) wd[k][w] = 0u;
+  const uint32_t hsh = (uint32_t)(VB * half);
 #pragma unroll
   for (int i = 0; i < 16; i++) {
     const int t = wave * 32 + 2 * i + half;
@@ -235,11 +227,26 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __re
       Param<PDT>::store(g.v_scale, pi, s);
       Param<PDT>::store(g.v_zero, pi, mn);
     }
+    const int w = (2 * i) / PW;
+    const uint32_t sh = (uint32_t)(((2 * i) % PW) * VB) + hsh;
 #pragma unroll
-    for (int k = 0; k < 4; k++) codes[(4 * l32 + k) * PITCH + t] = (uint16_t)quant_code(x[i][k], sp, zp, levels);
+    for (int k = 0; k < 4; k++) wd[k][w] |= quant_code(x[i][k], sp, zp, levels) << sh;
   }
-  __syncthreads();
-  pack_vtile_store<VB, PITCH>(codes, g.v_codes + v_tile_offset(g, b, h, tile));
+  // merge the two halves (lane l and l ^ 32 hold the even and odd slots) and
+  // store: half 0 writes channels 4*l32 + 0, 1, half 1 channels 4*l32 + 2, 3
+  uint32_t* out = (uint32_t*)(g.v_codes + v_tile_offset(g, b, h, tile));
+#pragma unroll
+  for (int k = 0; k < 4; k++)
+#pragma unroll
+    for (int w = 0; w < NWD; w++) {
+      uint32_t r0, r1;
+      lane_swap32(wd[k][w], r0, r1);
+      if ((k >> 1) == half) {
+        const int c = 4 * l32 + k;
+        const int hh = c >> 6, q = (c >> 4) & 3, n = c & 15;
+        out[w * 512 + ((hh * 16 + n) * 4 + wave) * 4 + q] = r0 | r1;
+      }
+    }
 }
 
 // ---------------------------------------------------------------------------
