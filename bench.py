@@ -181,6 +181,54 @@ def progressive_rows(torch, kvq, synth, dev, scale):
                                      "note": "pool layout, single cache (partly Infinity-Cache resident)"}}
 
 
+def qwen32b_step_rows(torch, kvq, synth, dev, scale, n_steps=5):
+    """Qwen2.5-32B-shaped full decode step: 64 layers (B=16, Hkv=8, Hq=40,
+    T=32768), each layer's cache packed at the width of the seeded per-layer
+    table (8 bits for layer 0, else 4 or 2, mean about 2.84 bits), generated
+    with the layer generator (seed = base + layer) and quantized one layer at
+    a time.  One step = the 64 layers' decode calls back to back; the 26 GB of
+    packed caches are far larger than the Infinity Cache."""
+    B, H, Hq, T, L = 16, 8, 40, 32768, 64
+    bits = synth.layer_bits_table(L, seed=0)
+    caches, qs, alg = [], [], 0
+    for layer, b in enumerate(bits):
+        inp = synth.layer_device(B, H, Hq, T, seed=500 + layer, device=dev)
+        c = kvq.PackedCache(B, H, T, b, b, kvq.F16, device=dev)
+        c.quantize(inp["k"], inp["v"], 0)
+        qs.append(inp["q"])
+        caches.append(c)
+        alg += decode_bytes(B, H, Hq, T, b, b, 2)
+        del inp
+        torch.cuda.empty_cache()
+    ws = caches[0].workspace(Hq)
+    for c in caches[1:]:
+        assert c.workspace_bytes(Hq) <= ws.numel()
+    out = torch.empty((B, Hq, 128), dtype=torch.float32, device=dev)
+
+    def step(i):
+        for c, q in zip(caches, qs):
+            c.decode_attn(q, scale, out=out, workspace=ws)
+    step(0)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for i in range(n_steps):
+        step(i)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / n_steps
+    counts = {w: bits.count(w) for w in sorted(set(bits))}
+    del caches, qs
+    torch.cuda.empty_cache()
+    return {"qwen32b_64_layer_step": {
+        "ms": round(ms, 4), "GB/s": round(alg / ms / 1e6, 1), "pct_of_peak": round(100 * alg / ms / 1e6 / PEAK_HBM_GBS, 2),
+        "tokens_per_s": round(B / (ms * 1e-3), 1), "bytes": alg,
+        "layers_per_width": {str(k): v for k, v in counts.items()},
+        "mean_bits": round(sum(bits) / len(bits), 3),
+        "note": "attention only, 64 back-to-back layer calls per step"}}
+
+
 def cpu_baseline(inp, B, H, Hq, k_bits, pdt, seconds):
     """The CPU oracle (as it stands) on a bounded sample of the same workload:
     quantize + fp64 decode attention of whole (batch, kv-head) streams, run in
@@ -350,6 +398,7 @@ def main():
         del rk, rv
         rows.update(mixed_128k_rows(torch, kvq, synth, dev, scale))
         rows.update(progressive_rows(torch, kvq, synth, dev, scale))
+        rows.update(qwen32b_step_rows(torch, kvq, synth, dev, scale))
 
     if args.copy_calibration:
         src = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
