@@ -392,10 +392,17 @@ __device__ __forceinline__ void pload(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 // that; measured, a second resident wave hides more latency than any
 // register-hungry schedule of a single one.  16-bit codes and mixed keys with
 // 1-bit values need the full register file.
+// waves per SIMD of three-stream 4-bit instances (they fit 256 registers).
+// Three streams (15 of 16 columns for G = 5) measured no faster than two at
+// two waves per SIMD, and 1.8x slower at one; 2-bit ones spill at two.
+#ifndef KVQ_DECODE_NS3_OCC
+#define KVQ_DECODE_NS3_OCC 1
+#endif
 constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
   (void)pdt;
   if (KVQ_DECODE_WAVES_PER_SIMD) return KVQ_DECODE_WAVES_PER_SIMD;
-  if (kb == 16 || (kb == 0 && vb == 1) || ns >= 3) return 1;
+  if (kb == 16 || (kb == 0 && vb == 1) || ns >= 4) return 1;
+  if (ns == 3) return kb == 4 ? KVQ_DECODE_NS3_OCC : 1;
   return 2;
 }
 
@@ -1172,9 +1179,13 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 // ---------------------------------------------------------------------------
 // kv streams per wave: as many query groups as fit the 16 MFMA columns,
 // capped per width so the kernel keeps two waves per SIMD without spilling.
+// streams per wave allowed for 4- and 2-bit codes (see KVQ_DECODE_NS3_OCC)
+#ifndef KVQ_DECODE_NS_CAP_LOW
+#define KVQ_DECODE_NS_CAP_LOW 2
+#endif
 constexpr int ns_cap(int kb, int vb) {
   if (kb == 0) return vb == 4 ? 2 : 1;
-  return (kb == 4 || kb == 2) ? 2 : 1;
+  return (kb == 4 || kb == 2) ? KVQ_DECODE_NS_CAP_LOW : 1;
 }
 
 // Launch plan (shared by workspace sizing, validation and launch): NS streams
