@@ -229,6 +229,65 @@ def qwen32b_step_rows(torch, kvq, synth, dev, scale, n_steps=5):
         "note": "attention only, 64 back-to-back layer calls per step"}}
 
 
+def halving_rule_rows(torch, kvq, synth, dev, scale):
+    """Ablation of the halving rule (PM-KVQ Key design 1 and its ablation
+    table, which reports task accuracy; here the stand-in is the decode
+    output): 7B-shaped layer slice (B=4, Hkv=4, Hq=28, T=32768) quantized to
+    4 bits, halved to 2 bits by ERS, the direct right shift and the modified
+    (rounded) shift.  For each: the shrink kernel's time and the decode
+    output's error against binary32 attention over the unquantized K/V (per
+    row ||o - o_ref||_inf / ||o_ref||_inf: max and mean over rows); 4-bit
+    before the halving and a direct 2-bit quantization for reference."""
+    B, H, Hq, T = 4, 4, 28, 32768
+    G = Hq // H
+    inp = synth.layer_device(B, H, Hq, T, seed=71, device=dev)
+    k, v, q = inp["k"], inp["v"], inp["q"]
+    # binary32 reference attention over the unquantized keys and values
+    qf = q.float().view(B, H, G, 128)
+    s_ = torch.matmul(qf, k.transpose(2, 3).contiguous()) * scale          # [B][H][G][T]
+    p_ = torch.softmax(s_, dim=-1)
+    ref = torch.matmul(p_, v).reshape(B, Hq, 128)
+    del s_, p_
+
+    def err(o):
+        e = (o - ref).abs().amax(dim=-1) / ref.abs().amax(dim=-1)
+        return {"max_row_rel_err": float(e.max()), "mean_row_rel_err": float(e.mean())}
+    base = kvq.PackedCache(B, H, T, 4, 4, kvq.F16, device=dev)
+    base.quantize(k, v, 0)
+    out = {"4-bit": err(base.decode_attn(q, scale))}
+    names = {kvq.SHIFT_ERS: "ers", kvq.SHIFT_DIRECT: "direct_shift", kvq.SHIFT_MODIFIED: "modified_shift"}
+    nbytes = B * H * (T // 128) * (2 * 8192 + 2 * 4096) + 2 * 2 * B * H * T * 2
+    for m, nm in names.items():
+        c = kvq.PackedCache(B, H, T, 4, 4, kvq.F16, device=dev)
+        tms = []
+        for i in range(4):
+            for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+                getattr(c, name).copy_(getattr(base, name))
+            c.s.n_tokens, c.s.k_bits, c.s.v_bits = T, 4, 4
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            c.shrink(2, method=m)
+            e1.record()
+            torch.cuda.synchronize()
+            if i:
+                tms.append(e0.elapsed_time(e1))
+        row = err(c.decode_attn(q, scale))
+        ms = sum(tms) / len(tms)
+        row.update({"shrink_ms": round(ms, 4), "shrink_GB/s": round(nbytes / ms / 1e6, 1)})
+        out["4->2 " + nm] = row
+        del c
+    d2 = kvq.PackedCache(B, H, T, 2, 2, kvq.F16, device=dev)
+    d2.quantize(k, v, 0)
+    out["2-bit direct quantization"] = err(d2.decode_attn(q, scale))
+    for key in out:
+        for f in ("max_row_rel_err", "mean_row_rel_err"):
+            out[key][f] = round(out[key][f], 5)
+    del base, d2, inp, k, v, ref
+    torch.cuda.empty_cache()
+    return {"halving_rule_ablation": out}
+
+
 def cpu_baseline(inp, B, H, Hq, k_bits, pdt, seconds):
     """The CPU oracle (as it stands) on a bounded sample of the same workload:
     quantize + fp64 decode attention of whole (batch, kv-head) streams, run in
@@ -398,6 +457,7 @@ def main():
         del rk, rv
         rows.update(mixed_128k_rows(torch, kvq, synth, dev, scale))
         rows.update(progressive_rows(torch, kvq, synth, dev, scale))
+        rows.update(halving_rule_rows(torch, kvq, synth, dev, scale))
         rows.update(qwen32b_step_rows(torch, kvq, synth, dev, scale))
 
     if args.copy_calibration:

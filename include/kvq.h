@@ -195,6 +195,20 @@ kvq_status kvq_quantize(kvq_cache *cache, const void *k, const void *v, kvq_dtyp
  * {8, 4, 2, 1}.  On success k_bits = v_bits = to_bits. */
 kvq_status kvq_shrink(kvq_cache *cache, int32_t to_bits, hipStream_t stream);
 
+/* Bit-width halving rules compared in [PMKVQ]'s ablation (Key design 1 and
+ * the ablation table): the Equivalent Right Shift above; the direct right
+ * shift, which keeps the high b bits (X_b = X_2b >> b, S_b = 2^b * S_2b); and
+ * the modified right shift, which the page names but does not define -- read
+ * here as the rounded shift X_b = min((X_2b + 2^(b-1)) >> b, 2^b - 1),
+ * S_b = 2^b * S_2b.  Zero points stay in every case; scales are narrowed to
+ * the parameter dtype after the exact binary32 product. */
+typedef enum { KVQ_SHIFT_ERS = 0, KVQ_SHIFT_DIRECT = 1, KVQ_SHIFT_MODIFIED = 2 } kvq_shift;
+
+/* kvq_shrink with the halving rule chosen by method (kvq_shrink is
+ * method = KVQ_SHIFT_ERS).  Same requirements, layout and effect on k_bits /
+ * v_bits; KVQ_EINVAL for an unknown method. */
+kvq_status kvq_shrink_shift(kvq_cache *cache, int32_t to_bits, kvq_shift method, hipStream_t stream);
+
 /* Workspace bytes kvq_decode_attn needs for this cache geometry (sized for
  * max_tokens, so it stays valid as the cache grows).  0 on invalid input. */
 /* Leading workspace bytes that hold the decode completion counters, for a

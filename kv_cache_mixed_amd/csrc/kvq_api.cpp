@@ -133,15 +133,21 @@ kvq_status kvq_quantize(kvq_cache* c, const void* k, const void* v, kvq_dtype in
 }
 
 kvq_status kvq_shrink(kvq_cache* c, int32_t to_bits, hipStream_t stream) {
+  return kvq_shrink_shift(c, to_bits, KVQ_SHIFT_ERS, stream);
+}
+
+kvq_status kvq_shrink_shift(kvq_cache* c, int32_t to_bits, kvq_shift method, hipStream_t stream) {
   try {
     kvq_status s = check_cache(c);
     if (s != KVQ_OK) return s;
+    if (method != KVQ_SHIFT_ERS && method != KVQ_SHIFT_DIRECT && method != KVQ_SHIFT_MODIFIED)
+      return KVQ_EINVAL;
     if (to_bits != 8 && to_bits != 4 && to_bits != 2 && to_bits != 1) return KVQ_EINVAL;
     if (c->k_bits == KVQ_KMIXED) return KVQ_EUNSUPPORTED;
     if (c->k_bits != 2 * to_bits || c->v_bits != 2 * to_bits) return KVQ_EINVAL;
     if ((int64_t)c->batch * c->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
     kvq::Geo g = make_geo(c);
-    hipError_t e = kvq::launch_shrink(g, to_bits, stream);
+    hipError_t e = kvq::launch_shrink(g, to_bits, (int)method, stream);
     if (e != hipSuccess) return KVQ_EHIP;
     c->k_bits = to_bits;
     c->v_bits = to_bits;

@@ -226,7 +226,7 @@ namespace kvq {
 hipError_t launch_quantize(const Geo& g, const void* k, const void* v, int in_dtype,
                            const int64_t* ks, const int64_t* vs, int t0, int n_new,
                            hipStream_t st);
-hipError_t launch_shrink(const Geo& g, int to_bits, hipStream_t st);
+hipError_t launch_shrink(const Geo& g, int to_bits, int method, hipStream_t st);
 // partial slots per stream: up to KVQ_MAX_CHUNKS packed chunks, then one per
 // KVQ_RES_CHUNK residual tokens; the combine kernel takes at most 128
 constexpr int KVQ_RES_CHUNK = 32;

@@ -4,6 +4,10 @@
 //   X_b = ((2^(2b) - 2^b + 1) * (X + 2^(b-1))) >> 3b,
 // the zero point is kept and the scale becomes (2^b + 1) * S.  The product
 // stays below 2^32 for b <= 8, so the arithmetic is unsigned 32-bit.
+// The same page's ablation compares it with a direct right shift (keep the
+// high b bits: X_b = X >> b) and a "modified" right shift, which it does not
+// define; here that is the rounded shift min((X + 2^(b-1)) >> b, 2^b - 1).
+// Both keep the zero point and scale by 2^b.
 //
 // A uniform-width key tile is a stream of 16384 codes whose order the shrink
 // keeps.  A value tile's word planes depend on the width: output word
@@ -20,24 +24,31 @@
 
 namespace kvq {
 
-template <int B>
-__device__ __forceinline__ uint32_t ers(uint32_t x) {
-  constexpr uint32_t C = (1u << (2 * B)) - (1u << B) + 1u;
+// one 2B-bit code -> B bits by method M (KVQ_SHIFT_ERS / _DIRECT / _MODIFIED)
+template <int B, int M>
+__device__ __forceinline__ uint32_t shift_code(uint32_t x) {
   constexpr uint32_t HALF = 1u << (B - 1);
-  return (C * (x + HALF)) >> (3 * B);
+  if constexpr (M == KVQ_SHIFT_DIRECT) {
+    return x >> B;
+  } else if constexpr (M == KVQ_SHIFT_MODIFIED) {
+    return min((x + HALF) >> B, (1u << B) - 1u);
+  } else {
+    constexpr uint32_t C = (1u << (2 * B)) - (1u << B) + 1u;
+    return (C * (x + HALF)) >> (3 * B);
+  }
 }
 
-// ERS of n codes of 2B bits in the low bits of w (LSB first) -> n codes of B bits
-template <int B, int N>
-__device__ __forceinline__ uint32_t ers_word(uint32_t w) {
+// n codes of 2B bits in the low bits of w (LSB first) -> n codes of B bits
+template <int B, int M, int N>
+__device__ __forceinline__ uint32_t shift_word(uint32_t w) {
   constexpr uint32_t MASK = (2 * B == 32) ? 0xffffffffu : ((1u << (2 * B)) - 1u);
   uint32_t o = 0;
 #pragma unroll
-  for (int i = 0; i < N; i++) o |= ers<B>((w >> (i * 2 * B)) & MASK) << (i * B);
+  for (int i = 0; i < N; i++) o |= shift_code<B, M>((w >> (i * 2 * B)) & MASK) << (i * B);
   return o;
 }
 
-template <int B, int PDT>
+template <int B, int PDT, int M>
 __global__ __launch_bounds__(256) void shrink_kernel(Geo g) {
   constexpr int IN_WORDS = 4 * B;             // per thread: 64 codes * 2B bits / 32
   constexpr int OUT_WORDS = 2 * B;            // per thread: 64 codes * B bits / 32
@@ -73,7 +84,9 @@ __global__ __launch_bounds__(256) void shrink_kernel(Geo g) {
   float s_new = 0.0f;
   if (threadIdx.x < 128) {
     const float s_old = Param<PDT>::load(sarr, pbase + threadIdx.x);
-    s_new = (float)((1u << B) + 1u) * s_old;        // exact for 16/8/4-bit significands
+    // (2^b + 1) * S is exact for 16/8/4-bit significands; 2^b * S is exact
+    const float f = (M == KVQ_SHIFT_ERS) ? (float)((1u << B) + 1u) : (float)(1u << B);
+    s_new = f * s_old;
   }
   __syncthreads();   // every code of the tile is in registers before any write
 
@@ -83,36 +96,46 @@ __global__ __launch_bounds__(256) void shrink_kernel(Geo g) {
 #pragma unroll
     for (int k = 0; k < OUT_WORDS; k++)
       out[threadIdx.x * OUT_WORDS + k] =
-          ers_word<B, 16 / B>(w[2 * k]) | (ers_word<B, 16 / B>(w[2 * k + 1]) << 16);
+          shift_word<B, M, 16 / B>(w[2 * k]) | (shift_word<B, M, 16 / B>(w[2 * k + 1]) << 16);
   } else {
 #pragma unroll
     for (int k = 0; k < OUT_WORDS; k++)
       out[threadIdx.x + 256 * k] =
-          ers_word<B, 16 / B>(w[2 * k]) | (ers_word<B, 16 / B>(w[2 * k + 1]) << 16);
+          shift_word<B, M, 16 / B>(w[2 * k]) | (shift_word<B, M, 16 / B>(w[2 * k + 1]) << 16);
   }
   if (threadIdx.x < 128) Param<PDT>::store(sarr, pbase + threadIdx.x, s_new);
 }
 
-template <int PDT>
-static hipError_t launch_shrink_pdt(const Geo& g, int to_bits, hipStream_t st) {
+template <int PDT, int M>
+static hipError_t launch_shrink_m(const Geo& g, int to_bits, hipStream_t st) {
   dim3 grid(g.n_tiles, g.B * g.H, 2), block(256);
   switch (to_bits) {
-    case 8: hipLaunchKernelGGL((shrink_kernel<8, PDT>), grid, block, 0, st, g); break;
-    case 4: hipLaunchKernelGGL((shrink_kernel<4, PDT>), grid, block, 0, st, g); break;
-    case 2: hipLaunchKernelGGL((shrink_kernel<2, PDT>), grid, block, 0, st, g); break;
-    case 1: hipLaunchKernelGGL((shrink_kernel<1, PDT>), grid, block, 0, st, g); break;
+    case 8: hipLaunchKernelGGL((shrink_kernel<8, PDT, M>), grid, block, 0, st, g); break;
+    case 4: hipLaunchKernelGGL((shrink_kernel<4, PDT, M>), grid, block, 0, st, g); break;
+    case 2: hipLaunchKernelGGL((shrink_kernel<2, PDT, M>), grid, block, 0, st, g); break;
+    case 1: hipLaunchKernelGGL((shrink_kernel<1, PDT, M>), grid, block, 0, st, g); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-hipError_t launch_shrink(const Geo& g, int to_bits, hipStream_t st) {
+template <int PDT>
+static hipError_t launch_shrink_pdt(const Geo& g, int to_bits, int method, hipStream_t st) {
+  switch (method) {
+    case KVQ_SHIFT_ERS: return launch_shrink_m<PDT, KVQ_SHIFT_ERS>(g, to_bits, st);
+    case KVQ_SHIFT_DIRECT: return launch_shrink_m<PDT, KVQ_SHIFT_DIRECT>(g, to_bits, st);
+    case KVQ_SHIFT_MODIFIED: return launch_shrink_m<PDT, KVQ_SHIFT_MODIFIED>(g, to_bits, st);
+  }
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_shrink(const Geo& g, int to_bits, int method, hipStream_t st) {
   if (g.n_tiles == 0) return hipSuccess;
   switch (g.pdt) {
-    case KVQ_F32: return launch_shrink_pdt<KVQ_F32>(g, to_bits, st);
-    case KVQ_F16: return launch_shrink_pdt<KVQ_F16>(g, to_bits, st);
-    case KVQ_BF16: return launch_shrink_pdt<KVQ_BF16>(g, to_bits, st);
-    case KVQ_E4M3: return launch_shrink_pdt<KVQ_E4M3>(g, to_bits, st);
+    case KVQ_F32: return launch_shrink_pdt<KVQ_F32>(g, to_bits, method, st);
+    case KVQ_F16: return launch_shrink_pdt<KVQ_F16>(g, to_bits, method, st);
+    case KVQ_BF16: return launch_shrink_pdt<KVQ_BF16>(g, to_bits, method, st);
+    case KVQ_E4M3: return launch_shrink_pdt<KVQ_E4M3>(g, to_bits, method, st);
   }
   return hipErrorInvalidValue;
 }

@@ -21,6 +21,7 @@ PARAM_BYTES = {F32: 4, F16: 2, BF16: 2, E4M3: 1}
 KMIXED = 0
 MIXED_TILE_BYTES = 4352
 OK, EINVAL, EUNSUPPORTED, EBUDGET, EWORKSPACE, EHIP = range(6)
+SHIFT_ERS, SHIFT_DIRECT, SHIFT_MODIFIED = range(3)   # kvq_shift of the header
 MAX_RESIDUAL = 512          # KVQ_MAX_RESIDUAL of the header
 
 
@@ -49,7 +50,7 @@ class KvqError(RuntimeError):
 _lib = None
 
 EXPORTS = ["kvq_strerror", "kvq_tile_bytes", "kvq_cache_bytes", "kvq_quantize", "kvq_shrink",
-           "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_decode_attn_residual",
+           "kvq_shrink_shift", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_decode_attn_residual",
            "kvq_pool_create", "kvq_pool_destroy", "kvq_pool_used_bytes", "kvq_pool_high_water",
            "kvq_append"]
 
@@ -74,6 +75,8 @@ def load():
     L.kvq_quantize.argtypes = [P, vp, vp, ctypes.c_int, vp, vp, i32, i32, vp]
     L.kvq_shrink.restype = ctypes.c_int
     L.kvq_shrink.argtypes = [P, i32, vp]
+    L.kvq_shrink_shift.restype = ctypes.c_int
+    L.kvq_shrink_shift.argtypes = [P, i32, ctypes.c_int, vp]
     L.kvq_decode_workspace_bytes.restype = ctypes.c_size_t
     L.kvq_decode_workspace_bytes.argtypes = [P, i32]
     L.kvq_decode_attn.restype = ctypes.c_int
@@ -238,8 +241,12 @@ class PackedCache:
                                  t0, n_new, _stream_ptr(stream))
         _check(st, "kvq_quantize")
 
-    def shrink(self, to_bits, stream=None):
-        _check(load().kvq_shrink(ctypes.byref(self.s), to_bits, _stream_ptr(stream)), "kvq_shrink")
+    def shrink(self, to_bits, stream=None, method=SHIFT_ERS):
+        if method == SHIFT_ERS:
+            _check(load().kvq_shrink(ctypes.byref(self.s), to_bits, _stream_ptr(stream)), "kvq_shrink")
+        else:
+            _check(load().kvq_shrink_shift(ctypes.byref(self.s), to_bits, method, _stream_ptr(stream)),
+                   "kvq_shrink_shift")
 
     def append(self, k, v, budget_bytes, floor_bits, stream=None):
         import torch

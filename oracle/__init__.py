@@ -84,6 +84,10 @@ def lib():
             L.orc_quantize_v.argtypes = [vp, i64, i32, i32, i32, vp, i64, vp, vp]
             L.orc_shrink_tile.argtypes = [vp, i32]
             L.orc_shrink_scales.argtypes = [vp, i64, i32, i32]
+            L.orc_shrink_tile_m.argtypes = [vp, i32, i32]
+            L.orc_shrink_vtile_m.argtypes = [vp, i32, i32]
+            L.orc_shrink_scales_m.argtypes = [vp, i64, i32, i32, i32]
+            L.orc_shift_array.argtypes = [vp, i64, i32, i32, vp]
             L.orc_decode_attn.restype = i32
             L.orc_decode_attn.argtypes = [vp, i64, vp, vp, i32, vp, vp, i64, vp, vp, i32,
                                           i32, i32, vp, i32, ctypes.c_float, vp]
@@ -122,6 +126,18 @@ def decode(raw: np.ndarray, pdt: int) -> np.ndarray:
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """binary32 -> bfloat16 raw bits (RNE)."""
     return narrow(x, BF16)
+
+
+SHIFT_ERS, SHIFT_DIRECT, SHIFT_MODIFIED = 0, 1, 2
+
+
+def shift(x: np.ndarray, b: int, method: int) -> np.ndarray:
+    """2b-bit codes -> b bits by a halving rule of the ablation (0 ERS, 1
+    direct right shift, 2 modified (rounded, clamped) right shift)."""
+    x = np.ascontiguousarray(x, dtype=np.uint32)
+    out = np.empty_like(x)
+    lib().orc_shift_array(_p(x), x.size, b, method, _p(out))
+    return out
 
 
 def ers(x: np.ndarray, b: int) -> np.ndarray:
@@ -246,22 +262,23 @@ def quantize_stream(k: np.ndarray, v: np.ndarray, k_bits: int, v_bits: int, pdt:
     return Stream(k_bits, v_bits, pdt, kt, ks, kz, vt, vs, vz, sc)
 
 
-def shrink_stream(st: Stream, to_bits: int) -> Stream:
-    """ERS 2b -> b of every tile of a uniform-width stream (returns a new Stream)."""
+def shrink_stream(st: Stream, to_bits: int, method: int = SHIFT_ERS) -> Stream:
+    """2b -> b of every tile of a uniform-width stream (returns a new Stream);
+    method: 0 ERS, 1 direct right shift, 2 modified right shift."""
     assert st.k_bits == 2 * to_bits and st.v_bits == 2 * to_bits
     L = lib()
     out = []
-    for tiles, fn in ((st.k_tiles, L.orc_shrink_tile), (st.v_tiles, L.orc_shrink_vtile)):
+    for tiles, fn in ((st.k_tiles, L.orc_shrink_tile_m), (st.v_tiles, L.orc_shrink_vtile_m)):
         t2 = np.array(tiles, copy=True)
         for i in range(t2.shape[0]):
             row = np.ascontiguousarray(t2[i])
-            fn(_p(row), to_bits)
+            fn(_p(row), to_bits, method)
             t2[i] = row
         out.append(np.ascontiguousarray(t2[:, : tile_bytes(to_bits)]))
     ks = np.array(st.ks, copy=True)
     vs = np.array(st.vs, copy=True)
-    L.orc_shrink_scales(_p(ks), ks.size, to_bits, st.pdt)
-    L.orc_shrink_scales(_p(vs), vs.size, to_bits, st.pdt)
+    L.orc_shrink_scales_m(_p(ks), ks.size, to_bits, st.pdt, method)
+    L.orc_shrink_scales_m(_p(vs), vs.size, to_bits, st.pdt, method)
     return Stream(to_bits, to_bits, st.pdt, out[0], ks, st.kz.copy(), out[1], vs, st.vz.copy(),
                   st.slot_chan)
 

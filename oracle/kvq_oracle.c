@@ -436,42 +436,66 @@ uint32_t orc_ers(uint32_t x2b, int b)
     return (uint32_t)((c * n) >> (3 * b));
 }
 
+/* The halving rules of [PMKVQ]'s ablation (Key design 1 and the ablation
+ * table), method 0/1/2:
+ *   0 Equivalent Right Shift, as above;
+ *   1 direct right shift -- keep the high b bits of the 2b-bit code, i.e.
+ *     floor(X / 2^b);
+ *   2 modified right shift -- not defined on the page; read as the shift with
+ *     rounding, floor((X + 2^(b-1)) / 2^b), clamped to 2^b - 1.
+ * Zero points stay; the scale becomes (2^b + 1) S for ERS and 2^b S for the
+ * two shifts (one step of the new code spans 2^b old steps). */
+uint32_t orc_shift(uint32_t x2b, int b, int method)
+{
+    uint32_t top = (1u << b) - 1u;
+    if (method == 1) return x2b / (1u << b);
+    if (method == 2) {
+        uint32_t r = (x2b + (1u << (b - 1))) / (1u << b);
+        return r < top ? r : top;
+    }
+    return orc_ers(x2b, b);
+}
+
 /* Shrink one packed uniform-width key tile in place: 16384 codes of 2b bits
  * -> b bits, code order unchanged. */
-void orc_shrink_tile(uint8_t *tile, int to_bits)
+void orc_shrink_tile_m(uint8_t *tile, int to_bits, int method)
 {
     int from = 2 * to_bits;
     uint16_t *c = (uint16_t *)malloc(128 * 128 * sizeof(uint16_t));
     orc_unpack_rows(tile, from, c);
-    for (int i = 0; i < 128 * 128; i++) c[i] = (uint16_t)orc_ers(c[i], to_bits);
+    for (int i = 0; i < 128 * 128; i++) c[i] = (uint16_t)orc_shift(c[i], to_bits, method);
     memset(tile, 0, (size_t)16 * from * 128);
     orc_pack_rows(c, to_bits, tile);
     free(c);
 }
+void orc_shrink_tile(uint8_t *tile, int to_bits) { orc_shrink_tile_m(tile, to_bits, 0); }
 
 /* Shrink one value tile in place: every code goes from its position in the
  * 2b-bit word planes to its position in the b-bit word planes. */
-void orc_shrink_vtile(uint8_t *tile, int to_bits)
+void orc_shrink_vtile_m(uint8_t *tile, int to_bits, int method)
 {
     int from = 2 * to_bits;
     uint16_t *c = (uint16_t *)malloc(128 * 128 * sizeof(uint16_t));
     orc_unpack_vtile(tile, from, c);
-    for (int i = 0; i < 128 * 128; i++) c[i] = (uint16_t)orc_ers(c[i], to_bits);
+    for (int i = 0; i < 128 * 128; i++) c[i] = (uint16_t)orc_shift(c[i], to_bits, method);
     memset(tile, 0, (size_t)16 * from * 128);
     orc_pack_vtile(c, to_bits, tile);
     free(c);
 }
+void orc_shrink_vtile(uint8_t *tile, int to_bits) { orc_shrink_vtile_m(tile, to_bits, 0); }
 
-/* S_b = narrow(binary32((2^b + 1) * S_2b)); exact before narrowing for
- * binary16, bfloat16 and e4m3 scales (at most 11 + 9 significant bits). */
-void orc_shrink_scales(void *s, int64_t n, int to_bits, int pdt)
+/* S_b = narrow(binary32(f * S_2b)), f = 2^b + 1 (ERS) or 2^b (the shifts);
+ * exact before narrowing for binary16, bfloat16 and e4m3 scales (at most
+ * 11 + 9 significant bits). */
+void orc_shrink_scales_m(void *s, int64_t n, int to_bits, int pdt, int method)
 {
-    float f = (float)((1u << to_bits) + 1u);
+    float f = method == 0 ? (float)((1u << to_bits) + 1u) : (float)(1u << to_bits);
     for (int64_t i = 0; i < n; i++) {
         float sv = (float)param_load(s, i, pdt);
         param_store(s, i, pdt, f * sv);
     }
 }
+void orc_shrink_scales(void *s, int64_t n, int to_bits, int pdt) { orc_shrink_scales_m(s, n, to_bits, pdt, 0); }
 
 /* ------------------------------------------------------------------------ */
 /* O7/O8. Decode attention over one (batch, kv-head) stream, binary64.       */
@@ -588,6 +612,11 @@ void orc_narrow_array(const float *x, int64_t n, int pdt, void *out)
 void orc_decode_array(const void *in, int64_t n, int pdt, double *out)
 {
     for (int64_t i = 0; i < n; i++) out[i] = param_load(in, i, pdt);
+}
+
+void orc_shift_array(const uint32_t *x, int64_t n, int b, int method, uint32_t *out)
+{
+    for (int64_t i = 0; i < n; i++) out[i] = orc_shift(x[i], b, method);
 }
 
 void orc_ers_array(const uint32_t *x, int64_t n, int b, uint32_t *out)

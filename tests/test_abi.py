@@ -96,6 +96,12 @@ def test_validation_rejects_before_launch():
     bad = _fake_struct(2, 2, 1024, 4, 4)
     bad.k_codes = FAKE + 4                                   # misaligned code buffer
     assert L.kvq_quantize(P(bad), vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 0, 128, None) == kvq.EINVAL
+    # shrink with an unknown halving rule, or a known one at a wrong width
+    s2m = _fake_struct(2, 2, 1024, 4, 4)
+    assert L.kvq_shrink_shift(P(s2m), 2, 3, None) == kvq.EINVAL
+    assert L.kvq_shrink_shift(P(s2m), 2, -1, None) == kvq.EINVAL
+    assert L.kvq_shrink_shift(P(s2m), 1, kvq.SHIFT_DIRECT, None) == kvq.EINVAL
+    assert s2m.k_bits == 4 and s2m.v_bits == 4
     # shrink
     s2 = _fake_struct(2, 2, 1024, 4, 4)
     assert L.kvq_shrink(P(s2), 4, None) == kvq.EINVAL        # 4 -> 4 is not a halving

@@ -90,6 +90,25 @@ def test_shrink_bitexact(to_bits, pdt):
             assert_stream_bytes_equal(cache, st, b, h, "shrink to %d" % to_bits)
 
 
+@pytest.mark.parametrize("to_bits", [8, 4, 2, 1])
+@pytest.mark.parametrize("method", [kvq.SHIFT_DIRECT, kvq.SHIFT_MODIFIED])
+def test_shrink_other_rules_bitexact(to_bits, method):
+    """The ablation's direct and modified right shifts, bytes and scales
+    against the oracle; decode over the shrunk cache within tolerance."""
+    print("case shrink rule=%d to=%d" % (method, to_bits), flush=True)
+    inp, cache = _quantized(2, 2, 8, 384, 2 * to_bits, 2 * to_bits, kvq.F16, seed=40 + to_bits + 7 * method)
+    cache.shrink(to_bits, method=method)
+    torch.cuda.synchronize()
+    assert cache.k_bits == to_bits and cache.v_bits == to_bits
+    out = cache.decode_attn(q_to_dev(inp["q_bf16"], torch), SCALE).cpu().numpy()
+    for b in range(2):
+        for h in range(2):
+            st = oracle.shrink_stream(oracle_stream(inp, b, h, 2 * to_bits, 2 * to_bits, kvq.F16), to_bits, method)
+            assert_stream_bytes_equal(cache, st, b, h, "shrink rule %d to %d" % (method, to_bits))
+            ref = oracle_attn(st, inp["q_bf16"][b, h * 4:(h + 1) * 4])
+            assert rel_err_rows(out[b, h * 4:(h + 1) * 4], ref).max() <= REL_TOL
+
+
 def _decode_case(B, H, Hq, T, k_bits, v_bits, pdt, seed, mixed=False, pairs=None):
     inp, cache = _quantized(B, H, Hq, T, k_bits, v_bits, pdt, seed, mixed)
     q = q_to_dev(inp["q_bf16"], torch)
