@@ -296,6 +296,30 @@ kvq_status kvq_append(kvq_cache *cache, kvq_pool *pool, int64_t budget_bytes, in
                       const int64_t k_strides[3], const int64_t v_strides[3], int32_t n_new,
                       hipStream_t stream, int32_t *n_shrinks);
 
+/* ------------------------------------------------------------------------
+ * Block-wise bit-width allocation ([PMKVQ] Key design 2: each transformer
+ * block gets one width, minimising the summed sensitivity s_{i,b} with the
+ * blocks' total KV-cache memory within the budget M).  Host-only; the
+ * sensitivities are the caller's (the page derives them from loss
+ * gradients).
+ *
+ * sens: host [n_blocks][n_choices] finite binary64; bytes: host
+ * [n_blocks][n_choices] cache bytes of block i at choice j (> 0, at most
+ * 2^50).  Finds choice[i] in [0, n_choices) minimising
+ *   s[0][c0] + (s[1][c1] + ( ... + s[n-1][c_{n-1}]))   (binary64, that order)
+ * subject to sum_i bytes[i][c_i] <= budget_bytes, exactly (dynamic
+ * programming over the costs divided by their greatest common divisor);
+ * among minimal allocations the lexicographically smallest choice vector.
+ * *cost (may be NULL) receives the minimum.  KVQ_EBUDGET if even the
+ * cheapest choices exceed the budget; KVQ_EUNSUPPORTED if the table would
+ * exceed KVQ_ALLOC_MAX_STATES entries (n_blocks + 1) * (budget / gcd + 1);
+ * KVQ_EINVAL for bad arguments.  choice is written only on KVQ_OK. */
+#define KVQ_ALLOC_MAX_CHOICES 16
+#define KVQ_ALLOC_MAX_STATES ((int64_t)1 << 26)
+kvq_status kvq_allocate_bits(int32_t n_blocks, int32_t n_choices, const double *sens,
+                             const int64_t *bytes, int64_t budget_bytes, int32_t *choice,
+                             double *cost);
+
 #ifdef __cplusplus
 }
 #endif

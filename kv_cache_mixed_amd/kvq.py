@@ -52,7 +52,7 @@ _lib = None
 EXPORTS = ["kvq_strerror", "kvq_tile_bytes", "kvq_cache_bytes", "kvq_quantize", "kvq_shrink",
            "kvq_shrink_shift", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_decode_attn_residual",
            "kvq_pool_create", "kvq_pool_destroy", "kvq_pool_used_bytes", "kvq_pool_high_water",
-           "kvq_append"]
+           "kvq_append", "kvq_allocate_bits"]
 
 
 def load():
@@ -84,6 +84,8 @@ def load():
     L.kvq_decode_attn_residual.restype = ctypes.c_int
     L.kvq_decode_attn_residual.argtypes = [P, vp, i32, ctypes.c_float, vp, vp, ctypes.c_int, vp, vp,
                                            i32, vp, vp, ctypes.c_size_t, vp]
+    L.kvq_allocate_bits.restype = ctypes.c_int
+    L.kvq_allocate_bits.argtypes = [i32, i32, vp, vp, i64, vp, ctypes.POINTER(ctypes.c_double)]
     L.kvq_pool_create.restype = ctypes.c_int
     L.kvq_pool_create.argtypes = [P, i64, vp, vp, ctypes.POINTER(vp)]
     L.kvq_pool_destroy.restype = None
@@ -122,6 +124,21 @@ def _strides3(t):
     """(b, h, t) element strides of a [B][H][T][128] tensor with unit channel stride."""
     assert t.dim() == 4 and t.shape[-1] == 128 and t.stride(-1) == 1
     return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+def allocate_bits(sens, nbytes, budget_bytes):
+    """kvq_allocate_bits: sens [n_blocks][n_choices] (float64), nbytes
+    [n_blocks][n_choices] (int64) host arrays -> (choice indices, minimum)."""
+    import numpy as np
+    s = np.ascontiguousarray(sens, dtype=np.float64)
+    w = np.ascontiguousarray(nbytes, dtype=np.int64)
+    assert s.ndim == 2 and s.shape == w.shape
+    choice = np.zeros(s.shape[0], dtype=np.int32)
+    cost = ctypes.c_double(0.0)
+    st = load().kvq_allocate_bits(s.shape[0], s.shape[1], s.ctypes.data, w.ctypes.data, int(budget_bytes),
+                                  choice.ctypes.data, ctypes.byref(cost))
+    _check(st, "kvq_allocate_bits")
+    return choice, cost.value
 
 
 def tile_bytes(bits: int) -> int:

@@ -373,3 +373,26 @@ def schedule(B, H, n_total, start_bits, floor_bits, pdt, budget):
     if n < 0:
         return None
     return [(int(ev[2 * i]), int(ev[2 * i + 1])) for i in range(n)]
+
+
+# --------------------------------------------------------------------------
+# block-wise bit-width allocation (PM-KVQ Key design 2), by enumeration
+# --------------------------------------------------------------------------
+def allocate_bits_bruteforce(sens, nbytes, budget_bytes):
+    """Every choice vector in lexicographic order; the objective is the sum
+    s[0][c0] + (s[1][c1] + (... + s[n-1][c_{n-1}])) in binary64 (Python
+    float) under sum_i nbytes[i][c_i] <= budget_bytes; the first vector with
+    the smallest sum wins.  None if no vector fits.  Small instances only."""
+    import itertools
+    n, m = len(sens), len(sens[0])
+    best, best_cost = None, None
+    for cv in itertools.product(range(m), repeat=n):
+        if sum(int(nbytes[i][cv[i]]) for i in range(n)) > budget_bytes:
+            continue
+        c = 0.0
+        for i in reversed(range(n)):
+            c = float(sens[i][cv[i]]) + c
+        if best_cost is None or c < best_cost:
+            best, best_cost = cv, c
+    return (None, None) if best is None else (list(best), best_cost)
+
