@@ -1183,8 +1183,17 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #ifndef KVQ_DECODE_NS_CAP_LOW
 #define KVQ_DECODE_NS_CAP_LOW 2
 #endif
+// a plan packing several streams per wave falls back to one stream when its
+// chunks would hold fewer tiles than this
+#ifndef KVQ_DECODE_NS_MIN_TPC
+#define KVQ_DECODE_NS_MIN_TPC 16
+#endif
+// measured: two mixed-key streams per wave 30% slower, three 2x slower
+#ifndef KVQ_DECODE_NS_CAP_MIXED2
+#define KVQ_DECODE_NS_CAP_MIXED2 1
+#endif
 constexpr int ns_cap(int kb, int vb) {
-  if (kb == 0) return vb == 4 ? 2 : 1;
+  if (kb == 0) return vb == 4 ? 2 : (vb == 2 ? KVQ_DECODE_NS_CAP_MIXED2 : 1);
   return (kb == 4 || kb == 2) ? KVQ_DECODE_NS_CAP_LOW : 1;
 }
 
@@ -1221,7 +1230,7 @@ DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_til
   if (ns > KVQ_DECODE_NS_MAX) ns = KVQ_DECODE_NS_MAX;
   ns = ns > cap ? cap : (ns < 1 ? 1 : ns);
   DecodePlan p = plan_for(BH, ns, k_bits, v_bits, pdt, n_tiles);
-  if (ns > 1 && p.tpc < 16) p = plan_for(BH, 1, k_bits, v_bits, pdt, n_tiles);
+  if (ns > 1 && p.tpc < KVQ_DECODE_NS_MIN_TPC) p = plan_for(BH, 1, k_bits, v_bits, pdt, n_tiles);
   return p;
 }
 
