@@ -249,15 +249,25 @@ struct UInfo {
   static constexpr int NW = B;
 };
 
+// -1.0f in an SGPR that the compiler cannot see through: fma(h, -1, x) with
+// a literal -1 is rewritten into a subtraction, which then needs the half
+// widened first
+__device__ __forceinline__ float opaque_m1() {
+  uint32_t b;
+  asm("s_mov_b32 %0, 0xbf800000" : "=s"(b));
+  return __builtin_bit_cast(float, b);
+}
+
 // f16 split of a pair: hi = f16 truncation of x (one v_cvt_pkrtz for both),
 // lo = f16 of the binary32 residual x - hi, which is exact (hi is x with low
 // significand bits cleared); the residual reads hi's halves directly
-// (v_fma_mix_f32), so the pair costs two conversions and two mixed fmas.
-__device__ __forceinline__ void split_pack(float xl, float xh, uint32_t& hi, uint32_t& lo) {
+// (v_fma_mix_f32 with m1 = -1), so the pair costs two conversions and two
+// mixed fmas.
+__device__ __forceinline__ void split_pack(float xl, float xh, uint32_t& hi, uint32_t& lo, float m1) {
   const auto h = __builtin_amdgcn_cvt_pkrtz(xl, xh);
   hi = __builtin_bit_cast(uint32_t, h);
-  const float rl = __builtin_fmaf((float)h[0], -1.0f, xl);
-  const float rh = __builtin_fmaf((float)h[1], -1.0f, xh);
+  const float rl = __builtin_fmaf((float)h[0], m1, xl);
+  const float rh = __builtin_fmaf((float)h[1], m1, xh);
   lo = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(rl, rh));
 }
 
@@ -514,6 +524,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 
   float m_run = -INFINITY, l_run = 0.0f, z_run = 0.0f;
   int e_run = -1000;
+  const float m1 = opaque_m1();
   float ak = 0.0f, bk0 = 0.0f;
   // output accumulators: one set per stream when SACC (no masking of the
   // probabilities; column n then takes its own stream's set at the end)
@@ -716,24 +727,40 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     };
     uint32_t qw[16];
     load_q(qw);
-    float beta = 0.0f;
+    // beta in four independent chains (a single chain of 32 fmas is latency bound)
+    float beta;
     {
       uint32_t zw[4 * PWK];
       load_kp(1, zw);
+      float bc[4] = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
-      for (int li = 0; li < 32; li++) beta = fmaf(qget(qw, li), pget<PDT>(zw, li), beta);
+      for (int li = 0; li < 32; li++) bc[li & 3] = fmaf(qget(qw, li), pget<PDT>(zw, li), bc[li & 3]);
+      beta = (bc[0] + bc[1]) + (bc[2] + bc[3]);
     }
     uint32_t sw[4 * PWK];
     load_kp(0, sw);
     uint32_t smax = 0;
+    if constexpr (PDT == KVQ_F16) {
+      // scales are >= +0, so their binary16 patterns order like the values
+      uint32_t m2 = sw[0];
 #pragma unroll
-    for (int li = 0; li < 32; li++) smax = max(smax, f2u(pget<PDT>(sw, li)));   // scales are >= +0
+      for (int i = 1; i < 4 * PWK; i++) m2 = pk_max_u16(m2, sw[i]);
+      smax = f2u((float)__builtin_bit_cast(_Float16, (uint16_t)max(m2 & 0xffffu, m2 >> 16)));
+    } else {
+#pragma unroll
+      for (int li = 0; li < 32; li++) smax = max(smax, f2u(pget<PDT>(sw, li)));   // scales are >= +0
+    }
     // eq + es is bounded below so that kf * 2^(field weight) stays finite when
     // a tile's scales are all zero (codes then 0, u = 0)
     const int eqs = max(eq + expo(u2f(wave_maxu16x4(smax))), -100);
     beta = wave_sum16x4(beta);
     const float kf = exp2i(KH - eqs);
-    auto uval = [&](int li) -> float { return qget(qw, li) * pget<PDT>(sw, li); };
+    // q * S; a binary16 scale is read by a mixed fma (+0 addend: the product
+    // itself, up to the sign of a zero)
+    auto uval = [&](int li) -> float {
+      if constexpr (PDT == KVQ_F16) return __builtin_fmaf(qget(qw, li), pget<PDT>(sw, li), 0.0f);
+      else return qget(qw, li) * pget<PDT>(sw, li);
+    };
 #pragma unroll
     for (int f = 0; f < NFK; f++) {
       float ul, uh, w;
@@ -749,7 +776,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
         w = kf * exp2i(F.wexp - F.pos);
       }
       uint32_t hi, lo;
-      split_pack(ul * w, uh * w, hi, lo);
+      split_pack(ul * w, uh * w, hi, lo, m1);
       // [k-step][hi/lo][lane][4]: one ds_read_b128 per operand group
       my_lds[(((f >> 2) * 2 + 0) * 64 + lane) * 4 + (f & 3)] = hi;
       my_lds[(((f >> 2) * 2 + 1) * 64 + lane) * 4 + (f & 3)] = lo;
@@ -919,7 +946,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       // carries the weight of its first field; the other gets the difference
       const Fld F = ufield<VB>(ff);
       const float dw = exp2i((F.wexp - F.pos) - tok_w<VB, FVS>(F.lo));
-      split_pack(p[F.lo] * dw, p[F.hi] * dw, bvh[ff], bvl[ff]);
+      split_pack(p[F.lo] * dw, p[F.hi] * dw, bvh[ff], bvl[ff], m1);
     }
 #pragma unroll
     for (int s = 0; s < NS; s++) {
