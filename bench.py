@@ -33,14 +33,14 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, profiles/decode_kernel_*.md)
 # for the kernel source with the given digest, and the factors that map each
 # counter onto true bytes: a plain 512 MiB device copy in the same run reads
-# FETCH_SIZE = 262160.8 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
-# fetch counter is scaled by 524288/262160.8 and the write counter by 1.  The
+# FETCH_SIZE = 262160.5 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
+# fetch counter is scaled by 524288/262160.5 and the write counter by 1.  The
 # figure is reported only while the kernel source is unchanged.
 COUNTER_TRAFFIC = {
-    "source_sha256": "7592de8713b448f30be1375ddb627777dc0865cd254ed25f054b01dfec5238f8",
-    "fetch_kib": 147927.5,
+    "source_sha256": "198f5005386f2c94c3b686b7034bc2d0acec4e162a43b8547a32da35286989f0",
+    "fetch_kib": 147930.4,
     "write_kib": 3664.0,
-    "fetch_factor": 524288.0 / 262160.8,
+    "fetch_factor": 524288.0 / 262160.5,
     "write_factor": 1.0,
 }
 KERNEL_SOURCES = ("kv_cache_mixed_amd/csrc/decode_attn.hip", "kv_cache_mixed_amd/csrc/kvq_device.h")
