@@ -52,38 +52,9 @@
 #ifndef KVQ_DECODE_NSUB_MAX
 #define KVQ_DECODE_NSUB_MAX 4
 #endif
-// chunks own strided tile sets (1) or contiguous tile ranges (0)
-#ifndef KVQ_DECODE_STRIDED
-#define KVQ_DECODE_STRIDED 0
-#endif
 // most kv streams one decode wave packs into its MFMA columns
 #ifndef KVQ_DECODE_NS_MAX
 #define KVQ_DECODE_NS_MAX 3
-#endif
-// value words of sub-tile j are loaded at the start of sub-tile j (0) or of
-// sub-tile j-1 (1)
-#ifndef KVQ_DECODE_V_AHEAD
-#define KVQ_DECODE_V_AHEAD 0
-#endif
-// prefetch key blocks / value parameters two sub-tiles ahead, refilling a
-// buffer as soon as its part has been consumed (1), or one sub-tile ahead (0)
-#ifndef KVQ_DECODE_PF2
-#define KVQ_DECODE_PF2 1
-#endif
-// one set of output accumulators per packed stream (1) or one shared set with
-// the probabilities masked per stream (0)
-#ifndef KVQ_DECODE_SACC
-#define KVQ_DECODE_SACC 0
-#endif
-// hand the chunk's tiles to its waves one at a time through an LDS counter (1)
-// or in a fixed round robin (0)
-#ifndef KVQ_DECODE_DYN
-#define KVQ_DECODE_DYN 0
-#endif
-// rescale the output accumulators every sub-tile (1) or only when some head's
-// reference moved (0)
-#ifndef KVQ_DECODE_BRANCHLESS_RESCALE
-#define KVQ_DECODE_BRANCHLESS_RESCALE 0
 #endif
 // wave priority from the tiles a wave has left (1) or the default (0)
 #ifndef KVQ_DECODE_PRIO
@@ -92,8 +63,8 @@
 // streams split into at least this many chunks are combined inside the decode
 // kernel by the workgroup that finishes the last chunk of a stream group;
 // fewer chunks are combined by a second kernel.  Measured: a second kernel is
-// cheaper at the 16-32 chunks of batched layers, where the write-through wait
-// at the end of every workgroup costs more than the launch; the in-kernel
+// cheaper at the 16-32 chunks of batched layers, where the combine work of the
+// last workgroups at the tail costs more than the launch; the in-kernel
 // combine wins for the 64 chunks of single-sequence long contexts.
 #ifndef KVQ_DECODE_FUSED_MIN_CHUNKS
 #define KVQ_DECODE_FUSED_MIN_CHUNKS 48
@@ -106,10 +77,6 @@
 #endif
 #ifndef KVQ_DECODE_CPOL_PARAMS
 #define KVQ_DECODE_CPOL_PARAMS 0
-#endif
-// grid x = stream group, y = chunk (1) or x = chunk, y = stream group (0)
-#ifndef KVQ_DECODE_GRID_SWAP
-#define KVQ_DECODE_GRID_SWAP 0
 #endif
 // workgroups one decode launch aims at per wave-per-SIMD of the instance
 #ifndef KVQ_DECODE_WG_PER_OCC
@@ -458,7 +425,6 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   constexpr int PSMAX = 96;
   constexpr int ROW_K = MIXED ? 8 : 16 * KB;
   constexpr int LDS_WAVE = NFK * 2 * 64;             // u32 words of folded query per wave
-  constexpr bool SACC = (KVQ_DECODE_SACC != 0) && NS > 1;
   constexpr int CPOL = (KB == 16) ? 0 : KVQ_DECODE_CPOL_CODES;
   static_assert(KSV >= 1 && WVS >= 1, "sub-tile must hold whole value k-steps");
   static_assert(LDS_WAVE >= 16 * 128 && TPS % 8 == 0, "layout assumptions");
@@ -475,25 +441,17 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, lg = lane >> 4;
   // consecutive workgroup ids (which the dispatcher deals out to the XCDs in
-  // turn) walk the stream groups (1) or the chunks of one group (0)
-  const int grp = KVQ_DECODE_GRID_SWAP ? blockIdx.x : blockIdx.y;
-  const int chunk = KVQ_DECODE_GRID_SWAP ? blockIdx.y : blockIdx.x;
+  // turn) walk the chunks of one stream group
+  const int grp = blockIdx.y;
+  const int chunk = blockIdx.x;
   const int G = a.G;
   const int BH = g.B * g.H;
-  const int own = n / G, hn = n - (n / G) * G;
+  const int own = n / G;
   const int bh_own = grp * NS + own;
   const bool real = (own < NS) && (bh_own < BH);
-  const int b_own = real ? bh_own / g.H : 0, h_own = real ? bh_own % g.H : 0;
-  // the chunk's tiles, numbered k = 0 .. t_count-1: tile = t_base + t_stride * k
-#if KVQ_DECODE_STRIDED
-  // chunk c owns tiles c, c + n_chunks, ...: at any moment the workgroups of a
-  // stream read neighbouring tiles
-  const int t_count = (g.n_tiles - chunk + a.n_chunks - 1) / a.n_chunks;
-  const int t_base = chunk, t_stride = a.n_chunks;
-#else
+  // the chunk's tiles, numbered k = 0 .. t_count-1: tile = t_base + k
   const int t_count = min(a.tpc, g.n_tiles - chunk * a.tpc);
-  const int t_base = chunk * a.tpc, t_stride = 1;
-#endif
+  const int t_base = chunk * a.tpc;
 
   auto kslot = [&](int li) -> int {
     if constexpr (MIXED) return lg == 0 ? (li < 24 ? li : 96 + li) : 32 * lg - 8 + li;
@@ -526,23 +484,16 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   int e_run = -1000;
   const float m1 = opaque_m1();
   float ak = 0.0f, bk0 = 0.0f;
-  // output accumulators: one set per stream when SACC (no masking of the
-  // probabilities; column n then takes its own stream's set at the end)
-  constexpr int NA = SACC ? NS : 1;
-  f32x4 acc_o[NA][8];
+  // output accumulators, shared by the packed streams (the probabilities are
+  // masked per stream)
+  f32x4 acc_o[8];
 #pragma unroll
-  for (int s = 0; s < NA; s++)
-#pragma unroll
-    for (int cb = 0; cb < 8; cb++) acc_o[s][cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
+  for (int cb = 0; cb < 8; cb++) acc_o[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   uint32_t* my_lds = lds[wave];
 
-  // one sub-tile of raw operands
-  // value words travel outside the prefetch buffers: they are loaded at the
-  // start of their own sub-tile (in flight during its key product and
-  // softmax) or one sub-tile earlier
-  constexpr bool VAHEAD = KVQ_DECODE_V_AHEAD != 0;
-  constexpr bool PF2 = KVQ_DECODE_PF2 != 0;
-  constexpr bool DYN = KVQ_DECODE_DYN != 0;
+  // one sub-tile of raw operands; value words travel outside the prefetch
+  // buffers: they are loaded at the start of their own sub-tile (in flight
+  // during its key product and softmax)
   struct Buf {
     uint32_t kw[NS][JB][NWK];
     uint32_t vs[PWV], vz[PWV];
@@ -571,7 +522,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // sub-tile `sub` (a constant after unrolling) of the chunk's tile k: key
   // blocks (and, for sub-tile 0, the tile's key parameters) ...
   auto load_k = [&](Buf& bf, int k, int sub) {
-    const int tile = t_base + t_stride * k;
+    const int tile = t_base + k;
 #pragma unroll
     for (int s = 0; s < NS; s++) {
       const int bh = min(grp * NS + s, BH - 1);   // a missing stream re-reads a valid one
@@ -617,7 +568,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   };
   // ... and the own stream's value scales / zeros of the lane's TPS tokens
   auto load_p = [&](Buf& bf, int k, int sub) {
-    const int tile = t_base + t_stride * k;
+    const int tile = t_base + k;
     const uint32_t psoff = (uint32_t)(tile * 128 + sub * TPS) * PB;
     pload<PDT, TPS>(r_vs, vpoff, psoff, bf.vs);
     pload<PDT, TPS>(r_vz, vpoff, psoff, bf.vz);
@@ -629,21 +580,8 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 
   // the first sub-tile's loads are in flight while the query is staged
   Buf b0, b1;
-  // tiles of the chunk handed out to the waves one at a time (dynamic) or in
-  // the fixed order k = w, w + 4, ...; the queue holds the wave's next four
-  __shared__ int s_next;
-  auto grab = [&]() -> int {
-    int v = 0;
-    if (lane == 0) v = atomicAdd(&s_next, 1);
-    return __builtin_amdgcn_readfirstlane(v);
-  };
-  int q0, q1, q2, q3;
-  if constexpr (DYN) {
-    if (threadIdx.x == 0) s_next = 4;   // k = 0..3 go to waves 0..3 without an atomic
-    q0 = wave;
-  } else {
-    q0 = wave;
-  }
+  // wave w takes the chunk's tiles k = w, w + 4, ...; the queue holds its next four
+  int q0 = wave, q1, q2, q3;
   // ---- the query heads of the group in slot order, [column][slot] bf16 in
   // LDS (column n = stream n / G, head n % G; zero for columns without a
   // head).  Column cn is query row grp * NS * G + cn of q (rows are
@@ -790,14 +728,12 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // been read
   auto issue_v = [&](uint32_t* vw, int k, int sub) {
 #pragma unroll
-    for (int s = 0; s < NS; s++) load_vw(vw + s * 8 * WVS, v_rsrc(s, t_base + t_stride * k), sub);
+    for (int s = 0; s < NS; s++) load_vw(vw + s * 8 * WVS, v_rsrc(s, t_base + k), sub);
   };
-  auto compute = [&](Buf& bf, int ti, int sub, int ti2, int sub2, uint32_t* vcur, uint32_t* vnext,
-                     int ti1, int sub1) {
-    uint32_t vjit[VAHEAD ? 1 : NS * 8 * WVS];
-    if constexpr (VAHEAD) issue_v(vnext, ti1, sub1);
-    else issue_v(vjit, ti, sub);
-    const uint32_t* vwp = VAHEAD ? vcur : vjit;
+  auto compute = [&](Buf& bf, int ti, int sub, int ti2, int sub2) {
+    uint32_t vjit[NS * 8 * WVS];
+    issue_v(vjit, ti, sub);
+    const uint32_t* vwp = vjit;
     if (sub == 0) fold_query(bf);
     // ---- logits: k-step-major over all (stream, block) accumulators
     f32x4 acc[NS][JB];
@@ -836,7 +772,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
         for (int jj = 0; jj < JB; jj++) acc[s][jj] = mfma(av[s][jj], bl4, acc[s][jj]);
     }
-    if constexpr (PF2) load_k(bf, ti2, sub2);
+    load_k(bf, ti2, sub2);
     // ---- logits l = ak * v + bk0 (v the column's own raw sum) and an online
     // softmax with a lazy running max: the reference m_run only moves when a
     // logit exceeds it by more than TAU (so e <= 2^TAU), and the accumulator
@@ -886,7 +822,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       for (int i = 0; i < TPS; i++) vsmax = max(vsmax, f2u(vs[i]));   // scales are >= +0
       ev = expo(u2f(wave_maxu16x4(vsmax)));
     }
-    if constexpr (PF2) load_p(bf, ti2, sub2);
+    load_p(bf, ti2, sub2);
     const float m_new = (tmax > m_run + (float)TAU) ? tmax : m_run;
     const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // v_exp_f32, 0 for -inf
     const int e_new = max(e_run, ev);
@@ -923,19 +859,10 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       if (class_used<VB, FVS, TPS>(k)) zsum = fmaf(zc[k], exp2i(-class_w<VB>(k)), zsum);
     l_run = fmaf(l_run, rescale, lsum);
     z_run = fmaf(z_run, rescale, zsum);
-#if KVQ_DECODE_BRANCHLESS_RESCALE
-#pragma unroll
-    for (int s = 0; s < NA; s++)
-#pragma unroll
-      for (int cb = 0; cb < 8; cb++) acc_o[s][cb] *= rescale;
-#else
     if (__builtin_amdgcn_ballot_w64(rescale != 1.0f) != 0) {
 #pragma unroll
-      for (int s = 0; s < NA; s++)
-#pragma unroll
-        for (int cb = 0; cb < 8; cb++) acc_o[s][cb] *= rescale;
+      for (int cb = 0; cb < 8; cb++) acc_o[cb] *= rescale;
     }
-#endif
 
     // ---- P operand (split hi/lo) and PV; every sub-tile has the field
     // layout of sub-tile 0, shifted by WVS words and TPS tokens
@@ -953,11 +880,11 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       uint32_t bsh[FVS], bsl[FVS];
 #pragma unroll
       for (int ff = 0; ff < FVS; ff++) {
-        const bool sel = SACC || (NS == 1) || (own == s);
+        const bool sel = (NS == 1) || (own == s);
         bsh[ff] = sel ? bvh[ff] : 0u;
         bsl[ff] = sel ? bvl[ff] : 0u;
       }
-      f32x4* ao = acc_o[SACC ? s : 0];
+      f32x4* ao = acc_o;
 #pragma unroll
       for (int k = 0; k < KSV; k++) {
         uint32_t av[8][4];
@@ -983,24 +910,15 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // bounds) instead of branching.
   constexpr int U = NSUB >= 2 ? NSUB : 2;
   constexpr int TPI = U / NSUB;   // tiles per iteration (2 for one-sub-tile tiles)
-  if constexpr (DYN) {
-    q1 = grab(); q2 = grab(); q3 = grab();
-  } else {
-    q1 = q0 + 4; q2 = q0 + 8; q3 = q0 + 12;
-  }
+  q1 = q0 + 4; q2 = q0 + 8; q3 = q0 + 12;
   // the queue entry for sub-tile offset d (d = 0..3 tiles ahead), a valid tile
   // when it lies past the chunk (such prefetches are never consumed)
   auto qk = [&](int d) -> int {
     const int v = d == 0 ? q0 : (d == 1 ? q1 : (d == 2 ? q2 : q3));
     return v < t_count ? v : q0;
   };
-  if constexpr (PF2) {
-    if (q0 < t_count) load(b1, qk(1 / NSUB), 1 % NSUB);
-  }
-  uint32_t vb[VAHEAD ? 2 : 1][VAHEAD ? NS * 8 * WVS : 1];
-  if constexpr (VAHEAD) {
-    if (q0 < t_count) issue_v(vb[0], q0, 0);
-  }
+  // the second buffer: loads run two sub-tiles ahead of the computation
+  if (q0 < t_count) load(b1, qk(1 / NSUB), 1 % NSUB);
 #pragma unroll 1
   while (q0 < t_count) {
     if constexpr (KVQ_DECODE_PRIO != 0) {
@@ -1008,7 +926,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       // issues the older wave first when both are ready, so the older one
       // would finish early and leave its SIMDs half idle.  The wave with more
       // tiles left runs at the higher priority instead.
-      const int rem = DYN ? 3 : (t_count - q0 + 3) / 4 - 1;
+      const int rem = (t_count - q0 + 3) / 4 - 1;
       if (rem >= 3) __builtin_amdgcn_s_setprio(3);
       else if (rem == 2) __builtin_amdgcn_s_setprio(2);
       else if (rem == 1) __builtin_amdgcn_s_setprio(1);
@@ -1019,17 +937,15 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       if constexpr (NSUB == 1) {
         if (u == 1 && q1 >= t_count) break;
       }
-      if constexpr (!PF2) load((u % 2 == 0) ? b1 : b0, qk((u + 1) / NSUB), (u + 1) % NSUB);
-      compute((u % 2 == 0) ? b0 : b1, qk(u / NSUB), u % NSUB, qk((u + 2) / NSUB), (u + 2) % NSUB,
-              vb[VAHEAD ? u % 2 : 0], vb[VAHEAD ? (u + 1) % 2 : 0], qk((u + 1) / NSUB), (u + 1) % NSUB);
+      compute((u % 2 == 0) ? b0 : b1, qk(u / NSUB), u % NSUB, qk((u + 2) / NSUB), (u + 2) % NSUB);
     }
     if constexpr (TPI == 1) {
       q0 = q1; q1 = q2; q2 = q3;
-      q3 = DYN ? grab() : q3 + 4;
+      q3 = q3 + 4;
     } else {
       q0 = q2; q1 = q3;
-      q2 = DYN ? grab() : q2 + 8;
-      q3 = DYN ? grab() : q3 + 8;
+      q2 = q2 + 8;
+      q3 = q3 + 8;
     }
   }
 
@@ -1053,10 +969,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   for (int cb = 0; cb < 8; cb++)
 #pragma unroll
     for (int i = 0; i < 4; i++) {
-      float a = acc_o[0][cb][i];
-#pragma unroll
-      for (int s = 1; s < NA; s++)
-        if (own == s) a = acc_o[s][cb][i];
+      const float a = acc_o[cb][i];
       sh_o(wave, n, 16 * cb + 4 * lg + i) = (m_run == -INFINITY) ? 0.0f : a * of + z_tot;
     }
   __syncthreads();
@@ -1302,7 +1215,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
     n0 = fmaf(w, v[k].x, n0);
     n1 = fmaf(w, v[k].y, n1);
   }
-#pragma unroll 8
   for (int k = 16; k < nck; k++) {
     const float w = u2f(__builtin_amdgcn_readlane(f2u(k < 64 ? w0 : w1), k & 63));
     const float2 x = *(const float2*)(po + step * k);
@@ -1483,8 +1395,7 @@ static hipError_t launch_ns(const DecodeArgs& a0, hipStream_t st) {
   a.tpc = p.tpc;
   a.n_slots = p.n_chunks + a.n_slots;   // residual slots on entry
   a.fused = a.n_slots > 1 && p.n_chunks >= KVQ_DECODE_FUSED_MIN_CHUNKS;
-  const dim3 grid(KVQ_DECODE_GRID_SWAP ? a.n_groups : a.n_chunks, KVQ_DECODE_GRID_SWAP ? a.n_chunks : a.n_groups),
-      block(256);
+  const dim3 grid(a.n_chunks, a.n_groups), block(256);
   if (p.ns == 1) {
     hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 1>), grid, block, 0, st, a);
   } else if (p.ns == 2) {
