@@ -147,13 +147,16 @@ struct Param<KVQ_F32> {
 };
 template <>
 struct Param<KVQ_F16> {
+  // hardware conversions: v_cvt_f16_f32 rounds to nearest even with IEEE
+  // overflow to infinity and keeps binary16 subnormals (the kernels run with
+  // denormals enabled); v_cvt_f32_f16 is exact
   static constexpr int bytes = 2;
   __device__ static float load(const void* p, int64_t i) {
-    return f16_bits_to_f32(((const uint16_t*)p)[i]);
+    return (float)((const _Float16*)p)[i];
   }
-  __device__ static float narrow(float x) { return f16_bits_to_f32(f32_to_f16_bits(x)); }
-  __device__ static void store(void* p, int64_t i, float x) { ((uint16_t*)p)[i] = f32_to_f16_bits(x); }
-  __device__ static float dec(uint32_t raw) { return f16_bits_to_f32(raw); }
+  __device__ static float narrow(float x) { return (float)(_Float16)x; }
+  __device__ static void store(void* p, int64_t i, float x) { ((_Float16*)p)[i] = (_Float16)x; }
+  __device__ static float dec(uint32_t raw) { return (float)__builtin_bit_cast(_Float16, (uint16_t)raw); }
 };
 template <>
 struct Param<KVQ_BF16> {

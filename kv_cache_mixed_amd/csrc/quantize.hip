@@ -9,8 +9,10 @@
 // the stored dtype before the codes are computed from them.
 //
 // Bit-exactness: every step is one IEEE binary32 operation (no contraction),
-// division is correctly rounded (HIP default), rounding of the quotient is
-// round-half-even (v_rndne_f32), narrowing is done on the bit pattern.
+// division is correctly rounded (HIP default) -- the code quotient is formed
+// with a reciprocal and re-done by division wherever that could round
+// differently (quant_code) --, rounding of the quotient is round-half-even
+// (v_rndne_f32), narrowing is done on the bit pattern.
 //
 // One workgroup (256 threads) per (tile, kv head, batch).  The input tile is
 // read once with coalesced loads, codes are staged in LDS as uint16, and the
@@ -27,15 +29,47 @@ __device__ __forceinline__ float load_in(const void* p, int64_t i) {
   else return bf16_bits_to_f32(((const uint16_t*)p)[i]);
 }
 
-// Quantize one group member given the stored (narrowed) S', Z'.
-__device__ __forceinline__ uint32_t quant_code(float x, float sp, float zp, float levels) {
-  if (sp == 0.0f) return 0u;
-  float d = x - zp;
-  float r = d / sp;
-  float rr = __builtin_rintf(r);
-  rr = rr > 0.0f ? rr : 0.0f;   // also maps NaN to 0
-  rr = rr < levels ? rr : levels;
-  return (uint32_t)rr;
+// Codes of N members of one group given the stored (narrowed) S', Z'.
+//
+// A code is rint(fl32(d / S')), d = fl32(x - Z'), clamped to [0, levels].  It
+// is formed from r = d * rsp, rsp = v_rcp_f32(S') (within 1 ulp of 1/S'): r is
+// within |d/S'| * 2^-22 of fl32(d / S') (one ulp of the reciprocal, one
+// rounding of the product, one of the division), so both round to the same
+// integer unless r lies within that distance of a half-integer.  When any
+// lane of the wave has a member with r within |r| * 2^-19 of a half-integer
+// (or r not finite, or S' so large that its reciprocal is subnormal), the
+// wave redoes the N quotients with the correctly rounded division -- members
+// away from a half-integer get the same codes either way.  Widths above
+// 8 bits (quotients up to 65535, where that window would catch a large share)
+// always divide.  S' = 0 gives code 0.
+template <bool FAST, int N>
+__device__ __forceinline__ void quant_codes(const float* x, float sp, float zp, float levels, uint32_t* q) {
+  float d[N], rr[N];
+  bool redo = !FAST;
+#pragma unroll
+  for (int k = 0; k < N; k++) d[k] = x[k] - zp;
+  if constexpr (FAST) {
+    const float rsp = __builtin_amdgcn_rcpf(sp);
+    bool near = !(sp < 0x1p125f);
+#pragma unroll
+    for (int k = 0; k < N; k++) {
+      const float r = d[k] * rsp;
+      rr[k] = __builtin_rintf(r);
+      // distance of r from its nearest half-integer: 0.5 - |r - rint(r)|
+      near |= !(__builtin_fabsf(r - rr[k]) < __builtin_fmaf(__builtin_fabsf(r), -0x1p-19f, 0.5f));
+    }
+    redo = __builtin_amdgcn_ballot_w64(near && sp != 0.0f) != 0;
+  }
+  if (redo) {
+#pragma unroll
+    for (int k = 0; k < N; k++) rr[k] = __builtin_rintf(d[k] / sp);
+  }
+#pragma unroll
+  for (int k = 0; k < N; k++) {
+    float c = rr[k] > 0.0f ? rr[k] : 0.0f;   // also maps NaN to 0
+    c = c < levels ? c : levels;
+    q[k] = sp == 0.0f ? 0u : (uint32_t)c;
+  }
 }
 
 // Pack codes[row][elem] (LDS, uint16, row pitch PITCH) into 128 rows of
@@ -132,8 +166,12 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __re
     Param<PDT>::store(g.k_zero, pi, mn);
   }
 #pragma unroll
-  for (int i = 0; i < 64; i++)
-    codes[(half * 64 + i) * 128 + j] = (uint16_t)quant_code(x[i], sp, zp, levels);
+  for (int i = 0; i < 64; i += 8) {
+    uint32_t q[8];
+    quant_codes<KB <= 8, 8>(&x[i], sp, zp, levels, q);
+#pragma unroll
+    for (int k = 0; k < 8; k++) codes[(half * 64 + i + k) * 128 + j] = (uint16_t)q[k];
+  }
   __syncthreads();
   uint8_t* dst = g.k_codes + k_tile_offset(g, b, h, tile);
   if constexpr (KB == 0) pack_mixed_store(codes, dst);
@@ -141,28 +179,28 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __re
 }
 
 // ---------------------------------------------------------------------------
-// Values: wave w handles tokens [32w, 32w+32) of the tile.  Lanes 0..31 and
-// 32..63 each hold one token per load (lane l32 holds channels 4*l32..+3), so
-// one load instruction covers two whole token rows; all 16 loads of a wave are
-// issued before any reduction.  The min/max of a token is reduced inside its
-// 32-lane half.  Each lane packs the codes of its 4 channels into the value
-// word planes in registers (the two halves hold alternate tokens of a word and
-// are merged by a lane swap), so no LDS staging.  VEC: the input allows
-// 16-byte (F32) / 8-byte (BF16) loads of 4 channels.
+// Values: wave a handles tokens [32a, 32a+32) of the tile.  Row r of the wave
+// (16 lanes) takes tokens 32a + 8r + i, i = 0..7, one per step; lane j of the
+// row holds channels 4j..4j+3 and 64+4j..64+4j+3 of it, so one load
+// instruction covers four whole token rows, and all 16 loads of a lane are
+// issued before any reduction.  The min/max of a token is a reduction inside
+// its row (four DPP steps).  Each lane packs the codes of its 8 channels for
+// the row's 8 tokens into value words in registers: a row fills whole words
+// at b >= 4; at b = 2 (1) two (four) rows share a word and are merged by lane
+// swaps -- no LDS staging.  VEC: the input allows 16-byte (F32) / 8-byte
+// (BF16) loads of 4 channels.
 // ---------------------------------------------------------------------------
-// min / max over each 32-lane half of the wave, result in every lane:
+// min / max over each 16-lane row of the wave, result in every lane:
 // quad_perm xor 1 and xor 2, row_half_mirror, row_mirror (DPP, fused into the
-// min / max), then the row swap of v_permlane16_swap
+// min / max)
 template <bool MAX>
-__device__ __forceinline__ float half_reduce(float v) {
+__device__ __forceinline__ float row_reduce(float v) {
   auto op = [](float a, float b) { return MAX ? fmaxf(a, b) : fminf(a, b); };
   v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0xB1, 0xF, 0xF, false)));
   v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x4E, 0xF, 0xF, false)));
   v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x141, 0xF, 0xF, false)));
   v = op(v, __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), 0x140, 0xF, 0xF, false)));
-  uint32_t r0, r1;
-  lane_swap16(__builtin_bit_cast(uint32_t, v), r0, r1);
-  return op(__builtin_bit_cast(float, r0), __builtin_bit_cast(float, r1));
+  return v;
 }
 
 template <int IN, bool VEC>
@@ -187,66 +225,84 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __re
                                                          int64_t sb, int64_t sh, int64_t st,
                                                          int t0) {
   // word W[w][c][a] holds channel c of the tokens 32a + w*PW + i (i < PW,
-  // code i at bits [i*VB, (i+1)*VB)); a = wave, and local token 2i + half of
-  // iteration i lands in word (2i) / PW at slot (2i) % PW + half
-  constexpr int PW = 32 / VB;                    // codes per word (even: VB <= 16)
-  constexpr int NWD = 32 / PW;                   // words per channel per wave
+  // code i at bits [i*VB, (i+1)*VB)); token 32a + 8r + i (step i of row r)
+  // lands in word (8r + i) / PW at slot (8r + i) % PW
+  constexpr int PW = 32 / VB;                    // codes per word
+  constexpr int RW = (8 * VB + 31) / 32;         // words per channel a row fills (one when shared)
   const int tile_local = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tile = t0 / 128 + tile_local;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int half = lane >> 5, l32 = lane & 31;
+  const int row = lane >> 4, j = lane & 15;
   const float levels = (float)((1u << VB) - 1u);
-  const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (int64_t)(tile_local * 128) * st + 4 * l32;
-  float x[16][4];
+  const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (int64_t)(tile_local * 128) * st + 4 * j;
+  float x[8][8];   // [step][channel slot k: channel 64 * (k / 4) + 4j + k % 4]
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const int t = wave * 32 + 2 * i + half;
-    load4<IN, VEC>(vin, base + (int64_t)t * st, x[i]);
+  for (int i = 0; i < 8; i++) {
+    const int t = wave * 32 + 8 * row + i;
+    load4<IN, VEC>(vin, base + (int64_t)t * st, &x[i][0]);
+    load4<IN, VEC>(vin, base + (int64_t)t * st + 64, &x[i][4]);
   }
-  // codes of the lane's 4 channels packed in registers: this half's slots
-  uint32_t wd[4][NWD];
+  uint32_t wd[8][RW];
 #pragma unroll
-  for (int k = 0; k < 4; k++)
+  for (int k = 0; k < 8; k++)
 #pragma unroll
-    for (int w = 0; w < NWD; w++) wd[k][w] = 0u;
-  const uint32_t hsh = (uint32_t)(VB * half);
+    for (int w = 0; w < RW; w++) wd[k][w] = 0u;
 #pragma unroll
-  for (int i = 0; i < 16; i++) {
-    const int t = wave * 32 + 2 * i + half;
-    float mn = fminf(fminf(x[i][0], x[i][1]), fminf(x[i][2], x[i][3]));
-    float mx = fmaxf(fmaxf(x[i][0], x[i][1]), fmaxf(x[i][2], x[i][3]));
-    mn = half_reduce<false>(mn);
-    mx = half_reduce<true>(mx);
+  for (int i = 0; i < 8; i++) {
+    const int t = wave * 32 + 8 * row + i;
+    float mn = x[i][0], mx = x[i][0];
+#pragma unroll
+    for (int k = 1; k < 8; k++) {
+      mn = fminf(mn, x[i][k]);
+      mx = fmaxf(mx, x[i][k]);
+    }
+    mn = row_reduce<false>(mn);
+    mx = row_reduce<true>(mx);
     mn = mn + 0.0f;   // -0 and +0 are one value: keep +0 whatever the reduction order
     mx = mx + 0.0f;
     const float s = (mx - mn) / levels;
     const float sp = Param<PDT>::narrow(s);
     const float zp = Param<PDT>::narrow(mn);
-    if (l32 == 0) {
+    if (j == 0) {
       const int64_t pi = v_param_base(g, b, h, (int64_t)tile * 128 + t);
       Param<PDT>::store(g.v_scale, pi, s);
       Param<PDT>::store(g.v_zero, pi, mn);
     }
-    const int w = (2 * i) / PW;
-    const uint32_t sh = (uint32_t)(((2 * i) % PW) * VB) + hsh;
+    // word of the row (b >= 4: i / PW; shared words: the row's part of word 0)
+    const int lw = (VB >= 4) ? i / PW : 0;
+    const uint32_t sh = (VB >= 4) ? (uint32_t)((i % PW) * VB) : (uint32_t)(((8 * row + i) % PW) * VB);
+    uint32_t qc[8];
+    quant_codes<VB <= 8, 8>(x[i], sp, zp, levels, qc);
 #pragma unroll
-    for (int k = 0; k < 4; k++) wd[k][w] |= quant_code(x[i][k], sp, zp, levels) << sh;
+    for (int k = 0; k < 8; k++) wd[k][lw] |= qc[k] << sh;
   }
-  // merge the two halves (lane l and l ^ 32 hold the even and odd slots) and
-  // store: half 0 writes channels 4*l32 + 0, 1, half 1 channels 4*l32 + 2, 3
-  uint32_t* out = (uint32_t*)(g.v_codes + v_tile_offset(g, b, h, tile));
+  // rows sharing a word: merge rows (0, 1) and (2, 3), then (0-1, 2-3)
+  if constexpr (VB <= 2) {
 #pragma unroll
-  for (int k = 0; k < 4; k++)
-#pragma unroll
-    for (int w = 0; w < NWD; w++) {
+    for (int k = 0; k < 8; k++) {
       uint32_t r0, r1;
-      lane_swap32(wd[k][w], r0, r1);
-      if ((k >> 1) == half) {
-        const int c = 4 * l32 + k;
-        const int hh = c >> 6, q = (c >> 4) & 3, n = c & 15;
-        out[w * 512 + ((hh * 16 + n) * 4 + wave) * 4 + q] = r0 | r1;
+      lane_swap16(wd[k][0], r0, r1);
+      wd[k][0] = r0 | r1;
+      if constexpr (VB == 1) {
+        lane_swap32(wd[k][0], r0, r1);
+        wd[k][0] = r0 | r1;
       }
     }
+  }
+  const bool writer = (VB >= 4) || (VB == 2 ? (row & 1) == 0 : row == 0);
+  if (writer) {
+    uint32_t* out = (uint32_t*)(g.v_codes + v_tile_offset(g, b, h, tile));
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      // channel c = 64 hh + 16 q + n
+      const int hh = k >> 2, q = j >> 2, n = 4 * (j & 3) + (k & 3);
+#pragma unroll
+      for (int lw = 0; lw < RW; lw++) {
+        const int w = (VB >= 4) ? (8 * row) / PW + lw : (8 * row) / PW;
+        out[w * 512 + ((hh * 16 + n) * 4 + wave) * 4 + q] = wd[k][lw];
+      }
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
