@@ -12,11 +12,13 @@
 // division is correctly rounded (HIP default) -- the code quotient is formed
 // with a reciprocal and re-done by division wherever that could round
 // differently (quant_code) --, rounding of the quotient is round-half-even
-// (v_rndne_f32), narrowing is done on the bit pattern.
+// (v_rndne_f32), narrowing rounds to nearest even (binary16: v_cvt_f16_f32
+// with denormals kept; bfloat16 and e4m3: on the bit pattern).
 //
 // One workgroup (256 threads) per (tile, kv head, batch).  The input tile is
-// read once with coalesced loads, codes are staged in LDS as uint16, and the
-// packed rows are written with coalesced 32-bit stores.
+// read once with coalesced loads; key codes are staged in LDS as uint16 and
+// written as packed rows with coalesced 32-bit stores, value codes are packed
+// in registers.
 #pragma clang fp contract(off)
 
 #include "kvq_device.h"
