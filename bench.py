@@ -33,14 +33,14 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, profiles/decode_kernel_*.md)
 # for the kernel source with the given digest, and the factors that map each
 # counter onto true bytes: a plain 512 MiB device copy in the same run reads
-# FETCH_SIZE = 262160.5 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
-# fetch counter is scaled by 524288/262160.5 and the write counter by 1.  The
+# FETCH_SIZE = 262160.3 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
+# fetch counter is scaled by 524288/262160.3 and the write counter by 1.  The
 # figure is reported only while the kernel source is unchanged.
 COUNTER_TRAFFIC = {
-    "source_sha256": "198f5005386f2c94c3b686b7034bc2d0acec4e162a43b8547a32da35286989f0",
-    "fetch_kib": 147930.4,
+    "source_sha256": "e9afe16c9db2a6d30094e44be03032ed623e1cdbeb7db8f37a502ad14b5e77e2",
+    "fetch_kib": 147937.5,
     "write_kib": 3664.0,
-    "fetch_factor": 524288.0 / 262160.5,
+    "fetch_factor": 524288.0 / 262160.3,
     "write_factor": 1.0,
 }
 KERNEL_SOURCES = ("kv_cache_mixed_amd/csrc/decode_attn.hip", "kv_cache_mixed_amd/csrc/kvq_device.h")
@@ -134,8 +134,9 @@ def mixed_128k_rows(torch, kvq, synth, dev, scale):
 def progressive_rows(torch, kvq, synth, dev, scale):
     """Progressive schedule: 128-token groups appended from 16 bits under a
     128 MiB budget (B=8, Hkv=4, Hq=28) up to 32768 tokens.  Times every append
-    (the three that halve the cache include the whole-cache ERS), and decode at
-    the last token count of each width."""
+    (the three that halve the cache include the whole-cache ERS), the ERS
+    kernel of each halving on its own, and decode at the last token count of
+    each width."""
     B, H, Hq, T = 8, 4, 28, 32768
     budget = 128 << 20
     inp = synth.layer_device(B, H, Hq, T, seed=33, device=dev)
@@ -173,7 +174,35 @@ def progressive_rows(torch, kvq, synth, dev, scale):
             dms = d0.elapsed_time(d1) / 10
             alg = decode_bytes(B, H, Hq, t1, cache.k_bits, cache.v_bits, 2)
             dec["%d-bit@%d" % (cache.k_bits, t1)] = {"ms": round(dms, 4), "GB/s": round(alg / dms / 1e6, 1)}
-    del inp, cache
+    del cache
+    torch.cuda.empty_cache()
+    # the ERS kernel of each event on its own: the same (B, Hkv, tokens, width)
+    # in the contiguous layout, timed around the one shrink launch (the append
+    # above also carries the host-side pool bookkeeping and the group's quantize)
+    for ev in events:
+        t0, b = ev["tokens"], ev["from_bits"]
+        src = kvq.PackedCache(B, H, t0, b, b, kvq.F16, device=dev)
+        src.quantize(inp["k"][:, :, :t0], inp["v"][:, :, :t0], 0)
+        sh = kvq.PackedCache(B, H, t0, b, b, kvq.F16, device=dev)
+        tms = []
+        for i in range(4):
+            for name in ("k_codes", "v_codes", "k_scale", "k_zero", "v_scale", "v_zero"):
+                getattr(sh, name).copy_(getattr(src, name))
+            sh.s.n_tokens, sh.s.k_bits, sh.s.v_bits = t0, b, b
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record()
+            sh.shrink(b // 2)
+            e1.record()
+            torch.cuda.synchronize()
+            if i:
+                tms.append(e0.elapsed_time(e1))
+        ms = sum(tms) / len(tms)
+        # read both tiles at b bits, write both halves at b/2; read and write S'
+        nbytes = B * H * (t0 // 128) * (2 * 2048 * b + 2 * 2048 * (b // 2)) + 2 * 2 * B * H * t0 * 2
+        ev["ers_kernel"] = {"ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1), "bytes": nbytes}
+        del src, sh
+    del inp
     torch.cuda.empty_cache()
     return {"progressive_schedule": {"shrink_events": events,
                                      "append_ms_median": round(sorted(app_ms)[len(app_ms) // 2], 4),
