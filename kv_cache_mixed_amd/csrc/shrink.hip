@@ -60,10 +60,15 @@ __global__ __launch_bounds__(256) void shrink_kernel(Geo g) {
                        : g.k_codes + k_tile_offset(g, b, h, tile);
   uint32_t w[IN_WORDS];
   if (!is_v) {
-    // key tile: a flat stream of codes; thread t owns codes [64t, 64t + 64)
-    const uint32_t* in = (const uint32_t*)base + threadIdx.x * IN_WORDS;
+    // key tile: a flat stream of codes; output word o = t + 256k is made of
+    // input words 2o and 2o + 1 (one 8-byte load, consecutive across lanes)
+    const uint2* in = (const uint2*)base;
 #pragma unroll
-    for (int i = 0; i < IN_WORDS; i++) w[i] = in[i];
+    for (int k = 0; k < OUT_WORDS; k++) {
+      const uint2 v = in[threadIdx.x + 256 * k];
+      w[2 * k] = v.x;
+      w[2 * k + 1] = v.y;
+    }
   } else {
     // value tile: output word o = wp*512 + r (r: position inside the word
     // plane, the same function of (channel, lane group) at every width) takes
@@ -95,7 +100,7 @@ __global__ __launch_bounds__(256) void shrink_kernel(Geo g) {
     // 2 input words (2 * 16/B codes each) -> 1 output word
 #pragma unroll
     for (int k = 0; k < OUT_WORDS; k++)
-      out[threadIdx.x * OUT_WORDS + k] =
+      out[threadIdx.x + 256 * k] =
           shift_word<B, M, 16 / B>(w[2 * k]) | (shift_word<B, M, 16 / B>(w[2 * k + 1]) << 16);
   } else {
 #pragma unroll
