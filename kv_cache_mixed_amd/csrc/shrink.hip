@@ -38,10 +38,27 @@ __device__ __forceinline__ uint32_t shift_code(uint32_t x) {
   }
 }
 
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
 // n codes of 2B bits in the low bits of w (LSB first) -> n codes of B bits
 template <int B, int M, int N>
 __device__ __forceinline__ uint32_t shift_word(uint32_t w) {
   constexpr uint32_t MASK = (2 * B == 32) ? 0xffffffffu : ((1u << (2 * B)) - 1u);
+  if constexpr (M == KVQ_SHIFT_ERS && B <= 4 && N == 16 / B) {
+    // ERS in 16-bit halves: C * (X + 2^(b-1)) <= 241 * 263 < 2^16 for b <= 4.
+    // Pair i holds code i in the low half and code N/2 + i in the high half;
+    // the results land at bits B*i and 16 + B*i and are folded to 16 bits.
+    constexpr unsigned short C = (unsigned short)((1u << (2 * B)) - (1u << B) + 1u);
+    constexpr unsigned short CH = (unsigned short)(C * (1u << (B - 1)));
+    uint32_t acc = 0;
+#pragma unroll
+    for (int i = 0; i < N / 2; i++) {
+      const u16x2 x = __builtin_bit_cast(u16x2, (w >> (i * 2 * B)) & (MASK | (MASK << 16)));
+      const u16x2 y = (x * (u16x2){C, C} + (u16x2){CH, CH}) >> (u16x2){3 * B, 3 * B};
+      acc |= __builtin_bit_cast(uint32_t, y) << (i * B);
+    }
+    return (acc & 0xffu) | ((acc >> 8) & 0xff00u);
+  }
   uint32_t o = 0;
 #pragma unroll
   for (int i = 0; i < N; i++) o |= shift_code<B, M>((w >> (i * 2 * B)) & MASK) << (i * B);
