@@ -284,6 +284,48 @@ def test_quantize_edge_groups(pdt):
             assert_stream_bytes_equal(cache, st, 0, h, "edge bits=%d pdt=%d" % (bits, pdt))
 
 
+def _near_tie_values(lo, S, levels, n, rng):
+    """n float32 values whose quotients (x - lo) / S lie on, or a few ulps off,
+    half-integers k + 1/2 (lo and S exact in the parameter dtype)."""
+    k = rng.integers(0, levels, n)
+    x = (np.float32(lo) + (k + 0.5).astype(np.float32) * np.float32(S)).astype(np.float32)
+    steps = rng.integers(-3, 4, n)
+    for i in range(n):
+        for _ in range(abs(int(steps[i]))):
+            x[i] = np.nextafter(x[i], np.float32(np.inf if steps[i] > 0 else -np.inf))
+    return x
+
+
+@pytest.mark.parametrize("pdt", [kvq.F16, kvq.E4M3])
+def test_quantize_near_half_integer_quotients(pdt):
+    """Groups whose code quotients (x - Z')/S' sit exactly on, or within three
+    ulps of, half-integers, with S' = 0.375 (an inexact reciprocal): the codes
+    the kernels form from a reciprocal must equal those of the correctly
+    rounded division, ties to even."""
+    print("case near ties pdt=%d" % pdt, flush=True)
+    rng = np.random.default_rng(321)
+    T, lo, S = 256, -1.5, 0.375
+    for bits in (8, 4, 2):
+        levels = (1 << bits) - 1
+        hi = lo + levels * S
+        k = np.empty((1, 1, T, 128), np.float32)
+        v = np.empty((1, 1, T, 128), np.float32)
+        for t in range(T):                          # value groups: one token
+            v[0, 0, t, 0], v[0, 0, t, 1] = lo, hi
+            v[0, 0, t, 2:] = _near_tie_values(lo, S, levels, 126, rng)
+        for c in range(128):                        # key groups: one channel of a tile
+            for g in range(T // 128):
+                k[0, 0, 128 * g, c], k[0, 0, 128 * g + 1, c] = lo, hi
+                k[0, 0, 128 * g + 2:128 * g + 128, c] = _near_tie_values(lo, S, levels, 126, rng)
+        q = (v[0, 0, :, 2:] - np.float32(lo)) / np.float32(S)
+        assert np.mean(q == np.floor(q) + 0.5) > 0.05   # the construction hits exact ties
+        cache = kvq.PackedCache(1, 1, T, bits, bits, pdt)
+        cache.quantize(to_dev(k, torch), to_dev(v, torch), 0)
+        torch.cuda.synchronize()
+        st = oracle_stream(dict(k=k, v=v), 0, 0, bits, bits, pdt)
+        assert_stream_bytes_equal(cache, st, 0, 0, "near ties bits=%d pdt=%d" % (bits, pdt))
+
+
 # ---------------------------------------------------------------------------
 # decode with a residual segment of unquantized tokens
 # ---------------------------------------------------------------------------
