@@ -588,12 +588,17 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // (batch, kv head, head) in order), valid while cn < NS * G and the row is
   // inside q.  The query loads go out before the first tile's loads, so they
   // are not queued behind them when every workgroup starts at once.
+  // a negative softmax scale is folded into the staged query (bf16 sign
+  // flips are exact), so ak >= 0 and a lane's largest logit always comes from
+  // its largest raw sum
+  const uint32_t qflip = (a.sl2 < 0.0f) ? 0x80008000u : 0u;
   if constexpr (!MIXED) {
     // uniform widths: slot = channel, one 16-byte load per thread
     const int cn = threadIdx.x >> 4, part = threadIdx.x & 15;
     const int64_t row = (int64_t)grp * NS * G + cn;
     u32x4 v = (u32x4){0u, 0u, 0u, 0u};
     if (cn < NS * G && row < (int64_t)BH * G) v = *(const u32x4*)(a.q + row * 128 + 8 * part);
+    v ^= (u32x4)qflip;
     if (q0 < t_count) load(b0, q0, 0);
     *(u32x4*)&qs[cn][8 * part] = v;
   } else {
@@ -608,7 +613,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       qv[r] = 0;
       if (cs < NS && cbh < BH) {
         const int chh = cbh % g.H;
-        qv[r] = a.q[((int64_t)grp * NS * G + cn) * 128 + g.slot_chan[chh * 128 + j]];
+        qv[r] = a.q[((int64_t)grp * NS * G + cn) * 128 + g.slot_chan[chh * 128 + j]] ^ (uint16_t)qflip;
       }
     }
     if (q0 < t_count) load(b0, q0, 0);
@@ -719,8 +724,8 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       my_lds[(((f >> 2) * 2 + 0) * 64 + lane) * 4 + (f & 3)] = hi;
       my_lds[(((f >> 2) * 2 + 1) * 64 + lane) * 4 + (f & 3)] = lo;
     }
-    ak = a.sl2 * exp2i(24 - KH + eqs);
-    bk0 = a.sl2 * beta;
+    ak = __builtin_fabsf(a.sl2) * exp2i(24 - KH + eqs);
+    bk0 = __builtin_fabsf(a.sl2) * beta;
   };
 
   // compute sub-tile sub of the chunk's tile ti from bf; with the two-ahead
@@ -787,54 +792,58 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
       for (int i = 0; i < 4; i++) lv[4 * jj + i] = v[i];
     }
-    // the largest logit comes from the largest raw sum when ak >= 0 (ak has
-    // the sign of the softmax scale) and from the smallest otherwise; fma is
-    // monotone in v
+    // the lane's largest logit (ak >= 0: from its largest raw sum)
     float vx = lv[0];
-    if (a.sl2 >= 0.0f) {
 #pragma unroll
-      for (int i = 1; i < TPS; i++) vx = fmaxf(vx, lv[i]);
-    } else {
-#pragma unroll
-      for (int i = 1; i < TPS; i++) vx = fminf(vx, lv[i]);
-    }
-    const float tmax = wave_max16x4(fmaf(ak, vx, bk0));
+    for (int i = 1; i < TPS; i++) vx = fmaxf(vx, lv[i]);
+    const float lmax = fmaf(ak, vx, bk0);
     // value parameters of the sub-tile; binary16 ones stay raw and are read
-    // by mixed-precision fmas
+    // by mixed-precision fmas.  smx: the lane's largest value scale as a
+    // binary32 bit pattern (scales are >= +0, so patterns order like values)
     constexpr bool MIX = (PDT == KVQ_F16);
     uint32_t rvs[PWV], rvz[PWV];
     float vs[MIX ? 1 : TPS], vz[MIX ? 1 : TPS];
-    int ev;
+    uint32_t smx;
     if constexpr (MIX) {
 #pragma unroll
       for (int w = 0; w < PWV; w++) { rvs[w] = bf.vs[w]; rvz[w] = bf.vz[w]; }
-      // scales are >= +0, so their binary16 patterns order like the values
       uint32_t m2 = rvs[0];
 #pragma unroll
       for (int w = 1; w < PWV; w++) m2 = pk_max_u16(m2, rvs[w]);
-      const uint32_t mh = wave_maxu16x4(max(m2 & 0xffffu, m2 >> 16));
-      ev = expo((float)__builtin_bit_cast(_Float16, (uint16_t)mh));
+      smx = f2u((float)__builtin_bit_cast(_Float16, (uint16_t)max(m2 & 0xffffu, m2 >> 16)));
     } else {
       praw_unpack<PDT, TPS>(bf.vs, vs);
       praw_unpack<PDT, TPS>(bf.vz, vz);
-      uint32_t vsmax = 0;
+      smx = 0;
 #pragma unroll
-      for (int i = 0; i < TPS; i++) vsmax = max(vsmax, f2u(vs[i]));   // scales are >= +0
-      ev = expo(u2f(wave_maxu16x4(vsmax)));
+      for (int i = 0; i < TPS; i++) smx = max(smx, f2u(vs[i]));
     }
     load_p(bf, ti2, sub2);
-    const float m_new = (tmax > m_run + (float)TAU) ? tmax : m_run;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // v_exp_f32, 0 for -inf
-    const int e_new = max(e_run, ev);
-    // the probabilities carry 2^ps, ps = VH - e_new (capped so the scaled
-    // sums stay finite), which keeps the value operand below 2^15
-    const int ps_old = min(VH - e_run, PSMAX), ps_new = min(VH - e_new, PSMAX);
-    const float rescale = alpha * exp2i(ps_new - ps_old);
-    m_run = m_new;
-    e_run = e_new;
+    // A column's reference max moves only when one of its logits exceeds it
+    // by more than TAU, and its value-scale exponent e_run only when a larger
+    // scale arrives.  Both need the reductions over the four lane groups, so
+    // they (and the rescale of the running sums and accumulators) run only
+    // when some lane of the wave sees such a logit or scale.
+    if (__builtin_amdgcn_ballot_w64(lmax > m_run + (float)TAU || expo(u2f(smx)) > e_run) != 0) {
+      const float tmax = wave_max16x4(lmax);
+      const int ev = expo(u2f(wave_maxu16x4(smx)));
+      const float m_new = (tmax > m_run + (float)TAU) ? tmax : m_run;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // v_exp_f32, 0 for -inf
+      const int e_new = max(e_run, ev);
+      // the probabilities carry 2^ps, ps = VH - e_run (capped so the scaled
+      // sums stay finite), which keeps the value operand below 2^15
+      const int ps_old = min(VH - e_run, PSMAX), ps_new = min(VH - e_new, PSMAX);
+      const float rescale = alpha * exp2i(ps_new - ps_old);
+      m_run = m_new;
+      e_run = e_new;
+      l_run *= rescale;
+      z_run *= rescale;
+#pragma unroll
+      for (int cb = 0; cb < 8; cb++) acc_o[cb] *= rescale;
+    }
     // e''(i) = e(i) * 2^ps * 2^W(i) straight from the exponent; the running
     // sums l_run, z_run are kept in units of 2^ps
-    const float c0 = bk0 - m_new + (float)ps_new;
+    const float c0 = bk0 - m_run + (float)min(VH - e_run, PSMAX);
     float p[TPS];
     float lsum = 0.0f;
     float zc[10];
@@ -857,12 +866,8 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
     for (int k = 1; k < 10; k++)
       if (class_used<VB, FVS, TPS>(k)) zsum = fmaf(zc[k], exp2i(-class_w<VB>(k)), zsum);
-    l_run = fmaf(l_run, rescale, lsum);
-    z_run = fmaf(z_run, rescale, zsum);
-    if (__builtin_amdgcn_ballot_w64(rescale != 1.0f) != 0) {
-#pragma unroll
-      for (int cb = 0; cb < 8; cb++) acc_o[cb] *= rescale;
-    }
+    l_run += lsum;
+    z_run += zsum;
 
     // ---- P operand (split hi/lo) and PV; every sub-tile has the field
     // layout of sub-tile 0, shifted by WVS words and TPS tokens
