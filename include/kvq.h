@@ -320,6 +320,44 @@ kvq_status kvq_allocate_bits(int32_t n_blocks, int32_t n_choices, const double *
                              const int64_t *bytes, int64_t budget_bytes, int32_t *choice,
                              double *cost);
 
+/* ------------------------------------------------------------------------
+ * Pair-granular key widths ([PNMIX] abstract: the quantization error of a
+ * RoPE channel pair moves the attention logit in proportion to the product of
+ * the query's and the key's norms over that pair, so the pairs with the
+ * largest query-key pair-norm products get the higher widths, chosen once
+ * from prefill statistics and kept through the decode).  Pair p (0 <= p < 64)
+ * of a head is channels (p, p + 64), the rotate-half RoPE pairing.
+ *
+ * kvq_pair_norms: adds to out[h / group][p] (device binary32
+ * [n_heads / group][64]) the sum over b < batch, over the heads h of each
+ * group of `group` consecutive heads and over t < n_tokens of
+ *   sqrt(x[b][h][t][p]^2 + x[b][h][t][p + 64]^2)
+ * for x device [batch][n_heads][n_tokens][128] in in_dtype (KVQ_F32 or
+ * KVQ_BF16), element strides (b, h, t) as given (token stride >= 128) and
+ * unit channel stride.  Keys: group = 1 (one row per kv head); queries:
+ * group = G folds the query heads of each kv head.  out is accumulated into
+ * (zero it before the first call; calls over successive prefill chunks add
+ * up), with device atomics, so the order of the binary32 sums is
+ * unspecified.  With n_tokens == 0 nothing is read or enqueued (x may be
+ * NULL).  Enqueued on `stream`; KVQ_EINVAL for bad arguments (nothing
+ * enqueued), KVQ_EHIP if the launch fails. */
+kvq_status kvq_pair_norms(const void *x, kvq_dtype in_dtype, const int64_t strides[3], int32_t batch,
+                          int32_t n_heads, int32_t n_tokens, int32_t group, float *out,
+                          hipStream_t stream);
+
+/* kvq_pair_slot_map (host): the mixed key tile's slot order
+ * (k_slot_chan, see the mixed layout above) from per-pair saliency scores,
+ * score host [n_kv_heads][64] finite binary32 (e.g. the product of the
+ * prefill queries' and keys' kvq_pair_norms).  Per kv head the pairs are
+ * ranked by score, descending, equal scores by ascending pair index; the
+ * first 4 pairs fill the eight 4-bit slots, the next 4 the eight 3-bit slots,
+ * the last 4 the eight 1-bit slots and the other 52 the 104 2-bit slots, so
+ * both channels of a pair share a width; inside each class the channels are
+ * in ascending order.  slot_chan: host [n_kv_heads][128] output, written only
+ * on KVQ_OK; KVQ_EINVAL for NULL pointers, n_kv_heads < 1 or a score that is
+ * not finite. */
+kvq_status kvq_pair_slot_map(const float *score, int32_t n_kv_heads, int16_t *slot_chan);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,7 +52,7 @@ _lib = None
 EXPORTS = ["kvq_strerror", "kvq_tile_bytes", "kvq_cache_bytes", "kvq_quantize", "kvq_shrink",
            "kvq_shrink_shift", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_decode_attn_residual",
            "kvq_pool_create", "kvq_pool_destroy", "kvq_pool_used_bytes", "kvq_pool_high_water",
-           "kvq_append", "kvq_allocate_bits"]
+           "kvq_append", "kvq_allocate_bits", "kvq_pair_norms", "kvq_pair_slot_map"]
 
 
 def load():
@@ -86,6 +86,10 @@ def load():
                                            i32, vp, vp, ctypes.c_size_t, vp]
     L.kvq_allocate_bits.restype = ctypes.c_int
     L.kvq_allocate_bits.argtypes = [i32, i32, vp, vp, i64, vp, ctypes.POINTER(ctypes.c_double)]
+    L.kvq_pair_norms.restype = ctypes.c_int
+    L.kvq_pair_norms.argtypes = [vp, ctypes.c_int, ctypes.POINTER(ctypes.c_int64), i32, i32, i32, i32, vp, vp]
+    L.kvq_pair_slot_map.restype = ctypes.c_int
+    L.kvq_pair_slot_map.argtypes = [vp, i32, vp]
     L.kvq_pool_create.restype = ctypes.c_int
     L.kvq_pool_create.argtypes = [P, i64, vp, vp, ctypes.POINTER(vp)]
     L.kvq_pool_destroy.restype = None
@@ -124,6 +128,32 @@ def _strides3(t):
     """(b, h, t) element strides of a [B][H][T][128] tensor with unit channel stride."""
     assert t.dim() == 4 and t.shape[-1] == 128 and t.stride(-1) == 1
     return (ctypes.c_int64 * 3)(t.stride(0), t.stride(1), t.stride(2))
+
+
+def pair_norms(x, group=1, out=None, stream=None):
+    """kvq_pair_norms: x [B][H][T][128] float32 / bfloat16 device tensor with
+    unit channel stride -> out [H // group][64] float32 (added to when given,
+    else a fresh zero tensor)."""
+    import torch
+    in_dtype = {torch.float32: F32, torch.bfloat16: BF16}[x.dtype]
+    B, H, T, _ = x.shape
+    if out is None:
+        out = torch.zeros((H // group, 64), dtype=torch.float32, device=x.device)
+    assert out.dtype == torch.float32 and out.is_contiguous() and out.shape == (H // group, 64)
+    st = load().kvq_pair_norms(_ptr(x), in_dtype, _strides3(x), B, H, T, group, _ptr(out), _stream_ptr(stream))
+    _check(st, "kvq_pair_norms")
+    return out
+
+
+def pair_slot_map(score):
+    """kvq_pair_slot_map: score [Hkv][64] (host, float32) -> slot_chan
+    [Hkv][128] int16 (the mixed key tile's slot order)."""
+    import numpy as np
+    s = np.ascontiguousarray(score, dtype=np.float32)
+    assert s.ndim == 2 and s.shape[1] == 64
+    out = np.empty((s.shape[0], 128), dtype=np.int16)
+    _check(load().kvq_pair_slot_map(s.ctypes.data, s.shape[0], out.ctypes.data), "kvq_pair_slot_map")
+    return out
 
 
 def allocate_bits(sens, nbytes, budget_bytes):

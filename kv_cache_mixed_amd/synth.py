@@ -14,6 +14,12 @@ Recipes (stand-ins for real model activations; no dataset or weights are used):
            head a seeded permutation picks 8 channels at 4 bits, 8 at 3 bits,
            8 at 1 bit, the other 104 at 2 bits; K ~ N(0,1) with the 3/4-bit
            channels x6 and the 1-bit channels x0.2, no RoPE; V ~ N(0,1).
+  pairs    the mixed shape with RoPE-pair saliency: per kv head a seeded
+           permutation of the 64 RoPE pairs scales both channels of 4 pairs x8
+           and of 4 more x4, and of 4 pairs x0.2; K ~ N(0,1) otherwise, then
+           RoPE (which keeps every pair's norm); V ~ N(0,1); the decode query
+           and 64 prefill query tokens per head ~ N(0,1) (the prefill queries
+           with RoPE at positions 0..63).
 RoPE here is rotate-half over channel pairs (i, i+64), theta_i = 1e4^(-2i/128),
 angle = position * theta_i, evaluated in float64 and stored as float32.
 """
@@ -179,3 +185,68 @@ def mixed_layer_device(B: int, Hkv: int, Hq: int, T: int, seed: int, device):
     v = torch.randn((B, Hkv, T, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
     q = torch.randn((B, Hq, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
     return dict(k=k, v=v, q=q.to(torch.bfloat16), slot_chan=slot_chan)
+
+
+PAIR_SCALES = ((4, 8.0), (4, 4.0), (4, 0.2))   # (pairs, factor) after the seeded permutation
+
+
+def pair_scales(Hkv: int, seed: int) -> np.ndarray:
+    """[Hkv][64] per-pair key scale of the pairs recipe (1 for the unscaled pairs)."""
+    rng = np.random.default_rng(seed)
+    sc = np.ones((Hkv, 64), dtype=np.float32)
+    for h in range(Hkv):
+        perm = rng.permutation(64)
+        i = 0
+        for n, f in PAIR_SCALES:
+            sc[h, perm[i:i + n]] = f
+            i += n
+    return sc
+
+
+def pair_layer(B: int, Hkv: int, Hq: int, T: int, seed: int, Tq: int = 64):
+    """RoPE-pair saliency generator.  -> dict(k, v [B,Hkv,T,128] f32,
+    q_bf16 [B,Hq,128] uint16, q_prefill [B,Hq,Tq,128] f32, pair_scale [Hkv,64])"""
+    sc = pair_scales(Hkv, seed + 1)
+    rng = np.random.default_rng(seed)
+    k = rng.standard_normal((B, Hkv, T, HEAD_DIM), dtype=np.float32)
+    full = np.concatenate([sc, sc], axis=1)                      # both channels of a pair
+    k *= full[None, :, None, :]
+    for b in range(B):
+        for h in range(Hkv):
+            k[b, h] = apply_rope(k[b, h], 0)
+    v = rng.standard_normal((B, Hkv, T, HEAD_DIM), dtype=np.float32)
+    q = rng.standard_normal((B, Hq, HEAD_DIM), dtype=np.float32)
+    qp = rng.standard_normal((B, Hq, Tq, HEAD_DIM), dtype=np.float32)
+    for b in range(B):
+        for h in range(Hq):
+            qp[b, h] = apply_rope(qp[b, h], 0)
+    return dict(k=k, v=v, q_bf16=to_bf16_bits(q), q_prefill=qp, pair_scale=sc)
+
+
+def pair_layer_device(B: int, Hkv: int, Hq: int, T: int, seed: int, device, Tq: int = 64):
+    """Same recipe as pair_layer() drawn with torch on a device (pair scales from
+    the same seeded permutation; the normal draws differ from numpy's stream)."""
+    import torch
+    sc = pair_scales(Hkv, seed + 1)
+    g = torch.Generator(device=device)
+    g.manual_seed(seed)
+    k = torch.randn((B, Hkv, T, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    full = torch.as_tensor(np.concatenate([sc, sc], axis=1), device=device)
+    k *= full[None, :, None, :]
+    inv = torch.tensor(rope_inv_freq(), device=device, dtype=torch.float64)
+
+    def rope(x):
+        pos = torch.arange(x.shape[-2], device=device, dtype=torch.float64)
+        ang = pos[:, None] * inv[None, :]
+        c, s = torch.cos(ang), torch.sin(ang)
+        for b in range(x.shape[0]):
+            a = x[b, :, :, :64].double()
+            bb = x[b, :, :, 64:].double()
+            x[b, :, :, :64] = (a * c - bb * s).float()
+            x[b, :, :, 64:] = (a * s + bb * c).float()
+    rope(k)
+    v = torch.randn((B, Hkv, T, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    q = torch.randn((B, Hq, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    qp = torch.randn((B, Hq, Tq, HEAD_DIM), generator=g, device=device, dtype=torch.float32)
+    rope(qp)
+    return dict(k=k, v=v, q=q.to(torch.bfloat16), q_prefill=qp, pair_scale=sc)

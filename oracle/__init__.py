@@ -396,3 +396,45 @@ def allocate_bits_bruteforce(sens, nbytes, budget_bytes):
             best, best_cost = cv, c
     return (None, None) if best is None else (list(best), best_cost)
 
+
+
+# --------------------------------------------------------------------------
+# pair-granular key widths ("PN-Mix: Pair-Norm Guided Mixed-Precision Key
+# Cache Quantization ...", abstract: RoPE channel pairs ranked by the product
+# of query and key pair norms; the salient pairs get the higher widths)
+# --------------------------------------------------------------------------
+def pair_norms(x: np.ndarray, group: int = 1) -> np.ndarray:
+    """x [B][H][T][128] -> [H // group][64]: for pair p = channels (p, p + 64)
+    (rotate-half RoPE pairing), the sum over batch, tokens and the `group`
+    consecutive heads of each row of the Euclidean norm of the pair, in
+    binary64."""
+    x = np.asarray(x, dtype=np.float64)
+    B, H, T, D = x.shape
+    assert D == 128 and H % group == 0
+    norms = np.sqrt(x[..., :64] ** 2 + x[..., 64:] ** 2)        # [B][H][T][64]
+    per_head = norms.sum(axis=(0, 2))                            # [H][64]
+    return per_head.reshape(H // group, group, 64).sum(axis=1)
+
+
+def pair_slot_map(score: np.ndarray) -> np.ndarray:
+    """score [Hkv][64] -> slot_chan [Hkv][128] int16.  Per kv head, the pairs
+    in order of decreasing score (ties: the lower pair index first); the four
+    most salient pairs take the 4-bit class, the next four the 3-bit class, the
+    four least salient the 1-bit class and the rest the 2-bit class, both
+    channels of a pair together.  Slots follow the mixed key layout: 0..7 the
+    4-bit channels, 8, 10, .., 22 the 3-bit ones, 9, 11, .., 23 the 1-bit ones,
+    24..127 the 2-bit ones, ascending channel order inside each class."""
+    score = np.asarray(score, dtype=np.float32)
+    out = np.empty((score.shape[0], 128), dtype=np.int16)
+    for h in range(score.shape[0]):
+        order = sorted(range(64), key=lambda p: (-float(score[h, p]), p))
+        classes = {4: [], 3: [], 1: [], 2: []}
+        for r, p in enumerate(order):
+            width = 4 if r < 4 else (3 if r < 8 else (1 if r >= 60 else 2))
+            classes[width] += [p, p + 64]
+        c4, c3, c1, c2 = (sorted(classes[w]) for w in (4, 3, 1, 2))
+        out[h, 0:8] = c4
+        out[h, 8:24:2] = c3
+        out[h, 9:24:2] = c1
+        out[h, 24:] = c2
+    return out
