@@ -131,6 +131,44 @@ def mixed_128k_rows(torch, kvq, synth, dev, scale):
                                   "note": "4 cache copies rotated (%d MB each)" % (alg // 1000000)}}
 
 
+def pn_mix_rows(torch, kvq, synth, dev, scale):
+    """Pair-granular key widths on the Llama-3.1-8B-shaped 128K layer (pairs
+    recipe): RoPE pair norms of the prefill keys (the whole context) and
+    queries, the slot map, and decode with that map (mixed keys, 2-bit values,
+    e4m3 S/Z; four cache copies rotated)."""
+    import numpy as np
+    B, H, Hq, T = 1, 8, 32, 131072
+    G = Hq // H
+    inp = synth.pair_layer_device(B, H, Hq, T, seed=6, device=dev)
+    kn = torch.zeros((H, 64), dtype=torch.float32, device=dev)
+    n_ms, _ = time_events(torch, lambda i: kvq.pair_norms(inp["k"], 1, out=kn.zero_()), 10, 2)
+    n_bytes = B * H * T * 128 * 4
+    qn = kvq.pair_norms(inp["q_prefill"], G)
+    score = (qn * kvq.pair_norms(inp["k"], 1)).cpu().numpy()
+    t0 = time.perf_counter()
+    slot_chan = kvq.pair_slot_map(score)
+    map_us = (time.perf_counter() - t0) * 1e6
+    # the recipe's salient pairs (x8, x4) must hold the 4- and 3-bit slots
+    big = np.flatnonzero(inp["pair_scale"][0] >= 4.0)
+    assert sorted(slot_chan[0, :8].tolist() + slot_chan[0, 8:24:2].tolist()) == sorted(
+        np.concatenate([big, big + 64]).tolist())
+    caches = [kvq.PackedCache(B, H, T, kvq.KMIXED, 2, kvq.E4M3, slot_chan=slot_chan, device=dev)
+              for _ in range(4)]
+    for c in caches:
+        c.quantize(inp["k"], inp["v"], 0)
+    q = inp["q"]
+    del inp
+    torch.cuda.empty_cache()
+    outs = [torch.empty((B, Hq, 128), dtype=torch.float32, device=dev) for _ in caches]
+    d_ms, _ = time_events(torch, lambda i: caches[i % 4].decode_attn(q, scale, out=outs[i % 4]), 40, 4)
+    alg = decode_bytes(B, H, Hq, T, 0, 2, 1)
+    return {"pn_mix_pairs_128k": {
+        "pair_norms_ms": round(n_ms, 4), "pair_norms_GB/s": round(n_bytes / n_ms / 1e6, 1),
+        "slot_map_us": round(map_us, 1),
+        "decode_ms": round(d_ms, 4), "decode_GB/s": round(alg / d_ms / 1e6, 1),
+        "note": "keys' pair norms over the 128K context (fp32 in); decode with the pair-granular map"}}
+
+
 def progressive_rows(torch, kvq, synth, dev, scale):
     """Progressive schedule: 128-token groups appended from 16 bits under a
     128 MiB budget (B=8, Hkv=4, Hq=28) up to 32768 tokens.  Times every append
@@ -485,6 +523,7 @@ def main():
             "note": "single cache copy; residual bf16 [16][4][128][128]"}
         del rk, rv
         rows.update(mixed_128k_rows(torch, kvq, synth, dev, scale))
+        rows.update(pn_mix_rows(torch, kvq, synth, dev, scale))
         rows.update(progressive_rows(torch, kvq, synth, dev, scale))
         rows.update(halving_rule_rows(torch, kvq, synth, dev, scale))
         rows.update(qwen32b_step_rows(torch, kvq, synth, dev, scale))
