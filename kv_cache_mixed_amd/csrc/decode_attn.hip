@@ -207,6 +207,11 @@ struct DecodeArgs {
                       // entry, left zero (chunk combine inside the kernel)
   int fused;          // chunks combined inside the kernel (1) or by a second kernel (0)
   float sl2;          // softmax_scale * log2(e)
+  // residual segment run by extra workgroups of this launch (grid rows past
+  // n_groups), n_res blocks of 32 tokens per stream, partial slots
+  // n_chunks .. n_chunks + n_res - 1; n_res = 0: none (or a separate launch)
+  ResArgs res;
+  int res_dtype, n_res;
 };
 
 // Operand registers per 32 codes and row words per lane for width B.
@@ -395,6 +400,153 @@ constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
 // one 4-register group per k-step, computed once per tile.  Lanes of columns
 // that serve no head have q = 0, so their operands are harmless and never
 // masked.
+// Residual segment: R tokens per stream that are not packed (the first and
+// recent tokens the caller keeps at 16-bit or full precision), attended in
+// binary32.  Workgroup (rc, bh) takes tokens [32 rc, 32 rc + 32) of stream bh
+// and emits one more partial (m, l, o) per head in slot slot0 + rc -- or, when
+// it is the only partial of the stream, the normalised row straight into
+// `out`.  Every thread issues all its 16-byte loads (query, keys, values)
+// before the first use, so a workgroup costs one memory round trip; logits,
+// softmax and the value product then run out of LDS, the values taking the
+// keys' place once the logits are formed (27 KB).  The same block runs as its
+// own kernel or as extra workgroups of a decode launch (in the decode
+// kernel's LDS), where the dispatcher starts it as decode workgroups retire.
+template <int IN>
+__device__ __forceinline__ float res_elem(uint4 w, int j) {
+  if constexpr (IN == KVQ_F32) {
+    return u2f(j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w);
+  } else {
+    const uint32_t x = (j >> 1) == 0 ? w.x : (j >> 1) == 1 ? w.y : (j >> 1) == 2 ? w.z : w.w;
+    const uint32_t hbits = (j & 1) ? (x >> 16) : (x & 0xffffu);
+    if constexpr (IN == KVQ_F16) return (float)__builtin_bit_cast(_Float16, (uint16_t)hbits);
+    else return bf16_bits_to_f32(hbits);
+  }
+}
+
+// LDS floats of a residual block: query [16][129], keys then values
+// [32][129], weights [32][16], per-head (max, sum) [16][2]
+constexpr int RES_LDS_FLOATS = 16 * 129 + KVQ_RES_CHUNK * 129 + KVQ_RES_CHUNK * 16 + 32;
+
+template <int IN>
+__device__ __forceinline__ void residual_block(const ResArgs& r, const uint16_t* __restrict__ q, int H, int G,
+                                               float sl2, float* __restrict__ part_ml,
+                                               float* __restrict__ part_o, int n_slots, int slot0,
+                                               float* __restrict__ out, int rc, int bh, float* smem) {
+  constexpr int RC = KVQ_RES_CHUNK;
+  constexpr int VW = IN == KVQ_F32 ? 4 : 8;                 // elements per 16-byte load
+  constexpr int NV = RC * 128 / VW / 256;                   // loads per thread per operand
+  static_assert(RC == 32 && NV >= 1, "one token per half wave in the softmax");
+  float (*qv)[129] = (float (*)[129])smem;                  // padded rows: conflict-free across tokens
+  float (*kv)[129] = (float (*)[129])(smem + 16 * 129);     // keys, then values
+  float (*sp)[16] = (float (*)[16])(smem + 16 * 129 + RC * 129);   // [token][head]: logits, then weights
+  float (*sm)[2] = (float (*)[2])(smem + 16 * 129 + RC * 129 + RC * 16);   // per head: max, sum
+  const int tid = threadIdx.x;
+  const int b = bh / H, h = bh - (bh / H) * H;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int t0 = rc * RC, n = min(RC, r.R - t0);
+  const int64_t kb = (int64_t)b * r.ks[0] + (int64_t)h * r.ks[1] + (int64_t)t0 * r.ks[2];
+  const int64_t vb = (int64_t)b * r.vs[0] + (int64_t)h * r.vs[1] + (int64_t)t0 * r.vs[2];
+  const int esz = IN == KVQ_F32 ? 4 : 2;
+  uint4 qw = make_uint4(0u, 0u, 0u, 0u);
+  if (tid < G * 16) qw = ((const uint4*)(q + ((int64_t)b * H * G + (int64_t)h * G) * 128))[tid];
+  // rows past n repeat row n - 1 (in bounds, never used): the loads need no branch
+  uint4 kw[NV], vw[NV];
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int j = tid + 256 * i, t = min(j / (128 / VW), n - 1), c = (j % (128 / VW)) * VW;
+    kw[i] = *(const uint4*)((const uint8_t*)r.k + (kb + (int64_t)t * r.ks[2] + c) * esz);
+    vw[i] = *(const uint4*)((const uint8_t*)r.v + (vb + (int64_t)t * r.vs[2] + c) * esz);
+  }
+  if (tid < G * 16) {
+#pragma unroll
+    for (int e = 0; e < 8; e++) qv[tid >> 4][(tid & 15) * 8 + e] = res_elem<KVQ_BF16>(qw, e);
+  }
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int j = tid + 256 * i, t = j / (128 / VW), c = (j % (128 / VW)) * VW;
+#pragma unroll
+    for (int e = 0; e < VW; e++) kv[t][c + e] = res_elem<IN>(kw[i], e);
+  }
+  __syncthreads();
+  // logits: thread i takes head i / n, token i % n
+  for (int i = tid; i < n * G; i += 256) {
+    const int hh = i / n, t = i - (i / n) * n;
+    float d = 0.0f;
+#pragma unroll 16
+    for (int c = 0; c < 128; c++) d = fmaf(qv[hh][c], kv[t][c], d);
+    sp[t][hh] = d * sl2;
+  }
+  __syncthreads();
+  // the values take the keys' place (read again only after the next barrier)
+#pragma unroll
+  for (int i = 0; i < NV; i++) {
+    const int j = tid + 256 * i, t = j / (128 / VW), c = (j % (128 / VW)) * VW;
+#pragma unroll
+    for (int e = 0; e < VW; e++) kv[t][c + e] = res_elem<IN>(vw[i], e);
+  }
+  // softmax: each wave takes two heads at a time, one per half wave (lane & 31 = token)
+  for (int hp = wave; 2 * hp < G; hp += 4) {
+    const int hh = 2 * hp + (lane >> 5), t = lane & 31;
+    const bool ok = hh < G && t < n;
+    const float s = ok ? sp[t][hh] : -INFINITY;
+    float m = s;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
+    const float e = ok ? exp2f(s - m) : 0.0f;
+    float l = e;
+#pragma unroll
+    for (int o = 16; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
+    if (hh < G) {
+      sp[t][hh] = e;                              // 0 for the rows past n
+      if (t == 0) { sm[hh][0] = m; sm[hh][1] = l; }
+    }
+  }
+  __syncthreads();
+  // values: thread takes channel tid & 127 and heads 8 hb .. 8 hb + 7 (hb =
+  // tid >> 7, uniform per wave); the sums of heads >= G are never stored
+  const int c = tid & 127, hb = tid >> 7;
+  if (8 * hb >= G) return;
+  float acc[8];
+#pragma unroll
+  for (int j = 0; j < 8; j++) acc[j] = 0.0f;
+#pragma unroll 4
+  for (int t = 0; t < n; t++) {
+    const float x = kv[t][c];
+    const float4 w0 = *(const float4*)&sp[t][8 * hb];
+    const float4 w1 = *(const float4*)&sp[t][8 * hb + 4];
+    acc[0] = fmaf(w0.x, x, acc[0]);
+    acc[1] = fmaf(w0.y, x, acc[1]);
+    acc[2] = fmaf(w0.z, x, acc[2]);
+    acc[3] = fmaf(w0.w, x, acc[3]);
+    acc[4] = fmaf(w1.x, x, acc[4]);
+    acc[5] = fmaf(w1.y, x, acc[5]);
+    acc[6] = fmaf(w1.z, x, acc[6]);
+    acc[7] = fmaf(w1.w, x, acc[7]);
+  }
+#pragma unroll
+  for (int j = 0; j < 8; j++) {
+    const int hh = 8 * hb + j;
+    if (hh >= G) break;
+    if (out) {
+      out[((int64_t)b * H * G + (int64_t)h * G + hh) * 128 + c] = acc[j] / sm[hh][1];
+    } else {
+      const int64_t row = ((int64_t)bh * n_slots + slot0 + rc) * G + hh;
+      if (c == 0) { part_ml[2 * row] = sm[hh][0]; part_ml[2 * row + 1] = sm[hh][1]; }
+      part_o[row * 128 + c] = acc[j];
+    }
+  }
+}
+
+template <int IN>
+__global__ __launch_bounds__(256) void decode_residual_kernel(ResArgs r, const uint16_t* __restrict__ q,
+                                                              int H, int G, float sl2,
+                                                              float* __restrict__ part_ml,
+                                                              float* __restrict__ part_o, int n_slots,
+                                                              int slot0, float* __restrict__ out) {
+  __shared__ __attribute__((aligned(16))) float smem[RES_LDS_FLOATS];
+  residual_block<IN>(r, q, H, G, sl2, part_ml, part_o, n_slots, slot0, out, blockIdx.x, blockIdx.y, smem);
+}
+
 template <int KB, int VB, int PDT, int NS>
 __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kernel(DecodeArgs a) {
   constexpr bool MIXED = (KB == 0);
@@ -437,6 +589,25 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   __shared__ __attribute__((aligned(16))) uint16_t qs[16][128];
 
   const Geo& g = a.g;
+  if (blockIdx.y >= (unsigned)a.n_groups) {
+    // a residual workgroup: block r of the grid rows past the stream groups
+    const int r = (blockIdx.y - a.n_groups) * gridDim.x + blockIdx.x;
+    const int BHr = g.B * g.H;
+    if (r >= a.n_res * BHr) return;
+    static_assert(sizeof(lds) >= RES_LDS_FLOATS * sizeof(float), "residual block fits the decode LDS");
+    float* smem = (float*)&lds[0][0];
+    const int rc = r % a.n_res, bh = r / a.n_res;
+    if (a.res_dtype == KVQ_F32)
+      residual_block<KVQ_F32>(a.res, a.q, g.H, a.G, a.sl2, a.part_ml, a.part_o, a.n_slots, a.n_chunks, nullptr,
+                              rc, bh, smem);
+    else if (a.res_dtype == KVQ_F16)
+      residual_block<KVQ_F16>(a.res, a.q, g.H, a.G, a.sl2, a.part_ml, a.part_o, a.n_slots, a.n_chunks, nullptr,
+                              rc, bh, smem);
+    else
+      residual_block<KVQ_BF16>(a.res, a.q, g.H, a.G, a.sl2, a.part_ml, a.part_o, a.n_slots, a.n_chunks,
+                               nullptr, rc, bh, smem);
+    return;
+  }
   // the wave index is uniform: keep it (and everything derived) in SGPRs
   const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int n = lane & 15, lg = lane >> 4;
@@ -1231,135 +1402,6 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
   *(float2*)(out + ((int64_t)bo * H * G + (int64_t)ho * G + hh) * 128 + 2 * lane) = make_float2(n0 * inv, n1 * inv);
 }
 
-// Residual segment: R tokens per stream that are not packed (the first and
-// recent tokens the caller keeps at 16-bit or full precision), attended in
-// binary32.  Workgroup (rc, bh) takes tokens [32 rc, 32 rc + 32) of stream bh
-// and emits one more partial (m, l, o) per head in slot slot0 + rc -- or, when
-// it is the only partial of the stream, the normalised row straight into
-// `out`.  Every thread issues all its 16-byte loads (query, keys, values)
-// before the first use, so a workgroup costs one memory round trip; logits,
-// softmax and the value product then run out of LDS.  The LDS footprint
-// (~43 KB) leaves room to run beside two decode workgroups on a CU.
-template <int IN>
-__device__ __forceinline__ float res_elem(uint4 w, int j) {
-  if constexpr (IN == KVQ_F32) {
-    return u2f(j == 0 ? w.x : j == 1 ? w.y : j == 2 ? w.z : w.w);
-  } else {
-    const uint32_t x = (j >> 1) == 0 ? w.x : (j >> 1) == 1 ? w.y : (j >> 1) == 2 ? w.z : w.w;
-    const uint32_t hbits = (j & 1) ? (x >> 16) : (x & 0xffffu);
-    if constexpr (IN == KVQ_F16) return f16_bits_to_f32(hbits);
-    else return bf16_bits_to_f32(hbits);
-  }
-}
-
-template <int IN>
-__global__ __launch_bounds__(256) void decode_residual_kernel(ResArgs r, const uint16_t* __restrict__ q,
-                                                              int H, int G, float sl2,
-                                                              float* __restrict__ part_ml,
-                                                              float* __restrict__ part_o, int n_slots,
-                                                              int slot0, float* __restrict__ out) {
-  constexpr int RC = KVQ_RES_CHUNK;
-  constexpr int VW = IN == KVQ_F32 ? 4 : 8;                 // elements per 16-byte load
-  constexpr int NV = RC * 128 / VW / 256;                   // loads per thread per operand
-  static_assert(RC == 32 && NV >= 1, "one token per half wave in the softmax");
-  __shared__ float qv[16][129];                   // padded rows: conflict-free across tokens
-  __shared__ float ks[RC][129];
-  __shared__ float vs[RC][129];
-  __shared__ __align__(16) float sp[RC][16];      // [token][head]: logits, then weights
-  __shared__ float sm[16][2];                     // per head: max, sum
-  const int tid = threadIdx.x, rc = blockIdx.x, bh = blockIdx.y;
-  const int b = bh / H, h = bh - (bh / H) * H;
-  const int lane = tid & 63, wave = tid >> 6;
-  const int t0 = rc * RC, n = min(RC, r.R - t0);
-  const int64_t kb = (int64_t)b * r.ks[0] + (int64_t)h * r.ks[1] + (int64_t)t0 * r.ks[2];
-  const int64_t vb = (int64_t)b * r.vs[0] + (int64_t)h * r.vs[1] + (int64_t)t0 * r.vs[2];
-  const int esz = IN == KVQ_F32 ? 4 : 2;
-  uint4 qw = make_uint4(0u, 0u, 0u, 0u);
-  if (tid < G * 16) qw = ((const uint4*)(q + ((int64_t)b * H * G + (int64_t)h * G) * 128))[tid];
-  // rows past n repeat row n - 1 (in bounds, never used): the loads need no branch
-  uint4 kw[NV], vw[NV];
-#pragma unroll
-  for (int i = 0; i < NV; i++) {
-    const int j = tid + 256 * i, t = min(j / (128 / VW), n - 1), c = (j % (128 / VW)) * VW;
-    kw[i] = *(const uint4*)((const uint8_t*)r.k + (kb + (int64_t)t * r.ks[2] + c) * esz);
-    vw[i] = *(const uint4*)((const uint8_t*)r.v + (vb + (int64_t)t * r.vs[2] + c) * esz);
-  }
-  if (tid < G * 16) {
-#pragma unroll
-    for (int e = 0; e < 8; e++) qv[tid >> 4][(tid & 15) * 8 + e] = res_elem<KVQ_BF16>(qw, e);
-  }
-#pragma unroll
-  for (int i = 0; i < NV; i++) {
-    const int j = tid + 256 * i, t = j / (128 / VW), c = (j % (128 / VW)) * VW;
-#pragma unroll
-    for (int e = 0; e < VW; e++) {
-      ks[t][c + e] = res_elem<IN>(kw[i], e);
-      vs[t][c + e] = res_elem<IN>(vw[i], e);
-    }
-  }
-  __syncthreads();
-  // logits: thread i takes head i / n, token i % n
-  for (int i = tid; i < n * G; i += 256) {
-    const int hh = i / n, t = i - (i / n) * n;
-    float d = 0.0f;
-#pragma unroll 16
-    for (int c = 0; c < 128; c++) d = fmaf(qv[hh][c], ks[t][c], d);
-    sp[t][hh] = d * sl2;
-  }
-  __syncthreads();
-  // softmax: each wave takes two heads at a time, one per half wave (lane & 31 = token)
-  for (int hp = wave; 2 * hp < G; hp += 4) {
-    const int hh = 2 * hp + (lane >> 5), t = lane & 31;
-    const bool ok = hh < G && t < n;
-    const float s = ok ? sp[t][hh] : -INFINITY;
-    float m = s;
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) m = fmaxf(m, __shfl_xor(m, o, 64));
-    const float e = ok ? exp2f(s - m) : 0.0f;
-    float l = e;
-#pragma unroll
-    for (int o = 16; o >= 1; o >>= 1) l += __shfl_xor(l, o, 64);
-    if (hh < G) {
-      sp[t][hh] = e;                              // 0 for the rows past n
-      if (t == 0) { sm[hh][0] = m; sm[hh][1] = l; }
-    }
-  }
-  __syncthreads();
-  // values: thread takes channel tid & 127 and heads 8 hb .. 8 hb + 7 (hb =
-  // tid >> 7, uniform per wave); the sums of heads >= G are never stored
-  const int c = tid & 127, hb = tid >> 7;
-  if (8 * hb >= G) return;
-  float acc[8];
-#pragma unroll
-  for (int j = 0; j < 8; j++) acc[j] = 0.0f;
-#pragma unroll 4
-  for (int t = 0; t < n; t++) {
-    const float x = vs[t][c];
-    const float4 w0 = *(const float4*)&sp[t][8 * hb];
-    const float4 w1 = *(const float4*)&sp[t][8 * hb + 4];
-    acc[0] = fmaf(w0.x, x, acc[0]);
-    acc[1] = fmaf(w0.y, x, acc[1]);
-    acc[2] = fmaf(w0.z, x, acc[2]);
-    acc[3] = fmaf(w0.w, x, acc[3]);
-    acc[4] = fmaf(w1.x, x, acc[4]);
-    acc[5] = fmaf(w1.y, x, acc[5]);
-    acc[6] = fmaf(w1.z, x, acc[6]);
-    acc[7] = fmaf(w1.w, x, acc[7]);
-  }
-#pragma unroll
-  for (int j = 0; j < 8; j++) {
-    const int hh = 8 * hb + j;
-    if (hh >= G) break;
-    if (out) {
-      out[((int64_t)b * H * G + (int64_t)h * G + hh) * 128 + c] = acc[j] / sm[hh][1];
-    } else {
-      const int64_t row = ((int64_t)bh * n_slots + slot0 + rc) * G + hh;
-      if (c == 0) { part_ml[2 * row] = sm[hh][0]; part_ml[2 * row + 1] = sm[hh][1]; }
-      part_o[row * 128 + c] = acc[j];
-    }
-  }
-}
-
 static size_t ml_bytes(int BH, int n_chunks, int G) {
   return ((size_t)BH * n_chunks * G * 2 * 4 + 255) / 256 * 256;
 }
@@ -1400,7 +1442,10 @@ static hipError_t launch_ns(const DecodeArgs& a0, hipStream_t st) {
   a.tpc = p.tpc;
   a.n_slots = p.n_chunks + a.n_slots;   // residual slots on entry
   a.fused = a.n_slots > 1 && p.n_chunks >= KVQ_DECODE_FUSED_MIN_CHUNKS;
-  const dim3 grid(a.n_chunks, a.n_groups), block(256);
+  // residual workgroups ride along only when a second kernel combines
+  if (a.fused && a.n_res) return hipErrorInvalidValue;
+  const int res_rows = a.n_res ? (a.n_res * a.g.B * a.g.H + a.n_chunks - 1) / a.n_chunks : 0;
+  const dim3 grid(a.n_chunks, a.n_groups + res_rows), block(256);
   if (p.ns == 1) {
     hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 1>), grid, block, 0, st, a);
   } else if (p.ns == 2) {
@@ -1443,9 +1488,10 @@ hipError_t launch_residual(const ResArgs& res, int res_dtype, dim3 grid, const v
 
 // Packed cache (when it holds tokens) and residual segment (res.R > 0), then
 // the chunk combine when a stream has more than one partial slot.  All on the
-// caller's stream: the residual kernel is short (one memory round trip per
-// workgroup), so a fork onto a second stream would cost more in cross-queue
-// synchronisation than it hides.
+// caller's stream.  With the separate combine kernel the residual blocks are
+// extra workgroups of the decode launch: the dispatcher starts them as decode
+// workgroups retire, so they fill the decode kernel's tail instead of taking
+// a launch of their own.
 hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float* out, void* ws,
                          const ResArgs& res, int res_dtype, hipStream_t st) {
   const int BH = g.B * g.H;
@@ -1460,7 +1506,11 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
   float* part_ml = (float*)((uint8_t*)ws + cnt_bytes(BH));
   float* part_o = (float*)((uint8_t*)part_ml + ml_bytes(BH, n_slots, G));
   hipError_t e = hipSuccess;
-  if (n_res > 0) {
+  // with a second combine kernel the residual blocks ride along as extra
+  // workgroups of the decode launch; otherwise (in-kernel combine, or no
+  // packed tokens) they run first as their own kernel
+  const bool res_inline = has_packed && n_res > 0 && p.n_chunks < KVQ_DECODE_FUSED_MIN_CHUNKS;
+  if (n_res > 0 && !res_inline) {
     e = launch_residual(res, res_dtype, dim3(n_res, BH), q, g.H, G, sl2, part_ml, part_o, n_slots,
                         p.n_chunks, n_slots == 1 ? out : nullptr, st);
     if (e != hipSuccess) return e;
@@ -1478,6 +1528,9 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
     a.n_slots = n_res;
     a.counters = counters;
     a.fused = 0;   // set by the launch from the plan
+    a.res = res;
+    a.res_dtype = res_dtype;
+    a.n_res = res_inline ? n_res : 0;
     switch (g.pdt) {
       case KVQ_F32: e = launch_decode_pdt<KVQ_F32>(a, st); break;
       case KVQ_F16: e = launch_decode_pdt<KVQ_F16>(a, st); break;
