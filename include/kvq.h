@@ -297,6 +297,67 @@ kvq_status kvq_append(kvq_cache *cache, kvq_pool *pool, int64_t budget_bytes, in
                       hipStream_t stream, int32_t *n_shrinks);
 
 /* ------------------------------------------------------------------------
+ * Token-granular append ([PMKVQ] Training strategy and Related work: as in
+ * KIVI, the first token and the most recent tokens stay at 16-bit precision
+ * while the rest of the cache is packed).
+ *
+ * A kvq_window holds, for every stream of one cache, the tokens not packed:
+ * row 0 the sequence's first token (when keep_first is set, for the whole
+ * sequence), rows 1 .. n_recent the recent tokens that have not yet formed a
+ * 128-token group.  k and v are caller-owned device buffers of
+ * [batch][n_kv_heads][KVQ_WINDOW_ROWS][128] elements of `dtype`, 16-byte
+ * aligned; their contents need no initialisation.  The caller zero-fills
+ * n_first and n_recent for a new sequence; the library maintains them.
+ *
+ * Decode over cache + window: kvq_decode_attn_residual with
+ * res_k = k + (1 - n_first) * 128 elements (likewise res_v), res_len =
+ * n_first + n_recent, strides {n_kv_heads * KVQ_WINDOW_ROWS * 128,
+ * KVQ_WINDOW_ROWS * 128, 128} and res_dtype = dtype.  The order of the
+ * window rows is not token order, which attention does not depend on.
+ */
+#define KVQ_WINDOW_ROWS 129
+
+typedef struct kvq_window {
+    int32_t batch;            /* equal to the cache's batch */
+    int32_t n_kv_heads;       /* equal to the cache's n_kv_heads */
+    int32_t dtype;            /* kvq_dtype of the window and of appended tokens: F32 or BF16 */
+    int32_t keep_first;       /* 1: the first token stays unpacked in row 0; 0: it is packed */
+    void *k;                  /* device [B][Hkv][KVQ_WINDOW_ROWS][128] */
+    void *v;                  /* device [B][Hkv][KVQ_WINDOW_ROWS][128] */
+    int32_t n_first;          /* 0 or 1: row 0 holds the first token */
+    int32_t n_recent;         /* 0 .. 128: rows 1 .. n_recent hold recent tokens */
+} kvq_window;
+
+/* Append n_new >= 0 tokens to every stream, in order: k[b][h][t][0..128) and
+ * v[b][h][t][0..128) at element offsets b*s[0] + h*s[1] + t*s[2] + c of
+ * w->dtype (16-byte aligned, strides multiples of 16 bytes).
+ *   - With keep_first, the first token of an empty sequence (no packed
+ *     tokens, an empty window) goes to row 0.
+ *   - Every other token joins the recent rows.  When a token arrives while
+ *     128 recent tokens are held, those 128 are packed as the cache's next
+ *     group first (so after a call 1 .. 128 recent tokens are held, unless
+ *     no token reached the recent rows).  Runs of more than 128 tokens that
+ *     arrive with no recent tokens held are packed straight from k / v,
+ *     leaving the last 1 .. 128 for the window.
+ * Groups are packed by kvq_append under budget_bytes / floor_bits (with
+ * `pool`; uniform widths only) when budget_bytes >= 0, one group per call in
+ * token order, so the packed cache depends on the token sequence only and
+ * not on how it was split into calls; or by kvq_quantize at the cache's
+ * widths when budget_bytes < 0 (pool must be NULL).  The cache's
+ * n_tokens (and k_bits / v_bits after halvings) and the window's n_first /
+ * n_recent are updated; *n_shrinks (may be NULL) counts the halvings.
+ * Arguments, capacity (max_tokens) and the budget at floor_bits for the
+ * final token count are checked before any device work.  KVQ_EBUDGET from
+ * the pool allocator after some groups were packed (fragmentation) leaves
+ * the structs describing exactly the tokens taken so far; KVQ_EHIP as
+ * elsewhere.  All work is on `stream`; calls on one window must use one
+ * stream (or be ordered by the caller). */
+kvq_status kvq_window_append(kvq_window *w, kvq_cache *cache, kvq_pool *pool, int64_t budget_bytes,
+                             int32_t floor_bits, const void *k, const void *v,
+                             const int64_t k_strides[3], const int64_t v_strides[3], int32_t n_new,
+                             hipStream_t stream, int32_t *n_shrinks);
+
+/* ------------------------------------------------------------------------
  * Block-wise bit-width allocation ([PMKVQ] Key design 2: each transformer
  * block gets one width, minimising the summed sensitivity s_{i,b} with the
  * blocks' total KV-cache memory within the budget M).  Host-only; the

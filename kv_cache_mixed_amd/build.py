@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["quantize.hip", "shrink.hip", "decode_attn.hip", "pairs.hip", "kvq_api.cpp", "alloc.cpp"]
+SOURCES = ["quantize.hip", "shrink.hip", "decode_attn.hip", "pairs.hip", "window.hip", "kvq_api.cpp", "alloc.cpp"]
 ARCH = "gfx950"
 
 COMMON = ["-O3", "-std=c++17", "-fPIC", "--offload-arch=" + ARCH,

@@ -396,4 +396,125 @@ kvq_status kvq_append(kvq_cache* c, kvq_pool* pool, int64_t budget, int32_t floo
   }
 }
 
+
+// Token-granular append: the window of unpacked tokens (first token + recent
+// tokens) and the hand-over of full 128-token groups to the packed cache.
+kvq_status kvq_window_append(kvq_window* w, kvq_cache* c, kvq_pool* pool, int64_t budget,
+                             int32_t floor_bits, const void* k, const void* v, const int64_t ks[3],
+                             const int64_t vs[3], int32_t n_new, hipStream_t stream,
+                             int32_t* n_shrinks) {
+  try {
+    if (n_shrinks) *n_shrinks = 0;
+    kvq_status s = check_cache(c);
+    if (s != KVQ_OK) return s;
+    if (!w || w->batch != c->batch || w->n_kv_heads != c->n_kv_heads) return KVQ_EINVAL;
+    if (w->dtype != KVQ_F32 && w->dtype != KVQ_BF16) return KVQ_EINVAL;
+    if ((w->keep_first != 0 && w->keep_first != 1) || (w->n_first != 0 && w->n_first != 1) ||
+        (w->n_first && !w->keep_first))
+      return KVQ_EINVAL;
+    if (w->n_recent < 0 || w->n_recent > 128) return KVQ_EINVAL;
+    if (!w->k || !w->v || !aligned(w->k, 16) || !aligned(w->v, 16)) return KVQ_EINVAL;
+    if (n_new < 0) return KVQ_EINVAL;
+    if (n_new == 0) return KVQ_OK;
+    if (!k || !v || !ks || !vs || !aligned(k, 16) || !aligned(v, 16)) return KVQ_EINVAL;
+    const int elt = w->dtype == KVQ_F32 ? 4 : 2;
+    for (int i = 0; i < 3; i++)
+      if (ks[i] < 0 || vs[i] < 0 || (ks[i] * elt) % 16 || (vs[i] * elt) % 16) return KVQ_EINVAL;
+    if ((int64_t)c->batch * c->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+    if (budget >= 0) {
+      // the checks kvq_append makes, so that no group hand-over can fail on them later
+      if (c->k_bits == KVQ_KMIXED || c->k_bits != c->v_bits) return KVQ_EUNSUPPORTED;
+      if (!valid_bits(floor_bits) || floor_bits > c->k_bits) return KVQ_EINVAL;
+      if (pool && (pool->B != c->batch || pool->H != c->n_kv_heads ||
+                   pool->max_tiles != c->max_tokens / 128 || c->k_tile_off != pool->k_dev ||
+                   c->v_tile_off != pool->v_dev))
+        return KVQ_EINVAL;
+      if (!pool && (c->k_tile_off || c->v_tile_off)) return KVQ_EINVAL;
+    } else if (pool) {
+      return KVQ_EINVAL;
+    }
+
+    // plan: the first token, filling the recent rows, groups packed from the
+    // window (one each time a token arrives with 128 held) or straight from
+    // the input (runs longer than 128 arriving with no recent token held),
+    // and the rest into the recent rows
+    const int first = (w->keep_first && !w->n_first && c->n_tokens == 0 && w->n_recent == 0) ? 1 : 0;
+    int64_t packed = 0, direct = 0;
+    {
+      int64_t r = n_new - first;
+      int recent = w->n_recent;
+      if (r > 0 && recent == 128) { packed += 128; recent = 0; }
+      if (r > 0 && recent > 0) {
+        const int64_t fill = std::min<int64_t>(r, 128 - recent);
+        r -= fill;
+        if (r > 0) packed += 128;
+      }
+      if (r > 128) { direct = (r - 1) / 128 * 128; packed += direct; }
+    }
+    if ((int64_t)c->n_tokens + packed > c->max_tokens) return KVQ_EINVAL;
+    if (direct / 128 > 65535) return KVQ_EUNSUPPORTED;
+    if (budget >= 0 && packed > 0 &&
+        kvq_cache_bytes(c, (int32_t)(c->n_tokens + packed), floor_bits, floor_bits) > budget)
+      return KVQ_EBUDGET;
+
+    const int64_t wst[3] = {(int64_t)c->n_kv_heads * KVQ_WINDOW_ROWS * 128, KVQ_WINDOW_ROWS * 128, 128};
+    const uint8_t* wk_row1 = (const uint8_t*)w->k + 128 * elt;
+    const uint8_t* wv_row1 = (const uint8_t*)w->v + 128 * elt;
+    auto at = [&](const void* p, const int64_t* st, int64_t t) { return (const uint8_t*)p + t * st[2] * elt; };
+    auto copy = [&](int64_t t, int m, int slot0) -> kvq_status {
+      hipError_t e = kvq::launch_window_copy(at(k, ks, t), at(v, vs, t), ks, vs, elt, w->k, w->v,
+                                             c->batch, c->n_kv_heads, m, slot0, stream);
+      return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
+    };
+    auto pack = [&](const void* pk, const void* pv, const int64_t* sk, const int64_t* sv, int n) {
+      if (budget < 0)
+        return kvq_quantize(c, pk, pv, (kvq_dtype)w->dtype, sk, sv, c->n_tokens, n, stream);
+      int32_t ns = 0;
+      const kvq_status e = kvq_append(c, pool, budget, floor_bits, pk, pv, (kvq_dtype)w->dtype, sk, sv, n,
+                                      stream, &ns);
+      if (n_shrinks) *n_shrinks += ns;
+      return e;
+    };
+
+    int64_t t = 0;
+    if (first) {
+      if ((s = copy(0, 1, 0)) != KVQ_OK) return s;
+      w->n_first = 1;
+      t = 1;
+    }
+    if (t < n_new && w->n_recent == 128) {
+      if ((s = pack(wk_row1, wv_row1, wst, wst, 128)) != KVQ_OK) return s;
+      w->n_recent = 0;
+    }
+    if (t < n_new && w->n_recent > 0) {
+      const int fill = (int)std::min<int64_t>(n_new - t, 128 - w->n_recent);
+      if ((s = copy(t, fill, 1 + w->n_recent)) != KVQ_OK) return s;
+      w->n_recent += fill;
+      t += fill;
+      if (t < n_new) {
+        if ((s = pack(wk_row1, wv_row1, wst, wst, 128)) != KVQ_OK) return s;
+        w->n_recent = 0;
+      }
+    }
+    if (n_new - t > 128) {
+      // under a budget one group at a time, as if the tokens had come one by
+      // one (a halving decided for several groups at once would quantize the
+      // earlier ones at the narrower width instead of shrinking them)
+      const int d = (int)((n_new - t - 1) / 128 * 128);
+      const int step = budget >= 0 ? 128 : d;
+      for (int done = 0; done < d; done += step) {
+        if ((s = pack(at(k, ks, t), at(v, vs, t), ks, vs, step)) != KVQ_OK) return s;
+        t += step;
+      }
+    }
+    if (t < n_new) {
+      if ((s = copy(t, (int)(n_new - t), 1)) != KVQ_OK) return s;
+      w->n_recent = (int)(n_new - t);
+    }
+    return KVQ_OK;
+  } catch (...) {
+    return KVQ_EHIP;
+  }
+}
+
 }  // extern "C"

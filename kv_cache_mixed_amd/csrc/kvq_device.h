@@ -230,6 +230,13 @@ hipError_t launch_quantize(const Geo& g, const void* k, const void* v, int in_dt
                            const int64_t* ks, const int64_t* vs, int t0, int n_new,
                            hipStream_t st);
 hipError_t launch_shrink(const Geo& g, int to_bits, int method, hipStream_t st);
+// copy m token rows of every stream (b, h) of k and v (element strides ks / vs
+// of batch, kv head, token; channel stride 1; elt_bytes 2 or 4) into rows
+// slot0 .. slot0 + m - 1 of the window buffers wk / wv
+// ([B][H][KVQ_WINDOW_ROWS][128] elements)
+hipError_t launch_window_copy(const void* k, const void* v, const int64_t ks[3], const int64_t vs[3],
+                              int elt_bytes, void* wk, void* wv, int B, int H, int m, int slot0,
+                              hipStream_t st);
 // partial slots per stream: up to KVQ_MAX_CHUNKS packed chunks, then one per
 // KVQ_RES_CHUNK residual tokens; the combine kernel takes at most 128
 constexpr int KVQ_RES_CHUNK = 32;

@@ -41,6 +41,18 @@ class KvqCacheStruct(ctypes.Structure):
     ]
 
 
+WINDOW_ROWS = 129          # KVQ_WINDOW_ROWS of the header
+
+
+class KvqWindowStruct(ctypes.Structure):
+    _fields_ = [
+        ("batch", ctypes.c_int32), ("n_kv_heads", ctypes.c_int32),
+        ("dtype", ctypes.c_int32), ("keep_first", ctypes.c_int32),
+        ("k", ctypes.c_void_p), ("v", ctypes.c_void_p),
+        ("n_first", ctypes.c_int32), ("n_recent", ctypes.c_int32),
+    ]
+
+
 class KvqError(RuntimeError):
     def __init__(self, status: int, what: str):
         self.status = status
@@ -52,7 +64,7 @@ _lib = None
 EXPORTS = ["kvq_strerror", "kvq_tile_bytes", "kvq_cache_bytes", "kvq_quantize", "kvq_shrink",
            "kvq_shrink_shift", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_decode_attn_residual",
            "kvq_pool_create", "kvq_pool_destroy", "kvq_pool_used_bytes", "kvq_pool_high_water",
-           "kvq_append", "kvq_allocate_bits", "kvq_pair_norms", "kvq_pair_slot_map"]
+           "kvq_append", "kvq_window_append", "kvq_allocate_bits", "kvq_pair_norms", "kvq_pair_slot_map"]
 
 
 def load():
@@ -101,6 +113,9 @@ def load():
     L.kvq_append.restype = ctypes.c_int
     L.kvq_append.argtypes = [P, vp, i64, i32, vp, vp, ctypes.c_int, vp, vp, i32, vp,
                              ctypes.POINTER(i32)]
+    L.kvq_window_append.restype = ctypes.c_int
+    L.kvq_window_append.argtypes = [ctypes.POINTER(KvqWindowStruct), P, vp, i64, i32, vp, vp, vp, vp, i32, vp,
+                                    ctypes.POINTER(i32)]
     _lib = L
     return L
 
@@ -385,3 +400,59 @@ class PackedCache:
         sl = slice(base, base + self.n_tokens * pb)
         return (self.v_scale[sl].cpu().numpy().view(npdt),
                 self.v_zero[sl].cpu().numpy().view(npdt))
+
+
+class Window:
+    """The unpacked tokens of every stream of one cache (kvq_window of the
+    header): row 0 the first token (keep_first), rows 1..n_recent the recent
+    tokens not yet packed.  append() hands every full 128-token group to the
+    cache; residual() gives the views decode_attn attends with the cache."""
+
+    def __init__(self, cache, dtype=None, keep_first=True):
+        import torch
+        load()
+        dtype = torch.bfloat16 if dtype is None else dtype
+        self.cache = cache
+        self.dtype = dtype
+        shape = (cache.B, cache.H, WINDOW_ROWS, 128)
+        self.k = torch.zeros(shape, dtype=dtype, device=cache.device)
+        self.v = torch.zeros_like(self.k)
+        w = KvqWindowStruct()
+        w.batch, w.n_kv_heads = cache.B, cache.H
+        w.dtype = {torch.float32: F32, torch.bfloat16: BF16}[dtype]
+        w.keep_first = 1 if keep_first else 0
+        w.k, w.v = self.k.data_ptr(), self.v.data_ptr()
+        w.n_first = w.n_recent = 0
+        self.w = w
+
+    @property
+    def n_first(self):
+        return self.w.n_first
+
+    @property
+    def n_recent(self):
+        return self.w.n_recent
+
+    def append(self, k, v, budget_bytes=-1, floor_bits=1, stream=None):
+        """k, v: [B][H][n][128] device tensors of the window's dtype, unit
+        channel stride.  budget_bytes < 0: groups are packed at the cache's
+        widths; otherwise under the budget (progressive halvings, returned)."""
+        assert k.dtype == self.dtype and v.dtype == self.dtype and k.shape == v.shape
+        n = ctypes.c_int32(0)
+        c = self.cache
+        if budget_bytes < 0 and c.layout == "pool":
+            # the pool's offset tables hold no tiles for the new groups
+            raise ValueError("a pool-layout cache takes groups under a budget")
+        st = load().kvq_window_append(ctypes.byref(self.w), ctypes.byref(c.s),
+                                      c.pool if budget_bytes >= 0 else None, budget_bytes, floor_bits,
+                                      _ptr(k), _ptr(v), _strides3(k), _strides3(v), k.shape[2],
+                                      _stream_ptr(stream), ctypes.byref(n))
+        _check(st, "kvq_window_append")
+        return n.value
+
+    def residual(self):
+        """(res_k, res_v) views over the held rows, for decode_attn."""
+        lo = 1 - self.w.n_first
+        hi = 1 + self.w.n_recent
+        return self.k[:, :, lo:hi], self.v[:, :, lo:hi]
+

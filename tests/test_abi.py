@@ -204,3 +204,63 @@ def test_decode_counter_bytes_formula():
         want = eval(body.replace("n_streams", str(B * H)))
         assert c.workspace_counter_bytes() == want and want % 256 == 0 and want >= 4 * B * H
         assert L.kvq_decode_workspace_bytes(ctypes.byref(s), 8 * H) > want
+
+
+def _fake_window(s, dtype=kvq.BF16, keep_first=1):
+    w = kvq.KvqWindowStruct()
+    w.batch, w.n_kv_heads, w.dtype, w.keep_first = s.batch, s.n_kv_heads, dtype, keep_first
+    w.k, w.v = FAKE, FAKE + 1024
+    w.n_first = w.n_recent = 0
+    return w
+
+
+def test_window_validation_rejects_before_launch():
+    """kvq_window_append checks arguments, capacity and the budget for the
+    whole call before its first copy or group (no call here reaches the
+    device), and leaves both structs unchanged on rejection."""
+    L = _lib()
+    m = re.search(r"#define KVQ_WINDOW_ROWS (\d+)", open(HEADER).read())
+    assert m and int(m.group(1)) == kvq.WINDOW_ROWS
+    vp = ctypes.c_void_p
+    P = ctypes.byref
+    F = vp(FAKE)
+    st = (ctypes.c_int64 * 3)(2 * 1000 * 128, 1000 * 128, 128)
+
+    def call(w, s, n, budget=-1, floor=1, k=F, v=F, ks=st, vs=st, pool=None):
+        return L.kvq_window_append(P(w), P(s), pool, budget, floor, k, v, ks, vs, n, None, None)
+
+    s = _fake_struct(2, 2, 1024, 4, 4)
+    w = _fake_window(s)
+    assert call(w, s, 0) == kvq.OK                              # nothing to do
+    assert call(w, s, -1) == kvq.EINVAL
+    assert L.kvq_window_append(None, P(s), None, -1, 1, F, F, st, st, 5, None, None) == kvq.EINVAL
+    for field, bad in (("batch", 3), ("n_kv_heads", 1), ("dtype", kvq.F16), ("keep_first", 2),
+                       ("n_first", 2), ("n_recent", 129), ("n_recent", -1), ("k", 0), ("v", FAKE + 8)):
+        w = _fake_window(s)
+        setattr(w, field, bad)
+        assert call(w, s, 5) == kvq.EINVAL, field
+    w = _fake_window(s, keep_first=0)
+    w.n_first = 1                                               # a first row without keep_first
+    assert call(w, s, 5) == kvq.EINVAL
+    w = _fake_window(s)
+    assert call(w, s, 5, k=None) == kvq.EINVAL
+    assert call(w, s, 5, ks=None) == kvq.EINVAL
+    assert call(w, s, 5, v=vp(FAKE + 8)) == kvq.EINVAL           # misaligned input
+    assert call(w, s, 5, ks=(ctypes.c_int64 * 3)(0, 0, 132)) == kvq.EINVAL   # 264-byte rows: not 16-byte units
+    assert call(w, s, 5, vs=(ctypes.c_int64 * 3)(0, -128, 128)) == kvq.EINVAL
+    # capacity: 1 first token + 1024 packed + 128 recent > 1024 + 129 held
+    assert call(w, s, 1 + 1024 + 129) == kvq.EINVAL
+    # budget for the final count at the floor width: 4 streams x 8 groups at
+    # 1 bit with fp16 parameters, (2048 + 2048 + 4 * 128 * 2) B per group
+    s16 = _fake_struct(2, 2, 1024, 16, 16)
+    need = L.kvq_cache_bytes(P(s16), 1024, 1, 1)
+    assert need == 2 * 2 * 8 * (2048 + 2048 + 4 * 128 * 2)
+    w = _fake_window(s16)
+    assert call(w, s16, 1 + 1024 + 1, budget=need - 1, floor=1) == kvq.EBUDGET
+    assert call(w, s16, 1 + 1024 + 1, budget=1 << 40, floor=32) == kvq.EINVAL    # floor not a width
+    tabled = _fake_struct(2, 2, 1024, 16, 16)
+    tabled.k_tile_off = tabled.v_tile_off = FAKE                # tile tables without their pool
+    assert call(_fake_window(tabled), tabled, 300, budget=1 << 40) == kvq.EINVAL
+    mixed = _fake_struct(2, 2, 1024, kvq.KMIXED, 2)
+    assert call(_fake_window(mixed), mixed, 300, budget=1 << 40) == kvq.EUNSUPPORTED  # budget: uniform widths
+    assert w.n_first == 0 and w.n_recent == 0 and s16.n_tokens == 0 and s16.k_bits == 16

@@ -1,0 +1,196 @@
+"""GPU parity of the token-granular append (kvq_window_append; PM-KVQ page,
+Training strategy and Related work: the first token and the recent tokens
+stay at 16-bit, full 128-token groups are packed).  After every call the
+window and cache state follow the rule stated in the header, the packed bytes
+equal the oracle's quantization of the packed tokens, the held rows are exact
+copies of the tokens they hold, and decode over cache + window matches the
+oracle's attention over (packed tokens, held tokens)."""
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_mixed_amd import kvq, synth
+from tests.gpu_helpers import (PDT_ORACLE, REL_TOL, SCALE, assert_stream_bytes_equal, q_to_dev,
+                               rel_err_rows)
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    oracle.build(force=False)
+    kvq.load()
+
+
+class Model:
+    """Which tokens are packed and which are held, from the header's rule."""
+
+    def __init__(self, keep_first):
+        self.keep_first = keep_first
+        self.first = 0           # 1 when token 0 sits in row 0
+        self.packed = 0          # packed tokens: p0 .. p0 + packed - 1
+        self.recent = 0          # held recent tokens: after the packed ones
+        self.seen = 0
+
+    @property
+    def p0(self):
+        return self.first
+
+    def append(self, n):
+        for _ in range(n):
+            if self.keep_first and self.seen == 0:
+                self.first = 1
+            else:
+                if self.recent == 128:
+                    self.packed += 128
+                    self.recent = 0
+                self.recent += 1
+            self.seen += 1
+
+    def held(self):
+        """token indices of the window rows (1 - first) .. recent, in row order"""
+        rec = list(range(self.p0 + self.packed, self.p0 + self.packed + self.recent))
+        return ([0] if self.first else []) + rec
+
+
+def _check(cache, win, model, kf, vf, q_bits, G, pdt, k_bits, v_bits, what, check_bytes=True):
+    torch.cuda.synchronize()
+    assert (win.n_first, win.n_recent, cache.n_tokens) == (model.first, model.recent, model.packed), what
+    B, H = cache.B, cache.H
+    held = model.held()
+    rk, rv = win.residual()
+    assert rk.shape[2] == len(held)
+    rkf, rvf = rk.float().cpu().numpy(), rv.float().cpu().numpy()
+    assert np.array_equal(rkf, kf[:, :, held]) and np.array_equal(rvf, vf[:, :, held]), what + ": held rows"
+    out = cache.decode_attn(q_to_dev(q_bits, torch), SCALE, res_k=rk, res_v=rv).cpu().numpy()
+    lo, hi = model.p0, model.p0 + model.packed
+    for b in range(B):
+        for h in range(H):
+            st = None
+            if model.packed:
+                st = oracle.quantize_stream(kf[b, h, lo:hi], vf[b, h, lo:hi], k_bits, v_bits, PDT_ORACLE[pdt])
+                if check_bytes:
+                    assert_stream_bytes_equal(cache, st, b, h, what)
+            ref = oracle.decode_attn_residual(st, q_bits[b, h * G:(h + 1) * G], SCALE, kf[b, h, held],
+                                              vf[b, h, held])
+            err = rel_err_rows(out[b, h * G:(h + 1) * G], ref).max()
+            assert err <= REL_TOL, "%s (b=%d h=%d): %.3e" % (what, b, h, err)
+
+
+def test_window_token_by_token():
+    """One token per call from an empty sequence, first token kept: the
+    window fills, every 129th recent arrival packs a group, decode after
+    every token."""
+    print("case window token by token", flush=True)
+    B, H, Hq, N = 2, 2, 8, 3 * 128 + 46
+    G = Hq // H
+    inp = synth.layer(B, H, Hq, N, 970)
+    cache = kvq.PackedCache(B, H, 512, 4, 4, kvq.F16)
+    win = kvq.Window(cache, torch.bfloat16, keep_first=True)
+    kd = torch.from_numpy(inp["k"]).cuda().to(torch.bfloat16)
+    vd = torch.from_numpy(inp["v"]).cuda().to(torch.bfloat16)
+    kf, vf = kd.float().cpu().numpy(), vd.float().cpu().numpy()
+    model = Model(True)
+    for t in range(N):
+        win.append(kd[:, :, t:t + 1], vd[:, :, t:t + 1])
+        model.append(1)
+        boundary = t < 3 or (t - 1) % 128 in (126, 127, 0, 1) or t == N - 1
+        _check(cache, win, model, kf, vf, inp["q_bf16"], G, kvq.F16, 4, 4, "token %d" % t,
+               check_bytes=boundary)
+    assert cache.n_tokens == 384 and win.n_recent == 45 and win.n_first == 1
+
+
+@pytest.mark.parametrize("keep_first", [False, True])
+def test_window_runs(keep_first):
+    """Runs of many sizes: a 700-token prefill (groups packed straight from
+    the input), single tokens, a run that fills the window, packs it, packs a
+    group from the input and leaves a tail, exact multiples of 128, and empty
+    calls; float32 window, 2-bit codes with e4m3 parameters."""
+    print("case window runs keep_first=%s" % keep_first, flush=True)
+    B, H, Hq = 1, 3, 12
+    G = Hq // H
+    runs = [700, 1, 1, 0, 300, 128, 129, 1, 2, 256, 5]
+    N = sum(runs)
+    inp = synth.layer(B, H, Hq, N, 971 + int(keep_first))
+    cache = kvq.PackedCache(B, H, 2048, 2, 2, kvq.E4M3)
+    win = kvq.Window(cache, torch.float32, keep_first=keep_first)
+    kd = torch.from_numpy(inp["k"]).cuda()
+    vd = torch.from_numpy(inp["v"]).cuda()
+    model = Model(keep_first)
+    t = 0
+    for n in runs:
+        # a strided view: the run inside a larger token range
+        win.append(kd[:, :, t:t + n], vd[:, :, t:t + n])
+        model.append(n)
+        t += n
+        _check(cache, win, model, inp["k"], inp["v"], inp["q_bf16"], G, kvq.E4M3, 2, 2,
+               "after run %d (token %d)" % (n, t))
+
+
+def test_window_without_first_single_token_and_capacity():
+    """keep_first off: the first token is an ordinary recent token; a lone
+    held token is attended alone (output = its value row up to rounding);
+    a call that would overflow max_tokens is rejected with the state kept."""
+    print("case window edge", flush=True)
+    B, H, Hq = 1, 1, 4
+    inp = synth.layer(B, H, Hq, 400, 973)
+    cache = kvq.PackedCache(B, H, 256, 4, 4, kvq.F16)
+    win = kvq.Window(cache, torch.float32, keep_first=False)
+    kd = torch.from_numpy(inp["k"]).cuda()
+    vd = torch.from_numpy(inp["v"]).cuda()
+    win.append(kd[:, :, :1], vd[:, :, :1])
+    rk, rv = win.residual()
+    out = cache.decode_attn(q_to_dev(inp["q_bf16"], torch), SCALE, res_k=rk, res_v=rv).cpu().numpy()
+    assert np.allclose(out[0], np.broadcast_to(inp["v"][0, 0, 0], (Hq, 128)), rtol=1e-6, atol=1e-6)
+    # 256 packed + 128 held is the most this cache and window take
+    win.append(kd[:, :, 1:384], vd[:, :, 1:384])
+    torch.cuda.synchronize()
+    assert (cache.n_tokens, win.n_recent, win.n_first) == (256, 128, 0)
+    with pytest.raises(kvq.KvqError) as e:
+        win.append(kd[:, :, 384:385], vd[:, :, 384:385])
+    assert e.value.status == kvq.EINVAL
+    assert (cache.n_tokens, win.n_recent) == (256, 128)
+    model = Model(False)
+    model.append(384)
+    _check(cache, win, model, inp["k"], inp["v"], inp["q_bf16"], Hq // H, kvq.F16, 4, 4, "full")
+
+
+def test_window_under_budget_matches_append():
+    """Budget mode: the window hands its groups to kvq_append (pool layout,
+    16-bit start), so the cache it builds is byte-identical to one fed the
+    same groups through kvq_append directly, with the same halvings; decode
+    over cache + window equals decode over that cache + the same held rows."""
+    print("case window budget", flush=True)
+    B, H, Hq, N = 1, 2, 8, 1300
+    inp = synth.layer(B, H, Hq, N, 974)
+    kd = torch.from_numpy(inp["k"]).cuda().to(torch.bfloat16)
+    vd = torch.from_numpy(inp["v"]).cuda().to(torch.bfloat16)
+    pool_bytes = 4 << 20
+    mk = lambda: kvq.PackedCache(B, H, 2048, 16, 16, kvq.F16, layout="pool", pool_bytes=pool_bytes)
+    a, b = mk(), mk()
+    budget = a.cache_bytes(1024, 4, 4) + a.cache_bytes(128, 4, 4) // 2
+    win = kvq.Window(a, torch.bfloat16, keep_first=True)
+    shr_a = shr_b = 0
+    t = 0
+    for n in [1, 200, 1, 300, 5, 400, 393]:
+        shr_a += win.append(kd[:, :, t:t + n], vd[:, :, t:t + n], budget_bytes=budget, floor_bits=2)
+        t += n
+    # the same groups through kvq_append: tokens 1 .. 1 + a.n_tokens in 128-token groups
+    for g0 in range(1, 1 + a.n_tokens, 128):
+        shr_b += b.append(kd[:, :, g0:g0 + 128], vd[:, :, g0:g0 + 128], budget_bytes=budget, floor_bits=2)
+    torch.cuda.synchronize()
+    assert a.n_tokens == b.n_tokens and a.k_bits == b.k_bits and shr_a == shr_b and shr_a >= 2
+    for bb in range(B):
+        for h in range(H):
+            for g in range(a.n_tokens // 128):
+                assert np.array_equal(a.k_tile(bb, h, g), b.k_tile(bb, h, g))
+                assert np.array_equal(a.v_tile(bb, h, g), b.v_tile(bb, h, g))
+            for x, y in zip(a.k_params(bb, h) + a.v_params(bb, h), b.k_params(bb, h) + b.v_params(bb, h)):
+                assert np.array_equal(x.view(np.uint8), y.view(np.uint8))
+    q = q_to_dev(inp["q_bf16"], torch)
+    rk, rv = win.residual()
+    oa = a.decode_attn(q, SCALE, res_k=rk, res_v=rv)
+    ob = b.decode_attn(q, SCALE, res_k=rk.clone(), res_v=rv.clone())
+    torch.cuda.synchronize()
+    assert torch.equal(oa, ob)
