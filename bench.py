@@ -543,6 +543,7 @@ def main():
             "ms": round(dr_ms, 4), "GB/s": round(ar / dr_ms / 1e6, 1),
             "ms_without_residual": round(d0_ms, 4),
             "extra_us_per_round": [round((b - a) * 1e3, 1) for a, b in zip(d0s, drs)],
+            "extra_us_median": round(sorted(b - a for a, b in zip(d0s, drs))[2] * 1e3, 1),
             "note": "medians of 5 alternating rounds of 60 calls back to back, cache copies rotated as "
                     "in the headline step; residual bf16 [16][4][128][128]"}
         del rk, rv
