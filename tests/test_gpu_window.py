@@ -194,3 +194,40 @@ def test_window_under_budget_matches_append():
     ob = b.decode_attn(q, SCALE, res_k=rk.clone(), res_v=rv.clone())
     torch.cuda.synchronize()
     assert torch.equal(oa, ob)
+
+
+def test_window_mixed_keys():
+    """A mixed-width key cache (slot map per kv head, e4m3 parameters, 2-bit
+    values) fed through the window without a budget: groups packed by
+    kvq_quantize from the window and straight from the input."""
+    print("case window mixed keys", flush=True)
+    B, H, Hq = 1, 2, 8
+    G = Hq // H
+    inp = synth.mixed_layer(B, H, Hq, 1024, 975)
+    slot_chan = inp["slot_chan"]
+    cache = kvq.PackedCache(B, H, 1024, kvq.KMIXED, 2, kvq.E4M3, slot_chan=slot_chan)
+    win = kvq.Window(cache, torch.float32, keep_first=True)
+    kd = torch.from_numpy(np.ascontiguousarray(inp["k"])).cuda()
+    vd = torch.from_numpy(np.ascontiguousarray(inp["v"])).cuda()
+    model = Model(True)
+    t = 0
+    for n in [1, 130, 1, 200, 300]:
+        win.append(kd[:, :, t:t + n], vd[:, :, t:t + n])
+        model.append(n)
+        t += n
+        torch.cuda.synchronize()
+        assert (win.n_first, win.n_recent, cache.n_tokens) == (model.first, model.recent, model.packed)
+        held = model.held()
+        rk, rv = win.residual()
+        out = cache.decode_attn(q_to_dev(inp["q_bf16"], torch), SCALE, res_k=rk, res_v=rv).cpu().numpy()
+        lo, hi = model.p0, model.p0 + model.packed
+        for h in range(H):
+            st = None
+            if model.packed:
+                st = oracle.quantize_stream(inp["k"][0, h, lo:hi], inp["v"][0, h, lo:hi], 0, 2, oracle.E4M3,
+                                            slot_chan[h])
+                assert_stream_bytes_equal(cache, st, 0, h, "mixed after %d" % t)
+            ref = oracle.decode_attn_residual(st, inp["q_bf16"][0, h * G:(h + 1) * G], SCALE,
+                                              inp["k"][0, h, held], inp["v"][0, h, held])
+            err = rel_err_rows(out[0, h * G:(h + 1) * G], ref).max()
+            assert err <= REL_TOL, "mixed after %d (h=%d): %.3e" % (t, h, err)
