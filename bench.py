@@ -33,14 +33,14 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, profiles/decode_kernel_*.md)
 # for the kernel source with the given digest, and the factors that map each
 # counter onto true bytes: a plain 512 MiB device copy in the same run reads
-# FETCH_SIZE = 262161.2 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
-# fetch counter is scaled by 524288/262161.2 and the write counter by 1.  The
+# FETCH_SIZE = 262161.3 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
+# fetch counter is scaled by 524288/262161.3 and the write counter by 1.  The
 # figure is reported only while the kernel source is unchanged.
 COUNTER_TRAFFIC = {
-    "source_sha256": "5ee216d403afdfc86f0d6d2e5e8c48516a190905b498bb9df20523ffab278837",
-    "fetch_kib": 147934.3,
+    "source_sha256": "83a583f4be16bcb72e373cedb716954ff6c7f869102531c1c787b1c63fda7755",
+    "fetch_kib": 147930.0,
     "write_kib": 3664.0,
-    "fetch_factor": 524288.0 / 262161.2,
+    "fetch_factor": 524288.0 / 262161.3,
     "write_factor": 1.0,
 }
 KERNEL_SOURCES = ("kv_cache_mixed_amd/csrc/decode_attn.hip", "kv_cache_mixed_amd/csrc/kvq_device.h")
