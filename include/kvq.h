@@ -8,17 +8,22 @@
  *              Long-CoT LLMs" (papernotes.org summary).
  *   [CHANMIX] "Channel-Aware Mixed-Precision Quantization for Efficient
  *              Long-Context Inference" (papernotes.org summary).
+ *   [PNMIX]   "PN-Mix: Pair-Norm Guided Mixed-Precision Key Cache
+ *              Quantization" (shd-paper.top summary, abstract).
  *
  * ------------------------------------------------------------------------
  * Conventions
  *   - Every buffer is owned by the caller.  Pointers named "device" are HIP
  *     device memory; the library never allocates or frees device memory.
  *   - The kvq_cache struct is host memory and is read during the call only;
- *     kvq_quantize, kvq_shrink and kvq_append update its n_tokens / k_bits /
- *     v_bits fields as documented.
+ *     kvq_quantize, kvq_shrink, kvq_append and kvq_window_append update its
+ *     n_tokens / k_bits / v_bits fields (and the window's counts) as
+ *     documented.
  *   - All device work is enqueued on the given stream; calls return before it
  *     completes.  Every argument is validated on the host first: any status
- *     other than KVQ_OK / KVQ_EHIP means no device work was enqueued.
+ *     other than KVQ_OK / KVQ_EHIP means no device work was enqueued (one
+ *     exception, documented at kvq_window_append: a call that packs several
+ *     groups can run out of pool extents after its earlier groups).
  *     KVQ_EHIP means a HIP call failed (work already enqueued may be partial).
  *   - No exceptions cross the ABI.  The library holds no global mutable
  *     state; calls on different caches are independent.  Calls that touch the
@@ -288,8 +293,9 @@ int64_t kvq_pool_high_water(const kvq_pool *pool);
  * current width exceeds budget_bytes, halve the width with kvq_shrink (never
  * below floor_bits); then allocate the new tiles (from `pool`, or at the
  * contiguous placement when pool is NULL) and kvq_quantize them at the
- * resulting width.  If the group does not fit even at floor_bits, returns
- * KVQ_EBUDGET before any work.  *n_shrinks (may be NULL) receives the number
+ * resulting width.  If the group does not fit even at floor_bits, or the
+ * pool has no free extents left for the new tiles (after the halvings'
+ * releases), returns KVQ_EBUDGET before any work, the pool unchanged.  *n_shrinks (may be NULL) receives the number
  * of halvings performed.  Input arguments as for kvq_quantize. */
 kvq_status kvq_append(kvq_cache *cache, kvq_pool *pool, int64_t budget_bytes, int32_t floor_bits,
                       const void *k, const void *v, kvq_dtype in_dtype,

@@ -255,14 +255,13 @@ kvq_status kvq_decode_attn_residual(const kvq_cache* c, const void* q, int32_t n
 // Allocation takes the smallest free extent that fits (splitting larger ones)
 // before growing the high-water mark, so freed halves are always reused first.
 // ---------------------------------------------------------------------------
-struct kvq_pool {
-  int B, H, max_tiles;
-  int64_t capacity;
+// The extent state (free lists, high-water mark, bytes in use) is its own
+// value type, so a call can plan its releases and allocations on a copy and
+// commit them only once every allocation has succeeded.
+struct PoolExtents {
+  int64_t capacity = 0;
   int64_t high = 0;
   int64_t used = 0;
-  int64_t* k_dev;
-  int64_t* v_dev;
-  std::vector<int64_t> k_host, v_host;   // [max_tiles][B][H]
   std::map<int64_t, std::vector<int64_t>> free_by_size;
 
   bool alloc(int64_t size, int64_t* off) {
@@ -293,6 +292,14 @@ struct kvq_pool {
   }
 };
 
+struct kvq_pool {
+  int B, H, max_tiles;
+  int64_t* k_dev;
+  int64_t* v_dev;
+  std::vector<int64_t> k_host, v_host;   // [max_tiles][B][H]
+  PoolExtents ext;
+};
+
 extern "C" {
 
 kvq_status kvq_pool_create(const kvq_cache* c, int64_t pool_bytes, int64_t* k_dev, int64_t* v_dev,
@@ -311,7 +318,7 @@ kvq_status kvq_pool_create(const kvq_cache* c, int64_t pool_bytes, int64_t* k_de
     p->B = c->batch;
     p->H = c->n_kv_heads;
     p->max_tiles = c->max_tokens / 128;
-    p->capacity = pool_bytes;
+    p->ext.capacity = pool_bytes;
     p->k_dev = k_dev;
     p->v_dev = v_dev;
     const size_t n = (size_t)p->max_tiles * p->B * p->H;
@@ -325,8 +332,8 @@ kvq_status kvq_pool_create(const kvq_cache* c, int64_t pool_bytes, int64_t* k_de
 }
 
 void kvq_pool_destroy(kvq_pool* p) { delete p; }
-int64_t kvq_pool_used_bytes(const kvq_pool* p) { return p ? p->used : -1; }
-int64_t kvq_pool_high_water(const kvq_pool* p) { return p ? p->high : -1; }
+int64_t kvq_pool_used_bytes(const kvq_pool* p) { return p ? p->ext.used : -1; }
+int64_t kvq_pool_high_water(const kvq_pool* p) { return p ? p->ext.high : -1; }
 
 kvq_status kvq_append(kvq_cache* c, kvq_pool* pool, int64_t budget, int32_t floor_bits,
                       const void* k, const void* v, kvq_dtype in_dtype, const int64_t k_strides[3],
@@ -347,6 +354,8 @@ kvq_status kvq_append(kvq_cache* c, kvq_pool* pool, int64_t budget, int32_t floo
                  c->v_tile_off != pool->v_dev))
       return KVQ_EINVAL;
     if (!pool && (c->k_tile_off || c->v_tile_off)) return KVQ_EINVAL;
+    // the launch limits of kvq_shrink and kvq_quantize, checked before any shrink
+    if ((int64_t)c->batch * c->n_kv_heads > 65535 || n_new / 128 > 65535) return KVQ_EUNSUPPORTED;
     // plan the halvings first: fail with no work done if the floor cannot hold it
     int bits = c->k_bits, halvings = 0;
     const int32_t target = c->n_tokens + n_new;
@@ -355,34 +364,40 @@ kvq_status kvq_append(kvq_cache* c, kvq_pool* pool, int64_t budget, int32_t floo
       bits /= 2;
       halvings++;
     }
+    // the pool's side of the halvings (each frees the second half of every
+    // stored tile) and of the new tiles, planned on a copy of its extents:
+    // running out of free extents fails here, before any device work
+    const size_t per = (size_t)c->batch * c->n_kv_heads;
+    const int t_first = c->n_tokens / 128, t_last = target / 128;
+    std::vector<int64_t> new_k, new_v;
+    PoolExtents plan;
+    if (pool) {
+      plan = pool->ext;
+      int w = c->k_bits;
+      for (int i = 0; i < halvings; i++) {
+        w /= 2;
+        const int64_t half = tile_bytes(w);              // the halved tile size
+        for (size_t idx = 0; idx < (size_t)t_first * per; idx++) {
+          plan.release(pool->k_host[idx] + half, half);
+          plan.release(pool->v_host[idx] + half, half);
+        }
+      }
+      const int64_t sz = tile_bytes(w);
+      new_k.resize((size_t)(t_last - t_first) * per);
+      new_v.resize(new_k.size());
+      for (size_t i = 0; i < new_k.size(); i++)
+        if (!plan.alloc(sz, &new_k[i]) || !plan.alloc(sz, &new_v[i])) return KVQ_EBUDGET;
+    }
     for (int i = 0; i < halvings; i++) {
       s = kvq_shrink(c, c->k_bits / 2, stream);
       if (s != KVQ_OK) return s;
       if (n_shrinks) (*n_shrinks)++;
-      if (pool) {
-        const int64_t half = tile_bytes(c->k_bits);     // new (halved) tile size
-        const int n_tiles = c->n_tokens / 128;
-        for (int t = 0; t < n_tiles; t++)
-          for (int i2 = 0; i2 < c->batch * c->n_kv_heads; i2++) {
-            const size_t idx = (size_t)t * c->batch * c->n_kv_heads + i2;
-            pool->release(pool->k_host[idx] + half, half);
-            pool->release(pool->v_host[idx] + half, half);
-          }
-      }
     }
     if (pool) {
-      const int64_t sz = tile_bytes(c->k_bits);
-      const int t_first = c->n_tokens / 128, t_last = target / 128;
-      const size_t per = (size_t)c->batch * c->n_kv_heads;
-      for (int t = t_first; t < t_last; t++)
-        for (size_t i2 = 0; i2 < per; i2++) {
-          int64_t ko, vo;
-          if (!pool->alloc(sz, &ko)) return KVQ_EBUDGET;
-          if (!pool->alloc(sz, &vo)) return KVQ_EBUDGET;
-          pool->k_host[t * per + i2] = ko;
-          pool->v_host[t * per + i2] = vo;
-        }
+      pool->ext = std::move(plan);
       const size_t first = (size_t)t_first * per, count = (size_t)(t_last - t_first) * per;
+      std::copy(new_k.begin(), new_k.end(), pool->k_host.begin() + first);
+      std::copy(new_v.begin(), new_v.end(), pool->v_host.begin() + first);
       if (hipMemcpyAsync(pool->k_dev + first, pool->k_host.data() + first, count * 8,
                          hipMemcpyHostToDevice, stream) != hipSuccess)
         return KVQ_EHIP;

@@ -264,3 +264,27 @@ def test_window_validation_rejects_before_launch():
     mixed = _fake_struct(2, 2, 1024, kvq.KMIXED, 2)
     assert call(_fake_window(mixed), mixed, 300, budget=1 << 40) == kvq.EUNSUPPORTED  # budget: uniform widths
     assert w.n_first == 0 and w.n_recent == 0 and s16.n_tokens == 0 and s16.k_bits == 16
+
+
+def test_append_pool_exhausted_before_work():
+    """A pool without room for the new tiles fails kvq_append with
+    KVQ_EBUDGET before any device work: the cache and the pool's counters are
+    unchanged (the offset tables are never written, so fake pointers do)."""
+    L = _lib()
+    P = ctypes.byref
+    vp = ctypes.c_void_p
+    st3 = (ctypes.c_int64 * 3)(0, 0, 128)
+    s = _fake_struct(1, 2, 1024, 16, 16)
+    s.k_tile_off = s.v_tile_off = FAKE + 4096
+    s.k_tile_stride = s.v_tile_stride = 0
+    pool = vp()
+    # 64 KiB: two 32 KiB 16-bit tiles, while 128 tokens of 2 streams need four
+    assert L.kvq_pool_create(P(s), 64 << 10, vp(FAKE + 4096), vp(FAKE + 4096), P(pool)) == kvq.OK
+    try:
+        n = ctypes.c_int32(-1)
+        r = L.kvq_append(P(s), pool, 1 << 40, 16, vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 128, None, P(n))
+        assert r == kvq.EBUDGET and n.value == 0
+        assert s.n_tokens == 0 and s.k_bits == 16
+        assert L.kvq_pool_used_bytes(pool) == 0 and L.kvq_pool_high_water(pool) == 0
+    finally:
+        L.kvq_pool_destroy(pool)
