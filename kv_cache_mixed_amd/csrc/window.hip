@@ -38,6 +38,9 @@ hipError_t launch_window_copy(const void* k, const void* v, const int64_t ks[3],
                               int elt_bytes, void* wk, void* wv, int B, int H, int m, int slot0,
                               hipStream_t st) {
   if (m <= 0) return hipSuccess;
+  // the rows must lie inside the window (the caller's plan guarantees it)
+  if (slot0 < 0 || slot0 + m > KVQ_WINDOW_ROWS || (elt_bytes != 2 && elt_bytes != 4))
+    return hipErrorInvalidValue;
   const int row_bytes = 128 * elt_bytes;
   const int64_t n_chunks = (int64_t)B * H * m * (row_bytes / 16);
   const dim3 grid((unsigned)((n_chunks + 255) / 256), 2), block(256);
