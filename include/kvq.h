@@ -21,9 +21,7 @@
  *     documented.
  *   - All device work is enqueued on the given stream; calls return before it
  *     completes.  Every argument is validated on the host first: any status
- *     other than KVQ_OK / KVQ_EHIP means no device work was enqueued (one
- *     exception, documented at kvq_window_append: a call that packs several
- *     groups can run out of pool extents after its earlier groups).
+ *     other than KVQ_OK / KVQ_EHIP means no device work was enqueued.
  *     KVQ_EHIP means a HIP call failed (work already enqueued may be partial).
  *   - No exceptions cross the ABI.  The library holds no global mutable
  *     state; calls on different caches are independent.  Calls that touch the
@@ -120,7 +118,7 @@ typedef enum {
     KVQ_OK = 0,
     KVQ_EINVAL = 1,        /* invalid argument (null pointer, bad size, bad width ...) */
     KVQ_EUNSUPPORTED = 2,  /* valid request this build does not implement */
-    KVQ_EBUDGET = 3,       /* kvq_append: the group does not fit even at floor_bits */
+    KVQ_EBUDGET = 3,       /* kvq_append / kvq_window_append / kvq_allocate_bits: the budget or the pool cannot hold it */
     KVQ_EWORKSPACE = 4,    /* workspace pointer null or smaller than required */
     KVQ_EHIP = 5           /* a HIP runtime call or kernel launch failed */
 } kvq_status;
@@ -295,8 +293,9 @@ int64_t kvq_pool_high_water(const kvq_pool *pool);
  * contiguous placement when pool is NULL) and kvq_quantize them at the
  * resulting width.  If the group does not fit even at floor_bits, or the
  * pool has no free extents left for the new tiles (after the halvings'
- * releases), returns KVQ_EBUDGET before any work, the pool unchanged.  *n_shrinks (may be NULL) receives the number
- * of halvings performed.  Input arguments as for kvq_quantize. */
+ * releases), returns KVQ_EBUDGET before any work, the pool unchanged.
+ * *n_shrinks (may be NULL) receives the number of halvings performed.  Input
+ * arguments as for kvq_quantize. */
 kvq_status kvq_append(kvq_cache *cache, kvq_pool *pool, int64_t budget_bytes, int32_t floor_bits,
                       const void *k, const void *v, kvq_dtype in_dtype,
                       const int64_t k_strides[3], const int64_t v_strides[3], int32_t n_new,
@@ -352,11 +351,11 @@ typedef struct kvq_window {
  * widths when budget_bytes < 0 (pool must be NULL).  The cache's
  * n_tokens (and k_bits / v_bits after halvings) and the window's n_first /
  * n_recent are updated; *n_shrinks (may be NULL) counts the halvings.
- * Arguments, capacity (max_tokens) and the budget at floor_bits for the
- * final token count are checked before any device work.  KVQ_EBUDGET from
- * the pool allocator after some groups were packed (fragmentation) leaves
- * the structs describing exactly the tokens taken so far; KVQ_EHIP as
- * elsewhere.  All work is on `stream`; calls on one window must use one
+ * Arguments, capacity (max_tokens), the budget at floor_bits for the final
+ * token count and (with a pool) a replay of the group appends on a copy of
+ * the pool's free extents are checked before any device work: any status
+ * but KVQ_OK / KVQ_EHIP leaves the cache, the pool and the window as they
+ * were.  After KVQ_EHIP the structs describe the work enqueued so far.  All work is on `stream`; calls on one window must use one
  * stream (or be ordered by the caller). */
 kvq_status kvq_window_append(kvq_window *w, kvq_cache *cache, kvq_pool *pool, int64_t budget_bytes,
                              int32_t floor_bits, const void *k, const void *v,

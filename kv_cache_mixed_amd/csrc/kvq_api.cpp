@@ -414,6 +414,46 @@ kvq_status kvq_append(kvq_cache* c, kvq_pool* pool, int64_t budget, int32_t floo
 
 // Token-granular append: the window of unpacked tokens (first token + recent
 // tokens) and the hand-over of full 128-token groups to the packed cache.
+
+// Replays n_groups one-group kvq_append calls (halvings from the byte count,
+// the pool's releases and allocations in kvq_append's order) on a copy of the
+// pool's extents; false if an allocation would fail.  Offsets of the tiles
+// placed during the replay are tracked so that later halvings release their
+// halves too.
+static bool pool_replay_ok(const kvq_cache* c, const kvq_pool* pool, int64_t budget, int32_t floor_bits,
+                           int64_t n_groups) {
+  PoolExtents ext = pool->ext;
+  std::map<size_t, int64_t> k_new, v_new;
+  const size_t per = (size_t)c->batch * c->n_kv_heads;
+  auto off = [&](const std::map<size_t, int64_t>& placed, const std::vector<int64_t>& host, size_t idx) {
+    const auto it = placed.find(idx);
+    return it != placed.end() ? it->second : host[idx];
+  };
+  int32_t n = c->n_tokens;
+  int bits = c->k_bits;
+  for (int64_t g = 0; g < n_groups; g++) {
+    const int32_t target = n + 128;
+    while (kvq_cache_bytes(c, target, bits, bits) > budget) {
+      if (bits == 1 || bits / 2 < floor_bits) return false;
+      bits /= 2;
+      const int64_t half = tile_bytes(bits);
+      for (size_t idx = 0; idx < (size_t)(n / 128) * per; idx++) {
+        ext.release(off(k_new, pool->k_host, idx) + half, half);
+        ext.release(off(v_new, pool->v_host, idx) + half, half);
+      }
+    }
+    const int64_t sz = tile_bytes(bits);
+    for (size_t idx = (size_t)(n / 128) * per; idx < (size_t)(target / 128) * per; idx++) {
+      int64_t ko, vo;
+      if (!ext.alloc(sz, &ko) || !ext.alloc(sz, &vo)) return false;
+      k_new[idx] = ko;
+      v_new[idx] = vo;
+    }
+    n = target;
+  }
+  return true;
+}
+
 kvq_status kvq_window_append(kvq_window* w, kvq_cache* c, kvq_pool* pool, int64_t budget,
                              int32_t floor_bits, const void* k, const void* v, const int64_t ks[3],
                              const int64_t vs[3], int32_t n_new, hipStream_t stream,
@@ -470,6 +510,10 @@ kvq_status kvq_window_append(kvq_window* w, kvq_cache* c, kvq_pool* pool, int64_
     if (direct / 128 > 65535) return KVQ_EUNSUPPORTED;
     if (budget >= 0 && packed > 0 &&
         kvq_cache_bytes(c, (int32_t)(c->n_tokens + packed), floor_bits, floor_bits) > budget)
+      return KVQ_EBUDGET;
+    // under a budget the groups go to kvq_append one at a time: replay them
+    // on the pool first, so that running out of extents fails before any work
+    if (budget >= 0 && pool && packed > 0 && !pool_replay_ok(c, pool, budget, floor_bits, packed / 128))
       return KVQ_EBUDGET;
 
     const int64_t wst[3] = {(int64_t)c->n_kv_heads * KVQ_WINDOW_ROWS * 128, KVQ_WINDOW_ROWS * 128, 128};

@@ -288,3 +288,29 @@ def test_append_pool_exhausted_before_work():
         assert L.kvq_pool_used_bytes(pool) == 0 and L.kvq_pool_high_water(pool) == 0
     finally:
         L.kvq_pool_destroy(pool)
+
+
+def test_window_pool_exhausted_before_work():
+    """kvq_window_append under a budget replays its group appends on the
+    pool first: a pool without room for them fails with KVQ_EBUDGET before
+    the first copy, leaving cache, pool and window unchanged."""
+    L = _lib()
+    P = ctypes.byref
+    vp = ctypes.c_void_p
+    st = (ctypes.c_int64 * 3)(2 * 1000 * 128, 1000 * 128, 128)
+    s = _fake_struct(1, 2, 1024, 16, 16)
+    s.k_tile_off = s.v_tile_off = FAKE + 4096
+    s.k_tile_stride = s.v_tile_stride = 0
+    pool = vp()
+    # 192 KiB: room for the 16-bit tiles of one group of 2 streams (4 x 32 KiB), not of two
+    assert L.kvq_pool_create(P(s), 192 << 10, vp(FAKE + 4096), vp(FAKE + 4096), P(pool)) == kvq.OK
+    try:
+        w = _fake_window(s)
+        n = ctypes.c_int32(-1)
+        # first token + 300: two groups packed straight from the input, 43 held
+        r = L.kvq_window_append(P(w), P(s), pool, 1 << 40, 16, vp(FAKE), vp(FAKE), st, st, 301, None, P(n))
+        assert r == kvq.EBUDGET and n.value == 0
+        assert (w.n_first, w.n_recent, s.n_tokens, s.k_bits) == (0, 0, 0, 16)
+        assert L.kvq_pool_used_bytes(pool) == 0 and L.kvq_pool_high_water(pool) == 0
+    finally:
+        L.kvq_pool_destroy(pool)
