@@ -261,6 +261,10 @@ def test_window_validation_rejects_before_launch():
     tabled = _fake_struct(2, 2, 1024, 16, 16)
     tabled.k_tile_off = tabled.v_tile_off = FAKE                # tile tables without their pool
     assert call(_fake_window(tabled), tabled, 300, budget=1 << 40) == kvq.EINVAL
+    # without a budget the groups go to the contiguous placement: tile tables
+    # (a pool's, unfilled past its tiles) are rejected before any work
+    assert call(_fake_window(tabled), tabled, 300, budget=-1) == kvq.EINVAL
+    assert call(_fake_window(tabled), tabled, 5, budget=-1) == kvq.EINVAL
     mixed = _fake_struct(2, 2, 1024, kvq.KMIXED, 2)
     assert call(_fake_window(mixed), mixed, 300, budget=1 << 40) == kvq.EUNSUPPORTED  # budget: uniform widths
     assert w.n_first == 0 and w.n_recent == 0 and s16.n_tokens == 0 and s16.k_bits == 16

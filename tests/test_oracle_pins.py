@@ -658,3 +658,106 @@ def test_rope_period_against_pages():
     nx = np.hypot(x[:, :64].astype(np.float64), x[:, 64:])
     ny = np.hypot(y[:, :64].astype(np.float64), y[:, 64:])
     assert np.allclose(nx, ny, rtol=1e-6)
+
+
+# ---------------------------------------------------------------------------
+# mixed-width keys: the oracle's quantizer against an independent build
+# ---------------------------------------------------------------------------
+# Class widths of the mixed key tile, written here from the channel classes of
+# "Channel-Aware Mixed-Precision Quantization ..." (Key design 3: 4-bit
+# retrieval channels, 3-bit outlier channels paired with as many 1-bit
+# sub-normal channels, 2-bit for the rest, packed so that every byte holds 8
+# code bits) and the slot order of the header's mixed layout text: 8 slots of
+# 4 bits, then 8 (3-bit, 1-bit) pairs, then 104 slots of 2 bits.
+_MIXED_WIDTHS = [4] * 8 + [3, 1] * 8 + [2] * 104
+
+
+def _narrow_ref(x, pdt):
+    """binary32 -> exact value of its narrowing, by library routines (numpy
+    binary16, torch float8_e4m3fn), not by the oracle"""
+    import torch
+    x = np.float32(x)
+    if pdt == oracle.F16:
+        return float(np.float16(x))
+    assert pdt == oracle.E4M3 and abs(float(x)) <= 448.0
+    return float(torch.tensor([float(x)], dtype=torch.float32).to(torch.float8_e4m3fn).float()[0])
+
+
+def _mixed_row_bytes(codes_row):
+    """34-byte logical row of one token: little-endian bit string of the slot
+    codes in slot order at the class widths (header layout text)"""
+    bits = 0
+    pos = 0
+    for j, w in enumerate(_MIXED_WIDTHS):
+        assert 0 <= codes_row[j] < (1 << w)
+        bits |= int(codes_row[j]) << pos
+        pos += w
+    assert pos == 272
+    return bits.to_bytes(34, "little")
+
+
+def _mixed_tile_bytes(codes):
+    """[128 tokens][128 slots] -> 4352-byte tile: logical bytes [8p, 8p+8) of
+    token t at 1024p + 8t (p < 4), bytes 32, 33 at 4096 + 2t (header text)"""
+    tile = bytearray(4352)
+    for t in range(128):
+        row = _mixed_row_bytes(codes[t])
+        for p in range(4):
+            tile[1024 * p + 8 * t: 1024 * p + 8 * t + 8] = row[8 * p: 8 * p + 8]
+        tile[4096 + 2 * t: 4096 + 2 * t + 2] = row[32:34]
+    return np.frombuffer(bytes(tile), dtype=np.uint8)
+
+
+@pytest.mark.parametrize("pdt", [oracle.E4M3, oracle.F16])
+def test_mixed_key_quantizer_against_independent_build(pdt):
+    """Every slot j of the oracle's mixed key tile quantizes channel
+    slot_chan[j] of the tile's 128 tokens at its class width: Z'_j is the
+    narrowed channel minimum, S'_j the narrowed (max - min) / (2^b_j - 1),
+    codes 0 and 2^b_j - 1 sit at that channel's argmin and argmax, every code
+    is the nearest level S'q + Z' (brute force, exact rationals; only near-ties
+    may differ by one) and the bytes equal an independent packing of the
+    header's layout text.  Channels get distinct ranges and the permutation is
+    not the identity, so a slot that reads the wrong channel or uses the wrong
+    width fails."""
+    rng = np.random.default_rng(1234 + pdt)
+    T = 256
+    chan_scale = np.exp(rng.uniform(-1.5, 1.5, 128)).astype(np.float32)
+    chan_shift = rng.uniform(-1.0, 1.0, 128).astype(np.float32)
+    k = (rng.standard_normal((T, 128)).astype(np.float32) * chan_scale + chan_shift).astype(np.float32)
+    if pdt == oracle.E4M3:
+        k = (k * np.float32(0.5)).astype(np.float32)
+    v = rng.standard_normal((T, 128)).astype(np.float32)
+    slot_chan = rng.permutation(128).astype(np.int16)
+    assert (slot_chan != np.arange(128)).sum() > 100
+    st = oracle.quantize_stream(k, v, 0, 2, pdt, slot_chan)
+    S_raw = oracle.decode(st.ks, pdt)
+    Z_raw = oracle.decode(st.kz, pdt)
+    for g in range(T // 128):
+        codes = oracle.unpack_mixed(st.k_tiles[g]).astype(np.int64)      # [token][slot]
+        exp_codes = np.zeros((128, 128), np.int64)
+        for j in range(128):
+            b = _MIXED_WIDTHS[j]
+            x = k[128 * g: 128 * g + 128, slot_chan[j]]
+            mn, mx = np.float32(x.min()), np.float32(x.max())
+            s32 = np.float32(np.float32(mx - mn) / np.float32(2 ** b - 1))
+            S, Z = _narrow_ref(s32, pdt), _narrow_ref(mn, pdt)
+            assert S_raw[g, j] == S and Z_raw[g, j] == Z, (g, j)
+            assert codes[np.argmin(x), j] == 0
+            if S > 0 and (mx - Z) / S > (2 ** b - 1) - 0.5:
+                assert codes[np.argmax(x), j] == 2 ** b - 1
+            Sf, Zf = Fraction(S), Fraction(Z)
+            for t in range(128):
+                if S == 0:
+                    best = 0
+                else:
+                    ex = (Fraction(float(x[t])) - Zf) / Sf
+                    best = min(max(round(ex), 0), 2 ** b - 1)
+                    if codes[t, j] != best:
+                        tol = max(abs(ex), Fraction(1)) / 2 ** 21
+                        assert abs(abs(ex - math.floor(ex)) - Fraction(1, 2)) < tol, (g, j, t)
+                        best = int(codes[t, j])
+                exp_codes[t, j] = best
+            xhat = S * codes[:, j].astype(np.float64) + Z
+            bound = max(S / 2, Z - float(mn), float(mx) - Z - (2 ** b - 1) * S)
+            assert np.abs(x - xhat).max() <= bound * (1 + 1e-6) + 1e-7
+        assert np.array_equal(st.k_tiles[g], _mixed_tile_bytes(exp_codes))
