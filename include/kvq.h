@@ -162,7 +162,10 @@ typedef struct kvq_cache {
     void *v_scale;            /* device [B][Hkv][max_tokens] */
     void *v_zero;             /* device [B][Hkv][max_tokens] */
     const int16_t *k_slot_chan; /* device [Hkv][128]: channel held by slot j
-                                   (mixed keys only, a permutation per head) */
+                                   (mixed keys only, a permutation per head;
+                                   the kernels use only its low 7 bits, so a
+                                   map that is not a permutation reads wrong
+                                   channels but never outside a row) */
 } kvq_cache;
 
 /* Human-readable name of a status code (static string). */
@@ -348,7 +351,8 @@ typedef struct kvq_window {
  * `pool`; uniform widths only) when budget_bytes >= 0, one group per call in
  * token order, so the packed cache depends on the token sequence only and
  * not on how it was split into calls; or by kvq_quantize at the cache's
- * widths when budget_bytes < 0 (pool must be NULL).  The cache's
+ * widths when budget_bytes < 0 (pool and the cache's tile tables must then
+ * be NULL: groups go to the contiguous placement).  The cache's
  * n_tokens (and k_bits / v_bits after halvings) and the window's n_first /
  * n_recent are updated; *n_shrinks (may be NULL) counts the halvings.
  * Arguments, capacity (max_tokens), the budget at floor_bits for the final

@@ -784,7 +784,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       qv[r] = 0;
       if (cs < NS && cbh < BH) {
         const int chh = cbh % g.H;
-        qv[r] = a.q[((int64_t)grp * NS * G + cn) * 128 + g.slot_chan[chh * 128 + j]] ^ (uint16_t)qflip;
+        qv[r] = a.q[((int64_t)grp * NS * G + cn) * 128 + (g.slot_chan[chh * 128 + j] & 127)] ^ (uint16_t)qflip;
       }
     }
     if (q0 < t_count) load(b0, q0, 0);

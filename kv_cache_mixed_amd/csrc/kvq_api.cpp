@@ -485,7 +485,10 @@ kvq_status kvq_window_append(kvq_window* w, kvq_cache* c, kvq_pool* pool, int64_
                    c->v_tile_off != pool->v_dev))
         return KVQ_EINVAL;
       if (!pool && (c->k_tile_off || c->v_tile_off)) return KVQ_EINVAL;
-    } else if (pool) {
+    } else if (pool || c->k_tile_off || c->v_tile_off) {
+      // without a budget the groups go to kvq_quantize at the contiguous
+      // placement: tile tables (which a pool fills only when it allocates)
+      // could name tiles that were never placed
       return KVQ_EINVAL;
     }
 

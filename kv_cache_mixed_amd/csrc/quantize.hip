@@ -138,7 +138,7 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __re
   const int tile_local = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tile = t0 / 128 + tile_local;
   const int j = threadIdx.x & 127, half = threadIdx.x >> 7;
-  const int chan = (KB == 0) ? (int)g.slot_chan[h * 128 + j] : j;
+  const int chan = (KB == 0) ? ((int)g.slot_chan[h * 128 + j] & 127) : j;   // masked: never outside the row
   const int bits = (KB == 0) ? mixed_slot_bits(j) : KB;
 
   const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (int64_t)(tile_local * 128) * st + chan;
