@@ -58,6 +58,9 @@ def _parse():
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 512 MiB device copy three times (reference "
                          "dispatch for scaling HBM counters)")
+    ap.add_argument("--case", choices=sorted(CASES),
+                    help="time only the decode call of one workload (cold copies rotated), "
+                         "print one line and exit -- for per-kernel profiler runs")
     return ap.parse_args()
 
 
@@ -67,6 +70,53 @@ def decode_bytes(B, H, Hq, T, k_bits, v_bits, pb):
     per_tok = (128 * k_bits + 128 * v_bits) // 8 if k_bits else 34 + 128 * v_bits // 8
     params = 2 * pb + 2 * pb          # key S,Z per token (128 per 128-token tile) + value S,Z
     return B * H * T * (per_tok + params) + B * Hq * 128 * 2 + B * Hq * 128 * 4
+
+
+# single decode workloads for --case: (batch, kv heads, q heads, tokens,
+# key bits (0 = mixed), value bits, parameter dtype name)
+CASES = {
+    "qwen7b_layer_4bit": (16, 4, 28, 32768, 4, 4, "F16"),
+    "qwen7b_layer_2bit": (16, 4, 28, 32768, 2, 2, "F16"),
+    "qwen32b_layer_4bit": (16, 8, 40, 32768, 4, 4, "F16"),
+    "qwen32b_layer_2bit": (16, 8, 40, 32768, 2, 2, "F16"),
+    "qwen32b_layer_8bit": (16, 8, 40, 32768, 8, 8, "F16"),
+    "llama8b_mixed_128k": (1, 8, 32, 131072, 0, 2, "E4M3"),
+}
+
+
+def decode_case(name, steps, warmup):
+    """decode calls of one workload over rotated cache copies (> 600 MB
+    together); prints one JSON line with the event-timed call average"""
+    import torch
+    from kv_cache_mixed_amd import kvq, synth
+    kvq.load()
+    dev = torch.device("cuda:0")
+    B, H, Hq, T, kb, vb, pname = CASES[name]
+    pdt = getattr(kvq, pname)
+    scale = 1.0 / math.sqrt(128)
+    if kb == 0:
+        inp = synth.mixed_layer_device(B, H, Hq, T, seed=4, device=dev)
+        mk = lambda: kvq.PackedCache(B, H, T, kvq.KMIXED, vb, pdt, slot_chan=inp["slot_chan"], device=dev)
+    else:
+        inp = synth.layer_device(B, H, Hq, T, seed=1234, device=dev)
+        mk = lambda: kvq.PackedCache(B, H, T, kb, vb, pdt, device=dev)
+    alg = decode_bytes(B, H, Hq, T, kb, vb, kvq.PARAM_BYTES[pdt])
+    caches = []
+    for _ in range(max(2, math.ceil(600e6 / alg))):
+        c = mk()
+        c.quantize(inp["k"], inp["v"], 0)
+        caches.append(c)
+    q = inp["q"]
+    del inp
+    torch.cuda.empty_cache()
+    outs = [torch.empty((B, Hq, 128), dtype=torch.float32, device=dev) for _ in caches]
+    wss = [c.workspace(Hq) for c in caches]
+    nc = len(caches)
+    ms = time_block(torch, lambda i: caches[i % nc].decode_attn(q, scale, out=outs[i % nc], workspace=wss[i % nc]),
+                    steps, warmup)
+    print(json.dumps({"case": name, "ms": round(ms, 5), "GB/s": round(alg / ms / 1e6, 1),
+                      "pct_of_peak": round(100 * alg / ms / 1e6 / PEAK_HBM_GBS, 2), "bytes": alg,
+                      "copies": nc, "steps": steps}))
 
 
 def kernel_source_digest():
@@ -264,15 +314,34 @@ def progressive_rows(torch, kvq, synth, dev, scale):
                                      "note": "pool layout, single cache (partly Infinity-Cache resident)"}}
 
 
+STEP_WIDTHS = (2, 4, 8)
+STEP_BUDGET_FRAC = 0.195
+
+
+def step_width_table(kvq, synth, B=16, H=8, T=32768, L=64):
+    """Per-layer widths of the 64-layer step from the block-wise allocation
+    (PM-KVQ Key design 2, kvq_allocate_bits): synthetic sensitivities
+    (synth.layer_sensitivities), each layer's cache bytes at 2/4/8 bits with
+    binary16 scales and zeros, and a budget M of 19.5% of the 64 layers'
+    16-bit (binary16) KV size.  Returns (widths, M, objective)."""
+    import numpy as np
+    sens = synth.layer_sensitivities(L, STEP_WIDTHS, seed=0)
+    per = [B * H * T * (128 * b // 8 * 2 + 4 * 2) for b in STEP_WIDTHS]
+    nbytes = np.array([per] * L, dtype=np.int64)
+    budget = int(STEP_BUDGET_FRAC * L * B * H * T * 128 * 2 * 2)
+    choice, obj = kvq.allocate_bits(sens, nbytes, budget)
+    return [STEP_WIDTHS[c] for c in choice], budget, obj
+
+
 def qwen32b_step_rows(torch, kvq, synth, dev, scale, n_steps=5):
     """Qwen2.5-32B-shaped full decode step: 64 layers (B=16, Hkv=8, Hq=40,
-    T=32768), each layer's cache packed at the width of the seeded per-layer
-    table (8 bits for layer 0, else 4 or 2, mean about 2.84 bits), generated
-    with the layer generator (seed = base + layer) and quantized one layer at
-    a time.  One step = the 64 layers' decode calls back to back; the 26 GB of
+    T=32768), each layer's cache packed at the width the block-wise
+    allocation gives it under the budget M (step_width_table), generated with
+    the layer generator (seed = base + layer) and quantized one layer at a
+    time.  One step = the 64 layers' decode calls back to back; the 26 GB of
     packed caches are far larger than the Infinity Cache."""
     B, H, Hq, T, L = 16, 8, 40, 32768, 64
-    bits = synth.layer_bits_table(L, seed=0)
+    bits, budget, obj = step_width_table(kvq, synth, B, H, T, L)
     caches, qs, alg = [], [], 0
     for layer, b in enumerate(bits):
         inp = synth.layer_device(B, H, Hq, T, seed=500 + layer, device=dev)
@@ -309,6 +378,9 @@ def qwen32b_step_rows(torch, kvq, synth, dev, scale, n_steps=5):
         "tokens_per_s": round(B / (ms * 1e-3), 1), "bytes": alg,
         "layers_per_width": {str(k): v for k, v in counts.items()},
         "mean_bits": round(sum(bits) / len(bits), 3),
+        "widths_from": "kvq_allocate_bits, synthetic sensitivities, budget M = %d B (%.1f%% of the 16-bit size)"
+                       % (budget, 100 * STEP_BUDGET_FRAC),
+        "allocation_objective": obj,
         "note": "attention only, 64 back-to-back layer calls per step"}}
 
 
@@ -420,6 +492,9 @@ def cpu_baseline(inp, B, H, Hq, k_bits, pdt, seconds):
 
 def main():
     args = _parse()
+    if args.case:
+        decode_case(args.case, args.steps, args.warmup)
+        return
     if args.gpus != 1:
         print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)

@@ -127,16 +127,19 @@ def mixed_layer(B: int, Hkv: int, Hq: int, T: int, seed: int):
     return dict(k=k, v=v, q_bf16=to_bf16_bits(q), slot_chan=slot_chan)
 
 
-def layer_bits_table(n_layers: int = 64, seed: int = 0):
-    """Per-layer widths for the 64-layer step: layer 0 at 8 bits; layer l >= 1
-    at 4 bits with probability 0.75*l/(n_layers-1), else 2 bits (deeper layers
-    get more bits), so the expected mean is about 2.84 bits."""
+def layer_sensitivities(n_layers: int = 64, widths=(2, 4, 8), seed: int = 0) -> np.ndarray:
+    """Synthetic per-block sensitivities s[l][j] of block l at width widths[j]
+    ([n_layers][len(widths)] float64), standing in for PM-KVQ's
+    gradient-based ones (Key design 2), which need a trained model.  A block's
+    importance a_l grows with depth (1 + 3 l / (n_layers - 1)), block 0 is
+    weighted 500x (the first block's cache is the most sensitive), times a
+    seeded log-normal factor (sigma 0.5); s[l][j] = a_l / (2^b - 1)^2, the
+    rounding-error variance of a b-bit uniform code relative to the squared
+    group range."""
     rng = np.random.default_rng(seed)
-    u = rng.random(n_layers)
-    bits = [8]
-    for l in range(1, n_layers):
-        bits.append(4 if u[l] < 0.75 * l / (n_layers - 1) else 2)
-    return bits
+    a = (1.0 + 3.0 * np.arange(n_layers) / max(n_layers - 1, 1)) * np.exp(rng.normal(0.0, 0.5, n_layers))
+    a[0] *= 500.0
+    return np.array([[a[l] / float((1 << b) - 1) ** 2 for b in widths] for l in range(n_layers)])
 
 
 def layer_device(B: int, Hkv: int, Hq: int, T: int, seed: int, device, n_outliers: int = 4,

@@ -99,3 +99,50 @@ def test_more_sensitive_blocks_get_more_bits():
     used = int(w[np.arange(L), ch].sum())
     assert used <= budget and budget - used < int(w[0, 1] - w[0, 0])
     assert got_bits[0] == got_bits.max()           # block 0 is the most sensitive here
+
+
+def _step_instance(L, B=16, H=8, T=32768):
+    from kv_cache_mixed_amd import synth
+    widths = (2, 4, 8)
+    sens = synth.layer_sensitivities(L, widths, seed=0)
+    per = [B * H * T * (128 * b // 8 * 2 + 4 * 2) for b in widths]
+    nbytes = np.array([per] * L, dtype=np.int64)
+    budget = int(0.195 * L * B * H * T * 128 * 2 * 2)
+    return widths, sens, nbytes, budget
+
+
+def test_step_widths_reduced_instance_matches_enumeration():
+    """The allocation that drives the 64-layer step's widths, on a reduced
+    instance of the same recipe (10 layers, the same budget fraction): the
+    library's table equals the oracle's enumeration of all 3^10 tables."""
+    _lib_or_skip()
+    widths, sens, nbytes, budget = _step_instance(10)
+    want, want_cost = oracle.allocate_bits_bruteforce(sens, nbytes, budget)
+    got, got_cost = kvq.allocate_bits(sens, nbytes, budget)
+    assert got.tolist() == want and got_cost == want_cost
+
+
+def test_step_widths_full_instance():
+    """64 layers at 19.5% of the 16-bit size: the table fits the budget, the
+    first block takes 8 bits, deeper blocks hold more of the 4-bit widths,
+    and no single swap of two blocks' widths (same bytes) or move of one block
+    to a cheaper width lowers the objective."""
+    _lib_or_skip()
+    import bench
+    widths, sens, nbytes, budget = _step_instance(64)
+    bits, M, obj = bench.step_width_table(kvq, __import__("kv_cache_mixed_amd.synth").synth)
+    assert M == budget
+    ch = [widths.index(b) for b in bits]
+    assert sum(int(nbytes[i][c]) for i, c in enumerate(ch)) <= budget
+    assert bits[0] == 8 and 2.7 < np.mean(bits) < 3.0
+    assert sum(b == 4 for b in bits[32:]) > sum(b == 4 for b in bits[1:32])
+    total = sum(int(nbytes[i][c]) for i, c in enumerate(ch))
+    base = sum(sens[i][c] for i, c in enumerate(ch))
+    for i in range(64):
+        for j in range(64):
+            if ch[i] != ch[j]:
+                alt = base - sens[i][ch[i]] - sens[j][ch[j]] + sens[i][ch[j]] + sens[j][ch[i]]
+                assert alt >= base - 1e-12 * abs(base)
+        for c in range(3):
+            if total - nbytes[i][ch[i]] + nbytes[i][c] <= budget:
+                assert base - sens[i][ch[i]] + sens[i][c] >= base - 1e-12 * abs(base)
