@@ -89,6 +89,8 @@ typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
 
 // A bit field of a loaded 32-bit word that becomes one f16x2 operand register:
 // word index, right shift before masking, bit position and width inside each
@@ -1013,52 +1015,61 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       for (int cb = 0; cb < 8; cb++) acc_o[cb] *= rescale;
     }
     // e''(i) = e(i) * 2^ps * 2^W(i) straight from the exponent; the running
-    // sums l_run, z_run are kept in units of 2^ps
+    // sums l_run, z_run are kept in units of 2^ps.
+    // The probability operand of PV is one binary16 per token (P~ = rne(P)).
+    // Its rounding residual r = P - P~ meets every code of the token; the
+    // part r * VMID (VMID = the codes' midpoint (2^VB - 1) / 2) is added back
+    // exactly through the zero-point sum -- e * (Z + VMID * S) - VMID * P~ --
+    // and only r * (code - VMID), which has no common sign, is left out.
+    constexpr float VMID = 0.5f * (float)((1u << VB) - 1u);
     const float c0 = bk0 - m_run + (float)min(VH - e_run, PSMAX);
     float p[TPS];
     float lsum = 0.0f;
-    float zc[10];
+    float zc[10], zr[10];
 #pragma unroll
-    for (int k = 0; k < 10; k++) zc[k] = 0.0f;
+    for (int k = 0; k < 10; k++) { zc[k] = 0.0f; zr[k] = 0.0f; }
 #pragma unroll
     for (int i = 0; i < TPS; i++) {
       const int W = tok_w<VB, FVS>(i);
       const float e = __builtin_amdgcn_exp2f(fmaf(ak, lv[i], c0 + (float)W));
       lsum = fmaf(e, exp2i(-W), lsum);
       if constexpr (MIX) {
-        zc[w_class(W)] = fmaf(e, half_at(rvz, i), zc[w_class(W)]);
+        zc[w_class(W)] = fmaf(e, __builtin_fmaf(VMID, half_at(rvs, i), half_at(rvz, i)), zc[w_class(W)]);
         p[i] = fmaf(e, half_at(rvs, i), 0.0f);
       } else {
-        zc[w_class(W)] = fmaf(e, vz[i], zc[w_class(W)]);
+        zc[w_class(W)] = fmaf(e, fmaf(VMID, vs[i], vz[i]), zc[w_class(W)]);
         p[i] = e * vs[i];
       }
     }
-    float zsum = zc[0];
-#pragma unroll
-    for (int k = 1; k < 10; k++)
-      if (class_used<VB, FVS, TPS>(k)) zsum = fmaf(zc[k], exp2i(-class_w<VB>(k)), zsum);
     l_run += lsum;
-    z_run += zsum;
 
-    // ---- P operand (split hi/lo) and PV; every sub-tile has the field
-    // layout of sub-tile 0, shifted by WVS words and TPS tokens
-    uint32_t bvh[FVS], bvl[FVS];
+    // ---- P operand and PV; every sub-tile has the field layout of sub-tile
+    // 0, shifted by WVS words and TPS tokens
+    uint32_t bvh[FVS];
 #pragma unroll
     for (int ff = 0; ff < FVS; ff++) {
       // a token whose codes span two fields (the bytes of a 16-bit code)
       // carries the weight of its first field; the other gets the difference
       const Fld F = ufield<VB>(ff);
-      const float dw = exp2i((F.wexp - F.pos) - tok_w<VB, FVS>(F.lo));
-      split_pack(p[F.lo] * dw, p[F.hi] * dw, bvh[ff], bvl[ff], m1);
+      const int dwe = (F.wexp - F.pos) - tok_w<VB, FVS>(F.lo);
+      const f16x2 h = __builtin_convertvector((f32x2){p[F.lo] * exp2i(dwe), p[F.hi] * exp2i(dwe)}, f16x2);
+      bvh[ff] = __builtin_bit_cast(uint32_t, h);
+      // the tokens' first field: P~ of both tokens into the residual sums
+      if (dwe == 0) zr[w_class(tok_w<VB, FVS>(F.lo))] = __builtin_amdgcn_fdot2(h, (f16x2){1.0f16, 1.0f16},
+                                                                               zr[w_class(tok_w<VB, FVS>(F.lo))], false);
     }
+    float zsum = fmaf(-VMID, zr[0], zc[0]);
+#pragma unroll
+    for (int k = 1; k < 10; k++)
+      if (class_used<VB, FVS, TPS>(k)) zsum = fmaf(fmaf(-VMID, zr[k], zc[k]), exp2i(-class_w<VB>(k)), zsum);
+    z_run += zsum;
 #pragma unroll
     for (int s = 0; s < NS; s++) {
-      uint32_t bsh[FVS], bsl[FVS];
+      uint32_t bsh[FVS];
 #pragma unroll
       for (int ff = 0; ff < FVS; ff++) {
         const bool sel = (NS == 1) || (own == s);
         bsh[ff] = sel ? bvh[ff] : 0u;
-        bsl[ff] = sel ? bvl[ff] : 0u;
       }
       f32x4* ao = acc_o;
 #pragma unroll
@@ -1073,8 +1084,6 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
           }
 #pragma unroll
         for (int cb = 0; cb < 8; cb++) ao[cb] = mfma(av[cb], bsh + 4 * k, ao[cb]);
-#pragma unroll
-        for (int cb = 0; cb < 8; cb++) ao[cb] = mfma(av[cb], bsl + 4 * k, ao[cb]);
       }
     }
   };
