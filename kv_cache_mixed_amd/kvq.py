@@ -264,6 +264,34 @@ class PackedCache:
         except Exception:
             pass
 
+    def clone(self):
+        """A copy of the cache's device contents and widths, for decode only
+        (e.g. to rotate cold copies): a pool-layout clone keeps the tile
+        tables but no pool, so appends to it are rejected."""
+        import torch
+        c = PackedCache.__new__(PackedCache)
+        c.device, c.B, c.H, c.max_tokens = self.device, self.B, self.H, self.max_tokens
+        c.max_tiles, c.pdt, c.layout, c.pool, c._ws = self.max_tiles, self.pdt, self.layout, None, {}
+        s = KvqCacheStruct()
+        ctypes.pointer(s)[0] = self.s
+        c.k_codes = self.k_codes.clone()
+        c.v_codes = c.k_codes if self.v_codes is self.k_codes else self.v_codes.clone()
+        s.k_codes, s.v_codes = c.k_codes.data_ptr(), c.v_codes.data_ptr()
+        if self.layout == "contiguous":
+            c.k_stride, c.v_stride = self.k_stride, self.v_stride
+            c.k_off = c.v_off = None
+        else:
+            c.k_off, c.v_off = self.k_off.clone(), self.v_off.clone()
+            s.k_tile_off, s.v_tile_off = c.k_off.data_ptr(), c.v_off.data_ptr()
+        for name in ("k_scale", "k_zero", "v_scale", "v_zero"):
+            setattr(c, name, getattr(self, name).clone())
+        s.k_scale, s.k_zero = c.k_scale.data_ptr(), c.k_zero.data_ptr()
+        s.v_scale, s.v_zero = c.v_scale.data_ptr(), c.v_zero.data_ptr()
+        c.slot_chan = None if self.slot_chan is None else self.slot_chan.clone()
+        s.k_slot_chan = None if c.slot_chan is None else c.slot_chan.data_ptr()
+        c.s = s
+        return c
+
     # -- state ----------------------------------------------------------------
     @property
     def n_tokens(self):
