@@ -240,6 +240,25 @@ kvq_status kvq_decode_attn(const kvq_cache *cache, const void *q, int32_t n_q_he
                            float softmax_scale, float *out, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* Allocation-free decode attention, for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid allocation).  Same computation, arguments and errors as
+ * kvq_decode_attn, without a caller workspace: the counters and chunk
+ * partials live in a library-owned device array of KVQ_DECODE_SCRATCH_BYTES
+ * per GPU (static storage, held until the process ends; never allocated or
+ * freed by the call).  The array of the current device is used, so the
+ * stream must belong to the current device.  A call whose launch plan needs
+ * more scratch than the array holds returns KVQ_EWORKSPACE before any device
+ * work (about 520 * (n_chunks + 16) * batch * n_q_heads bytes; the Qwen2.5-7B- and
+ * 32B-shaped layers at 32K tokens need under 8 MiB).  The array keeps the
+ * last call's contents; its completion counters are zeroed by a small kernel
+ * on the stream at the first call on a device and after a failed launch.
+ * All calls on one GPU share the array: calls that may overlap in time (on
+ * different streams without ordering between them) race -- order them. */
+#define KVQ_DECODE_SCRATCH_BYTES (32u << 20)
+kvq_status kvq_decode_attn_noalloc(const kvq_cache *cache, const void *q, int32_t n_q_heads,
+                                   float softmax_scale, float *out, hipStream_t stream);
+
 /* Decode attention over the packed cache together with a residual segment
  * of res_len tokens per stream that are not packed ([PMKVQ] Training
  * strategy and Related work: as in KIVI, the first token and the most recent

@@ -42,6 +42,8 @@
 // exceeds it by more than TAU (log2 units), so e = 2^(logit - m) <= 2^TAU and
 // the output accumulator is rescaled only when some head's reference moved.
 #include "kvq_device.h"
+
+#include <mutex>
 // waves of the decode kernel resident per SIMD (register budget 512 / n)
 // A nonzero KVQ_DECODE_WAVES_PER_SIMD forces every decode instance to that
 // occupancy (tuning builds); 0 uses the per-instance table decode_occ().
@@ -1556,6 +1558,66 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
     e = hipGetLastError();
   }
   return e;
+}
+
+// ---------------------------------------------------------------------------
+// Scratch of the allocation-free decode: the counters and chunk partials that
+// a caller's workspace holds otherwise, in a file-scope device array (one
+// copy per GPU, kept until the process ends).  Host code never passes the
+// array's name to a kernel: its device address comes from
+// hipGetSymbolAddress, once per device, with that device current.
+// ---------------------------------------------------------------------------
+static __device__ __attribute__((aligned(256))) uint8_t scratch[KVQ_DECODE_SCRATCH_BYTES];
+
+__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0u;
+}
+
+namespace {
+constexpr int SCRATCH_DEVICES = 64;
+struct ScratchSlot {
+  void* ptr = nullptr;       // device address of this GPU's copy of `scratch`
+  bool clear = true;         // its counters must be zeroed before the next decode
+};
+std::mutex scratch_mu;
+ScratchSlot scratch_slots[SCRATCH_DEVICES];
+}  // namespace
+
+size_t decode_counter_bytes(int BH) { return cnt_bytes(BH); }
+
+hipError_t decode_scratch_acquire(void** ptr, int BH, hipStream_t st) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= SCRATCH_DEVICES) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lk(scratch_mu);
+  ScratchSlot& sl = scratch_slots[dev];
+  if (!sl.ptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (!p) return hipErrorInvalidSymbol;
+    sl.ptr = p;
+  }
+  if (sl.clear) {
+    // the counters of the in-kernel chunk combine start at zero; a fill
+    // kernel (not a memset node) on the caller's stream
+    const int n = (int)(cnt_bytes(BH) / 4);
+    hipLaunchKernelGGL(fill_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, st, (uint32_t*)sl.ptr, n);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    sl.clear = false;
+  }
+  *ptr = sl.ptr;
+  return hipSuccess;
+}
+
+void decode_scratch_mark_dirty() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_DEVICES) return;
+  std::lock_guard<std::mutex> lk(scratch_mu);
+  scratch_slots[dev].clear = true;
 }
 
 }  // namespace kvq

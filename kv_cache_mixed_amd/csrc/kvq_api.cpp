@@ -171,7 +171,7 @@ size_t kvq_decode_workspace_bytes(const kvq_cache* c, int32_t n_q_heads) {
 static kvq_status decode_common(const kvq_cache* c, const void* q, int32_t n_q_heads,
                                 float softmax_scale, const kvq::ResArgs& res, int res_dtype,
                                 float* out, void* workspace, size_t workspace_bytes,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool use_scratch = false) {
   kvq_status s = check_cache(c);
   if (s != KVQ_OK) return s;
   if (!q || !out) return KVQ_EINVAL;
@@ -196,6 +196,28 @@ static kvq_status decode_common(const kvq_cache* c, const void* q, int32_t n_q_h
   if (c->n_tokens > 0 && !kvq::decode_supported(c->k_bits, c->v_bits, c->param_dtype))
     return KVQ_EUNSUPPORTED;
   if ((int64_t)c->batch * c->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+  if (use_scratch) {
+    // allocation-free variant: this call's own plan must fit the library's
+    // scratch array
+    size_t need = kvq::decode_counter_bytes(c->batch * c->n_kv_heads);
+    if (c->n_tokens > 0) {
+      const kvq::DecodePlan plan = kvq::decode_plan(c->batch * c->n_kv_heads, G, c->k_bits, c->v_bits,
+                                                    c->param_dtype, c->n_tokens / 128);
+      if (plan.n_chunks > kvq::KVQ_MAX_CHUNKS || plan.n_chunks * plan.tpc < c->n_tokens / 128)
+        return KVQ_EWORKSPACE;
+      need = kvq::decode_workspace_needed(c->batch * c->n_kv_heads, G, plan);
+    }
+    if (need > (size_t)KVQ_DECODE_SCRATCH_BYTES) return KVQ_EWORKSPACE;
+    hipError_t e = kvq::decode_scratch_acquire(&workspace, c->batch * c->n_kv_heads, stream);
+    if (e != hipSuccess) return KVQ_EHIP;
+    kvq::Geo g = make_geo(c);
+    e = kvq::launch_decode(g, q, G, softmax_scale, out, workspace, res, res_dtype, stream);
+    if (e != hipSuccess) {
+      kvq::decode_scratch_mark_dirty();
+      return KVQ_EHIP;
+    }
+    return KVQ_OK;
+  }
   const size_t need = kvq::decode_workspace_bytes(c->batch, c->n_kv_heads, G, c->max_tokens / 128);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return KVQ_EWORKSPACE;
   if (c->n_tokens > 0) {
@@ -220,6 +242,17 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t n_q_heads,
     res.R = 0;
     return decode_common(c, q, n_q_heads, softmax_scale, res, KVQ_F32, out, workspace,
                          workspace_bytes, stream);
+  } catch (...) {
+    return KVQ_EHIP;
+  }
+}
+
+kvq_status kvq_decode_attn_noalloc(const kvq_cache* c, const void* q, int32_t n_q_heads,
+                                   float softmax_scale, float* out, hipStream_t stream) {
+  try {
+    kvq::ResArgs res{};
+    res.R = 0;
+    return decode_common(c, q, n_q_heads, softmax_scale, res, KVQ_F32, out, nullptr, 0, stream, true);
   } catch (...) {
     return KVQ_EHIP;
   }

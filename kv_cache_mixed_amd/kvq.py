@@ -61,7 +61,8 @@ class KvqError(RuntimeError):
 _lib = None
 
 EXPORTS = ["kvq_strerror", "kvq_tile_bytes", "kvq_cache_bytes", "kvq_quantize", "kvq_shrink",
-           "kvq_shrink_shift", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_decode_attn_residual",
+           "kvq_shrink_shift", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_decode_attn_noalloc",
+           "kvq_decode_attn_residual",
            "kvq_pool_create", "kvq_pool_destroy", "kvq_pool_used_bytes", "kvq_pool_high_water",
            "kvq_append", "kvq_window_append", "kvq_allocate_bits", "kvq_pair_norms", "kvq_pair_slot_map"]
 
@@ -92,6 +93,8 @@ def load():
     L.kvq_decode_workspace_bytes.argtypes = [P, i32]
     L.kvq_decode_attn.restype = ctypes.c_int
     L.kvq_decode_attn.argtypes = [P, vp, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+    L.kvq_decode_attn_noalloc.restype = ctypes.c_int
+    L.kvq_decode_attn_noalloc.argtypes = [P, vp, i32, ctypes.c_float, vp, vp]
     L.kvq_decode_attn_residual.restype = ctypes.c_int
     L.kvq_decode_attn_residual.argtypes = [P, vp, i32, ctypes.c_float, vp, vp, ctypes.c_int, vp, vp,
                                            i32, vp, vp, ctypes.c_size_t, vp]
@@ -389,6 +392,19 @@ class PackedCache:
                                              _strides3(res_v), res_k.shape[2], _ptr(out), _ptr(ws),
                                              ws.numel(), _stream_ptr(stream))
         _check(st, "kvq_decode_attn_residual")
+        return out
+
+    def decode_attn_noalloc(self, q, softmax_scale, out=None, stream=None):
+        """kvq_decode_attn_noalloc: decode attention with the library's own
+        scratch array instead of a workspace (nothing is allocated by the
+        call; out must be given to avoid the allocation here as well)."""
+        import torch
+        assert q.dtype == torch.bfloat16 and q.is_contiguous()
+        if out is None:
+            out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+        st = load().kvq_decode_attn_noalloc(ctypes.byref(self.s), _ptr(q), q.shape[1], float(softmax_scale),
+                                            _ptr(out), _stream_ptr(stream))
+        _check(st, "kvq_decode_attn_noalloc")
         return out
 
     # -- host views for tests --------------------------------------------------
