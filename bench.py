@@ -244,6 +244,55 @@ def pn_mix_rows(torch, kvq, synth, dev, scale):
         "note": "keys' pair norms over the 128K context (fp32 in); decode with the pair-granular map"}}
 
 
+def semkv_split_rows(torch, kvq, synth, dev, scale):
+    """Per-token split between two adjacent precisions (SemKV page, abstract)
+    on the Qwen2.5-7B-shaped layer (B=16, Hkv=4, Hq=28, T=32768): every
+    stream's tokens ranked by a model-internal score (the key's L2 norm), the
+    top 25% quantized at 4 bits and the rest at 2 bits (2.5 bits on average,
+    binary16 S/Z) from the same inputs through the gathered quantize; decode
+    over both caches merged by one combine, cache copies rotated past 600 MB."""
+    B, H, Hq, T, n_high = 16, 4, 28, 32768, 8192
+    inp = synth.layer_device(B, H, Hq, T, seed=77, device=dev)
+    t0 = time.perf_counter()
+    score = torch.linalg.vector_norm(inp["k"], dim=-1).reshape(B * H, T).cpu().numpy()
+    order = kvq.rank_tokens(score, n_high).reshape(B, H, T)
+    rank_ms = (time.perf_counter() - t0) * 1e3
+    tok_hi = torch.from_numpy(order[:, :, :n_high].copy()).to(dev)
+    tok_lo = torch.from_numpy(order[:, :, n_high:].copy()).to(dev)
+    alg = decode_bytes(B, H, Hq, n_high, 4, 4, 2) + decode_bytes(B, H, 0, T - n_high, 2, 2, 2)
+    pairs = []
+    for _ in range(max(2, math.ceil(600e6 / alg))):
+        hi = kvq.PackedCache(B, H, n_high, 4, 4, kvq.F16, device=dev)
+        lo = kvq.PackedCache(B, H, T - n_high, 2, 2, kvq.F16, device=dev)
+        pairs.append((hi, lo))
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    pairs[0][0].quantize_tokens(inp["k"], inp["v"], tok_hi)
+    pairs[0][1].quantize_tokens(inp["k"], inp["v"], tok_lo)
+    e1.record()
+    torch.cuda.synchronize()
+    q_ms = e0.elapsed_time(e1)
+    for hi, lo in pairs[1:]:
+        hi.quantize_tokens(inp["k"], inp["v"], tok_hi)
+        lo.quantize_tokens(inp["k"], inp["v"], tok_lo)
+    q = inp["q"]
+    del inp, tok_hi, tok_lo
+    torch.cuda.empty_cache()
+    nc = len(pairs)
+    outs = [torch.empty((B, Hq, 128), dtype=torch.float32, device=dev) for _ in pairs]
+    wss = [kvq.split_workspace(hi, lo, Hq) for hi, lo in pairs]
+    d_ms = time_block(torch, lambda i: kvq.decode_attn_split(pairs[i % nc][0], pairs[i % nc][1], q, scale,
+                                                             out=outs[i % nc], workspace=wss[i % nc]), 40, 4)
+    del pairs, outs, wss
+    torch.cuda.empty_cache()
+    return {"semkv_split_4_2_bits": {
+        "ms": round(d_ms, 4), "GB/s": round(alg / d_ms / 1e6, 1),
+        "pct_of_peak": round(100 * alg / d_ms / 1e6 / PEAK_HBM_GBS, 2), "bytes": alg,
+        "tokens_per_s": round(B / (d_ms * 1e-3), 1), "mean_bits": 2.5,
+        "rank_ms_host": round(rank_ms, 1), "gathered_quantize_ms": round(q_ms, 4),
+        "note": "top 25%% of each stream by key norm at 4 bits, the rest at 2 bits; %d copies rotated" % nc}}
+
+
 def progressive_rows(torch, kvq, synth, dev, scale):
     """Progressive schedule: 128-token groups appended from 16 bits under a
     128 MiB budget (B=8, Hkv=4, Hq=28) up to 32768 tokens.  Times every append
@@ -664,6 +713,7 @@ def main():
         del wins, nk, nv
         rows.update(mixed_128k_rows(torch, kvq, synth, dev, scale))
         rows.update(pn_mix_rows(torch, kvq, synth, dev, scale))
+        rows.update(semkv_split_rows(torch, kvq, synth, dev, scale))
         rows.update(progressive_rows(torch, kvq, synth, dev, scale))
         rows.update(halving_rule_rows(torch, kvq, synth, dev, scale))
         rows.update(qwen32b_step_rows(torch, kvq, synth, dev, scale))

@@ -10,6 +10,9 @@
  *              Long-Context Inference" (papernotes.org summary).
  *   [PNMIX]   "PN-Mix: Pair-Norm Guided Mixed-Precision Key Cache
  *              Quantization" (shd-paper.top summary, abstract).
+ *   [SEMKV]   "SemKV: Semantic Mixed-Precision KV Cache Quantization Guided
+ *              by the Quality Cliff for Long-Context LLM Inference"
+ *              (paperdance.org, abstract).
  *
  * ------------------------------------------------------------------------
  * Conventions
@@ -194,6 +197,31 @@ kvq_status kvq_quantize(kvq_cache *cache, const void *k, const void *v, kvq_dtyp
                         const int64_t k_strides[3], const int64_t v_strides[3],
                         int32_t t0, int32_t n_new, hipStream_t stream);
 
+/* kvq_quantize of gathered tokens ([SEMKV] abstract: every token is kept; the
+ * tokens of a stream, ranked by a model-internal score, go to one of two
+ * caches of adjacent precisions).  New token i of stream (b, h) is input row
+ * r = tok[(b * n_kv_heads + h) * n_new + i] of that stream: element
+ * (b, h, r, c) at base + b*s[0] + h*s[1] + r*s[2] + c.  tok: device int32
+ * [B][Hkv][n_new]; values outside [0, n_src) are clamped into it (a wrong
+ * index reads another row of the input, never outside it; n_src >= 1 is the
+ * number of input rows per stream).  Otherwise as kvq_quantize (same
+ * checks, layout and effect on n_tokens). */
+kvq_status kvq_quantize_tokens(kvq_cache *cache, const void *k, const void *v, kvq_dtype in_dtype,
+                               const int64_t k_strides[3], const int64_t v_strides[3],
+                               const int32_t *tok, int32_t n_src, int32_t t0, int32_t n_new,
+                               hipStream_t stream);
+
+/* kvq_rank_tokens (host; [SEMKV] abstract: tokens ranked by a model-internal
+ * score, the top-ranked at the higher of two precisions).  score: host
+ * [n_streams][n_tokens] finite binary32.  order: host [n_streams][n_tokens]
+ * output; per stream, the first n_high entries are the tokens with the
+ * n_high largest scores (equal scores: the earlier token ranks first) in
+ * ascending token order, the other n_tokens - n_high entries the remaining
+ * tokens in ascending order.  KVQ_EINVAL for NULL pointers, sizes out of
+ * range or a score that is not finite (order then unwritten). */
+kvq_status kvq_rank_tokens(const float *score, int32_t n_streams, int32_t n_tokens, int32_t n_high,
+                           int32_t *order);
+
 /* Equivalent Right Shift of the whole cache ([PMKVQ] Key design 1): every
  * stored key and value tile of every stream goes from 2*to_bits to to_bits
  * bits in place, scales become narrow((2^b + 1) * S'), zero points stay.
@@ -239,6 +267,24 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads);
 kvq_status kvq_decode_attn(const kvq_cache *cache, const void *q, int32_t n_q_heads,
                            float softmax_scale, float *out, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/* Decode attention over the tokens of two caches of the same streams
+ * ([SEMKV] abstract: every token kept, each stream's tokens split by rank
+ * between two adjacent precisions).  For batch b and query head hq the
+ * attended set is the union of cache a's and cache b's stored tokens of
+ * stream (b, hq / G) (attention does not depend on the order of the tokens,
+ * so the split need not follow positions).  The caches must have the same
+ * batch and n_kv_heads; widths, parameter dtypes and capacities may differ;
+ * either may hold no tokens, but together at least 128.  Each cache's chunks
+ * leave partials (max, sum, weighted values) per head in one workspace and
+ * one combine kernel merges them into out.  workspace: at least
+ * kvq_decode_split_workspace_bytes(a, b, n_q_heads) bytes, 256-byte aligned,
+ * no initial contents needed.  Other arguments and errors as for
+ * kvq_decode_attn. */
+size_t kvq_decode_split_workspace_bytes(const kvq_cache *a, const kvq_cache *b, int32_t n_q_heads);
+kvq_status kvq_decode_attn_split(const kvq_cache *a, const kvq_cache *b, const void *q, int32_t n_q_heads,
+                                 float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                                 hipStream_t stream);
 
 /* Allocation-free decode attention, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that

@@ -206,7 +206,8 @@ struct DecodeArgs {
   float* part_ml;     // [BH][n_slots][G][2]   (running max in log2 units, sum)
   float* part_o;      // [BH][n_slots][G][128] (unnormalised output)
   int G, n_chunks, tpc, n_groups;
-  int n_slots;        // partial slots per stream: n_chunks + residual slots
+  int n_slots;        // partial slots per stream: n_chunks + residual slots (+ another cache's)
+  int slot0;          // slot of this launch's chunk 0 (0, or after another cache's chunks)
   unsigned* counters; // [n_groups] finished chunks per stream group: zero on
                       // entry, left zero (chunk combine inside the kernel)
   int fused;          // chunks combined inside the kernel (1) or by a second kernel (0)
@@ -1188,7 +1189,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     sh_cd[col][1] = den;
     const int s = col / G, hh = col - s * G;
     const int bh = grp * NS + s;
-    sh_row[col] = bh >= BH ? -1 : (single ? bh * G + hh : (bh * a.n_slots + chunk) * G + hh);
+    sh_row[col] = bh >= BH ? -1 : (single ? bh * G + hh : (bh * a.n_slots + a.slot0 + chunk) * G + hh);
     sh_orow[col] = bh * G + hh;
   }
   __syncthreads();
@@ -1246,8 +1247,8 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       icol[it] = min(idx >> 5, 15);
       ic4[it] = (idx & 31) * 4;
       irow[it] = idx < ncol * 32 ? sh_row[icol[it]] : -1;
-      // partial row of slot k = irow + (k - chunk) * G
-      const int64_t r0 = (int64_t)irow[it] - (int64_t)chunk * G;
+      // partial row of slot k = irow + (k - slot0 - chunk) * G
+      const int64_t r0 = (int64_t)irow[it] - (int64_t)(a.slot0 + chunk) * G;
 #pragma unroll
       for (int k = 0; k < KR; k++) {
         ov[it][k] = (f32x4){0.f, 0.f, 0.f, 0.f};
@@ -1261,7 +1262,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       const int col = i / ns, k = i - (i / ns) * ns;
       float m = -INFINITY, l = 0.0f;
       if (sh_row[col] >= 0) {
-        const int64_t r = (int64_t)sh_row[col] + (int64_t)(k - chunk) * G;
+        const int64_t r = (int64_t)sh_row[col] + (int64_t)(k - a.slot0 - chunk) * G;
         m = a.part_ml[2 * r];
         l = a.part_ml[2 * r + 1];
       }
@@ -1292,7 +1293,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
       for (int k = 0; k < KR; k++)
         if (k < ns) num += wk[2 * k] * ov[it][k];
-      const int64_t r0 = (int64_t)irow[it] - (int64_t)chunk * G;
+      const int64_t r0 = (int64_t)irow[it] - (int64_t)(a.slot0 + chunk) * G;
       for (int k = KR; k < ns; k++) num += wk[2 * k] * *(const f32x4*)(a.part_o + (r0 + (int64_t)k * G) * 128 + ic4[it]);
       *(f32x4*)(a.out + (int64_t)sh_orow[col] * 128 + ic4[it]) = num / sden[col];
     }
@@ -1329,7 +1330,7 @@ constexpr int ns_cap(int kb, int vb) {
 // group cut into n_chunks chunks of tpc tiles, aiming at one round of
 // resident workgroups (256 CUs x waves per SIMD) with 4..64 tiles per chunk and
 // at most KVQ_MAX_CHUNKS chunks.
-static DecodePlan plan_for(int BH, int ns, int k_bits, int v_bits, int pdt, int n_tiles) {
+static DecodePlan plan_for(int BH, int ns, int k_bits, int v_bits, int pdt, int n_tiles, int max_chunks) {
   DecodePlan p;
   p.ns = ns;
   p.n_groups = (BH + ns - 1) / ns;
@@ -1340,7 +1341,7 @@ static DecodePlan plan_for(int BH, int ns, int k_bits, int v_bits, int pdt, int 
   tpc = ((tpc + 3) / 4) * 4;
   if (tpc < 4) tpc = 4;
   if (tpc > 64) tpc = 64;
-  const int tmin = (n_tiles + KVQ_MAX_CHUNKS - 1) / KVQ_MAX_CHUNKS;
+  const int tmin = (n_tiles + max_chunks - 1) / max_chunks;
   if (tpc < tmin) tpc = tmin;
   p.n_chunks = (n_tiles + tpc - 1) / tpc;
   p.tpc = (n_tiles + p.n_chunks - 1) / p.n_chunks;   // balanced, every chunk non-empty
@@ -1351,13 +1352,13 @@ static DecodePlan plan_for(int BH, int ns, int k_bits, int v_bits, int pdt, int 
 // leaves a wave fewer than four tiles, where a single stream per wave (twice
 // the tiles, the prologue and partial write amortised over more work) is
 // faster.
-DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_tiles) {
+DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_tiles, int max_chunks) {
   const int cap = ns_cap(k_bits, v_bits);
   int ns = 16 / G;
   if (ns > KVQ_DECODE_NS_MAX) ns = KVQ_DECODE_NS_MAX;
   ns = ns > cap ? cap : (ns < 1 ? 1 : ns);
-  DecodePlan p = plan_for(BH, ns, k_bits, v_bits, pdt, n_tiles);
-  if (ns > 1 && p.tpc < KVQ_DECODE_NS_MIN_TPC) p = plan_for(BH, 1, k_bits, v_bits, pdt, n_tiles);
+  DecodePlan p = plan_for(BH, ns, k_bits, v_bits, pdt, n_tiles, max_chunks);
+  if (ns > 1 && p.tpc < KVQ_DECODE_NS_MIN_TPC) p = plan_for(BH, 1, k_bits, v_bits, pdt, n_tiles, max_chunks);
   return p;
 }
 
@@ -1443,16 +1444,15 @@ bool decode_supported(int k_bits, int v_bits, int pdt) {
   return k_bits == v_bits && (k_bits == 1 || k_bits == 2 || k_bits == 4 || k_bits == 8 || k_bits == 16);
 }
 
+// a0 carries n_slots, slot0, fused and the residual rows; the plan gives the
+// grid (the same plan the caller validated the workspace against)
 template <int KB, int VB, int PDT>
-static hipError_t launch_ns(const DecodeArgs& a0, hipStream_t st) {
+static hipError_t launch_ns(const DecodeArgs& a0, const DecodePlan& p, hipStream_t st) {
   constexpr int CAP = ns_cap(KB, VB);
   DecodeArgs a = a0;
-  const DecodePlan p = decode_plan(a.g.B * a.g.H, a.G, KB, VB, PDT, a.g.n_tiles);
   a.n_groups = p.n_groups;
   a.n_chunks = p.n_chunks;
   a.tpc = p.tpc;
-  a.n_slots = p.n_chunks + a.n_slots;   // residual slots on entry
-  a.fused = a.n_slots > 1 && p.n_chunks >= KVQ_DECODE_FUSED_MIN_CHUNKS;
   // residual workgroups ride along only when a second kernel combines
   if (a.fused && a.n_res) return hipErrorInvalidValue;
   const int res_rows = a.n_res ? (a.n_res * a.g.B * a.g.H + a.n_chunks - 1) / a.n_chunks : 0;
@@ -1470,13 +1470,23 @@ static hipError_t launch_ns(const DecodeArgs& a0, hipStream_t st) {
 }
 
 template <int PDT>
-static hipError_t launch_decode_pdt(const DecodeArgs& a, hipStream_t st) {
+static hipError_t launch_decode_pdt(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
   const int kb = a.g.k_bits, vb = a.g.v_bits;
 #define KVQ_DEC(KBV, VBV) \
-  if (kb == KBV && vb == VBV) return launch_ns<KBV, VBV, PDT>(a, st);
+  if (kb == KBV && vb == VBV) return launch_ns<KBV, VBV, PDT>(a, p, st);
   KVQ_DEC(16, 16) KVQ_DEC(8, 8) KVQ_DEC(4, 4) KVQ_DEC(2, 2) KVQ_DEC(1, 1)
   KVQ_DEC(0, 1) KVQ_DEC(0, 2) KVQ_DEC(0, 4)
 #undef KVQ_DEC
+  return hipErrorInvalidValue;
+}
+
+static hipError_t launch_decode_any(const DecodeArgs& a, const DecodePlan& p, hipStream_t st) {
+  switch (a.g.pdt) {
+    case KVQ_F32: return launch_decode_pdt<KVQ_F32>(a, p, st);
+    case KVQ_F16: return launch_decode_pdt<KVQ_F16>(a, p, st);
+    case KVQ_BF16: return launch_decode_pdt<KVQ_BF16>(a, p, st);
+    case KVQ_E4M3: return launch_decode_pdt<KVQ_E4M3>(a, p, st);
+  }
   return hipErrorInvalidValue;
 }
 
@@ -1536,19 +1546,14 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
     a.G = G;
     a.sl2 = sl2;
     a.n_chunks = a.tpc = a.n_groups = 0;
-    a.n_slots = n_res;
+    a.n_slots = n_slots;
+    a.slot0 = 0;
     a.counters = counters;
-    a.fused = 0;   // set by the launch from the plan
+    a.fused = n_slots > 1 && p.n_chunks >= KVQ_DECODE_FUSED_MIN_CHUNKS;
     a.res = res;
     a.res_dtype = res_dtype;
     a.n_res = res_inline ? n_res : 0;
-    switch (g.pdt) {
-      case KVQ_F32: e = launch_decode_pdt<KVQ_F32>(a, st); break;
-      case KVQ_F16: e = launch_decode_pdt<KVQ_F16>(a, st); break;
-      case KVQ_BF16: e = launch_decode_pdt<KVQ_BF16>(a, st); break;
-      case KVQ_E4M3: e = launch_decode_pdt<KVQ_E4M3>(a, st); break;
-      default: return hipErrorInvalidValue;
-    }
+    e = launch_decode_any(a, p, st);
     if (e != hipSuccess) return e;
   }
   if (n_slots > 1 && (!has_packed || p.n_chunks < KVQ_DECODE_FUSED_MIN_CHUNKS)) {
@@ -1558,6 +1563,65 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
     e = hipGetLastError();
   }
   return e;
+}
+
+// Decode over the tokens of two caches of the same streams (each cache's
+// chunks in its own range of partial slots: cache a's chunks first), then one
+// combine over all slots.  Plans capped at KVQ_SPLIT_MAX_CHUNKS chunks each,
+// so the combine sees at most 128 slots; no in-kernel combine.
+hipError_t launch_decode_split(const Geo& ga, const Geo& gb, const void* q, int G, float scale, float* out,
+                               void* ws, hipStream_t st) {
+  const int BH = ga.B * ga.H;
+  const float sl2 = scale * 1.4426950408889634f;
+  const Geo* gs[2] = {&ga, &gb};
+  DecodePlan ps[2];
+  int n_slots = 0;
+  for (int i = 0; i < 2; i++) {
+    ps[i].n_chunks = 0;
+    if (gs[i]->n_tiles > 0)
+      ps[i] = decode_plan(BH, G, gs[i]->k_bits, gs[i]->v_bits, gs[i]->pdt, gs[i]->n_tiles, KVQ_SPLIT_MAX_CHUNKS);
+    n_slots += ps[i].n_chunks;
+  }
+  if (n_slots < 1 || n_slots > KVQ_MAX_SLOTS) return hipErrorInvalidValue;
+  float* part_ml = (float*)((uint8_t*)ws + cnt_bytes(BH));
+  float* part_o = (float*)((uint8_t*)part_ml + ml_bytes(BH, n_slots, G));
+  int slot0 = 0;
+  for (int i = 0; i < 2; i++) {
+    if (ps[i].n_chunks == 0) continue;
+    DecodeArgs a;
+    a.g = *gs[i];
+    a.q = (const uint16_t*)q;
+    a.out = out;
+    a.part_ml = part_ml;
+    a.part_o = part_o;
+    a.G = G;
+    a.sl2 = sl2;
+    a.n_chunks = a.tpc = a.n_groups = 0;
+    a.n_slots = n_slots;
+    a.slot0 = slot0;
+    a.counters = (unsigned*)ws;
+    a.fused = 0;
+    a.res = ResArgs{};
+    a.res.R = 0;
+    a.res_dtype = KVQ_F32;
+    a.n_res = 0;
+    hipError_t e = launch_decode_any(a, ps[i], st);
+    if (e != hipSuccess) return e;
+    slot0 += ps[i].n_chunks;
+  }
+  if (n_slots > 1) {
+    const int rows = BH * G;
+    hipLaunchKernelGGL(decode_combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, (const float*)part_ml,
+                       (const float*)part_o, out, BH, ga.H, G, n_slots);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+size_t decode_split_workspace_bytes(int B, int H, int G) {
+  DecodePlan p;
+  p.n_chunks = 2 * KVQ_SPLIT_MAX_CHUNKS - KVQ_MAX_RES_SLOTS;   // the bound adds the residual slots
+  return decode_workspace_needed(B * H, G, p);
 }
 
 // ---------------------------------------------------------------------------

@@ -132,6 +132,58 @@ kvq_status kvq_quantize(kvq_cache* c, const void* k, const void* v, kvq_dtype in
   }
 }
 
+kvq_status kvq_quantize_tokens(kvq_cache* c, const void* k, const void* v, kvq_dtype in_dtype,
+                               const int64_t k_strides[3], const int64_t v_strides[3],
+                               const int32_t* tok, int32_t n_src, int32_t t0, int32_t n_new,
+                               hipStream_t stream) {
+  try {
+    kvq_status s = check_cache(c);
+    if (s != KVQ_OK) return s;
+    if (!tok || n_src < 1) return KVQ_EINVAL;
+    if (!k && !v) return KVQ_EINVAL;
+    if (in_dtype != KVQ_F32 && in_dtype != KVQ_BF16) return KVQ_EINVAL;
+    if ((k && !k_strides) || (v && !v_strides)) return KVQ_EINVAL;
+    if (t0 < 0 || t0 % 128 || n_new < 128 || n_new % 128) return KVQ_EINVAL;
+    if ((int64_t)t0 + n_new > c->max_tokens) return KVQ_EINVAL;
+    if ((int64_t)n_new / 128 > 65535 || c->n_kv_heads > 65535 || c->batch > 65535)
+      return KVQ_EUNSUPPORTED;
+    const int64_t zero[3] = {0, 0, 0};
+    kvq::Geo g = make_geo(c);
+    hipError_t e = kvq::launch_quantize(g, k, v, in_dtype, k ? k_strides : zero, v ? v_strides : zero, t0,
+                                        n_new, stream, tok, n_src);
+    if (e != hipSuccess) return KVQ_EHIP;
+    c->n_tokens = std::max(c->n_tokens, t0 + n_new);
+    return KVQ_OK;
+  } catch (...) {
+    return KVQ_EHIP;
+  }
+}
+
+kvq_status kvq_rank_tokens(const float* score, int32_t n_streams, int32_t n_tokens, int32_t n_high,
+                           int32_t* order) {
+  try {
+    if (!score || !order || n_streams < 1 || n_tokens < 1 || n_high < 0 || n_high > n_tokens)
+      return KVQ_EINVAL;
+    const int64_t n = (int64_t)n_streams * n_tokens;
+    for (int64_t i = 0; i < n; i++)
+      if (!std::isfinite(score[i])) return KVQ_EINVAL;
+    std::vector<int32_t> idx(n_tokens), out((size_t)n);
+    for (int32_t sidx = 0; sidx < n_streams; sidx++) {
+      const float* sc = score + (int64_t)sidx * n_tokens;
+      for (int32_t t = 0; t < n_tokens; t++) idx[t] = t;
+      // the n_high largest scores (equal scores: the earlier token first)
+      std::stable_sort(idx.begin(), idx.end(), [&](int32_t a, int32_t b) { return sc[a] > sc[b]; });
+      std::sort(idx.begin(), idx.begin() + n_high);
+      std::sort(idx.begin() + n_high, idx.end());
+      std::copy(idx.begin(), idx.end(), out.begin() + (int64_t)sidx * n_tokens);
+    }
+    std::copy(out.begin(), out.end(), order);
+    return KVQ_OK;
+  } catch (...) {
+    return KVQ_EHIP;
+  }
+}
+
 kvq_status kvq_shrink(kvq_cache* c, int32_t to_bits, hipStream_t stream) {
   return kvq_shrink_shift(c, to_bits, KVQ_SHIFT_ERS, stream);
 }
@@ -242,6 +294,55 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t n_q_heads,
     res.R = 0;
     return decode_common(c, q, n_q_heads, softmax_scale, res, KVQ_F32, out, workspace,
                          workspace_bytes, stream);
+  } catch (...) {
+    return KVQ_EHIP;
+  }
+}
+
+size_t kvq_decode_split_workspace_bytes(const kvq_cache* a, const kvq_cache* b, int32_t n_q_heads) {
+  if (check_cache(a) != KVQ_OK || check_cache(b) != KVQ_OK) return 0;
+  if (a->batch != b->batch || a->n_kv_heads != b->n_kv_heads) return 0;
+  if (n_q_heads < a->n_kv_heads || n_q_heads % a->n_kv_heads) return 0;
+  return kvq::decode_split_workspace_bytes(a->batch, a->n_kv_heads, n_q_heads / a->n_kv_heads);
+}
+
+kvq_status kvq_decode_attn_split(const kvq_cache* a, const kvq_cache* b, const void* q, int32_t n_q_heads,
+                                 float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                                 hipStream_t stream) {
+  try {
+    const kvq_cache* cs[2] = {a, b};
+    for (const kvq_cache* c : cs) {
+      kvq_status s = check_cache(c);
+      if (s != KVQ_OK) return s;
+      if (c->n_tokens > 0 && !kvq::decode_supported(c->k_bits, c->v_bits, c->param_dtype))
+        return KVQ_EUNSUPPORTED;
+    }
+    if (a->batch != b->batch || a->n_kv_heads != b->n_kv_heads) return KVQ_EINVAL;
+    if (!q || !out) return KVQ_EINVAL;
+    if (n_q_heads < a->n_kv_heads || n_q_heads % a->n_kv_heads) return KVQ_EINVAL;
+    const int G = n_q_heads / a->n_kv_heads;
+    if (G > 16) return KVQ_EUNSUPPORTED;
+    if (a->n_tokens + (int64_t)b->n_tokens < 128) return KVQ_EINVAL;   // nothing to attend
+    if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY || softmax_scale == -INFINITY)
+      return KVQ_EINVAL;
+    if ((int64_t)a->batch * a->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+    const size_t need = kvq::decode_split_workspace_bytes(a->batch, a->n_kv_heads, G);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return KVQ_EWORKSPACE;
+    const int BH = a->batch * a->n_kv_heads;
+    int slots = 0;
+    for (const kvq_cache* c : cs) {
+      if (c->n_tokens == 0) continue;
+      const kvq::DecodePlan p = kvq::decode_plan(BH, G, c->k_bits, c->v_bits, c->param_dtype, c->n_tokens / 128,
+                                                 kvq::KVQ_SPLIT_MAX_CHUNKS);
+      if (p.n_chunks > kvq::KVQ_SPLIT_MAX_CHUNKS || p.n_chunks * p.tpc < c->n_tokens / 128) return KVQ_EWORKSPACE;
+      slots += p.n_chunks;
+    }
+    kvq::DecodePlan pall;
+    pall.n_chunks = slots - kvq::KVQ_MAX_RES_SLOTS;
+    if (slots > kvq::KVQ_MAX_SLOTS || (pall.n_chunks > 0 && kvq::decode_workspace_needed(BH, G, pall) > workspace_bytes))
+      return KVQ_EWORKSPACE;
+    hipError_t e = kvq::launch_decode_split(make_geo(a), make_geo(b), q, G, softmax_scale, out, workspace, stream);
+    return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
   } catch (...) {
     return KVQ_EHIP;
   }

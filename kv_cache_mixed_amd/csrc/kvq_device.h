@@ -226,9 +226,11 @@ __host__ __device__ constexpr int mixed_slot_bits(int j) {
 
 // launchers (host side), implemented in the .hip files
 namespace kvq {
+// tok (device [B][H][n_new] int32, or null): new token t of stream (b, h) is
+// input row tok[(b * H + h) * n_new + t], clamped to [0, n_src)
 hipError_t launch_quantize(const Geo& g, const void* k, const void* v, int in_dtype,
                            const int64_t* ks, const int64_t* vs, int t0, int n_new,
-                           hipStream_t st);
+                           hipStream_t st, const int32_t* tok = nullptr, int n_src = 0);
 hipError_t launch_shrink(const Geo& g, int to_bits, int method, hipStream_t st);
 // copy m token rows of every stream (b, h) of k and v (element strides ks / vs
 // of batch, kv head, token; channel stride 1; elt_bytes 2 or 4) into rows
@@ -246,7 +248,13 @@ constexpr int KVQ_MAX_SLOTS = KVQ_MAX_CHUNKS + KVQ_MAX_RES_SLOTS;
 struct DecodePlan {
   int ns, n_groups, n_chunks, tpc;
 };
-DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_tiles);
+DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_tiles,
+                       int max_chunks = KVQ_MAX_CHUNKS);
+// decode over two caches of the same streams (tokens split between them)
+constexpr int KVQ_SPLIT_MAX_CHUNKS = 64;
+hipError_t launch_decode_split(const Geo& ga, const Geo& gb, const void* q, int G, float scale, float* out,
+                               void* ws, hipStream_t st);
+size_t decode_split_workspace_bytes(int B, int H, int G);
 size_t decode_workspace_needed(int BH, int G, const DecodePlan& p);
 size_t decode_workspace_bytes(int B, int H, int G, int max_tiles);
 // residual segment of a decode call (R = 0: none)

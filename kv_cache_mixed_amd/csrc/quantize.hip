@@ -129,22 +129,43 @@ __device__ __forceinline__ void pack_mixed_store(const uint16_t* codes, uint8_t*
 // Keys: thread (slot j = tid & 127, half = tid >> 7) scans 64 tokens.
 // KB = 0 selects the mixed layout (slot j holds channel slot_chan[h][j]).
 // ---------------------------------------------------------------------------
-template <int KB, int PDT, int IN>
+// Gathered tokens (GATHER): new token t of stream (b, h) is input row
+// tok[(b * H + h) * n_new + t], clamped to [0, n_src).
+struct TokIdx {
+  const int32_t* tok;
+  int n_new, n_src;
+};
+__device__ __forceinline__ int64_t src_row(const TokIdx& ti, int b, int h, int H, int t) {
+  int r = ti.tok[((int64_t)b * H + h) * ti.n_new + t];
+  r = r < 0 ? 0 : (r >= ti.n_src ? ti.n_src - 1 : r);
+  return r;
+}
+
+template <int KB, int PDT, int IN, bool GATHER>
 __global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __restrict__ kin,
                                                          int64_t sb, int64_t sh, int64_t st,
-                                                         int t0) {
+                                                         int t0, TokIdx ti) {
   __shared__ uint16_t codes[128 * 128];
   __shared__ float red_mn[2][128], red_mx[2][128];
+  __shared__ int64_t rows[GATHER ? 128 : 1];
   const int tile_local = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tile = t0 / 128 + tile_local;
   const int j = threadIdx.x & 127, half = threadIdx.x >> 7;
   const int chan = (KB == 0) ? ((int)g.slot_chan[h * 128 + j] & 127) : j;   // masked: never outside the row
   const int bits = (KB == 0) ? mixed_slot_bits(j) : KB;
 
-  const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (int64_t)(tile_local * 128) * st + chan;
   float x[64];
+  if constexpr (GATHER) {
+    if (threadIdx.x < 128) rows[threadIdx.x] = src_row(ti, b, h, g.H, tile_local * 128 + threadIdx.x) * st;
+    __syncthreads();
+    const int64_t base = (int64_t)b * sb + (int64_t)h * sh + chan;
 #pragma unroll
-  for (int i = 0; i < 64; i++) x[i] = load_in<IN>(kin, base + (int64_t)(half * 64 + i) * st);
+    for (int i = 0; i < 64; i++) x[i] = load_in<IN>(kin, base + rows[half * 64 + i]);
+  } else {
+    const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (int64_t)(tile_local * 128) * st + chan;
+#pragma unroll
+    for (int i = 0; i < 64; i++) x[i] = load_in<IN>(kin, base + (int64_t)(half * 64 + i) * st);
+  }
   float mn = x[0], mx = x[0];
 #pragma unroll
   for (int i = 1; i < 64; i++) {
@@ -222,10 +243,10 @@ __device__ __forceinline__ void load4(const void* p, int64_t i, float* x) {
   }
 }
 
-template <int VB, int PDT, int IN, bool VEC>
+template <int VB, int PDT, int IN, bool VEC, bool GATHER>
 __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __restrict__ vin,
                                                          int64_t sb, int64_t sh, int64_t st,
-                                                         int t0) {
+                                                         int t0, TokIdx ti) {
   // word W[w][c][a] holds channel c of the tokens 32a + w*PW + i (i < PW,
   // code i at bits [i*VB, (i+1)*VB)); token 32a + 8r + i (step i of row r)
   // lands in word (8r + i) / PW at slot (8r + i) % PW
@@ -236,13 +257,14 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __re
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int row = lane >> 4, j = lane & 15;
   const float levels = (float)((1u << VB) - 1u);
-  const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (int64_t)(tile_local * 128) * st + 4 * j;
+  const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (GATHER ? 0 : (int64_t)(tile_local * 128) * st) + 4 * j;
   float x[8][8];   // [step][channel slot k: channel 64 * (k / 4) + 4j + k % 4]
 #pragma unroll
   for (int i = 0; i < 8; i++) {
     const int t = wave * 32 + 8 * row + i;
-    load4<IN, VEC>(vin, base + (int64_t)t * st, &x[i][0]);
-    load4<IN, VEC>(vin, base + (int64_t)t * st + 64, &x[i][4]);
+    const int64_t r = GATHER ? src_row(ti, b, h, g.H, tile_local * 128 + t) : (int64_t)t;
+    load4<IN, VEC>(vin, base + r * st, &x[i][0]);
+    load4<IN, VEC>(vin, base + r * st + 64, &x[i][4]);
   }
   uint32_t wd[8][RW];
 #pragma unroll
@@ -312,12 +334,16 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __re
 // ---------------------------------------------------------------------------
 template <int PDT, int IN>
 static hipError_t launch_k(const Geo& g, const void* k, const int64_t* s, int t0, int n_new,
-                           hipStream_t stm) {
+                           const TokIdx& ti, hipStream_t stm) {
   dim3 grid(n_new / 128, g.H, g.B), block(256);
-#define KVQ_QK(KBV)                                                                          \
-  case KBV:                                                                                  \
-    hipLaunchKernelGGL((quantize_k_kernel<KBV, PDT, IN>), grid, block, 0, stm, g, k, s[0],   \
-                       s[1], s[2], t0);                                                      \
+#define KVQ_QK(KBV)                                                                            \
+  case KBV:                                                                                    \
+    if (ti.tok)                                                                                \
+      hipLaunchKernelGGL((quantize_k_kernel<KBV, PDT, IN, true>), grid, block, 0, stm, g, k,   \
+                         s[0], s[1], s[2], t0, ti);                                            \
+    else                                                                                       \
+      hipLaunchKernelGGL((quantize_k_kernel<KBV, PDT, IN, false>), grid, block, 0, stm, g, k,  \
+                         s[0], s[1], s[2], t0, ti);                                            \
     break;
   switch (g.k_bits) {
     KVQ_QK(0) KVQ_QK(1) KVQ_QK(2) KVQ_QK(4) KVQ_QK(8) KVQ_QK(16)
@@ -329,19 +355,22 @@ static hipError_t launch_k(const Geo& g, const void* k, const int64_t* s, int t0
 
 template <int PDT, int IN>
 static hipError_t launch_v(const Geo& g, const void* v, const int64_t* s, int t0, int n_new,
-                           hipStream_t stm) {
+                           const TokIdx& ti, hipStream_t stm) {
   dim3 grid(n_new / 128, g.H, g.B), block(256);
   const int eb = (IN == KVQ_F32) ? 4 : 2;
   const bool vec = ((uintptr_t)v % (4 * eb) == 0) && (s[0] % 4 == 0) && (s[1] % 4 == 0) &&
                    (s[2] % 4 == 0);
-#define KVQ_QV(VBV)                                                                           \
-  case VBV:                                                                                   \
-    if (vec)                                                                                  \
-      hipLaunchKernelGGL((quantize_v_kernel<VBV, PDT, IN, true>), grid, block, 0, stm, g, v,  \
-                         s[0], s[1], s[2], t0);                                               \
-    else                                                                                      \
-      hipLaunchKernelGGL((quantize_v_kernel<VBV, PDT, IN, false>), grid, block, 0, stm, g, v, \
-                         s[0], s[1], s[2], t0);                                               \
+#define KVQ_QV(VBV)                                                                                   \
+  case VBV:                                                                                           \
+    if (ti.tok)                                                                                       \
+      hipLaunchKernelGGL((quantize_v_kernel<VBV, PDT, IN, false, true>), grid, block, 0, stm, g, v,   \
+                         s[0], s[1], s[2], t0, ti);                                                   \
+    else if (vec)                                                                                     \
+      hipLaunchKernelGGL((quantize_v_kernel<VBV, PDT, IN, true, false>), grid, block, 0, stm, g, v,   \
+                         s[0], s[1], s[2], t0, ti);                                                   \
+    else                                                                                              \
+      hipLaunchKernelGGL((quantize_v_kernel<VBV, PDT, IN, false, false>), grid, block, 0, stm, g, v,  \
+                         s[0], s[1], s[2], t0, ti);                                                   \
     break;
   switch (g.v_bits) {
     KVQ_QV(1) KVQ_QV(2) KVQ_QV(4) KVQ_QV(8) KVQ_QV(16)
@@ -354,26 +383,30 @@ static hipError_t launch_v(const Geo& g, const void* v, const int64_t* s, int t0
 template <int PDT>
 static hipError_t launch_pdt(const Geo& g, const void* k, const void* v, int in_dtype,
                              const int64_t* ks, const int64_t* vs, int t0, int n_new,
-                             hipStream_t st) {
+                             const TokIdx& ti, hipStream_t st) {
   hipError_t e = hipSuccess;
   if (in_dtype == KVQ_F32) {
-    if (k) e = launch_k<PDT, KVQ_F32>(g, k, ks, t0, n_new, st);
-    if (e == hipSuccess && v) e = launch_v<PDT, KVQ_F32>(g, v, vs, t0, n_new, st);
+    if (k) e = launch_k<PDT, KVQ_F32>(g, k, ks, t0, n_new, ti, st);
+    if (e == hipSuccess && v) e = launch_v<PDT, KVQ_F32>(g, v, vs, t0, n_new, ti, st);
   } else {
-    if (k) e = launch_k<PDT, KVQ_BF16>(g, k, ks, t0, n_new, st);
-    if (e == hipSuccess && v) e = launch_v<PDT, KVQ_BF16>(g, v, vs, t0, n_new, st);
+    if (k) e = launch_k<PDT, KVQ_BF16>(g, k, ks, t0, n_new, ti, st);
+    if (e == hipSuccess && v) e = launch_v<PDT, KVQ_BF16>(g, v, vs, t0, n_new, ti, st);
   }
   return e;
 }
 
 hipError_t launch_quantize(const Geo& g, const void* k, const void* v, int in_dtype,
                            const int64_t* ks, const int64_t* vs, int t0, int n_new,
-                           hipStream_t st) {
+                           hipStream_t st, const int32_t* tok, int n_src) {
+  TokIdx ti;
+  ti.tok = tok;
+  ti.n_new = n_new;
+  ti.n_src = n_src;
   switch (g.pdt) {
-    case KVQ_F32: return launch_pdt<KVQ_F32>(g, k, v, in_dtype, ks, vs, t0, n_new, st);
-    case KVQ_F16: return launch_pdt<KVQ_F16>(g, k, v, in_dtype, ks, vs, t0, n_new, st);
-    case KVQ_BF16: return launch_pdt<KVQ_BF16>(g, k, v, in_dtype, ks, vs, t0, n_new, st);
-    case KVQ_E4M3: return launch_pdt<KVQ_E4M3>(g, k, v, in_dtype, ks, vs, t0, n_new, st);
+    case KVQ_F32: return launch_pdt<KVQ_F32>(g, k, v, in_dtype, ks, vs, t0, n_new, ti, st);
+    case KVQ_F16: return launch_pdt<KVQ_F16>(g, k, v, in_dtype, ks, vs, t0, n_new, ti, st);
+    case KVQ_BF16: return launch_pdt<KVQ_BF16>(g, k, v, in_dtype, ks, vs, t0, n_new, ti, st);
+    case KVQ_E4M3: return launch_pdt<KVQ_E4M3>(g, k, v, in_dtype, ks, vs, t0, n_new, ti, st);
   }
   return hipErrorInvalidValue;
 }

@@ -62,7 +62,8 @@ _lib = None
 
 EXPORTS = ["kvq_strerror", "kvq_tile_bytes", "kvq_cache_bytes", "kvq_quantize", "kvq_shrink",
            "kvq_shrink_shift", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_decode_attn_noalloc",
-           "kvq_decode_attn_residual",
+           "kvq_decode_attn_residual", "kvq_quantize_tokens", "kvq_rank_tokens",
+           "kvq_decode_split_workspace_bytes", "kvq_decode_attn_split",
            "kvq_pool_create", "kvq_pool_destroy", "kvq_pool_used_bytes", "kvq_pool_high_water",
            "kvq_append", "kvq_window_append", "kvq_allocate_bits", "kvq_pair_norms", "kvq_pair_slot_map"]
 
@@ -93,6 +94,14 @@ def load():
     L.kvq_decode_workspace_bytes.argtypes = [P, i32]
     L.kvq_decode_attn.restype = ctypes.c_int
     L.kvq_decode_attn.argtypes = [P, vp, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
+    L.kvq_quantize_tokens.restype = ctypes.c_int
+    L.kvq_quantize_tokens.argtypes = [P, vp, vp, ctypes.c_int, vp, vp, vp, i32, i32, i32, vp]
+    L.kvq_rank_tokens.restype = ctypes.c_int
+    L.kvq_rank_tokens.argtypes = [vp, i32, i32, i32, vp]
+    L.kvq_decode_split_workspace_bytes.restype = ctypes.c_size_t
+    L.kvq_decode_split_workspace_bytes.argtypes = [P, P, i32]
+    L.kvq_decode_attn_split.restype = ctypes.c_int
+    L.kvq_decode_attn_split.argtypes = [P, P, vp, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
     L.kvq_decode_attn_noalloc.restype = ctypes.c_int
     L.kvq_decode_attn_noalloc.argtypes = [P, vp, i32, ctypes.c_float, vp, vp]
     L.kvq_decode_attn_residual.restype = ctypes.c_int
@@ -186,6 +195,42 @@ def allocate_bits(sens, nbytes, budget_bytes):
                                   choice.ctypes.data, ctypes.byref(cost))
     _check(st, "kvq_allocate_bits")
     return choice, cost.value
+
+
+def rank_tokens(score, n_high):
+    """kvq_rank_tokens: score [n_streams][n_tokens] float32 (host) -> order
+    [n_streams][n_tokens] int32: per stream the n_high highest-scoring tokens
+    (ascending), then the others (ascending)."""
+    import numpy as np
+    sc = np.ascontiguousarray(score, dtype=np.float32)
+    assert sc.ndim == 2
+    order = np.empty(sc.shape, dtype=np.int32)
+    _check(load().kvq_rank_tokens(sc.ctypes.data, sc.shape[0], sc.shape[1], int(n_high), order.ctypes.data),
+           "kvq_rank_tokens")
+    return order
+
+
+def split_workspace(cache_a, cache_b, n_q_heads):
+    """device workspace for decode_attn_split (uint8 tensor)"""
+    import torch
+    n = int(load().kvq_decode_split_workspace_bytes(ctypes.byref(cache_a.s), ctypes.byref(cache_b.s), n_q_heads))
+    if n == 0:
+        raise KvqError(EINVAL, "kvq_decode_split_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=cache_a.device)
+
+
+def decode_attn_split(cache_a, cache_b, q, softmax_scale, out=None, workspace=None, stream=None):
+    """kvq_decode_attn_split: attention over the union of two caches' tokens
+    (same batch and kv heads)."""
+    import torch
+    assert q.dtype == torch.bfloat16 and q.is_contiguous()
+    if out is None:
+        out = torch.empty(q.shape, dtype=torch.float32, device=q.device)
+    ws = workspace if workspace is not None else split_workspace(cache_a, cache_b, q.shape[1])
+    st = load().kvq_decode_attn_split(ctypes.byref(cache_a.s), ctypes.byref(cache_b.s), _ptr(q), q.shape[1],
+                                      float(softmax_scale), _ptr(out), _ptr(ws), ws.numel(), _stream_ptr(stream))
+    _check(st, "kvq_decode_attn_split")
+    return out
 
 
 def tile_bytes(bits: int) -> int:
@@ -393,6 +438,19 @@ class PackedCache:
                                              ws.numel(), _stream_ptr(stream))
         _check(st, "kvq_decode_attn_residual")
         return out
+
+    def quantize_tokens(self, k, v, tok, t0=0, stream=None):
+        """kvq_quantize_tokens: k, v [B][H][n_src][128] float32 / bfloat16
+        device tensors, tok [B][H][n_new] int32 device tensor of input rows."""
+        import torch
+        ref = k if k is not None else v
+        in_dtype = {torch.float32: F32, torch.bfloat16: BF16}[ref.dtype]
+        assert tok.dtype == torch.int32 and tok.is_contiguous() and tok.shape[:2] == (self.B, self.H)
+        st = load().kvq_quantize_tokens(ctypes.byref(self.s), _ptr(k), _ptr(v), in_dtype,
+                                        _strides3(k) if k is not None else None,
+                                        _strides3(v) if v is not None else None,
+                                        _ptr(tok), ref.shape[2], t0, tok.shape[2], _stream_ptr(stream))
+        _check(st, "kvq_quantize_tokens")
 
     def decode_attn_noalloc(self, q, softmax_scale, out=None, stream=None):
         """kvq_decode_attn_noalloc: decode attention with the library's own

@@ -360,6 +360,42 @@ def decode_attn_residual(st, q_bf16: np.ndarray, scale: float, res_k: np.ndarray
 
 
 # --------------------------------------------------------------------------
+# per-token split between two precisions ("SemKV: Semantic Mixed-Precision KV
+# Cache Quantization ...", abstract: every token is kept; tokens are ranked by
+# a model-internal score and given one of two adjacent precisions)
+# --------------------------------------------------------------------------
+def rank_tokens(score, n_high: int) -> np.ndarray:
+    """score [S][T] -> order [S][T]: per stream, the n_high tokens with the
+    largest scores (a larger score ranks first; equal scores, the earlier
+    token first) in ascending token order, then the other tokens in
+    ascending order.  Plain Python sort on (-score, token)."""
+    out = []
+    for sc in np.asarray(score, dtype=np.float32):
+        ranked = sorted(range(len(sc)), key=lambda t: (-float(sc[t]), t))
+        out.append(sorted(ranked[:n_high]) + sorted(ranked[n_high:]))
+    return np.array(out, dtype=np.int64)
+
+
+def decode_attn_union(streams, q_bf16: np.ndarray, scale: float) -> np.ndarray:
+    """Attention of the G query heads over the union of several packed
+    streams' reconstructed tokens (the same kv head's tokens split between
+    caches).  Written as its plain definition in float64: dequantize every
+    stream, concatenate, softmax(sigma * q K^T) V.  Streams holding no tokens
+    may be None."""
+    qf = decode(np.ascontiguousarray(q_bf16, dtype=np.uint16), BF16)
+    ks = [dequant_k(st) for st in streams if st is not None and st.n_tok > 0]
+    vs = [dequant_v(st) for st in streams if st is not None and st.n_tok > 0]
+    K = np.concatenate(ks)
+    V = np.concatenate(vs)
+    sigma = float(np.float32(scale))
+    s = sigma * (qf @ K.T)
+    s -= s.max(axis=1, keepdims=True)
+    p = np.exp(s)
+    p /= p.sum(axis=1, keepdims=True)
+    return p @ V
+
+
+# --------------------------------------------------------------------------
 # schedule accounting
 # --------------------------------------------------------------------------
 def block_bytes(B, H, n_tok, k_bits, v_bits, pdt) -> int:
