@@ -77,10 +77,12 @@
  *     2-bit.  A token's logical 34-byte row is the packed row of its 128 slot
  *     codes in slot order (widths as listed), so bytes 0..3 hold 4-bit pairs,
  *     bytes 4..7 hold (3,1,3,1)-bit groups, bytes 8..33 hold 2-bit quads.  The
- *     tile stores these rows as five column planes: logical bytes [0,8),
- *     [8,16), [16,24), [24,32) go to planes 0..3 at tile offsets 0, 1024, 2048,
- *     3072 with 8 bytes per token; logical bytes [32,34) go to plane 4 at tile
- *     offset 4096 with 2 bytes per token; tokens are in order inside a plane.
+ *     tile stores these rows as five column planes.  Plane g (g < 4) sits at
+ *     tile offset 1024*g with 8 bytes per token: logical bytes g, 4+g,
+ *     8+6g, 9+6g, 10+6g, 11+6g, 12+6g, 13+6g in that order (so every plane
+ *     holds two 4-bit, two 3-bit, two 1-bit and 24 2-bit slots).  Plane 4
+ *     sits at tile offset 4096 with 2 bytes per token: logical bytes 32, 33.
+ *     Tokens are in order inside a plane.
  *
  *   Tile placement: tile g of stream (b, h) starts at
  *     k_codes + k_tile_off[(g * batch + b) * n_kv_heads + h]   if k_tile_off,

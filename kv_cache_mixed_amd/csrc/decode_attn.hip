@@ -117,19 +117,72 @@ __host__ __device__ constexpr Fld ufield(int i) {
   return {w, k >= 10 ? 10 : 0, k >= 10 ? k - 10 : k, 1, 32 * w + k, 32 * w + 16 + k, 0};
 }
 
-// Mixed key layout, lane group 0: word 0 = slots 0..7 (4-bit), word 1 = slots
-// 8..23 ((3,1)-bit pairs), word 2 = slots 120..127 (2-bit) spread so that
-// slots 120..123 sit in the low half and 124..127 in the high half.  Lane-local
-// index = slot for slots 0..23, 24 + (slot - 120) for the others.
-__host__ __device__ constexpr Fld mfield0(int i) {
-  if (i < 4) { const int k = i; return {0, k >= 2 ? 8 : 0, (k % 2) * 4, 4, k, 4 + k, 0}; }
-  if (i < 12) {
-    const int k = i - 4, kk = k % 4;
-    return {1, k >= 4 ? 8 : 0, (kk / 2) * 4 + (kk % 2) * 3, (kk % 2) ? 1 : 3, 8 + k, 16 + k, 0};
-  }
-  const int k = i - 12;
-  return {2, 0, 2 * k, 2, 24 + k, 28 + k, 0};
+// Mixed key tile, lane group g (every group has the same class mix): the
+// lane's words are D0 = plane g bytes 0..3 (a 4-bit pair, a (3,1,3,1) group,
+// two 2-bit quads), D1 = plane g bytes 4..7 (four 2-bit quads) and N = the
+// group's nibble of plane 4 (two 2-bit slots) at bits 0..3.  Operand register
+// f (two fields, one per 16-bit half) and its halves' bit positions:
+//   f0  D0 & (0xF,  0x3 <<16)  lo 4-bit @0  hi 2-bit @0
+//   f1  D0 & (0xF0, 0xC <<16)  lo 4-bit @4  hi 2-bit @2
+//   f2..f5  (D0 >> 8): lo 3/1/3/1-bit @0/3/4/7, hi 2-bit @0/2/4/6
+//   f6  D0 & (0x3 << 20) | N & 0x3   lo 2-bit @0  hi 2-bit @4
+//   f7  D0 & (0xC << 20) | N & 0xC   lo 2-bit @2  hi 2-bit @6
+//   f8..f15  D1 as a uniform 2-bit word (ufield<2>)
+// Lane-local index li = 2f + half; mixed_lane_slot gives its slot.
+__host__ __device__ constexpr int mixed_pos(int f, int half) {
+  constexpr int lo[8] = {0, 4, 0, 3, 4, 7, 0, 2};
+  constexpr int hi[8] = {0, 2, 0, 2, 4, 6, 4, 6};
+  if (f >= 8) return 2 * ((f - 8) < 5 ? (f - 8) : (f - 8) - 5);
+  return half ? hi[f] : lo[f];
 }
+__host__ __device__ constexpr int mixed_lane_slot(int g, int li) {
+  const int f = li >> 1, h = li & 1;
+  if (f >= 8) return 32 + 24 * g + (f - 8) + 8 * h;
+  // high halves of f0..f7 hold 2-bit slots 24 + 24g + {0, 1, 4, 5, 6, 7, 2, 3}
+  if (h) return 24 + 24 * g + (f < 2 ? f : (f < 6 ? f + 2 : f - 4));
+  if (f < 2) return 2 * g + f;
+  if (f < 6) return 8 + 4 * g + (f - 2);
+  return 120 + 2 * g + (f - 6);
+}
+// inverse: the lane-order position 32 g + li of slot j
+__host__ __device__ constexpr int mixed_slot_lpos(int j) {
+  if (j < 8) return 32 * (j >> 1) + 2 * (j & 1);
+  if (j < 24) return 32 * ((j - 8) >> 2) + 2 * (2 + ((j - 8) & 3));
+  if (j >= 120) return 32 * ((j - 120) >> 1) + 2 * (6 + ((j - 120) & 1));
+  const int m = j - 24, g = m / 24, i = m % 24;
+  if (i < 8) return 32 * g + 2 * (i < 2 ? i : (i < 4 ? i + 4 : i - 2)) + 1;
+  return 32 * g + 2 * (8 + ((i - 8) & 7)) + ((i - 8) >> 3);
+}
+__device__ __forceinline__ uint32_t mixed_field(const uint32_t* kw, int f) {
+  const uint32_t d0 = kw[0], d1 = kw[1], nn = kw[2];
+  switch (f) {
+    case 0: return d0 & 0x0003000Fu;
+    case 1: return d0 & 0x000C00F0u;
+    case 2: return (d0 >> 8) & 0x00030007u;
+    case 3: return (d0 >> 8) & 0x000C0008u;
+    case 4: return (d0 >> 8) & 0x00300070u;
+    case 5: return (d0 >> 8) & 0x00C00080u;
+    case 6: return (d0 & 0x00300000u) | (nn & 0x3u);
+    case 7: return (d0 & 0x00C00000u) | (nn & 0xCu);
+    default: {
+      const Fld F = ufield<2>(f - 8);
+      const uint32_t m = ((1u << F.wid) - 1u) << F.pos;
+      return (F.sh ? (d1 >> F.sh) : d1) & (m | (m << 16));
+    }
+  }
+}
+namespace mixed_check {
+// the lane map is a bijection of the 128 slots and its inverse is exact
+constexpr bool ok() {
+  for (int g = 0; g < 4; g++)
+    for (int li = 0; li < 32; li++) {
+      const int j = mixed_lane_slot(g, li);
+      if (j < 0 || j > 127 || mixed_slot_lpos(j) != 32 * g + li) return false;
+    }
+  return true;
+}
+static_assert(ok(), "mixed lane map");
+}  // namespace mixed_check
 
 
 
@@ -630,8 +683,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   const int t_base = chunk * a.tpc;
 
   auto kslot = [&](int li) -> int {
-    if constexpr (MIXED) return lg == 0 ? (li < 24 ? li : 96 + li) : 32 * lg - 8 + li;
-    else return 32 * lg + li;
+    return 32 * lg + li;   // query and key parameters are staged in lane order
   };
 
   // ---- lane offsets, fixed for the whole kernel
@@ -639,7 +691,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // 4*KB bytes of the row (mixed: its plane's 8 bytes, lane group 0 also the
   // 2 plane-4 bytes)
   const uint32_t row0 = 32 * (n >> 2) + (n & 3);
-  const uint32_t koff = MIXED ? (uint32_t)((lg == 0 ? 0 : 1024 * lg) + 8 * row0)
+  const uint32_t koff = MIXED ? (uint32_t)(1024 * lg + 8 * row0)
                               : (uint32_t)(row0 * ROW_K + 4 * KB * lg);
   const uint32_t koff4 = 4096 + 2 * row0;                       // mixed plane 4
   const uint32_t voff4 = (uint32_t)(4 * n + lg) * 16;           // value words (w, h, n, lg, 0..3)
@@ -655,6 +707,15 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // key parameters: lane l loads word l (and l + 64) of the tile's 128 (e4m3:
   // lanes 32.. repeat words 0..31)
   const uint32_t kloff = (uint32_t)((PB == 1) ? (lane & 31) : lane) * 4;
+  // mixed keys: lane-order positions of the parameters this lane stages
+  // (its word j holds slots (kloff / PB) + 256 j / PB + e)
+  int mlpos[4 / PB * KPL > 0 ? 4 / PB * KPL : 1];
+  if constexpr (MIXED) {
+#pragma unroll
+    for (int j = 0; j < KPL; j++)
+#pragma unroll
+      for (int e = 0; e < 4 / PB; e++) mlpos[j * (4 / PB) + e] = mixed_slot_lpos((int)(kloff / PB) + 256 * j / PB + e);
+  }
 
   float m_run = -INFINITY, l_run = 0.0f, z_run = 0.0f;
   int e_run = -1000;
@@ -713,7 +774,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
           const uint32_t w2 = __builtin_amdgcn_raw_buffer_load_b16(rk, koff4 + jj * 8, soff / 4, CPOL);
           bf.kw[s][jj][0] = v[0];
           bf.kw[s][jj][1] = v[1];
-          bf.kw[s][jj][2] = (w2 & 0xffu) | ((w2 & 0xff00u) << 8);
+          bf.kw[s][jj][2] = (uint32_t)w2 >> (4 * lg);   // the lane group's nibble at bits 0..3
         } else if constexpr (NWK >= 4) {
 #pragma unroll
           for (int w = 0; w < NWK; w += 4) {
@@ -778,17 +839,19 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     if (q0 < t_count) load(b0, q0, 0);
     *(u32x4*)&qs[cn][8 * part] = v;
   } else {
-    // mixed widths: slot j holds channel slot_chan[kv head][j]
+    // mixed widths: lane-order position p = 32 lane group + li holds slot
+    // mixed_lane_slot(p / 32, p % 32), i.e. channel slot_chan[kv head][slot]
     uint16_t qv[8];
 #pragma unroll
     for (int r = 0; r < 8; r++) {
       const int i = threadIdx.x + 256 * r;
-      const int cn = i >> 7, j = i & 127;
+      const int cn = i >> 7, pp = i & 127;
       const int cs = cn / G;
       const int cbh = grp * NS + cs;
       qv[r] = 0;
       if (cs < NS && cbh < BH) {
         const int chh = cbh % g.H;
+        const int j = mixed_lane_slot(pp >> 5, pp & 31);
         qv[r] = a.q[((int64_t)grp * NS * G + cn) * 128 + (g.slot_chan[chh * 128 + j] & 127)] ^ (uint16_t)qflip;
       }
     }
@@ -825,13 +888,37 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // operand registers in LDS; logit constants ak, bk0
   auto fold_query = [&](const Buf& bf) {
     // stage the tile's key parameters in LDS, then read the own stream's 32
-    // slots (four runs of 8 consecutive slots)
+    // slots (four runs of 8 consecutive slots).  Mixed keys: each parameter
+    // goes to its slot's lane-order position
+    if constexpr (!MIXED) {
 #pragma unroll
-    for (int s = 0; s < NS; s++)
+      for (int s = 0; s < NS; s++)
 #pragma unroll
-      for (int a2 = 0; a2 < 2; a2++)
+        for (int a2 = 0; a2 < 2; a2++)
 #pragma unroll
-        for (int j = 0; j < KPL; j++) kst[wave][s][a2][(kloff >> 2) + 64 * j] = bf.kp[s][a2][j];
+          for (int j = 0; j < KPL; j++) kst[wave][s][a2][(kloff >> 2) + 64 * j] = bf.kp[s][a2][j];
+    } else {
+#pragma unroll
+      for (int s = 0; s < NS; s++)
+#pragma unroll
+        for (int a2 = 0; a2 < 2; a2++) {
+          uint8_t* dst = (uint8_t*)&kst[wave][s][a2][0];
+#pragma unroll
+          for (int j = 0; j < KPL; j++)
+#pragma unroll
+            for (int e = 0; e < 4 / PB; e++) {
+              const int pi = j * (4 / PB) + e;
+              const uint32_t v = bf.kp[s][a2][j] >> (8 * PB * e);
+              if constexpr (PB == 1) {
+                if (lane < 32) dst[mlpos[pi]] = (uint8_t)v;
+              } else if constexpr (PB == 2) {
+                *(uint16_t*)(dst + 2 * mlpos[pi]) = (uint16_t)v;
+              } else {
+                *(uint32_t*)(dst + 4 * mlpos[pi]) = v;
+              }
+            }
+        }
+    }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -883,19 +970,22 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
     for (int f = 0; f < NFK; f++) {
       float ul, uh, w;
+      float wh;
       if constexpr (MIXED) {
-        const Fld F0 = mfield0(f), F1 = ufield<2>(f);
-        ul = (lg == 0) ? uval(F0.lo) : uval(F1.lo);
-        uh = (lg == 0) ? uval(F0.hi) : uval(F1.hi);
-        w = kf * ((lg == 0) ? exp2i(F0.wexp - F0.pos) : exp2i(F1.wexp - F1.pos));
+        // lane order: register f holds li = 2f (low half) and 2f + 1 (high half)
+        ul = uval(2 * f);
+        uh = uval(2 * f + 1);
+        w = kf * exp2i(-mixed_pos(f, 0));
+        wh = kf * exp2i(-mixed_pos(f, 1));
       } else {
         const Fld F = ufield<KB>(f);
         ul = uval(F.lo);
         uh = uval(F.hi);
         w = kf * exp2i(F.wexp - F.pos);
+        wh = w;
       }
       uint32_t hi, lo;
-      split_pack(ul * w, uh * w, hi, lo, m1);
+      split_pack(ul * w, uh * wh, hi, lo, m1);
       // [k-step][hi/lo][lane][4]: one ds_read_b128 per operand group
       my_lds[(((f >> 2) * 2 + 0) * 64 + lane) * 4 + (f & 3)] = hi;
       my_lds[(((f >> 2) * 2 + 1) * 64 + lane) * 4 + (f & 3)] = lo;
@@ -937,9 +1027,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
           for (int r = 0; r < 4; r++) {
             const int f = 4 * k + r;
             if constexpr (MIXED) {
-              const uint32_t x0 = field_subnormal(bf.kw[s][jj][mfield0(f).w], mfield0(f));
-              const uint32_t x1 = field_subnormal(bf.kw[s][jj][ufield<2>(f).w], ufield<2>(f));
-              av[s][jj][r] = (lg == 0) ? x0 : x1;
+              av[s][jj][r] = mixed_field(bf.kw[s][jj], f);
             } else {
               av[s][jj][r] = field_subnormal(bf.kw[s][jj][ufield<KB>(f).w], ufield<KB>(f));
             }

@@ -92,25 +92,33 @@ __device__ __forceinline__ void pack_rows_store(const uint16_t* codes, uint8_t* 
   }
 }
 
-// Mixed key tile: codes[t][slot]; five planes (see include/kvq.h).
+// Logical byte b (0..33) of a token's mixed row from its slot codes:
+// bytes 0..3 hold 4-bit pairs (slots 2b, 2b+1), bytes 4..7 (3,1,3,1)
+// groups (slots 8+4m .. 11+4m), bytes 8..33 2-bit quads (slots 24+4m ..).
+__device__ __forceinline__ uint32_t mixed_logical_byte(const uint16_t* c, int b) {
+  if (b < 4) return (uint32_t)c[2 * b] | ((uint32_t)c[2 * b + 1] << 4);
+  if (b < 8) {
+    const uint16_t* p = c + 8 + 4 * (b - 4);
+    return (uint32_t)p[0] | ((uint32_t)p[1] << 3) | ((uint32_t)p[2] << 4) | ((uint32_t)p[3] << 7);
+  }
+  const uint16_t* p = c + 24 + 4 * (b - 8);
+  return (uint32_t)p[0] | ((uint32_t)p[1] << 2) | ((uint32_t)p[2] << 4) | ((uint32_t)p[3] << 6);
+}
+
+// Mixed key tile: codes[t][slot]; five planes (see include/kvq.h): plane g
+// holds logical bytes g, 4+g, 8+6g .. 13+6g, plane 4 bytes 32, 33.
 __device__ __forceinline__ void pack_mixed_store(const uint16_t* codes, uint8_t* tile) {
   // planes 0..3: 8 bytes per token = 2 words; 1024 words in total
   uint32_t* out = (uint32_t*)tile;
   for (int w = threadIdx.x; w < 1024; w += blockDim.x) {
-    int plane = w >> 8, t = (w >> 1) & 127, half = w & 1;
+    const int plane = w >> 8, t = (w >> 1) & 127, half = w & 1;
     const uint16_t* c = codes + t * 128;
     uint32_t word = 0;
-    if (plane == 0 && half == 0) {            // logical bytes 0..3: slots 0..7 at 4 bits
 #pragma unroll
-      for (int i = 0; i < 8; i++) word |= (uint32_t)c[i] << (4 * i);
-    } else if (plane == 0) {                  // logical bytes 4..7: (3,1) pairs, slots 8..23
-#pragma unroll
-      for (int i = 0; i < 8; i++)
-        word |= ((uint32_t)c[8 + 2 * i] << (4 * i)) | ((uint32_t)c[9 + 2 * i] << (4 * i + 3));
-    } else {                                  // logical bytes 8p+4h .. : 16 two-bit slots
-      int s0 = 24 + 32 * (plane - 1) + 16 * half;
-#pragma unroll
-      for (int i = 0; i < 16; i++) word |= (uint32_t)c[s0 + i] << (2 * i);
+    for (int k = 0; k < 4; k++) {
+      const int i = 4 * half + k;                                   // byte of the plane row
+      const int b = i == 0 ? plane : (i == 1 ? 4 + plane : 8 + 6 * plane + (i - 2));
+      word |= mixed_logical_byte(c, b) << (8 * k);
     }
     out[w] = word;
   }

@@ -317,10 +317,12 @@ void orc_unpack_vtile(const uint8_t *tile, int bits, uint16_t *codes)
  * Slot widths (header layout text): slots 0..7 are 4-bit; slots 8..23
  * alternate 3-bit (even slot) and 1-bit (odd slot); slots 24..127 are 2-bit.
  * A token's 34-byte logical row is the little-endian bit string of its 128
- * slot codes in slot order.  The tile stores those rows as five column planes:
- * row bytes [0,8), [8,16), [16,24), [24,32) and [32,34); plane p (p<4) sits
- * at tile offset 1024*p with 8 bytes per token, plane 4 at offset 4096 with
- * 2 bytes per token; tokens are in order inside every plane.  Tile size 4352. */
+ * slot codes in slot order.  The tile stores those rows as five column planes
+ * (header layout text): plane g < 4 sits at tile offset 1024*g with 8 bytes
+ * per token, holding logical bytes g, 4+g, 8+6g .. 13+6g in that order (one
+ * 4-bit pair, one (3,1,3,1) group, six 2-bit quads); plane 4 sits at offset
+ * 4096 with 2 bytes per token, holding logical bytes 32 and 33; tokens are in
+ * order inside every plane.  Tile size 4352. */
 int orc_mixed_slot_bits(int j)
 {
     if (j < 8) return 4;
@@ -337,8 +339,12 @@ static int mixed_slot_bitpos(int j)
 
 static int64_t mixed_byte_addr(int t, int rb)  /* token t, logical row byte rb */
 {
-    if (rb < 32) return 1024 * (rb / 8) + 8 * t + (rb % 8);
-    return 4096 + 2 * t + (rb - 32);
+    int plane, at;
+    if (rb >= 32) return 4096 + 2 * t + (rb - 32);
+    if (rb < 4) { plane = rb; at = 0; }                 /* 4-bit pair */
+    else if (rb < 8) { plane = rb - 4; at = 1; }        /* (3,1,3,1) group */
+    else { plane = (rb - 8) / 6; at = 2 + (rb - 8) % 6; }   /* 2-bit quads */
+    return 1024 * plane + 8 * t + at;
 }
 
 /* codes[t][j] (128x128, token-major, slot order) -> 4352-byte tile */

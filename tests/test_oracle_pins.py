@@ -391,17 +391,26 @@ def test_value_tile_positions_by_hand():
 
 
 def test_mixed_pack_by_hand():
+    """Byte positions worked out by hand from the header's mixed layout text:
+    plane g holds logical bytes g, 4+g, 8+6g .. 13+6g at plane bytes 0..7."""
     c = np.zeros((128, 128), np.uint16)
-    c[0, 0] = 0x9                 # 4-bit slot 0 -> logical byte 0 low nibble
+    c[0, 0] = 0x9                 # 4-bit slot 0 -> logical byte 0 low nibble -> plane 0 byte 0
+    c[0, 7] = 0xA                 # 4-bit slot 7 -> logical byte 3 high nibble -> plane 3 byte 0
     c[0, 8], c[0, 9] = 5, 1       # 3-bit slot 8, 1-bit slot 9 -> logical byte 4 = 0b1101
-    c[0, 10], c[0, 11] = 7, 0     # -> high nibble of logical byte 4 = 0b0111
-    c[3, 24] = 3                  # first 2-bit slot -> logical byte 8 of token 3 (plane 1)
+    c[0, 10], c[0, 11] = 7, 0     # -> high nibble of logical byte 4 = 0b0111; plane 0 byte 1
+    c[3, 24] = 3                  # first 2-bit slot -> logical byte 8 of token 3 -> plane 0 byte 2
+    c[1, 77] = 2                  # slot 77 -> logical byte 21 bits 2-3 -> plane 2 byte 3
+    c[2, 119] = 1                 # slot 119 -> logical byte 31 bits 6-7 -> plane 3 byte 7
     c[5, 127] = 2                 # last 2-bit slot -> logical byte 33 of token 5 (plane 4)
     t = oracle.pack_mixed(c)
     assert t[0] == 0x09
-    assert t[4] == 0x7D
-    assert t[1024 + 8 * 3 + 0] == 0x03
+    assert t[3072 + 0] == 0xA0
+    assert t[1] == 0x7D
+    assert t[8 * 3 + 2] == 0x03
+    assert t[2048 + 8 * 1 + 3] == 0x08
+    assert t[3072 + 8 * 2 + 7] == 0x40
     assert t[4096 + 2 * 5 + 1] == 0x80
+    assert int(np.count_nonzero(t)) == 7
     assert list(oracle.mixed_slot_bits()[:12]) == [4] * 8 + [3, 1, 3, 1]
     assert oracle.mixed_slot_bits().sum() == 272        # 34 bytes, 8 bits per byte
 
@@ -697,13 +706,15 @@ def _mixed_row_bytes(codes_row):
 
 
 def _mixed_tile_bytes(codes):
-    """[128 tokens][128 slots] -> 4352-byte tile: logical bytes [8p, 8p+8) of
-    token t at 1024p + 8t (p < 4), bytes 32, 33 at 4096 + 2t (header text)"""
+    """[128 tokens][128 slots] -> 4352-byte tile: plane g (g < 4) at 1024g + 8t
+    holds logical bytes g, 4+g, 8+6g .. 13+6g; bytes 32, 33 at 4096 + 2t
+    (header text)"""
     tile = bytearray(4352)
     for t in range(128):
         row = _mixed_row_bytes(codes[t])
-        for p in range(4):
-            tile[1024 * p + 8 * t: 1024 * p + 8 * t + 8] = row[8 * p: 8 * p + 8]
+        for g in range(4):
+            plane = [row[g], row[4 + g]] + [row[8 + 6 * g + i] for i in range(6)]
+            tile[1024 * g + 8 * t: 1024 * g + 8 * t + 8] = bytes(plane)
         tile[4096 + 2 * t: 4096 + 2 * t + 2] = row[32:34]
     return np.frombuffer(bytes(tile), dtype=np.uint8)
 
