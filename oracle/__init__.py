@@ -36,6 +36,7 @@ F32, F16, BF16, E4M3 = 0, 1, 2, 3
 PARAM_NP = {F32: np.float32, F16: np.uint16, BF16: np.uint16, E4M3: np.uint8}
 PARAM_BYTES = {F32: 4, F16: 2, BF16: 2, E4M3: 1}
 MIXED_TILE_BYTES = 4352
+VMIXED_TILE_BYTES = 5120
 
 _lock = threading.Lock()
 _lib = None
@@ -89,7 +90,12 @@ def lib():
             L.orc_shrink_scales_m.argtypes = [vp, i64, i32, i32, i32]
             L.orc_shift_array.argtypes = [vp, i64, i32, i32, vp]
             L.orc_decode_attn.restype = i32
-            L.orc_decode_attn.argtypes = [vp, i64, vp, vp, i32, vp, vp, i64, vp, vp, i32,
+            L.orc_pack_vmixed.argtypes = [vp, vp]
+            L.orc_unpack_vmixed.argtypes = [vp, vp]
+            L.orc_vmixed_slot_bits.restype = i32
+            L.orc_vmixed_slot_bits.argtypes = [i32]
+            L.orc_quantize_v_mixed.argtypes = [vp, i64, i32, i32, vp, vp, i64, vp, vp]
+            L.orc_decode_attn.argtypes = [vp, i64, vp, vp, i32, vp, vp, i64, vp, vp, i32, vp,
                                           i32, i32, vp, i32, ctypes.c_float, vp]
             L.orc_block_bytes.restype = i64
             L.orc_block_bytes.argtypes = [i32, i32, i64, i32, i32, i32]
@@ -206,6 +212,26 @@ def unpack_mixed(tile: np.ndarray) -> np.ndarray:
     return codes
 
 
+def pack_vmixed(codes: np.ndarray) -> np.ndarray:
+    """codes[slot][t] (128 x 128) -> 5120-byte mixed-width value tile"""
+    codes = np.ascontiguousarray(codes, dtype=np.uint16).reshape(128, 128)
+    tile = np.zeros(VMIXED_TILE_BYTES, dtype=np.uint8)
+    lib().orc_pack_vmixed(_p(codes), _p(tile))
+    return tile
+
+
+def unpack_vmixed(tile: np.ndarray) -> np.ndarray:
+    tile = np.ascontiguousarray(tile, dtype=np.uint8)
+    assert tile.size >= VMIXED_TILE_BYTES
+    codes = np.empty((128, 128), dtype=np.uint16)
+    lib().orc_unpack_vmixed(_p(tile), _p(codes))
+    return codes
+
+
+def vmixed_slot_bits() -> np.ndarray:
+    return np.array([lib().orc_vmixed_slot_bits(j) for j in range(128)], dtype=np.int32)
+
+
 def mixed_slot_bits() -> np.ndarray:
     return np.array([lib().orc_mixed_slot_bits(j) for j in range(128)], dtype=np.int32)
 
@@ -225,7 +251,8 @@ class Stream:
     v_tiles: [n_tiles, 2048*v_bits] uint8, vs/vz: [n_tok] raw
     """
 
-    def __init__(self, k_bits, v_bits, pdt, k_tiles, ks, kz, v_tiles, vs, vz, slot_chan=None):
+    def __init__(self, k_bits, v_bits, pdt, k_tiles, ks, kz, v_tiles, vs, vz, slot_chan=None, v_slot_chan=None):
+        self.v_slot_chan = v_slot_chan
         self.k_bits, self.v_bits, self.pdt = k_bits, v_bits, pdt
         self.k_tiles, self.ks, self.kz = k_tiles, ks, kz
         self.v_tiles, self.vs, self.vz = v_tiles, vs, vz
@@ -237,7 +264,7 @@ class Stream:
 
 
 def quantize_stream(k: np.ndarray, v: np.ndarray, k_bits: int, v_bits: int, pdt: int,
-                    slot_chan: np.ndarray | None = None) -> Stream:
+                    slot_chan: np.ndarray | None = None, v_slot_chan: np.ndarray | None = None) -> Stream:
     """k, v: [T, 128] float32 (T multiple of 128).  k_bits == 0 -> mixed keys."""
     k = np.ascontiguousarray(k, dtype=np.float32)
     v = np.ascontiguousarray(v, dtype=np.float32)
@@ -255,6 +282,15 @@ def quantize_stream(k: np.ndarray, v: np.ndarray, k_bits: int, v_bits: int, pdt:
     else:
         sc = None
         L.orc_quantize_k(_p(k), 128, T, k_bits, pdt, _p(kt), kt.shape[1], _p(ks), _p(kz))
+    if v_bits == 0:
+        # value channel classes (4/3/1/2 bits), one group per (token, class)
+        vsc = np.ascontiguousarray(v_slot_chan, dtype=np.int16)
+        assert vsc.shape == (128,) and sorted(vsc.tolist()) == list(range(128))
+        vt = np.zeros((nt, VMIXED_TILE_BYTES), dtype=np.uint8)
+        vs = np.empty((T, 4), dtype=PARAM_NP[pdt])
+        vz = np.empty((T, 4), dtype=PARAM_NP[pdt])
+        L.orc_quantize_v_mixed(_p(v), 128, T, pdt, _p(vsc), _p(vt), vt.shape[1], _p(vs), _p(vz))
+        return Stream(k_bits, v_bits, pdt, kt, ks, kz, vt, vs, vz, sc, vsc)
     vt = np.zeros((nt, tile_bytes(v_bits)), dtype=np.uint8)
     vs = np.empty(T, dtype=PARAM_NP[pdt])
     vz = np.empty(T, dtype=PARAM_NP[pdt])
@@ -307,6 +343,14 @@ def dequant_v(st: Stream) -> np.ndarray:
     S = decode(st.vs, st.pdt)
     Z = decode(st.vz, st.pdt)
     out = np.empty((nt * 128, 128), dtype=np.float64)
+    if st.v_bits == 0:
+        cls = np.array([0] * 16 + [1] * 16 + [2] * 16 + [3] * 80)
+        for g in range(nt):
+            codes = unpack_vmixed(st.v_tiles[g]).astype(np.float64)         # [slot][t]
+            Sg, Zg = S[g * 128:(g + 1) * 128], Z[g * 128:(g + 1) * 128]     # [t][class]
+            val = codes.T * Sg[:, cls] + Zg[:, cls]                         # [t][slot]
+            out[g * 128:(g + 1) * 128][:, st.v_slot_chan.astype(np.int64)] = val
+        return out
     for g in range(nt):
         codes = unpack_vtile(st.v_tiles[g], st.v_bits).astype(np.float64)  # [c][t]
         out[g * 128:(g + 1) * 128] = codes.T * S[g * 128:(g + 1) * 128, None] + \
@@ -321,12 +365,14 @@ def decode_attn(st: Stream, q_bf16: np.ndarray, scale: float) -> np.ndarray:
     out = np.empty((G, 128), dtype=np.float64)
     sc = st.slot_chan if st.slot_chan is not None else np.zeros(128, dtype=np.int16)
     sc = np.ascontiguousarray(sc, dtype=np.int16)
+    vsc = st.v_slot_chan if st.v_slot_chan is not None else np.zeros(128, dtype=np.int16)
+    vsc = np.ascontiguousarray(vsc, dtype=np.int16)
     kt = np.ascontiguousarray(st.k_tiles)
     vt = np.ascontiguousarray(st.v_tiles)
     rc = lib().orc_decode_attn(_p(kt), kt.shape[1], _p(np.ascontiguousarray(st.ks)),
                                _p(np.ascontiguousarray(st.kz)), st.k_bits, _p(sc),
                                _p(vt), vt.shape[1], _p(np.ascontiguousarray(st.vs)),
-                               _p(np.ascontiguousarray(st.vz)), st.v_bits, st.pdt, st.n_tok,
+                               _p(np.ascontiguousarray(st.vz)), st.v_bits, _p(vsc), st.pdt, st.n_tok,
                                _p(q), G, ctypes.c_float(scale), _p(out))
     if rc != 0:
         raise RuntimeError("orc_decode_attn failed: %d" % rc)

@@ -369,6 +369,51 @@ void orc_unpack_mixed(const uint8_t *tile, uint16_t *codes)
     }
 }
 
+/* Mixed-width value tile (header layout text; value channel classes as in
+ * [CHANMIX] Key design 3, read for values with per-class token groups):
+ * value slot j holds channel v_slot_chan[j]; slots 0..15 are 4-bit, 16..31
+ * 3-bit, 32..47 1-bit, 48..127 2-bit.  Each (token, class) is one group with
+ * its own S', Z' (params [token][4], class order 4, 3, 1, 2 bits).  The tile
+ * holds eight blocks of 16 slots (block b = slots 16b .. 16b+15) in order;
+ * block b stores its codes in fields of cw = 4 bits (b < 2; the 3-bit codes
+ * of block 1 in the low 3 bits) or cw = 2 bits (b >= 2; the 1-bit codes of
+ * block 2 in the low bit).  Block b starts at word 64 * (4b) for b < 2 and
+ * 64 * (8 + 2(b - 2)) after; inside it, word (w * 16 + n) * 4 + a (w < cw,
+ * n < 16, a < 4) holds slot 16b + n for the 32/cw tokens
+ * 32a + w * (32/cw) + i, code i at bits [i*cw, i*cw + cw).  Tile size 5120. */
+int orc_vmixed_slot_bits(int j)
+{
+    return j < 16 ? 4 : (j < 32 ? 3 : (j < 48 ? 1 : 2));
+}
+
+static int vmixed_class(int j) { return j < 16 ? 0 : (j < 32 ? 1 : (j < 48 ? 2 : 3)); }
+
+static int vmixed_field(int j) { return j < 32 ? 4 : 2; }     /* stored field width */
+
+static int64_t vmixed_bitpos(int j, int t)
+{
+    int b = j / 16, n = j % 16, cw = vmixed_field(j), per = 32 / cw;
+    int64_t base = 64 * (int64_t)(b < 2 ? 4 * b : 8 + 2 * (b - 2));
+    int a = t / 32, w = (t % 32) / per, i = t % per;
+    int64_t word = base + ((int64_t)w * 16 + n) * 4 + a;
+    return word * 32 + (int64_t)i * cw;
+}
+
+/* codes[j][t] (128 slots x 128 tokens) -> 5120-byte tile */
+void orc_pack_vmixed(const uint16_t *codes, uint8_t *tile)
+{
+    for (int j = 0; j < 128; j++)
+        for (int t = 0; t < 128; t++)
+            put_bits(tile, vmixed_bitpos(j, t), vmixed_field(j), codes[j * 128 + t]);
+}
+
+void orc_unpack_vmixed(const uint8_t *tile, uint16_t *codes)
+{
+    for (int j = 0; j < 128; j++)
+        for (int t = 0; t < 128; t++)
+            codes[j * 128 + t] = (uint16_t)get_bits(tile, vmixed_bitpos(j, t), vmixed_field(j));
+}
+
 /* ------------------------------------------------------------------------ */
 /* O3/O4. Quantize one (batch, kv-head) stream of n_tok tokens (multiple of  */
 /* 128), token t0 at element 0.                                              */
@@ -424,6 +469,32 @@ void orc_quantize_v(const float *v, int64_t t_stride, int n_tok, int bits, int p
     }
     free(tc);
     free(ct);
+}
+
+/* Values with mixed channel widths: for every token, the slots of each class
+ * form one group (the class's channels of that token) quantized at the
+ * class width; params s[tok * 4 + class], z[...]. */
+void orc_quantize_v_mixed(const float *v, int64_t t_stride, int n_tok, int pdt,
+                          const int16_t *slot_chan, uint8_t *codes, int64_t tile_stride,
+                          void *s, void *z)
+{
+    uint16_t *jt = (uint16_t *)malloc(128 * 128 * sizeof(uint16_t));   /* [slot][t] */
+    static const int first[5] = {0, 16, 32, 48, 128};
+    for (int g = 0; g < n_tok / 128; g++) {
+        for (int t = 0; t < 128; t++) {
+            int64_t tok = (int64_t)g * 128 + t;
+            for (int k = 0; k < 4; k++) {
+                float x[128];
+                uint16_t q[128];
+                int n = first[k + 1] - first[k];
+                for (int i = 0; i < n; i++) x[i] = v[tok * t_stride + slot_chan[first[k] + i]];
+                orc_quantize_group(x, 1, n, orc_vmixed_slot_bits(first[k]), pdt, q, 1, s, z, tok * 4 + k);
+                for (int i = 0; i < n; i++) jt[(first[k] + i) * 128 + t] = q[i];
+            }
+        }
+        orc_pack_vmixed(jt, codes + (int64_t)g * tile_stride);
+    }
+    free(jt);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -516,6 +587,7 @@ void orc_shrink_scales(void *s, int64_t n, int to_bits, int pdt) { orc_shrink_sc
 int orc_decode_attn(const uint8_t *kc, int64_t k_tile_stride, const void *ks, const void *kz, int k_bits,
                     const int16_t *slot_chan,
                     const uint8_t *vc, int64_t v_tile_stride, const void *vs, const void *vz, int v_bits,
+                    const int16_t *v_slot_chan,
                     int pdt, int n_tok, const uint16_t *q, int G, float scale, double *out)
 {
     if (n_tok <= 0 || n_tok % 128) return 1;
@@ -536,13 +608,25 @@ int orc_decode_attn(const uint8_t *kc, int64_t k_tile_stride, const void *ks, co
                 double Z = param_load(kz, (int64_t)g * 128 + j, pdt);
                 K[((int64_t)g * 128 + t) * 128 + ch] = S * codes[t * 128 + j] + Z;
             }
-        /* values: codes[c][t] */
-        orc_unpack_vtile(vc + (int64_t)g * v_tile_stride, v_bits, codes);
-        for (int t = 0; t < 128; t++) {
-            int64_t tok = (int64_t)g * 128 + t;
-            double S = param_load(vs, tok, pdt);
-            double Z = param_load(vz, tok, pdt);
-            for (int ch = 0; ch < 128; ch++) V[tok * 128 + ch] = S * codes[ch * 128 + t] + Z;
+        /* values: codes[c][t] (mixed widths: codes[slot][t]) */
+        if (v_bits == 0) {
+            orc_unpack_vmixed(vc + (int64_t)g * v_tile_stride, codes);
+            for (int t = 0; t < 128; t++) {
+                int64_t tok = (int64_t)g * 128 + t;
+                for (int j = 0; j < 128; j++) {
+                    double S = param_load(vs, tok * 4 + vmixed_class(j), pdt);
+                    double Z = param_load(vz, tok * 4 + vmixed_class(j), pdt);
+                    V[tok * 128 + v_slot_chan[j]] = S * codes[j * 128 + t] + Z;
+                }
+            }
+        } else {
+            orc_unpack_vtile(vc + (int64_t)g * v_tile_stride, v_bits, codes);
+            for (int t = 0; t < 128; t++) {
+                int64_t tok = (int64_t)g * 128 + t;
+                double S = param_load(vs, tok, pdt);
+                double Z = param_load(vz, tok, pdt);
+                for (int ch = 0; ch < 128; ch++) V[tok * 128 + ch] = S * codes[ch * 128 + t] + Z;
+            }
         }
     }
 

@@ -772,3 +772,121 @@ def test_mixed_key_quantizer_against_independent_build(pdt):
             bound = max(S / 2, Z - float(mn), float(mx) - Z - (2 ** b - 1) * S)
             assert np.abs(x - xhat).max() <= bound * (1 + 1e-6) + 1e-7
         assert np.array_equal(st.k_tiles[g], _mixed_tile_bytes(exp_codes))
+
+
+# ---------------------------------------------------------------------------
+# mixed-width values: the oracle's tile and quantizer against independent builds
+# ---------------------------------------------------------------------------
+# Value slot classes (header layout text; ChanMix Key design 3's classes read
+# for values with one group per token and class): 16 x 4-bit, 16 x 3-bit,
+# 16 x 1-bit, 80 x 2-bit; stored fields 4 bits for slots 0..31, 2 bits after.
+_VMIXED_WIDTHS = [4] * 16 + [3] * 16 + [1] * 16 + [2] * 80
+_VMIXED_CLASS = [0] * 16 + [1] * 16 + [2] * 16 + [3] * 80
+
+
+def _vmixed_bitpos(j, t):
+    """bit position of (value slot j, token t) in the 5120-byte tile, from the
+    header text: block b = j // 16 at word 64 * (4b) (b < 2) or 64 * (8 + 2(b-2));
+    word (w * 16 + n) * 4 + a holds 32 / cw tokens 32a + w * (32/cw) + i"""
+    b, n = divmod(j, 16)
+    cw = 4 if b < 2 else 2
+    base = 64 * (4 * b if b < 2 else 8 + 2 * (b - 2))
+    a, r = divmod(t, 32)
+    w, i = divmod(r, 32 // cw)
+    return (base + (w * 16 + n) * 4 + a) * 32 + i * cw, cw
+
+
+def test_vmixed_tile_positions_by_hand():
+    c = np.zeros((128, 128), np.uint16)      # [slot][token]
+    c[0, 0] = 0x9                            # block 0, word 0, bits 0..3
+    c[17, 9] = 0x5                           # 3-bit slot 17, token 9: word 256 + 17*4 = 324, bits 4..7
+    c[33, 40] = 1                            # 1-bit slot 33, token 40: word 512 + 4 + 1 = 517, bit 16
+    c[127, 127] = 3                          # last slot and token: word 1279, bits 30..31
+    t = oracle.pack_vmixed(c)
+    assert t.size == 5120
+    assert t[0] == 0x09
+    assert t[4 * 324] == 0x50
+    assert t[4 * 517 + 2] == 0x01
+    assert t[4 * 1279 + 3] == 0xC0
+    assert int(np.count_nonzero(t)) == 4
+    assert list(oracle.vmixed_slot_bits()) == _VMIXED_WIDTHS
+    r = np.random.default_rng(9).integers(0, 1 << 16, (128, 128))
+    r = (r % (1 << np.array(_VMIXED_WIDTHS))[:, None]).astype(np.uint16)
+    assert np.array_equal(oracle.unpack_vmixed(oracle.pack_vmixed(r)), r)
+
+
+@pytest.mark.parametrize("pdt", [oracle.E4M3, oracle.F16])
+def test_mixed_value_quantizer_against_independent_build(pdt):
+    """Every token's value slots of one class form one group: Z' is the
+    narrowed minimum of the class's channels (slot -> channel through the
+    map), S' the narrowed range / (2^b - 1) at the class width, every code the
+    nearest level (brute force, exact rationals), and the bytes equal an
+    independent packing of the header's layout text; params are [token][class]."""
+    rng = np.random.default_rng(4321 + pdt)
+    T = 128
+    chan_scale = np.exp(rng.uniform(-1.5, 1.5, 128)).astype(np.float32)
+    v = (rng.standard_normal((T, 128)).astype(np.float32) * chan_scale).astype(np.float32)
+    if pdt == oracle.E4M3:
+        v = (v * np.float32(0.5)).astype(np.float32)
+    k = rng.standard_normal((T, 128)).astype(np.float32)
+    vsc = rng.permutation(128).astype(np.int16)
+    st = oracle.quantize_stream(k, v, 4, 0, pdt, None, vsc)
+    S = oracle.decode(st.vs, pdt)
+    Z = oracle.decode(st.vz, pdt)
+    assert S.shape == (T, 4)
+    exp_codes = np.zeros((128, T), np.int64)
+    first = [0, 16, 32, 48, 128]
+    for t in range(T):
+        for cls in range(4):
+            slots = list(range(first[cls], first[cls + 1]))
+            b = _VMIXED_WIDTHS[first[cls]]
+            x = v[t, vsc[slots]]
+            mn, mx = np.float32(x.min()), np.float32(x.max())
+            s32 = np.float32(np.float32(mx - mn) / np.float32(2 ** b - 1))
+            Sx, Zx = _narrow_ref(s32, pdt), _narrow_ref(mn, pdt)
+            assert S[t, cls] == Sx and Z[t, cls] == Zx, (t, cls)
+            for j, xv in zip(slots, x.tolist()):
+                if Sx == 0:
+                    exp_codes[j, t] = 0
+                    continue
+                ex = (Fraction(xv) - Fraction(Zx)) / Fraction(Sx)
+                exp_codes[j, t] = min(max(round(ex), 0), 2 ** b - 1)
+    got = oracle.unpack_vmixed(st.v_tiles[0]).astype(np.int64)
+    diff = np.argwhere(got != exp_codes)
+    for j, t in diff:          # near-ties only (two binary32 roundings)
+        b = _VMIXED_WIDTHS[j]
+        cls = _VMIXED_CLASS[j]
+        ex = (Fraction(float(v[t, vsc[j]])) - Fraction(float(Z[t, cls]))) / Fraction(float(S[t, cls]))
+        assert abs(abs(ex - math.floor(ex)) - Fraction(1, 2)) < max(abs(ex), Fraction(1)) / 2 ** 21
+        assert abs(int(got[j, t]) - int(exp_codes[j, t])) == 1
+        exp_codes[j, t] = got[j, t]
+    bits = 0
+    for j in range(128):
+        for t in range(T):
+            pos, cw = _vmixed_bitpos(j, t)
+            bits |= int(exp_codes[j, t]) << pos
+    assert np.array_equal(st.v_tiles[0], np.frombuffer(bits.to_bytes(5120, "little"), np.uint8))
+    # reconstruction within the storage-mode bound of each (token, class):
+    # max(S'/2, Z' - min, max - Z' - (2^b - 1) S')
+    V = oracle.dequant_v(st)
+    for cls in range(4):
+        ch = vsc[first[cls]:first[cls + 1]].astype(np.int64)
+        b = _VMIXED_WIDTHS[first[cls]]
+        err = np.abs(V[:, ch] - v[:, ch]).max(axis=1)
+        mn, mx = v[:, ch].min(axis=1), v[:, ch].max(axis=1)
+        bound = np.maximum.reduce([S[:, cls] / 2, Z[:, cls] - mn, mx - Z[:, cls] - (2 ** b - 1) * S[:, cls]])
+        assert np.all(err <= bound + 1e-6)
+
+
+def test_mixed_value_attention_c_matches_numpy():
+    """The C two-pass attention reading the mixed value tile (its own unpack
+    and slot -> channel scatter) equals the numpy path (dequant_v, softmax)."""
+    rng = np.random.default_rng(77)
+    k = rng.standard_normal((384, 128)).astype(np.float32)
+    v = rng.standard_normal((384, 128)).astype(np.float32)
+    q = oracle.narrow(rng.standard_normal((4, 128)).astype(np.float32), oracle.BF16)
+    for kb, sc in ((4, None), (0, rng.permutation(128).astype(np.int16))):
+        st = oracle.quantize_stream(k, v, kb, 0, oracle.E4M3, sc, rng.permutation(128).astype(np.int16))
+        a = oracle.decode_attn(st, q, 1 / math.sqrt(128))
+        b = oracle.decode_attn_union([st], q, 1 / math.sqrt(128))
+        assert np.allclose(a, b, rtol=1e-11, atol=1e-13)
