@@ -260,7 +260,7 @@ class Stream:
 
     @property
     def n_tok(self):
-        return self.vs.shape[0]
+        return self.k_tiles.shape[0] * 128
 
 
 def quantize_stream(k: np.ndarray, v: np.ndarray, k_bits: int, v_bits: int, pdt: int,
@@ -287,8 +287,8 @@ def quantize_stream(k: np.ndarray, v: np.ndarray, k_bits: int, v_bits: int, pdt:
         vsc = np.ascontiguousarray(v_slot_chan, dtype=np.int16)
         assert vsc.shape == (128,) and sorted(vsc.tolist()) == list(range(128))
         vt = np.zeros((nt, VMIXED_TILE_BYTES), dtype=np.uint8)
-        vs = np.empty((T, 4), dtype=PARAM_NP[pdt])
-        vz = np.empty((T, 4), dtype=PARAM_NP[pdt])
+        vs = np.empty((4, T), dtype=PARAM_NP[pdt])      # [class][token]
+        vz = np.empty((4, T), dtype=PARAM_NP[pdt])
         L.orc_quantize_v_mixed(_p(v), 128, T, pdt, _p(vsc), _p(vt), vt.shape[1], _p(vs), _p(vz))
         return Stream(k_bits, v_bits, pdt, kt, ks, kz, vt, vs, vz, sc, vsc)
     vt = np.zeros((nt, tile_bytes(v_bits)), dtype=np.uint8)
@@ -347,7 +347,7 @@ def dequant_v(st: Stream) -> np.ndarray:
         cls = np.array([0] * 16 + [1] * 16 + [2] * 16 + [3] * 80)
         for g in range(nt):
             codes = unpack_vmixed(st.v_tiles[g]).astype(np.float64)         # [slot][t]
-            Sg, Zg = S[g * 128:(g + 1) * 128], Z[g * 128:(g + 1) * 128]     # [t][class]
+            Sg, Zg = S[:, g * 128:(g + 1) * 128].T, Z[:, g * 128:(g + 1) * 128].T   # [t][class]
             val = codes.T * Sg[:, cls] + Zg[:, cls]                         # [t][slot]
             out[g * 128:(g + 1) * 128][:, st.v_slot_chan.astype(np.int64)] = val
         return out

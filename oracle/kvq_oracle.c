@@ -373,7 +373,8 @@ void orc_unpack_mixed(const uint8_t *tile, uint16_t *codes)
  * [CHANMIX] Key design 3, read for values with per-class token groups):
  * value slot j holds channel v_slot_chan[j]; slots 0..15 are 4-bit, 16..31
  * 3-bit, 32..47 1-bit, 48..127 2-bit.  Each (token, class) is one group with
- * its own S', Z' (params [token][4], class order 4, 3, 1, 2 bits).  The tile
+ * its own S', Z' (params [class][token] per stream, class order 4, 3, 1, 2
+ * bits).  The tile
  * holds eight blocks of 16 slots (block b = slots 16b .. 16b+15) in order;
  * block b stores its codes in fields of cw = 4 bits (b < 2; the 3-bit codes
  * of block 1 in the low 3 bits) or cw = 2 bits (b >= 2; the 1-bit codes of
@@ -473,7 +474,7 @@ void orc_quantize_v(const float *v, int64_t t_stride, int n_tok, int bits, int p
 
 /* Values with mixed channel widths: for every token, the slots of each class
  * form one group (the class's channels of that token) quantized at the
- * class width; params s[tok * 4 + class], z[...]. */
+ * class width; params s[class * n_tok + tok], z[...]. */
 void orc_quantize_v_mixed(const float *v, int64_t t_stride, int n_tok, int pdt,
                           const int16_t *slot_chan, uint8_t *codes, int64_t tile_stride,
                           void *s, void *z)
@@ -488,7 +489,8 @@ void orc_quantize_v_mixed(const float *v, int64_t t_stride, int n_tok, int pdt,
                 uint16_t q[128];
                 int n = first[k + 1] - first[k];
                 for (int i = 0; i < n; i++) x[i] = v[tok * t_stride + slot_chan[first[k] + i]];
-                orc_quantize_group(x, 1, n, orc_vmixed_slot_bits(first[k]), pdt, q, 1, s, z, tok * 4 + k);
+                orc_quantize_group(x, 1, n, orc_vmixed_slot_bits(first[k]), pdt, q, 1, s, z,
+                                   (int64_t)k * n_tok + tok);
                 for (int i = 0; i < n; i++) jt[(first[k] + i) * 128 + t] = q[i];
             }
         }
@@ -614,8 +616,8 @@ int orc_decode_attn(const uint8_t *kc, int64_t k_tile_stride, const void *ks, co
             for (int t = 0; t < 128; t++) {
                 int64_t tok = (int64_t)g * 128 + t;
                 for (int j = 0; j < 128; j++) {
-                    double S = param_load(vs, tok * 4 + vmixed_class(j), pdt);
-                    double Z = param_load(vz, tok * 4 + vmixed_class(j), pdt);
+                    double S = param_load(vs, (int64_t)vmixed_class(j) * n_tok + tok, pdt);
+                    double Z = param_load(vz, (int64_t)vmixed_class(j) * n_tok + tok, pdt);
                     V[tok * 128 + v_slot_chan[j]] = S * codes[j * 128 + t] + Z;
                 }
             }

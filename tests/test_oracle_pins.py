@@ -821,7 +821,7 @@ def test_mixed_value_quantizer_against_independent_build(pdt):
     narrowed minimum of the class's channels (slot -> channel through the
     map), S' the narrowed range / (2^b - 1) at the class width, every code the
     nearest level (brute force, exact rationals), and the bytes equal an
-    independent packing of the header's layout text; params are [token][class]."""
+    independent packing of the header's layout text; params are [class][token]."""
     rng = np.random.default_rng(4321 + pdt)
     T = 128
     chan_scale = np.exp(rng.uniform(-1.5, 1.5, 128)).astype(np.float32)
@@ -831,8 +831,8 @@ def test_mixed_value_quantizer_against_independent_build(pdt):
     k = rng.standard_normal((T, 128)).astype(np.float32)
     vsc = rng.permutation(128).astype(np.int16)
     st = oracle.quantize_stream(k, v, 4, 0, pdt, None, vsc)
-    S = oracle.decode(st.vs, pdt)
-    Z = oracle.decode(st.vz, pdt)
+    S = oracle.decode(st.vs, pdt).T          # params are [class][token]
+    Z = oracle.decode(st.vz, pdt).T
     assert S.shape == (T, 4)
     exp_codes = np.zeros((128, T), np.int64)
     first = [0, 16, 32, 48, 128]
