@@ -33,14 +33,14 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, profiles/decode_kernel_*.md)
 # for the kernel source with the given digest, and the factors that map each
 # counter onto true bytes: a plain 512 MiB device copy in the same run reads
-# FETCH_SIZE = 262161.3 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
-# fetch counter is scaled by 524288/262161.3 and the write counter by 1.  The
+# FETCH_SIZE = 262160.2 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
+# fetch counter is scaled by 524288/262160.2 and the write counter by 1.  The
 # figure is reported only while the kernel source is unchanged.
 COUNTER_TRAFFIC = {
-    "source_sha256": "83a583f4be16bcb72e373cedb716954ff6c7f869102531c1c787b1c63fda7755",
-    "fetch_kib": 147930.0,
+    "source_sha256": "47a1d787eca7363cc1f04f8c7962b3de4e749aee4bbee936870a1d6729357e89",
+    "fetch_kib": 139901.8,
     "write_kib": 3664.0,
-    "fetch_factor": 524288.0 / 262161.3,
+    "fetch_factor": 524288.0 / 262160.2,
     "write_factor": 1.0,
 }
 KERNEL_SOURCES = ("kv_cache_mixed_amd/csrc/decode_attn.hip", "kv_cache_mixed_amd/csrc/kvq_device.h")

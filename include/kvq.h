@@ -42,7 +42,8 @@
  *   small enough that S' and Z' are finite in the parameter dtype.
  *   Keys are grouped channel-wise: one group = one channel (slot) over one
  *   128-token tile.  Values are grouped token-wise: one group = the 128
- *   channels of one token ([CHANMIX] Background; [PMKVQ] related work on KIVI).
+ *   channels of one token, or for mixed values the channels of one width
+ *   class of one token ([CHANMIX] Background; [PMKVQ] related work on KIVI).
  *   Bit widths: 16, 8, 4, 2, 1 ("16-bit" is an integer code, not fp16).
  *
  * Equivalent Right Shift ([PMKVQ] Key design 1, ERS equation), per code:
@@ -84,6 +85,20 @@
  *     sits at tile offset 4096 with 2 bytes per token: logical bytes 32, 33.
  *     Tokens are in order inside a plane.
  *
+ *   Value tile, mixed width (v_bits == KVQ_VMIXED, 5120 bytes) (the [CHANMIX]
+ *     Key design 3 channel classes read for values: token-wise groups, one
+ *     per class of each token): slot j of a token holds channel
+ *     v_slot_chan[h][j]; slots 0..15 are 4-bit, 16..31 3-bit, 32..47 1-bit,
+ *     48..127 2-bit (class k = 0, 1, 2, 3 in that order; 2.25 code bits per
+ *     value).  The tile is eight blocks of 16 slots, block m = slots
+ *     16m .. 16m + 15, stored at byte 1024*m (m < 2) or 2048 + 512*(m - 2)
+ *     (m >= 2).  Block m keeps its codes in fields of f = 4 bits (m < 2; the
+ *     3-bit codes of block 1 in the field's low bits) or f = 2 bits (m >= 2;
+ *     the 1-bit codes of block 2 in the field's low bit), so every code stays
+ *     inside one 32-bit word: inside the block, 32-bit word
+ *     (w * 16 + n) * 4 + a (w < f, n < 16, a < 4) holds slot 16m + n of the
+ *     32/f tokens 128g + 32a + w*(32/f) + i, code i at bits [i*f, i*f + f).
+ *
  *   Tile placement: tile g of stream (b, h) starts at
  *     k_codes + k_tile_off[(g * batch + b) * n_kv_heads + h]   if k_tile_off,
  *     k_codes + ((b * n_kv_heads + h) * max_tiles + g) * k_tile_stride   else,
@@ -96,7 +111,9 @@
  *   Parameters (S', Z' raw values of param_dtype):
  *     k_scale, k_zero: [batch][n_kv_heads][max_tiles][128]  (per tile, per slot;
  *                      for uniform keys slot j is channel j)
- *     v_scale, v_zero: [batch][n_kv_heads][max_tokens]       (per token)
+ *     v_scale, v_zero: [batch][n_kv_heads][max_tokens]       (per token), or
+ *                      [batch][n_kv_heads][4][max_tokens]    (mixed values:
+ *                      per class k and token, class-major)
  *
  * ------------------------------------------------------------------------
  * Decode attention ([CHANMIX] Overall framework and Key design 3: read the
@@ -107,6 +124,9 @@
  *     out[b][hq][c] = sum_t softmax(s)_t * V^[b][h][t][c]
  *   where K^, V^ are the reconstructions S' * q + Z' of the stored codes.
  *   q is bfloat16 [batch][n_q_heads][128]; out is float32, same shape.
+ *   Widths decoded: k_bits == v_bits in {16, 8, 4, 2, 1}; mixed keys with
+ *   4-, 2- or 1-bit values; mixed keys with mixed values when param_dtype
+ *   is KVQ_E4M3 or KVQ_F16.  Other pairs return KVQ_EUNSUPPORTED.
  */
 #ifndef KVQ_H
 #define KVQ_H
@@ -138,12 +158,14 @@ typedef enum {
 #define KVQ_HEAD_DIM 128
 #define KVQ_GROUP 128
 #define KVQ_KMIXED 0          /* k_bits value selecting the mixed-width key tile */
+#define KVQ_VMIXED 0          /* v_bits value selecting the mixed-width value tile */
 /* Largest per-stream capacity (2^26 tokens): device offsets into the
  * per-stream parameter arrays are 32-bit. */
 #define KVQ_MAX_TOKENS (1 << 26)
 /* Most residual (unquantized) tokens one decode call attends per stream. */
 #define KVQ_MAX_RESIDUAL 512
 #define KVQ_MIXED_TILE_BYTES 4352
+#define KVQ_VMIXED_TILE_BYTES 5120
 
 typedef struct kvq_cache {
     int32_t batch;            /* B >= 1 */
@@ -153,7 +175,7 @@ typedef struct kvq_cache {
     int32_t max_tokens;       /* capacity per stream, multiple of 128, <= KVQ_MAX_TOKENS */
     int32_t n_tokens;         /* tokens stored per stream, multiple of 128 */
     int32_t k_bits;           /* 16, 8, 4, 2, 1, or KVQ_KMIXED */
-    int32_t v_bits;           /* 16, 8, 4, 2, 1 */
+    int32_t v_bits;           /* 16, 8, 4, 2, 1, or KVQ_VMIXED */
     int32_t param_dtype;      /* kvq_dtype of S' and Z': F32, F16, BF16 or E4M3 */
     int32_t reserved0;        /* must be 0 */
     void *k_codes;            /* device: key tiles */
@@ -164,26 +186,31 @@ typedef struct kvq_cache {
     int64_t v_tile_stride;    /* bytes between tiles when v_tile_off is NULL */
     void *k_scale;            /* device [B][Hkv][max_tiles][128] */
     void *k_zero;             /* device [B][Hkv][max_tiles][128] */
-    void *v_scale;            /* device [B][Hkv][max_tokens] */
-    void *v_zero;             /* device [B][Hkv][max_tokens] */
+    void *v_scale;            /* device [B][Hkv][max_tokens] ([B][Hkv][4][max_tokens] mixed) */
+    void *v_zero;             /* device, as v_scale */
     const int16_t *k_slot_chan; /* device [Hkv][128]: channel held by slot j
                                    (mixed keys only, a permutation per head;
                                    the kernels use only its low 7 bits, so a
                                    map that is not a permutation reads wrong
                                    channels but never outside a row) */
+    const int16_t *v_slot_chan; /* device [Hkv][128]: channel held by value
+                                   slot j (mixed values only; same rules) */
 } kvq_cache;
 
 /* Human-readable name of a status code (static string). */
 const char *kvq_strerror(kvq_status status);
 
 /* Bytes of one packed tile at width `bits` (KVQ_KMIXED: the mixed key tile);
- * 0 for an invalid width. */
+ * 0 for an invalid width.  kvq_value_tile_bytes: the same for value tiles
+ * (KVQ_VMIXED: the mixed value tile). */
 size_t kvq_tile_bytes(int32_t bits);
+size_t kvq_value_tile_bytes(int32_t bits);
 
 /* Memory of a cache holding n_tokens tokens per stream at the given widths,
  * as the progressive schedule counts it ([PMKVQ] Key design 2: total KV
  * memory within the budget): key codes + value codes + every stored scale and
- * zero point, over all B * Hkv streams.  k_bits may be KVQ_KMIXED.  Returns -1
+ * zero point, over all B * Hkv streams.  k_bits may be KVQ_KMIXED, v_bits
+ * KVQ_VMIXED (four value scales and zero points per token).  Returns -1
  * for invalid arguments. */
 int64_t kvq_cache_bytes(const kvq_cache *cache, int32_t n_tokens, int32_t k_bits, int32_t v_bits);
 

@@ -441,7 +441,7 @@ __device__ __forceinline__ void pload(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
   (void)pdt;
   if (KVQ_DECODE_WAVES_PER_SIMD) return KVQ_DECODE_WAVES_PER_SIMD;
-  if (kb == 16 || (kb == 0 && vb == 1) || ns >= 4) return 1;
+  if (kb == 16 || (kb == 0 && vb <= 1) || ns >= 4) return 1;
   if (ns == 3) return kb == 4 ? KVQ_DECODE_NS3_OCC : 1;
   return 2;
 }
@@ -608,12 +608,15 @@ __global__ __launch_bounds__(256) void decode_residual_kernel(ResArgs r, const u
 template <int KB, int VB, int PDT, int NS>
 __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kernel(DecodeArgs a) {
   constexpr bool MIXED = (KB == 0);
+  constexpr bool VMIX = (VB == 0);                   // mixed-width values
   constexpr int NFK = MIXED ? 16 : UInfo<KB>::NF;    // key operand registers per token
   constexpr int NWK = MIXED ? 3 : UInfo<KB>::NW;     // key words per lane per token
   constexpr int NKK = NFK / 4;                       // key k-steps
-  constexpr int NFV = UInfo<VB>::NF;
-  constexpr int NWV = UInfo<VB>::NW;
-  constexpr int NSUB0 = (VB == 1) ? 1 : ((VB == 2) ? 2 : 4);
+  // mixed values: every slot block has 16 operand registers per tile (four
+  // 4-bit-field words or two 2-bit-field words); WVS below is then unused
+  constexpr int NFV = VMIX ? 16 : UInfo<VB>::NF;
+  constexpr int NWV = VMIX ? 2 : UInfo<VB>::NW;
+  constexpr int NSUB0 = VMIX ? 2 : ((VB == 1) ? 1 : ((VB == 2) ? 2 : 4));
   constexpr int NSUB = NSUB0 < KVQ_DECODE_NSUB_MAX ? NSUB0 : KVQ_DECODE_NSUB_MAX;  // sub-tiles per tile
   constexpr int TPS = 32 / NSUB;                     // tokens per lane per sub-tile
   constexpr int JB = 8 / NSUB;                       // key blocks per sub-tile
@@ -621,7 +624,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   constexpr int WVS = NWV / NSUB;                    // value words per sub-tile
   constexpr int KSV = FVS / 4;                       // value k-steps per sub-tile
   constexpr int PB = (PDT == KVQ_F32) ? 4 : ((PDT == KVQ_E4M3) ? 1 : 2);
-  constexpr int PWV = PW<PDT, TPS>::W;               // value-parameter words per sub-tile
+  constexpr int PWV = PW<PDT, TPS>::W;               // value-parameter words per sub-tile (and class)
+  constexpr int NCV = VMIX ? 4 : 1;                  // value parameter classes
+  constexpr int NVW = VMIX ? 10 : 8 * WVS;           // value words per stream per sub-tile
   constexpr int PWK = PW<PDT, 8>::W;                 // key-parameter words per 8 slots
   constexpr int KPA = 32 * PB;                       // words per 128 key parameters
   constexpr int KPL = (PB == 4) ? 2 : 1;             // of which one lane loads
@@ -637,6 +642,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   constexpr int LDS_WAVE = NFK * 2 * 64;             // u32 words of folded query per wave
   constexpr int CPOL = (KB == 16) ? 0 : KVQ_DECODE_CPOL_CODES;
   static_assert(KSV >= 1 && WVS >= 1, "sub-tile must hold whole value k-steps");
+  static_assert(!VMIX || (NS == 1 && TPS == 16), "mixed values: one stream, 16 tokens per sub-tile");
   static_assert(LDS_WAVE >= 16 * 128 && TPS % 8 == 0, "layout assumptions");
 
   // folded query (per wave) during the loop; the wave partial afterwards
@@ -695,13 +701,14 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
                               : (uint32_t)(row0 * ROW_K + 4 * KB * lg);
   const uint32_t koff4 = 4096 + 2 * row0;                       // mixed plane 4
   const uint32_t voff4 = (uint32_t)(4 * n + lg) * 16;           // value words (w, h, n, lg, 0..3)
+  const uint32_t voffm = (uint32_t)(16 * n + 4 * lg);            // mixed value words (w, n, lg)
   // parameter arrays from the group's first stream on (offsets stay below 2^32:
   // the host bounds max_tokens)
   const int64_t s0 = (int64_t)grp * NS;
   const int own_c = real ? own : 0;
-  const uint32_t vpoff = (uint32_t)(((int64_t)own_c * g.max_tokens + 32 * lg) * PB);
-  const __amdgpu_buffer_rsrc_t r_vs = rsrc((const uint8_t*)g.v_scale + s0 * g.max_tokens * PB, 0xffffffffu);
-  const __amdgpu_buffer_rsrc_t r_vz = rsrc((const uint8_t*)g.v_zero + s0 * g.max_tokens * PB, 0xffffffffu);
+  const uint32_t vpoff = (uint32_t)(((int64_t)own_c * NCV * g.max_tokens + 32 * lg) * PB);
+  const __amdgpu_buffer_rsrc_t r_vs = rsrc((const uint8_t*)g.v_scale + s0 * NCV * g.max_tokens * PB, 0xffffffffu);
+  const __amdgpu_buffer_rsrc_t r_vz = rsrc((const uint8_t*)g.v_zero + s0 * NCV * g.max_tokens * PB, 0xffffffffu);
   const __amdgpu_buffer_rsrc_t r_ks = rsrc((const uint8_t*)g.k_scale + s0 * g.max_tokens * PB, 0xffffffffu);
   const __amdgpu_buffer_rsrc_t r_kz = rsrc((const uint8_t*)g.k_zero + s0 * g.max_tokens * PB, 0xffffffffu);
   // key parameters: lane l loads word l (and l + 64) of the tile's 128 (e4m3:
@@ -718,6 +725,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   }
 
   float m_run = -INFINITY, l_run = 0.0f, z_run = 0.0f;
+  float zm_run[NCV];   // mixed values: zero-point sums per class
+#pragma unroll
+  for (int k = 0; k < NCV; k++) zm_run[k] = 0.0f;
   int e_run = -1000;
   const float m1 = opaque_m1();
   float ak = 0.0f, bk0 = 0.0f;
@@ -733,7 +743,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // during its key product and softmax)
   struct Buf {
     uint32_t kw[NS][JB][NWK];
-    uint32_t vs[PWV], vz[PWV];
+    uint32_t vs[NCV * PWV], vz[NCV * PWV];
     uint32_t kp[NS][2][KPL];   // next tile's key scales / zeros (sub-tile 0 only)
   };
 
@@ -742,6 +752,23 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // channels n, 16+n, 32+n, 48+n (h = 0) and 64+n, ... (h = 1) as 16
   // contiguous bytes: two 16-byte loads per plane, 1 KB per wave each
   auto load_vw = [&](uint32_t* vw, __amdgpu_buffer_rsrc_t rv, int sub) {
+    if constexpr (VMIX) {
+      // mixed values: block m's word (w, n, lg) at 4 * (block word + 64 w) +
+      // voffm; the sub-tile's 16 tokens are planes 2 sub, 2 sub + 1 of the
+      // 4-bit-field blocks 0, 1 (vw[2m + 0..1]) and plane sub of the
+      // 2-bit-field blocks 2..7 (vw[2 + m])
+#pragma unroll
+      for (int m = 0; m < 2; m++)
+#pragma unroll
+        for (int w = 0; w < 2; w++)
+          vw[2 * m + w] = __builtin_amdgcn_raw_buffer_load_b32(
+              rv, voffm, (uint32_t)(vmixed_block_word(m) + 64 * (2 * sub + w)) * 4, CPOL);
+#pragma unroll
+      for (int m = 2; m < 8; m++)
+        vw[2 + m] = __builtin_amdgcn_raw_buffer_load_b32(rv, voffm, (uint32_t)(vmixed_block_word(m) + 64 * sub) * 4,
+                                                         CPOL);
+      return;
+    }
 #pragma unroll
     for (int w = 0; w < WVS; w++)
 #pragma unroll
@@ -753,7 +780,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   };
   auto v_rsrc = [&](int s, int tile) {
     const int bh = min(grp * NS + s, BH - 1);
-    return rsrc(g.v_codes + v_tile_offset(g, bh / g.H, bh % g.H, tile), 2048 * VB);
+    return rsrc(g.v_codes + v_tile_offset(g, bh / g.H, bh % g.H, tile), VMIX ? KVQ_VMIXED_TILE_BYTES : 2048 * VB);
   };
 
   // sub-tile `sub` (a constant after unrolling) of the chunk's tile k: key
@@ -807,8 +834,11 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   auto load_p = [&](Buf& bf, int k, int sub) {
     const int tile = t_base + k;
     const uint32_t psoff = (uint32_t)(tile * 128 + sub * TPS) * PB;
-    pload<PDT, TPS>(r_vs, vpoff, psoff, bf.vs);
-    pload<PDT, TPS>(r_vz, vpoff, psoff, bf.vz);
+#pragma unroll
+    for (int k = 0; k < NCV; k++) {   // mixed values: class k's parameters k * max_tokens further
+      pload<PDT, TPS>(r_vs, vpoff, psoff + (uint32_t)(k * g.max_tokens * PB), bf.vs + k * PWV);
+      pload<PDT, TPS>(r_vz, vpoff, psoff + (uint32_t)(k * g.max_tokens * PB), bf.vz + k * PWV);
+    }
   };
   auto load = [&](Buf& bf, int k, int sub) {
     load_k(bf, k, sub);
@@ -999,10 +1029,10 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // been read
   auto issue_v = [&](uint32_t* vw, int k, int sub) {
 #pragma unroll
-    for (int s = 0; s < NS; s++) load_vw(vw + s * 8 * WVS, v_rsrc(s, t_base + k), sub);
+    for (int s = 0; s < NS; s++) load_vw(vw + s * NVW, v_rsrc(s, t_base + k), sub);
   };
   auto compute = [&](Buf& bf, int ti, int sub, int ti2, int sub2) {
-    uint32_t vjit[NS * 8 * WVS];
+    uint32_t vjit[NS * NVW];
     issue_v(vjit, ti, sub);
     const uint32_t* vwp = vjit;
     if (sub == 0) fold_query(bf);
@@ -1041,7 +1071,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
         for (int jj = 0; jj < JB; jj++) acc[s][jj] = mfma(av[s][jj], bl4, acc[s][jj]);
     }
-    load_k(bf, ti2, sub2);
+    if (ti2 >= 0) load_k(bf, ti2, sub2);   // nothing to prefetch past the wave's last tile
     // ---- logits l = ak * v + bk0 (v the column's own raw sum) and an online
     // softmax with a lazy running max: the reference m_run only moves when a
     // logit exceeds it by more than TAU (so e <= 2^TAU), and the accumulator
@@ -1065,10 +1095,30 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     // by mixed-precision fmas.  smx: the lane's largest value scale as a
     // binary32 bit pattern (scales are >= +0, so patterns order like values)
     constexpr bool MIX = (PDT == KVQ_F16);
-    uint32_t rvs[PWV], rvz[PWV];
-    float vs[MIX ? 1 : TPS], vz[MIX ? 1 : TPS];
+    uint32_t rvs[NCV * PWV], rvz[NCV * PWV];
+    float vs[(MIX || VMIX) ? 1 : TPS], vz[(MIX || VMIX) ? 1 : TPS];
+    // mixed values with binary32-converted scales: class k, token i at sv[k * TPS + i]
+    float sv[(VMIX && !MIX) ? NCV * TPS : 1];
     uint32_t smx;
-    if constexpr (MIX) {
+    if constexpr (VMIX) {
+#pragma unroll
+      for (int w = 0; w < NCV * PWV; w++) { rvs[w] = bf.vs[w]; rvz[w] = bf.vz[w]; }
+      if constexpr (MIX) {
+        uint32_t m2 = rvs[0];
+#pragma unroll
+        for (int w = 1; w < NCV * PWV; w++) m2 = pk_max_u16(m2, rvs[w]);
+        smx = f2u((float)__builtin_bit_cast(_Float16, (uint16_t)max(m2 & 0xffffu, m2 >> 16)));
+      } else {
+        smx = 0;
+#pragma unroll
+        for (int k = 0; k < NCV; k++)
+#pragma unroll
+          for (int i = 0; i < TPS; i++) {
+            sv[k * TPS + i] = pget<PDT>(rvs + k * PWV, i);
+            smx = max(smx, f2u(sv[k * TPS + i]));   // scales are >= +0
+          }
+      }
+    } else if constexpr (MIX) {
 #pragma unroll
       for (int w = 0; w < PWV; w++) { rvs[w] = bf.vs[w]; rvz[w] = bf.vz[w]; }
       uint32_t m2 = rvs[0];
@@ -1082,7 +1132,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
       for (int i = 0; i < TPS; i++) smx = max(smx, f2u(vs[i]));
     }
-    load_p(bf, ti2, sub2);
+    if (ti2 >= 0) load_p(bf, ti2, sub2);
     // A column's reference max moves only when one of its logits exceeds it
     // by more than TAU, and its value-scale exponent e_run only when a larger
     // scale arrives.  Both need the reductions over the four lane groups, so
@@ -1103,98 +1153,165 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       l_run *= rescale;
       z_run *= rescale;
 #pragma unroll
+      for (int k = 0; k < NCV; k++) zm_run[k] *= rescale;
+#pragma unroll
       for (int cb = 0; cb < 8; cb++) acc_o[cb] *= rescale;
     }
-    // e''(i) = e(i) * 2^ps * 2^W(i) straight from the exponent; the running
-    // sums l_run, z_run are kept in units of 2^ps.
-    // The probability operand of PV is one binary16 per token (P~ = rne(P)).
-    // Its rounding residual r = P - P~ meets every code of the token; the
-    // part r * VMID (VMID = the codes' midpoint (2^VB - 1) / 2) is added back
-    // exactly through the zero-point sum -- e * (Z + VMID * S) - VMID * P~ --
-    // and only r * (code - VMID), which has no common sign, is left out.
-    constexpr float VMID = 0.5f * (float)((1u << VB) - 1u);
-    const float c0 = bk0 - m_run + (float)min(VH - e_run, PSMAX);
-    float p[TPS];
-    float lsum = 0.0f;
-    float zc[10], zr[10];
+    if constexpr (VMIX) {
+      // Mixed-width values.  e(i) = 2^(logit - m) * 2^ps without field
+      // weight; class k's probability operand is P_k(i) = e(i) * S_k(i) *
+      // 2^W(i), W(i) the weight of token i's field in the class's container
+      // (4-bit fields for classes 0, 1, 2-bit fields for classes 2, 3).
+      // Each class keeps its own zero-point sum, with the rounding of its
+      // binary16 P~ made up at the class's code midpoint as for uniform
+      // widths; the residual sums read P~ * 2^-W exactly through fdot2.
+      const float c0 = bk0 - m_run + (float)min(VH - e_run, PSMAX);
+      float e[TPS], ew4[TPS], ew2[TPS];
+      float lsum = 0.0f;
 #pragma unroll
-    for (int k = 0; k < 10; k++) { zc[k] = 0.0f; zr[k] = 0.0f; }
-#pragma unroll
-    for (int i = 0; i < TPS; i++) {
-      const int W = tok_w<VB, FVS>(i);
-      const float e = __builtin_amdgcn_exp2f(fmaf(ak, lv[i], c0 + (float)W));
-      lsum = fmaf(e, exp2i(-W), lsum);
-      if constexpr (MIX) {
-        zc[w_class(W)] = fmaf(e, __builtin_fmaf(VMID, half_at(rvs, i), half_at(rvz, i)), zc[w_class(W)]);
-        p[i] = fmaf(e, half_at(rvs, i), 0.0f);
-      } else {
-        zc[w_class(W)] = fmaf(e, fmaf(VMID, vs[i], vz[i]), zc[w_class(W)]);
-        p[i] = e * vs[i];
+      for (int i = 0; i < TPS; i++) {
+        e[i] = __builtin_amdgcn_exp2f(fmaf(ak, lv[i], c0));
+        lsum += e[i];
+        ew4[i] = e[i] * exp2i(tok_w<4, FVS>(i));
+        ew2[i] = e[i] * exp2i(tok_w<2, FVS>(i));
       }
-    }
-    l_run += lsum;
-
-    // ---- P operand and PV; every sub-tile has the field layout of sub-tile
-    // 0, shifted by WVS words and TPS tokens
-    uint32_t bvh[FVS];
+      l_run += lsum;
+      uint32_t bv[4][FVS];
 #pragma unroll
-    for (int ff = 0; ff < FVS; ff++) {
-      // a token whose codes span two fields (the bytes of a 16-bit code)
-      // carries the weight of its first field; the other gets the difference
-      const Fld F = ufield<VB>(ff);
-      const int dwe = (F.wexp - F.pos) - tok_w<VB, FVS>(F.lo);
-      const f16x2 h = __builtin_convertvector((f32x2){p[F.lo] * exp2i(dwe), p[F.hi] * exp2i(dwe)}, f16x2);
-      bvh[ff] = __builtin_bit_cast(uint32_t, h);
-      // the tokens' first field: P~ of both tokens into the residual sums
-      if (dwe == 0) zr[w_class(tok_w<VB, FVS>(F.lo))] = __builtin_amdgcn_fdot2(h, (f16x2){1.0f16, 1.0f16},
-                                                                               zr[w_class(tok_w<VB, FVS>(F.lo))], false);
-    }
-    float zsum = fmaf(-VMID, zr[0], zc[0]);
+      for (int k = 0; k < 4; k++) {
+        const float vmid = 0.5f * (float)((1u << vmixed_class_bits(k)) - 1u);
+        const uint32_t* ks = rvs + k * PWV;
+        const uint32_t* kz = rvz + k * PWV;
+        float zc = 0.0f, zr = 0.0f;
+        float p[TPS];
 #pragma unroll
-    for (int k = 1; k < 10; k++)
-      if (class_used<VB, FVS, TPS>(k)) zsum = fmaf(fmaf(-VMID, zr[k], zc[k]), exp2i(-class_w<VB>(k)), zsum);
-    z_run += zsum;
+        for (int i = 0; i < TPS; i++) {
+          const float ew = k < 2 ? ew4[i] : ew2[i];
+          if constexpr (MIX) {
+            zc = fmaf(e[i], __builtin_fmaf(vmid, half_at(ks, i), half_at(kz, i)), zc);
+            p[i] = fmaf(ew, half_at(ks, i), 0.0f);
+          } else {
+            zc = fmaf(e[i], fmaf(vmid, sv[k * TPS + i], pget<PDT>(kz, i)), zc);
+            p[i] = ew * sv[k * TPS + i];
+          }
+        }
 #pragma unroll
-    for (int s = 0; s < NS; s++) {
-      uint32_t bsh[FVS];
-#pragma unroll
-      for (int ff = 0; ff < FVS; ff++) {
-        const bool sel = (NS == 1) || (own == s);
-        bsh[ff] = sel ? bvh[ff] : 0u;
+        for (int ff = 0; ff < FVS; ff++) {
+          const Fld F = k < 2 ? ufield<4>(ff) : ufield<2>(ff);
+          const f16x2 h = __builtin_convertvector((f32x2){p[F.lo], p[F.hi]}, f16x2);
+          bv[k][ff] = __builtin_bit_cast(uint32_t, h);
+          const _Float16 iw = (_Float16)exp2i(F.pos - F.wexp);   // 2^-W: 1 .. 256, exact
+          zr = __builtin_amdgcn_fdot2(h, (f16x2){iw, iw}, zr, false);
+        }
+        zm_run[k] += fmaf(-vmid, zr, zc);
       }
-      f32x4* ao = acc_o;
+      // PV: block cb (slots 16 cb .. 16 cb + 15) against its class's operand
 #pragma unroll
-      for (int k = 0; k < KSV; k++) {
+      for (int kk = 0; kk < KSV; kk++) {
         uint32_t av[8][4];
 #pragma unroll
         for (int cb = 0; cb < 8; cb++)
 #pragma unroll
           for (int r = 0; r < 4; r++) {
-            const Fld F = ufield<VB>(4 * k + r);
-            av[cb][r] = field_subnormal(vwp[(s * 8 + cb) * WVS + F.w], F);
+            const Fld F = cb < 2 ? ufield<4>(4 * kk + r) : ufield<2>(4 * kk + r);
+            av[cb][r] = field_subnormal(cb < 2 ? vwp[2 * cb + F.w] : vwp[2 + cb], F);
           }
 #pragma unroll
-        for (int cb = 0; cb < 8; cb++) ao[cb] = mfma(av[cb], bsh + 4 * k, ao[cb]);
+        for (int cb = 0; cb < 8; cb++) acc_o[cb] = mfma(av[cb], &bv[vmixed_block_class(cb)][4 * kk], acc_o[cb]);
+      }
+    } else {
+      // e''(i) = e(i) * 2^ps * 2^W(i) straight from the exponent; the running
+      // sums l_run, z_run are kept in units of 2^ps.
+      // The probability operand of PV is one binary16 per token (P~ = rne(P)).
+      // Its rounding residual r = P - P~ meets every code of the token; the
+      // part r * VMID (VMID = the codes' midpoint (2^VB - 1) / 2) is added back
+      // exactly through the zero-point sum -- e * (Z + VMID * S) - VMID * P~ --
+      // and only r * (code - VMID), which has no common sign, is left out.
+      constexpr float VMID = 0.5f * (float)((1u << VB) - 1u);
+      const float c0 = bk0 - m_run + (float)min(VH - e_run, PSMAX);
+      float p[TPS];
+      float lsum = 0.0f;
+      float zc[10], zr[10];
+  #pragma unroll
+      for (int k = 0; k < 10; k++) { zc[k] = 0.0f; zr[k] = 0.0f; }
+  #pragma unroll
+      for (int i = 0; i < TPS; i++) {
+        const int W = tok_w<VB, FVS>(i);
+        const float e = __builtin_amdgcn_exp2f(fmaf(ak, lv[i], c0 + (float)W));
+        lsum = fmaf(e, exp2i(-W), lsum);
+        if constexpr (MIX) {
+          zc[w_class(W)] = fmaf(e, __builtin_fmaf(VMID, half_at(rvs, i), half_at(rvz, i)), zc[w_class(W)]);
+          p[i] = fmaf(e, half_at(rvs, i), 0.0f);
+        } else {
+          zc[w_class(W)] = fmaf(e, fmaf(VMID, vs[i], vz[i]), zc[w_class(W)]);
+          p[i] = e * vs[i];
+        }
+      }
+      l_run += lsum;
+
+      // ---- P operand and PV; every sub-tile has the field layout of sub-tile
+      // 0, shifted by WVS words and TPS tokens
+      uint32_t bvh[FVS];
+  #pragma unroll
+      for (int ff = 0; ff < FVS; ff++) {
+        // a token whose codes span two fields (the bytes of a 16-bit code)
+        // carries the weight of its first field; the other gets the difference
+        const Fld F = ufield<VB>(ff);
+        const int dwe = (F.wexp - F.pos) - tok_w<VB, FVS>(F.lo);
+        const f16x2 h = __builtin_convertvector((f32x2){p[F.lo] * exp2i(dwe), p[F.hi] * exp2i(dwe)}, f16x2);
+        bvh[ff] = __builtin_bit_cast(uint32_t, h);
+        // the tokens' first field: P~ of both tokens into the residual sums
+        if (dwe == 0) zr[w_class(tok_w<VB, FVS>(F.lo))] = __builtin_amdgcn_fdot2(h, (f16x2){1.0f16, 1.0f16},
+                                                                                 zr[w_class(tok_w<VB, FVS>(F.lo))], false);
+      }
+      float zsum = fmaf(-VMID, zr[0], zc[0]);
+  #pragma unroll
+      for (int k = 1; k < 10; k++)
+        if (class_used<VB, FVS, TPS>(k)) zsum = fmaf(fmaf(-VMID, zr[k], zc[k]), exp2i(-class_w<VB>(k)), zsum);
+      z_run += zsum;
+  #pragma unroll
+      for (int s = 0; s < NS; s++) {
+        uint32_t bsh[FVS];
+  #pragma unroll
+        for (int ff = 0; ff < FVS; ff++) {
+          const bool sel = (NS == 1) || (own == s);
+          bsh[ff] = sel ? bvh[ff] : 0u;
+        }
+        f32x4* ao = acc_o;
+  #pragma unroll
+        for (int k = 0; k < KSV; k++) {
+          uint32_t av[8][4];
+  #pragma unroll
+          for (int cb = 0; cb < 8; cb++)
+  #pragma unroll
+            for (int r = 0; r < 4; r++) {
+              const Fld F = ufield<VB>(4 * k + r);
+              av[cb][r] = field_subnormal(vwp[(s * 8 + cb) * WVS + F.w], F);
+            }
+  #pragma unroll
+          for (int cb = 0; cb < 8; cb++) ao[cb] = mfma(av[cb], bsh + 4 * k, ao[cb]);
+        }
       }
     }
   };
 
   // ---- software-pipelined main loop (two register buffers).  One iteration
   // covers U sub-tiles (a whole tile, or two one-sub-tile tiles) unrolled, so
-  // the fold and every buffer choice are compile-time; the prefetch of the
-  // sub-tile after the wave's last one re-reads that last one (harmless, in
-  // bounds) instead of branching.
+  // the fold and every buffer choice are compile-time; past the wave's last
+  // tile the prefetches are skipped (a wave-uniform branch).  Re-reading the
+  // last tile instead measured 6% more DRAM reads than the algorithmic bytes
+  // (non-temporal code loads miss on the re-read).
   constexpr int U = NSUB >= 2 ? NSUB : 2;
   constexpr int TPI = U / NSUB;   // tiles per iteration (2 for one-sub-tile tiles)
   q1 = q0 + 4; q2 = q0 + 8; q3 = q0 + 12;
-  // the queue entry for sub-tile offset d (d = 0..3 tiles ahead), a valid tile
-  // when it lies past the chunk (such prefetches are never consumed)
+  // the queue entry for sub-tile offset d (d = 0..3 tiles ahead), or -1 when
+  // it lies past the chunk
   auto qk = [&](int d) -> int {
     const int v = d == 0 ? q0 : (d == 1 ? q1 : (d == 2 ? q2 : q3));
-    return v < t_count ? v : q0;
+    return v < t_count ? v : -1;
   };
   // the second buffer: loads run two sub-tiles ahead of the computation
-  if (q0 < t_count) load(b1, qk(1 / NSUB), 1 % NSUB);
+  if (q0 < t_count && qk(1 / NSUB) >= 0) load(b1, qk(1 / NSUB), 1 % NSUB);
 #pragma unroll 1
   while (q0 < t_count) {
     if constexpr (KVQ_DECODE_PRIO != 0) {
@@ -1236,17 +1353,27 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   const float unps = exp2i(-ps);
   const float l_tot = wave_sum16x4(l_run) * unps;
   const float z_tot = wave_sum16x4(z_run) * unps;
+  float zm_tot[NCV];
+#pragma unroll
+  for (int k = 0; k < NCV; k++) zm_tot[k] = VMIX ? wave_sum16x4(zm_run[k]) * unps : 0.0f;
   const float of = exp2i(24 - ps);           // acc_o * 2^24 / 2^ps
   if (lg == 0) {
     sh_ml[wave][n][0] = m_run;
     sh_ml[wave][n][1] = l_tot;
   }
+  // output row 16 cb + 4 lg + i is value slot 16 cb + 4 lg + i: channel
+  // v_slot_chan[kv head][slot] for mixed values (low 7 bits, so a map that
+  // is not a permutation scatters within the row), the slot itself otherwise
+  const int16_t* vsc = VMIX ? g.v_slot_chan + (int64_t)((real ? bh_own : 0) % g.H) * 128 : nullptr;
 #pragma unroll
   for (int cb = 0; cb < 8; cb++)
 #pragma unroll
     for (int i = 0; i < 4; i++) {
       const float a = acc_o[cb][i];
-      sh_o(wave, n, 16 * cb + 4 * lg + i) = (m_run == -INFINITY) ? 0.0f : a * of + z_tot;
+      const int slot = 16 * cb + 4 * lg + i;
+      const int ch = VMIX ? ((int)vsc[slot] & 127) : slot;
+      const float zt = VMIX ? zm_tot[vmixed_block_class(cb)] : z_tot;
+      sh_o(wave, n, ch) = (m_run == -INFINITY) ? 0.0f : a * of + zt;
     }
   __syncthreads();
 
@@ -1382,7 +1509,16 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       for (int k = 0; k < KR; k++)
         if (k < ns) num += wk[2 * k] * ov[it][k];
       const int64_t r0 = (int64_t)irow[it] - (int64_t)(a.slot0 + chunk) * G;
-      for (int k = KR; k < ns; k++) num += wk[2 * k] * *(const f32x4*)(a.part_o + (r0 + (int64_t)k * G) * 128 + ic4[it]);
+      // the other slots in batches of KR independent loads (one round trip
+      // per batch; a batch past the last slot re-reads that slot at weight 0)
+      for (int k0 = KR; k0 < ns; k0 += KR) {
+        f32x4 x[KR];
+#pragma unroll
+        for (int k = 0; k < KR; k++)
+          x[k] = *(const f32x4*)(a.part_o + (r0 + (int64_t)min(k0 + k, ns - 1) * G) * 128 + ic4[it]);
+#pragma unroll
+        for (int k = 0; k < KR; k++) num += (k0 + k < ns ? wk[2 * (k0 + k)] : 0.0f) * x[k];
+      }
       *(f32x4*)(a.out + (int64_t)sh_orow[col] * 128 + ic4[it]) = num / sden[col];
     }
     if (threadIdx.x == 0) __hip_atomic_store(a.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -1527,8 +1663,7 @@ size_t decode_workspace_bytes(int B, int H, int G, int max_tiles) {
 }
 
 bool decode_supported(int k_bits, int v_bits, int pdt) {
-  (void)pdt;
-  if (k_bits == 0) return v_bits == 1 || v_bits == 2 || v_bits == 4;
+  if (k_bits == 0) return v_bits == 1 || v_bits == 2 || v_bits == 4 || (v_bits == 0 && (pdt == KVQ_E4M3 || pdt == KVQ_F16));
   return k_bits == v_bits && (k_bits == 1 || k_bits == 2 || k_bits == 4 || k_bits == 8 || k_bits == 16);
 }
 
@@ -1564,6 +1699,9 @@ static hipError_t launch_decode_pdt(const DecodeArgs& a, const DecodePlan& p, hi
   if (kb == KBV && vb == VBV) return launch_ns<KBV, VBV, PDT>(a, p, st);
   KVQ_DEC(16, 16) KVQ_DEC(8, 8) KVQ_DEC(4, 4) KVQ_DEC(2, 2) KVQ_DEC(1, 1)
   KVQ_DEC(0, 1) KVQ_DEC(0, 2) KVQ_DEC(0, 4)
+  if constexpr (PDT == KVQ_E4M3 || PDT == KVQ_F16) {
+    KVQ_DEC(0, 0)
+  }
 #undef KVQ_DEC
   return hipErrorInvalidValue;
 }

@@ -19,11 +19,17 @@ namespace {
 
 bool valid_bits(int b) { return b == 1 || b == 2 || b == 4 || b == 8 || b == 16; }
 bool valid_kbits(int b) { return b == KVQ_KMIXED || valid_bits(b); }
+bool valid_vbits(int b) { return b == KVQ_VMIXED || valid_bits(b); }
 bool valid_pdt(int p) { return p == KVQ_F32 || p == KVQ_F16 || p == KVQ_BF16 || p == KVQ_E4M3; }
 int param_bytes(int p) { return p == KVQ_F32 ? 4 : (p == KVQ_E4M3 ? 1 : 2); }
 int64_t tile_bytes(int bits) {
   return bits == KVQ_KMIXED ? (int64_t)KVQ_MIXED_TILE_BYTES : (int64_t)2048 * bits;
 }
+int64_t vtile_bytes(int bits) {
+  return bits == KVQ_VMIXED ? (int64_t)KVQ_VMIXED_TILE_BYTES : (int64_t)2048 * bits;
+}
+// value scales (and zero points) per token
+int vparams_per_token(int bits) { return bits == KVQ_VMIXED ? 4 : 1; }
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
 // Structural checks shared by every call.  `bits_ok` lets callers validate
@@ -34,7 +40,7 @@ kvq_status check_cache(const kvq_cache* c) {
   if (c->head_dim != KVQ_HEAD_DIM || c->group != KVQ_GROUP) return KVQ_EUNSUPPORTED;
   if (c->max_tokens < 128 || c->max_tokens % 128 || c->max_tokens > KVQ_MAX_TOKENS) return KVQ_EINVAL;
   if (c->n_tokens < 0 || c->n_tokens % 128 || c->n_tokens > c->max_tokens) return KVQ_EINVAL;
-  if (!valid_kbits(c->k_bits) || !valid_bits(c->v_bits)) return KVQ_EINVAL;
+  if (!valid_kbits(c->k_bits) || !valid_vbits(c->v_bits)) return KVQ_EINVAL;
   if (!valid_pdt(c->param_dtype) || c->reserved0 != 0) return KVQ_EINVAL;
   if (!c->k_codes || !c->v_codes || !c->k_scale || !c->k_zero || !c->v_scale || !c->v_zero)
     return KVQ_EINVAL;
@@ -43,11 +49,12 @@ kvq_status check_cache(const kvq_cache* c) {
       !aligned(c->v_zero, 16))
     return KVQ_EINVAL;
   if (c->k_bits == KVQ_KMIXED && !c->k_slot_chan) return KVQ_EINVAL;
+  if (c->v_bits == KVQ_VMIXED && !c->v_slot_chan) return KVQ_EINVAL;
   if (!c->k_tile_off) {
     if (c->k_tile_stride < tile_bytes(c->k_bits) || c->k_tile_stride % 256) return KVQ_EINVAL;
   }
   if (!c->v_tile_off) {
-    if (c->v_tile_stride < tile_bytes(c->v_bits) || c->v_tile_stride % 256) return KVQ_EINVAL;
+    if (c->v_tile_stride < vtile_bytes(c->v_bits) || c->v_tile_stride % 256) return KVQ_EINVAL;
   }
   return KVQ_OK;
 }
@@ -73,6 +80,7 @@ kvq::Geo make_geo(const kvq_cache* c) {
   g.v_scale = c->v_scale;
   g.v_zero = c->v_zero;
   g.slot_chan = c->k_slot_chan;
+  g.v_slot_chan = c->v_slot_chan;
   return g;
 }
 
@@ -97,13 +105,18 @@ size_t kvq_tile_bytes(int32_t bits) {
   return (size_t)tile_bytes(bits);
 }
 
+size_t kvq_value_tile_bytes(int32_t bits) {
+  if (!valid_vbits(bits)) return 0;
+  return (size_t)vtile_bytes(bits);
+}
+
 int64_t kvq_cache_bytes(const kvq_cache* c, int32_t n_tokens, int32_t k_bits, int32_t v_bits) {
   if (!c || c->batch < 1 || c->n_kv_heads < 1 || !valid_pdt(c->param_dtype)) return -1;
-  if (n_tokens < 0 || n_tokens % 128 || !valid_kbits(k_bits) || !valid_bits(v_bits)) return -1;
+  if (n_tokens < 0 || n_tokens % 128 || !valid_kbits(k_bits) || !valid_vbits(v_bits)) return -1;
   const int64_t groups = n_tokens / 128;
   const int64_t pb = param_bytes(c->param_dtype);
-  const int64_t per_group = tile_bytes(k_bits) + tile_bytes(v_bits) + 2 * 128 * pb  // key S,Z
-                            + 2 * 128 * pb;                                         // value S,Z
+  const int64_t per_group = tile_bytes(k_bits) + vtile_bytes(v_bits) + 2 * 128 * pb  // key S,Z
+                            + 2 * 128 * pb * vparams_per_token(v_bits);              // value S,Z
   return (int64_t)c->batch * c->n_kv_heads * groups * per_group;
 }
 

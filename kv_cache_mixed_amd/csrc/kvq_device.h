@@ -196,6 +196,7 @@ struct Geo {
   void* v_zero;
   const int16_t* slot_chan;
   int32_t max_tokens;
+  const int16_t* v_slot_chan;   // mixed values: channel of value slot j per head
 };
 
 // The offset tables are read through the constant address space (they never
@@ -216,6 +217,19 @@ __device__ __forceinline__ int64_t k_param_base(const Geo& g, int b, int h, int 
 __device__ __forceinline__ int64_t v_param_base(const Geo& g, int b, int h, int64_t t) {
   return ((int64_t)b * g.H + h) * (int64_t)g.max_tokens + t;
 }
+// mixed values: parameter of class k (0..3) of token t, class-major per stream
+__device__ __forceinline__ int64_t vm_param_index(const Geo& g, int b, int h, int k, int64_t t) {
+  return (((int64_t)b * g.H + h) * 4 + k) * (int64_t)g.max_tokens + t;
+}
+
+// mixed-width value slots: 0..15 4-bit, 16..31 3-bit, 32..47 1-bit,
+// 48..127 2-bit (classes 0..3); blocks of 16 slots, the codes of block m in
+// fields of 4 bits (m < 2) or 2 bits (m >= 2)
+__host__ __device__ constexpr int vmixed_class_bits(int k) { return k == 0 ? 4 : (k == 1 ? 3 : (k == 2 ? 1 : 2)); }
+__host__ __device__ constexpr int vmixed_block_class(int m) { return m < 3 ? m : 3; }
+__host__ __device__ constexpr int vmixed_block_field(int m) { return m < 2 ? 4 : 2; }
+// first 32-bit word of block m in the 5120-byte tile
+__host__ __device__ constexpr int vmixed_block_word(int m) { return m < 2 ? 256 * m : 512 + 128 * (m - 2); }
 
 // mixed-width key slots: 0..7 4-bit, 8..23 alternating 3/1-bit, 24..127 2-bit
 __host__ __device__ constexpr int mixed_slot_bits(int j) {

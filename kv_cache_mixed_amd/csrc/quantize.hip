@@ -25,6 +25,9 @@
 
 namespace kvq {
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
 template <int IN>  // KVQ_F32 or KVQ_BF16
 __device__ __forceinline__ float load_in(const void* p, int64_t i) {
   if constexpr (IN == KVQ_F32) return __builtin_nontemporal_load((const float*)p + i);
@@ -338,6 +341,120 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __re
 }
 
 // ---------------------------------------------------------------------------
+// Values with mixed channel widths: for every token, the slots of each width
+// class (4, 3, 1, 2 bits; slot j holds channel v_slot_chan[h][j]) form one
+// group with its own S', Z'.  The tile's inputs pass through LDS in two
+// halves of 64 tokens (binary32, row pitch 129 words, so a wave reading one
+// channel of 64 tokens hits 32 banks).  Wave w quantizes slot blocks w and
+// w + 4 (16 slots each; the block's class, and so its width, is uniform over
+// the wave) of the half's 64 tokens, one token per lane: block minima and
+// maxima go through LDS so the five blocks of the 2-bit class share one
+// group.  Codes are staged as bytes [slot][token] and packed into the tile's
+// 32-bit words at the end, one word per thread and step, in tile order.
+// ---------------------------------------------------------------------------
+template <int PDT, int IN, bool VEC, bool GATHER>
+__global__ __launch_bounds__(256) void quantize_vmixed_kernel(Geo g, const void* __restrict__ vin,
+                                                              int64_t sb, int64_t sh, int64_t st,
+                                                              int t0, TokIdx ti) {
+  __shared__ float xs[64][129];
+  __shared__ __attribute__((aligned(16))) uint8_t codes[128][128];   // [slot][token]
+  __shared__ float bmn[8][64], bmx[8][64];                            // [block][token]
+  __shared__ int chan[128];
+  const int tile_local = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+  const int tile = t0 / 128 + tile_local;
+  const int wave = threadIdx.x >> 6, r = threadIdx.x & 63;
+  if (threadIdx.x < 128) chan[threadIdx.x] = (int)g.v_slot_chan[h * 128 + threadIdx.x] & 127;
+  const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (GATHER ? 0 : (int64_t)(tile_local * 128) * st);
+#pragma unroll 1
+  for (int half = 0; half < 2; half++) {
+    // stage 64 tokens: item i = (token row i / 32, channels 4 (i % 32) ..)
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int i = threadIdx.x + 256 * k;
+      const int tr = i >> 5, c4 = (i & 31) * 4;
+      const int t = half * 64 + tr;
+      const int64_t row = GATHER ? src_row(ti, b, h, g.H, tile_local * 128 + t) : (int64_t)t;
+      float x4[4];
+      load4<IN, VEC>(vin, base + row * st + c4, x4);
+#pragma unroll
+      for (int e = 0; e < 4; e++) xs[tr][c4 + e] = x4[e];
+    }
+    __syncthreads();
+    float x[2][16];
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int m = wave + 4 * u;
+      float mn, mx;
+#pragma unroll
+      for (int j = 0; j < 16; j++) {
+        x[u][j] = xs[r][chan[16 * m + j]];
+        mn = j ? fminf(mn, x[u][j]) : x[u][j];
+        mx = j ? fmaxf(mx, x[u][j]) : x[u][j];
+      }
+      bmn[m][r] = mn;
+      bmx[m][r] = mx;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 2; u++) {
+      const int m = wave + 4 * u;
+      const int k = vmixed_block_class(m);
+      float mn = bmn[m][r], mx = bmx[m][r];
+      if (k == 3) {
+#pragma unroll
+        for (int m2 = 3; m2 < 8; m2++) {
+          mn = fminf(mn, bmn[m2][r]);
+          mx = fmaxf(mx, bmx[m2][r]);
+        }
+      }
+      mn = mn + 0.0f;   // -0 and +0 are one value: keep +0 whatever the reduction order
+      mx = mx + 0.0f;
+      const float levels = (float)((1u << vmixed_class_bits(k)) - 1u);
+      const float s = (mx - mn) / levels;
+      const float sp = Param<PDT>::narrow(s);
+      const float zp = Param<PDT>::narrow(mn);
+      if (m < 4) {   // the class's first block stores its parameters
+        const int64_t pi = vm_param_index(g, b, h, k, (int64_t)tile * 128 + half * 64 + r);
+        Param<PDT>::store(g.v_scale, pi, s);
+        Param<PDT>::store(g.v_zero, pi, mn);
+      }
+#pragma unroll
+      for (int j = 0; j < 16; j += 8) {
+        uint32_t q[8];
+        quant_codes<true, 8>(&x[u][j], sp, zp, levels, q);
+#pragma unroll
+        for (int e = 0; e < 8; e++) codes[16 * m + j + e][half * 64 + r] = (uint8_t)q[e];
+      }
+    }
+    __syncthreads();   // xs and the block extremes are reused by the next half
+  }
+  // word wi of the tile: block m, inside it word (w * 16 + n) * 4 + a holds
+  // slot 16m + n for the 32/f tokens 32a + w * (32/f) + i, code i at bits
+  // [i*f, i*f + f)
+  uint32_t* out = (uint32_t*)(g.v_codes + v_tile_offset(g, b, h, tile));
+#pragma unroll
+  for (int k = 0; k < 5; k++) {
+    const int wi = threadIdx.x + 256 * k;
+    const bool wide = wi < 512;
+    const int m = wide ? (wi >> 8) : 2 + ((wi - 512) >> 7);
+    const int li = wide ? (wi & 255) : ((wi - 512) & 127);
+    const int a = li & 3, n = (li >> 2) & 15, w = li >> 6;
+    const uint8_t* src = &codes[16 * m + n][0];
+    uint32_t word = 0;
+    if (wide) {
+      const u32x2 c = *(const u32x2*)(src + 32 * a + 8 * w);
+#pragma unroll
+      for (int i = 0; i < 8; i++) word |= ((c[i / 4] >> (8 * (i % 4))) & 0xFu) << (4 * i);
+    } else {
+      const u32x4 c = *(const u32x4*)(src + 32 * a + 16 * w);
+#pragma unroll
+      for (int i = 0; i < 16; i++) word |= ((c[i / 4] >> (8 * (i % 4))) & 0x3u) << (2 * i);
+    }
+    out[wi] = word;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // host launchers
 // ---------------------------------------------------------------------------
 template <int PDT, int IN>
@@ -381,6 +498,17 @@ static hipError_t launch_v(const Geo& g, const void* v, const int64_t* s, int t0
                          s[0], s[1], s[2], t0, ti);                                                   \
     break;
   switch (g.v_bits) {
+    case 0:
+      if (ti.tok)
+        hipLaunchKernelGGL((quantize_vmixed_kernel<PDT, IN, false, true>), grid, block, 0, stm, g, v, s[0], s[1],
+                           s[2], t0, ti);
+      else if (vec)
+        hipLaunchKernelGGL((quantize_vmixed_kernel<PDT, IN, true, false>), grid, block, 0, stm, g, v, s[0], s[1],
+                           s[2], t0, ti);
+      else
+        hipLaunchKernelGGL((quantize_vmixed_kernel<PDT, IN, false, false>), grid, block, 0, stm, g, v, s[0], s[1],
+                           s[2], t0, ti);
+      break;
     KVQ_QV(1) KVQ_QV(2) KVQ_QV(4) KVQ_QV(8) KVQ_QV(16)
     default: return hipErrorInvalidValue;
   }

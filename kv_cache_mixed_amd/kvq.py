@@ -18,7 +18,9 @@ LIB_PATH = os.path.join(_HERE, "libkvq.so")
 F32, F16, BF16, E4M3 = 0, 1, 2, 3
 PARAM_BYTES = {F32: 4, F16: 2, BF16: 2, E4M3: 1}
 KMIXED = 0
+VMIXED = 0                 # v_bits selecting the mixed-width value tile
 MIXED_TILE_BYTES = 4352
+VMIXED_TILE_BYTES = 5120
 OK, EINVAL, EUNSUPPORTED, EBUDGET, EWORKSPACE, EHIP = range(6)
 SHIFT_ERS, SHIFT_DIRECT, SHIFT_MODIFIED = range(3)   # kvq_shift of the header
 MAX_RESIDUAL = 512          # KVQ_MAX_RESIDUAL of the header
@@ -37,6 +39,7 @@ class KvqCacheStruct(ctypes.Structure):
         ("k_scale", ctypes.c_void_p), ("k_zero", ctypes.c_void_p),
         ("v_scale", ctypes.c_void_p), ("v_zero", ctypes.c_void_p),
         ("k_slot_chan", ctypes.c_void_p),
+        ("v_slot_chan", ctypes.c_void_p),
     ]
 
 
@@ -60,7 +63,7 @@ class KvqError(RuntimeError):
 
 _lib = None
 
-EXPORTS = ["kvq_strerror", "kvq_tile_bytes", "kvq_cache_bytes", "kvq_quantize", "kvq_shrink",
+EXPORTS = ["kvq_strerror", "kvq_tile_bytes", "kvq_value_tile_bytes", "kvq_cache_bytes", "kvq_quantize", "kvq_shrink",
            "kvq_shrink_shift", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_decode_attn_noalloc",
            "kvq_decode_attn_residual", "kvq_quantize_tokens", "kvq_rank_tokens",
            "kvq_decode_split_workspace_bytes", "kvq_decode_attn_split",
@@ -82,6 +85,8 @@ def load():
     L.kvq_strerror.argtypes = [ctypes.c_int]
     L.kvq_tile_bytes.restype = ctypes.c_size_t
     L.kvq_tile_bytes.argtypes = [i32]
+    L.kvq_value_tile_bytes.restype = ctypes.c_size_t
+    L.kvq_value_tile_bytes.argtypes = [i32]
     L.kvq_cache_bytes.restype = i64
     L.kvq_cache_bytes.argtypes = [P, i32, i32, i32]
     L.kvq_quantize.restype = ctypes.c_int
@@ -237,6 +242,10 @@ def tile_bytes(bits: int) -> int:
     return int(load().kvq_tile_bytes(bits))
 
 
+def value_tile_bytes(bits: int) -> int:
+    return int(load().kvq_value_tile_bytes(bits))
+
+
 class PackedCache:
     """Device buffers of one block's packed cache plus the kvq_cache struct.
 
@@ -246,7 +255,7 @@ class PackedCache:
     """
 
     def __init__(self, batch, n_kv_heads, max_tokens, k_bits, v_bits, param_dtype=F16,
-                 slot_chan=None, device="cuda", layout="contiguous", pool_bytes=None):
+                 slot_chan=None, device="cuda", layout="contiguous", pool_bytes=None, v_slot_chan=None):
         import torch
         load()
         self.device = torch.device(device)
@@ -264,7 +273,7 @@ class PackedCache:
         self.pool = None
         if layout == "contiguous":
             self.k_stride = tile_bytes(k_bits)
-            self.v_stride = tile_bytes(v_bits)
+            self.v_stride = value_tile_bytes(v_bits)
             self.k_codes = torch.zeros(n_streams * self.max_tiles * self.k_stride, **u8)
             self.v_codes = torch.zeros(n_streams * self.max_tiles * self.v_stride, **u8)
             s.k_codes, s.v_codes = self.k_codes.data_ptr(), self.v_codes.data_ptr()
@@ -285,7 +294,8 @@ class PackedCache:
             raise ValueError(layout)
         self.k_scale = torch.zeros(n_streams * self.max_tiles * 128 * pb, **u8)
         self.k_zero = torch.zeros_like(self.k_scale)
-        self.v_scale = torch.zeros(n_streams * max_tokens * pb, **u8)
+        self.v_classes = 4 if v_bits == VMIXED else 1
+        self.v_scale = torch.zeros(n_streams * self.v_classes * max_tokens * pb, **u8)
         self.v_zero = torch.zeros_like(self.v_scale)
         s.k_scale, s.k_zero = self.k_scale.data_ptr(), self.k_zero.data_ptr()
         s.v_scale, s.v_zero = self.v_scale.data_ptr(), self.v_zero.data_ptr()
@@ -296,6 +306,12 @@ class PackedCache:
             s.k_slot_chan = self.slot_chan.data_ptr()
         else:
             s.k_slot_chan = None
+        self.v_slot_chan = None
+        s.v_slot_chan = None
+        if v_slot_chan is not None:
+            self.v_slot_chan = torch.as_tensor(np.ascontiguousarray(v_slot_chan, dtype=np.int16),
+                                               device=self.device)
+            s.v_slot_chan = self.v_slot_chan.data_ptr()
         self.s = s
         self._ws = {}
         if layout == "pool":
@@ -320,6 +336,7 @@ class PackedCache:
         c = PackedCache.__new__(PackedCache)
         c.device, c.B, c.H, c.max_tokens = self.device, self.B, self.H, self.max_tokens
         c.max_tiles, c.pdt, c.layout, c.pool, c._ws = self.max_tiles, self.pdt, self.layout, None, {}
+        c.v_classes = self.v_classes
         s = KvqCacheStruct()
         ctypes.pointer(s)[0] = self.s
         c.k_codes = self.k_codes.clone()
@@ -337,6 +354,8 @@ class PackedCache:
         s.v_scale, s.v_zero = c.v_scale.data_ptr(), c.v_zero.data_ptr()
         c.slot_chan = None if self.slot_chan is None else self.slot_chan.clone()
         s.k_slot_chan = None if c.slot_chan is None else c.slot_chan.data_ptr()
+        c.v_slot_chan = None if self.v_slot_chan is None else self.v_slot_chan.clone()
+        s.v_slot_chan = None if c.v_slot_chan is None else c.v_slot_chan.data_ptr()
         c.s = s
         return c
 
@@ -474,7 +493,7 @@ class PackedCache:
         return self.k_codes[off:off + n].cpu().numpy()
 
     def v_tile(self, b, h, g):
-        n = tile_bytes(self.v_bits)
+        n = value_tile_bytes(self.v_bits)
         off = self._tile_off(self.v_off, self.v_stride if self.layout == "contiguous" else 0,
                              b, h, g)
         return self.v_codes[off:off + n].cpu().numpy()
@@ -495,12 +514,17 @@ class PackedCache:
                 self.k_zero[sl].cpu().numpy().view(npdt).reshape(nt, 128))
 
     def v_params(self, b, h):
+        """(S raw, Z raw) of stream (b, h)'s stored tokens: [n_tokens] numpy,
+        or [4][n_tokens] (class-major) for mixed values."""
         pb = PARAM_BYTES[self.pdt]
-        base = ((b * self.H + h) * self.max_tokens) * pb
+        nc, T = self.v_classes, self.max_tokens
         npdt = {F32: np.float32, F16: np.uint16, BF16: np.uint16, E4M3: np.uint8}[self.pdt]
-        sl = slice(base, base + self.n_tokens * pb)
-        return (self.v_scale[sl].cpu().numpy().view(npdt),
-                self.v_zero[sl].cpu().numpy().view(npdt))
+        out = []
+        for arr in (self.v_scale, self.v_zero):
+            base = (b * self.H + h) * nc * T * pb
+            a = arr[base:base + nc * T * pb].cpu().numpy().view(npdt).reshape(nc, T)[:, :self.n_tokens]
+            out.append(a if nc > 1 else a[0])
+        return tuple(out)
 
 
 class Window:

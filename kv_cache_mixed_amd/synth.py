@@ -127,6 +127,49 @@ def mixed_layer(B: int, Hkv: int, Hq: int, T: int, seed: int):
     return dict(k=k, v=v, q_bf16=to_bf16_bits(q), slot_chan=slot_chan)
 
 
+VMIXED_CLASS_SCALES = (3.0, 2.0, 0.25, 1.0)   # value channel scale per class (4, 3, 1, 2 bits)
+
+
+def vmixed_class_map(Hkv: int, seed: int):
+    """Per kv head: a seeded permutation picks 16 value channels for 4 bits,
+    the next 16 for 3 bits, the next 16 for 1 bit and the other 80 for 2 bits
+    (ascending channel order inside every class).  Returns v_slot_chan
+    [Hkv,128] int16 in the mixed value layout's slot order and the
+    per-channel value scale [Hkv,128] float32 (VMIXED_CLASS_SCALES by class:
+    wider classes get the wider channels)."""
+    rng = np.random.default_rng(seed)
+    vsc = np.empty((Hkv, HEAD_DIM), dtype=np.int16)
+    scale = np.empty((Hkv, HEAD_DIM), dtype=np.float32)
+    for h in range(Hkv):
+        perm = rng.permutation(HEAD_DIM)
+        parts = (np.sort(perm[:16]), np.sort(perm[16:32]), np.sort(perm[32:48]), np.sort(perm[48:]))
+        vsc[h] = np.concatenate(parts)
+        for cls, ch in enumerate(parts):
+            scale[h, ch] = VMIXED_CLASS_SCALES[cls]
+    return vsc, scale
+
+
+def mixed_kv_layer(B: int, Hkv: int, Hq: int, T: int, seed: int):
+    """mixed_layer() plus value channel classes: values scaled per channel by
+    their class.  -> dict(k, v, q_bf16, slot_chan, v_slot_chan)"""
+    d = mixed_layer(B, Hkv, Hq, T, seed)
+    vsc, vscale = vmixed_class_map(Hkv, seed + 2)
+    d["v"] = (d["v"] * vscale[None, :, None, :]).astype(np.float32)
+    d["v_slot_chan"] = vsc
+    return d
+
+
+def mixed_kv_layer_device(B: int, Hkv: int, Hq: int, T: int, seed: int, device):
+    """mixed_layer_device() plus value channel classes (same class map as
+    mixed_kv_layer())."""
+    import torch
+    d = mixed_layer_device(B, Hkv, Hq, T, seed, device)
+    vsc, vscale = vmixed_class_map(Hkv, seed + 2)
+    d["v"] *= torch.as_tensor(vscale, device=device)[None, :, None, :]
+    d["v_slot_chan"] = vsc
+    return d
+
+
 def layer_sensitivities(n_layers: int = 64, widths=(2, 4, 8), seed: int = 0) -> np.ndarray:
     """Synthetic per-block sensitivities s[l][j] of block l at width widths[j]
     ([n_layers][len(widths)] float64), standing in for PM-KVQ's

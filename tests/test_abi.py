@@ -60,9 +60,10 @@ def _fake_struct(B, H, T, kb, vb, pdt=kvq.F16):
     s.k_codes = s.v_codes = FAKE
     s.k_tile_off = s.v_tile_off = None
     s.k_tile_stride = kvq.tile_bytes(kb)
-    s.v_tile_stride = kvq.tile_bytes(vb)
+    s.v_tile_stride = kvq.value_tile_bytes(vb)
     s.k_scale = s.k_zero = s.v_scale = s.v_zero = FAKE
     s.k_slot_chan = FAKE if kb == 0 else None
+    s.v_slot_chan = FAKE if vb == 0 else None
     return s
 
 
@@ -125,6 +126,42 @@ def test_validation_rejects_before_launch():
     assert L.kvq_decode_attn(P(s4), vp(FAKE), 8, 0.088, vp(FAKE), vp(FAKE), ws, None) == kvq.EUNSUPPORTED
     s5 = _fake_struct(2, 2, 1024, 4, 4)                      # empty cache
     assert L.kvq_decode_attn(P(s5), vp(FAKE), 8, 0.088, vp(FAKE), vp(FAKE), ws, None) == kvq.EINVAL
+
+
+def test_mixed_value_sizes_and_validation():
+    """Mixed-width values (v_bits = KVQ_VMIXED): a 5120-byte tile (16 x 4 +
+    16 x 4 + 16 x 2 + 80 x 2 bits per token: 3-bit codes in 4-bit fields,
+    1-bit codes in 2-bit fields), four scales and zero points per token, a
+    required slot map, no halving and no budgeted append."""
+    L = _lib()
+    P = ctypes.byref
+    vp = ctypes.c_void_p
+    st3 = (ctypes.c_int64 * 3)(0, 0, 128)
+    assert kvq.value_tile_bytes(0) == 5120 and kvq.value_tile_bytes(4) == 8192
+    assert kvq.value_tile_bytes(3) == 0 and kvq.tile_bytes(0) == 4352
+    s = _fake_struct(1, 8, 131072, 0, 0, kvq.E4M3)
+    # per 128-token group and stream: 4352 + 5120 code bytes, 2 x 128 key
+    # parameters and 2 x 4 x 128 value parameters of one byte
+    assert L.kvq_cache_bytes(P(s), 131072, 0, 0) == 8 * 1024 * (4352 + 5120 + 256 + 1024)
+    f = _fake_struct(1, 8, 131072, 0, 0, kvq.F16)
+    assert L.kvq_cache_bytes(P(f), 128, 0, 0) == 8 * (4352 + 5120 + 512 + 2048)
+    assert L.kvq_cache_bytes(P(f), 128, 4, 0) == 8 * (8192 + 5120 + 512 + 2048)
+    bad = _fake_struct(2, 2, 1024, 0, 0)
+    bad.v_slot_chan = None
+    assert L.kvq_quantize(P(bad), vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 0, 128, None) == kvq.EINVAL
+    bad = _fake_struct(2, 2, 1024, 0, 0)
+    bad.v_tile_stride = 4352                                 # below the mixed value tile
+    assert L.kvq_quantize(P(bad), vp(FAKE), vp(FAKE), kvq.F32, st3, st3, 0, 128, None) == kvq.EINVAL
+    sm = _fake_struct(1, 1, 1024, 0, 0)
+    assert L.kvq_shrink(P(sm), 1, None) == kvq.EUNSUPPORTED
+    # decode: mixed keys with mixed values need e4m3 or binary16 parameters,
+    # and uniform keys with mixed values are not built
+    for kb, pdt, want in ((0, kvq.BF16, kvq.EUNSUPPORTED), (0, kvq.F32, kvq.EUNSUPPORTED),
+                          (4, kvq.E4M3, kvq.EUNSUPPORTED)):
+        d = _fake_struct(2, 2, 1024, kb, 0, pdt)
+        d.n_tokens = 512
+        ws = L.kvq_decode_workspace_bytes(P(d), 8)
+        assert L.kvq_decode_attn(P(d), vp(FAKE), 8, 0.088, vp(FAKE), vp(FAKE), ws, None) == want
 
 
 def test_append_budget_rejected_before_work():
