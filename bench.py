@@ -33,14 +33,14 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, profiles/decode_kernel_*.md)
 # for the kernel source with the given digest, and the factors that map each
 # counter onto true bytes: a plain 512 MiB device copy in the same run reads
-# FETCH_SIZE = 262160.2 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
-# fetch counter is scaled by 524288/262160.2 and the write counter by 1.  The
+# FETCH_SIZE = 262159.2 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
+# fetch counter is scaled by 524288/262159.2 and the write counter by 1.  The
 # figure is reported only while the kernel source is unchanged.
 COUNTER_TRAFFIC = {
-    "source_sha256": "47a1d787eca7363cc1f04f8c7962b3de4e749aee4bbee936870a1d6729357e89",
-    "fetch_kib": 139901.8,
+    "source_sha256": "1031671c6fbe898ffb7c9d5d615d07832f9b10aaa9a29c9462d0a7dbb2b64eb7",
+    "fetch_kib": 139907.7,
     "write_kib": 3664.0,
-    "fetch_factor": 524288.0 / 262160.2,
+    "fetch_factor": 524288.0 / 262159.2,
     "write_factor": 1.0,
 }
 KERNEL_SOURCES = ("kv_cache_mixed_amd/csrc/decode_attn.hip", "kv_cache_mixed_amd/csrc/kvq_device.h")
@@ -66,9 +66,10 @@ def _parse():
 
 def decode_bytes(B, H, Hq, T, k_bits, v_bits, pb):
     """algorithmic bytes of one decode call: codes + S/Z of every stored token,
-    plus the bf16 query and the f32 output"""
-    per_tok = (128 * k_bits + 128 * v_bits) // 8 if k_bits else 34 + 128 * v_bits // 8
-    params = 2 * pb + 2 * pb          # key S,Z per token (128 per 128-token tile) + value S,Z
+    plus the bf16 query and the f32 output.  k_bits 0: mixed keys (34 B per
+    token); v_bits 0: mixed values (40 B per token, four S/Z pairs)"""
+    per_tok = (34 if k_bits == 0 else 16 * k_bits) + (40 if v_bits == 0 else 16 * v_bits)
+    params = 2 * pb + 2 * pb * (4 if v_bits == 0 else 1)   # key S,Z (128 per 128-token tile) + value S,Z
     return B * H * T * (per_tok + params) + B * Hq * 128 * 2 + B * Hq * 128 * 4
 
 
@@ -81,6 +82,7 @@ CASES = {
     "qwen32b_layer_2bit": (16, 8, 40, 32768, 2, 2, "F16"),
     "qwen32b_layer_8bit": (16, 8, 40, 32768, 8, 8, "F16"),
     "llama8b_mixed_128k": (1, 8, 32, 131072, 0, 2, "E4M3"),
+    "llama8b_mixed_kv_128k": (1, 8, 32, 131072, 0, 0, "E4M3"),
 }
 
 
@@ -94,7 +96,11 @@ def decode_case(name, steps, warmup):
     B, H, Hq, T, kb, vb, pname = CASES[name]
     pdt = getattr(kvq, pname)
     scale = 1.0 / math.sqrt(128)
-    if kb == 0:
+    if kb == 0 and vb == 0:
+        inp = synth.mixed_kv_layer_device(B, H, Hq, T, seed=4, device=dev)
+        mk = lambda: kvq.PackedCache(B, H, T, kvq.KMIXED, kvq.VMIXED, pdt, slot_chan=inp["slot_chan"],
+                                     v_slot_chan=inp["v_slot_chan"], device=dev)
+    elif kb == 0:
         inp = synth.mixed_layer_device(B, H, Hq, T, seed=4, device=dev)
         mk = lambda: kvq.PackedCache(B, H, T, kvq.KMIXED, vb, pdt, slot_chan=inp["slot_chan"], device=dev)
     else:
@@ -169,14 +175,19 @@ def time_block(torch, fn, n, warmup):
     return e0.elapsed_time(e1) / n
 
 
-def mixed_128k_rows(torch, kvq, synth, dev, scale):
+def mixed_128k_rows(torch, kvq, synth, dev, scale, vb=2):
     """Llama-3.1-8B-shaped 128K context: mixed 4/3/2/1-bit keys (34 B per token),
-    2-bit values, e4m3 S/Z.  Quantize of the whole context, then decode (nine
-    cache copies rotated, > 600 MB together)."""
+    2-bit values (vb = 2) or mixed 4/3/1/2-bit values (vb = 0: 40 B per token,
+    four S/Z pairs), e4m3 S/Z.  Quantize of the whole context, then decode
+    (cache copies rotated, > 600 MB together)."""
     B, H, Hq, T = 1, 8, 32, 131072
-    inp = synth.mixed_layer_device(B, H, Hq, T, seed=4, device=dev)
-    alg = decode_bytes(B, H, Hq, T, 0, 2, 1)
-    caches = [kvq.PackedCache(B, H, T, kvq.KMIXED, 2, kvq.E4M3, slot_chan=inp["slot_chan"], device=dev)
+    if vb == 0:
+        inp = synth.mixed_kv_layer_device(B, H, Hq, T, seed=4, device=dev)
+    else:
+        inp = synth.mixed_layer_device(B, H, Hq, T, seed=4, device=dev)
+    alg = decode_bytes(B, H, Hq, T, 0, vb, 1)
+    caches = [kvq.PackedCache(B, H, T, kvq.KMIXED, vb, kvq.E4M3, slot_chan=inp["slot_chan"],
+                              v_slot_chan=inp.get("v_slot_chan"), device=dev)
               for _ in range(max(2, math.ceil(600e6 / alg)))]
 
     def quant(i):
@@ -184,7 +195,7 @@ def mixed_128k_rows(torch, kvq, synth, dev, scale):
         c.s.n_tokens = 0
         c.quantize(inp["k"], inp["v"], 0)
     q_ms, _ = time_events(torch, quant, 8, 4)
-    q_bytes = 2 * B * H * T * 128 * 4 + decode_bytes(B, H, 0, T, 0, 2, 1)
+    q_bytes = 2 * B * H * T * 128 * 4 + decode_bytes(B, H, 0, T, 0, vb, 1)
     for i in range(len(caches)):        # every copy holds the quantized context
         quant(i)
     q = inp["q"]
@@ -195,8 +206,9 @@ def mixed_128k_rows(torch, kvq, synth, dev, scale):
     wss = [c.workspace(Hq) for c in caches]
     d_ms = time_block(torch, lambda i: caches[i % nc].decode_attn(q, scale, out=outs[i % nc], workspace=wss[i % nc]),
                       40, 4)
-    return {"quantize_mixed_128k": {"ms": round(q_ms, 4), "GB/s": round(q_bytes / q_ms / 1e6, 1), "bytes": q_bytes},
-            "decode_mixed_128k": {"ms": round(d_ms, 4), "GB/s": round(alg / d_ms / 1e6, 1), "bytes": alg,
+    tag = "mixed_kv_128k" if vb == 0 else "mixed_128k"
+    return {"quantize_" + tag: {"ms": round(q_ms, 4), "GB/s": round(q_bytes / q_ms / 1e6, 1), "bytes": q_bytes},
+            "decode_" + tag: {"ms": round(d_ms, 4), "GB/s": round(alg / d_ms / 1e6, 1), "bytes": alg,
                                   "pct_of_peak": round(100 * alg / d_ms / 1e6 / PEAK_HBM_GBS, 2),
                                   "tokens_per_s": round(B / (d_ms * 1e-3), 1),
                                   "note": "%d cache copies rotated (%d MB each), 40 calls back to back"
@@ -712,6 +724,7 @@ def main():
                     "decode over the packed layer + the 1..22 held tokens"}
         del wins, nk, nv
         rows.update(mixed_128k_rows(torch, kvq, synth, dev, scale))
+        rows.update(mixed_128k_rows(torch, kvq, synth, dev, scale, vb=0))
         rows.update(pn_mix_rows(torch, kvq, synth, dev, scale))
         rows.update(semkv_split_rows(torch, kvq, synth, dev, scale))
         rows.update(progressive_rows(torch, kvq, synth, dev, scale))

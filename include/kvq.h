@@ -290,9 +290,10 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads);
  * (after any other status, zero them again).  The rest holds per-chunk
  * partials and needs no initial contents.  When the tokens are split over
  * several chunks, the partials are combined into out by a second kernel on
- * the same stream or, for streams cut into many chunks, inside the same
- * kernel by the workgroup that finishes the last chunk of a group of streams.
- * Concurrent calls must not share a workspace. */
+ * the same stream (a build of the library may instead combine inside the
+ * decode kernel, in the workgroup that finishes the last chunk of a group of
+ * streams; the counters serve that).  Concurrent calls must not share a
+ * workspace. */
 kvq_status kvq_decode_attn(const kvq_cache *cache, const void *q, int32_t n_q_heads,
                            float softmax_scale, float *out, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);

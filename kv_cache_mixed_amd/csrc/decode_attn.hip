@@ -51,6 +51,11 @@
 #define KVQ_DECODE_WAVES_PER_SIMD 0
 #endif
 // most sub-tiles a 128-token tile is cut into (4, 2 or 1)
+// value words of the next sub-tile are loaded while the current one is
+// computed (1), or at the start of their own sub-tile (0)
+#ifndef KVQ_DECODE_VPF
+#define KVQ_DECODE_VPF 0
+#endif
 #ifndef KVQ_DECODE_NSUB_MAX
 #define KVQ_DECODE_NSUB_MAX 4
 #endif
@@ -64,12 +69,13 @@
 #endif
 // streams split into at least this many chunks are combined inside the decode
 // kernel by the workgroup that finishes the last chunk of a stream group;
-// fewer chunks are combined by a second kernel.  Measured: a second kernel is
-// cheaper at the 16-32 chunks of batched layers, where the combine work of the
-// last workgroups at the tail costs more than the launch; the in-kernel
-// combine wins for the 64 chunks of single-sequence long contexts.
+// fewer chunks are combined by a second kernel.  Measured on MI355X, the
+// second kernel (its chunk loads issued 16 at a time) is the faster one at
+// every chunk count: 14% faster on one 128K-token sequence of 8 kv heads (64
+// chunks), even at the 16 chunks of batched layers.  So by default no launch
+// combines in-kernel; the in-kernel combine stays a build option.
 #ifndef KVQ_DECODE_FUSED_MIN_CHUNKS
-#define KVQ_DECODE_FUSED_MIN_CHUNKS 48
+#define KVQ_DECODE_FUSED_MIN_CHUNKS (1 << 30)
 #endif
 // cache-policy bits of the code loads (sc0 = 1, nt = 2, sc1 = 16) and of the
 // parameter loads.  Codes are read once: non-temporal loads measured 6-11%
@@ -1031,9 +1037,18 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
     for (int s = 0; s < NS; s++) load_vw(vw + s * NVW, v_rsrc(s, t_base + k), sub);
   };
-  auto compute = [&](Buf& bf, int ti, int sub, int ti2, int sub2) {
+  // (KVQ_DECODE_VPF) the value words of the sub-tile after the current one,
+  // in flight while the current one is computed
+  uint32_t vnext[KVQ_DECODE_VPF ? NS * NVW : 1];
+  auto compute = [&](Buf& bf, int ti, int sub, int ti2, int sub2, int ti1, int sub1) {
     uint32_t vjit[NS * NVW];
-    issue_v(vjit, ti, sub);
+    if constexpr (KVQ_DECODE_VPF) {
+#pragma unroll
+      for (int i = 0; i < NS * NVW; i++) vjit[i] = vnext[i];
+      if (ti1 >= 0) issue_v(vnext, ti1, sub1);
+    } else {
+      issue_v(vjit, ti, sub);
+    }
     const uint32_t* vwp = vjit;
     if (sub == 0) fold_query(bf);
     // ---- logits: k-step-major over all (stream, block) accumulators
@@ -1312,6 +1327,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   };
   // the second buffer: loads run two sub-tiles ahead of the computation
   if (q0 < t_count && qk(1 / NSUB) >= 0) load(b1, qk(1 / NSUB), 1 % NSUB);
+  if constexpr (KVQ_DECODE_VPF) {
+    if (q0 < t_count) issue_v(vnext, q0, 0);
+  }
 #pragma unroll 1
   while (q0 < t_count) {
     if constexpr (KVQ_DECODE_PRIO != 0) {
@@ -1330,7 +1348,8 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       if constexpr (NSUB == 1) {
         if (u == 1 && q1 >= t_count) break;
       }
-      compute((u % 2 == 0) ? b0 : b1, qk(u / NSUB), u % NSUB, qk((u + 2) / NSUB), (u + 2) % NSUB);
+      compute((u % 2 == 0) ? b0 : b1, qk(u / NSUB), u % NSUB, qk((u + 2) / NSUB), (u + 2) % NSUB,
+              qk((u + 1) / NSUB), (u + 1) % NSUB);
     }
     if constexpr (TPI == 1) {
       q0 = q1; q1 = q2; q2 = q3;
@@ -1627,11 +1646,19 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
     n0 = fmaf(w, v[k].x, n0);
     n1 = fmaf(w, v[k].y, n1);
   }
-  for (int k = 16; k < nck; k++) {
-    const float w = u2f(__builtin_amdgcn_readlane(f2u(k < 64 ? w0 : w1), k & 63));
-    const float2 x = *(const float2*)(po + step * k);
-    n0 = fmaf(w, x.x, n0);
-    n1 = fmaf(w, x.y, n1);
+  // the other chunks in batches of 16 independent loads (a batch past the
+  // last chunk re-reads that chunk, at weight 0)
+  for (int k0 = 16; k0 < nck; k0 += 16) {
+    float2 x[16];
+#pragma unroll
+    for (int k = 0; k < 16; k++) x[k] = *(const float2*)(po + step * min(k0 + k, nck - 1));
+#pragma unroll
+    for (int k = 0; k < 16; k++) {
+      const int kk = k0 + k;
+      const float w = u2f(__builtin_amdgcn_readlane(f2u(kk < 64 ? w0 : w1), kk & 63));   // 0 beyond nck
+      n0 = fmaf(w, x[k].x, n0);
+      n1 = fmaf(w, x[k].y, n1);
+    }
   }
   const float inv = 1.0f / den;
   const int bo = bh / H, ho = bh - (bh / H) * H;
