@@ -1112,10 +1112,11 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     constexpr bool MIX = (PDT == KVQ_F16);
     uint32_t rvs[NCV * PWV], rvz[NCV * PWV];
     float vs[(MIX || VMIX) ? 1 : TPS], vz[(MIX || VMIX) ? 1 : TPS];
-    // mixed values with binary32-converted scales: class k, token i at sv[k * TPS + i]
-    float sv[(VMIX && !MIX) ? NCV * TPS : 1];
     uint32_t smx;
     if constexpr (VMIX) {
+      // raw words only; the largest scale straight from the patterns (scales
+      // are >= +0, so binary16 and e4m3 patterns order like their values)
+      static_assert(!VMIX || PDT == KVQ_F16 || PDT == KVQ_E4M3, "mixed values: binary16 or e4m3 parameters");
 #pragma unroll
       for (int w = 0; w < NCV * PWV; w++) { rvs[w] = bf.vs[w]; rvz[w] = bf.vz[w]; }
       if constexpr (MIX) {
@@ -1124,14 +1125,17 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
         for (int w = 1; w < NCV * PWV; w++) m2 = pk_max_u16(m2, rvs[w]);
         smx = f2u((float)__builtin_bit_cast(_Float16, (uint16_t)max(m2 & 0xffffu, m2 >> 16)));
       } else {
-        smx = 0;
+        // bytes 1 and 3 of each word lead their 16-bit halves, so the halves'
+        // maxima of the words carry the largest byte 1 / byte 3 in their high
+        // bytes; the words shifted left by 8 do the same for bytes 0 and 2
+        uint32_t hi = rvs[0], lo = rvs[0] << 8;
 #pragma unroll
-        for (int k = 0; k < NCV; k++)
-#pragma unroll
-          for (int i = 0; i < TPS; i++) {
-            sv[k * TPS + i] = pget<PDT>(rvs + k * PWV, i);
-            smx = max(smx, f2u(sv[k * TPS + i]));   // scales are >= +0
-          }
+        for (int w = 1; w < NCV * PWV; w++) {
+          hi = pk_max_u16(hi, rvs[w]);
+          lo = pk_max_u16(lo, rvs[w] << 8);
+        }
+        const uint32_t m2 = pk_max_u16(hi, lo);
+        smx = f2u(__builtin_amdgcn_cvt_f32_fp8((int)max((m2 >> 8) & 0xffu, m2 >> 24), 0));
       }
     } else if constexpr (MIX) {
 #pragma unroll
@@ -1181,17 +1185,16 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       // binary16 P~ made up at the class's code midpoint as for uniform
       // widths; the residual sums read P~ * 2^-W exactly through fdot2.
       const float c0 = bk0 - m_run + (float)min(VH - e_run, PSMAX);
-      float e[TPS], ew4[TPS], ew2[TPS];
+      float e[TPS];
       float lsum = 0.0f;
 #pragma unroll
       for (int i = 0; i < TPS; i++) {
         e[i] = __builtin_amdgcn_exp2f(fmaf(ak, lv[i], c0));
         lsum += e[i];
-        ew4[i] = e[i] * exp2i(tok_w<4, FVS>(i));
-        ew2[i] = e[i] * exp2i(tok_w<2, FVS>(i));
       }
       l_run += lsum;
-      uint32_t bv[4][FVS];
+      // one class at a time: its operand, its zero-point sum, then the value
+      // products of its slot blocks (block k for k < 3, blocks 3..7 for k = 3)
 #pragma unroll
       for (int k = 0; k < 4; k++) {
         const float vmid = 0.5f * (float)((1u << vmixed_class_bits(k)) - 1u);
@@ -1201,38 +1204,40 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
         float p[TPS];
 #pragma unroll
         for (int i = 0; i < TPS; i++) {
-          const float ew = k < 2 ? ew4[i] : ew2[i];
+          const float ew = e[i] * exp2i(k < 2 ? tok_w<4, FVS>(i) : tok_w<2, FVS>(i));
           if constexpr (MIX) {
             zc = fmaf(e[i], __builtin_fmaf(vmid, half_at(ks, i), half_at(kz, i)), zc);
             p[i] = fmaf(ew, half_at(ks, i), 0.0f);
           } else {
-            zc = fmaf(e[i], fmaf(vmid, sv[k * TPS + i], pget<PDT>(kz, i)), zc);
-            p[i] = ew * sv[k * TPS + i];
+            const float sk = pget<PDT>(ks, i);
+            zc = fmaf(e[i], fmaf(vmid, sk, pget<PDT>(kz, i)), zc);
+            p[i] = ew * sk;
           }
         }
+        uint32_t bv[FVS];
 #pragma unroll
         for (int ff = 0; ff < FVS; ff++) {
           const Fld F = k < 2 ? ufield<4>(ff) : ufield<2>(ff);
           const f16x2 h = __builtin_convertvector((f32x2){p[F.lo], p[F.hi]}, f16x2);
-          bv[k][ff] = __builtin_bit_cast(uint32_t, h);
+          bv[ff] = __builtin_bit_cast(uint32_t, h);
           const _Float16 iw = (_Float16)exp2i(F.pos - F.wexp);   // 2^-W: 1 .. 256, exact
           zr = __builtin_amdgcn_fdot2(h, (f16x2){iw, iw}, zr, false);
         }
         zm_run[k] += fmaf(-vmid, zr, zc);
-      }
-      // PV: block cb (slots 16 cb .. 16 cb + 15) against its class's operand
 #pragma unroll
-      for (int kk = 0; kk < KSV; kk++) {
-        uint32_t av[8][4];
+        for (int cb = 0; cb < 8; cb++) {
+          if (vmixed_block_class(cb) != k) continue;
 #pragma unroll
-        for (int cb = 0; cb < 8; cb++)
+          for (int kk = 0; kk < KSV; kk++) {
+            uint32_t av[4];
 #pragma unroll
-          for (int r = 0; r < 4; r++) {
-            const Fld F = cb < 2 ? ufield<4>(4 * kk + r) : ufield<2>(4 * kk + r);
-            av[cb][r] = field_subnormal(cb < 2 ? vwp[2 * cb + F.w] : vwp[2 + cb], F);
+            for (int r = 0; r < 4; r++) {
+              const Fld F = cb < 2 ? ufield<4>(4 * kk + r) : ufield<2>(4 * kk + r);
+              av[r] = field_subnormal(cb < 2 ? vwp[2 * cb + F.w] : vwp[2 + cb], F);
+            }
+            acc_o[cb] = mfma(av, bv + 4 * kk, acc_o[cb]);
           }
-#pragma unroll
-        for (int cb = 0; cb < 8; cb++) acc_o[cb] = mfma(av[cb], &bv[vmixed_block_class(cb)][4 * kk], acc_o[cb]);
+        }
       }
     } else {
       // e''(i) = e(i) * 2^ps * 2^W(i) straight from the exponent; the running
@@ -1610,6 +1615,7 @@ DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_til
 //   o = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k.
 // Lane k holds the (m, l) of chunks k and k + 64; each lane owns two channels
 // of o and walks the chunks with the weight broadcast from its owner lane.
+template <int KP>
 __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part_ml,
                                                              const float* __restrict__ part_o,
                                                              float* __restrict__ out, int BH, int H,
@@ -1625,13 +1631,13 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
     m1 = part_ml[2 * (r0 + (int64_t)(lane + 64) * G)];
     l1 = part_ml[2 * (r0 + (int64_t)(lane + 64) * G) + 1];
   }
-  // the first 16 chunk outputs are loaded before the weights are known, so a
-  // typical combine costs one memory round trip
+  // the first KP (>= nck up to 64) chunk outputs are loaded before the
+  // weights are known, so the combine costs one memory round trip
   const float* po = part_o + r0 * 128 + 2 * lane;
   const int64_t step = (int64_t)G * 128;
-  float2 v[16];
+  float2 v[KP];
 #pragma unroll
-  for (int k = 0; k < 16; k++) v[k] = (k < nck) ? *(const float2*)(po + step * k) : make_float2(0.f, 0.f);
+  for (int k = 0; k < KP; k++) v[k] = (k < nck) ? *(const float2*)(po + step * k) : make_float2(0.f, 0.f);
   float M = fmaxf(m0, m1);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, 64));
@@ -1641,14 +1647,14 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
   for (int o = 32; o >= 1; o >>= 1) den += __shfl_xor(den, o, 64);
   float n0 = 0.0f, n1 = 0.0f;
 #pragma unroll
-  for (int k = 0; k < 16; k++) {
+  for (int k = 0; k < KP; k++) {
     const float w = u2f(__builtin_amdgcn_readlane(f2u(w0), k));   // 0 beyond nck
     n0 = fmaf(w, v[k].x, n0);
     n1 = fmaf(w, v[k].y, n1);
   }
-  // the other chunks in batches of 16 independent loads (a batch past the
-  // last chunk re-reads that chunk, at weight 0)
-  for (int k0 = 16; k0 < nck; k0 += 16) {
+  // slots past 64 (residual partials) in batches of 16 independent loads (a
+  // batch past the last slot re-reads that slot, at weight 0)
+  for (int k0 = KP; k0 < nck; k0 += 16) {
     float2 x[16];
 #pragma unroll
     for (int k = 0; k < 16; k++) x[k] = *(const float2*)(po + step * min(k0 + k, nck - 1));
@@ -1663,6 +1669,20 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
   const float inv = 1.0f / den;
   const int bo = bh / H, ho = bh - (bh / H) * H;
   *(float2*)(out + ((int64_t)bo * H * G + (int64_t)ho * G + hh) * 128 + 2 * lane) = make_float2(n0 * inv, n1 * inv);
+}
+
+// the combine instance that preloads every slot up to 64
+static hipError_t launch_combine(const float* part_ml, const float* part_o, float* out, int BH, int H, int G,
+                                 int n_slots, hipStream_t st) {
+  const int rows = BH * G;
+  const dim3 grid((rows + 3) / 4), block(256);
+  if (n_slots <= 16)
+    hipLaunchKernelGGL(decode_combine_kernel<16>, grid, block, 0, st, part_ml, part_o, out, BH, H, G, n_slots);
+  else if (n_slots <= 32)
+    hipLaunchKernelGGL(decode_combine_kernel<32>, grid, block, 0, st, part_ml, part_o, out, BH, H, G, n_slots);
+  else
+    hipLaunchKernelGGL(decode_combine_kernel<64>, grid, block, 0, st, part_ml, part_o, out, BH, H, G, n_slots);
+  return hipGetLastError();
 }
 
 static size_t ml_bytes(int BH, int n_chunks, int G) {
@@ -1809,12 +1829,8 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
     e = launch_decode_any(a, p, st);
     if (e != hipSuccess) return e;
   }
-  if (n_slots > 1 && (!has_packed || p.n_chunks < KVQ_DECODE_FUSED_MIN_CHUNKS)) {
-    const int rows = BH * G;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, (const float*)part_ml,
-                       (const float*)part_o, out, BH, g.H, G, n_slots);
-    e = hipGetLastError();
-  }
+  if (n_slots > 1 && (!has_packed || p.n_chunks < KVQ_DECODE_FUSED_MIN_CHUNKS))
+    e = launch_combine(part_ml, part_o, out, BH, g.H, G, n_slots, st);
   return e;
 }
 
@@ -1862,12 +1878,7 @@ hipError_t launch_decode_split(const Geo& ga, const Geo& gb, const void* q, int 
     if (e != hipSuccess) return e;
     slot0 += ps[i].n_chunks;
   }
-  if (n_slots > 1) {
-    const int rows = BH * G;
-    hipLaunchKernelGGL(decode_combine_kernel, dim3((rows + 3) / 4), dim3(256), 0, st, (const float*)part_ml,
-                       (const float*)part_o, out, BH, ga.H, G, n_slots);
-    return hipGetLastError();
-  }
+  if (n_slots > 1) return launch_combine(part_ml, part_o, out, BH, ga.H, G, n_slots, st);
   return hipSuccess;
 }
 
