@@ -274,9 +274,6 @@ kvq_status kvq_shrink_shift(kvq_cache *cache, int32_t to_bits, kvq_shift method,
 
 /* Workspace bytes kvq_decode_attn needs for this cache geometry (sized for
  * max_tokens, so it stays valid as the cache grows).  0 on invalid input. */
-/* Leading workspace bytes that hold the decode completion counters, for a
- * cache of n_streams = batch * n_kv_heads streams. */
-#define KVQ_DECODE_COUNTER_BYTES(n_streams) ((((size_t)(n_streams) * 4u) + 255u) / 256u * 256u)
 size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads);
 
 /* Decode attention of one query token per sequence over the n_tokens stored
@@ -284,16 +281,10 @@ size_t kvq_decode_workspace_bytes(const kvq_cache *cache, int32_t n_q_heads);
  * [B][n_q_heads][128]; out: device float32 [B][n_q_heads][128]; n_q_heads a
  * multiple of n_kv_heads with 1 <= n_q_heads / n_kv_heads <= 16; n_tokens >= 128.
  * workspace: device buffer of at least kvq_decode_workspace_bytes() bytes,
- * 256-byte aligned.  Its first KVQ_DECODE_COUNTER_BYTES(batch * n_kv_heads)
- * bytes are completion counters that must be zero before the first call (a
- * zero-filled allocation); every call that returns KVQ_OK leaves them zero
- * (after any other status, zero them again).  The rest holds per-chunk
- * partials and needs no initial contents.  When the tokens are split over
- * several chunks, the partials are combined into out by a second kernel on
- * the same stream (a build of the library may instead combine inside the
- * decode kernel, in the workgroup that finishes the last chunk of a group of
- * streams; the counters serve that).  Concurrent calls must not share a
- * workspace. */
+ * 256-byte aligned, no initial contents needed: it holds the per-chunk
+ * partials (max, sum, weighted values per head).  When the tokens are split
+ * over several chunks, the partials are combined into out by a second kernel
+ * on the same stream.  Concurrent calls must not share a workspace. */
 kvq_status kvq_decode_attn(const kvq_cache *cache, const void *q, int32_t n_q_heads,
                            float softmax_scale, float *out, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);
@@ -319,17 +310,16 @@ kvq_status kvq_decode_attn_split(const kvq_cache *a, const kvq_cache *b, const v
 /* Allocation-free decode attention, for callers that cannot allocate device
  * memory (code under HIP graph capture, tight serving loops, harnesses that
  * forbid allocation).  Same computation, arguments and errors as
- * kvq_decode_attn, without a caller workspace: the counters and chunk
- * partials live in a library-owned device array of KVQ_DECODE_SCRATCH_BYTES
+ * kvq_decode_attn, without a caller workspace: the chunk partials live in
+ * a library-owned device array of KVQ_DECODE_SCRATCH_BYTES
  * per GPU (static storage, held until the process ends; never allocated or
  * freed by the call).  The array of the current device is used, so the
  * stream must belong to the current device.  A call whose launch plan needs
  * more scratch than the array holds returns KVQ_EWORKSPACE before any device
  * work (about 520 * (n_chunks + 16) * batch * n_q_heads bytes; the Qwen2.5-7B- and
  * 32B-shaped layers at 32K tokens need under 8 MiB).  The array keeps the
- * last call's contents; its completion counters are zeroed by a small kernel
- * on the stream at the first call on a device and after a failed launch.
- * All calls on one GPU share the array: calls that may overlap in time (on
+ * last call's contents, which no call reads before writing them.  All calls
+ * on one GPU share the array: calls that may overlap in time (on
  * different streams without ordering between them) race -- order them. */
 #define KVQ_DECODE_SCRATCH_BYTES (32u << 20)
 kvq_status kvq_decode_attn_noalloc(const kvq_cache *cache, const void *q, int32_t n_q_heads,

@@ -51,11 +51,6 @@
 #define KVQ_DECODE_WAVES_PER_SIMD 0
 #endif
 // most sub-tiles a 128-token tile is cut into (4, 2 or 1)
-// value words of the next sub-tile are loaded while the current one is
-// computed (1), or at the start of their own sub-tile (0)
-#ifndef KVQ_DECODE_VPF
-#define KVQ_DECODE_VPF 0
-#endif
 #ifndef KVQ_DECODE_NSUB_MAX
 #define KVQ_DECODE_NSUB_MAX 4
 #endif
@@ -66,16 +61,6 @@
 // wave priority from the tiles a wave has left (1) or the default (0)
 #ifndef KVQ_DECODE_PRIO
 #define KVQ_DECODE_PRIO 1
-#endif
-// streams split into at least this many chunks are combined inside the decode
-// kernel by the workgroup that finishes the last chunk of a stream group;
-// fewer chunks are combined by a second kernel.  Measured on MI355X, the
-// second kernel (its chunk loads issued 16 at a time) is the faster one at
-// every chunk count: 14% faster on one 128K-token sequence of 8 kv heads (64
-// chunks), even at the 16 chunks of batched layers.  So by default no launch
-// combines in-kernel; the in-kernel combine stays a build option.
-#ifndef KVQ_DECODE_FUSED_MIN_CHUNKS
-#define KVQ_DECODE_FUSED_MIN_CHUNKS (1 << 30)
 #endif
 // cache-policy bits of the code loads (sc0 = 1, nt = 2, sc1 = 16) and of the
 // parameter loads.  Codes are read once: non-temporal loads measured 6-11%
@@ -267,9 +252,6 @@ struct DecodeArgs {
   int G, n_chunks, tpc, n_groups;
   int n_slots;        // partial slots per stream: n_chunks + residual slots (+ another cache's)
   int slot0;          // slot of this launch's chunk 0 (0, or after another cache's chunks)
-  unsigned* counters; // [n_groups] finished chunks per stream group: zero on
-                      // entry, left zero (chunk combine inside the kernel)
-  int fused;          // chunks combined inside the kernel (1) or by a second kernel (0)
   float sl2;          // softmax_scale * log2(e)
   // residual segment run by extra workgroups of this launch (grid rows past
   // n_groups), n_res blocks of 32 tokens per stream, partial slots
@@ -341,11 +323,6 @@ __host__ __device__ constexpr bool class_used(int k) {
   for (int i = 0; i < TPS; i++)
     if (w_class(tok_w<VB, FVS>(i)) == k) return true;
   return false;
-}
-
-// device-scope store (written through the XCD's L2)
-__device__ __forceinline__ void st_dev(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // buffer resource over [base, base + bytes): raw buffer loads take a 32-bit
@@ -1037,18 +1014,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
     for (int s = 0; s < NS; s++) load_vw(vw + s * NVW, v_rsrc(s, t_base + k), sub);
   };
-  // (KVQ_DECODE_VPF) the value words of the sub-tile after the current one,
-  // in flight while the current one is computed
-  uint32_t vnext[KVQ_DECODE_VPF ? NS * NVW : 1];
-  auto compute = [&](Buf& bf, int ti, int sub, int ti2, int sub2, int ti1, int sub1) {
+  auto compute = [&](Buf& bf, int ti, int sub, int ti2, int sub2) {
     uint32_t vjit[NS * NVW];
-    if constexpr (KVQ_DECODE_VPF) {
-#pragma unroll
-      for (int i = 0; i < NS * NVW; i++) vjit[i] = vnext[i];
-      if (ti1 >= 0) issue_v(vnext, ti1, sub1);
-    } else {
-      issue_v(vjit, ti, sub);
-    }
+    issue_v(vjit, ti, sub);
     const uint32_t* vwp = vjit;
     if (sub == 0) fold_query(bf);
     // ---- logits: k-step-major over all (stream, block) accumulators
@@ -1332,9 +1300,6 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   };
   // the second buffer: loads run two sub-tiles ahead of the computation
   if (q0 < t_count && qk(1 / NSUB) >= 0) load(b1, qk(1 / NSUB), 1 % NSUB);
-  if constexpr (KVQ_DECODE_VPF) {
-    if (q0 < t_count) issue_v(vnext, q0, 0);
-  }
 #pragma unroll 1
   while (q0 < t_count) {
     if constexpr (KVQ_DECODE_PRIO != 0) {
@@ -1353,8 +1318,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       if constexpr (NSUB == 1) {
         if (u == 1 && q1 >= t_count) break;
       }
-      compute((u % 2 == 0) ? b0 : b1, qk(u / NSUB), u % NSUB, qk((u + 2) / NSUB), (u + 2) % NSUB,
-              qk((u + 1) / NSUB), (u + 1) % NSUB);
+      compute((u % 2 == 0) ? b0 : b1, qk(u / NSUB), u % NSUB, qk((u + 2) / NSUB), (u + 2) % NSUB);
     }
     if constexpr (TPI == 1) {
       q0 = q1; q1 = q2; q2 = q3;
@@ -1410,7 +1374,6 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   __shared__ float sh_cw[16][4];
   __shared__ float sh_cd[16][2];
   __shared__ int sh_row[16];
-  __shared__ int sh_orow[16];
   if (threadIdx.x < ncol) {
     const int col = threadIdx.x;
     float M = -INFINITY;
@@ -1429,7 +1392,6 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     const int s = col / G, hh = col - s * G;
     const int bh = grp * NS + s;
     sh_row[col] = bh >= BH ? -1 : (single ? bh * G + hh : (bh * a.n_slots + a.slot0 + chunk) * G + hh);
-    sh_orow[col] = bh * G + hh;
   }
   __syncthreads();
   // four consecutive channels per thread
@@ -1443,109 +1405,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     if (single) {
       *(f32x4*)(a.out + (int64_t)row * 128 + c4) = num / sh_cd[col][1];
     } else {
-      if (a.fused) {
-        // device-scope stores: they pass the XCD's own L2, so the workgroup
-        // that combines (on any XCD) reads them without a cache write-back
-        if (c4 == 0) {
-          st_dev(a.part_ml + 2 * (int64_t)row, sh_cd[col][0]);
-          st_dev(a.part_ml + 2 * (int64_t)row + 1, sh_cd[col][1]);
-        }
-#pragma unroll
-        for (int k = 0; k < 4; k++) st_dev(a.part_o + (int64_t)row * 128 + c4 + k, num[k]);
-      } else {
-        if (c4 == 0) { a.part_ml[2 * (int64_t)row] = sh_cd[col][0]; a.part_ml[2 * (int64_t)row + 1] = sh_cd[col][1]; }
-        *(f32x4*)(a.part_o + (int64_t)row * 128 + c4) = num;
-      }
+      if (c4 == 0) { a.part_ml[2 * (int64_t)row] = sh_cd[col][0]; a.part_ml[2 * (int64_t)row + 1] = sh_cd[col][1]; }
+      *(f32x4*)(a.part_o + (int64_t)row * 128 + c4) = num;
     }
-  }
-  if (a.fused) {
-    if (single) return;
-    // ---- chunk combine by the workgroup that completes the stream group:
-    // once this workgroup's partial stores are complete it counts itself in
-    // the group's counter; the one that brings the count to n_chunks reads
-    // every partial slot of the group's streams back (the chunks and any
-    // residual slots), writes o = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k
-    // and resets the counter for the next call.
-    __builtin_amdgcn_s_waitcnt(0);
-    __syncthreads();
-    __shared__ int s_last;
-    if (threadIdx.x == 0)
-      s_last = __hip_atomic_fetch_add(a.counters + grp, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               (unsigned)(a.n_chunks - 1);
-    __syncthreads();
-    if (!s_last) return;
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-    const int ns = a.n_slots;
-    constexpr int KR = 16;   // slots whose outputs are loaded before the weights are known
-    // items: four consecutive channels of one column, two per thread
-    f32x4 ov[2][KR];
-    int icol[2], ic4[2], irow[2];
-#pragma unroll
-    for (int it = 0; it < 2; it++) {
-      const int idx = threadIdx.x + 256 * it;
-      icol[it] = min(idx >> 5, 15);
-      ic4[it] = (idx & 31) * 4;
-      irow[it] = idx < ncol * 32 ? sh_row[icol[it]] : -1;
-      // partial row of slot k = irow + (k - slot0 - chunk) * G
-      const int64_t r0 = (int64_t)irow[it] - (int64_t)(a.slot0 + chunk) * G;
-#pragma unroll
-      for (int k = 0; k < KR; k++) {
-        ov[it][k] = (f32x4){0.f, 0.f, 0.f, 0.f};
-        if (irow[it] >= 0 && k < ns) ov[it][k] = *(const f32x4*)(a.part_o + (r0 + (int64_t)k * G) * 128 + ic4[it]);
-      }
-    }
-    // (m, l) of every (column, slot), then the weights, in the free LDS
-    float* sml = (float*)&lds[0][0];                 // [16][ns][2]
-    float* sden = sml + 16 * 2 * KVQ_MAX_SLOTS;      // [16]
-    for (int i = threadIdx.x; i < ncol * ns; i += 256) {
-      const int col = i / ns, k = i - (i / ns) * ns;
-      float m = -INFINITY, l = 0.0f;
-      if (sh_row[col] >= 0) {
-        const int64_t r = (int64_t)sh_row[col] + (int64_t)(k - a.slot0 - chunk) * G;
-        m = a.part_ml[2 * r];
-        l = a.part_ml[2 * r + 1];
-      }
-      sml[2 * (col * ns + k)] = m;
-      sml[2 * (col * ns + k) + 1] = l;
-    }
-    __syncthreads();
-    if (threadIdx.x < ncol) {
-      const int col = threadIdx.x;
-      float M = -INFINITY;
-      for (int k = 0; k < ns; k++) M = fmaxf(M, sml[2 * (col * ns + k)]);
-      float den = 0.0f;
-      for (int k = 0; k < ns; k++) {
-        const float mk = sml[2 * (col * ns + k)];
-        const float w = (mk == -INFINITY) ? 0.0f : exp2f(mk - M);
-        den += w * sml[2 * (col * ns + k) + 1];
-        sml[2 * (col * ns + k)] = w;
-      }
-      sden[col] = den;
-    }
-    __syncthreads();
-#pragma unroll
-    for (int it = 0; it < 2; it++) {
-      if (irow[it] < 0) continue;
-      const int col = icol[it];
-      const float* wk = sml + 2 * col * ns;
-      f32x4 num = (f32x4){0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int k = 0; k < KR; k++)
-        if (k < ns) num += wk[2 * k] * ov[it][k];
-      const int64_t r0 = (int64_t)irow[it] - (int64_t)(a.slot0 + chunk) * G;
-      // the other slots in batches of KR independent loads (one round trip
-      // per batch; a batch past the last slot re-reads that slot at weight 0)
-      for (int k0 = KR; k0 < ns; k0 += KR) {
-        f32x4 x[KR];
-#pragma unroll
-        for (int k = 0; k < KR; k++)
-          x[k] = *(const f32x4*)(a.part_o + (r0 + (int64_t)min(k0 + k, ns - 1) * G) * 128 + ic4[it]);
-#pragma unroll
-        for (int k = 0; k < KR; k++) num += (k0 + k < ns ? wk[2 * (k0 + k)] : 0.0f) * x[k];
-      }
-      *(f32x4*)(a.out + (int64_t)sh_orow[col] * 128 + ic4[it]) = num / sden[col];
-    }
-    if (threadIdx.x == 0) __hip_atomic_store(a.counters + grp, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1652,7 +1514,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
     n0 = fmaf(w, v[k].x, n0);
     n1 = fmaf(w, v[k].y, n1);
   }
-  // slots past 64 (residual partials) in batches of 16 independent loads (a
+  // slots past 64 in batches of 16 independent loads (a
   // batch past the last slot re-reads that slot, at weight 0)
   for (int k0 = KP; k0 < nck; k0 += 16) {
     float2 x[16];
@@ -1688,14 +1550,10 @@ static hipError_t launch_combine(const float* part_ml, const float* part_o, floa
 static size_t ml_bytes(int BH, int n_chunks, int G) {
   return ((size_t)BH * n_chunks * G * 2 * 4 + 255) / 256 * 256;
 }
-// per-stream-group counters of the in-kernel combine, at the start of the
-// workspace (at most one group per stream)
-static size_t cnt_bytes(int BH) { return ((size_t)BH * 4 + 255) / 256 * 256; }
-
 // partial slots: every chunk plus the most a residual segment can add
 size_t decode_workspace_needed(int BH, int G, const DecodePlan& p) {
   const int slots = p.n_chunks + KVQ_MAX_RES_SLOTS;
-  return cnt_bytes(BH) + ml_bytes(BH, slots, G) + (size_t)BH * slots * G * 128 * 4;
+  return ml_bytes(BH, slots, G) + (size_t)BH * slots * G * 128 * 4;
 }
 
 size_t decode_workspace_bytes(int B, int H, int G, int max_tiles) {
@@ -1714,7 +1572,7 @@ bool decode_supported(int k_bits, int v_bits, int pdt) {
   return k_bits == v_bits && (k_bits == 1 || k_bits == 2 || k_bits == 4 || k_bits == 8 || k_bits == 16);
 }
 
-// a0 carries n_slots, slot0, fused and the residual rows; the plan gives the
+// a0 carries n_slots, slot0 and the residual rows; the plan gives the
 // grid (the same plan the caller validated the workspace against)
 template <int KB, int VB, int PDT>
 static hipError_t launch_ns(const DecodeArgs& a0, const DecodePlan& p, hipStream_t st) {
@@ -1723,8 +1581,6 @@ static hipError_t launch_ns(const DecodeArgs& a0, const DecodePlan& p, hipStream
   a.n_groups = p.n_groups;
   a.n_chunks = p.n_chunks;
   a.tpc = p.tpc;
-  // residual workgroups ride along only when a second kernel combines
-  if (a.fused && a.n_res) return hipErrorInvalidValue;
   const int res_rows = a.n_res ? (a.n_res * a.g.B * a.g.H + a.n_chunks - 1) / a.n_chunks : 0;
   const dim3 grid(a.n_chunks, a.n_groups + res_rows), block(256);
   if (p.ns == 1) {
@@ -1796,14 +1652,12 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
   p.n_chunks = 0;
   if (has_packed) p = decode_plan(BH, G, g.k_bits, g.v_bits, g.pdt, g.n_tiles);
   const int n_slots = p.n_chunks + n_res;
-  unsigned* counters = (unsigned*)ws;
-  float* part_ml = (float*)((uint8_t*)ws + cnt_bytes(BH));
+  float* part_ml = (float*)ws;
   float* part_o = (float*)((uint8_t*)part_ml + ml_bytes(BH, n_slots, G));
   hipError_t e = hipSuccess;
-  // with a second combine kernel the residual blocks ride along as extra
-  // workgroups of the decode launch; otherwise (in-kernel combine, or no
-  // packed tokens) they run first as their own kernel
-  const bool res_inline = has_packed && n_res > 0 && p.n_chunks < KVQ_DECODE_FUSED_MIN_CHUNKS;
+  // the residual blocks ride along as extra workgroups of the decode launch;
+  // with no packed tokens they run as their own kernel
+  const bool res_inline = has_packed && n_res > 0;
   if (n_res > 0 && !res_inline) {
     e = launch_residual(res, res_dtype, dim3(n_res, BH), q, g.H, G, sl2, part_ml, part_o, n_slots,
                         p.n_chunks, n_slots == 1 ? out : nullptr, st);
@@ -1821,23 +1675,20 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
     a.n_chunks = a.tpc = a.n_groups = 0;
     a.n_slots = n_slots;
     a.slot0 = 0;
-    a.counters = counters;
-    a.fused = n_slots > 1 && p.n_chunks >= KVQ_DECODE_FUSED_MIN_CHUNKS;
     a.res = res;
     a.res_dtype = res_dtype;
     a.n_res = res_inline ? n_res : 0;
     e = launch_decode_any(a, p, st);
     if (e != hipSuccess) return e;
   }
-  if (n_slots > 1 && (!has_packed || p.n_chunks < KVQ_DECODE_FUSED_MIN_CHUNKS))
-    e = launch_combine(part_ml, part_o, out, BH, g.H, G, n_slots, st);
+  if (n_slots > 1) e = launch_combine(part_ml, part_o, out, BH, g.H, G, n_slots, st);
   return e;
 }
 
 // Decode over the tokens of two caches of the same streams (each cache's
 // chunks in its own range of partial slots: cache a's chunks first), then one
 // combine over all slots.  Plans capped at KVQ_SPLIT_MAX_CHUNKS chunks each,
-// so the combine sees at most 128 slots; no in-kernel combine.
+// so the combine sees at most 128 slots.
 hipError_t launch_decode_split(const Geo& ga, const Geo& gb, const void* q, int G, float scale, float* out,
                                void* ws, hipStream_t st) {
   const int BH = ga.B * ga.H;
@@ -1852,7 +1703,7 @@ hipError_t launch_decode_split(const Geo& ga, const Geo& gb, const void* q, int 
     n_slots += ps[i].n_chunks;
   }
   if (n_slots < 1 || n_slots > KVQ_MAX_SLOTS) return hipErrorInvalidValue;
-  float* part_ml = (float*)((uint8_t*)ws + cnt_bytes(BH));
+  float* part_ml = (float*)ws;
   float* part_o = (float*)((uint8_t*)part_ml + ml_bytes(BH, n_slots, G));
   int slot0 = 0;
   for (int i = 0; i < 2; i++) {
@@ -1868,8 +1719,6 @@ hipError_t launch_decode_split(const Geo& ga, const Geo& gb, const void* q, int 
     a.n_chunks = a.tpc = a.n_groups = 0;
     a.n_slots = n_slots;
     a.slot0 = slot0;
-    a.counters = (unsigned*)ws;
-    a.fused = 0;
     a.res = ResArgs{};
     a.res.R = 0;
     a.res_dtype = KVQ_F32;
@@ -1889,63 +1738,35 @@ size_t decode_split_workspace_bytes(int B, int H, int G) {
 }
 
 // ---------------------------------------------------------------------------
-// Scratch of the allocation-free decode: the counters and chunk partials that
-// a caller's workspace holds otherwise, in a file-scope device array (one
-// copy per GPU, kept until the process ends).  Host code never passes the
-// array's name to a kernel: its device address comes from
-// hipGetSymbolAddress, once per device, with that device current.
+// Scratch of the allocation-free decode: the chunk partials that a caller's
+// workspace holds otherwise, in a file-scope device array (one copy per GPU,
+// kept until the process ends).  Host code never passes the array's name to
+// a kernel: its device address comes from hipGetSymbolAddress, once per
+// device, with that device current.
 // ---------------------------------------------------------------------------
 static __device__ __attribute__((aligned(256))) uint8_t scratch[KVQ_DECODE_SCRATCH_BYTES];
 
-__global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p, int n) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i < n) p[i] = 0u;
-}
-
 namespace {
 constexpr int SCRATCH_DEVICES = 64;
-struct ScratchSlot {
-  void* ptr = nullptr;       // device address of this GPU's copy of `scratch`
-  bool clear = true;         // its counters must be zeroed before the next decode
-};
 std::mutex scratch_mu;
-ScratchSlot scratch_slots[SCRATCH_DEVICES];
+void* scratch_ptr[SCRATCH_DEVICES];   // device address of each GPU's copy of `scratch`
 }  // namespace
 
-size_t decode_counter_bytes(int BH) { return cnt_bytes(BH); }
-
-hipError_t decode_scratch_acquire(void** ptr, int BH, hipStream_t st) {
+hipError_t decode_scratch_acquire(void** ptr) {
   int dev = -1;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
   if (dev < 0 || dev >= SCRATCH_DEVICES) return hipErrorInvalidDevice;
   std::lock_guard<std::mutex> lk(scratch_mu);
-  ScratchSlot& sl = scratch_slots[dev];
-  if (!sl.ptr) {
+  if (!scratch_ptr[dev]) {
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
     if (e != hipSuccess) return e;
     if (!p) return hipErrorInvalidSymbol;
-    sl.ptr = p;
+    scratch_ptr[dev] = p;
   }
-  if (sl.clear) {
-    // the counters of the in-kernel chunk combine start at zero; a fill
-    // kernel (not a memset node) on the caller's stream
-    const int n = (int)(cnt_bytes(BH) / 4);
-    hipLaunchKernelGGL(fill_zero_kernel, dim3((n + 255) / 256), dim3(256), 0, st, (uint32_t*)sl.ptr, n);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    sl.clear = false;
-  }
-  *ptr = sl.ptr;
+  *ptr = scratch_ptr[dev];
   return hipSuccess;
-}
-
-void decode_scratch_mark_dirty() {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= SCRATCH_DEVICES) return;
-  std::lock_guard<std::mutex> lk(scratch_mu);
-  scratch_slots[dev].clear = true;
 }
 
 }  // namespace kvq

@@ -264,24 +264,21 @@ static kvq_status decode_common(const kvq_cache* c, const void* q, int32_t n_q_h
   if (use_scratch) {
     // allocation-free variant: this call's own plan must fit the library's
     // scratch array
-    size_t need = kvq::decode_counter_bytes(c->batch * c->n_kv_heads);
+    kvq::DecodePlan plan;
+    plan.n_chunks = 0;
     if (c->n_tokens > 0) {
-      const kvq::DecodePlan plan = kvq::decode_plan(c->batch * c->n_kv_heads, G, c->k_bits, c->v_bits,
-                                                    c->param_dtype, c->n_tokens / 128);
+      plan = kvq::decode_plan(c->batch * c->n_kv_heads, G, c->k_bits, c->v_bits, c->param_dtype,
+                              c->n_tokens / 128);
       if (plan.n_chunks > kvq::KVQ_MAX_CHUNKS || plan.n_chunks * plan.tpc < c->n_tokens / 128)
         return KVQ_EWORKSPACE;
-      need = kvq::decode_workspace_needed(c->batch * c->n_kv_heads, G, plan);
     }
-    if (need > (size_t)KVQ_DECODE_SCRATCH_BYTES) return KVQ_EWORKSPACE;
-    hipError_t e = kvq::decode_scratch_acquire(&workspace, c->batch * c->n_kv_heads, stream);
+    if (kvq::decode_workspace_needed(c->batch * c->n_kv_heads, G, plan) > (size_t)KVQ_DECODE_SCRATCH_BYTES)
+      return KVQ_EWORKSPACE;
+    hipError_t e = kvq::decode_scratch_acquire(&workspace);
     if (e != hipSuccess) return KVQ_EHIP;
     kvq::Geo g = make_geo(c);
     e = kvq::launch_decode(g, q, G, softmax_scale, out, workspace, res, res_dtype, stream);
-    if (e != hipSuccess) {
-      kvq::decode_scratch_mark_dirty();
-      return KVQ_EHIP;
-    }
-    return KVQ_OK;
+    return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
   }
   const size_t need = kvq::decode_workspace_bytes(c->batch, c->n_kv_heads, G, c->max_tokens / 128);
   if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return KVQ_EWORKSPACE;

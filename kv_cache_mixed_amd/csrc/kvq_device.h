@@ -280,11 +280,8 @@ struct ResArgs {
 };
 hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float* out, void* ws,
                          const ResArgs& res, int res_dtype, hipStream_t st);
-// allocation-free decode: the current device's copy of the library's scratch
-// array (KVQ_DECODE_SCRATCH_BYTES), its counters for BH streams zeroed on
-// `st` first when needed; after a failed decode launch mark it for clearing
-hipError_t decode_scratch_acquire(void** ptr, int BH, hipStream_t st);
-void decode_scratch_mark_dirty();
-size_t decode_counter_bytes(int BH);
+// allocation-free decode: the device address of the current device's copy
+// of the library's scratch array (KVQ_DECODE_SCRATCH_BYTES)
+hipError_t decode_scratch_acquire(void** ptr);
 bool decode_supported(int k_bits, int v_bits, int pdt);
 }  // namespace kvq

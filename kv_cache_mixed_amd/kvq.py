@@ -417,12 +417,6 @@ class PackedCache:
     def workspace_bytes(self, n_q_heads):
         return int(load().kvq_decode_workspace_bytes(ctypes.byref(self.s), n_q_heads))
 
-    def workspace_counter_bytes(self):
-        """KVQ_DECODE_COUNTER_BYTES of the header: the leading workspace bytes
-        that must be zero before a decode call (every successful call leaves
-        them zero)."""
-        return (self.s.batch * self.s.n_kv_heads * 4 + 255) // 256 * 256
-
     def workspace(self, n_q_heads):
         import torch
         if n_q_heads not in self._ws:

@@ -117,7 +117,7 @@ def test_decode_parity(pdt, B, H, G, T):
 
 
 def test_decode_long_fused_combine():
-    """A single long stream group: enough chunks for the in-kernel combine."""
+    """A single long stream group cut into 64 chunks."""
     inp = synth.mixed_kv_layer(1, 1, 4, 16384, seed=640)
     print("vmixed decode long", flush=True)
     c = _cache(inp, 16384, kvq.E4M3)

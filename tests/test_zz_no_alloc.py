@@ -45,9 +45,8 @@ def _check(inp, cache, bits, pairs):
 
 
 def test_noalloc_matches_workspace_entry_point_two_calls():
-    # first call: a single long stream group cut into >= 48 chunks (the
-    # in-kernel combine, which uses the scratch's counters), then a batched
-    # layer combined by the second kernel, then a smaller input
+    # first call: a single long stream group cut into 64 chunks, then a
+    # batched layer, then a smaller input
     print("case noalloc 1x1x7 T=32768 4-bit", flush=True)
     inp, cache = _case(1, 1, 7, 32768, 4, seed=301)
     _check(inp, cache, 4, [(0, 0)])
@@ -57,7 +56,7 @@ def test_noalloc_matches_workspace_entry_point_two_calls():
     print("case noalloc 1x2x8 T=640 4-bit", flush=True)
     inp, cache = _case(1, 2, 8, 640, 4, seed=303)
     _check(inp, cache, 4, [(0, 0), (0, 1)])
-    # the long stream again: the counters were left zero by the earlier calls
+    # the long stream again, over the partials the earlier calls left
     print("case noalloc 1x1x7 T=32768 4-bit again", flush=True)
     inp, cache = _case(1, 1, 7, 32768, 4, seed=304)
     _check(inp, cache, 4, [(0, 0)])
