@@ -51,6 +51,11 @@
 #define KVQ_DECODE_WAVES_PER_SIMD 0
 #endif
 // most sub-tiles a 128-token tile is cut into (4, 2 or 1)
+// folded query operand kept in registers across a tile's sub-tiles (1) or
+// staged in the wave's LDS region (0)
+#ifndef KVQ_DECODE_QREG
+#define KVQ_DECODE_QREG 1
+#endif
 #ifndef KVQ_DECODE_NSUB_MAX
 #define KVQ_DECODE_NSUB_MAX 4
 #endif
@@ -720,6 +725,13 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
   for (int cb = 0; cb < 8; cb++) acc_o[cb] = (f32x4){0.f, 0.f, 0.f, 0.f};
   uint32_t* my_lds = lds[wave];
+  // the folded query operand of the current tile, [k-step][hi/lo][4]: in
+  // registers (QREG), or in the wave's LDS region where its 32 registers
+  // would spill: 16-bit keys (64 registers), 1-bit codes and two streams of
+  // 2-bit codes (measured 9% slower there, 3-5% faster at 4 bits), and
+  // binary32 parameters (twice the parameter registers)
+  constexpr bool QREG = KVQ_DECODE_QREG && KB != 16 && KB != 1 && !(KB == 2 && NS >= 2) && PDT != KVQ_F32;
+  uint32_t qop[QREG ? NKK : 1][2][4];
 
   // one sub-tile of raw operands; value words travel outside the prefetch
   // buffers: they are loaded at the start of their own sub-tile (in flight
@@ -1000,8 +1012,13 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       uint32_t hi, lo;
       split_pack(ul * w, uh * wh, hi, lo, m1);
       // [k-step][hi/lo][lane][4]: one ds_read_b128 per operand group
-      my_lds[(((f >> 2) * 2 + 0) * 64 + lane) * 4 + (f & 3)] = hi;
-      my_lds[(((f >> 2) * 2 + 1) * 64 + lane) * 4 + (f & 3)] = lo;
+      if constexpr (QREG) {
+        qop[f >> 2][0][f & 3] = hi;
+        qop[f >> 2][1][f & 3] = lo;
+      } else {
+        my_lds[(((f >> 2) * 2 + 0) * 64 + lane) * 4 + (f & 3)] = hi;
+        my_lds[(((f >> 2) * 2 + 1) * 64 + lane) * 4 + (f & 3)] = lo;
+      }
     }
     ak = __builtin_fabsf(a.sl2) * exp2i(24 - KH + eqs);
     bk0 = __builtin_fabsf(a.sl2) * beta;
@@ -1027,10 +1044,16 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       for (int jj = 0; jj < JB; jj++) acc[s][jj] = (f32x4){0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int k = 0; k < NKK; k++) {
-      const u32x4 bhv = *(const u32x4*)(my_lds + ((k * 2 + 0) * 64 + lane) * 4);
-      const u32x4 blv = *(const u32x4*)(my_lds + ((k * 2 + 1) * 64 + lane) * 4);
-      const uint32_t bh4[4] = {bhv[0], bhv[1], bhv[2], bhv[3]};
-      const uint32_t bl4[4] = {blv[0], blv[1], blv[2], blv[3]};
+      uint32_t bh4[4], bl4[4];
+      if constexpr (QREG) {
+#pragma unroll
+        for (int r = 0; r < 4; r++) { bh4[r] = qop[k][0][r]; bl4[r] = qop[k][1][r]; }
+      } else {
+        const u32x4 bhv = *(const u32x4*)(my_lds + ((k * 2 + 0) * 64 + lane) * 4);
+        const u32x4 blv = *(const u32x4*)(my_lds + ((k * 2 + 1) * 64 + lane) * 4);
+#pragma unroll
+        for (int r = 0; r < 4; r++) { bh4[r] = bhv[r]; bl4[r] = blv[r]; }
+      }
       uint32_t av[NS][JB][4];
 #pragma unroll
       for (int s = 0; s < NS; s++)
