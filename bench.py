@@ -33,14 +33,14 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, profiles/decode_kernel_*.md)
 # for the kernel source with the given digest, and the factors that map each
 # counter onto true bytes: a plain 512 MiB device copy in the same run reads
-# FETCH_SIZE = 262158.6 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
-# fetch counter is scaled by 524288/262158.6 and the write counter by 1.  The
+# FETCH_SIZE = 262159.1 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
+# fetch counter is scaled by 524288/262159.1 and the write counter by 1.  The
 # figure is reported only while the kernel source is unchanged.
 COUNTER_TRAFFIC = {
-    "source_sha256": "45dbe960d54a5507c31ae2e87c2e8a1f87b80ca7183525b130b5c27fc9b2a12a",
+    "source_sha256": "0580ae042a69429f7a8d1ef59d9768561e4261cb9d07facb73d265a6fba1bf58",
     "fetch_kib": 139895.2,
     "write_kib": 3664.0,
-    "fetch_factor": 524288.0 / 262158.6,
+    "fetch_factor": 524288.0 / 262159.1,
     "write_factor": 1.0,
 }
 KERNEL_SOURCES = ("kv_cache_mixed_amd/csrc/decode_attn.hip", "kv_cache_mixed_amd/csrc/kvq_device.h")

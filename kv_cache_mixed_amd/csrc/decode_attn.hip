@@ -50,12 +50,12 @@
 #ifndef KVQ_DECODE_WAVES_PER_SIMD
 #define KVQ_DECODE_WAVES_PER_SIMD 0
 #endif
-// most sub-tiles a 128-token tile is cut into (4, 2 or 1)
 // folded query operand kept in registers across a tile's sub-tiles (1) or
 // staged in the wave's LDS region (0)
 #ifndef KVQ_DECODE_QREG
 #define KVQ_DECODE_QREG 1
 #endif
+// most sub-tiles a 128-token tile is cut into (4, 2 or 1)
 #ifndef KVQ_DECODE_NSUB_MAX
 #define KVQ_DECODE_NSUB_MAX 4
 #endif
@@ -615,6 +615,11 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   constexpr int PWV = PW<PDT, TPS>::W;               // value-parameter words per sub-tile (and class)
   constexpr int NCV = VMIX ? 4 : 1;                  // value parameter classes
   constexpr int NVW = VMIX ? 10 : 8 * WVS;           // value words per stream per sub-tile
+  // mixed values: the sub-tile's value parameters (4 classes, 32 registers
+  // per buffer with e4m3) are loaded with its value words instead of two
+  // sub-tiles ahead (measured 7% faster with binary16 parameters, equal with
+  // e4m3, at one wave per SIMD; two waves per SIMD spill even so)
+  constexpr bool PJIT = VMIX;
   constexpr int PWK = PW<PDT, 8>::W;                 // key-parameter words per 8 slots
   constexpr int KPA = 32 * PB;                       // words per 128 key parameters
   constexpr int KPL = (PB == 4) ? 2 : 1;             // of which one lane loads
@@ -730,7 +735,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // would spill: 16-bit keys (64 registers), 1-bit codes and two streams of
   // 2-bit codes (measured 9% slower there, 3-5% faster at 4 bits), and
   // binary32 parameters (twice the parameter registers)
-  constexpr bool QREG = KVQ_DECODE_QREG && KB != 16 && KB != 1 && !(KB == 2 && NS >= 2) && PDT != KVQ_F32;
+  constexpr bool QREG = KVQ_DECODE_QREG && KB != 16 && KB != 1 && !(KB == 2 && NS >= 2) && PDT != KVQ_F32 && !VMIX;
   uint32_t qop[QREG ? NKK : 1][2][4];
 
   // one sub-tile of raw operands; value words travel outside the prefetch
@@ -738,7 +743,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // during its key product and softmax)
   struct Buf {
     uint32_t kw[NS][JB][NWK];
-    uint32_t vs[NCV * PWV], vz[NCV * PWV];
+    uint32_t vs[PJIT ? 1 : NCV * PWV], vz[PJIT ? 1 : NCV * PWV];
     uint32_t kp[NS][2][KPL];   // next tile's key scales / zeros (sub-tile 0 only)
   };
 
@@ -826,14 +831,17 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     }
   };
   // ... and the own stream's value scales / zeros of the lane's TPS tokens
-  auto load_p = [&](Buf& bf, int k, int sub) {
+  auto load_p_to = [&](uint32_t* ps, uint32_t* pz, int k, int sub) {
     const int tile = t_base + k;
     const uint32_t psoff = (uint32_t)(tile * 128 + sub * TPS) * PB;
 #pragma unroll
-    for (int k = 0; k < NCV; k++) {   // mixed values: class k's parameters k * max_tokens further
-      pload<PDT, TPS>(r_vs, vpoff, psoff + (uint32_t)(k * g.max_tokens * PB), bf.vs + k * PWV);
-      pload<PDT, TPS>(r_vz, vpoff, psoff + (uint32_t)(k * g.max_tokens * PB), bf.vz + k * PWV);
+    for (int c = 0; c < NCV; c++) {   // mixed values: class c's parameters c * max_tokens further
+      pload<PDT, TPS>(r_vs, vpoff, psoff + (uint32_t)(c * g.max_tokens * PB), ps + c * PWV);
+      pload<PDT, TPS>(r_vz, vpoff, psoff + (uint32_t)(c * g.max_tokens * PB), pz + c * PWV);
     }
+  };
+  auto load_p = [&](Buf& bf, int k, int sub) {
+    if constexpr (!PJIT) load_p_to(bf.vs, bf.vz, k, sub);
   };
   auto load = [&](Buf& bf, int k, int sub) {
     load_k(bf, k, sub);
@@ -1034,6 +1042,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   auto compute = [&](Buf& bf, int ti, int sub, int ti2, int sub2) {
     uint32_t vjit[NS * NVW];
     issue_v(vjit, ti, sub);
+    // (PJIT) the sub-tile's value parameters, loaded with its value words
+    uint32_t pjs[PJIT ? NCV * PWV : 1], pjz[PJIT ? NCV * PWV : 1];
+    if constexpr (PJIT) load_p_to(pjs, pjz, ti, sub);
     const uint32_t* vwp = vjit;
     if (sub == 0) fold_query(bf);
     // ---- logits: k-step-major over all (stream, block) accumulators
@@ -1109,7 +1120,15 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       // are >= +0, so binary16 and e4m3 patterns order like their values)
       static_assert(!VMIX || PDT == KVQ_F16 || PDT == KVQ_E4M3, "mixed values: binary16 or e4m3 parameters");
 #pragma unroll
-      for (int w = 0; w < NCV * PWV; w++) { rvs[w] = bf.vs[w]; rvz[w] = bf.vz[w]; }
+      for (int w = 0; w < NCV * PWV; w++) {
+        if constexpr (PJIT) {
+          rvs[w] = pjs[w];
+          rvz[w] = pjz[w];
+        } else {
+          rvs[w] = bf.vs[w];
+          rvz[w] = bf.vz[w];
+        }
+      }
       if constexpr (MIX) {
         uint32_t m2 = rvs[0];
 #pragma unroll
