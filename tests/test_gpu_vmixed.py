@@ -202,3 +202,49 @@ def test_decode_split_mixed_and_uniform():
         ref = oracle.decode_attn_union([sa, sb], inp["q_bf16"][0, 4 * h:4 * h + 4], SCALE)
         worst = max(worst, rel_err_rows(out[0, 4 * h:4 * h + 4], ref).max())
     assert worst <= REL_TOL, "max row relative error %.3e" % worst
+
+
+def test_decode_noalloc_equals_workspace_call():
+    """The allocation-free entry point on a mixed K+V cache gives the same
+    bits as the workspace entry point."""
+    inp = synth.mixed_kv_layer(1, 2, 8, 2048, seed=690)
+    print("vmixed noalloc", flush=True)
+    c = _cache(inp, 2048, kvq.E4M3)
+    c.quantize(to_dev(inp["k"], torch), to_dev(inp["v"], torch), 0)
+    q = q_to_dev(inp["q_bf16"], torch)
+    a = c.decode_attn(q, SCALE)
+    b = c.decode_attn_noalloc(q, SCALE)
+    torch.cuda.synchronize()
+    assert torch.equal(a, b)
+
+
+def test_window_append_and_residual_decode():
+    """Token-granular append into a mixed K+V cache (first token and recent
+    tokens held in bfloat16, full groups packed at the mixed widths), then
+    decode over cache + window against the oracle's attention over (packed
+    tokens, held tokens)."""
+    B, H, G, T = 1, 2, 4, 300
+    inp = synth.mixed_kv_layer(B, H, H * G, T, seed=700)
+    k16 = torch.from_numpy(inp["k"]).to(torch.bfloat16)
+    v16 = torch.from_numpy(inp["v"]).to(torch.bfloat16)
+    kf, vf = k16.float().numpy(), v16.float().numpy()
+    print("vmixed window append", flush=True)
+    c = _cache(inp, 512, kvq.E4M3)
+    win = kvq.Window(c, torch.bfloat16, keep_first=True)
+    for a, b in ((0, 1), (1, 130), (130, 131), (131, 300)):
+        win.append(k16[:, :, a:b].contiguous().cuda(), v16[:, :, a:b].contiguous().cuda())
+    torch.cuda.synchronize()
+    # token 0 in row 0, tokens 1..256 packed (two groups), 257..299 held
+    assert (win.w.n_first, win.w.n_recent, c.n_tokens) == (1, 43, 256)
+    held = [0] + list(range(257, 300))
+    rk, rv = win.residual()
+    out = c.decode_attn(q_to_dev(inp["q_bf16"], torch), SCALE, res_k=rk, res_v=rv).cpu().numpy()
+    worst = 0.0
+    for h in range(H):
+        st = oracle.quantize_stream(kf[0, h, 1:257], vf[0, h, 1:257], kvq.KMIXED, kvq.VMIXED, oracle.E4M3,
+                                    inp["slot_chan"][h], inp["v_slot_chan"][h])
+        assert_stream_bytes_equal(c, st, 0, h, "window")
+        ref = oracle.decode_attn_residual(st, inp["q_bf16"][0, h * G:(h + 1) * G], SCALE, kf[0, h, held],
+                                          vf[0, h, held])
+        worst = max(worst, rel_err_rows(out[0, h * G:(h + 1) * G], ref).max())
+    assert worst <= REL_TOL, "max row relative error %.3e" % worst
