@@ -7,11 +7,11 @@
 // parameters into the softmax weights, so the two contractions run on the raw
 // integer codes with MFMA.
 //
-// Work decomposition.  Grid = (chunk, b * Hkv).  A workgroup of 4 waves owns
-// one chunk of 128-token tiles of one (batch, kv head) stream and all G query
-// heads of that kv head; wave w takes tiles w, w+4, ... of the chunk.  Per tile
-// a wave computes, with the G heads padded to the 16 columns of a
-// 16x16x32 f16 MFMA:
+// Work decomposition.  Grid = (chunk, stream group).  A workgroup of 4 waves
+// owns one chunk of 128-token tiles of NS (batch, kv head) streams and all G
+// query heads of each (NS * G <= 16 columns); wave w takes tiles w, w+4, ...
+// of the chunk.  Per tile a wave computes, with the heads padded to the 16
+// columns of a 16x16x32 f16 MFMA:
 //   S^T[t][n] = sum_c K[t][c] * u[n][c],   u = q * S_K * 2^k (per tile, f16)
 //   logit_n(t) = sigma * (S^T / 2^k + sum_c q[n][c] Z_K[c])
 //   online softmax in the log2 domain (running max per head, shared by the
@@ -34,9 +34,16 @@
 // bit position p (p + b <= 10) of both 16-bit halves of a loaded word, masked in
 // place, is the f16 subnormal code * 2^(p - 24), which MFMA multiplies exactly.
 // The power-of-two field weights (2^-p, and 2^8 for the high byte of 16-bit
-// codes) are folded into the other operand.  That operand (u for keys, P for
-// values) is split into f16 hi + lo parts (two MFMAs), so the products carry
-// about 22 significant bits and the sums accumulate in binary32.
+// codes) are folded into the other operand.  For keys that operand (u) is
+// split into f16 hi + lo parts (two MFMAs), so the products carry about 22
+// significant bits; for values P is one rounded binary16 per token, and its
+// rounding residual times the codes' midpoint is added back exactly through
+// the zero-point sum.  The sums accumulate in binary32.
+//
+// Mixed-width keys (4/3/1/2-bit slots in five byte planes) and mixed-width
+// values (4/3/1/2-bit slot classes in 4- and 2-bit fields, one probability
+// operand and one zero-point sum per class) use the same loop with their own
+// field extraction.
 //
 // Softmax uses a lazy running max: the reference m only moves when a logit
 // exceeds it by more than TAU (log2 units), so e = 2^(logit - m) <= 2^TAU and
