@@ -289,6 +289,51 @@ kvq_status kvq_decode_attn(const kvq_cache *cache, const void *q, int32_t n_q_he
                            float softmax_scale, float *out, void *workspace,
                            size_t workspace_bytes, hipStream_t stream);
 
+/* Decode attention in its two phases, as separate calls.  kvq_decode_attn
+ * is the same two launches back to back.  The split is the one of
+ * FlashAttention-style decoding (attention over token ranges, then a
+ * rescaled sum), applied to the attention over the reconstructed cache of
+ * [CHANMIX] Overall framework.  It serves callers that combine partials from
+ * several sources (for example one sequence's tokens held on several
+ * devices: each runs the first phase over its share, the partial slots are
+ * gathered into one array, and one combine finishes), and callers that time
+ * the phases apart.
+ *
+ * kvq_decode_attn_partials: the first phase over the packed cache.  The
+ * stored tiles of every stream are cut into *n_slots chunks of
+ * *tiles_per_slot consecutive tiles (the last may hold fewer); slot s covers
+ * tokens [128 * s * tiles_per_slot, min(128 * (s + 1) * tiles_per_slot,
+ * n_tokens)).  For stream bh = b * n_kv_heads + h, slot s and query head
+ * j < G of the stream (query head h * G + j), with row r = (bh * n_slots + s)
+ * * G + j and x_t = softmax_scale * log2(e) * (q . k^_t) over the slot's
+ * tokens t (k^, v^ the reconstructions S' * q + Z'), it writes
+ *   float ml[r][2] = {m, l},  l = sum_t 2^(x_t - m)
+ *   float o[r][128]          = sum_t 2^(x_t - m) * v^_t  (not normalised)
+ * where m is a reference the kernel picks (m <= max_t x_t <= m + 8 up to
+ * rounding; the combine takes any finite m).  ml starts at byte 0 of
+ * the workspace, o at byte round_up(8 * B * n_kv_heads * n_slots * G, 256)
+ * (kvq_decode_partials_bytes gives the total).  Always written as partials,
+ * also when n_slots is 1.  Requirements, workspace (at least
+ * kvq_decode_workspace_bytes()) and errors as for kvq_decode_attn;
+ * n_slots and tiles_per_slot: host pointers, written on success.
+ *
+ * kvq_decode_combine: the second phase.  For every (b, query head) it reads
+ * n_slots partial rows in the layout above and writes
+ *   out[b][hq][c] = sum_s 2^(m_s - M) o_s[c] / sum_s 2^(m_s - M) l_s,
+ *   M = max_s m_s
+ * (out: device float32 [B][n_q_heads][128], 16-byte aligned).  1 <= n_slots
+ * <= 128, else KVQ_EINVAL; workspace 256-byte aligned with at least
+ * kvq_decode_partials_bytes(batch, n_kv_heads, n_q_heads, n_slots) bytes,
+ * else KVQ_EWORKSPACE; n_q_heads a multiple of n_kv_heads, at most 16 query
+ * heads per kv head. */
+kvq_status kvq_decode_attn_partials(const kvq_cache *cache, const void *q, int32_t n_q_heads,
+                                    float softmax_scale, void *workspace, size_t workspace_bytes,
+                                    int32_t *n_slots, int32_t *tiles_per_slot, hipStream_t stream);
+size_t kvq_decode_partials_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads, int32_t n_slots);
+kvq_status kvq_decode_combine(const void *workspace, size_t workspace_bytes, int32_t batch,
+                              int32_t n_kv_heads, int32_t n_q_heads, int32_t n_slots, float *out,
+                              hipStream_t stream);
+
 /* Decode attention over the tokens of two caches of the same streams
  * ([SEMKV] abstract: every token kept, each stream's tokens split by rank
  * between two adjacent precisions).  For batch b and query head hq the

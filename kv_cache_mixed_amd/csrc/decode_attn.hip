@@ -1415,7 +1415,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   __syncthreads();
 
   const int ncol = NS * G;
-  const bool single = (a.n_slots == 1);
+  const bool single = (a.n_slots == 1) && a.out != nullptr;   // no out: partials only
   // per column: the workgroup max M, the weight 2^(m_w - M) of each wave's
   // partial, the sum and the destination row -- the output row
   // (batch, query head) = grp * NS * G + col when this is the stream's only
@@ -1526,13 +1526,20 @@ DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_til
 //   o = sum_k 2^(m_k - M) o_k / sum_k 2^(m_k - M) l_k,  M = max_k m_k.
 // Lane k holds the (m, l) of chunks k and k + 64; each lane owns two channels
 // of o and walks the chunks with the weight broadcast from its owner lane.
+// output rows (one wave each) per combine workgroup.  One: the rows spread
+// over as many CUs as there are rows, which measured 2% faster per call on
+// a single 128K sequence (32 rows) than four rows per workgroup, and the same
+// on the batched layers.
+#ifndef KVQ_COMBINE_WAVES
+#define KVQ_COMBINE_WAVES 1
+#endif
 template <int KP>
-__global__ __launch_bounds__(256) void decode_combine_kernel(const float* __restrict__ part_ml,
+__global__ __launch_bounds__(64 * KVQ_COMBINE_WAVES) void decode_combine_kernel(const float* __restrict__ part_ml,
                                                              const float* __restrict__ part_o,
                                                              float* __restrict__ out, int BH, int H,
                                                              int G, int nck) {
   const int lane = threadIdx.x & 63;
-  const int row = blockIdx.x * 4 + (threadIdx.x >> 6);   // bh * G + hh
+  const int row = blockIdx.x * KVQ_COMBINE_WAVES + (threadIdx.x >> 6);   // bh * G + hh
   if (row >= BH * G) return;
   const int bh = row / G, hh = row - (row / G) * G;
   const int64_t r0 = (int64_t)bh * nck * G + hh;         // partial row of chunk 0
@@ -1586,7 +1593,7 @@ __global__ __launch_bounds__(256) void decode_combine_kernel(const float* __rest
 static hipError_t launch_combine(const float* part_ml, const float* part_o, float* out, int BH, int H, int G,
                                  int n_slots, hipStream_t st) {
   const int rows = BH * G;
-  const dim3 grid((rows + 3) / 4), block(256);
+  const dim3 grid((rows + KVQ_COMBINE_WAVES - 1) / KVQ_COMBINE_WAVES), block(64 * KVQ_COMBINE_WAVES);
   if (n_slots <= 16)
     hipLaunchKernelGGL(decode_combine_kernel<16>, grid, block, 0, st, part_ml, part_o, out, BH, H, G, n_slots);
   else if (n_slots <= 32)
@@ -1732,6 +1739,46 @@ hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float*
   }
   if (n_slots > 1) e = launch_combine(part_ml, part_o, out, BH, g.H, G, n_slots, st);
   return e;
+}
+
+// First phase alone: the packed cache's chunk partials, written to the
+// workspace even when the plan has a single chunk (out = null tells the
+// kernel so); the plan's slot count and tiles per slot go to the caller.
+hipError_t launch_decode_partials(const Geo& g, const void* q, int G, float scale, void* ws, int* n_slots,
+                                  int* tiles_per_slot, hipStream_t st) {
+  const int BH = g.B * g.H;
+  const DecodePlan p = decode_plan(BH, G, g.k_bits, g.v_bits, g.pdt, g.n_tiles);
+  DecodeArgs a;
+  a.g = g;
+  a.q = (const uint16_t*)q;
+  a.out = nullptr;
+  a.part_ml = (float*)ws;
+  a.part_o = (float*)((uint8_t*)ws + ml_bytes(BH, p.n_chunks, G));
+  a.G = G;
+  a.sl2 = scale * 1.4426950408889634f;
+  a.n_chunks = a.tpc = a.n_groups = 0;
+  a.n_slots = p.n_chunks;
+  a.slot0 = 0;
+  a.res = ResArgs{};
+  a.res.R = 0;
+  a.res_dtype = KVQ_F32;
+  a.n_res = 0;
+  *n_slots = p.n_chunks;
+  *tiles_per_slot = p.tpc;
+  return launch_decode_any(a, p, st);
+}
+
+// Second phase alone: the combine over n_slots partial slots laid out as the
+// first phase writes them.
+hipError_t launch_decode_combine(const void* ws, int B, int H, int G, int n_slots, float* out, hipStream_t st) {
+  const int BH = B * H;
+  const float* part_ml = (const float*)ws;
+  const float* part_o = (const float*)((const uint8_t*)ws + ml_bytes(BH, n_slots, G));
+  return launch_combine(part_ml, part_o, out, BH, H, G, n_slots, st);
+}
+
+size_t decode_partials_bytes(int BH, int G, int n_slots) {
+  return ml_bytes(BH, n_slots, G) + (size_t)BH * n_slots * G * 128 * 4;
 }
 
 // Decode over the tokens of two caches of the same streams (each cache's

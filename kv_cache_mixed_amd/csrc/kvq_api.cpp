@@ -309,6 +309,66 @@ kvq_status kvq_decode_attn(const kvq_cache* c, const void* q, int32_t n_q_heads,
   }
 }
 
+kvq_status kvq_decode_attn_partials(const kvq_cache* c, const void* q, int32_t n_q_heads, float softmax_scale,
+                                    void* workspace, size_t workspace_bytes, int32_t* n_slots,
+                                    int32_t* tiles_per_slot, hipStream_t stream) {
+  try {
+    kvq_status s = check_cache(c);
+    if (s != KVQ_OK) return s;
+    if (!q || !n_slots || !tiles_per_slot || !aligned(q, 16)) return KVQ_EINVAL;
+    if (n_q_heads < 1 || n_q_heads % c->n_kv_heads) return KVQ_EINVAL;
+    const int G = n_q_heads / c->n_kv_heads;
+    if (G > 16) return KVQ_EUNSUPPORTED;
+    if (c->n_tokens < 128) return KVQ_EINVAL;   // nothing to attend
+    if (!(softmax_scale == softmax_scale) || softmax_scale == INFINITY || softmax_scale == -INFINITY)
+      return KVQ_EINVAL;
+    if (!kvq::decode_supported(c->k_bits, c->v_bits, c->param_dtype)) return KVQ_EUNSUPPORTED;
+    if ((int64_t)c->batch * c->n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+    const int BH = c->batch * c->n_kv_heads;
+    const size_t need = kvq::decode_workspace_bytes(c->batch, c->n_kv_heads, G, c->max_tokens / 128);
+    if (!workspace || workspace_bytes < need || !aligned(workspace, 256)) return KVQ_EWORKSPACE;
+    const kvq::DecodePlan plan =
+        kvq::decode_plan(BH, G, c->k_bits, c->v_bits, c->param_dtype, c->n_tokens / 128);
+    if (plan.n_chunks < 1 || plan.n_chunks > kvq::KVQ_MAX_CHUNKS || plan.n_chunks * plan.tpc < c->n_tokens / 128 ||
+        kvq::decode_partials_bytes(BH, G, plan.n_chunks) > workspace_bytes)
+      return KVQ_EWORKSPACE;
+    int ns = 0, tps = 0;
+    hipError_t e = kvq::launch_decode_partials(make_geo(c), q, G, softmax_scale, workspace, &ns, &tps, stream);
+    if (e != hipSuccess) return KVQ_EHIP;
+    *n_slots = ns;
+    *tiles_per_slot = tps;
+    return KVQ_OK;
+  } catch (...) {
+    return KVQ_EHIP;
+  }
+}
+
+size_t kvq_decode_partials_bytes(int32_t batch, int32_t n_kv_heads, int32_t n_q_heads, int32_t n_slots) {
+  if (batch < 1 || n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads) return 0;
+  const int G = n_q_heads / n_kv_heads;
+  if (G > 16 || n_slots < 1 || n_slots > kvq::KVQ_MAX_SLOTS) return 0;
+  if ((int64_t)batch * n_kv_heads > 65535) return 0;
+  return kvq::decode_partials_bytes(batch * n_kv_heads, G, n_slots);
+}
+
+kvq_status kvq_decode_combine(const void* workspace, size_t workspace_bytes, int32_t batch, int32_t n_kv_heads,
+                              int32_t n_q_heads, int32_t n_slots, float* out, hipStream_t stream) {
+  try {
+    if (batch < 1 || n_kv_heads < 1 || n_q_heads < 1 || n_q_heads % n_kv_heads) return KVQ_EINVAL;
+    const int G = n_q_heads / n_kv_heads;
+    if (G > 16 || (int64_t)batch * n_kv_heads > 65535) return KVQ_EUNSUPPORTED;
+    if (n_slots < 1 || n_slots > kvq::KVQ_MAX_SLOTS) return KVQ_EINVAL;
+    if (!out || !aligned(out, 16)) return KVQ_EINVAL;
+    if (!workspace || !aligned(workspace, 256) ||
+        workspace_bytes < kvq::decode_partials_bytes(batch * n_kv_heads, G, n_slots))
+      return KVQ_EWORKSPACE;
+    hipError_t e = kvq::launch_decode_combine(workspace, batch, n_kv_heads, G, n_slots, out, stream);
+    return e == hipSuccess ? KVQ_OK : KVQ_EHIP;
+  } catch (...) {
+    return KVQ_EHIP;
+  }
+}
+
 size_t kvq_decode_split_workspace_bytes(const kvq_cache* a, const kvq_cache* b, int32_t n_q_heads) {
   if (check_cache(a) != KVQ_OK || check_cache(b) != KVQ_OK) return 0;
   if (a->batch != b->batch || a->n_kv_heads != b->n_kv_heads) return 0;

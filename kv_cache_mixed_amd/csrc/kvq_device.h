@@ -280,6 +280,15 @@ struct ResArgs {
 };
 hipError_t launch_decode(const Geo& g, const void* q, int G, float scale, float* out, void* ws,
                          const ResArgs& res, int res_dtype, hipStream_t st);
+// the two phases of launch_decode (packed cache only) as separate launches:
+// the chunk partials (always written to ws, also for a single chunk), and the
+// combine of n_slots slots of that layout into out
+hipError_t launch_decode_partials(const Geo& g, const void* q, int G, float scale, void* ws, int* n_slots,
+                                  int* tiles_per_slot, hipStream_t st);
+hipError_t launch_decode_combine(const void* ws, int B, int H, int G, int n_slots, float* out, hipStream_t st);
+// bytes of n_slots partial slots per stream (the (m, l) array rounded up to
+// 256 bytes, then the outputs)
+size_t decode_partials_bytes(int BH, int G, int n_slots);
 // allocation-free decode: the device address of the current device's copy
 // of the library's scratch array (KVQ_DECODE_SCRATCH_BYTES)
 hipError_t decode_scratch_acquire(void** ptr);

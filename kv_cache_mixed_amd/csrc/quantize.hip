@@ -343,9 +343,10 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __re
 // ---------------------------------------------------------------------------
 // Values with mixed channel widths: for every token, the slots of each width
 // class (4, 3, 1, 2 bits; slot j holds channel v_slot_chan[h][j]) form one
-// group with its own S', Z'.  The tile's inputs pass through LDS in two
-// halves of 64 tokens (binary32, row pitch 129 words, so a wave reading one
-// channel of 64 tokens hits 32 banks).  Wave w quantizes slot blocks w and
+// group with its own S', Z'.  Every thread issues its loads of the whole tile
+// first (16 x 16 bytes); the inputs then pass through LDS in two halves of
+// 64 tokens (binary32, row pitch 129 words, so a wave reading one channel of
+// 64 tokens hits 32 banks).  Wave w quantizes slot blocks w and
 // w + 4 (16 slots each; the block's class, and so its width, is uniform over
 // the wave) of the half's 64 tokens, one token per lane: block minima and
 // maxima go through LDS so the five blocks of the 2-bit class share one
@@ -365,19 +366,25 @@ __global__ __launch_bounds__(256) void quantize_vmixed_kernel(Geo g, const void*
   const int wave = threadIdx.x >> 6, r = threadIdx.x & 63;
   if (threadIdx.x < 128) chan[threadIdx.x] = (int)g.v_slot_chan[h * 128 + threadIdx.x] & 127;
   const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (GATHER ? 0 : (int64_t)(tile_local * 128) * st);
-#pragma unroll 1
+  // item i of half hf = token row 64 hf + i / 32, channels 4 (i % 32) ..
+  float xin[2][8][4];
+#pragma unroll
+  for (int hf = 0; hf < 2; hf++)
+#pragma unroll
+    for (int k = 0; k < 8; k++) {
+      const int i = threadIdx.x + 256 * k;
+      const int t = hf * 64 + (i >> 5);
+      const int64_t row = GATHER ? src_row(ti, b, h, g.H, tile_local * 128 + t) : (int64_t)t;
+      load4<IN, VEC>(vin, base + row * st + (i & 31) * 4, xin[hf][k]);
+    }
+#pragma unroll
   for (int half = 0; half < 2; half++) {
-    // stage 64 tokens: item i = (token row i / 32, channels 4 (i % 32) ..)
 #pragma unroll
     for (int k = 0; k < 8; k++) {
       const int i = threadIdx.x + 256 * k;
       const int tr = i >> 5, c4 = (i & 31) * 4;
-      const int t = half * 64 + tr;
-      const int64_t row = GATHER ? src_row(ti, b, h, g.H, tile_local * 128 + t) : (int64_t)t;
-      float x4[4];
-      load4<IN, VEC>(vin, base + row * st + c4, x4);
 #pragma unroll
-      for (int e = 0; e < 4; e++) xs[tr][c4 + e] = x4[e];
+      for (int e = 0; e < 4; e++) xs[tr][c4 + e] = xin[half][k][e];
     }
     __syncthreads();
     float x[2][16];

@@ -67,6 +67,7 @@ EXPORTS = ["kvq_strerror", "kvq_tile_bytes", "kvq_value_tile_bytes", "kvq_cache_
            "kvq_shrink_shift", "kvq_decode_workspace_bytes", "kvq_decode_attn", "kvq_decode_attn_noalloc",
            "kvq_decode_attn_residual", "kvq_quantize_tokens", "kvq_rank_tokens",
            "kvq_decode_split_workspace_bytes", "kvq_decode_attn_split",
+           "kvq_decode_attn_partials", "kvq_decode_partials_bytes", "kvq_decode_combine",
            "kvq_pool_create", "kvq_pool_destroy", "kvq_pool_used_bytes", "kvq_pool_high_water",
            "kvq_append", "kvq_window_append", "kvq_allocate_bits", "kvq_pair_norms", "kvq_pair_slot_map"]
 
@@ -109,6 +110,13 @@ def load():
     L.kvq_decode_attn_split.argtypes = [P, P, vp, i32, ctypes.c_float, vp, vp, ctypes.c_size_t, vp]
     L.kvq_decode_attn_noalloc.restype = ctypes.c_int
     L.kvq_decode_attn_noalloc.argtypes = [P, vp, i32, ctypes.c_float, vp, vp]
+    L.kvq_decode_attn_partials.restype = ctypes.c_int
+    L.kvq_decode_attn_partials.argtypes = [P, vp, i32, ctypes.c_float, vp, ctypes.c_size_t,
+                                           ctypes.POINTER(i32), ctypes.POINTER(i32), vp]
+    L.kvq_decode_partials_bytes.restype = ctypes.c_size_t
+    L.kvq_decode_partials_bytes.argtypes = [i32, i32, i32, i32]
+    L.kvq_decode_combine.restype = ctypes.c_int
+    L.kvq_decode_combine.argtypes = [vp, ctypes.c_size_t, i32, i32, i32, i32, vp, vp]
     L.kvq_decode_attn_residual.restype = ctypes.c_int
     L.kvq_decode_attn_residual.argtypes = [P, vp, i32, ctypes.c_float, vp, vp, ctypes.c_int, vp, vp,
                                            i32, vp, vp, ctypes.c_size_t, vp]
@@ -235,6 +243,37 @@ def decode_attn_split(cache_a, cache_b, q, softmax_scale, out=None, workspace=No
     st = load().kvq_decode_attn_split(ctypes.byref(cache_a.s), ctypes.byref(cache_b.s), _ptr(q), q.shape[1],
                                       float(softmax_scale), _ptr(out), _ptr(ws), ws.numel(), _stream_ptr(stream))
     _check(st, "kvq_decode_attn_split")
+    return out
+
+
+def partials_bytes(batch, n_kv_heads, n_q_heads, n_slots):
+    """kvq_decode_partials_bytes: bytes of n_slots partial slots per stream
+    (0 for invalid arguments)."""
+    return int(load().kvq_decode_partials_bytes(batch, n_kv_heads, n_q_heads, n_slots))
+
+
+def partials_views(ws, batch, n_kv_heads, n_q_heads, n_slots):
+    """(ml, o) float32 views of a partials workspace: ml [B*Hkv][n_slots][G][2],
+    o [B*Hkv][n_slots][G][128]."""
+    import torch
+    G = n_q_heads // n_kv_heads
+    BH = batch * n_kv_heads
+    n_ml = BH * n_slots * G * 2
+    o_off = (n_ml * 4 + 255) // 256 * 256
+    f = ws[:partials_bytes(batch, n_kv_heads, n_q_heads, n_slots)]
+    ml = f[:n_ml * 4].view(torch.float32).view(BH, n_slots, G, 2)
+    o = f[o_off:o_off + BH * n_slots * G * 128 * 4].view(torch.float32).view(BH, n_slots, G, 128)
+    return ml, o
+
+
+def decode_combine(ws, batch, n_kv_heads, n_q_heads, n_slots, out=None, stream=None):
+    """kvq_decode_combine: the partial slots in ws -> out [B][Hq][128] float32."""
+    import torch
+    if out is None:
+        out = torch.empty((batch, n_q_heads, 128), dtype=torch.float32, device=ws.device)
+    st = load().kvq_decode_combine(_ptr(ws), ws.numel(), batch, n_kv_heads, n_q_heads, n_slots, _ptr(out),
+                                   _stream_ptr(stream))
+    _check(st, "kvq_decode_combine")
     return out
 
 
@@ -451,6 +490,19 @@ class PackedCache:
                                              ws.numel(), _stream_ptr(stream))
         _check(st, "kvq_decode_attn_residual")
         return out
+
+    def decode_partials(self, q, softmax_scale, workspace=None, stream=None):
+        """kvq_decode_attn_partials: the chunk partials of the packed cache in
+        workspace -> (n_slots, tiles_per_slot)."""
+        import torch
+        assert q.dtype == torch.bfloat16 and q.is_contiguous()
+        ws = workspace if workspace is not None else self.workspace(q.shape[1])
+        ns, tps = ctypes.c_int32(0), ctypes.c_int32(0)
+        st = load().kvq_decode_attn_partials(ctypes.byref(self.s), _ptr(q), q.shape[1], float(softmax_scale),
+                                             _ptr(ws), ws.numel(), ctypes.byref(ns), ctypes.byref(tps),
+                                             _stream_ptr(stream))
+        _check(st, "kvq_decode_attn_partials")
+        return ns.value, tps.value
 
     def quantize_tokens(self, k, v, tok, t0=0, stream=None):
         """kvq_quantize_tokens: k, v [B][H][n_src][128] float32 / bfloat16

@@ -240,6 +240,51 @@ def test_decode_workspace_bytes_cover_the_partials():
             assert need <= got <= need + 512, (B, H, T, G, got, need)
 
 
+def test_two_phase_decode_sizes_and_validation():
+    """kvq_decode_partials_bytes: the (max, sum) pairs rounded up to 256
+    bytes, then 512 bytes per head and slot; the partials and combine calls
+    reject bad arguments on the host."""
+    L = _lib()
+    vp, P = ctypes.c_void_p, ctypes.byref
+    for B, H, Hq, n in [(16, 4, 28, 16), (1, 8, 32, 64), (3, 5, 5, 1), (2, 2, 32, 128)]:
+        BH, G = B * H, Hq // H
+        want = (8 * BH * n * G + 255) // 256 * 256 + 512 * BH * n * G
+        assert L.kvq_decode_partials_bytes(B, H, Hq, n) == want
+    assert L.kvq_decode_partials_bytes(16, 4, 28, 0) == 0       # no slot
+    assert L.kvq_decode_partials_bytes(16, 4, 28, 129) == 0     # past the combine's 128
+    assert L.kvq_decode_partials_bytes(16, 4, 30, 16) == 0      # not a multiple of the kv heads
+    assert L.kvq_decode_partials_bytes(1, 1, 17, 16) == 0       # G > 16
+    comb = L.kvq_decode_combine
+    need = L.kvq_decode_partials_bytes(2, 2, 8, 16)
+    assert comb(vp(FAKE), need, 2, 2, 8, 0, vp(FAKE), None) == kvq.EINVAL
+    assert comb(vp(FAKE), need, 2, 2, 8, 129, vp(FAKE), None) == kvq.EINVAL
+    assert comb(vp(FAKE), need, 2, 2, 7, 16, vp(FAKE), None) == kvq.EINVAL
+    assert comb(vp(FAKE), need, 2, 2, 8, 16, None, None) == kvq.EINVAL
+    assert comb(vp(FAKE), need, 2, 2, 8, 16, vp(FAKE + 4), None) == kvq.EINVAL     # out not 16-byte aligned
+    assert comb(None, need, 2, 2, 8, 16, vp(FAKE), None) == kvq.EWORKSPACE
+    assert comb(vp(FAKE), need - 4, 2, 2, 8, 16, vp(FAKE), None) == kvq.EWORKSPACE
+    assert comb(vp(FAKE + 128), need, 2, 2, 8, 16, vp(FAKE), None) == kvq.EWORKSPACE  # not 256-byte aligned
+    assert comb(vp(FAKE), need, 1, 1, 17, 16, vp(FAKE), None) == kvq.EUNSUPPORTED
+    part = L.kvq_decode_attn_partials
+    s = _fake_struct(2, 2, 1024, 4, 4)
+    s.n_tokens = 512
+    ws = L.kvq_decode_workspace_bytes(P(s), 8)
+    ns, tps = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    assert part(P(s), vp(FAKE), 8, 0.088, None, ws, P(ns), P(tps), None) == kvq.EWORKSPACE
+    assert part(P(s), vp(FAKE), 8, 0.088, vp(FAKE), ws - 4, P(ns), P(tps), None) == kvq.EWORKSPACE
+    assert part(P(s), vp(FAKE), 8, 0.088, vp(FAKE), ws, None, P(tps), None) == kvq.EINVAL
+    assert part(P(s), vp(FAKE), 8, 0.088, vp(FAKE), ws, P(ns), None, None) == kvq.EINVAL
+    assert part(P(s), vp(FAKE), 7, 0.088, vp(FAKE), ws, P(ns), P(tps), None) == kvq.EINVAL
+    assert part(P(s), vp(FAKE), 8, float("inf"), vp(FAKE), ws, P(ns), P(tps), None) == kvq.EINVAL
+    assert part(P(s), vp(FAKE), 2 * 17, 0.088, vp(FAKE), ws, P(ns), P(tps), None) == kvq.EUNSUPPORTED
+    s4 = _fake_struct(2, 2, 1024, 4, 2)                      # K4/V2 is not built
+    s4.n_tokens = 512
+    assert part(P(s4), vp(FAKE), 8, 0.088, vp(FAKE), ws, P(ns), P(tps), None) == kvq.EUNSUPPORTED
+    s5 = _fake_struct(2, 2, 1024, 4, 4)                      # empty cache
+    assert part(P(s5), vp(FAKE), 8, 0.088, vp(FAKE), ws, P(ns), P(tps), None) == kvq.EINVAL
+    assert ns.value == -1 and tps.value == -1                # untouched on failure
+
+
 def _fake_window(s, dtype=kvq.BF16, keep_first=1):
     w = kvq.KvqWindowStruct()
     w.batch, w.n_kv_heads, w.dtype, w.keep_first = s.batch, s.n_kv_heads, dtype, keep_first
