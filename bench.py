@@ -33,14 +33,14 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, profiles/decode_kernel_*.md)
 # for the kernel source with the given digest, and the factors that map each
 # counter onto true bytes: a plain 512 MiB device copy in the same run reads
-# FETCH_SIZE = 262159.1 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
-# fetch counter is scaled by 524288/262159.1 and the write counter by 1.  The
+# FETCH_SIZE = 262159.4 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
+# fetch counter is scaled by 524288/262159.4 and the write counter by 1.  The
 # figure is reported only while the kernel source is unchanged.
 COUNTER_TRAFFIC = {
-    "source_sha256": "98f89a7f1cfd7d9a53e19fd53973520a74cece3fa8aa7b83c5359dd902ab717e",
-    "fetch_kib": 139895.2,
+    "source_sha256": "a89f519d73111c58b9b6f61f39e9349211d99bbac275d8962df5ad64df8ad0a0",
+    "fetch_kib": 139900.5,
     "write_kib": 3664.0,
-    "fetch_factor": 524288.0 / 262159.1,
+    "fetch_factor": 524288.0 / 262159.4,
     "write_factor": 1.0,
 }
 KERNEL_SOURCES = ("kv_cache_mixed_amd/csrc/decode_attn.hip", "kv_cache_mixed_amd/csrc/kvq_device.h")
@@ -51,6 +51,9 @@ def _parse():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--settle-ms", type=float, default=1000.0,
+                    help="untimed back-to-back steps before the warmup steps (GPU clocks ramp up over "
+                         "the first tens of ms of sustained work)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-rows", action="store_true", help="time only the decode step")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
@@ -165,9 +168,27 @@ def time_events(torch, fn, n, warmup):
     return sum(ms) / len(ms), ms[len(ms) // 2]
 
 
-def time_block(torch, fn, n, warmup):
+def settle(torch, fn, ms):
+    """fn(i) back to back for about ms milliseconds (untimed): the GPU's
+    clocks ramp up over the first tens of milliseconds of sustained work, and
+    drop again within milliseconds of idling"""
+    t0 = time.perf_counter()
+    i = 0
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(20):
+            fn(i)
+            i += 1
+        torch.cuda.synchronize()
+
+
+ROW_SETTLE_MS = 200.0   # untimed calls before each row's timing loop (--settle-ms / 5)
+
+
+def time_block(torch, fn, n, warmup, settle_ms=None):
     """average duration of fn() over n calls issued back to back between one
-    pair of HIP events (throughput of a stream of calls)"""
+    pair of HIP events (throughput of a stream of calls), after settle_ms
+    (default ROW_SETTLE_MS) of untimed calls and the warmup calls"""
+    settle(torch, fn, ROW_SETTLE_MS if settle_ms is None else settle_ms)
     for i in range(warmup):
         fn(i)
     torch.cuda.synchronize()
@@ -213,7 +234,8 @@ def mixed_128k_rows(torch, kvq, synth, dev, scale, vb=2):
     d_ms = time_block(torch, lambda i: caches[i % nc].decode_attn(q, scale, out=outs[i % nc], workspace=wss[i % nc]),
                       40, 4)
     tag = "mixed_kv_128k" if vb == 0 else "mixed_128k"
-    return {"quantize_" + tag: {"ms": round(q_ms, 4), "GB/s": round(q_bytes / q_ms / 1e6, 1), "bytes": q_bytes},
+    return {"quantize_" + tag: {"ms": round(q_ms, 4), "GB/s": round(q_bytes / q_ms / 1e6, 1), "bytes": q_bytes,
+                                "pct_of_peak": round(100 * q_bytes / q_ms / 1e6 / PEAK_HBM_GBS, 2)},
             "decode_" + tag: {"ms": round(d_ms, 4), "GB/s": round(alg / d_ms / 1e6, 1), "bytes": alg,
                                   "pct_of_peak": round(100 * alg / d_ms / 1e6 / PEAK_HBM_GBS, 2),
                                   "tokens_per_s": round(B / (d_ms * 1e-3), 1),
@@ -383,7 +405,8 @@ def progressive_rows(torch, kvq, synth, dev, scale):
         ms = sum(tms) / len(tms)
         # read both tiles at b bits, write both halves at b/2; read and write S'
         nbytes = B * H * (t0 // 128) * (2 * 2048 * b + 2 * 2048 * (b // 2)) + 2 * 2 * B * H * t0 * 2
-        ev["ers_kernel"] = {"ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1), "bytes": nbytes}
+        ev["ers_kernel"] = {"ms": round(ms, 4), "GB/s": round(nbytes / ms / 1e6, 1), "bytes": nbytes,
+                            "pct_of_peak": round(100 * nbytes / ms / 1e6 / PEAK_HBM_GBS, 2)}
         del src, sh
     del inp
     torch.cuda.empty_cache()
@@ -440,7 +463,7 @@ def qwen32b_step_rows(torch, kvq, synth, dev, scale, n_steps=5):
     def step(i):
         for c, q in zip(caches, qs):
             c.decode_attn(q, scale, out=out, workspace=ws)
-    step(0)
+    settle(torch, step, 1.5 * ROW_SETTLE_MS)
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -571,7 +594,9 @@ def cpu_baseline(inp, B, H, Hq, k_bits, pdt, seconds):
 
 
 def main():
+    global ROW_SETTLE_MS
     args = _parse()
+    ROW_SETTLE_MS = args.settle_ms / 5
     if args.case:
         decode_case(args.case, args.steps, args.warmup)
         return
@@ -603,7 +628,7 @@ def main():
     q_ms, _ = time_events(torch, quant, 5 if not args.no_rows else 1, 1)
     q_bytes = 2 * B * H * T * 128 * 4 + decode_bytes(B, H, 0, T, BITS, BITS, 2)
     rows["quantize_k_v_4bit"] = {"ms": round(q_ms, 4), "GB/s": round(q_bytes / q_ms / 1e6, 1),
-                                 "bytes": q_bytes}
+                                 "bytes": q_bytes, "pct_of_peak": round(100 * q_bytes / q_ms / 1e6 / PEAK_HBM_GBS, 2)}
     del kd, vd
     torch.cuda.empty_cache()
 
@@ -624,6 +649,7 @@ def main():
         j = i % len(caches)
         caches[j].decode_attn(q, scale, out=outs[j], workspace=wss[j])
 
+    settle(torch, step, args.settle_ms)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -640,9 +666,23 @@ def main():
     ev1.record(st)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    kern_avg = ev0.elapsed_time(ev1) / args.steps      # one decode call: main + combine kernel
+    call_avg = ev0.elapsed_time(ev1) / args.steps      # one decode call: main + combine kernel
     ms_per_step = wall * 1e3 / args.steps
     value = alg / (ms_per_step * 1e-3) / 1e9
+
+    # the dominant kernel alone: K calls of the first phase of the C ABI
+    # (kvq_decode_attn_partials: the decode kernel only) back to back over the
+    # same rotated copies, between one pair of HIP events on the launch
+    # stream.  An event pair around every single launch would add the idle
+    # launch latency that back-to-back launches hide.
+    n_slots = []
+
+    def part(i):
+        j = i % len(caches)
+        n_slots.append(caches[j].decode_partials(q, scale, workspace=wss[j])[0])
+
+    # median of three rounds, each right after the previous (no idle time)
+    kern_avg = sorted(time_block(torch, part, args.steps, args.warmup, 0.0 if r else 50.0) for r in range(3))[1]
     achieved = alg / (kern_avg * 1e-3) / 1e9
 
     # ---- other rows of the path
@@ -669,7 +709,7 @@ def main():
         s_ms = sum(tms) / len(tms)
         s_bytes = B * H * (T // 128) * (2 * 8192 + 2 * 4096) + 2 * 2 * B * H * T * 2
         rows["ers_shrink_4to2"] = {"ms": round(s_ms, 4), "GB/s": round(s_bytes / s_ms / 1e6, 1),
-                                   "bytes": s_bytes}
+                                   "bytes": s_bytes, "pct_of_peak": round(100 * s_bytes / s_ms / 1e6 / PEAK_HBM_GBS, 2)}
         a2 = decode_bytes(B, H, Hq, T, 2, 2, 2)
         shs = [sh] + [sh.clone() for _ in range(max(2, math.ceil(600e6 / a2)) - 1)]
         n2 = len(shs)
@@ -721,7 +761,7 @@ def main():
             wk, wv = w.residual()
             caches[i % nc].decode_attn(q, scale, out=outs[i % nc], workspace=wss[i % nc], res_k=wk, res_v=wv)
 
-        dw_ms = time_block(torch, window_step, 60, 5)
+        dw_ms = time_block(torch, window_step, 60, 5, settle_ms=0.0)   # 65 tokens: no untimed calls beyond the warmup
         d1_ms = time_block(torch, lambda i: caches[i % nc].decode_attn(q, scale, out=outs[i % nc],
                                                                        workspace=wss[i % nc]), 60, 5)
         rows["decode_step_window_append"] = {
@@ -771,10 +811,17 @@ def main():
         "algorithmic_bytes_per_step": alg,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBS,
                      "unit": "GB/s", "frac": round(achieved / PEAK_HBM_GBS, 4), "traffic": counter_traffic(),
-                     "kernel": "decode_kernel<4,4,f16,2> + decode_combine_kernel",
-                     "kernel_ms_avg": round(kern_avg, 5)},
+                     "kernel": "decode_kernel<4,4,f16,2>",
+                     "kernel_ms_avg": round(kern_avg, 5),
+                     "call_ms_avg": round(call_avg, 5),
+                     "call_frac": round(alg / (call_avg * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+                     "partial_slots": n_slots[-1],
+                     "note": "achieved: algorithmic bytes of one call over the decode kernel's average "
+                             "launch time (K kvq_decode_attn_partials calls back to back between HIP events); "
+                             "call_frac: over the whole call (decode + combine kernels)"},
         "rows": rows,
         "cpu_baseline": cpu,
+        "settle_ms": args.settle_ms,
     }
     print(json.dumps(line))
 
