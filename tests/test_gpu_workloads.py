@@ -53,11 +53,20 @@ def test_qwen7b_layer_full_size():
     kd, vd = to_dev(inp["k"], torch), to_dev(inp["v"], torch)
     cache.quantize(kd, vd, 0)
     del kd, vd
-    out = cache.decode_attn(q_to_dev(inp["q_bf16"], torch), SCALE).cpu().numpy()
+    q = q_to_dev(inp["q_bf16"], torch)
+    out = cache.decode_attn(q, SCALE).cpu().numpy()
     assert np.isfinite(out).all()
     worst = _check_streams(cache, inp, out, [(0, 0), (3, 1), (7, 2), (10, 3), (15, 0), (15, 3)],
                            4, 4, kvq.F16, Hq // H, what="qwen7b")
     print("qwen7b worst row rel err %.3e" % worst, flush=True)
+    # the benchmark times the decode kernel alone through the first phase of
+    # the two-phase entry points: the same plan, so the two phases reproduce
+    # the call bit for bit
+    ws = cache.workspace(Hq)
+    n, tps = cache.decode_partials(q, SCALE, workspace=ws)
+    assert n == 16 and tps == 16
+    two = kvq.decode_combine(ws, B, H, Hq, n).cpu().numpy()
+    assert np.array_equal(two.view(np.uint32), out.view(np.uint32))
 
 
 def _progressive_oracle(inp, b, h, events, t_end, pdt):
