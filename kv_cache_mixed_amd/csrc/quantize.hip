@@ -18,7 +18,7 @@
 // One workgroup (256 threads) per (tile, kv head, batch).  The input tile is
 // read once with coalesced loads; key codes are staged in LDS as uint16 and
 // written as packed rows with coalesced 32-bit stores, value codes are packed
-// in registers.
+// into words in registers and written through LDS as 16-byte stores.
 #pragma clang fp contract(off)
 
 #include "kvq_device.h"
@@ -221,8 +221,9 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __re
 // its row (four DPP steps).  Each lane packs the codes of its 8 channels for
 // the row's 8 tokens into value words in registers: a row fills whole words
 // at b >= 4; at b = 2 (1) two (four) rows share a word and are merged by lane
-// swaps -- no LDS staging.  VEC: the input allows 16-byte (F32) / 8-byte
-// (BF16) loads of 4 channels.
+// swaps.  The finished words pass through LDS only to leave as 16-byte stores
+// in tile order.  VEC: the input allows 16-byte (F32) / 8-byte (BF16) loads
+// of 4 channels.
 // ---------------------------------------------------------------------------
 // min / max over each 16-lane row of the wave, result in every lane:
 // quad_perm xor 1 and xor 2, row_half_mirror, row_mirror (DPP, fused into the
@@ -325,8 +326,12 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __re
     }
   }
   const bool writer = (VB >= 4) || (VB == 2 ? (row & 1) == 0 : row == 0);
+  // the words go to LDS at their tile positions, then out with 16-byte
+  // stores that cover the tile in order (storing each word from its register
+  // scatters a wave's stores over the tile: 4.5% slower at 4 and 2 bits)
+  constexpr int TW = 32 * VB * 16;   // words per tile (2048 * VB bytes / 4)
+  __shared__ __attribute__((aligned(16))) uint32_t tw[TW];
   if (writer) {
-    uint32_t* out = (uint32_t*)(g.v_codes + v_tile_offset(g, b, h, tile));
 #pragma unroll
     for (int k = 0; k < 8; k++) {
       // channel c = 64 hh + 16 q + n
@@ -334,9 +339,16 @@ __global__ __launch_bounds__(256) void quantize_v_kernel(Geo g, const void* __re
 #pragma unroll
       for (int lw = 0; lw < RW; lw++) {
         const int w = (VB >= 4) ? (8 * row) / PW + lw : (8 * row) / PW;
-        out[w * 512 + ((hh * 16 + n) * 4 + wave) * 4 + q] = wd[k][lw];
+        tw[w * 512 + ((hh * 16 + n) * 4 + wave) * 4 + q] = wd[k][lw];
       }
     }
+  }
+  __syncthreads();
+  {
+    uint32_t* out = (uint32_t*)(g.v_codes + v_tile_offset(g, b, h, tile));
+    typedef uint32_t u4 __attribute__((ext_vector_type(4)));
+#pragma unroll
+    for (int o = threadIdx.x * 4; o < TW; o += 1024) *(u4*)(out + o) = *(const u4*)(tw + o);
   }
 }
 
