@@ -191,8 +191,10 @@ typedef struct kvq_cache {
     const int16_t *k_slot_chan; /* device [Hkv][128]: channel held by slot j
                                    (mixed keys only, a permutation per head;
                                    the kernels use only its low 7 bits, so a
-                                   map that is not a permutation reads wrong
-                                   channels but never outside a row) */
+                                   map that is not a permutation gives wrong
+                                   or unspecified codes for some slots but no
+                                   access outside a row, a tile or its
+                                   parameters) */
     const int16_t *v_slot_chan; /* device [Hkv][128]: channel held by value
                                    slot j (mixed values only; same rules) */
 } kvq_cache;

@@ -159,11 +159,16 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __re
   __shared__ uint16_t codes[128 * 128];
   __shared__ float red_mn[2][128], red_mx[2][128];
   __shared__ int64_t rows[GATHER ? 128 : 1];
+  __shared__ uint8_t slot_of[KB == 0 ? 128 : 1];
   const int tile_local = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tile = t0 / 128 + tile_local;
+  // thread (j, half) reads channel j, so a wave's loads cover whole rows
+  // whatever the slot map; mixed keys quantize channel j as the slot the map
+  // gives it (the inverse of slot -> channel, built in LDS; entries are used
+  // through their low 7 bits, so a map that is not a permutation leaves some
+  // slots unspecified but every access inside the tile and its parameters)
   const int j = threadIdx.x & 127, half = threadIdx.x >> 7;
-  const int chan = (KB == 0) ? ((int)g.slot_chan[h * 128 + j] & 127) : j;   // masked: never outside the row
-  const int bits = (KB == 0) ? mixed_slot_bits(j) : KB;
+  const int chan = j;
 
   float x[64];
   if constexpr (GATHER) {
@@ -177,6 +182,14 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __re
 #pragma unroll
     for (int i = 0; i < 64; i++) x[i] = load_in<IN>(kin, base + (int64_t)(half * 64 + i) * st);
   }
+  // (the slot map is read while the tile's loads are in flight)
+  int slot = j;
+  if constexpr (KB == 0) {
+    if (threadIdx.x < 128) slot_of[(int)g.slot_chan[h * 128 + threadIdx.x] & 127] = (uint8_t)threadIdx.x;
+    __syncthreads();
+    slot = slot_of[j] & 127;
+  }
+  const int bits = (KB == 0) ? mixed_slot_bits(slot) : KB;
   float mn = x[0], mx = x[0];
 #pragma unroll
   for (int i = 1; i < 64; i++) {
@@ -195,7 +208,7 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __re
   const float sp = Param<PDT>::narrow(s);
   const float zp = Param<PDT>::narrow(mn);
   if (half == 0) {
-    const int64_t pi = k_param_base(g, b, h, tile) + j;
+    const int64_t pi = k_param_base(g, b, h, tile) + slot;
     Param<PDT>::store(g.k_scale, pi, s);
     Param<PDT>::store(g.k_zero, pi, mn);
   }
@@ -204,7 +217,7 @@ __global__ __launch_bounds__(256) void quantize_k_kernel(Geo g, const void* __re
     uint32_t q[8];
     quant_codes<KB <= 8, 8>(&x[i], sp, zp, levels, q);
 #pragma unroll
-    for (int k = 0; k < 8; k++) codes[(half * 64 + i + k) * 128 + j] = (uint16_t)q[k];
+    for (int k = 0; k < 8; k++) codes[(half * 64 + i + k) * 128 + slot] = (uint16_t)q[k];
   }
   __syncthreads();
   uint8_t* dst = g.k_codes + k_tile_offset(g, b, h, tile);
