@@ -385,11 +385,9 @@ __global__ __launch_bounds__(256) void quantize_vmixed_kernel(Geo g, const void*
   __shared__ float xs[64][129];
   __shared__ __attribute__((aligned(16))) uint8_t codes[128][128];   // [slot][token]
   __shared__ float bmn[8][64], bmx[8][64];                            // [block][token]
-  __shared__ int chan[128];
   const int tile_local = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int tile = t0 / 128 + tile_local;
-  const int wave = threadIdx.x >> 6, r = threadIdx.x & 63;
-  if (threadIdx.x < 128) chan[threadIdx.x] = (int)g.v_slot_chan[h * 128 + threadIdx.x] & 127;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), r = threadIdx.x & 63;
   const int64_t base = (int64_t)b * sb + (int64_t)h * sh + (GATHER ? 0 : (int64_t)(tile_local * 128) * st);
   // item i of half hf = token row 64 hf + i / 32, channels 4 (i % 32) ..
   float xin[2][8][4];
@@ -402,6 +400,13 @@ __global__ __launch_bounds__(256) void quantize_vmixed_kernel(Geo g, const void*
       const int64_t row = GATHER ? src_row(ti, b, h, g.H, tile_local * 128 + t) : (int64_t)t;
       load4<IN, VEC>(vin, base + row * st + (i & 31) * 4, xin[hf][k]);
     }
+  // the channels of the wave's two slot blocks (the same for every lane:
+  // scalar registers)
+  int chan[2][16];
+#pragma unroll
+  for (int u = 0; u < 2; u++)
+#pragma unroll
+    for (int j = 0; j < 16; j++) chan[u][j] = (int)g.v_slot_chan[h * 128 + 16 * (wave + 4 * u) + j] & 127;
 #pragma unroll
   for (int half = 0; half < 2; half++) {
 #pragma unroll
@@ -419,7 +424,7 @@ __global__ __launch_bounds__(256) void quantize_vmixed_kernel(Geo g, const void*
       float mn, mx;
 #pragma unroll
       for (int j = 0; j < 16; j++) {
-        x[u][j] = xs[r][chan[16 * m + j]];
+        x[u][j] = xs[r][chan[u][j]];
         mn = j ? fminf(mn, x[u][j]) : x[u][j];
         mx = j ? fmaxf(mx, x[u][j]) : x[u][j];
       }
