@@ -56,6 +56,23 @@ def test_pair_norms_strided_and_accumulated():
     assert np.allclose(out.cpu().numpy(), ref, rtol=NORM_RTOL, atol=0)
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_pair_norms_unaligned_rows(dtype):
+    """Token rows 130 elements apart and a base 2 elements into the buffer
+    (no alignment beyond the element)."""
+    print("case pair norms unaligned %s" % dtype, flush=True)
+    rng = np.random.default_rng(46)
+    big = rng.standard_normal((1, 3, 300, 130)).astype(np.float32)
+    bd = to_dev(big, torch)
+    if dtype == "bf16":
+        bd = bd.to(torch.bfloat16)
+        big = bd.float().cpu().numpy()
+    view = bd[:, :, :, 2:]                      # [1][3][300][128], row stride 130
+    out = kvq.pair_norms(view, 1)
+    ref = oracle.pair_norms(big[:, :, :, 2:], 1)
+    assert np.allclose(out.cpu().numpy(), ref, rtol=NORM_RTOL, atol=0)
+
+
 @pytest.mark.parametrize("v_bits", [2, 4])
 def test_pn_mix_chain(v_bits):
     """Pairs recipe: scores from the GPU pair norms of the prefill queries and
