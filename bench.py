@@ -603,7 +603,7 @@ def main():
         decode_case(args.case, args.steps, args.warmup)
         return
     if args.gpus != 1:
-        print("bench.py runs on exactly one GPU: this build has no multi-GPU path "
+        print("bench.py runs on exactly one GPU: the library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
     import numpy as np

@@ -142,7 +142,7 @@ extern "C" {
 typedef enum {
     KVQ_OK = 0,
     KVQ_EINVAL = 1,        /* invalid argument (null pointer, bad size, bad width ...) */
-    KVQ_EUNSUPPORTED = 2,  /* valid request this build does not implement */
+    KVQ_EUNSUPPORTED = 2,  /* valid request the library does not implement */
     KVQ_EBUDGET = 3,       /* kvq_append / kvq_window_append / kvq_allocate_bits: the budget or the pool cannot hold it */
     KVQ_EWORKSPACE = 4,    /* workspace pointer null or smaller than required */
     KVQ_EHIP = 5           /* a HIP runtime call or kernel launch failed */
