@@ -86,12 +86,18 @@ CASES = {
     "qwen32b_layer_8bit": (16, 8, 40, 32768, 8, 8, "F16"),
     "llama8b_mixed_128k": (1, 8, 32, 131072, 0, 2, "E4M3"),
     "llama8b_mixed_kv_128k": (1, 8, 32, 131072, 0, 0, "E4M3"),
+    "llama8b_mixed_32k_b8": (8, 8, 32, 32768, 0, 2, "E4M3"),
 }
 
 
 def decode_case(name, steps, warmup):
     """decode calls of one workload over rotated cache copies (> 600 MB
     together); prints one JSON line with the event-timed call average"""
+    print(json.dumps(decode_case_row(name, steps, warmup)))
+
+
+def decode_case_row(name, steps, warmup):
+    """the timing of decode_case() as a dict"""
     import torch
     from kv_cache_mixed_amd import kvq, synth
     kvq.load()
@@ -123,9 +129,11 @@ def decode_case(name, steps, warmup):
     nc = len(caches)
     ms = time_block(torch, lambda i: caches[i % nc].decode_attn(q, scale, out=outs[i % nc], workspace=wss[i % nc]),
                     steps, warmup)
-    print(json.dumps({"case": name, "ms": round(ms, 5), "GB/s": round(alg / ms / 1e6, 1),
-                      "pct_of_peak": round(100 * alg / ms / 1e6 / PEAK_HBM_GBS, 2), "bytes": alg,
-                      "copies": nc, "steps": steps}))
+    del caches, outs, wss
+    torch.cuda.empty_cache()
+    return {"case": name, "ms": round(ms, 5), "GB/s": round(alg / ms / 1e6, 1),
+            "pct_of_peak": round(100 * alg / ms / 1e6 / PEAK_HBM_GBS, 2), "bytes": alg,
+            "copies": nc, "steps": steps}
 
 
 def kernel_source_digest():
@@ -772,6 +780,10 @@ def main():
                     "decode over the packed layer + the 1..22 held tokens"}
         del wins, nk, nv
         rows.update(mixed_128k_rows(torch, kvq, synth, dev, scale))
+        r8 = decode_case_row("llama8b_mixed_32k_b8", 40, 5)
+        r8["note"] = ("mixed keys, 2-bit values, e4m3 S/Z, B = 8 x 32768 tokens (two streams per wave); "
+                      "cache copies rotated")
+        rows["decode_mixed_32k_b8"] = r8
         rows.update(mixed_128k_rows(torch, kvq, synth, dev, scale, vb=0))
         rows.update(pn_mix_rows(torch, kvq, synth, dev, scale))
         rows.update(semkv_split_rows(torch, kvq, synth, dev, scale))

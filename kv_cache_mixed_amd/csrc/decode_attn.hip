@@ -57,6 +57,11 @@
 #ifndef KVQ_DECODE_WAVES_PER_SIMD
 #define KVQ_DECODE_WAVES_PER_SIMD 0
 #endif
+// mixed keys and 2-bit values with several streams per wave prefetch one
+// sub-tile ahead in a single buffer (1) or two ahead in two buffers (0)
+#ifndef KVQ_DECODE_PF1
+#define KVQ_DECODE_PF1 1
+#endif
 // folded query operand kept in registers across a tile's sub-tiles (1) or
 // staged in the wave's LDS region (0)
 #ifndef KVQ_DECODE_QREG
@@ -627,6 +632,10 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // sub-tiles ahead (measured 7% faster with binary16 parameters, equal with
   // e4m3, at one wave per SIMD; two waves per SIMD spill even so)
   constexpr bool PJIT = VMIX;
+  // one prefetch buffer (operands one sub-tile ahead instead of two): mixed
+  // keys and 2-bit values with several streams per wave, where the second
+  // buffer's registers would spill
+  constexpr bool PF1 = KVQ_DECODE_PF1 && MIXED && VB == 2 && NS >= 2;
   constexpr int PWK = PW<PDT, 8>::W;                 // key-parameter words per 8 slots
   constexpr int KPA = 32 * PB;                       // words per 128 key parameters
   constexpr int KPL = (PB == 4) ? 2 : 1;             // of which one lane loads
@@ -739,10 +748,12 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   uint32_t* my_lds = lds[wave];
   // the folded query operand of the current tile, [k-step][hi/lo][4]: in
   // registers (QREG), or in the wave's LDS region where its 32 registers
-  // would spill: 16-bit keys (64 registers), 1-bit codes and two streams of
-  // 2-bit codes (measured 9% slower there, 3-5% faster at 4 bits), and
-  // binary32 parameters (twice the parameter registers)
-  constexpr bool QREG = KVQ_DECODE_QREG && KB != 16 && KB != 1 && !(KB == 2 && NS >= 2) && PDT != KVQ_F32 && !VMIX;
+  // would spill: 16-bit keys (64 registers), 1-bit codes, two streams of
+  // 2-bit codes (measured 9% slower there, 3-5% faster at 4 bits) or of mixed
+  // keys with 2-bit values (5% slower there), and binary32 parameters (twice
+  // the parameter registers)
+  constexpr bool QREG = KVQ_DECODE_QREG && KB != 16 && KB != 1 && !(KB == 2 && NS >= 2) &&
+                        !(MIXED && VB == 2 && NS >= 2) && PDT != KVQ_F32 && !VMIX;
   uint32_t qop[QREG ? NKK : 1][2][4];
 
   // one sub-tile of raw operands; value words travel outside the prefetch
@@ -1347,8 +1358,10 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     const int v = d == 0 ? q0 : (d == 1 ? q1 : (d == 2 ? q2 : q3));
     return v < t_count ? v : -1;
   };
-  // the second buffer: loads run two sub-tiles ahead of the computation
-  if (q0 < t_count && qk(1 / NSUB) >= 0) load(b1, qk(1 / NSUB), 1 % NSUB);
+  // the second buffer: loads run two sub-tiles ahead of the computation (one
+  // ahead, in the single buffer, for PF1 instances)
+  if constexpr (!PF1)
+    if (q0 < t_count && qk(1 / NSUB) >= 0) load(b1, qk(1 / NSUB), 1 % NSUB);
 #pragma unroll 1
   while (q0 < t_count) {
     if constexpr (KVQ_DECODE_PRIO != 0) {
@@ -1367,7 +1380,10 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       if constexpr (NSUB == 1) {
         if (u == 1 && q1 >= t_count) break;
       }
-      compute((u % 2 == 0) ? b0 : b1, qk(u / NSUB), u % NSUB, qk((u + 2) / NSUB), (u + 2) % NSUB);
+      if constexpr (PF1)
+        compute(b0, qk(u / NSUB), u % NSUB, qk((u + 1) / NSUB), (u + 1) % NSUB);
+      else
+        compute((u % 2 == 0) ? b0 : b1, qk(u / NSUB), u % NSUB, qk((u + 2) / NSUB), (u + 2) % NSUB);
     }
     if constexpr (TPI == 1) {
       q0 = q1; q1 = q2; q2 = q3;
@@ -1475,9 +1491,14 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #ifndef KVQ_DECODE_NS_MIN_TPC
 #define KVQ_DECODE_NS_MIN_TPC 16
 #endif
-// measured: two mixed-key streams per wave 30% slower, three 2x slower
+// streams per wave for mixed keys with 2-bit values.  Two, with one
+// prefetch buffer (PF1) and the folded query in LDS, fit two waves per SIMD
+// without spills: 12-18% faster than one stream on batched 32K and 128K
+// mixed-key layers (G = 4), the same at B = 4 x 128K; single sequences keep
+// one stream (too few tiles per chunk, KVQ_DECODE_NS_MIN_TPC).  With two
+// buffers they spilled and ran 30% slower; three streams 2x slower.
 #ifndef KVQ_DECODE_NS_CAP_MIXED2
-#define KVQ_DECODE_NS_CAP_MIXED2 1
+#define KVQ_DECODE_NS_CAP_MIXED2 2
 #endif
 constexpr int ns_cap(int kb, int vb) {
   if (kb == 0) return vb == 4 ? 2 : (vb == 2 ? KVQ_DECODE_NS_CAP_MIXED2 : 1);
@@ -1512,7 +1533,8 @@ static DecodePlan plan_for(int BH, int ns, int k_bits, int v_bits, int pdt, int 
 // the tiles, the prologue and partial write amortised over more work) is
 // faster.
 DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_tiles, int max_chunks) {
-  const int cap = ns_cap(k_bits, v_bits);
+  // (binary32 parameters of mixed keys with 2-bit values: one stream, two spill)
+  const int cap = (k_bits == 0 && v_bits == 2 && pdt == KVQ_F32) ? 1 : ns_cap(k_bits, v_bits);
   int ns = 16 / G;
   if (ns > KVQ_DECODE_NS_MAX) ns = KVQ_DECODE_NS_MAX;
   ns = ns > cap ? cap : (ns < 1 ? 1 : ns);

@@ -136,6 +136,33 @@ def test_progressive_schedule_full_size():
     assert cache.pool_high_water() <= budget
 
 
+@pytest.mark.parametrize("B,T,pdt,slots", [(2, 131072, kvq.E4M3, 64), (4, 65536, kvq.F16, 32)],
+                         ids=["b2_128k_e4m3", "b4_64k_f16"])
+def test_mixed_keys_two_streams_per_wave(B, T, pdt, slots):
+    """Batched mixed-key layers (G = 4) whose chunks are long enough for two
+    streams per wave: the plan's slot count says so (one stream per wave
+    would give half as many slots), sampled streams bit-exact and within the
+    attention tolerance, and the two decode phases reproduce the call."""
+    H, Hq = 8, 32
+    print("case mixed keys two streams B=%d T=%d pdt=%d" % (B, T, pdt), flush=True)
+    inp = synth.mixed_layer(B, H, Hq, T, seed=13 + B)
+    cache = kvq.PackedCache(B, H, T, kvq.KMIXED, 2, pdt, slot_chan=inp["slot_chan"])
+    kd, vd = to_dev(inp["k"], torch), to_dev(inp["v"], torch)
+    cache.quantize(kd, vd, 0)
+    del kd, vd
+    q = q_to_dev(inp["q_bf16"], torch)
+    out = cache.decode_attn(q, SCALE).cpu().numpy()
+    assert np.isfinite(out).all()
+    ws = cache.workspace(Hq)
+    n, tps = cache.decode_partials(q, SCALE, workspace=ws)
+    assert n == slots and n * tps == T // 128
+    two = kvq.decode_combine(ws, B, H, Hq, n).cpu().numpy()
+    assert np.array_equal(two.view(np.uint32), out.view(np.uint32))
+    worst = _check_streams(cache, inp, out, [(0, 0), (0, 3), (B - 1, 6), (B - 1, 7)], 0, 2, pdt, Hq // H,
+                           inp["slot_chan"], what="mixed two streams")
+    print("mixed two streams worst row rel err %.3e" % worst, flush=True)
+
+
 def test_llama_128k_mixed_full_size():
     """Mixed-width keys (8 x 4-bit, 8 x 3-bit, 8 x 1-bit, 104 x 2-bit per kv
     head), 2-bit values, e4m3 S/Z, one sequence of 131072 tokens: every stream
