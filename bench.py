@@ -33,14 +33,14 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, profiles/decode_kernel_*.md)
 # for the kernel source with the given digest, and the factors that map each
 # counter onto true bytes: a plain 512 MiB device copy in the same run reads
-# FETCH_SIZE = 262159.4 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
-# fetch counter is scaled by 524288/262159.4 and the write counter by 1.  The
+# FETCH_SIZE = 262158.9 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
+# fetch counter is scaled by 524288/262158.9 and the write counter by 1.  The
 # figure is reported only while the kernel source is unchanged.
 COUNTER_TRAFFIC = {
-    "source_sha256": "a89f519d73111c58b9b6f61f39e9349211d99bbac275d8962df5ad64df8ad0a0",
-    "fetch_kib": 139900.5,
+    "source_sha256": "b66e0b2c8abe7aff25733196439351bfa2482791e40e07bb82748e4802170e78",
+    "fetch_kib": 139901.5,
     "write_kib": 3664.0,
-    "fetch_factor": 524288.0 / 262159.4,
+    "fetch_factor": 524288.0 / 262158.9,
     "write_factor": 1.0,
 }
 KERNEL_SOURCES = ("kv_cache_mixed_amd/csrc/decode_attn.hip", "kv_cache_mixed_amd/csrc/kvq_device.h")

@@ -62,6 +62,26 @@
 #ifndef KVQ_DECODE_PF1
 #define KVQ_DECODE_PF1 1
 #endif
+// uniform 2-bit codes: most streams per wave, waves per SIMD of three-stream
+// instances, and the stream count from which they prefetch through a single
+// buffer (0: never).  Two-stream 2-bit instances with one buffer fit 241
+// registers instead of spilling at 256 and run 18-20% faster (7B- and
+// 32B-shaped layers); three streams still spill.  4-bit (PF1_4BIT) with one
+// buffer measured mixed: 2.7% faster on the 7B-shaped layer, 1.7% slower on
+// the 32B-shaped one, 3% slower on one 128K sequence; and at three waves per
+// SIMD (with the folded query in LDS) 6% slower on the 7B-shaped layer.
+#ifndef KVQ_DECODE_NS_CAP_2BIT
+#define KVQ_DECODE_NS_CAP_2BIT 2
+#endif
+#ifndef KVQ_DECODE_NS3_OCC_2BIT
+#define KVQ_DECODE_NS3_OCC_2BIT 1
+#endif
+#ifndef KVQ_DECODE_PF1_2BIT
+#define KVQ_DECODE_PF1_2BIT 2
+#endif
+#ifndef KVQ_DECODE_PF1_4BIT
+#define KVQ_DECODE_PF1_4BIT 0
+#endif
 // folded query operand kept in registers across a tile's sub-tiles (1) or
 // staged in the wave's LDS region (0)
 #ifndef KVQ_DECODE_QREG
@@ -442,7 +462,7 @@ constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
   (void)pdt;
   if (KVQ_DECODE_WAVES_PER_SIMD) return KVQ_DECODE_WAVES_PER_SIMD;
   if (kb == 16 || (kb == 0 && vb <= 1) || ns >= 4) return 1;
-  if (ns == 3) return kb == 4 ? KVQ_DECODE_NS3_OCC : 1;
+  if (ns == 3) return kb == 4 ? KVQ_DECODE_NS3_OCC : (kb == 2 ? KVQ_DECODE_NS3_OCC_2BIT : 1);
   return 2;
 }
 
@@ -450,9 +470,12 @@ constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
 // into the 16 MFMA columns (column n serves stream n / G, head n % G).
 //
 // Main loop: the wave walks its tiles in sub-tiles of TPS tokens per lane
-// group.  Sub-tile operands (key blocks, value words, value parameters) are
-// double buffered in registers: the loads of the next sub-tile are issued
-// before the current one is computed.  All loads are raw buffer loads with an
+// group.  Sub-tile operands (key blocks, key and value parameters) are
+// double buffered in registers and loaded two sub-tiles ahead -- or, for the
+// two-stream instances of 2-bit codes and of mixed keys with 2-bit values
+// (PF1), single buffered and loaded one sub-tile ahead, which keeps them out
+// of spills; value words arrive at the start of their own sub-tile.  All
+// loads are raw buffer loads with an
 // SGPR base per (stream, tile) and lane offsets fixed for the whole kernel.
 // The folded query u = q * S_K * 2^k (split into f16 hi + lo) lives in LDS,
 // one 4-register group per k-step, computed once per tile.  Lanes of columns
@@ -635,7 +658,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // one prefetch buffer (operands one sub-tile ahead instead of two): mixed
   // keys and 2-bit values with several streams per wave, where the second
   // buffer's registers would spill
-  constexpr bool PF1 = KVQ_DECODE_PF1 && MIXED && VB == 2 && NS >= 2;
+  constexpr bool PF1 = KVQ_DECODE_PF1 && ((MIXED && VB == 2 && NS >= 2) ||
+                                          (KVQ_DECODE_PF1_2BIT && KB == 2 && NS >= KVQ_DECODE_PF1_2BIT) ||
+                                          (KVQ_DECODE_PF1_4BIT && KB == 4 && NS >= KVQ_DECODE_PF1_4BIT));
   constexpr int PWK = PW<PDT, 8>::W;                 // key-parameter words per 8 slots
   constexpr int KPA = 32 * PB;                       // words per 128 key parameters
   constexpr int KPL = (PB == 4) ? 2 : 1;             // of which one lane loads
@@ -1502,7 +1527,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #endif
 constexpr int ns_cap(int kb, int vb) {
   if (kb == 0) return vb == 4 ? 2 : (vb == 2 ? KVQ_DECODE_NS_CAP_MIXED2 : 1);
-  return (kb == 4 || kb == 2) ? KVQ_DECODE_NS_CAP_LOW : 1;
+  return kb == 4 ? KVQ_DECODE_NS_CAP_LOW : (kb == 2 ? KVQ_DECODE_NS_CAP_2BIT : 1);
 }
 
 // Launch plan (shared by workspace sizing, validation and launch): NS streams

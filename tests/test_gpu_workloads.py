@@ -163,6 +163,31 @@ def test_mixed_keys_two_streams_per_wave(B, T, pdt, slots):
     print("mixed two streams worst row rel err %.3e" % worst, flush=True)
 
 
+def test_qwen7b_layer_2bit_e4m3_two_streams_per_wave():
+    """The 7B-shaped layer at 2 bits with e4m3 parameters: two streams per
+    wave (16 slots of 16 tiles; one stream per wave would give 8), sampled
+    streams bit-exact and within the attention tolerance."""
+    B, H, Hq, T = 16, 4, 28, 32768
+    G = Hq // H
+    print("case qwen7b layer 2-bit e4m3", flush=True)
+    dev = synth.layer_device(B, H, Hq, T, seed=610, device="cuda")
+    cache = kvq.PackedCache(B, H, T, 2, 2, kvq.E4M3)
+    cache.quantize(dev["k"], dev["v"], 0)
+    out = cache.decode_attn(dev["q"], SCALE).cpu().numpy()
+    assert np.isfinite(out).all()
+    ws = cache.workspace(Hq)
+    n, tps = cache.decode_partials(dev["q"], SCALE, workspace=ws)
+    assert n == 16 and tps == 16
+    q_bits = dev["q"].view(torch.int16).cpu().numpy().view(np.uint16)
+    for b, h in [(0, 0), (7, 3), (15, 1)]:
+        k = dev["k"][b, h].cpu().numpy()
+        v = dev["v"][b, h].cpu().numpy()
+        st = oracle.quantize_stream(k, v, 2, 2, oracle.E4M3)
+        assert_stream_bytes_equal(cache, st, b, h, "qwen7b 2-bit e4m3")
+        err = rel_err_rows(out[b, h * G:(h + 1) * G], oracle_attn(st, q_bits[b, h * G:(h + 1) * G])).max()
+        assert err <= REL_TOL, "qwen7b 2-bit e4m3 stream (%d,%d) rel err %.3e" % (b, h, err)
+
+
 def test_llama_128k_mixed_full_size():
     """Mixed-width keys (8 x 4-bit, 8 x 3-bit, 8 x 1-bit, 104 x 2-bit per kv
     head), 2-bit values, e4m3 S/Z, one sequence of 131072 tokens: every stream
