@@ -82,6 +82,11 @@
 #ifndef KVQ_DECODE_PF1_4BIT
 #define KVQ_DECODE_PF1_4BIT 0
 #endif
+// mixed values through one prefetch buffer: 256 VGPRs + 83 AGPRs instead of
+// + 95, 21% faster (128K mixed-KV layer, e4m3 and binary16 parameters)
+#ifndef KVQ_DECODE_PF1_VMIX
+#define KVQ_DECODE_PF1_VMIX 1
+#endif
 // folded query operand kept in registers across a tile's sub-tiles (1) or
 // staged in the wave's LDS region (0)
 #ifndef KVQ_DECODE_QREG
@@ -458,10 +463,22 @@ __device__ __forceinline__ void pload(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 #ifndef KVQ_DECODE_NS3_OCC
 #define KVQ_DECODE_NS3_OCC 1
 #endif
+// waves per SIMD of the 16-bit instances and of mixed values.  At two, the
+// 16-bit instances fit 256 registers without spills but measured no faster
+// (32K and 8K layers), and mixed values spill 32 registers and run 7-140%
+// slower.
+#ifndef KVQ_DECODE_OCC16
+#define KVQ_DECODE_OCC16 1
+#endif
+#ifndef KVQ_DECODE_OCC_VMIX
+#define KVQ_DECODE_OCC_VMIX 1
+#endif
 constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
   (void)pdt;
   if (KVQ_DECODE_WAVES_PER_SIMD) return KVQ_DECODE_WAVES_PER_SIMD;
-  if (kb == 16 || (kb == 0 && vb <= 1) || ns >= 4) return 1;
+  if (kb == 16) return KVQ_DECODE_OCC16;
+  if (kb == 0 && vb == 0) return KVQ_DECODE_OCC_VMIX;
+  if ((kb == 0 && vb <= 1) || ns >= 4) return 1;
   if (ns == 3) return kb == 4 ? KVQ_DECODE_NS3_OCC : (kb == 2 ? KVQ_DECODE_NS3_OCC_2BIT : 1);
   return 2;
 }
@@ -472,9 +489,10 @@ constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
 // Main loop: the wave walks its tiles in sub-tiles of TPS tokens per lane
 // group.  Sub-tile operands (key blocks, key and value parameters) are
 // double buffered in registers and loaded two sub-tiles ahead -- or, for the
-// two-stream instances of 2-bit codes and of mixed keys with 2-bit values
-// (PF1), single buffered and loaded one sub-tile ahead, which keeps them out
-// of spills; value words arrive at the start of their own sub-tile.  All
+// two-stream instances of 2-bit codes and of mixed keys with 2-bit values and
+// for mixed values (PF1), single buffered and loaded one sub-tile ahead,
+// which keeps them out of spills; value words arrive at the start of their
+// own sub-tile.  All
 // loads are raw buffer loads with an
 // SGPR base per (stream, tile) and lane offsets fixed for the whole kernel.
 // The folded query u = q * S_K * 2^k (split into f16 hi + lo) lives in LDS,
@@ -656,11 +674,13 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // e4m3, at one wave per SIMD; two waves per SIMD spill even so)
   constexpr bool PJIT = VMIX;
   // one prefetch buffer (operands one sub-tile ahead instead of two): mixed
-  // keys and 2-bit values with several streams per wave, where the second
-  // buffer's registers would spill
+  // keys and 2-bit values or 2-bit codes with several streams per wave, where
+  // the second buffer's registers would spill, and mixed values, whose
+  // registers overflow into AGPRs
   constexpr bool PF1 = KVQ_DECODE_PF1 && ((MIXED && VB == 2 && NS >= 2) ||
                                           (KVQ_DECODE_PF1_2BIT && KB == 2 && NS >= KVQ_DECODE_PF1_2BIT) ||
-                                          (KVQ_DECODE_PF1_4BIT && KB == 4 && NS >= KVQ_DECODE_PF1_4BIT));
+                                          (KVQ_DECODE_PF1_4BIT && KB == 4 && NS >= KVQ_DECODE_PF1_4BIT) ||
+                                          (KVQ_DECODE_PF1_VMIX && VMIX));
   constexpr int PWK = PW<PDT, 8>::W;                 // key-parameter words per 8 slots
   constexpr int KPA = 32 * PB;                       // words per 128 key parameters
   constexpr int KPL = (PB == 4) ? 2 : 1;             // of which one lane loads
