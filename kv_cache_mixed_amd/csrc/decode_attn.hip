@@ -57,35 +57,19 @@
 #ifndef KVQ_DECODE_WAVES_PER_SIMD
 #define KVQ_DECODE_WAVES_PER_SIMD 0
 #endif
-// mixed keys and 2-bit values with several streams per wave prefetch one
-// sub-tile ahead in a single buffer (1) or two ahead in two buffers (0)
+// Operand prefetch: some instances load the next sub-tile's operands into a
+// single buffer (one sub-tile ahead), the others into two (two ahead); see
+// pf1_instance().  1: that choice; 0: two buffers everywhere.
 #ifndef KVQ_DECODE_PF1
 #define KVQ_DECODE_PF1 1
 #endif
-// uniform 2-bit codes: most streams per wave, waves per SIMD of three-stream
-// instances, and the stream count from which they prefetch through a single
-// buffer (0: never).  Two-stream 2-bit instances with one buffer fit 241
-// registers instead of spilling at 256 and run 18-20% faster (7B- and
-// 32B-shaped layers); three streams still spill.  4-bit (PF1_4BIT) with one
-// buffer measured mixed: 2.7% faster on the 7B-shaped layer, 1.7% slower on
-// the 32B-shaped one, 3% slower on one 128K sequence; and at three waves per
-// SIMD (with the folded query in LDS) 6% slower on the 7B-shaped layer.
+// uniform 2-bit codes: most streams per wave, and waves per SIMD of
+// three-stream instances (three streams spill even with one buffer)
 #ifndef KVQ_DECODE_NS_CAP_2BIT
 #define KVQ_DECODE_NS_CAP_2BIT 2
 #endif
 #ifndef KVQ_DECODE_NS3_OCC_2BIT
 #define KVQ_DECODE_NS3_OCC_2BIT 1
-#endif
-#ifndef KVQ_DECODE_PF1_2BIT
-#define KVQ_DECODE_PF1_2BIT 2
-#endif
-#ifndef KVQ_DECODE_PF1_4BIT
-#define KVQ_DECODE_PF1_4BIT 0
-#endif
-// mixed values through one prefetch buffer: 256 VGPRs + 83 AGPRs instead of
-// + 95, 21% faster (128K mixed-KV layer, e4m3 and binary16 parameters)
-#ifndef KVQ_DECODE_PF1_VMIX
-#define KVQ_DECODE_PF1_VMIX 1
 #endif
 // folded query operand kept in registers across a tile's sub-tiles (1) or
 // staged in the wave's LDS region (0)
@@ -473,6 +457,21 @@ __device__ __forceinline__ void pload(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 #ifndef KVQ_DECODE_OCC_VMIX
 #define KVQ_DECODE_OCC_VMIX 1
 #endif
+// Instances that prefetch through a single buffer, one sub-tile ahead
+// (settled A/B against two buffers): two-stream 2-bit codes 18-20% faster
+// (with two buffers they spill), mixed values 21%, mixed keys 2-8% with 1-,
+// 2- and 4-bit values (and two streams with 2-bit values fit only so), 2-bit
+// with one stream 2%, 8-bit 1-2%, 1-bit 1.5%.  4-bit codes measured mixed
+// (+2.7% on the 7B-shaped layer, -1.7% on the 32B-shaped one, -3% on a 128K
+// sequence; at three waves per SIMD 6% slower) and 16-bit neutral: they
+// keep two buffers.
+constexpr bool pf1_instance(int kb, int vb, int ns) {
+  (void)vb;
+  (void)ns;
+  if (KVQ_DECODE_PF1 == 0) return false;
+  return kb != 4 && kb != 16;
+}
+
 constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
   (void)pdt;
   if (KVQ_DECODE_WAVES_PER_SIMD) return KVQ_DECODE_WAVES_PER_SIMD;
@@ -488,11 +487,10 @@ constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
 //
 // Main loop: the wave walks its tiles in sub-tiles of TPS tokens per lane
 // group.  Sub-tile operands (key blocks, key and value parameters) are
-// double buffered in registers and loaded two sub-tiles ahead -- or, for the
-// two-stream instances of 2-bit codes and of mixed keys with 2-bit values and
-// for mixed values (PF1), single buffered and loaded one sub-tile ahead,
-// which keeps them out of spills; value words arrive at the start of their
-// own sub-tile.  All
+// double buffered in registers and loaded two sub-tiles ahead, or single
+// buffered and loaded one sub-tile ahead where that measured faster
+// (pf1_instance: it mostly keeps instances out of spills); value words arrive
+// at the start of their own sub-tile.  All
 // loads are raw buffer loads with an
 // SGPR base per (stream, tile) and lane offsets fixed for the whole kernel.
 // The folded query u = q * S_K * 2^k (split into f16 hi + lo) lives in LDS,
@@ -673,14 +671,8 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // sub-tiles ahead (measured 7% faster with binary16 parameters, equal with
   // e4m3, at one wave per SIMD; two waves per SIMD spill even so)
   constexpr bool PJIT = VMIX;
-  // one prefetch buffer (operands one sub-tile ahead instead of two): mixed
-  // keys and 2-bit values or 2-bit codes with several streams per wave, where
-  // the second buffer's registers would spill, and mixed values, whose
-  // registers overflow into AGPRs
-  constexpr bool PF1 = KVQ_DECODE_PF1 && ((MIXED && VB == 2 && NS >= 2) ||
-                                          (KVQ_DECODE_PF1_2BIT && KB == 2 && NS >= KVQ_DECODE_PF1_2BIT) ||
-                                          (KVQ_DECODE_PF1_4BIT && KB == 4 && NS >= KVQ_DECODE_PF1_4BIT) ||
-                                          (KVQ_DECODE_PF1_VMIX && VMIX));
+  // one prefetch buffer (operands one sub-tile ahead instead of two)
+  constexpr bool PF1 = pf1_instance(KB, VB, NS);
   constexpr int PWK = PW<PDT, 8>::W;                 // key-parameter words per 8 slots
   constexpr int KPA = 32 * PB;                       // words per 128 key parameters
   constexpr int KPL = (PB == 4) ? 2 : 1;             // of which one lane loads
