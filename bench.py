@@ -33,14 +33,14 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, profiles/decode_kernel_*.md)
 # for the kernel source with the given digest, and the factors that map each
 # counter onto true bytes: a plain 512 MiB device copy in the same run reads
-# FETCH_SIZE = 262159.8 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
-# fetch counter is scaled by 524288/262159.8 and the write counter by 1.  The
+# FETCH_SIZE = 262158.7 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
+# fetch counter is scaled by 524288/262158.7 and the write counter by 1.  The
 # figure is reported only while the kernel source is unchanged.
 COUNTER_TRAFFIC = {
-    "source_sha256": "bdc859d7c9cf37540b78cbf75b5a6b13ff908b5498aaf9ce725b77830d2f2206",
+    "source_sha256": "45c521b321371d277e14942b746fbd2f9a07f05cb36f7a17bbd0ca7488a32811",
     "fetch_kib": 139900.0,
     "write_kib": 3664.0,
-    "fetch_factor": 524288.0 / 262159.8,
+    "fetch_factor": 524288.0 / 262158.7,
     "write_factor": 1.0,
 }
 KERNEL_SOURCES = ("kv_cache_mixed_amd/csrc/decode_attn.hip", "kv_cache_mixed_amd/csrc/kvq_device.h")

@@ -457,6 +457,12 @@ __device__ __forceinline__ void pload(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
 #ifndef KVQ_DECODE_OCC_VMIX
 #define KVQ_DECODE_OCC_VMIX 1
 #endif
+// waves per SIMD of mixed keys with 1-bit values: two, with one prefetch
+// buffer, fit 256 registers without spills (binary32 parameters aside, which
+// stay at one) and run 29-35% faster than one (128K sequence, batched 32K)
+#ifndef KVQ_DECODE_OCC_MIXED1
+#define KVQ_DECODE_OCC_MIXED1 2
+#endif
 // Instances that prefetch through a single buffer, one sub-tile ahead
 // (settled A/B against two buffers): two-stream 2-bit codes 18-20% faster
 // (with two buffers they spill), mixed values 21%, mixed keys 2-8% with 1-,
@@ -473,11 +479,11 @@ constexpr bool pf1_instance(int kb, int vb, int ns) {
 }
 
 constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
-  (void)pdt;
   if (KVQ_DECODE_WAVES_PER_SIMD) return KVQ_DECODE_WAVES_PER_SIMD;
   if (kb == 16) return KVQ_DECODE_OCC16;
   if (kb == 0 && vb == 0) return KVQ_DECODE_OCC_VMIX;
-  if ((kb == 0 && vb <= 1) || ns >= 4) return 1;
+  if (kb == 0 && vb == 1) return pdt == KVQ_F32 ? 1 : KVQ_DECODE_OCC_MIXED1;
+  if (ns >= 4) return 1;
   if (ns == 3) return kb == 4 ? KVQ_DECODE_NS3_OCC : (kb == 2 ? KVQ_DECODE_NS3_OCC_2BIT : 1);
   return 2;
 }
