@@ -188,6 +188,18 @@ __device__ __forceinline__ uint32_t mixed_field(const uint32_t* kw, int f) {
     }
   }
 }
+// the compacted softmax's token runs and field weights (2-bit value words):
+// register k pairs tokens k and 8 + k at bit position 2k (k < 5) or 2(k - 5)
+namespace cmp_check {
+constexpr bool ok() {
+  for (int k = 0; k < 8; k++) {
+    const Fld F = ufield<2>(k);
+    if (F.w != 0 || F.lo != k || F.hi != 8 + k || F.wexp != 0 || F.pos != (k < 5 ? 2 * k : 2 * (k - 5))) return false;
+  }
+  return true;
+}
+static_assert(ok(), "2-bit value field map");
+}  // namespace cmp_check
 namespace mixed_check {
 // the lane map is a bijection of the 128 slots and its inverse is exact
 constexpr bool ok() {
@@ -326,6 +338,42 @@ __device__ __forceinline__ uint32_t pk_max_u16(uint32_t a, uint32_t b) {
                                                                 __builtin_bit_cast(u16x2, b)));
 }
 
+// Row-local DPP moves (rows are 16 lanes, banks 4 lanes of a row).  The lanes
+// of the banks in BANKS take src from the lane SH below (shr) or above (shl)
+// in their row; every other lane keeps old.  ror rotates the whole row.
+template <int SH, int BANKS>
+__device__ __forceinline__ uint32_t dpp_shr(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, 0x110 + SH, 0xF, BANKS, false);
+}
+template <int SH, int BANKS>
+__device__ __forceinline__ uint32_t dpp_shl(uint32_t old, uint32_t src) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)old, (int)src, 0x100 + SH, 0xF, BANKS, false);
+}
+template <int SH>
+__device__ __forceinline__ uint32_t dpp_ror(uint32_t x) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)x, (int)x, 0x120 + SH, 0xF, 0xF, false);
+}
+// Reductions over the CMP parts of a row (lanes n, n + 16/CMP, ... of one
+// column, see the compacted softmax of decode_kernel); every lane gets the result.
+template <int CMP>
+__device__ __forceinline__ float part_max(float v) {
+  if constexpr (CMP >= 2) { const float o = u2f(dpp_ror<8>(f2u(v))); v = o > v ? o : v; }
+  if constexpr (CMP >= 4) { const float o = u2f(dpp_ror<4>(f2u(v))); v = o > v ? o : v; }
+  return v;
+}
+template <int CMP>
+__device__ __forceinline__ uint32_t part_maxu(uint32_t v) {
+  if constexpr (CMP >= 2) v = max(v, dpp_ror<8>(v));
+  if constexpr (CMP >= 4) v = max(v, dpp_ror<4>(v));
+  return v;
+}
+template <int CMP>
+__device__ __forceinline__ float part_sum(float v) {
+  if constexpr (CMP >= 2) v += u2f(dpp_ror<8>(f2u(v)));
+  if constexpr (CMP >= 4) v += u2f(dpp_ror<4>(f2u(v)));
+  return v;
+}
+
 // Value field weights.  Token i of a sub-tile (lane-local index) has its codes
 // in field F of ufield<VB>, whose MFMA operand carries code * 2^(pos - 24);
 // the probability operand carries 2^W(i), W = wexp - pos, to make up for it.
@@ -434,6 +482,22 @@ __device__ __forceinline__ void pload(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
     w[0] = __builtin_amdgcn_raw_buffer_load_b32(r, voff, soff, KVQ_DECODE_CPOL_PARAMS);
   }
 }
+// two runs of N consecutive parameters (at voff_lo and voff_hi) as one array
+// of 2N: the token slots of a compacted softmax lane
+template <int PDT, int N>
+__device__ __forceinline__ void pload_runs(__amdgpu_buffer_rsrc_t r, uint32_t voff_lo, uint32_t voff_hi,
+                                           uint32_t soff, uint32_t* w) {
+  constexpr int RB = N * (PDT == KVQ_F32 ? 4 : (PDT == KVQ_E4M3 ? 1 : 2));
+  if constexpr (RB >= 4) {
+    pload<PDT, N>(r, voff_lo, soff, w);
+    pload<PDT, N>(r, voff_hi, soff, w + RB / 4);
+  } else {
+    static_assert(RB == 2, "parameter run");
+    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, voff_lo, soff, KVQ_DECODE_CPOL_PARAMS);
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, voff_hi, soff, KVQ_DECODE_CPOL_PARAMS);
+    w[0] = lo | (hi << 16);
+  }
+}
 
 // Waves per SIMD a decode instance is compiled for.  Two (two workgroups of 4
 // waves per CU) wherever the instance fits in 256 registers per lane with at
@@ -477,6 +541,15 @@ constexpr bool pf1_instance(int kb, int vb, int ns) {
   if (KVQ_DECODE_PF1 == 0) return false;
   return kb != 4 && kb != 16;
 }
+
+// Instances with a compacted-softmax variant (one stream per wave, 2-bit
+// values): with G <= 4 heads (8), each column's logits are spread over four
+// (two) lanes of its row instead of leaving 12 (8) of a row's 16 softmax lanes
+// on columns without a head.  0 switches the variants off (tuning builds).
+#ifndef KVQ_DECODE_CMP
+#define KVQ_DECODE_CMP 1
+#endif
+constexpr bool cmp_instance(int kb, int vb) { return vb == 2 && (kb == 0 || kb == 2); }
 
 constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
   if (KVQ_DECODE_WAVES_PER_SIMD) return KVQ_DECODE_WAVES_PER_SIMD;
@@ -650,7 +723,7 @@ __global__ __launch_bounds__(256) void decode_residual_kernel(ResArgs r, const u
   residual_block<IN>(r, q, H, G, sl2, part_ml, part_o, n_slots, slot0, out, blockIdx.x, blockIdx.y, smem);
 }
 
-template <int KB, int VB, int PDT, int NS>
+template <int KB, int VB, int PDT, int NS, int CMP>
 __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kernel(DecodeArgs a) {
   constexpr bool MIXED = (KB == 0);
   constexpr bool VMIX = (VB == 0);                   // mixed-width values
@@ -669,7 +742,16 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   constexpr int WVS = NWV / NSUB;                    // value words per sub-tile
   constexpr int KSV = FVS / 4;                       // value k-steps per sub-tile
   constexpr int PB = (PDT == KVQ_F32) ? 4 : ((PDT == KVQ_E4M3) ? 1 : 2);
-  constexpr int PWV = PW<PDT, TPS>::W;               // value-parameter words per sub-tile (and class)
+  // Compacted softmax (CMP = 2 or 4, one stream of G <= 16 / CMP heads): the
+  // columns that hold heads are the first CPW = 16 / CMP of each row, so the
+  // logits of column c are spread over lanes c, c + CPW, ... (part a of the
+  // row takes the tokens of probability registers a * RPL .. a * RPL + RPL - 1)
+  // and the probability registers go back to lane c for the value product.
+  static_assert(CMP == 1 || ((CMP == 2 || CMP == 4) && NS == 1 && VB == 2), "compaction: one stream, 2-bit values");
+  constexpr int CPW = 16 / CMP;                      // lanes per part
+  constexpr int RPL = FVS / CMP;                     // probability registers per lane (compacted)
+  constexpr int NL = CMP > 1 ? 2 * RPL : TPS;        // tokens per lane in the softmax
+  constexpr int PWV = CMP > 1 ? (NL * PB + 3) / 4 : PW<PDT, TPS>::W;   // value-parameter words per sub-tile (and class)
   constexpr int NCV = VMIX ? 4 : 1;                  // value parameter classes
   constexpr int NVW = VMIX ? 10 : 8 * WVS;           // value words per stream per sub-tile
   // mixed values: the sub-tile's value parameters (4 classes, 32 registers
@@ -759,6 +841,23 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   const int64_t s0 = (int64_t)grp * NS;
   const int own_c = real ? own : 0;
   const uint32_t vpoff = (uint32_t)(((int64_t)own_c * NCV * g.max_tokens + 32 * lg) * PB);
+  // compacted softmax: the lane's part and the column it serves; its tokens
+  // are the two runs (low and high halves of its probability registers) of
+  // RPL tokens at ufield offsets cpart * RPL and ufield<VB>(0).hi + cpart * RPL
+  const int cpart = n / CPW, ccol = n % CPW;
+  const uint32_t vpoff_lo = vpoff + (uint32_t)(cpart * RPL * PB);
+  const uint32_t vpoff_hi = vpoff + (uint32_t)((ufield<VB == 0 ? 2 : VB>(0).hi + cpart * RPL) * PB);
+  // field weights of the lane's probability registers: W = wexp - pos
+  float cw[CMP > 1 ? RPL : 1], ciw[CMP > 1 ? RPL : 1];
+  if constexpr (CMP > 1) {
+#pragma unroll
+    for (int r = 0; r < RPL; r++) {
+      const int k = cpart * RPL + r;   // register index in the sub-tile (one value word)
+      const int pos = k < 5 ? 2 * k : 2 * (k - 5);   // ufield<2>(k).pos
+      cw[r] = -(float)pos;
+      ciw[r] = exp2i(pos);
+    }
+  }
   const __amdgpu_buffer_rsrc_t r_vs = rsrc((const uint8_t*)g.v_scale + s0 * NCV * g.max_tokens * PB, 0xffffffffu);
   const __amdgpu_buffer_rsrc_t r_vz = rsrc((const uint8_t*)g.v_zero + s0 * NCV * g.max_tokens * PB, 0xffffffffu);
   const __amdgpu_buffer_rsrc_t r_ks = rsrc((const uint8_t*)g.k_scale + s0 * g.max_tokens * PB, 0xffffffffu);
@@ -895,6 +994,11 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   auto load_p_to = [&](uint32_t* ps, uint32_t* pz, int k, int sub) {
     const int tile = t_base + k;
     const uint32_t psoff = (uint32_t)(tile * 128 + sub * TPS) * PB;
+    if constexpr (CMP > 1) {
+      pload_runs<PDT, RPL>(r_vs, vpoff_lo, vpoff_hi, psoff, ps);
+      pload_runs<PDT, RPL>(r_vz, vpoff_lo, vpoff_hi, psoff, pz);
+      return;
+    }
 #pragma unroll
     for (int c = 0; c < NCV; c++) {   // mixed values: class c's parameters c * max_tokens further
       pload<PDT, TPS>(r_vs, vpoff, psoff + (uint32_t)(c * g.max_tokens * PB), ps + c * PWV);
@@ -961,7 +1065,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   auto load_q = [&](uint32_t* qw) {
 #pragma unroll
     for (int c = 0; c < 4; c++) {
-      const u32x4 v = *(const u32x4*)&qs[n][kslot(8 * c)];
+      const u32x4 v = *(const u32x4*)&qs[CMP > 1 ? ccol : n][kslot(8 * c)];
       qw[4 * c] = v[0]; qw[4 * c + 1] = v[1]; qw[4 * c + 2] = v[2]; qw[4 * c + 3] = v[3];
     }
   };
@@ -1164,17 +1268,40 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
 #pragma unroll
       for (int i = 0; i < 4; i++) lv[4 * jj + i] = v[i];
     }
-    // the lane's largest logit (ak >= 0: from its largest raw sum)
-    float vx = lv[0];
+    // compacted softmax: slot s of part a is token ufield(a * RPL + s).lo for
+    // s < RPL, ufield(a * RPL + s - RPL).hi above, fetched from lane ccol of
+    // the row (part 0 keeps its own)
+    float lc[NL];
+    if constexpr (CMP > 1) {
+      // (ufield<2>(k).lo = k and .hi = 8 + k: cmp_check)
+      auto tok = [](int pa, int sl) -> int { return sl < RPL ? pa * RPL + sl : 8 + pa * RPL + sl - RPL; };
 #pragma unroll
-    for (int i = 1; i < TPS; i++) vx = fmaxf(vx, lv[i]);
+      for (int sl = 0; sl < NL; sl++) {
+        uint32_t x = f2u(lv[tok(0, sl)]);
+        if constexpr (CMP == 2) {
+          x = dpp_shr<8, 0xC>(x, f2u(lv[tok(1, sl)]));
+        } else {
+          x = dpp_shr<4, 0x2>(x, f2u(lv[tok(1, sl)]));
+          x = dpp_shr<8, 0x4>(x, f2u(lv[tok(2, sl)]));
+          x = dpp_shr<12, 0x8>(x, f2u(lv[tok(3, sl)]));
+        }
+        lc[sl] = u2f(x);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < TPS; i++) lc[i] = lv[i];
+    }
+    // the lane's largest logit (ak >= 0: from its largest raw sum)
+    float vx = lc[0];
+#pragma unroll
+    for (int i = 1; i < NL; i++) vx = fmaxf(vx, lc[i]);
     const float lmax = fmaf(ak, vx, bk0);
     // value parameters of the sub-tile; binary16 ones stay raw and are read
     // by mixed-precision fmas.  smx: the lane's largest value scale as a
     // binary32 bit pattern (scales are >= +0, so patterns order like values)
     constexpr bool MIX = (PDT == KVQ_F16);
     uint32_t rvs[NCV * PWV], rvz[NCV * PWV];
-    float vs[(MIX || VMIX) ? 1 : TPS], vz[(MIX || VMIX) ? 1 : TPS];
+    float vs[(MIX || VMIX) ? 1 : NL], vz[(MIX || VMIX) ? 1 : NL];
     uint32_t smx;
     if constexpr (VMIX) {
       // raw words only; the largest scale straight from the patterns (scales
@@ -1216,11 +1343,11 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       for (int w = 1; w < PWV; w++) m2 = pk_max_u16(m2, rvs[w]);
       smx = f2u((float)__builtin_bit_cast(_Float16, (uint16_t)max(m2 & 0xffffu, m2 >> 16)));
     } else {
-      praw_unpack<PDT, TPS>(bf.vs, vs);
-      praw_unpack<PDT, TPS>(bf.vz, vz);
+      praw_unpack<PDT, NL>(bf.vs, vs);
+      praw_unpack<PDT, NL>(bf.vz, vz);
       smx = 0;
 #pragma unroll
-      for (int i = 0; i < TPS; i++) smx = max(smx, f2u(vs[i]));
+      for (int i = 0; i < NL; i++) smx = max(smx, f2u(vs[i]));
     }
     if (ti2 >= 0) load_p(bf, ti2, sub2);
     // A column's reference max moves only when one of its logits exceeds it
@@ -1229,8 +1356,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     // they (and the rescale of the running sums and accumulators) run only
     // when some lane of the wave sees such a logit or scale.
     if (__builtin_amdgcn_ballot_w64(lmax > m_run + (float)TAU || expo(u2f(smx)) > e_run) != 0) {
-      const float tmax = wave_max16x4(lmax);
-      const int ev = expo(u2f(wave_maxu16x4(smx)));
+      // (compacted: over the lanes of the column in every part too)
+      const float tmax = part_max<CMP>(wave_max16x4(lmax));
+      const int ev = expo(u2f(part_maxu<CMP>(wave_maxu16x4(smx))));
       const float m_new = (tmax > m_run + (float)TAU) ? tmax : m_run;
       const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);   // v_exp_f32, 0 for -inf
       const int e_new = max(e_run, ev);
@@ -1320,46 +1448,92 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       // and only r * (code - VMID), which has no common sign, is left out.
       constexpr float VMID = 0.5f * (float)((1u << VB) - 1u);
       const float c0 = bk0 - m_run + (float)min(VH - e_run, PSMAX);
-      float p[TPS];
-      float lsum = 0.0f;
-      float zc[10], zr[10];
-  #pragma unroll
-      for (int k = 0; k < 10; k++) { zc[k] = 0.0f; zr[k] = 0.0f; }
-  #pragma unroll
-      for (int i = 0; i < TPS; i++) {
-        const int W = tok_w<VB, FVS>(i);
-        const float e = __builtin_amdgcn_exp2f(fmaf(ak, lv[i], c0 + (float)W));
-        lsum = fmaf(e, exp2i(-W), lsum);
-        if constexpr (MIX) {
-          zc[w_class(W)] = fmaf(e, __builtin_fmaf(VMID, half_at(rvs, i), half_at(rvz, i)), zc[w_class(W)]);
-          p[i] = fmaf(e, half_at(rvs, i), 0.0f);
-        } else {
-          zc[w_class(W)] = fmaf(e, fmaf(VMID, vs[i], vz[i]), zc[w_class(W)]);
-          p[i] = e * vs[i];
-        }
-      }
-      l_run += lsum;
-
-      // ---- P operand and PV; every sub-tile has the field layout of sub-tile
-      // 0, shifted by WVS words and TPS tokens
       uint32_t bvh[FVS];
-  #pragma unroll
-      for (int ff = 0; ff < FVS; ff++) {
-        // a token whose codes span two fields (the bytes of a 16-bit code)
-        // carries the weight of its first field; the other gets the difference
-        const Fld F = ufield<VB>(ff);
-        const int dwe = (F.wexp - F.pos) - tok_w<VB, FVS>(F.lo);
-        const f16x2 h = __builtin_convertvector((f32x2){p[F.lo] * exp2i(dwe), p[F.hi] * exp2i(dwe)}, f16x2);
-        bvh[ff] = __builtin_bit_cast(uint32_t, h);
-        // the tokens' first field: P~ of both tokens into the residual sums
-        if (dwe == 0) zr[w_class(tok_w<VB, FVS>(F.lo))] = __builtin_amdgcn_fdot2(h, (f16x2){1.0f16, 1.0f16},
-                                                                                 zr[w_class(tok_w<VB, FVS>(F.lo))], false);
+      if constexpr (CMP > 1) {
+        // compacted: the lane's NL slots (one column, two runs of RPL tokens),
+        // then its RPL probability registers (slot r low, slot RPL + r high)
+        // back to lane ccol of part 0 as registers cpart * RPL + r
+        float p[NL];
+        float lsum = 0.0f;
+        float zc[RPL], zr[RPL];
+#pragma unroll
+        for (int r = 0; r < RPL; r++) { zc[r] = 0.0f; zr[r] = 0.0f; }
+#pragma unroll
+        for (int sl = 0; sl < NL; sl++) {
+          const int r = sl % RPL;
+          const float e = __builtin_amdgcn_exp2f(fmaf(ak, lc[sl], c0 + cw[r]));
+          lsum = fmaf(e, ciw[r], lsum);
+          if constexpr (MIX) {
+            zc[r] = fmaf(e, __builtin_fmaf(VMID, half_at(rvs, sl), half_at(rvz, sl)), zc[r]);
+            p[sl] = fmaf(e, half_at(rvs, sl), 0.0f);
+          } else {
+            zc[r] = fmaf(e, fmaf(VMID, vs[sl], vz[sl]), zc[r]);
+            p[sl] = e * vs[sl];
+          }
+        }
+        l_run += lsum;
+        uint32_t pr[RPL];
+        float zsum = 0.0f;
+#pragma unroll
+        for (int r = 0; r < RPL; r++) {
+          const f16x2 h = __builtin_convertvector((f32x2){p[r], p[RPL + r]}, f16x2);
+          pr[r] = __builtin_bit_cast(uint32_t, h);
+          zr[r] = __builtin_amdgcn_fdot2(h, (f16x2){1.0f16, 1.0f16}, zr[r], false);
+          zsum = fmaf(fmaf(-VMID, zr[r], zc[r]), ciw[r], zsum);
+        }
+        z_run += zsum;
+#pragma unroll
+        for (int r = 0; r < RPL; r++) {
+          bvh[r] = pr[r];
+          if constexpr (CMP == 2) {
+            bvh[RPL + r] = dpp_shl<8, 0x3>(pr[r], pr[r]);
+          } else {
+            bvh[RPL + r] = dpp_shl<4, 0x1>(pr[r], pr[r]);
+            bvh[2 * RPL + r] = dpp_shl<8, 0x1>(pr[r], pr[r]);
+            bvh[3 * RPL + r] = dpp_shl<12, 0x1>(pr[r], pr[r]);
+          }
+        }
+      } else {
+        float p[TPS];
+        float lsum = 0.0f;
+        float zc[10], zr[10];
+    #pragma unroll
+        for (int k = 0; k < 10; k++) { zc[k] = 0.0f; zr[k] = 0.0f; }
+    #pragma unroll
+        for (int i = 0; i < TPS; i++) {
+          const int W = tok_w<VB, FVS>(i);
+          const float e = __builtin_amdgcn_exp2f(fmaf(ak, lv[i], c0 + (float)W));
+          lsum = fmaf(e, exp2i(-W), lsum);
+          if constexpr (MIX) {
+            zc[w_class(W)] = fmaf(e, __builtin_fmaf(VMID, half_at(rvs, i), half_at(rvz, i)), zc[w_class(W)]);
+            p[i] = fmaf(e, half_at(rvs, i), 0.0f);
+          } else {
+            zc[w_class(W)] = fmaf(e, fmaf(VMID, vs[i], vz[i]), zc[w_class(W)]);
+            p[i] = e * vs[i];
+          }
+        }
+        l_run += lsum;
+
+        // ---- P operand and PV; every sub-tile has the field layout of sub-tile
+        // 0, shifted by WVS words and TPS tokens
+    #pragma unroll
+        for (int ff = 0; ff < FVS; ff++) {
+          // a token whose codes span two fields (the bytes of a 16-bit code)
+          // carries the weight of its first field; the other gets the difference
+          const Fld F = ufield<VB>(ff);
+          const int dwe = (F.wexp - F.pos) - tok_w<VB, FVS>(F.lo);
+          const f16x2 h = __builtin_convertvector((f32x2){p[F.lo] * exp2i(dwe), p[F.hi] * exp2i(dwe)}, f16x2);
+          bvh[ff] = __builtin_bit_cast(uint32_t, h);
+          // the tokens' first field: P~ of both tokens into the residual sums
+          if (dwe == 0) zr[w_class(tok_w<VB, FVS>(F.lo))] = __builtin_amdgcn_fdot2(h, (f16x2){1.0f16, 1.0f16},
+                                                                                   zr[w_class(tok_w<VB, FVS>(F.lo))], false);
+        }
+        float zsum = fmaf(-VMID, zr[0], zc[0]);
+    #pragma unroll
+        for (int k = 1; k < 10; k++)
+          if (class_used<VB, FVS, TPS>(k)) zsum = fmaf(fmaf(-VMID, zr[k], zc[k]), exp2i(-class_w<VB>(k)), zsum);
+        z_run += zsum;
       }
-      float zsum = fmaf(-VMID, zr[0], zc[0]);
-  #pragma unroll
-      for (int k = 1; k < 10; k++)
-        if (class_used<VB, FVS, TPS>(k)) zsum = fmaf(fmaf(-VMID, zr[k], zc[k]), exp2i(-class_w<VB>(k)), zsum);
-      z_run += zsum;
   #pragma unroll
       for (int s = 0; s < NS; s++) {
         uint32_t bsh[FVS];
@@ -1447,8 +1621,9 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   static_assert(sizeof(lds[0]) >= sizeof(float) * 16 * 128, "partial fits the wave region");
   const int ps = min(VH - e_run, PSMAX);
   const float unps = exp2i(-ps);
-  const float l_tot = wave_sum16x4(l_run) * unps;
-  const float z_tot = wave_sum16x4(z_run) * unps;
+  // (compacted: the column's sums are spread over the parts of its row)
+  const float l_tot = part_sum<CMP>(wave_sum16x4(l_run)) * unps;
+  const float z_tot = part_sum<CMP>(wave_sum16x4(z_run)) * unps;
   float zm_tot[NCV];
 #pragma unroll
   for (int k = 0; k < NCV; k++) zm_tot[k] = VMIX ? wave_sum16x4(zm_run[k]) * unps : 0.0f;
@@ -1705,13 +1880,25 @@ static hipError_t launch_ns(const DecodeArgs& a0, const DecodePlan& p, hipStream
   const int res_rows = a.n_res ? (a.n_res * a.g.B * a.g.H + a.n_chunks - 1) / a.n_chunks : 0;
   const dim3 grid(a.n_chunks, a.n_groups + res_rows), block(256);
   if (p.ns == 1) {
-    hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 1>), grid, block, 0, st, a);
+    // one stream: a compacted softmax where the heads fill at most a half or
+    // a quarter of the MFMA columns
+    if constexpr (cmp_instance(KB, VB)) {
+      if (KVQ_DECODE_CMP && a.G <= 4) {
+        hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 1, 4>), grid, block, 0, st, a);
+        return hipGetLastError();
+      }
+      if (KVQ_DECODE_CMP && a.G <= 8) {
+        hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 1, 2>), grid, block, 0, st, a);
+        return hipGetLastError();
+      }
+    }
+    hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 1, 1>), grid, block, 0, st, a);
   } else if (p.ns == 2) {
-    if constexpr (CAP >= 2) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 2>), grid, block, 0, st, a);
+    if constexpr (CAP >= 2) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 2, 1>), grid, block, 0, st, a);
   } else if (p.ns == 3) {
-    if constexpr (CAP >= 3) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 3>), grid, block, 0, st, a);
+    if constexpr (CAP >= 3) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 3, 1>), grid, block, 0, st, a);
   } else {
-    if constexpr (CAP >= 4) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 4>), grid, block, 0, st, a);
+    if constexpr (CAP >= 4) hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 4, 1>), grid, block, 0, st, a);
   }
   return hipGetLastError();
 }

@@ -1,0 +1,97 @@
+"""GPU parity of the compacted-softmax decode instances.
+
+With one kv stream per wave and at most 8 (4) query heads, the decode kernel
+spreads each head's logits over two (four) lanes of its MFMA row and gathers
+the probability operands back for the value product (2-bit values, uniform or
+mixed-width keys).  The cases below force that plan (few streams and tiles, so
+the launch takes one stream per wave) for every group size it serves, every
+parameter dtype, a softmax whose reference max moves inside tiles (the rescale
+branch and its reductions over the lane parts), a negative scale and ragged
+chunk splits; each is gated against the float64 oracle at the per-row
+relative error of 2e-3 (ChanMix page, Overall framework: dequantize, then
+ordinary attention).
+"""
+import numpy as np
+import pytest
+
+import oracle
+from kv_cache_mixed_amd import kvq, synth
+from tests.gpu_helpers import PDT_ORACLE, REL_TOL, SCALE, q_to_dev, rel_err_rows, to_dev
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _setup():
+    oracle.build(force=False)
+    kvq.load()
+
+
+def _check(k, v, q_bits, kb, pdt, scale, slot_chan=None, what=""):
+    B, H, T, _ = k.shape
+    G = q_bits.shape[1] // H
+    print("case %s B=%d H=%d G=%d T=%d kb=%d pdt=%d scale=%g" % (what, B, H, G, T, kb, pdt, scale), flush=True)
+    cache = kvq.PackedCache(B, H, T, kb, 2, pdt, slot_chan=slot_chan)
+    cache.quantize(to_dev(k, torch), to_dev(v, torch), 0)
+    out = cache.decode_attn(q_to_dev(q_bits, torch), scale).cpu().numpy()
+    assert np.all(np.isfinite(out)), what
+    worst = 0.0
+    for b in range(B):
+        for h in range(H):
+            st = oracle.quantize_stream(k[b, h], v[b, h], kb, 2, PDT_ORACLE[pdt],
+                                        None if slot_chan is None else slot_chan[h])
+            ref = oracle.decode_attn(st, q_bits[b, h * G:(h + 1) * G], scale)
+            worst = max(worst, rel_err_rows(out[b, h * G:(h + 1) * G], ref).max())
+    assert worst <= REL_TOL, "%s: max row relative error %.3e" % (what, worst)
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 5, 7, 8])
+@pytest.mark.parametrize("pdt", [kvq.E4M3, kvq.F16, kvq.BF16, kvq.F32])
+def test_mixed_keys_compacted(G, pdt):
+    inp = synth.mixed_layer(1, 2, 2 * G, 2944, seed=300 + 10 * G + pdt)
+    _check(inp["k"], inp["v"], inp["q_bf16"], kvq.KMIXED, pdt, SCALE, inp["slot_chan"], what="mixed G=%d" % G)
+
+
+@pytest.mark.parametrize("G", [1, 3, 4, 6, 8])
+@pytest.mark.parametrize("pdt", [kvq.F16, kvq.E4M3, kvq.BF16, kvq.F32])
+def test_two_bit_compacted(G, pdt):
+    inp = synth.layer(2, 1, G, 3200, seed=400 + 10 * G + pdt)
+    _check(inp["k"], inp["v"], inp["q_bf16"], 2, pdt, SCALE, what="2-bit G=%d" % G)
+
+
+@pytest.mark.parametrize("kb,G", [(2, 4), (2, 7), (kvq.KMIXED, 4), (kvq.KMIXED, 6)])
+def test_compacted_climbing_logits(kb, G):
+    """Keys ramped along each head's query: logits climb by ~40 log2 units
+    inside every tile and across tiles, so the per-column reference moves
+    (reductions over the lane parts of a row) in most sub-tiles."""
+    rng = np.random.default_rng(500 + G + (kb or 50))
+    B, H, T = 1, 2, 4096
+    k = rng.standard_normal((B, H, T, 128)).astype(np.float32)
+    v = rng.standard_normal((B, H, T, 128)).astype(np.float32)
+    q = rng.standard_normal((B, H * G, 128)).astype(np.float32)
+    t = np.arange(T)
+    ramp = (t % 128) / 127.0 * 3.0 + (t // 128) / (T // 128)
+    for h in range(H):
+        d = q[0, h * G] / np.linalg.norm(q[0, h * G])
+        k[0, h] += (ramp[:, None] * d[None, :] * 10.0).astype(np.float32)
+    slot_chan = None
+    if kb == kvq.KMIXED:
+        slot_chan = synth.mixed_layer(1, H, H * G, 128, seed=510)["slot_chan"]
+    _check(k, v, synth.to_bf16_bits(q), kb, kvq.F16, SCALE, slot_chan, what="climbing kb=%d G=%d" % (kb, G))
+    _check(k, v, synth.to_bf16_bits(q), kb, kvq.E4M3, -SCALE, slot_chan, what="climbing, negative kb=%d G=%d" % (kb, G))
+
+
+def test_compacted_128k_sequence_sampled():
+    """A single 128K-token sequence of mixed keys (the long-context layer's
+    launch: one stream per wave, 64 chunk partials), checked on sampled heads."""
+    B, H, G, T = 1, 2, 4, 131072
+    inp = synth.mixed_layer(B, H, H * G, T, seed=520)
+    cache = kvq.PackedCache(B, H, T, kvq.KMIXED, 2, kvq.E4M3, slot_chan=inp["slot_chan"])
+    cache.quantize(to_dev(inp["k"], torch), to_dev(inp["v"], torch), 0)
+    out = cache.decode_attn(q_to_dev(inp["q_bf16"], torch), SCALE).cpu().numpy()
+    for h in range(H):
+        st = oracle.quantize_stream(inp["k"][0, h], inp["v"][0, h], kvq.KMIXED, 2, PDT_ORACLE[kvq.E4M3],
+                                    inp["slot_chan"][h])
+        ref = oracle.decode_attn(st, inp["q_bf16"][0, h * G:(h + 1) * G], SCALE)
+        assert rel_err_rows(out[0, h * G:(h + 1) * G], ref).max() <= REL_TOL
