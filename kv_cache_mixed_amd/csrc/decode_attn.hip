@@ -1081,6 +1081,44 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     for (int li = 0; li < 32; li++) qmax = max(qmax, f2u(qget(qw, li)) & 0x7fffffffu);
     eq = expo(u2f(wave_maxu16x4(qmax)));
   }
+  // Compacted fold (CMP > 1): part a of the row computes registers
+  // a * NFP .. a * NFP + NFP - 1 of its column's folded query, from the
+  // part's 2 NFP slots (lane-order positions cpbase + offset; register j's
+  // halves at offsets foff(j, 0), foff(j, 1)), whose query values stay in
+  // registers; DPP row shifts gather the registers back to lane ccol.
+  constexpr int NFP = NFK / CMP;
+  // uniform widths with four parts: the part's slots are two runs of NFP
+  // (low halves, then high halves 8 slots further); otherwise one run
+  constexpr bool FRUN2 = !MIXED && CMP == 4;
+  auto foff = [](int j, int half) -> int { return MIXED ? 2 * j + half : j + half * NFP; };
+  auto fli = [](int off) -> int { return FRUN2 ? (off < NFP ? off : 8 + off - NFP) : off; };   // offset -> li - cpbase
+  const int cpbase = MIXED ? 2 * NFP * cpart : (CMP == 4 ? 4 * cpart + 8 * (cpart >> 1) : 16 * cpart);
+  float qv[CMP > 1 ? 2 * NFP : 1];
+  int fwl[CMP > 1 ? NFP : 1], fwh[CMP > 1 ? NFP : 1];   // field weight exponents of register j's halves
+  if constexpr (CMP > 1) {
+#pragma unroll
+    for (int off = 0; off < 2 * NFP; off++)
+      qv[off] = u2f((uint32_t)qs[ccol][kslot(cpbase + fli(off))] << 16);
+#pragma unroll
+    for (int j = 0; j < NFP; j++) {
+      int el = 0, eh = 0;
+#pragma unroll
+      for (int pa = 0; pa < CMP; pa++) {
+        const int f = pa * NFP + j;
+        int l0, h0;
+        if constexpr (MIXED) {
+          l0 = -mixed_pos(f, 0);
+          h0 = -mixed_pos(f, 1);
+        } else {
+          const Fld F = ufield<MIXED ? 2 : KB>(f);
+          l0 = h0 = F.wexp - F.pos;
+        }
+        if (cpart == pa) { el = l0; eh = h0; }
+      }
+      fwl[j] = el;
+      fwh[j] = eh;
+    }
+  }
 
   // fold the key scales of `tile` into the query: u = q * S * 2^k as f16 hi/lo
   // operand registers in LDS; logit constants ak, bk0
@@ -1120,6 +1158,73 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if constexpr (CMP > 1) {
+      // the part's 2 NFP key parameters, in offset order
+      constexpr int RW = (FRUN2 ? NFP : 2 * NFP) * PB / 4;   // words per run
+      auto load_kpp = [&](int which, uint32_t* pw) {
+        const uint32_t* src = &kst[wave][0][which][0];
+        const int w0 = kslot(cpbase) * PB / 4;
+#pragma unroll
+        for (int i = 0; i < RW; i++) pw[i] = src[w0 + i];
+        if constexpr (FRUN2) {
+#pragma unroll
+          for (int i = 0; i < RW; i++) pw[RW + i] = src[w0 + 8 * PB / 4 + i];
+        }
+      };
+      constexpr int PWP = (FRUN2 ? 2 : 1) * RW;
+      uint32_t zw[PWP], sw[PWP];
+      load_kpp(1, zw);
+      load_kpp(0, sw);
+      float bc[2] = {0.0f, 0.0f};
+#pragma unroll
+      for (int t = 0; t < 2 * NFP; t++) bc[t & 1] = fmaf(qv[t], pget<PDT>(zw, t), bc[t & 1]);
+      float beta = bc[0] + bc[1];
+      uint32_t smax = 0;
+      if constexpr (PDT == KVQ_F16) {
+        uint32_t m2 = sw[0];
+#pragma unroll
+        for (int i = 1; i < PWP; i++) m2 = pk_max_u16(m2, sw[i]);
+        smax = f2u((float)__builtin_bit_cast(_Float16, (uint16_t)max(m2 & 0xffffu, m2 >> 16)));
+      } else {
+#pragma unroll
+        for (int t = 0; t < 2 * NFP; t++) smax = max(smax, f2u(pget<PDT>(sw, t)));
+      }
+      const int eqs = max(eq + expo(u2f(part_maxu<CMP>(wave_maxu16x4(smax)))), -100);
+      beta = part_sum<CMP>(wave_sum16x4(beta));
+      const float kf = exp2i(KH - eqs);
+      auto uval = [&](int t) -> float {
+        if constexpr (PDT == KVQ_F16) return __builtin_fmaf(qv[t], pget<PDT>(sw, t), 0.0f);
+        else return qv[t] * pget<PDT>(sw, t);
+      };
+      uint32_t oh[NFP], ol[NFP];
+#pragma unroll
+      for (int j = 0; j < NFP; j++)
+        split_pack(uval(foff(j, 0)) * (kf * exp2i(fwl[j])), uval(foff(j, 1)) * (kf * exp2i(fwh[j])), oh[j], ol[j], m1);
+      // register f of part 0's lane from part f / NFP of its row
+      constexpr int P0 = CMP == 4 ? 0x1 : 0x3;
+      auto to0 = [&](uint32_t x, int pa) -> uint32_t {
+        if (pa == 1) return dpp_shl<CPW, P0>(x, x);
+        if constexpr (CMP == 4) {
+          if (pa == 2) return dpp_shl<2 * CPW, P0>(x, x);
+          if (pa == 3) return dpp_shl<3 * CPW, P0>(x, x);
+        }
+        return x;
+      };
+#pragma unroll
+      for (int f = 0; f < NFK; f++) {
+        const uint32_t hi = to0(oh[f % NFP], f / NFP), lo = to0(ol[f % NFP], f / NFP);
+        if constexpr (QREG) {
+          qop[f >> 2][0][f & 3] = hi;
+          qop[f >> 2][1][f & 3] = lo;
+        } else {
+          my_lds[(((f >> 2) * 2 + 0) * 64 + lane) * 4 + (f & 3)] = hi;
+          my_lds[(((f >> 2) * 2 + 1) * 64 + lane) * 4 + (f & 3)] = lo;
+        }
+      }
+      ak = __builtin_fabsf(a.sl2) * exp2i(24 - KH + eqs);
+      bk0 = __builtin_fabsf(a.sl2) * beta;
+      return;
+    }
     // raw words of the lane's 32 key parameters (four runs of 8 slots)
     auto load_kp = [&](int which, uint32_t* pw) {
 #pragma unroll
