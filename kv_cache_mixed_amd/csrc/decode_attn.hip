@@ -549,12 +549,23 @@ constexpr bool pf1_instance(int kb, int vb, int ns) {
 #ifndef KVQ_DECODE_CMP
 #define KVQ_DECODE_CMP 1
 #endif
-constexpr bool cmp_instance(int kb, int vb) { return vb == 2 && (kb == 0 || kb == 2); }
+constexpr bool cmp_instance(int kb, int vb) { return (vb == 2 && (kb == 0 || kb == 2)) || (kb == 0 && vb == 0); }
+// the compaction a launch of ns streams per wave with G heads per stream uses
+constexpr int cmp_for(int kb, int vb, int ns, int G) {
+  if (!KVQ_DECODE_CMP || ns != 1 || !cmp_instance(kb, vb)) return 1;
+  return G <= 4 ? 4 : (G <= 8 ? 2 : 1);
+}
+// waves per SIMD of mixed values with the four-part compacted softmax: its
+// registers fit 256 per lane, and two waves per SIMD ran 17% faster than
+// one (128K sequence, G = 4: 42.9 -> 35.6 us per call)
+#ifndef KVQ_DECODE_OCC_VMIX_CMP4
+#define KVQ_DECODE_OCC_VMIX_CMP4 2
+#endif
 
-constexpr int decode_occ(int kb, int vb, int pdt, int ns) {
+constexpr int decode_occ(int kb, int vb, int pdt, int ns, int cmp = 1) {
   if (KVQ_DECODE_WAVES_PER_SIMD) return KVQ_DECODE_WAVES_PER_SIMD;
   if (kb == 16) return KVQ_DECODE_OCC16;
-  if (kb == 0 && vb == 0) return KVQ_DECODE_OCC_VMIX;
+  if (kb == 0 && vb == 0) return cmp == 4 ? KVQ_DECODE_OCC_VMIX_CMP4 : KVQ_DECODE_OCC_VMIX;
   if (kb == 0 && vb == 1) return pdt == KVQ_F32 ? 1 : KVQ_DECODE_OCC_MIXED1;
   if (ns >= 4) return 1;
   if (ns == 3) return kb == 4 ? KVQ_DECODE_NS3_OCC : (kb == 2 ? KVQ_DECODE_NS3_OCC_2BIT : 1);
@@ -724,7 +735,7 @@ __global__ __launch_bounds__(256) void decode_residual_kernel(ResArgs r, const u
 }
 
 template <int KB, int VB, int PDT, int NS, int CMP>
-__global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS, CMP)) void decode_kernel(DecodeArgs a) {
   constexpr bool MIXED = (KB == 0);
   constexpr bool VMIX = (VB == 0);                   // mixed-width values
   constexpr int NFK = MIXED ? 16 : UInfo<KB>::NF;    // key operand registers per token
@@ -747,7 +758,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   // logits of column c are spread over lanes c, c + CPW, ... (part a of the
   // row takes the tokens of probability registers a * RPL .. a * RPL + RPL - 1)
   // and the probability registers go back to lane c for the value product.
-  static_assert(CMP == 1 || ((CMP == 2 || CMP == 4) && NS == 1 && VB == 2), "compaction: one stream, 2-bit values");
+  static_assert(CMP == 1 || ((CMP == 2 || CMP == 4) && NS <= 2 && (VB == 2 || VMIX)), "compaction: 2-bit or mixed values");
   constexpr int CPW = 16 / CMP;                      // lanes per part
   constexpr int RPL = FVS / CMP;                     // probability registers per lane (compacted)
   constexpr int NL = CMP > 1 ? 2 * RPL : TPS;        // tokens per lane in the softmax
@@ -815,7 +826,8 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   const int chunk = blockIdx.x;
   const int G = a.G;
   const int BH = g.B * g.H;
-  const int own = n / G;
+  // (compacted softmax: lanes of every part work for column n % CPW)
+  const int own = (CMP > 1 ? n % CPW : n) / G;
   const int bh_own = grp * NS + own;
   const bool real = (own < NS) && (bh_own < BH);
   // the chunk's tiles, numbered k = 0 .. t_count-1: tile = t_base + k
@@ -848,7 +860,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   const uint32_t vpoff_lo = vpoff + (uint32_t)(cpart * RPL * PB);
   const uint32_t vpoff_hi = vpoff + (uint32_t)((ufield<VB == 0 ? 2 : VB>(0).hi + cpart * RPL) * PB);
   // field weights of the lane's probability registers: W = wexp - pos
-  float cw[CMP > 1 ? RPL : 1], ciw[CMP > 1 ? RPL : 1];
+  float cw[CMP > 1 ? RPL : 1], ciw[CMP > 1 ? RPL : 1], cew[CMP > 1 ? RPL : 1];
   if constexpr (CMP > 1) {
 #pragma unroll
     for (int r = 0; r < RPL; r++) {
@@ -856,6 +868,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       const int pos = k < 5 ? 2 * k : 2 * (k - 5);   // ufield<2>(k).pos
       cw[r] = -(float)pos;
       ciw[r] = exp2i(pos);
+      cew[r] = exp2i(-pos);
     }
   }
   const __amdgpu_buffer_rsrc_t r_vs = rsrc((const uint8_t*)g.v_scale + s0 * NCV * g.max_tokens * PB, 0xffffffffu);
@@ -995,8 +1008,12 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
     const int tile = t_base + k;
     const uint32_t psoff = (uint32_t)(tile * 128 + sub * TPS) * PB;
     if constexpr (CMP > 1) {
-      pload_runs<PDT, RPL>(r_vs, vpoff_lo, vpoff_hi, psoff, ps);
-      pload_runs<PDT, RPL>(r_vz, vpoff_lo, vpoff_hi, psoff, pz);
+#pragma unroll
+      for (int c = 0; c < NCV; c++) {   // mixed values: class c's parameters c * max_tokens further
+        const uint32_t co = psoff + (uint32_t)(c * g.max_tokens * PB);
+        pload_runs<PDT, RPL>(r_vs, vpoff_lo, vpoff_hi, co, ps + c * PWV);
+        pload_runs<PDT, RPL>(r_vz, vpoff_lo, vpoff_hi, co, pz + c * PWV);
+      }
       return;
     }
 #pragma unroll
@@ -1162,7 +1179,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       // the part's 2 NFP key parameters, in offset order
       constexpr int RW = (FRUN2 ? NFP : 2 * NFP) * PB / 4;   // words per run
       auto load_kpp = [&](int which, uint32_t* pw) {
-        const uint32_t* src = &kst[wave][0][which][0];
+        const uint32_t* src = &kst[wave][own_c][which][0];
         const int w0 = kslot(cpbase) * PB / 4;
 #pragma unroll
         for (int i = 0; i < RW; i++) pw[i] = src[w0 + i];
@@ -1489,57 +1506,161 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
       // binary16 P~ made up at the class's code midpoint as for uniform
       // widths; the residual sums read P~ * 2^-W exactly through fdot2.
       const float c0 = bk0 - m_run + (float)min(VH - e_run, PSMAX);
-      float e[TPS];
-      float lsum = 0.0f;
+      if constexpr (CMP > 1) {
+        // compacted (slot sl of the lane: token parity sl % 2, probability
+        // register sl % RPL of its 2-bit field): per class the lane's NL
+        // binary16 operands as pairs Q[m] = (slot 2m, slot 2m + 1), then the
+        // registers of part 0's lane.  4-bit container register ff pairs
+        // tokens t and t + 4 (t = 8 (ff / 4) + ff % 4), held by parts p and
+        // p + CMP / 2 of the row at the same slot; 2-bit container register
+        // a * RPL + r pairs slots r and RPL + r of part a.
+        float e[NL];
+        float lsum = 0.0f;
 #pragma unroll
-      for (int i = 0; i < TPS; i++) {
-        e[i] = __builtin_amdgcn_exp2f(fmaf(ak, lv[i], c0));
-        lsum += e[i];
-      }
-      l_run += lsum;
-      // one class at a time: its operand, its zero-point sum, then the value
-      // products of its slot blocks (block k for k < 3, blocks 3..7 for k = 3)
+        for (int sl = 0; sl < NL; sl++) {
+          e[sl] = __builtin_amdgcn_exp2f(fmaf(ak, lc[sl], c0));
+          lsum += e[sl];
+        }
+        l_run += lsum;
+        constexpr int P0 = CMP == 4 ? 0x1 : 0x3;
 #pragma unroll
-      for (int k = 0; k < 4; k++) {
-        const float vmid = 0.5f * (float)((1u << vmixed_class_bits(k)) - 1u);
-        const uint32_t* ks = rvs + k * PWV;
-        const uint32_t* kz = rvz + k * PWV;
-        float zc = 0.0f, zr = 0.0f;
-        float p[TPS];
+        for (int k = 0; k < 4; k++) {
+          const float vmid = 0.5f * (float)((1u << vmixed_class_bits(k)) - 1u);
+          const uint32_t* ks = rvs + k * PWV;
+          const uint32_t* kz = rvz + k * PWV;
+          float zc = 0.0f, zr = 0.0f;
+          float p[NL];
 #pragma unroll
-        for (int i = 0; i < TPS; i++) {
-          const float ew = e[i] * exp2i(k < 2 ? tok_w<4, FVS>(i) : tok_w<2, FVS>(i));
-          if constexpr (MIX) {
-            zc = fmaf(e[i], __builtin_fmaf(vmid, half_at(ks, i), half_at(kz, i)), zc);
-            p[i] = fmaf(ew, half_at(ks, i), 0.0f);
+          for (int sl = 0; sl < NL; sl++) {
+            const float ew = e[sl] * (k < 2 ? ((sl & 1) ? 0.0625f : 1.0f) : cew[sl % RPL]);
+            if constexpr (MIX) {
+              zc = fmaf(e[sl], __builtin_fmaf(vmid, half_at(ks, sl), half_at(kz, sl)), zc);
+              p[sl] = fmaf(ew, half_at(ks, sl), 0.0f);
+            } else {
+              const float sk = pget<PDT>(ks, sl);
+              zc = fmaf(e[sl], fmaf(vmid, sk, pget<PDT>(kz, sl)), zc);
+              p[sl] = ew * sk;
+            }
+          }
+          uint32_t qp[NL / 2];
+#pragma unroll
+          for (int m = 0; m < NL / 2; m++) {
+            const f16x2 h = __builtin_convertvector((f32x2){p[2 * m], p[2 * m + 1]}, f16x2);
+            qp[m] = __builtin_bit_cast(uint32_t, h);
+          }
+          uint32_t bv[FVS];
+          if (k < 2) {
+            // 2^-W of the 4-bit fields: 1 (even tokens), 16 (odd)
+#pragma unroll
+            for (int m = 0; m < NL / 2; m++)
+              zr = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, qp[m]), (f16x2){1.0f16, 16.0f16}, zr, false);
+#pragma unroll
+            for (int ff = 0; ff < FVS; ff++) {
+              uint32_t lo, hi;   // the pair's halves: parts pl (low token) and pl + CMP / 2
+              int m;
+              if constexpr (CMP == 4) {
+                m = ff / 4;
+                const int pl = (ff % 4) / 2;
+                lo = pl == 0 ? qp[m] : dpp_shl<4, P0>(qp[m], qp[m]);
+                hi = pl == 0 ? dpp_shl<8, P0>(qp[m], qp[m]) : dpp_shl<12, P0>(qp[m], qp[m]);
+              } else {
+                m = ff / 2;
+                lo = qp[m];
+                hi = dpp_shl<8, P0>(qp[m], qp[m]);
+              }
+              (void)m;
+              bv[ff] = (ff & 1) ? __builtin_amdgcn_perm(hi, lo, 0x07060302u) : __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+            }
           } else {
-            const float sk = pget<PDT>(ks, i);
-            zc = fmaf(e[i], fmaf(vmid, sk, pget<PDT>(kz, i)), zc);
-            p[i] = ew * sk;
+            uint32_t pr[RPL];
+#pragma unroll
+            for (int r = 0; r < RPL; r++) {
+              const uint32_t a0 = qp[r / 2], a1 = qp[(RPL + r) / 2];
+              pr[r] = (r & 1) ? __builtin_amdgcn_perm(a1, a0, 0x07060302u) : __builtin_amdgcn_perm(a1, a0, 0x05040100u);
+              const _Float16 iw = (_Float16)ciw[r];
+              zr = __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2, pr[r]), (f16x2){iw, iw}, zr, false);
+            }
+#pragma unroll
+            for (int r = 0; r < RPL; r++) {
+              bv[r] = pr[r];
+              if constexpr (CMP == 2) {
+                bv[RPL + r] = dpp_shl<8, 0x3>(pr[r], pr[r]);
+              } else {
+                bv[RPL + r] = dpp_shl<4, 0x1>(pr[r], pr[r]);
+                bv[2 * RPL + r] = dpp_shl<8, 0x1>(pr[r], pr[r]);
+                bv[3 * RPL + r] = dpp_shl<12, 0x1>(pr[r], pr[r]);
+              }
+            }
+          }
+          zm_run[k] += fmaf(-vmid, zr, zc);
+#pragma unroll
+          for (int cb = 0; cb < 8; cb++) {
+            if (vmixed_block_class(cb) != k) continue;
+#pragma unroll
+            for (int kk = 0; kk < KSV; kk++) {
+              uint32_t av[4];
+#pragma unroll
+              for (int r = 0; r < 4; r++) {
+                const Fld F = cb < 2 ? ufield<4>(4 * kk + r) : ufield<2>(4 * kk + r);
+                av[r] = field_subnormal(cb < 2 ? vwp[2 * cb + F.w] : vwp[2 + cb], F);
+              }
+              acc_o[cb] = mfma(av, bv + 4 * kk, acc_o[cb]);
+            }
           }
         }
-        uint32_t bv[FVS];
-#pragma unroll
-        for (int ff = 0; ff < FVS; ff++) {
-          const Fld F = k < 2 ? ufield<4>(ff) : ufield<2>(ff);
-          const f16x2 h = __builtin_convertvector((f32x2){p[F.lo], p[F.hi]}, f16x2);
-          bv[ff] = __builtin_bit_cast(uint32_t, h);
-          const _Float16 iw = (_Float16)exp2i(F.pos - F.wexp);   // 2^-W: 1 .. 256, exact
-          zr = __builtin_amdgcn_fdot2(h, (f16x2){iw, iw}, zr, false);
+      } else {
+        float e[TPS];
+        float lsum = 0.0f;
+  #pragma unroll
+        for (int i = 0; i < TPS; i++) {
+          e[i] = __builtin_amdgcn_exp2f(fmaf(ak, lv[i], c0));
+          lsum += e[i];
         }
-        zm_run[k] += fmaf(-vmid, zr, zc);
-#pragma unroll
-        for (int cb = 0; cb < 8; cb++) {
-          if (vmixed_block_class(cb) != k) continue;
-#pragma unroll
-          for (int kk = 0; kk < KSV; kk++) {
-            uint32_t av[4];
-#pragma unroll
-            for (int r = 0; r < 4; r++) {
-              const Fld F = cb < 2 ? ufield<4>(4 * kk + r) : ufield<2>(4 * kk + r);
-              av[r] = field_subnormal(cb < 2 ? vwp[2 * cb + F.w] : vwp[2 + cb], F);
+        l_run += lsum;
+        // one class at a time: its operand, its zero-point sum, then the value
+        // products of its slot blocks (block k for k < 3, blocks 3..7 for k = 3)
+  #pragma unroll
+        for (int k = 0; k < 4; k++) {
+          const float vmid = 0.5f * (float)((1u << vmixed_class_bits(k)) - 1u);
+          const uint32_t* ks = rvs + k * PWV;
+          const uint32_t* kz = rvz + k * PWV;
+          float zc = 0.0f, zr = 0.0f;
+          float p[TPS];
+  #pragma unroll
+          for (int i = 0; i < TPS; i++) {
+            const float ew = e[i] * exp2i(k < 2 ? tok_w<4, FVS>(i) : tok_w<2, FVS>(i));
+            if constexpr (MIX) {
+              zc = fmaf(e[i], __builtin_fmaf(vmid, half_at(ks, i), half_at(kz, i)), zc);
+              p[i] = fmaf(ew, half_at(ks, i), 0.0f);
+            } else {
+              const float sk = pget<PDT>(ks, i);
+              zc = fmaf(e[i], fmaf(vmid, sk, pget<PDT>(kz, i)), zc);
+              p[i] = ew * sk;
             }
-            acc_o[cb] = mfma(av, bv + 4 * kk, acc_o[cb]);
+          }
+          uint32_t bv[FVS];
+  #pragma unroll
+          for (int ff = 0; ff < FVS; ff++) {
+            const Fld F = k < 2 ? ufield<4>(ff) : ufield<2>(ff);
+            const f16x2 h = __builtin_convertvector((f32x2){p[F.lo], p[F.hi]}, f16x2);
+            bv[ff] = __builtin_bit_cast(uint32_t, h);
+            const _Float16 iw = (_Float16)exp2i(F.pos - F.wexp);   // 2^-W: 1 .. 256, exact
+            zr = __builtin_amdgcn_fdot2(h, (f16x2){iw, iw}, zr, false);
+          }
+          zm_run[k] += fmaf(-vmid, zr, zc);
+  #pragma unroll
+          for (int cb = 0; cb < 8; cb++) {
+            if (vmixed_block_class(cb) != k) continue;
+  #pragma unroll
+            for (int kk = 0; kk < KSV; kk++) {
+              uint32_t av[4];
+  #pragma unroll
+              for (int r = 0; r < 4; r++) {
+                const Fld F = cb < 2 ? ufield<4>(4 * kk + r) : ufield<2>(4 * kk + r);
+                av[r] = field_subnormal(cb < 2 ? vwp[2 * cb + F.w] : vwp[2 + cb], F);
+              }
+              acc_o[cb] = mfma(av, bv + 4 * kk, acc_o[cb]);
+            }
           }
         }
       }
@@ -1731,7 +1852,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS)) void decode_kerne
   const float z_tot = part_sum<CMP>(wave_sum16x4(z_run)) * unps;
   float zm_tot[NCV];
 #pragma unroll
-  for (int k = 0; k < NCV; k++) zm_tot[k] = VMIX ? wave_sum16x4(zm_run[k]) * unps : 0.0f;
+  for (int k = 0; k < NCV; k++) zm_tot[k] = VMIX ? part_sum<CMP>(wave_sum16x4(zm_run[k])) * unps : 0.0f;
   const float of = exp2i(24 - ps);           // acc_o * 2^24 / 2^ps
   if (lg == 0) {
     sh_ml[wave][n][0] = m_run;
@@ -1833,13 +1954,13 @@ constexpr int ns_cap(int kb, int vb) {
 // group cut into n_chunks chunks of tpc tiles, aiming at one round of
 // resident workgroups (256 CUs x waves per SIMD) with 4..64 tiles per chunk and
 // at most KVQ_MAX_CHUNKS chunks.
-static DecodePlan plan_for(int BH, int ns, int k_bits, int v_bits, int pdt, int n_tiles, int max_chunks) {
+static DecodePlan plan_for(int BH, int ns, int k_bits, int v_bits, int pdt, int n_tiles, int max_chunks, int G) {
   DecodePlan p;
   p.ns = ns;
   p.n_groups = (BH + ns - 1) / ns;
   const long total = (long)p.n_groups * n_tiles;
   // about one round of resident workgroups
-  const long wg_target = (long)KVQ_DECODE_WG_PER_OCC * decode_occ(k_bits, v_bits, pdt, ns);
+  const long wg_target = (long)KVQ_DECODE_WG_PER_OCC * decode_occ(k_bits, v_bits, pdt, ns, cmp_for(k_bits, v_bits, ns, G));
   int tpc = (int)((total + wg_target - 1) / wg_target);
   tpc = ((tpc + 3) / 4) * 4;
   if (tpc < 4) tpc = 4;
@@ -1861,8 +1982,8 @@ DecodePlan decode_plan(int BH, int G, int k_bits, int v_bits, int pdt, int n_til
   int ns = 16 / G;
   if (ns > KVQ_DECODE_NS_MAX) ns = KVQ_DECODE_NS_MAX;
   ns = ns > cap ? cap : (ns < 1 ? 1 : ns);
-  DecodePlan p = plan_for(BH, ns, k_bits, v_bits, pdt, n_tiles, max_chunks);
-  if (ns > 1 && p.tpc < KVQ_DECODE_NS_MIN_TPC) p = plan_for(BH, 1, k_bits, v_bits, pdt, n_tiles, max_chunks);
+  DecodePlan p = plan_for(BH, ns, k_bits, v_bits, pdt, n_tiles, max_chunks, G);
+  if (ns > 1 && p.tpc < KVQ_DECODE_NS_MIN_TPC) p = plan_for(BH, 1, k_bits, v_bits, pdt, n_tiles, max_chunks, G);
   return p;
 }
 
@@ -1986,13 +2107,15 @@ static hipError_t launch_ns(const DecodeArgs& a0, const DecodePlan& p, hipStream
   const dim3 grid(a.n_chunks, a.n_groups + res_rows), block(256);
   if (p.ns == 1) {
     // one stream: a compacted softmax where the heads fill at most a half or
-    // a quarter of the MFMA columns
+    // a quarter of the MFMA columns (with two streams per wave it measured no
+    // faster: B = 8 x 32K mixed keys and B = 16 x 32K 2-bit codes, G = 4)
     if constexpr (cmp_instance(KB, VB)) {
-      if (KVQ_DECODE_CMP && a.G <= 4) {
+      const int cmp = cmp_for(KB, VB, 1, a.G);
+      if (cmp == 4) {
         hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 1, 4>), grid, block, 0, st, a);
         return hipGetLastError();
       }
-      if (KVQ_DECODE_CMP && a.G <= 8) {
+      if (cmp == 2) {
         hipLaunchKernelGGL((decode_kernel<KB, VB, PDT, 1, 2>), grid, block, 0, st, a);
         return hipGetLastError();
       }

@@ -1,10 +1,10 @@
 """GPU parity of the compacted-softmax decode instances.
 
-With one kv stream per wave and at most 8 (4) query heads, the decode kernel
-spreads each head's logits over two (four) lanes of its MFMA row and gathers
-the probability operands back for the value product (2-bit values, uniform or
-mixed-width keys).  The cases below force that plan (few streams and tiles, so
-the launch takes one stream per wave) for every group size it serves, every
+With one kv stream per wave whose heads fill at most half (a quarter) of the
+16 MFMA columns, the decode kernel spreads each head's logits and query fold
+over two (four) lanes of its MFMA row and gathers the operands back for the
+two products (2-bit values, uniform or mixed-width keys).  The cases below
+force that plan (few streams and tiles) for every group size, every
 parameter dtype, a softmax whose reference max moves inside tiles (the rescale
 branch and its reductions over the lane parts), a negative scale and ragged
 chunk splits; each is gated against the float64 oracle at the per-row
@@ -95,3 +95,85 @@ def test_compacted_128k_sequence_sampled():
                                     inp["slot_chan"][h])
         ref = oracle.decode_attn(st, inp["q_bf16"][0, h * G:(h + 1) * G], SCALE)
         assert rel_err_rows(out[0, h * G:(h + 1) * G], ref).max() <= REL_TOL
+
+
+@pytest.mark.parametrize("kb,B,H,G,T", [(2, 16, 8, 4, 32768), (2, 16, 8, 2, 32768), (kvq.KMIXED, 4, 8, 2, 65536)],
+                         ids=["2bit_g4", "2bit_g2", "mixed_g2"])
+def test_compacted_two_streams_sampled(kb, B, H, G, T):
+    """Layers with chunks long enough for two streams per wave whose heads
+    fill half (G = 4) or a quarter (G = 2) of the MFMA columns (these keep
+    the uncompacted softmax): sampled streams, both members of a stream pair
+    among them, and the two decode phases reproduce the call bit for bit."""
+    Hq = H * G
+    print("case two streams kb=%d B=%d H=%d G=%d T=%d" % (kb, B, H, G, T), flush=True)
+    if kb == kvq.KMIXED:
+        dev = synth.mixed_layer_device(B, H, Hq, T, seed=530 + G, device="cuda")
+        cache = kvq.PackedCache(B, H, T, kb, 2, kvq.E4M3, slot_chan=dev["slot_chan"])
+        pdt = kvq.E4M3
+    else:
+        dev = synth.layer_device(B, H, Hq, T, seed=540 + G, device="cuda")
+        cache = kvq.PackedCache(B, H, T, kb, 2, kvq.F16)
+        pdt = kvq.F16
+    cache.quantize(dev["k"], dev["v"], 0)
+    out = cache.decode_attn(dev["q"], SCALE).cpu().numpy()
+    assert np.isfinite(out).all()
+    ws = cache.workspace(Hq)
+    n, tps = cache.decode_partials(dev["q"], SCALE, workspace=ws)
+    assert n * tps >= T // 128 and (n - 1) * tps < T // 128
+    two = kvq.decode_combine(ws, B, H, Hq, n).cpu().numpy()
+    assert np.array_equal(two.view(np.uint32), out.view(np.uint32))
+    q_bits = dev["q"].view(torch.int16).cpu().numpy().view(np.uint16)
+    for b, h in [(0, 0), (0, 1), (B // 2, 5), (B - 1, 6), (B - 1, 7)]:
+        k = dev["k"][b, h].cpu().numpy()
+        v = dev["v"][b, h].cpu().numpy()
+        sc = None if kb != kvq.KMIXED else np.asarray(dev["slot_chan"])[h]
+        st = oracle.quantize_stream(k, v, kb, 2, PDT_ORACLE[pdt], sc)
+        ref = oracle.decode_attn(st, q_bits[b, h * G:(h + 1) * G], SCALE)
+        err = rel_err_rows(out[b, h * G:(h + 1) * G], ref).max()
+        assert err <= REL_TOL, "stream (%d,%d) rel err %.3e" % (b, h, err)
+
+
+@pytest.mark.parametrize("G", [2, 3, 4, 5, 8])
+@pytest.mark.parametrize("pdt", [kvq.E4M3, kvq.F16])
+def test_mixed_values_compacted(G, pdt):
+    """Mixed-width keys and values (4/3/1/2-bit value classes in 4- and 2-bit
+    field containers, whose probability registers pair tokens differently)."""
+    inp = synth.mixed_kv_layer(1, 2, 2 * G, 2432, seed=700 + 10 * G + pdt)
+    print("case mixed K+V G=%d pdt=%d" % (G, pdt), flush=True)
+    cache = kvq.PackedCache(1, 2, 2432, kvq.KMIXED, kvq.VMIXED, pdt, slot_chan=inp["slot_chan"],
+                            v_slot_chan=inp["v_slot_chan"])
+    cache.quantize(to_dev(inp["k"], torch), to_dev(inp["v"], torch), 0)
+    for scale in (SCALE, -SCALE):
+        out = cache.decode_attn(q_to_dev(inp["q_bf16"], torch), scale).cpu().numpy()
+        assert np.all(np.isfinite(out))
+        for h in range(2):
+            st = oracle.quantize_stream(inp["k"][0, h], inp["v"][0, h], kvq.KMIXED, kvq.VMIXED, PDT_ORACLE[pdt],
+                                        inp["slot_chan"][h], inp["v_slot_chan"][h])
+            ref = oracle.decode_attn(st, inp["q_bf16"][0, h * G:(h + 1) * G], scale)
+            err = rel_err_rows(out[0, h * G:(h + 1) * G], ref).max()
+            assert err <= REL_TOL, "mixed K+V G=%d scale=%g head %d: %.3e" % (G, scale, h, err)
+
+
+@pytest.mark.parametrize("G", [4, 7])
+def test_mixed_values_compacted_climbing(G):
+    """Mixed K+V with keys ramped along each head's query (the rescale of the
+    four per-class zero-point sums across the lane parts)."""
+    T = 4096
+    inp = synth.mixed_kv_layer(1, 2, 2 * G, T, seed=750 + G)
+    k = inp["k"].copy()
+    q = synth.bf16_bits_to_f32(inp["q_bf16"])
+    t = np.arange(T)
+    ramp = (t % 128) / 127.0 * 3.0 + (t // 128) / (T // 128)
+    for h in range(2):
+        d = q[0, h * G] / np.linalg.norm(q[0, h * G])
+        k[0, h] += (ramp[:, None] * d[None, :] * 10.0).astype(np.float32)
+    cache = kvq.PackedCache(1, 2, T, kvq.KMIXED, kvq.VMIXED, kvq.E4M3, slot_chan=inp["slot_chan"],
+                            v_slot_chan=inp["v_slot_chan"])
+    cache.quantize(to_dev(k, torch), to_dev(inp["v"], torch), 0)
+    out = cache.decode_attn(q_to_dev(inp["q_bf16"], torch), SCALE).cpu().numpy()
+    for h in range(2):
+        st = oracle.quantize_stream(k[0, h], inp["v"][0, h], kvq.KMIXED, kvq.VMIXED, PDT_ORACLE[kvq.E4M3],
+                                    inp["slot_chan"][h], inp["v_slot_chan"][h])
+        ref = oracle.decode_attn(st, inp["q_bf16"][0, h * G:(h + 1) * G], SCALE)
+        err = rel_err_rows(out[0, h * G:(h + 1) * G], ref).max()
+        assert err <= REL_TOL, "mixed K+V climbing G=%d head %d: %.3e" % (G, h, err)
