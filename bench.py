@@ -33,14 +33,14 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, profiles/decode_kernel_*.md)
 # for the kernel source with the given digest, and the factors that map each
 # counter onto true bytes: a plain 512 MiB device copy in the same run reads
-# FETCH_SIZE = 262158.7 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
-# fetch counter is scaled by 524288/262158.7 and the write counter by 1.  The
+# FETCH_SIZE = 262160.4 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
+# fetch counter is scaled by 524288/262160.4 and the write counter by 1.  The
 # figure is reported only while the kernel source is unchanged.
 COUNTER_TRAFFIC = {
-    "source_sha256": "45c521b321371d277e14942b746fbd2f9a07f05cb36f7a17bbd0ca7488a32811",
-    "fetch_kib": 139900.0,
+    "source_sha256": "e812367a567e0897e6eeb82ea99eff0946e4cbc61c294c3b927d893896d98fb7",
+    "fetch_kib": 139901.5,
     "write_kib": 3664.0,
-    "fetch_factor": 524288.0 / 262158.7,
+    "fetch_factor": 524288.0 / 262160.4,
     "write_factor": 1.0,
 }
 KERNEL_SOURCES = ("kv_cache_mixed_amd/csrc/decode_attn.hip", "kv_cache_mixed_amd/csrc/kvq_device.h")
