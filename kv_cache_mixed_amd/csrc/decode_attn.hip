@@ -1055,22 +1055,46 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS, CMP)) void decode_
     *(u32x4*)&qs[cn][8 * part] = v;
   } else {
     // mixed widths: lane-order position p = 32 lane group + li holds slot
-    // mixed_lane_slot(p / 32, p % 32), i.e. channel slot_chan[kv head][slot]
+    // mixed_lane_slot(p / 32, p % 32), i.e. channel slot_chan[kv head][slot].
+    // The raw query rows (one 16-byte load per thread) and the group's slot
+    // maps go to LDS together -- one memory round trip instead of a map load
+    // followed by a gather that depends on it -- and the permutation runs in
+    // LDS (the raw rows sit in wave 0's folded-query region, unused until the
+    // first fold, after the barrier below).
+    uint16_t* qraw = (uint16_t*)&lds[0][0];     // [16][128], channel order
+    int16_t* smap = (int16_t*)(qraw + 16 * 128);   // [NS][128] slot -> channel
+    static_assert(sizeof(lds[0]) >= (16 * 128 + NS * 128) * 2, "raw query rows and slot maps fit");
+    {
+      const int cn = threadIdx.x >> 4, part = threadIdx.x & 15;
+      const int64_t row = (int64_t)grp * NS * G + cn;
+      u32x4 v = (u32x4){0u, 0u, 0u, 0u};
+      if (cn < NS * G && row < (int64_t)BH * G) v = *(const u32x4*)(a.q + row * 128 + 8 * part);
+      int16_t sm[(NS * 128 + 255) / 256];
+#pragma unroll
+      for (int e = 0; e < (NS * 128 + 255) / 256; e++) {
+        const int idx = threadIdx.x + 256 * e, cs = idx >> 7;
+        sm[e] = (idx < NS * 128 && grp * NS + cs < BH) ? g.slot_chan[((grp * NS + cs) % g.H) * 128 + (idx & 127)] : 0;
+      }
+      v ^= (u32x4)qflip;
+      if (q0 < t_count) load(b0, q0, 0);
+      *(u32x4*)&qraw[cn * 128 + 8 * part] = v;
+#pragma unroll
+      for (int e = 0; e < (NS * 128 + 255) / 256; e++) {
+        const int idx = threadIdx.x + 256 * e;
+        if (idx < NS * 128) smap[idx] = sm[e];
+      }
+    }
+    __syncthreads();
     uint16_t qv[8];
 #pragma unroll
     for (int r = 0; r < 8; r++) {
       const int i = threadIdx.x + 256 * r;
       const int cn = i >> 7, pp = i & 127;
       const int cs = cn / G;
-      const int cbh = grp * NS + cs;
       qv[r] = 0;
-      if (cs < NS && cbh < BH) {
-        const int chh = cbh % g.H;
-        const int j = mixed_lane_slot(pp >> 5, pp & 31);
-        qv[r] = a.q[((int64_t)grp * NS * G + cn) * 128 + (g.slot_chan[chh * 128 + j] & 127)] ^ (uint16_t)qflip;
-      }
+      if (cs < NS && grp * NS + cs < BH)
+        qv[r] = qraw[cn * 128 + (smap[cs * 128 + mixed_lane_slot(pp >> 5, pp & 31)] & 127)];
     }
-    if (q0 < t_count) load(b0, q0, 0);
 #pragma unroll
     for (int r = 0; r < 8; r++) {
       const int i = threadIdx.x + 256 * r;
