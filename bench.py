@@ -83,6 +83,8 @@ CASES = {
     "qwen7b_layer_2bit": (16, 4, 28, 32768, 2, 2, "F16"),
     "qwen7b_b8_layer_2bit": (8, 4, 28, 32768, 2, 2, "F16"),
     "llama8b_layer_2bit": (16, 8, 32, 32768, 2, 2, "F16"),
+    "qwen7b_b8_layer_4bit": (8, 4, 28, 32768, 4, 4, "F16"),
+    "qwen7b_b8_layer_8bit": (8, 4, 28, 16384, 8, 8, "F16"),
     "qwen32b_layer_4bit": (16, 8, 40, 32768, 4, 4, "F16"),
     "qwen32b_layer_2bit": (16, 8, 40, 32768, 2, 2, "F16"),
     "qwen32b_layer_8bit": (16, 8, 40, 32768, 8, 8, "F16"),

@@ -200,6 +200,76 @@ constexpr bool ok() {
 }
 static_assert(ok(), "2-bit value field map");
 }  // namespace cmp_check
+
+// Compacted-softmax geometry.  Value side: part pa of a row owns probability
+// registers pa * RPL .. pa * RPL + RPL - 1 of a sub-tile; slot sl < RPL of
+// the part is the low-half token of register pa * RPL + sl, slot RPL + r the
+// high-half token of register pa * RPL + r.
+template <int VB, int RPL>
+__host__ __device__ constexpr int cmp_tok(int pa, int sl) {
+  return sl < RPL ? ufield<VB>(pa * RPL + sl).lo : ufield<VB>(pa * RPL + sl - RPL).hi;
+}
+// Key side (the fold): part pa computes folded-query registers pa * NFP ..;
+// register f's halves hold the lane-order slots kslot_lo(f), kslot_hi(f)
+// (mixed keys: 2f and 2f + 1).
+template <int KB>
+__host__ __device__ constexpr int kslot_lo(int f) { return KB == 0 ? 2 * f : ufield<KB == 0 ? 2 : KB>(f).lo; }
+template <int KB>
+__host__ __device__ constexpr int kslot_hi(int f) { return KB == 0 ? 2 * f + 1 : ufield<KB == 0 ? 2 : KB>(f).hi; }
+namespace cmp_check {
+// every part's low and high tokens are two runs of RPL consecutive tokens
+template <int VB, int CMP, int FVS>
+constexpr bool vruns() {
+  constexpr int RPL = FVS / CMP;
+  for (int pa = 0; pa < CMP; pa++)
+    for (int r = 0; r < RPL; r++)
+      if (cmp_tok<VB, RPL>(pa, r) != cmp_tok<VB, RPL>(pa, 0) + r ||
+          cmp_tok<VB, RPL>(pa, RPL + r) != cmp_tok<VB, RPL>(pa, RPL) + r)
+        return false;
+  return true;
+}
+static_assert(vruns<2, 2, 8>() && vruns<2, 4, 8>() && vruns<4, 2, 4>() && vruns<4, 4, 4>() && vruns<8, 2, 4>() &&
+              vruns<8, 4, 4>(), "value token runs");
+// a part's slot offsets from its first slot do not depend on the part
+template <int KB, int CMP>
+constexpr bool kshift() {
+  constexpr int NFP = 16 / CMP;
+  for (int pa = 0; pa < CMP; pa++)
+    for (int j = 0; j < NFP; j++)
+      if (kslot_lo<KB>(pa * NFP + j) - kslot_lo<KB>(pa * NFP) != kslot_lo<KB>(j) - kslot_lo<KB>(0) ||
+          kslot_hi<KB>(pa * NFP + j) - kslot_lo<KB>(pa * NFP) != kslot_hi<KB>(j) - kslot_lo<KB>(0))
+        return false;
+  return true;
+}
+static_assert(kshift<0, 2>() && kshift<0, 4>() && kshift<2, 2>() && kshift<2, 4>() && kshift<4, 2>() &&
+              kshift<4, 4>() && kshift<8, 2>() && kshift<8, 4>(), "key slot offsets");
+}  // namespace cmp_check
+// whether a part's 2 NFP key slots form one run (else: low halves j, then
+// high halves at kslot_hi(0) - kslot_lo(0) + j)
+template <int KB, int CMP>
+__host__ __device__ constexpr bool kslot_run1() {
+  constexpr int NFP = 16 / CMP;
+  for (int t = 0; t < 2 * NFP; t++) {
+    bool found = false;
+    for (int j = 0; j < NFP; j++)
+      if (kslot_lo<KB>(j) - kslot_lo<KB>(0) == t || kslot_hi<KB>(j) - kslot_lo<KB>(0) == t) found = true;
+    if (!found) return false;
+  }
+  return true;
+}
+namespace cmp_check {
+template <int KB, int CMP>
+constexpr bool krun2() {   // two runs: lows are j, highs HIOFF + j
+  constexpr int NFP = 16 / CMP;
+  for (int j = 0; j < NFP; j++)
+    if (kslot_lo<KB>(j) - kslot_lo<KB>(0) != j || kslot_hi<KB>(j) - kslot_hi<KB>(0) != j) return false;
+  return true;
+}
+static_assert((kslot_run1<0, 2>() || krun2<0, 2>()) && (kslot_run1<0, 4>() || krun2<0, 4>()) &&
+              (kslot_run1<2, 2>() || krun2<2, 2>()) && (kslot_run1<2, 4>() || krun2<2, 4>()) &&
+              (kslot_run1<4, 2>() || krun2<4, 2>()) && (kslot_run1<4, 4>() || krun2<4, 4>()) &&
+              (kslot_run1<8, 2>() || krun2<8, 2>()) && (kslot_run1<8, 4>() || krun2<8, 4>()), "key slot runs");
+}  // namespace cmp_check
 namespace mixed_check {
 // the lane map is a bijection of the 128 slots and its inverse is exact
 constexpr bool ok() {
@@ -491,11 +561,15 @@ __device__ __forceinline__ void pload_runs(__amdgpu_buffer_rsrc_t r, uint32_t vo
   if constexpr (RB >= 4) {
     pload<PDT, N>(r, voff_lo, soff, w);
     pload<PDT, N>(r, voff_hi, soff, w + RB / 4);
-  } else {
-    static_assert(RB == 2, "parameter run");
+  } else if constexpr (RB == 2) {
     const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(r, voff_lo, soff, KVQ_DECODE_CPOL_PARAMS);
     const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(r, voff_hi, soff, KVQ_DECODE_CPOL_PARAMS);
     w[0] = lo | (hi << 16);
+  } else {
+    static_assert(RB == 1, "parameter run");
+    const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b8(r, voff_lo, soff, KVQ_DECODE_CPOL_PARAMS);
+    const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b8(r, voff_hi, soff, KVQ_DECODE_CPOL_PARAMS);
+    w[0] = lo | (hi << 8);
   }
 }
 
@@ -549,7 +623,9 @@ constexpr bool pf1_instance(int kb, int vb, int ns) {
 #ifndef KVQ_DECODE_CMP
 #define KVQ_DECODE_CMP 1
 #endif
-constexpr bool cmp_instance(int kb, int vb) { return (vb == 2 && (kb == 0 || kb == 2)) || (kb == 0 && vb == 0); }
+constexpr bool cmp_instance(int kb, int vb) {
+  return (vb == 2 && (kb == 0 || kb == 2)) || (kb == 0 && vb == 0) || (kb == vb && (vb == 4 || vb == 8));
+}
 // the compaction a launch of ns streams per wave with G heads per stream uses
 constexpr int cmp_for(int kb, int vb, int ns, int G) {
   if (!KVQ_DECODE_CMP || ns != 1 || !cmp_instance(kb, vb)) return 1;
@@ -758,7 +834,8 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS, CMP)) void decode_
   // logits of column c are spread over lanes c, c + CPW, ... (part a of the
   // row takes the tokens of probability registers a * RPL .. a * RPL + RPL - 1)
   // and the probability registers go back to lane c for the value product.
-  static_assert(CMP == 1 || ((CMP == 2 || CMP == 4) && NS <= 2 && (VB == 2 || VMIX)), "compaction: 2-bit or mixed values");
+  static_assert(CMP == 1 || ((CMP == 2 || CMP == 4) && NS <= 2 && (VB == 2 || VB == 4 || VB == 8 || VMIX)),
+                "compaction: 2-, 4-, 8-bit or mixed values");
   constexpr int CPW = 16 / CMP;                      // lanes per part
   constexpr int RPL = FVS / CMP;                     // probability registers per lane (compacted)
   constexpr int NL = CMP > 1 ? 2 * RPL : TPS;        // tokens per lane in the softmax
@@ -857,20 +934,27 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS, CMP)) void decode_
   // are the two runs (low and high halves of its probability registers) of
   // RPL tokens at ufield offsets cpart * RPL and ufield<VB>(0).hi + cpart * RPL
   const int cpart = n / CPW, ccol = n % CPW;
-  const uint32_t vpoff_lo = vpoff + (uint32_t)(cpart * RPL * PB);
-  const uint32_t vpoff_hi = vpoff + (uint32_t)((ufield<VB == 0 ? 2 : VB>(0).hi + cpart * RPL) * PB);
+  constexpr int VBF = VB == 0 ? 2 : VB;   // mixed values: the 2-bit container's token order
+  int ctl = 0, cth = 0;   // first low / high token of the lane's part
   // field weights of the lane's probability registers: W = wexp - pos
   float cw[CMP > 1 ? RPL : 1], ciw[CMP > 1 ? RPL : 1], cew[CMP > 1 ? RPL : 1];
   if constexpr (CMP > 1) {
 #pragma unroll
+    for (int pa = 0; pa < CMP; pa++)
+      if (cpart == pa) { ctl = cmp_tok<VBF, RPL>(pa, 0); cth = cmp_tok<VBF, RPL>(pa, RPL); }
+#pragma unroll
     for (int r = 0; r < RPL; r++) {
-      const int k = cpart * RPL + r;   // register index in the sub-tile (one value word)
-      const int pos = k < 5 ? 2 * k : 2 * (k - 5);   // ufield<2>(k).pos
-      cw[r] = -(float)pos;
-      ciw[r] = exp2i(pos);
-      cew[r] = exp2i(-pos);
+      int w = 0;
+#pragma unroll
+      for (int pa = 0; pa < CMP; pa++)
+        if (cpart == pa) w = ufield<VBF>(pa * RPL + r).wexp - ufield<VBF>(pa * RPL + r).pos;
+      cw[r] = (float)w;
+      ciw[r] = exp2i(-w);
+      cew[r] = exp2i(w);
     }
   }
+  const uint32_t vpoff_lo = vpoff + (uint32_t)(ctl * PB);
+  const uint32_t vpoff_hi = vpoff + (uint32_t)(cth * PB);
   const __amdgpu_buffer_rsrc_t r_vs = rsrc((const uint8_t*)g.v_scale + s0 * NCV * g.max_tokens * PB, 0xffffffffu);
   const __amdgpu_buffer_rsrc_t r_vz = rsrc((const uint8_t*)g.v_zero + s0 * NCV * g.max_tokens * PB, 0xffffffffu);
   const __amdgpu_buffer_rsrc_t r_ks = rsrc((const uint8_t*)g.k_scale + s0 * g.max_tokens * PB, 0xffffffffu);
@@ -1128,12 +1212,22 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS, CMP)) void decode_
   // halves at offsets foff(j, 0), foff(j, 1)), whose query values stay in
   // registers; DPP row shifts gather the registers back to lane ccol.
   constexpr int NFP = NFK / CMP;
-  // uniform widths with four parts: the part's slots are two runs of NFP
-  // (low halves, then high halves 8 slots further); otherwise one run
-  constexpr bool FRUN2 = !MIXED && CMP == 4;
-  auto foff = [](int j, int half) -> int { return MIXED ? 2 * j + half : j + half * NFP; };
-  auto fli = [](int off) -> int { return FRUN2 ? (off < NFP ? off : 8 + off - NFP) : off; };   // offset -> li - cpbase
-  const int cpbase = MIXED ? 2 * NFP * cpart : (CMP == 4 ? 4 * cpart + 8 * (cpart >> 1) : 16 * cpart);
+  // the part's 2 NFP slots: one run from cpbase, or (2-bit keys with four
+  // parts) two runs of NFP, the low halves and the high halves HIOFF slots
+  // further.  foff: register j's halves as indices into the part's parameter
+  // array, fli: such an index as a slot offset from cpbase
+  constexpr bool FRUN2 = !kslot_run1<KB, CMP>();
+  constexpr int HIOFF = kslot_hi<KB>(0) - kslot_lo<KB>(0);
+  auto foff = [](int j, int half) -> int {
+    return FRUN2 ? j + half * NFP : (half ? kslot_hi<KB>(j) : kslot_lo<KB>(j)) - kslot_lo<KB>(0);
+  };
+  auto fli = [](int off) -> int { return FRUN2 ? (off < NFP ? off : HIOFF + off - NFP) : off; };
+  int cpbase = 0;
+  if constexpr (CMP > 1) {
+#pragma unroll
+    for (int pa = 0; pa < CMP; pa++)
+      if (cpart == pa) cpbase = kslot_lo<KB>(pa * NFP);
+  }
   float qv[CMP > 1 ? 2 * NFP : 1];
   int fwl[CMP > 1 ? NFP : 1], fwh[CMP > 1 ? NFP : 1];   // field weight exponents of register j's halves
   if constexpr (CMP > 1) {
@@ -1209,7 +1303,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS, CMP)) void decode_
         for (int i = 0; i < RW; i++) pw[i] = src[w0 + i];
         if constexpr (FRUN2) {
 #pragma unroll
-          for (int i = 0; i < RW; i++) pw[RW + i] = src[w0 + 8 * PB / 4 + i];
+          for (int i = 0; i < RW; i++) pw[RW + i] = src[w0 + HIOFF * PB / 4 + i];
         }
       };
       constexpr int PWP = (FRUN2 ? 2 : 1) * RW;
@@ -1419,8 +1513,7 @@ __global__ __launch_bounds__(256, decode_occ(KB, VB, PDT, NS, CMP)) void decode_
     // the row (part 0 keeps its own)
     float lc[NL];
     if constexpr (CMP > 1) {
-      // (ufield<2>(k).lo = k and .hi = 8 + k: cmp_check)
-      auto tok = [](int pa, int sl) -> int { return sl < RPL ? pa * RPL + sl : 8 + pa * RPL + sl - RPL; };
+      auto tok = [](int pa, int sl) -> int { return cmp_tok<VBF, RPL>(pa, sl); };
 #pragma unroll
       for (int sl = 0; sl < NL; sl++) {
         uint32_t x = f2u(lv[tok(0, sl)]);

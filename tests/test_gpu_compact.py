@@ -3,7 +3,8 @@
 With one kv stream per wave whose heads fill at most half (a quarter) of the
 16 MFMA columns, the decode kernel spreads each head's logits and query fold
 over two (four) lanes of its MFMA row and gathers the operands back for the
-two products (2-bit values, uniform or mixed-width keys).  The cases below
+two products (2-, 4- and 8-bit values with keys of the same width, 2-bit or
+mixed values with mixed-width keys).  The cases below
 force that plan (few streams and tiles) for every group size, every
 parameter dtype, a softmax whose reference max moves inside tiles (the rescale
 branch and its reductions over the lane parts), a negative scale and ragged
@@ -28,18 +29,18 @@ def _setup():
     kvq.load()
 
 
-def _check(k, v, q_bits, kb, pdt, scale, slot_chan=None, what=""):
+def _check(k, v, q_bits, kb, pdt, scale, slot_chan=None, what="", vb=2):
     B, H, T, _ = k.shape
     G = q_bits.shape[1] // H
-    print("case %s B=%d H=%d G=%d T=%d kb=%d pdt=%d scale=%g" % (what, B, H, G, T, kb, pdt, scale), flush=True)
-    cache = kvq.PackedCache(B, H, T, kb, 2, pdt, slot_chan=slot_chan)
+    print("case %s B=%d H=%d G=%d T=%d kb=%d vb=%d pdt=%d scale=%g" % (what, B, H, G, T, kb, vb, pdt, scale), flush=True)
+    cache = kvq.PackedCache(B, H, T, kb, vb, pdt, slot_chan=slot_chan)
     cache.quantize(to_dev(k, torch), to_dev(v, torch), 0)
     out = cache.decode_attn(q_to_dev(q_bits, torch), scale).cpu().numpy()
     assert np.all(np.isfinite(out)), what
     worst = 0.0
     for b in range(B):
         for h in range(H):
-            st = oracle.quantize_stream(k[b, h], v[b, h], kb, 2, PDT_ORACLE[pdt],
+            st = oracle.quantize_stream(k[b, h], v[b, h], kb, vb, PDT_ORACLE[pdt],
                                         None if slot_chan is None else slot_chan[h])
             ref = oracle.decode_attn(st, q_bits[b, h * G:(h + 1) * G], scale)
             worst = max(worst, rel_err_rows(out[b, h * G:(h + 1) * G], ref).max())
@@ -60,7 +61,17 @@ def test_two_bit_compacted(G, pdt):
     _check(inp["k"], inp["v"], inp["q_bf16"], 2, pdt, SCALE, what="2-bit G=%d" % G)
 
 
-@pytest.mark.parametrize("kb,G", [(2, 4), (2, 7), (kvq.KMIXED, 4), (kvq.KMIXED, 6)])
+@pytest.mark.parametrize("bits", [4, 8])
+@pytest.mark.parametrize("G", [1, 3, 4, 6, 8])
+@pytest.mark.parametrize("pdt", [kvq.F16, kvq.E4M3, kvq.BF16, kvq.F32])
+def test_wider_codes_compacted(bits, G, pdt):
+    """4- and 8-bit codes: sub-tiles of 8 tokens per lane group, so a part
+    holds one (four parts) or two (two parts) probability registers."""
+    inp = synth.layer(2, 1, G, 2944, seed=800 + 10 * G + pdt + bits)
+    _check(inp["k"], inp["v"], inp["q_bf16"], bits, pdt, SCALE, what="%d-bit G=%d" % (bits, G), vb=bits)
+
+
+@pytest.mark.parametrize("kb,G", [(2, 4), (2, 7), (kvq.KMIXED, 4), (kvq.KMIXED, 6), (4, 3), (4, 7), (8, 4), (8, 8)])
 def test_compacted_climbing_logits(kb, G):
     """Keys ramped along each head's query: logits climb by ~40 log2 units
     inside every tile and across tiles, so the per-column reference moves
@@ -78,8 +89,10 @@ def test_compacted_climbing_logits(kb, G):
     slot_chan = None
     if kb == kvq.KMIXED:
         slot_chan = synth.mixed_layer(1, H, H * G, 128, seed=510)["slot_chan"]
-    _check(k, v, synth.to_bf16_bits(q), kb, kvq.F16, SCALE, slot_chan, what="climbing kb=%d G=%d" % (kb, G))
-    _check(k, v, synth.to_bf16_bits(q), kb, kvq.E4M3, -SCALE, slot_chan, what="climbing, negative kb=%d G=%d" % (kb, G))
+    vb = 2 if kb in (2, kvq.KMIXED) else kb
+    _check(k, v, synth.to_bf16_bits(q), kb, kvq.F16, SCALE, slot_chan, what="climbing kb=%d G=%d" % (kb, G), vb=vb)
+    _check(k, v, synth.to_bf16_bits(q), kb, kvq.E4M3, -SCALE, slot_chan, what="climbing, negative kb=%d G=%d" % (kb, G),
+           vb=vb)
 
 
 def test_compacted_128k_sequence_sampled():
