@@ -33,14 +33,14 @@ PEAK_HBM_GBS = 8000.0
 # (FETCH_SIZE and WRITE_SIZE, KiB per dispatch, profiles/decode_kernel_*.md)
 # for the kernel source with the given digest, and the factors that map each
 # counter onto true bytes: a plain 512 MiB device copy in the same run reads
-# FETCH_SIZE = 262160.1 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
-# fetch counter is scaled by 524288/262160.1 and the write counter by 1.  The
+# FETCH_SIZE = 262160.5 KiB and WRITE_SIZE = 524288.0 KiB per dispatch, so the
+# fetch counter is scaled by 524288/262160.5 and the write counter by 1.  The
 # figure is reported only while the kernel source is unchanged.
 COUNTER_TRAFFIC = {
-    "source_sha256": "57f7af10f6de280e986f3daa10aa732fceb3f10440e06da67e1fc735749c7e5a",
-    "fetch_kib": 139901.5,
+    "source_sha256": "00f4b36e8ecfbb924845dc2833802270d4e6366c35fcf5b4ab1e53b4deabe8b8",
+    "fetch_kib": 139895.0,
     "write_kib": 3664.0,
-    "fetch_factor": 524288.0 / 262160.1,
+    "fetch_factor": 524288.0 / 262160.5,
     "write_factor": 1.0,
 }
 KERNEL_SOURCES = ("kv_cache_mixed_amd/csrc/decode_attn.hip", "kv_cache_mixed_amd/csrc/kvq_device.h")
