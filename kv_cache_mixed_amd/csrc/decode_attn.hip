@@ -48,6 +48,15 @@
 // Softmax uses a lazy running max: the reference m only moves when a logit
 // exceeds it by more than TAU (log2 units), so e = 2^(logit - m) <= 2^TAU and
 // the output accumulator is rescaled only when some head's reference moved.
+//
+// Compacted softmax (one stream per wave with G <= 8 or G <= 4 heads, 1/2 or
+// 3/4 of the 16 columns without a head): the CMP lane parts of an MFMA row
+// share each head's work.  DPP row shifts spread the column's logits over the
+// parts (each takes the tokens of its share of the probability registers),
+// every part runs the softmax, the value-parameter loads and the zero-point
+// sums on its tokens and folds its share of the query slots, and DPP row
+// shifts bring the probability and folded-query registers back to the lanes
+// of the head columns for the two products.
 #include "kvq_device.h"
 
 #include <mutex>
